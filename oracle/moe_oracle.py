@@ -1,0 +1,275 @@
+"""Float64 CPU oracle of the fused MoE layer, forward and backward. TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the package's smoke check and the benchmark's CPU-baseline leg may import
+this module. The HIP library never calls it. It shares no code with the HIP path, and it imports
+nothing from the product package.
+
+What the layer computes comes from three news pages about Prime Intellect's "Prime Mega MoE"
+(an extension of DeepSeek's "Mega MoE" kernel).
+ * Dispatch of tokens to experts, the experts' linear layers, SwiGLU and the combine of the
+   results happen in one fused call: "A Magia da Fusão" on "IA: MoE Kernel 3x Mais Rápido
+   Chegou!", and "Qué se ha publicado" on the ai-daily-news.org page.
+ * Experts are gated SwiGLU without biases: "Detalhes Técnicos Rápidos" on the first page.
+ * 128 experts with top-8 routing: "Os Números que Impressionam" on the first page, and
+   "Analisi dei kernel layer" on "Prime Mega MoE: il kernel che accelera il training AI
+   del 55%".
+ * The backward pass is the part Prime added: "Afinal, o que é esse Prime Mega MoE?" on the
+   first page.
+The pages give no formulas. Where they are silent, this module takes the plainest reading:
+ * softmax routing over fp32 logits, top-k, renormalised over the chosen k;
+ * ties go to the lower expert index;
+ * silu(gate) * up;
+ * a weighted sum in the combine;
+ * no capacity limit and no token dropping.
+Each function states its reading.
+
+Arrays may arrive as float32, including bf16-exact values. Every computation converts them to
+float64 before any arithmetic.
+
+Parity status: every function here is pinned by tests that do not go through this code:
+ * brute-force loops;
+ * closed forms;
+ * torch's own functional ops and autograd;
+ * central finite differences.
+No function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+# ----------------------------------------------------------------------------------------------
+# routing
+
+def topk_select(logits, k):
+    """Top-k expert indices per token, ordered by (logit descending, expert index ascending).
+
+    Reading: the pages only say "top-8 routing". Selection is on the fp32 logits themselves.
+    Softmax is monotone, so in exact arithmetic this is the same set as top-k over the
+    probabilities. Ties go to the lower expert index, and -0.0 equals +0.0.
+    """
+    lg = _f64(logits)
+    # a stable sort of the negated logits puts equal values in ascending index order
+    order = np.argsort(-lg, axis=1, kind="stable")
+    return order[:, :k].astype(np.int64)
+
+
+def renormalised_weights(logits, idx):
+    """w[t,j] = softmax over all experts, restricted to the chosen k and renormalised.
+
+    The softmax normaliser cancels in the renormalisation, so
+    w_tj = exp(l_{t,S_tj} - m_t) / sum_i exp(l_{t,S_ti} - m_t), with m_t the largest chosen
+    logit. No epsilon is added to the denominator.
+    """
+    lg = _f64(logits)
+    sel = np.take_along_axis(lg, idx, axis=1)
+    z = np.exp(sel - sel.max(axis=1, keepdims=True))
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def route(logits, k, e0=0, e_local=None):
+    """Full routing metadata for the experts [e0, e0+e_local).
+
+    Returns a dict:
+      idx      [T,k]   chosen experts (global ids)
+      w        [T,k]   renormalised weights
+      counts   [El]    pairs routed to each local expert
+      offsets  [El+1]  exclusive prefix sum of counts
+      perm     [P]     pair ids (t*k + j) sorted by (local expert, pair id): a stable counting
+                       sort, which is the "token sorting" the pages name as a cost
+      pair_pos [T*k]   inverse of perm; -1 for pairs whose expert is not local
+    """
+    lg = _f64(logits)
+    T, E = lg.shape
+    el = E - e0 if e_local is None else e_local
+    idx = topk_select(lg, k)
+    w = renormalised_weights(lg, idx)
+    flat = idx.reshape(-1)
+    local = (flat >= e0) & (flat < e0 + el)
+    pair_ids = np.nonzero(local)[0]
+    experts = flat[pair_ids] - e0
+    counts = np.bincount(experts, minlength=el).astype(np.int64)
+    offsets = np.zeros(el + 1, np.int64)
+    offsets[1:] = np.cumsum(counts)
+    perm = pair_ids[np.argsort(experts, kind="stable")]
+    pair_pos = np.full(T * k, -1, np.int64)
+    pair_pos[perm] = np.arange(perm.size)
+    return dict(idx=idx, w=w, counts=counts, offsets=offsets, perm=perm, pair_pos=pair_pos,
+                k=k, e0=e0, el=el)
+
+
+# ----------------------------------------------------------------------------------------------
+# expert feed-forward (gated SwiGLU, no biases)
+
+def sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def silu(z):
+    return z * sigmoid(z)
+
+
+def dsilu(z):
+    """d/dz [z * sigmoid(z)] = sigmoid(z) * (1 + z * (1 - sigmoid(z)))."""
+    s = sigmoid(z)
+    return s * (1.0 + z * (1.0 - s))
+
+
+def expert_forward(xr, wg_e, wu_e, wd_e):
+    """One expert on its rows xr [n,H]: a = xr Wg^T, b = xr Wu^T, h = silu(a)*b, o = h Wd^T."""
+    xr = _f64(xr)
+    a = xr @ _f64(wg_e).T
+    b = xr @ _f64(wu_e).T
+    h = silu(a) * b
+    o = h @ _f64(wd_e).T
+    return a, b, h, o
+
+
+def _expert_rows(r, i):
+    """(pair ids, token ids, weights) of local expert i, in the stable pair order."""
+    pairs = r["perm"][r["offsets"][i]:r["offsets"][i + 1]]
+    return pairs, pairs // r["k"], r["w"].reshape(-1)[pairs]
+
+
+# ----------------------------------------------------------------------------------------------
+# forward
+
+def forward(x, logits, wg, wu, wd, k, e0=0, e_local=None):
+    """y[t] = sum over the local chosen slots j of w_tj * FFN_{S_tj}(x_t).
+
+    wg, wu [El,F,H] and wd [El,H,F] hold the local experts e0..e0+El-1. A token with no local
+    slot gets y = 0. For a share of the experts, y is that share's partial sum; the layer output
+    is the sum over shares.
+    """
+    x = _f64(x)
+    T, H = x.shape
+    r = route(logits, k, e0, e_local if e_local is not None else len(wg))
+    y = np.zeros((T, H))
+    for i in range(r["el"]):
+        pairs, toks, wr = _expert_rows(r, i)
+        if pairs.size == 0:
+            continue
+        _, _, _, o = expert_forward(x[toks], wg[i], wu[i], wd[i])
+        y[toks] += wr[:, None] * o          # a token meets an expert at most once
+    return y, r
+
+
+# ----------------------------------------------------------------------------------------------
+# backward
+
+def backward(dy, x, logits, wg, wu, wd, k, e0=0, e_local=None):
+    """Gradients of L = <dY, y> with respect to x, the router logits and the expert weights.
+
+    Per routed pair (t, j) with expert e and weight w = w_tj:
+      u  = Wd[e]^T dY_t                   (dL/dh before the routing weight)
+      g  = <u, h> = <dY_t, o_tj>         (dL/dw_tj)
+      dh = w u
+      da = dh * b * dsilu(a),  db = dh * silu(a)
+      dWd[e] += (w dY_t) h^T,  dWg[e] += da x_t^T,  dWu[e] += db x_t^T
+      dx_t   += Wg[e]^T da + Wu[e]^T db
+    Router: dlogits[t, S_ti] = w_ti (g_ti - sum_j w_tj g_tj). Slots whose expert is not local
+    have g = 0. Unchosen experts get 0. The index selection is piecewise constant and carries no
+    gradient.
+    Reading: the pages name only a backward pass (dgrad, wgrad, dSwiGLU and the router-weight
+    gradient are the parts any such pass must produce).
+    """
+    x, dy = _f64(x), _f64(dy)
+    T, H = x.shape
+    el = e_local if e_local is not None else len(wg)
+    r = route(logits, k, e0, el)
+    E = np.asarray(logits).shape[1]
+    dx = np.zeros((T, H))
+    g = np.zeros(T * k)
+    dwg = np.zeros(np.shape(wg))
+    dwu = np.zeros(np.shape(wu))
+    dwd = np.zeros(np.shape(wd))
+    for i in range(el):
+        pairs, toks, wr = _expert_rows(r, i)
+        if pairs.size == 0:
+            continue
+        xe, dye = x[toks], dy[toks]
+        a, b, h, _ = expert_forward(xe, wg[i], wu[i], wd[i])
+        u = dye @ _f64(wd[i])
+        g[pairs] = np.sum(u * h, axis=1)
+        dh = wr[:, None] * u
+        da = dh * b * dsilu(a)
+        db = dh * silu(a)
+        dwd[i] = (wr[:, None] * dye).T @ h
+        dwg[i] = da.T @ xe
+        dwu[i] = db.T @ xe
+        dx[toks] += da @ _f64(wg[i]) + db @ _f64(wu[i])
+    dlogits = router_grad(r, g.reshape(T, k), E)
+    return dict(dx=dx, dlogits=dlogits, dwg=dwg, dwu=dwu, dwd=dwd, g=g.reshape(T, k)), r
+
+
+def router_grad(r, g, E):
+    """dlogits [T,E] from g[t,j] = dL/dw_tj through the renormalised softmax."""
+    w = r["w"]
+    T, k = w.shape
+    dsel = w * (g - np.sum(w * g, axis=1, keepdims=True))
+    dl = np.zeros((T, E))
+    np.put_along_axis(dl, r["idx"], dsel, axis=1)
+    return dl
+
+
+# ----------------------------------------------------------------------------------------------
+# sampled evaluation for full-size layers: each quantity below depends only on the pairs named
+
+def token_rows(tokens, dy, x, logits, wg, wu, wd, k, e0=0, e_local=None):
+    """y, dx and dlogits rows of the given tokens. They need only those tokens' own pairs."""
+    x, dy = _f64(x), _f64(dy)
+    el = e_local if e_local is not None else len(wg)
+    lg = _f64(logits)[np.asarray(tokens)]
+    idx = topk_select(lg, k)
+    w = renormalised_weights(lg, idx)
+    n, H = len(tokens), x.shape[1]
+    y = np.zeros((n, H))
+    dx = np.zeros((n, H))
+    g = np.zeros((n, k))
+    for q, t in enumerate(tokens):
+        for j in range(k):
+            e = int(idx[q, j])
+            if not (e0 <= e < e0 + el):
+                continue
+            i = e - e0
+            a, b, h, o = expert_forward(x[t:t + 1], wg[i], wu[i], wd[i])
+            y[q] += w[q, j] * o[0]
+            u = dy[t:t + 1] @ _f64(wd[i])
+            g[q, j] = np.sum(u * h)
+            dh = w[q, j] * u
+            da = dh * b * dsilu(a)
+            db = dh * silu(a)
+            dx[q] += (da @ _f64(wg[i]) + db @ _f64(wu[i]))[0]
+    rr = dict(w=w, idx=idx)
+    return dict(y=y, dx=dx, dlogits=router_grad(rr, g, lg.shape[1]), idx=idx, w=w)
+
+
+def expert_grads(i, dy, x, logits, wg_i, wu_i, wd_i, k, e0=0, e_local=None, r=None):
+    """dW_gate, dW_up, dW_down of local expert i. They need only that expert's rows."""
+    x, dy = _f64(x), _f64(dy)
+    if r is None:
+        r = route(logits, k, e0, e_local)
+    pairs, toks, wr = _expert_rows(r, i)
+    F, H = np.shape(wg_i)
+    if pairs.size == 0:
+        return np.zeros((F, H)), np.zeros((F, H)), np.zeros((H, F))
+    xe, dye = x[toks], dy[toks]
+    a, b, h, _ = expert_forward(xe, wg_i, wu_i, wd_i)
+    u = dye @ _f64(wd_i)
+    dh = wr[:, None] * u
+    da = dh * b * dsilu(a)
+    db = dh * silu(a)
+    return da.T @ xe, db.T @ xe, (wr[:, None] * dye).T @ h
+
+
+def rel_frobenius(got, ref):
+    """||got - ref||_F / ||ref||_F in float64. If ref is exactly zero, got must be zero too."""
+    got, ref = _f64(got), _f64(ref)
+    nr = np.linalg.norm(ref)
+    if nr == 0.0:
+        return 0.0 if not np.any(got) else float("inf")
+    return float(np.linalg.norm(got - ref) / nr)
