@@ -1,0 +1,192 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MoE layer (forward + backward) on one MI355X.
+
+One step is one forward and one backward pass of the whole layer:
+ * routing;
+ * gate/up GEMM with SwiGLU;
+ * down GEMM;
+ * combine;
+ * the backward GEMMs with dSwiGLU, and the dx/dlogits combine.
+It runs on one batch of synthetic inputs already resident in HBM. The default workload is the
+Qwen3-30B-A3B-shaped layer: T=16384, H=2048, 128 experts, F=768, top-8, bf16.
+
+Printed on one JSON line:
+  value         whole-layer TFLOP/s = 18*H*F*pairs / (forward+backward time)
+  roofline      the dominant kernel: algorithmic flops per launch / its mean duration (HIP events
+                on the launch stream) against the bf16 MFMA peak
+  cpu_baseline  the float64 oracle on a bounded sample (the pairs of 16 experts), host cores
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd+bwd ms and TFLOP/s (% MFMA peak), Qwen3-30B-A3B shape, T=16384"
+PEAK_TFLOPS = {"bf16": 2516.6, "fp32": 157.3}    # MI355X dense MFMA peaks
+PEAK_HBM_GBS = 8000.0
+
+# algorithmic work per kernel, per routed pair (GEMMs) or per launch (HBM kernels)
+GEMM_FLOPS_PER_PAIR = {  # in units of H*F
+    "gemm_gateup_swiglu": 4, "gemm_down": 2, "gemm_bwd_dh_dswiglu": 2,
+    "gemm_wgrad_down": 2, "gemm_wgrad_gateup": 4, "gemm_dgrad_x": 4,
+}
+
+
+def hbm_bytes(name, cfg, P, elem):
+    T, H, E, k = cfg.T, cfg.H, cfg.E, cfg.k
+    if name == "combine":
+        return P * H * elem + T * H * elem + T * k * 4
+    if name == "combine_bwd":
+        return P * H * elem + T * H * elem + T * E * 4 + T * k * (4 + 4 + 4) + P * (cfg.F // 64) * 4
+    if name == "route_topk":
+        return T * E * 4 + T * k * 8
+    return None
+
+
+def cpu_baseline(cfg, L, n_experts=16):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 0) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    sl = slice(0, n_experts)
+    args = dict(x=L["x"], logits=L["logits"], wg=L["wg"][sl], wu=L["wu"][sl], wd=L["wd"][sl], k=cfg.k, e0=0,
+                e_local=n_experts)
+    t0 = time.perf_counter()
+    _, r = oracle.forward(**args)
+    oracle.backward(dy=L["dy"], **args)
+    dt = time.perf_counter() - t0
+    P = int(r["counts"].sum())
+    fl = 18.0 * cfg.H * cfg.F * P
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"experts 0-{n_experts - 1} of {cfg.name} ({P} routed pairs), float64 forward+backward, "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="qwen3_30b_a3b")
+    ap.add_argument("--mode", default=None, help="fp32 or bf16 (default: the workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print("bench.py measures the one-GPU layer only: this build runs on a single MI355X and has no "
+              "multi-GPU path (how the layer would shard over experts is described in DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from mixture_experts_layer_32_amd import binding, inputs
+    from mixture_experts_layer_32_amd.layer import MoELayer
+
+    cfg = inputs.CONFIGS[a.config]
+    mode = a.mode or cfg.dtype
+    dt = torch.float32 if mode == "fp32" else torch.bfloat16
+    print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
+    L = inputs.make_layer(cfg)
+    dev = lambda arr, t=dt: torch.from_numpy(np.ascontiguousarray(arr)).to("cuda").to(t)
+    x, dy, lg = dev(L["x"]), dev(L["dy"]), dev(L["logits"], torch.float32)
+    wg, wu, wd = dev(L["wg"]), dev(L["wu"]), dev(L["wd"])
+    layer = MoELayer(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, mode, cfg.el, cfg.e0)
+    y = torch.empty(cfg.T, cfg.H, dtype=dt, device="cuda")
+    grads = dict(dx=torch.empty_like(x), dlogits=torch.empty(cfg.T, cfg.E, dtype=torch.float32, device="cuda"),
+                 dw_gate=torch.empty_like(wg), dw_up=torch.empty_like(wu), dw_down=torch.empty_like(wd))
+
+    def step():
+        layer.forward(x, lg, wg, wu, wd, y)
+        layer.backward(dy, x, wg, wu, wd, out=grads)
+
+    print(f"[bench] warmup {a.warmup}", file=sys.stderr, flush=True)
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    P = int(layer.routing()["offsets"][-1])
+
+    # timed region: K steps, forward/backward split by events on the library's stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in evs:
+        e0.record()
+        layer.forward(x, lg, wg, wu, wd, y)
+        e1.record()
+        layer.backward(dy, x, wg, wu, wd, out=grads)
+        e2.record()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / a.steps
+    fwd_ms = float(np.median([e0.elapsed_time(e1) for e0, e1, _ in evs]))
+    bwd_ms = float(np.median([e1.elapsed_time(e2) for _, e1, e2 in evs]))
+
+    # per-kernel durations: the same K steps again with every launch bracketed by HIP events
+    binding.profile_enable(64 * a.steps)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step_prof = (time.perf_counter() - t1) * 1e3 / a.steps
+    kern = binding.profile_collect()
+    binding.profile_disable()
+
+    flops = 18.0 * cfg.H * cfg.F * P
+    value = flops / (ms_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[mode]
+    per_kernel = {}
+    for name, (n, tot) in kern.items():
+        avg = tot / n
+        ent = {"avg_ms": round(avg, 5), "launches": n}
+        if name in GEMM_FLOPS_PER_PAIR:
+            fl = GEMM_FLOPS_PER_PAIR[name] * cfg.H * cfg.F * P
+            ent["tflops"] = round(fl / (avg * 1e-3) / 1e12, 2)
+            ent["pct_peak"] = round(100 * ent["tflops"] / peak, 2)
+        else:
+            by = hbm_bytes(name, cfg, P, 4 if mode == "fp32" else 2)
+            if by:
+                ent["gbs"] = round(by / (avg * 1e-3) / 1e9, 1)
+        per_kernel[name] = ent
+    dom = max(kern, key=lambda n: kern[n][1])
+    dn, dtot = kern[dom]
+    davg = dtot / dn
+    if dom in GEMM_FLOPS_PER_PAIR:
+        ach = GEMM_FLOPS_PER_PAIR[dom] * cfg.H * cfg.F * P / (davg * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4), "traffic": None, "kernel": dom, "avg_ms": round(davg, 5)}
+    else:
+        ach = hbm_bytes(dom, cfg, P, 4 if mode == "fp32" else 2) / (davg * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom, "avg_ms": round(davg, 5)}
+
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": mode, "data": "synthetic (seeded; random-init expert weights)",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "F": cfg.F, "E": cfg.E, "E_local": cfg.el,
+                   "topk": cfg.k, "routed_pairs": P},
+        "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+        "full_layer_2f_b_ms": round(2 * fwd_ms + bwd_ms, 4),
+        "pct_mfma_peak": round(100 * value / peak, 2),
+        "ms_per_step_with_kernel_events": round(ms_step_prof, 4),
+        "kernels": per_kernel, "roofline": roof,
+    }
+    if not a.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(cfg, L)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

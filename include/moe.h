@@ -1,0 +1,164 @@
+/*
+ * moe.h - C ABI of libmoe.so, a fused Mixture-of-Experts layer (forward and backward) for one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the layer computes. The pages on Prime Intellect's "Prime Mega MoE" (an extension of
+ * DeepSeek's "Mega MoE") describe one fused call per pass:
+ *  - "A Magia da Fusão" on "IA: MoE Kernel 3x Mais Rápido Chegou!" lists its steps: dispatch of
+ *    tokens to experts, the experts' linear layers, SwiGLU, and the combine of the results.
+ *  - "Afinal, o que é esse Prime Mega MoE?" on the same page adds the backward pass.
+ *  - "Detalhes Técnicos Rápidos" on the same page requires gated SwiGLU experts without biases,
+ *    hidden size a multiple of 256 and expert FFN size a multiple of 128.
+ *  - "Supporto di precisione e vincoli hardware" on "Prime Mega MoE: il kernel che accelera il
+ *    training AI del 55%" gives the precision modes.
+ *
+ * With T tokens, hidden size H, expert FFN size F, E routed experts and top-k routing:
+ *    S_t  = the k largest router logits of token t (ties to the lower expert index)
+ *    w_tj = exp(l_{t,S_tj}) / sum_i exp(l_{t,S_ti})        (softmax renormalised over S_t)
+ *    y_t  = sum_j w_tj * W_down[e] (silu(W_gate[e] x_t) * (W_up[e] x_t)),  e = S_tj
+ * The backward returns dx, dlogits (through the renormalised softmax) and dW_gate, dW_up,
+ * dW_down for the gradient dy of y.
+ *
+ * Expert share. The library computes the experts [expert_offset, expert_offset + E_local) of
+ * E_total. Routing always runs over all E_total experts, and w stays renormalised over the
+ * full top-k. Pairs routed outside the share are skipped. Outputs y, dx and dlogits are then
+ * this share's linear contribution: summed over all shares they give the full layer.
+ *
+ * Conventions common to every entry point:
+ *  - Every pointer is a device pointer unless the comment says "host". The caller allocates
+ *    every buffer, including the workspace and the saved-activation buffer sized by
+ *    moe_query_sizes(). The library never allocates, frees or caches device memory.
+ *  - All tensors are dense row-major. Let elem be float in MOE_MODE_FP32 and bf16 (raw 16-bit
+ *    storage) in every other mode:
+ *      x, y, dy, dx                  [T, H]            elem
+ *      logits, dlogits               [T, E_total]      float (fp32)
+ *      w_gate, w_up, dw_gate, dw_up  [E_local, F, H]   elem (out x in, K contiguous)
+ *      w_down, dw_down               [E_local, H, F]   elem
+ *  - stream is a hipStream_t (NULL: the default stream). Every call only enqueues work on it
+ *    and returns. No call synchronises the host or copies device data to the host.
+ *  - Validation happens on the host before anything is enqueued. On any error nothing is
+ *    enqueued and no output is touched. Launch failures return MOE_ERR_HIP. A device fault
+ *    surfaces at the caller's next synchronisation.
+ *  - Preconditions that are not checked: logits are finite, and buffers do not overlap.
+ *  - Results are deterministic: no floating-point atomics anywhere, so repeated calls give
+ *    bitwise-identical outputs.
+ *  - The library keeps no state between calls apart from the profiling records and a
+ *    thread-local error string. Calls on different streams may run concurrently if their
+ *    buffers are distinct.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Precision modes ("Supporto di precisione e vincoli hardware"; "A Magia da Fusão"):
+ *   FP32     all storage and arithmetic in fp32 (test mode).
+ *   BF16     bf16 storage; GEMMs on bf16 MFMA with fp32 accumulation; routing,
+ *            softmax, SwiGLU and combines in fp32.
+ *   MXFP8    bf16 storage; every GEMM operand quantised to MXFP8 (e4m3 elements, one e8m0
+ *            scale per 32 elements along the contraction axis) in both passes.
+ *   FP8_BWD  bf16 forward, MXFP8 backward. */
+typedef enum {
+  MOE_MODE_FP32 = 0,
+  MOE_MODE_BF16 = 1,
+  MOE_MODE_MXFP8 = 2,
+  MOE_MODE_FP8_BWD = 3
+} moe_mode;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,        /* null pointer, non-positive size, k > E_total, bad share */
+  MOE_ERR_UNSUPPORTED_SHAPE = 2,  /* H % 256, F % 128, E_total > 512, k > 32, T*k >= 2^31 */
+  MOE_ERR_UNSUPPORTED_MODE = 3,   /* mode value unknown or not built into this library */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 4,
+  MOE_ERR_HIP = 5                 /* a HIP runtime call failed; see moe_last_error() */
+} moe_status;
+
+/* Layer description; passed by host pointer to every call. */
+typedef struct {
+  int64_t T;              /* tokens, >= 1 */
+  int32_t H;              /* hidden size, multiple of 256 */
+  int32_t F;              /* expert FFN size, multiple of 128 */
+  int32_t E_total;        /* routed experts, 1..512 */
+  int32_t E_local;        /* experts computed here, >= 1 */
+  int32_t expert_offset;  /* first computed expert; expert_offset + E_local <= E_total */
+  int32_t topk;           /* experts per token, 1..min(E_total, 32) */
+  int32_t mode;           /* moe_mode */
+} moe_desc;
+
+/* Byte sizes of the caller-allocated buffers for the description (host pointers out; any may
+ * be NULL). Each size is a multiple of 256. The base pointers must be 256-byte aligned.
+ *   fwd_ws   workspace for moe_route and moe_fwd (contents need not be preserved)
+ *   bwd_ws   workspace for moe_bwd
+ *   saved    routing metadata and activations written by moe_fwd/moe_route and read by
+ *            moe_bwd; it must stay untouched between the two calls.
+ * Host-only: no device work. */
+moe_status moe_query_sizes(const moe_desc* d, size_t* fwd_ws, size_t* bwd_ws, size_t* saved);
+
+/* Routing only ("A Magia da Fusão": dispatch; "kernel fuso per l'addestramento MoE": routing
+ * is part of the fused operation). Writes the routing half of `saved` (layout below).
+ * moe_fwd does this itself; this entry point exists so that routing can be tested alone. */
+moe_status moe_route(const moe_desc* d, const float* logits, void* saved, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* Forward: routing, dispatch (gathered inside the gate/up GEMM's operand loads), gate/up GEMM
+ * with the SwiGLU epilogue, down GEMM, and the weighted combine into y. y is overwritten.
+ * `saved` receives what moe_bwd needs. */
+moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits,
+                   const void* w_gate, const void* w_up, const void* w_down,
+                   void* y, void* saved, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of <dy, y> with the same x, weights and the `saved` of the matching moe_fwd.
+ * Outputs (all overwritten, never accumulated):
+ *   dx                 [T,H]
+ *   dlogits            [T,E_total] fp32, zero outside each token's chosen experts
+ *   dw_gate, dw_up     [E_local,F,H]
+ *   dw_down            [E_local,H,F]
+ * An expert that received no tokens gets exactly zero weight gradients. */
+moe_status moe_bwd(const moe_desc* d, const void* dy, const void* x,
+                   const void* w_gate, const void* w_up, const void* w_down, const void* saved,
+                   void* dx, float* dlogits, void* dw_gate, void* dw_up, void* dw_down,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* Byte offsets of the routing results inside `saved`.
+ *   idx       int32 [T*k]      chosen experts, slot order (logit desc, index asc)
+ *   weight    float [T*k]      renormalised routing weights
+ *   counts    int32 [E_local]  pairs per local expert
+ *   offsets   int32 [E_local+1] exclusive prefix sum of counts (offsets[E_local] = P)
+ *   perm      int32 [T*k]      first P entries: pair ids t*k+j sorted by (expert, pair id)
+ *   pair_pos  int32 [T*k]      position of pair t*k+j in perm, -1 if its expert is not local
+ * Host-only pointer arithmetic, for tests and tools. */
+typedef struct {
+  size_t idx, weight, counts, offsets, perm, pair_pos;
+} moe_saved_offsets;
+moe_status moe_saved_layout(const moe_desc* d, moe_saved_offsets* out);
+
+/* Static description of a status code. */
+const char* moe_status_string(moe_status s);
+/* Detail of the last error on the calling thread (empty string if none). */
+const char* moe_last_error(void);
+
+/* Kernel timing with HIP events, for measurement tools. While enabled, every kernel the
+ * library launches is bracketed by two events recorded on the launch stream. The library
+ * creates them up front, `max_launches` pairs, and reuses them. Launches beyond that are not
+ * recorded. moe_profile_enable() clears earlier records.
+ * moe_profile_collect() waits for the recorded events and sums each kernel's durations.
+ * Kernel names are returned by index: moe_profile_kernel(i, &name, &launches, &total_ms)
+ * gives MOE_ERR_INVALID_ARG once i runs past the last kernel. */
+moe_status moe_profile_enable(int max_launches);
+moe_status moe_profile_disable(void);
+moe_status moe_profile_collect(void);
+moe_status moe_profile_kernel(int i, const char** name, int* launches, double* total_ms);
+
+/* Version string of the library build. */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

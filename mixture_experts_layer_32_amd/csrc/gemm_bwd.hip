@@ -1,0 +1,339 @@
+// Backward of the fused MoE layer: the pass Prime added to DeepSeek's forward-only kernel
+// ("Afinal, o que é esse Prime Mega MoE?" on "IA: MoE Kernel 3x Mais Rápido Chegou!"; "Qué se ha
+// publicado" on the ai-daily-news.org page).
+//
+// The forward saved, per routed pair r (expert-sorted order), a = x W_gate^T, b = x W_up^T and
+// hw = w_r silu(a) b. With u = W_down[e]^T dY_t:
+//   k_bwd_dh         row-tiled: u = gather(dY) W_down[e] (contraction over H). The epilogue
+//                    recomputes h = silu(a) b and writes
+//                      g partials   <u, h> per 64-column slice
+//                      da           w u b silu'(a)
+//                      db           w u silu(a)
+//   k_wgrad_down     per expert: dW_down[e] = sum_r dY_t hw_r^T. Contraction over the expert's
+//                    rows; both operands are contiguous along M or N and are transposed on
+//                    their way into LDS.
+//   k_wgrad_gateup   per expert: [dW_gate; dW_up][e] = sum_r [da; db]_r x_t^T.
+//   k_dgrad_x        row-tiled: dX_r = [da db]_r [W_gate[e]; W_up[e]] (contraction over 2F).
+//   k_combine_bwd    dx_t = sum over local slots of dX; dlogits through the renormalised
+//                    softmax, with g_tj = sum of the partials = <dY_t, o_tj>.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+// contraction row k of W_down[e] restricted to columns [n0, n0+128): contiguous along F
+template <class T>
+struct WdRows {
+  const T* base;  // wd + e*H*F + n0
+  int F;
+  __device__ __forceinline__ const char* row(int k) const {
+    return reinterpret_cast<const char*>(base + (size_t)k * F);
+  }
+};
+
+// contraction row k of [W_gate[e]; W_up[e]] (2F rows of length H) restricted to [n0, n0+128)
+template <class T>
+struct GateUpRows {
+  const T* g;  // wg + e*F*H + n0
+  const T* u;  // wu + e*F*H + n0
+  int F, H;
+  __device__ __forceinline__ const char* row(int k) const {
+    return reinterpret_cast<const char*>(k < F ? g + (size_t)k * H : u + (size_t)(k - F) * H);
+  }
+};
+
+// contraction row k = expert-local pair index: token row of a [T, ld] tensor, via perm
+template <class T>
+struct GatherRows {
+  const T* base;  // tensor + c0
+  const int* perm;
+  int seg0, seg_end, topk, ld;
+  __device__ __forceinline__ const char* row(int k) const {
+    const int r = seg0 + k;
+    return r < seg_end ? reinterpret_cast<const char*>(base + (size_t)(perm[r] / topk) * ld) : nullptr;
+  }
+};
+
+// contraction row k = expert-local pair index: row seg0+k of a pair-indexed [rows, ld] tensor
+template <class T>
+struct PairRows {
+  const T* base;  // tensor + c0
+  int seg0, seg_end, ld;
+  __device__ __forceinline__ const char* row(int k) const {
+    const int r = seg0 + k;
+    return r < seg_end ? reinterpret_cast<const char*>(base + (size_t)r * ld) : nullptr;
+  }
+};
+
+template <class T>
+__global__ __launch_bounds__(kThreads, 2) void k_bwd_dh(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const T* __restrict__ dy = static_cast<const T*>(p.dy);
+  const T* __restrict__ wd = static_cast<const T*>(p.wd);
+  const T* __restrict__ ab = static_cast<const T*>(p.ab);
+  T* __restrict__ dab = static_cast<T*>(p.dab);
+  const int H = p.H, F = p.F;
+  const int ntn = F / 128;
+  const int total = *p.num_mtiles * ntn;
+  const int nk = H / Elem<T>::BK;
+  const XcdRange xr = xcd_range(total);
+  const int brow[4] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
+  for (int tile = xr.first; tile < xr.end; tile += xr.stride) {
+    const int mt = tile / ntn, nt = tile - mt * ntn;
+    const int2 me = p.mtile[mt];
+    const int e = me.x, r0 = me.y;
+    const int seg_end = p.offsets[e + 1];
+    KLoader<128> la;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = r0 + (tid >> 3) + 32 * i;
+      la.p[i] = r < seg_end ? reinterpret_cast<const char*>(dy + (size_t)(p.perm[r] / p.k) * H) + (tid & 7) * 16
+                            : nullptr;
+    }
+    MNLoader<T, 128, WdRows<T>> lb;
+    lb.src = WdRows<T>{wd + (size_t)e * H * F + nt * 128, F};
+    lb.init(tid);
+    f32x4 acc[4][4];
+    mainloop<T>(acc, smem, la, lb, nk, wm * 64, brow);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = r0 + wm * 64 + i * 16 + 4 * (lane >> 4) + q;
+        const bool valid = r < seg_end;
+        const float w = valid ? p.weight[p.perm[r]] : 0.f;
+        float gsum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int f = nt * 128 + wn * 64 + j * 16 + (lane & 15);
+          if (valid) {
+            const float av = (float)ab[(size_t)r * 2 * F + f];
+            const float bv = (float)ab[(size_t)r * 2 * F + F + f];
+            const float sg = sigmoidf_(av);
+            const float si = av * sg;
+            const float u = acc[i][j][q];
+            gsum += u * (si * bv);
+            const float dh = w * u;
+            dab[(size_t)r * 2 * F + f] = cvt_out<T>(dh * bv * sg * (1.0f + av * (1.0f - sg)));
+            dab[(size_t)r * 2 * F + F + f] = cvt_out<T>(dh * si);
+          }
+        }
+        gsum += __shfl_xor(gsum, 1);
+        gsum += __shfl_xor(gsum, 2);
+        gsum += __shfl_xor(gsum, 4);
+        gsum += __shfl_xor(gsum, 8);
+        if (valid && (lane & 15) == 0) p.gpart[(size_t)(nt * 2 + wn) * p.rows + r] = gsum;
+      }
+    }
+  }
+}
+
+template <class T>
+__global__ __launch_bounds__(kThreads, 2) void k_dgrad_x(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const T* __restrict__ dab = static_cast<const T*>(p.dab);
+  const T* __restrict__ wg = static_cast<const T*>(p.wg);
+  const T* __restrict__ wu = static_cast<const T*>(p.wu);
+  T* __restrict__ dxp = static_cast<T*>(p.dxp);
+  const int H = p.H, F = p.F;
+  const int ntn = H / 128;
+  const int total = *p.num_mtiles * ntn;
+  const int nk = 2 * F / Elem<T>::BK;
+  const XcdRange xr = xcd_range(total);
+  const int brow[4] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
+  for (int tile = xr.first; tile < xr.end; tile += xr.stride) {
+    const int mt = tile / ntn, nt = tile - mt * ntn;
+    const int2 me = p.mtile[mt];
+    const int e = me.x, r0 = me.y;
+    const int seg_end = p.offsets[e + 1];
+    KLoader<128> la;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = r0 + (tid >> 3) + 32 * i;
+      la.p[i] = r < seg_end ? reinterpret_cast<const char*>(dab + (size_t)r * 2 * F) + (tid & 7) * 16 : nullptr;
+    }
+    MNLoader<T, 128, GateUpRows<T>> lb;
+    lb.src = GateUpRows<T>{wg + (size_t)e * F * H + nt * 128, wu + (size_t)e * F * H + nt * 128, F, H};
+    lb.init(tid);
+    f32x4 acc[4][4];
+    mainloop<T>(acc, smem, la, lb, nk, wm * 64, brow);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = r0 + wm * 64 + i * 16 + 4 * (lane >> 4) + q;
+        if (r >= seg_end) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = nt * 128 + wn * 64 + j * 16 + (lane & 15);
+          dxp[(size_t)r * H + n] = cvt_out<T>(acc[i][j][q]);
+        }
+      }
+    }
+  }
+}
+
+// dW_down[e] (H x F) = sum over the expert's pairs r of dY_{t_r} hw_r^T
+template <class T>
+__global__ __launch_bounds__(kThreads, 2) void k_wgrad_down(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int H = p.H, F = p.F;
+  const int ntn = F / 128, tpe = (H / 128) * ntn;
+  const int lid = xcd_logical_block(gridDim.x);
+  const int e = lid / tpe, t = lid - e * tpe;
+  const int mt = t / ntn, nt = t - mt * ntn;
+  const int seg0 = p.offsets[e], seg_end = p.offsets[e + 1];
+  const int nk = (seg_end - seg0 + Elem<T>::BK - 1) / Elem<T>::BK;
+  MNLoader<T, 128, GatherRows<T>> la;
+  la.src = GatherRows<T>{static_cast<const T*>(p.dy) + mt * 128, p.perm, seg0, seg_end, p.k, H};
+  la.init(tid);
+  MNLoader<T, 128, PairRows<T>> lb;
+  lb.src = PairRows<T>{static_cast<const T*>(p.hw) + nt * 128, seg0, seg_end, F};
+  lb.init(tid);
+  const int brow[4] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
+  f32x4 acc[4][4];
+  mainloop<T>(acc, smem, la, lb, nk, wm * 64, brow);
+  T* __restrict__ out = static_cast<T*>(p.dwd) + (size_t)e * H * F;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int m = mt * 128 + wm * 64 + i * 16 + 4 * (lane >> 4) + q;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = nt * 128 + wn * 64 + j * 16 + (lane & 15);
+        out[(size_t)m * F + n] = cvt_out<T>(acc[i][j][q]);
+      }
+    }
+}
+
+// [dW_gate; dW_up][e] (2F x H) = sum over the expert's pairs r of [da; db]_r x_{t_r}^T
+template <class T>
+__global__ __launch_bounds__(kThreads, 2) void k_wgrad_gateup(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int H = p.H, F = p.F;
+  const int ntn = H / 128, tpe = (2 * F / 128) * ntn;
+  const int lid = xcd_logical_block(gridDim.x);
+  const int e = lid / tpe, t = lid - e * tpe;
+  const int mt = t / ntn, nt = t - mt * ntn;
+  const int seg0 = p.offsets[e], seg_end = p.offsets[e + 1];
+  const int nk = (seg_end - seg0 + Elem<T>::BK - 1) / Elem<T>::BK;
+  MNLoader<T, 128, PairRows<T>> la;
+  la.src = PairRows<T>{static_cast<const T*>(p.dab) + mt * 128, seg0, seg_end, 2 * F};
+  la.init(tid);
+  MNLoader<T, 128, GatherRows<T>> lb;
+  lb.src = GatherRows<T>{static_cast<const T*>(p.x) + nt * 128, p.perm, seg0, seg_end, p.k, H};
+  lb.init(tid);
+  const int brow[4] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
+  f32x4 acc[4][4];
+  mainloop<T>(acc, smem, la, lb, nk, wm * 64, brow);
+  const bool gate = mt * 128 < F;
+  T* __restrict__ out = static_cast<T*>(gate ? p.dwg : p.dwu) + (size_t)e * F * H;
+  const int m0 = gate ? mt * 128 : mt * 128 - F;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int m = m0 + wm * 64 + i * 16 + 4 * (lane >> 4) + q;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = nt * 128 + wn * 64 + j * 16 + (lane & 15);
+        out[(size_t)m * H + n] = cvt_out<T>(acc[i][j][q]);
+      }
+    }
+}
+
+template <class T>
+__global__ __launch_bounds__(256) void k_combine_bwd(BwdParams p) {
+  constexpr int VEC = Elem<T>::VEC;
+  __shared__ float gs[kMaxTopk];
+  __shared__ float gbar;
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x, k = p.k, H = p.H;
+  if (tid < k) {
+    const int pp = p.pair_pos[t * k + tid];
+    float g = 0.f;
+    if (pp >= 0)
+      for (int q = 0; q < p.np; ++q) g += p.gpart[(size_t)q * p.rows + pp];
+    gs[tid] = g;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float s = 0.f;
+    for (int j = 0; j < k; ++j) s += p.weight[t * k + j] * gs[j];
+    gbar = s;
+  }
+  __syncthreads();
+  for (int e = tid; e < p.E; e += 256) {
+    float v = 0.f;
+    for (int j = 0; j < k; ++j)
+      if (p.idx[t * k + j] == e) v = p.weight[t * k + j] * (gs[j] - gbar);
+    p.dlogits[t * p.E + e] = v;
+  }
+  const T* __restrict__ src = static_cast<const T*>(p.dxp);
+  T* __restrict__ out = static_cast<T*>(p.dx);
+  const int nch = H / VEC;
+  for (int c = tid; c < nch; c += 256) {
+    float acc[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int pp = p.pair_pos[t * k + j];
+      if (pp < 0) continue;
+      const uint4 raw = ld16(src + (size_t)pp * H + (size_t)c * VEC);
+      const T* ev = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) acc[v] += (float)ev[v];
+    }
+    uint4 res;
+    T* r = reinterpret_cast<T*>(&res);
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) r[v] = cvt_out<T>(acc[v]);
+    st16(out + (size_t)t * H + (size_t)c * VEC, res);
+  }
+}
+
+template <class T>
+hipError_t launch_backward(const BwdParams& p, int grid, hipStream_t s) {
+  hipError_t err;
+  prof_mark_begin("gemm_bwd_dh_dswiglu", s);
+  k_bwd_dh<T><<<grid, kThreads, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+
+  const int nb_wd = p.El * (p.H / 128) * (p.F / 128);
+  prof_mark_begin("gemm_wgrad_down", s);
+  k_wgrad_down<T><<<nb_wd, kThreads, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+
+  const int nb_wgu = p.El * (2 * p.F / 128) * (p.H / 128);
+  prof_mark_begin("gemm_wgrad_gateup", s);
+  k_wgrad_gateup<T><<<nb_wgu, kThreads, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+
+  prof_mark_begin("gemm_dgrad_x", s);
+  k_dgrad_x<T><<<grid, kThreads, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+
+  prof_mark_begin("combine_bwd", s);
+  k_combine_bwd<T><<<(unsigned)p.T, 256, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+  return hipSuccess;
+}
+
+template hipError_t launch_backward<float>(const BwdParams&, int, hipStream_t);
+template hipError_t launch_backward<bf16>(const BwdParams&, int, hipStream_t);
+
+}  // namespace moe

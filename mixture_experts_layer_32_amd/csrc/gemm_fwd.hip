@@ -1,0 +1,176 @@
+// Forward expert computation. "A Magia da Fusão" on "IA: MoE Kernel 3x Mais Rápido Chegou!" lists
+// it: the experts' linear layers with SwiGLU between them, then the combine of the expert outputs.
+// "Detalhes Técnicos Rápidos" on the same page requires gated SwiGLU experts without biases.
+//
+//   k_gateup   persistent grouped GEMM over (M-tile of an expert's rows, 64-column slice of F).
+//              A = x rows gathered through the permutation, so the dispatched copy of x is never
+//              stored. B = the matching 64 rows of W_gate[e] and 64 rows of W_up[e].
+//              Epilogue: a, b (saved for the backward) and hw = w_r * silu(a) * b.
+//   k_down     persistent grouped GEMM: o'[r] = hw[r] W_down[e]^T. The routing weight is
+//              already in hw.
+//   k_combine  y_t = sum over the token's local slots of o'[pair_pos]. Gather-sum, fp32
+//              accumulation, one block per token, 16-byte coalesced row reads.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+template <class T>
+__global__ __launch_bounds__(kThreads, 2) void k_gateup(FwdParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const T* __restrict__ x = static_cast<const T*>(p.x);
+  const T* __restrict__ wg = static_cast<const T*>(p.wg);
+  const T* __restrict__ wu = static_cast<const T*>(p.wu);
+  T* __restrict__ ab = static_cast<T*>(p.ab);
+  T* __restrict__ hw = static_cast<T*>(p.hw);
+  const int H = p.H, F = p.F;
+  const int ntn = F / 64;
+  const int total = *p.num_mtiles * ntn;
+  const int nk = H / Elem<T>::BK;
+  const XcdRange xr = xcd_range(total);
+  const int brow[4] = {wn * 32, wn * 32 + 16, 64 + wn * 32, 64 + wn * 32 + 16};
+  for (int tile = xr.first; tile < xr.end; tile += xr.stride) {
+    const int mt = tile / ntn, nt = tile - mt * ntn;
+    const int2 me = p.mtile[mt];
+    const int e = me.x, r0 = me.y;
+    const int seg_end = p.offsets[e + 1];
+    KLoader<128> la, lb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (tid >> 3) + 32 * i;
+      const int r = r0 + row;
+      la.p[i] = r < seg_end ? reinterpret_cast<const char*>(x + (size_t)(p.perm[r] / p.k) * H) + (tid & 7) * 16
+                            : nullptr;
+      const T* wrow = row < 64 ? wg + ((size_t)e * F + nt * 64 + row) * H
+                               : wu + ((size_t)e * F + nt * 64 + row - 64) * H;
+      lb.p[i] = reinterpret_cast<const char*>(wrow) + (tid & 7) * 16;
+    }
+    f32x4 acc[4][4];
+    mainloop<T>(acc, smem, la, lb, nk, wm * 64, brow);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = r0 + wm * 64 + i * 16 + 4 * (lane >> 4) + q;
+        if (r >= seg_end) continue;
+        const float w = p.weight[p.perm[r]];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int f = nt * 64 + wn * 32 + j * 16 + (lane & 15);
+          const float av = acc[i][j][q], bv = acc[i][j + 2][q];
+          const float h = av * sigmoidf_(av) * bv;
+          ab[(size_t)r * 2 * F + f] = cvt_out<T>(av);
+          ab[(size_t)r * 2 * F + F + f] = cvt_out<T>(bv);
+          hw[(size_t)r * F + f] = cvt_out<T>(w * h);
+        }
+      }
+    }
+  }
+}
+
+template <class T>
+__global__ __launch_bounds__(kThreads, 2) void k_down(FwdParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const T* __restrict__ hw = static_cast<const T*>(p.hw);
+  const T* __restrict__ wd = static_cast<const T*>(p.wd);
+  T* __restrict__ o = static_cast<T*>(p.o);
+  const int H = p.H, F = p.F;
+  const int ntn = H / 128;
+  const int total = *p.num_mtiles * ntn;
+  const int nk = F / Elem<T>::BK;
+  const XcdRange xr = xcd_range(total);
+  const int brow[4] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
+  for (int tile = xr.first; tile < xr.end; tile += xr.stride) {
+    const int mt = tile / ntn, nt = tile - mt * ntn;
+    const int2 me = p.mtile[mt];
+    const int e = me.x, r0 = me.y;
+    const int seg_end = p.offsets[e + 1];
+    KLoader<128> la, lb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (tid >> 3) + 32 * i;
+      const int r = r0 + row;
+      la.p[i] = r < seg_end ? reinterpret_cast<const char*>(hw + (size_t)r * F) + (tid & 7) * 16 : nullptr;
+      lb.p[i] = reinterpret_cast<const char*>(wd + ((size_t)e * H + nt * 128 + row) * F) + (tid & 7) * 16;
+    }
+    f32x4 acc[4][4];
+    mainloop<T>(acc, smem, la, lb, nk, wm * 64, brow);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = r0 + wm * 64 + i * 16 + 4 * (lane >> 4) + q;
+        if (r >= seg_end) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = nt * 128 + wn * 64 + j * 16 + (lane & 15);
+          o[(size_t)r * H + n] = cvt_out<T>(acc[i][j][q]);
+        }
+      }
+    }
+  }
+}
+
+// out[t] = sum over j with pair_pos[t*k+j] >= 0 of src[pair_pos[t*k+j]]; fp32 accumulation in
+// slot order. A token with no local slot gets zeros.
+template <class T>
+__global__ __launch_bounds__(256) void k_combine(const T* __restrict__ src, const int* __restrict__ pair_pos,
+                                                 T* __restrict__ out, int k, int H) {
+  constexpr int VEC = Elem<T>::VEC;
+  const int64_t t = blockIdx.x;
+  const int nch = H / VEC;
+  for (int c = threadIdx.x; c < nch; c += 256) {
+    float acc[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int pp = pair_pos[t * k + j];
+      if (pp < 0) continue;
+      const uint4 raw = ld16(src + (size_t)pp * H + (size_t)c * VEC);
+      const T* e = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) acc[v] += (float)e[v];
+    }
+    uint4 res;
+    T* r = reinterpret_cast<T*>(&res);
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) r[v] = cvt_out<T>(acc[v]);
+    st16(out + (size_t)t * H + (size_t)c * VEC, res);
+  }
+}
+
+template <class T>
+hipError_t launch_forward_gemms(const FwdParams& p, int grid, hipStream_t s) {
+  hipError_t err;
+  prof_mark_begin("gemm_gateup_swiglu", s);
+  k_gateup<T><<<grid, kThreads, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+  prof_mark_begin("gemm_down", s);
+  k_down<T><<<grid, kThreads, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+  return hipSuccess;
+}
+
+template <class T>
+hipError_t launch_combine(const void* src, const int* pair_pos, void* out, int64_t T_, int k, int H,
+                          hipStream_t s) {
+  prof_mark_begin("combine", s);
+  k_combine<T><<<(unsigned)T_, 256, 0, s>>>(static_cast<const T*>(src), pair_pos, static_cast<T*>(out), k, H);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  prof_mark_end(s);
+  return hipSuccess;
+}
+
+template hipError_t launch_forward_gemms<float>(const FwdParams&, int, hipStream_t);
+template hipError_t launch_forward_gemms<bf16>(const FwdParams&, int, hipStream_t);
+template hipError_t launch_combine<float>(const void*, const int*, void*, int64_t, int, int, hipStream_t);
+template hipError_t launch_combine<bf16>(const void*, const int*, void*, int64_t, int, int, hipStream_t);
+
+}  // namespace moe

@@ -1,0 +1,411 @@
+// libmoe C ABI: validation, buffer layout, launch sequencing and kernel timing.
+// Everything a call needs is checked on the host before the first launch; the library never
+// allocates device memory and never synchronises the host inside moe_route/moe_fwd/moe_bwd.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+static thread_local std::string g_last_error;
+
+static moe_status fail(moe_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+Layout make_layout(const moe_desc& d) {
+  Layout L{};
+  L.rows = d.T * (int64_t)d.topk;
+  L.nblk_route = (int)((d.T + kRouteTokens - 1) / kRouteTokens);
+  L.mtile_cap = (int)(L.rows / kBM) + d.E_local + 1;
+  L.np = d.F / 64;
+  L.elem = d.mode == MOE_MODE_FP32 ? 4 : 2;
+  const size_t rows = (size_t)L.rows, El = (size_t)d.E_local;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  L.idx = take(rows * 4);
+  L.weight = take(rows * 4);
+  L.counts = take(El * 4);
+  L.offsets = take((El + 1) * 4);
+  L.perm = take(rows * 4);
+  L.pair_pos = take(rows * 4);
+  L.mtile = take((size_t)L.mtile_cap * 8);
+  L.num_mtiles = take(4);
+  L.ab = take(rows * 2 * d.F * L.elem);
+  L.hw = take(rows * d.F * L.elem);
+  L.saved_total = off;
+
+  off = 0;
+  const size_t cells = (size_t)L.nblk_route * El;
+  L.blk_mask = take(cells * 8);
+  L.blk_count = take(cells * 4);
+  L.blk_prefix = take(cells * 4);
+  L.o = take(rows * d.H * L.elem);
+  L.fwd_total = off;
+
+  off = 0;
+  L.dab = take(rows * 2 * d.F * L.elem);
+  L.gpart = take((size_t)L.np * rows * 4);
+  L.dxp = take(rows * d.H * L.elem);
+  L.bwd_total = off;
+  return L;
+}
+
+static moe_status validate(const moe_desc* d) {
+  if (!d) return fail(MOE_ERR_INVALID_ARG, "desc is null");
+  if (d->T < 1 || d->H < 1 || d->F < 1 || d->E_total < 1 || d->E_local < 1 || d->topk < 1 ||
+      d->expert_offset < 0)
+    return fail(MOE_ERR_INVALID_ARG, "sizes must be positive (expert_offset >= 0)");
+  if (d->topk > d->E_total) return fail(MOE_ERR_INVALID_ARG, "topk exceeds E_total");
+  if ((int64_t)d->expert_offset + d->E_local > d->E_total)
+    return fail(MOE_ERR_INVALID_ARG, "expert_offset + E_local exceeds E_total");
+  if (d->H % 256 != 0) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "H must be a multiple of 256");
+  if (d->F % 128 != 0) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "F must be a multiple of 128");
+  if (d->E_total > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "E_total must be <= 512");
+  if (d->topk > kMaxTopk) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "topk must be <= 32");
+  if (d->T * (int64_t)d->topk >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "T*topk must be < 2^31");
+  if (d->mode != MOE_MODE_FP32 && d->mode != MOE_MODE_BF16) {
+    if (d->mode == MOE_MODE_MXFP8 || d->mode == MOE_MODE_FP8_BWD)
+      return fail(MOE_ERR_UNSUPPORTED_MODE, "MX modes are not built into this library version");
+    return fail(MOE_ERR_UNSUPPORTED_MODE, "unknown mode");
+  }
+  return MOE_OK;
+}
+
+static bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+static moe_status check_ptrs(std::initializer_list<std::pair<const void*, const char*>> ps, size_t a) {
+  for (auto& q : ps) {
+    if (!q.first) return fail(MOE_ERR_INVALID_ARG, std::string(q.second) + " is null");
+    if (!aligned(q.first, a))
+      return fail(MOE_ERR_INVALID_ARG, std::string(q.second) + " is not " + std::to_string(a) + "-byte aligned");
+  }
+  return MOE_OK;
+}
+
+static moe_status hip_fail(hipError_t e, const char* where) {
+  return fail(MOE_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+int persistent_grid(int blocks_per_cu) {
+  static int cached_dev = -1, cached_cus = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (dev != cached_dev) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached_cus = cus;
+    cached_dev = dev;
+  }
+  const int g = (cached_cus * blocks_per_cu) & ~7;
+  return g < 8 ? 8 : g;
+}
+
+// ------------------------------------------------------------------------------------ profiling
+namespace {
+struct Prof {
+  std::mutex mu;
+  bool on = false;
+  int cap = 0, n = 0;
+  std::vector<hipEvent_t> ev;  // 2 per record
+  std::vector<int> rec_kernel;
+  std::vector<std::string> names;
+  std::vector<int> launches;
+  std::vector<double> total_ms;
+};
+Prof& prof() {
+  static Prof p;
+  return p;
+}
+thread_local int t_pending = -1;
+}  // namespace
+
+void prof_mark_begin(const char* name, hipStream_t s) {
+  Prof& P = prof();
+  if (!P.on) return;
+  std::lock_guard<std::mutex> g(P.mu);
+  if (!P.on || P.n >= P.cap) return;
+  int kid = -1;
+  for (size_t i = 0; i < P.names.size(); ++i)
+    if (P.names[i] == name) kid = (int)i;
+  if (kid < 0) {
+    P.names.push_back(name);
+    P.launches.push_back(0);
+    P.total_ms.push_back(0.0);
+    kid = (int)P.names.size() - 1;
+  }
+  if (hipEventRecord(P.ev[2 * P.n], s) == hipSuccess) t_pending = kid;
+}
+
+void prof_mark_end(hipStream_t s) {
+  Prof& P = prof();
+  if (!P.on || t_pending < 0) return;
+  std::lock_guard<std::mutex> g(P.mu);
+  const int kid = t_pending;
+  t_pending = -1;
+  if (P.n >= P.cap) return;
+  if (hipEventRecord(P.ev[2 * P.n + 1], s) != hipSuccess) return;
+  P.rec_kernel[P.n] = kid;
+  P.n++;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_version(void) { return "libmoe 0.1 (gfx950; fp32/bf16; persistent grouped GEMM 128x128x128B)"; }
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case MOE_ERR_UNSUPPORTED_MODE: return "unsupported mode";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_query_sizes(const moe_desc* d, size_t* fwd_ws, size_t* bwd_ws, size_t* saved) {
+  g_last_error.clear();
+  moe_status st = validate(d);
+  if (st != MOE_OK) return st;
+  const Layout L = make_layout(*d);
+  if (fwd_ws) *fwd_ws = L.fwd_total;
+  if (bwd_ws) *bwd_ws = L.bwd_total;
+  if (saved) *saved = L.saved_total;
+  return MOE_OK;
+}
+
+moe_status moe_saved_layout(const moe_desc* d, moe_saved_offsets* out) {
+  g_last_error.clear();
+  moe_status st = validate(d);
+  if (st != MOE_OK) return st;
+  if (!out) return fail(MOE_ERR_INVALID_ARG, "out is null");
+  const Layout L = make_layout(*d);
+  out->idx = L.idx;
+  out->weight = L.weight;
+  out->counts = L.counts;
+  out->offsets = L.offsets;
+  out->perm = L.perm;
+  out->pair_pos = L.pair_pos;
+  return MOE_OK;
+}
+
+static RouteParams route_params(const moe_desc& d, const Layout& L, const float* logits, void* saved, void* ws) {
+  char* sv = static_cast<char*>(saved);
+  char* w = static_cast<char*>(ws);
+  RouteParams p{};
+  p.logits = logits;
+  p.idx = reinterpret_cast<int*>(sv + L.idx);
+  p.weight = reinterpret_cast<float*>(sv + L.weight);
+  p.counts = reinterpret_cast<int*>(sv + L.counts);
+  p.offsets = reinterpret_cast<int*>(sv + L.offsets);
+  p.perm = reinterpret_cast<int*>(sv + L.perm);
+  p.pair_pos = reinterpret_cast<int*>(sv + L.pair_pos);
+  p.mtile = reinterpret_cast<int2*>(sv + L.mtile);
+  p.num_mtiles = reinterpret_cast<int*>(sv + L.num_mtiles);
+  p.blk_mask = reinterpret_cast<unsigned long long*>(w + L.blk_mask);
+  p.blk_count = reinterpret_cast<int*>(w + L.blk_count);
+  p.blk_prefix = reinterpret_cast<int*>(w + L.blk_prefix);
+  p.T = d.T;
+  p.E = d.E_total;
+  p.El = d.E_local;
+  p.e0 = d.expert_offset;
+  p.k = d.topk;
+  p.nblk = L.nblk_route;
+  return p;
+}
+
+moe_status moe_route(const moe_desc* d, const float* logits, void* saved, void* ws, size_t ws_bytes,
+                     void* stream) {
+  g_last_error.clear();
+  moe_status st = validate(d);
+  if (st != MOE_OK) return st;
+  if ((st = check_ptrs({{logits, "logits"}}, 4)) != MOE_OK) return st;
+  if ((st = check_ptrs({{saved, "saved"}, {ws, "ws"}}, 256)) != MOE_OK) return st;
+  const Layout L = make_layout(*d);
+  if (ws_bytes < L.fwd_total) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "forward workspace too small");
+  hipError_t e = launch_route(route_params(*d, L, logits, saved, ws), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "route launch");
+  return MOE_OK;
+}
+
+moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits, const void* w_gate, const void* w_up,
+                   const void* w_down, void* y, void* saved, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  moe_status st = validate(d);
+  if (st != MOE_OK) return st;
+  if ((st = check_ptrs({{x, "x"}, {w_gate, "w_gate"}, {w_up, "w_up"}, {w_down, "w_down"}, {y, "y"}}, 16)) != MOE_OK)
+    return st;
+  if ((st = check_ptrs({{logits, "logits"}}, 4)) != MOE_OK) return st;
+  if ((st = check_ptrs({{saved, "saved"}, {ws, "ws"}}, 256)) != MOE_OK) return st;
+  const Layout L = make_layout(*d);
+  if (ws_bytes < L.fwd_total) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "forward workspace too small");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const RouteParams rp = route_params(*d, L, logits, saved, ws);
+  hipError_t e = launch_route(rp, s);
+  if (e != hipSuccess) return hip_fail(e, "route launch");
+  char* sv = static_cast<char*>(saved);
+  FwdParams fp{};
+  fp.x = x;
+  fp.wg = w_gate;
+  fp.wu = w_up;
+  fp.wd = w_down;
+  fp.perm = rp.perm;
+  fp.offsets = rp.offsets;
+  fp.mtile = rp.mtile;
+  fp.num_mtiles = rp.num_mtiles;
+  fp.weight = rp.weight;
+  fp.ab = sv + L.ab;
+  fp.hw = sv + L.hw;
+  fp.o = static_cast<char*>(ws) + L.o;
+  fp.pair_pos = rp.pair_pos;
+  fp.y = y;
+  fp.T = d->T;
+  fp.H = d->H;
+  fp.F = d->F;
+  fp.k = d->topk;
+  fp.El = d->E_local;
+  const int grid = persistent_grid(2);
+  if (d->mode == MOE_MODE_FP32) {
+    if ((e = launch_forward_gemms<float>(fp, grid, s)) != hipSuccess) return hip_fail(e, "forward GEMM launch");
+    if ((e = launch_combine<float>(fp.o, fp.pair_pos, y, d->T, d->topk, d->H, s)) != hipSuccess)
+      return hip_fail(e, "combine launch");
+  } else {
+    if ((e = launch_forward_gemms<bf16>(fp, grid, s)) != hipSuccess) return hip_fail(e, "forward GEMM launch");
+    if ((e = launch_combine<bf16>(fp.o, fp.pair_pos, y, d->T, d->topk, d->H, s)) != hipSuccess)
+      return hip_fail(e, "combine launch");
+  }
+  return MOE_OK;
+}
+
+moe_status moe_bwd(const moe_desc* d, const void* dy, const void* x, const void* w_gate, const void* w_up,
+                   const void* w_down, const void* saved, void* dx, float* dlogits, void* dw_gate, void* dw_up,
+                   void* dw_down, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  moe_status st = validate(d);
+  if (st != MOE_OK) return st;
+  if ((st = check_ptrs({{dy, "dy"}, {x, "x"}, {w_gate, "w_gate"}, {w_up, "w_up"}, {w_down, "w_down"}, {dx, "dx"},
+                        {dw_gate, "dw_gate"}, {dw_up, "dw_up"}, {dw_down, "dw_down"}},
+                       16)) != MOE_OK)
+    return st;
+  if ((st = check_ptrs({{dlogits, "dlogits"}}, 4)) != MOE_OK) return st;
+  if ((st = check_ptrs({{saved, "saved"}, {ws, "ws"}}, 256)) != MOE_OK) return st;
+  const Layout L = make_layout(*d);
+  if (ws_bytes < L.bwd_total) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "backward workspace too small");
+  const char* sv = static_cast<const char*>(saved);
+  char* w = static_cast<char*>(ws);
+  BwdParams p{};
+  p.dy = dy;
+  p.x = x;
+  p.wg = w_gate;
+  p.wu = w_up;
+  p.wd = w_down;
+  p.idx = reinterpret_cast<const int*>(sv + L.idx);
+  p.weight = reinterpret_cast<const float*>(sv + L.weight);
+  p.perm = reinterpret_cast<const int*>(sv + L.perm);
+  p.offsets = reinterpret_cast<const int*>(sv + L.offsets);
+  p.pair_pos = reinterpret_cast<const int*>(sv + L.pair_pos);
+  p.mtile = reinterpret_cast<const int2*>(sv + L.mtile);
+  p.num_mtiles = reinterpret_cast<const int*>(sv + L.num_mtiles);
+  p.ab = sv + L.ab;
+  p.hw = sv + L.hw;
+  p.dab = w + L.dab;
+  p.gpart = reinterpret_cast<float*>(w + L.gpart);
+  p.dxp = w + L.dxp;
+  p.dx = dx;
+  p.dlogits = dlogits;
+  p.dwg = dw_gate;
+  p.dwu = dw_up;
+  p.dwd = dw_down;
+  p.T = d->T;
+  p.rows = L.rows;
+  p.H = d->H;
+  p.F = d->F;
+  p.k = d->topk;
+  p.E = d->E_total;
+  p.El = d->E_local;
+  p.np = L.np;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int grid = persistent_grid(2);
+  hipError_t e = d->mode == MOE_MODE_FP32 ? launch_backward<float>(p, grid, s) : launch_backward<bf16>(p, grid, s);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return MOE_OK;
+}
+
+moe_status moe_profile_enable(int max_launches) {
+  g_last_error.clear();
+  if (max_launches < 1) return fail(MOE_ERR_INVALID_ARG, "max_launches must be >= 1");
+  Prof& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  while ((int)P.ev.size() < 2 * max_launches) {
+    hipEvent_t ev;
+    hipError_t e = hipEventCreate(&ev);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+    P.ev.push_back(ev);
+  }
+  P.cap = max_launches;
+  P.rec_kernel.assign(max_launches, -1);
+  P.n = 0;
+  P.names.clear();
+  P.launches.clear();
+  P.total_ms.clear();
+  P.on = true;
+  return MOE_OK;
+}
+
+moe_status moe_profile_disable(void) {
+  Prof& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  P.on = false;
+  return MOE_OK;
+}
+
+moe_status moe_profile_collect(void) {
+  g_last_error.clear();
+  Prof& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  for (int i = 0; i < P.n; ++i) {
+    hipError_t e = hipEventSynchronize(P.ev[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, P.ev[2 * i], P.ev[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    const int kid = P.rec_kernel[i];
+    P.launches[kid] += 1;
+    P.total_ms[kid] += ms;
+  }
+  P.n = 0;
+  return MOE_OK;
+}
+
+moe_status moe_profile_kernel(int i, const char** name, int* launches, double* total_ms) {
+  Prof& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  if (i < 0 || i >= (int)P.names.size()) return MOE_ERR_INVALID_ARG;
+  if (name) *name = P.names[i].c_str();
+  if (launches) *launches = P.launches[i];
+  if (total_ms) *total_ms = P.total_ms[i];
+  return MOE_OK;
+}
+
+}  // extern "C"

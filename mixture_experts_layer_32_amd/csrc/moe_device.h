@@ -1,0 +1,239 @@
+// Device building blocks shared by the MoE kernels (gfx950 / CDNA4): element traits, the LDS
+// tile layout, MFMA micro-steps, global->LDS operand loaders and the double-buffered main loop.
+//
+// GEMM data movement is counted in 16-byte chunks. One K-tile of an operand occupies one
+// 128-byte LDS row per M (or N) index: 64 bf16 or 32 fp32 contraction elements, 8 chunks.
+// Chunk c of row r is stored at slot c ^ ((r ^ (r >> 3)) & 7), so that
+//   * the MFMA fragment reads (16 rows, same chunk) hit 8 distinct 16-byte slots per 8 lanes;
+//   * the transposing stores of contraction-axis-contiguous operands (rows 8 apart, same
+//     chunk) hit distinct slots too.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;   // 4 wavefronts of 64
+constexpr int kRowBytes = 128;  // one K-tile row in LDS
+
+template <class T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int VEC = 4;    // elements per 16-byte chunk
+  static constexpr int BK = 32;    // contraction elements per K-tile
+};
+template <> struct Elem<bf16> {
+  static constexpr int VEC = 8;
+  static constexpr int BK = 64;
+};
+
+__device__ __forceinline__ int lds_slot(int row, int c) { return c ^ ((row ^ (row >> 3)) & 7); }
+__device__ __forceinline__ int lds_off(int row, int c) { return row * kRowBytes + (lds_slot(row, c) << 4); }
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// ---------------------------------------------------------------------------------------------
+// MFMA micro-step on one 16x16 output block. Lane l supplies row (l & 15) of A and column
+// (l & 15) of B, and the 16-byte chunk (l >> 4) of the current 4-chunk contraction step. The
+// same lane-to-k assignment is used for both operands, so the k order inside a step does not
+// change the sum. Accumulator element q of lane l is C[4*(l >> 4) + q][l & 15].
+template <class T> __device__ __forceinline__ void mma16(f32x4& acc, const uint4& a, const uint4& b);
+
+template <> __device__ __forceinline__ void mma16<bf16>(f32x4& acc, const uint4& a, const uint4& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+
+// fp32: a chunk is 4 contraction elements; four 16x16x4 MFMAs consume one each.
+template <> __device__ __forceinline__ void mma16<float>(f32x4& acc, const uint4& a, const uint4& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+}
+
+// One wave's 64x64 sub-tile over one K-tile: A rows arow0 + 16*i, B rows brow[j].
+template <class T>
+__device__ __forceinline__ void wave_mma(f32x4 (&acc)[4][4], const char* ldsA, const char* ldsB,
+                                         int arow0, const int (&brow)[4], int lane) {
+  const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    uint4 fa[4], fb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = ld16(ldsA + lds_off(arow0 + 16 * i + lr, 4 * s + lg));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = ld16(ldsB + lds_off(brow[j] + lr, 4 * s + lg));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mma16<T>(acc[i][j], fa[i], fb[j]);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Operand loaders. Each moves one K-tile (128 bytes of contraction per row) of a ROWS-row operand
+// tile from global memory into registers (fetch), then into the LDS layout above (store).
+
+// K-major operand: row i is contiguous along K. This thread moves chunk (tid & 7) of rows
+// (tid >> 3) + 32*i. p[i] points at that chunk of K-tile 0, or is null for a zero row.
+template <int ROWS>
+struct KLoader {
+  static constexpr int N = ROWS / 32;
+  const char* p[N];
+  uint4 r[N];
+  __device__ __forceinline__ void fetch(int kt) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      r[i] = p[i] ? ld16(p[i] + (size_t)kt * kRowBytes) : make_uint4(0, 0, 0, 0);
+  }
+  __device__ __forceinline__ void store(char* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) st16(lds + lds_off((tid >> 3) + 32 * i, tid & 7), r[i]);
+  }
+};
+
+// MN-major operand: each contraction index k owns a contiguous row of ROWS elements (the tile's
+// M or N extent). A micro-block is 4 consecutive k by one 16-byte chunk of the row. It is loaded
+// as 4 chunks, transposed in registers, and stored as VEC LDS rows of 4 contraction elements.
+// Src::row(k) returns the byte address of element 0 of contraction row k of this tile, or null
+// when k is out of range (that row reads as zero).
+template <class T, int ROWS, class Src>
+struct MNLoader {
+  static constexpr int VEC = Elem<T>::VEC;
+  static constexpr int BK = Elem<T>::BK;
+  static constexpr int NCOL = ROWS / VEC;      // 16-byte chunks per contraction row
+  static constexpr int NMB = 2 * ROWS / kThreads;  // micro-blocks per thread ((BK/4)*NCOL == 2*ROWS)
+  Src src;
+  int kq[NMB], mc[NMB];
+  uint4 r[NMB][4];
+  __device__ __forceinline__ void init(int tid) {
+#pragma unroll
+    for (int i = 0; i < NMB; ++i) {
+      const int mb = tid + kThreads * i;
+      kq[i] = mb / NCOL;
+      mc[i] = mb % NCOL;
+    }
+  }
+  __device__ __forceinline__ void fetch(int kt) {
+#pragma unroll
+    for (int i = 0; i < NMB; ++i)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const char* p = src.row(kt * BK + 4 * kq[i] + kk);
+        r[i][kk] = p ? ld16(p + 16 * mc[i]) : make_uint4(0, 0, 0, 0);
+      }
+  }
+  __device__ __forceinline__ void store(char* lds, int) const;
+};
+
+template <class T, int ROWS, class Src>
+__device__ __forceinline__ void MNLoader<T, ROWS, Src>::store(char* lds, int) const {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < NMB; ++i) {
+      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[i][0]);
+      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[i][1]);
+      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[i][2]);
+      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[i][3]);
+      const int c = kq[i] >> 1, half = (kq[i] & 1) * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int sh = (j & 1) * 16;
+        const uint32_t e0 = (w0[j >> 1] >> sh) & 0xFFFFu, e1 = (w1[j >> 1] >> sh) & 0xFFFFu;
+        const uint32_t e2 = (w2[j >> 1] >> sh) & 0xFFFFu, e3 = (w3[j >> 1] >> sh) & 0xFFFFu;
+        const int row = mc[i] * 8 + j;
+        uint2 v = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+        *reinterpret_cast<uint2*>(lds + lds_off(row, c) + half) = v;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NMB; ++i) {
+      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[i][0]);
+      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[i][1]);
+      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[i][2]);
+      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[i][3]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = mc[i] * 4 + j;
+        st16(lds + lds_off(row, kq[i]), make_uint4(w0[j], w1[j], w2[j], w3[j]));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Double-buffered main loop over nk K-tiles for a 128x128 block tile computed by 4 waves, each
+// a 64x64 sub-tile (A rows arow0.., B rows brow[]). smem holds 2 x (A 16 KB + B 16 KB).
+// Global loads for K-tile kt+1 are in flight while the MFMAs of K-tile kt run.
+constexpr int kTileBytes = 128 * kRowBytes;     // 16 KB per operand per buffer
+constexpr int kSmemBytes = 4 * kTileBytes;      // 64 KB
+
+template <class T, class LA, class LB>
+__device__ __forceinline__ void mainloop(f32x4 (&acc)[4][4], char* smem, LA& la, LB& lb, int nk,
+                                         int arow0, const int (&brow)[4]) {
+  const int tid = threadIdx.x, lane = tid & 63;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (nk <= 0) return;
+  la.fetch(0);
+  lb.fetch(0);
+  la.store(smem, tid);
+  lb.store(smem + kTileBytes, tid);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    char* cur = smem + (kt & 1) * 2 * kTileBytes;
+    char* nxt = smem + ((kt + 1) & 1) * 2 * kTileBytes;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      la.fetch(kt + 1);
+      lb.fetch(kt + 1);
+    }
+    wave_mma<T>(acc, cur, cur + kTileBytes, arow0, brow, lane);
+    if (more) {
+      la.store(nxt, tid);
+      lb.store(nxt + kTileBytes, tid);
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Work distribution. Workgroups are dispatched to the 8 XCDs round-robin by workgroup id, and
+// each XCD has its own L2. Persistent kernels therefore give each XCD one contiguous range of
+// the tile list (tiles of the same expert share operands). The grid must be a multiple of 8.
+struct XcdRange {
+  int begin, end, stride, first;
+};
+__device__ __forceinline__ XcdRange xcd_range(int total) {
+  const int per_xcd_blocks = gridDim.x >> 3;
+  const int xcd = blockIdx.x & 7;
+  const int per = (total + 7) >> 3;
+  XcdRange r;
+  r.begin = xcd * per;
+  r.end = min(total, r.begin + per);
+  r.stride = per_xcd_blocks;
+  r.first = r.begin + (blockIdx.x >> 3);
+  return r;
+}
+
+// Non-persistent grids: logical block id such that consecutive logical ids share an XCD.
+__device__ __forceinline__ int xcd_logical_block(int nblocks) {
+  const int b = blockIdx.x;
+  const int q = nblocks >> 3, rem = nblocks & 7, x = b & 7;
+  const int base = x < rem ? x * (q + 1) : rem * (q + 1) + (x - rem) * q;
+  return base + (b >> 3);
+}
+
+template <class T> __device__ __forceinline__ T cvt_out(float v) { return (T)v; }
+
+__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+}  // namespace moe

@@ -1,0 +1,108 @@
+// Host-side internals of libmoe: buffer layout and kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kBM = 128;            // rows per M-tile of the row-tiled grouped GEMMs
+constexpr int kRouteTokens = 64;    // tokens per routing block (one 64-bit mask word per expert)
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopk = 32;
+
+// Byte offsets of every region inside the three caller-provided buffers.
+struct Layout {
+  int64_t rows;        // T*k: upper bound on routed pairs
+  int nblk_route;      // ceil(T / kRouteTokens)
+  int mtile_cap;       // upper bound on M-tiles: rows / kBM + E_local + 1
+  int np;              // partial sums of g per pair (F / 64)
+  size_t elem;         // bytes per stored element (4 or 2)
+  // saved
+  size_t idx, weight, counts, offsets, perm, pair_pos, mtile, num_mtiles, ab, hw, saved_total;
+  // forward workspace
+  size_t blk_mask, blk_count, blk_prefix, o, fwd_total;
+  // backward workspace
+  size_t dab, gpart, dxp, bwd_total;
+};
+
+Layout make_layout(const moe_desc& d);
+
+// Launch helper: optional event timing, error capture.
+void prof_mark_begin(const char* name, hipStream_t s);
+void prof_mark_end(hipStream_t s);
+
+struct RouteParams {
+  const float* logits;
+  int* idx;
+  float* weight;
+  int* counts;
+  int* offsets;
+  int* perm;
+  int* pair_pos;
+  int2* mtile;
+  int* num_mtiles;
+  unsigned long long* blk_mask;
+  int* blk_count;
+  int* blk_prefix;
+  int64_t T;
+  int E, El, e0, k, nblk;
+};
+hipError_t launch_route(const RouteParams& p, hipStream_t s);
+
+// Row-tiled grouped GEMMs and wgrad GEMMs; T = float or bf16.
+struct FwdParams {
+  const void* x;
+  const void* wg;
+  const void* wu;
+  const void* wd;
+  const int* perm;
+  const int* offsets;
+  const int2* mtile;
+  const int* num_mtiles;
+  const float* weight;
+  void* ab;
+  void* hw;
+  void* o;
+  const int* pair_pos;
+  void* y;
+  int64_t T;
+  int H, F, k, El;
+};
+template <class T> hipError_t launch_forward_gemms(const FwdParams& p, int grid, hipStream_t s);
+template <class T> hipError_t launch_combine(const void* src, const int* pair_pos, void* out, int64_t ntok,
+                                             int k, int H, hipStream_t s);
+
+struct BwdParams {
+  const void* dy;
+  const void* x;
+  const void* wg;
+  const void* wu;
+  const void* wd;
+  const int* idx;
+  const float* weight;
+  const int* perm;
+  const int* offsets;
+  const int* pair_pos;
+  const int2* mtile;
+  const int* num_mtiles;
+  const void* ab;
+  const void* hw;
+  void* dab;
+  float* gpart;
+  void* dxp;
+  void* dx;
+  float* dlogits;
+  void* dwg;
+  void* dwu;
+  void* dwd;
+  int64_t T, rows;
+  int H, F, k, E, El, np;
+};
+template <class T> hipError_t launch_backward(const BwdParams& p, int grid, hipStream_t s);
+
+int persistent_grid(int blocks_per_cu);
+
+}  // namespace moe

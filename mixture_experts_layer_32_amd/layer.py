@@ -1,0 +1,67 @@
+"""Device-memory plumbing around the C ABI: torch allocates the caller-owned buffers.
+
+MoELayer holds the workspace and saved buffers for one layer shape, and calls moe_fwd/moe_bwd
+through the binding. No arithmetic happens here.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import binding
+
+
+class MoELayer:
+    def __init__(self, T, H, F, E_total, topk, mode="bf16", E_local=None, expert_offset=0, device="cuda"):
+        self.desc = binding.Desc.make(T, H, F, E_total, topk, mode, E_local, expert_offset)
+        self.mode = mode
+        self.dtype = torch.float32 if mode == "fp32" else torch.bfloat16
+        self.device = torch.device(device)
+        self.fwd_ws_bytes, self.bwd_ws_bytes, self.saved_bytes = binding.query_sizes(self.desc)
+        u8 = dict(dtype=torch.uint8, device=self.device)
+        self.ws = torch.empty(max(self.fwd_ws_bytes, self.bwd_ws_bytes), **u8)
+        self.saved = torch.empty(self.saved_bytes, **u8)
+
+    @property
+    def shape(self):
+        d = self.desc
+        return dict(T=d.T, H=d.H, F=d.F, E=d.E_total, E_local=d.E_local, e0=d.expert_offset, k=d.topk)
+
+    def forward(self, x, logits, w_gate, w_up, w_down, y=None, stream=None):
+        d = self.desc
+        if y is None:
+            y = torch.empty(d.T, d.H, dtype=self.dtype, device=self.device)
+        binding.moe_fwd(d, x, logits, w_gate, w_up, w_down, y, self.saved, self.ws, self.ws.numel(), stream)
+        return y
+
+    def route(self, logits, stream=None):
+        binding.moe_route(self.desc, logits, self.saved, self.ws, self.ws.numel(), stream)
+
+    def backward(self, dy, x, w_gate, w_up, w_down, out=None, stream=None):
+        d = self.desc
+        if out is None:
+            kw = dict(dtype=self.dtype, device=self.device)
+            out = dict(dx=torch.empty(d.T, d.H, **kw),
+                       dlogits=torch.empty(d.T, d.E_total, dtype=torch.float32, device=self.device),
+                       dw_gate=torch.empty(d.E_local, d.F, d.H, **kw),
+                       dw_up=torch.empty(d.E_local, d.F, d.H, **kw),
+                       dw_down=torch.empty(d.E_local, d.H, d.F, **kw))
+        binding.moe_bwd(d, dy, x, w_gate, w_up, w_down, self.saved, out["dx"], out["dlogits"], out["dw_gate"],
+                        out["dw_up"], out["dw_down"], self.ws, self.ws.numel(), stream)
+        return out
+
+    def routing(self):
+        """Routing results from `saved` as CPU tensors: idx, weight, counts, offsets, perm, pair_pos."""
+        d = self.desc
+        off = binding.saved_layout(d)
+        rows = d.T * d.topk
+        s = self.saved
+
+        def view(name, n, dt):
+            b = 4 * n
+            return s[off[name]:off[name] + b].view(dt).cpu()
+        offsets = view("offsets", d.E_local + 1, torch.int32)
+        P = int(offsets[-1])
+        return dict(idx=view("idx", rows, torch.int32).view(d.T, d.topk),
+                    weight=view("weight", rows, torch.float32).view(d.T, d.topk),
+                    counts=view("counts", d.E_local, torch.int32), offsets=offsets,
+                    perm=view("perm", rows, torch.int32)[:P], pair_pos=view("pair_pos", rows, torch.int32))

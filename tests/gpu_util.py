@@ -1,0 +1,40 @@
+"""Helpers for the GPU parity tests: run the HIP layer through the C ABI on seeded inputs."""
+import numpy as np
+import torch
+
+from mixture_experts_layer_32_amd.layer import MoELayer
+
+TOL = {"fp32": 1e-5, "bf16": 1e-2}
+OUTS = ("y", "dx", "dlogits", "dwg", "dwu", "dwd")
+
+
+def to_dev(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dtype)
+
+
+def run_layer(cfg, L, mode=None, poison=False, keep_layer=False):
+    """Forward + backward on the GPU. Returns float64 numpy outputs and the routing results."""
+    mode = mode or cfg.dtype
+    dt = torch.float32 if mode == "fp32" else torch.bfloat16
+    layer = MoELayer(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, mode, cfg.el, cfg.e0)
+    if poison:                              # NaN bit patterns in every scratch byte
+        layer.ws.fill_(0xFF)
+        layer.saved.fill_(0xFF)
+    x, dy = to_dev(L["x"], dt), to_dev(L["dy"], dt)
+    lg = to_dev(L["logits"], torch.float32)
+    wg, wu, wd = to_dev(L["wg"], dt), to_dev(L["wu"], dt), to_dev(L["wd"], dt)
+    y = layer.forward(x, lg, wg, wu, wd)
+    g = layer.backward(dy, x, wg, wu, wd)
+    torch.cuda.synchronize()
+    out = dict(y=y, dx=g["dx"], dlogits=g["dlogits"], dwg=g["dw_gate"], dwu=g["dw_up"], dwd=g["dw_down"])
+    res = {n: t.float().cpu().numpy().astype(np.float64) for n, t in out.items()}
+    res["routing"] = {n: t.numpy() for n, t in layer.routing().items()}
+    if keep_layer:
+        res["_layer"] = layer
+    return res
+
+
+def raw_bits(cfg, L, mode=None, poison=False):
+    """Output tensors as raw bytes (for bitwise comparisons)."""
+    r = run_layer(cfg, L, mode, poison)
+    return {n: r[n].tobytes() for n in OUTS}

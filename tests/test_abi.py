@@ -1,0 +1,87 @@
+"""C ABI checks that need no GPU: exports, validation errors, buffer sizing (no compute calls).
+
+Every error below is returned by host-side validation before anything is enqueued. The fake
+device addresses passed here are never dereferenced.
+"""
+import ctypes
+
+import pytest
+
+from mixture_experts_layer_32_amd import binding as b
+
+FAKE = 1 << 20          # a 256-byte-aligned non-null address, never touched on the host
+
+
+def desc(**kw):
+    base = dict(T=256, H=256, F=128, E_total=8, topk=2, mode="bf16")
+    base.update(kw)
+    return b.Desc.make(**base)
+
+
+def test_library_exports_every_declared_function():
+    L = b.lib()
+    names = b.header_functions()
+    assert {"moe_fwd", "moe_bwd", "moe_route", "moe_query_sizes", "moe_saved_layout"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert "gfx950" in b.version()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=0), "MOE_ERR_INVALID_ARG"),
+    (dict(topk=9), "MOE_ERR_INVALID_ARG"),
+    (dict(topk=0), "MOE_ERR_INVALID_ARG"),
+    (dict(E_local=4, expert_offset=5), "MOE_ERR_INVALID_ARG"),
+    (dict(H=384), "MOE_ERR_UNSUPPORTED_SHAPE"),
+    (dict(F=192), "MOE_ERR_UNSUPPORTED_SHAPE"),
+    (dict(E_total=513, topk=2), "MOE_ERR_UNSUPPORTED_SHAPE"),
+    (dict(E_total=64, topk=33), "MOE_ERR_UNSUPPORTED_SHAPE"),
+    (dict(T=1 << 28, topk=8), "MOE_ERR_UNSUPPORTED_SHAPE"),
+    (dict(mode=7), "MOE_ERR_UNSUPPORTED_MODE"),
+    (dict(mode="mxfp8"), "MOE_ERR_UNSUPPORTED_MODE"),
+    (dict(mode="fp8_bwd"), "MOE_ERR_UNSUPPORTED_MODE"),
+])
+def test_validation_errors(kw, code):
+    with pytest.raises(b.MoEError) as ei:
+        b.query_sizes(desc(**kw))
+    assert ei.value.code == code
+    assert b.lib().moe_last_error().decode()
+
+
+def test_fwd_bwd_reject_bad_pointers_and_small_workspace_without_launching():
+    d = desc()
+    fwd, bwd, saved = b.query_sizes(d)
+    with pytest.raises(b.MoEError, match="MOE_ERR_INVALID_ARG"):
+        b.moe_fwd(d, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, fwd, stream=0)
+    with pytest.raises(b.MoEError, match="not 16-byte aligned"):
+        b.moe_fwd(d, FAKE + 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, fwd, stream=0)
+    with pytest.raises(b.MoEError, match="MOE_ERR_WORKSPACE_TOO_SMALL"):
+        b.moe_fwd(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, fwd - 1, stream=0)
+    with pytest.raises(b.MoEError, match="MOE_ERR_WORKSPACE_TOO_SMALL"):
+        b.moe_bwd(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, bwd - 256, stream=0)
+    with pytest.raises(b.MoEError, match="dlogits is null"):
+        b.moe_bwd(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, bwd, stream=0)
+    with pytest.raises(b.MoEError, match="saved is not 256-byte aligned"):
+        b.moe_route(d, FAKE, FAKE + 16, FAKE, fwd, stream=0)
+
+
+def test_sizes_cover_the_layout():
+    d = desc(T=1000, H=512, F=256, E_total=16, topk=4)
+    fwd, bwd, saved = b.query_sizes(d)
+    rows = 1000 * 4
+    assert all(v % 256 == 0 for v in (fwd, bwd, saved))
+    assert saved >= rows * (4 * 4) + rows * 3 * 256 * 2           # routing + a, b, hw (bf16)
+    assert fwd >= rows * 512 * 2                                  # per-pair expert outputs
+    assert bwd >= rows * 512 * 2 + rows * 2 * 256 * 2 + rows * 4 * (256 // 64)
+    off = b.saved_layout(d)
+    assert off["idx"] == 0 and off["weight"] >= rows * 4
+    assert off["pair_pos"] + rows * 4 <= saved
+    f32 = b.query_sizes(desc(T=1000, H=512, F=256, E_total=16, topk=4, mode="fp32"))
+    assert f32[2] > saved                                        # fp32 activations are wider
+
+
+def test_status_strings():
+    L = b.lib()
+    for code in range(6):
+        assert L.moe_status_string(code)
+    assert L.moe_profile_kernel(10 ** 6, None, None, None) != 0

@@ -1,0 +1,144 @@
+"""GPU parity: the HIP layer (through the C ABI) against the float64 oracle on the same seeded inputs.
+
+Bar:
+ * Routing (indices, counts, offsets, permutation, inverse): bit-exact.
+ * Routing weights: within 1e-6 absolute.
+ * y, dx, dlogits, dW_gate, dW_up, dW_down: relative Frobenius error within 1e-2 for bf16 and
+   1e-5 for fp32.
+ * Experts that receive no tokens: weight gradients exactly zero.
+Full-size workloads are checked on sampled tokens (y, dx, dlogits rows) and sampled experts
+(dW). The oracle recomputes those from the token's or the expert's own pairs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_layer_32_amd import inputs
+from gpu_util import OUTS, TOL, run_layer
+
+pytestmark = pytest.mark.gpu
+
+
+def check_routing(cfg, L, rt):
+    r = oracle.route(L["logits"], cfg.k, cfg.e0, cfg.el)
+    assert np.array_equal(rt["idx"], r["idx"]), "expert indices differ"
+    assert np.array_equal(rt["counts"], r["counts"]), "expert counts differ"
+    assert np.array_equal(rt["offsets"], r["offsets"]), "expert offsets differ"
+    assert np.array_equal(rt["perm"], r["perm"]), "permutation differs"
+    assert np.array_equal(rt["pair_pos"], r["pair_pos"]), "inverse permutation differs"
+    assert np.max(np.abs(rt["weight"] - r["w"])) <= 1e-6
+    return r
+
+
+def oracle_full(cfg, L):
+    args = dict(x=L["x"], logits=L["logits"], wg=L["wg"], wu=L["wu"], wd=L["wd"], k=cfg.k, e0=cfg.e0,
+                e_local=cfg.el)
+    y, _ = oracle.forward(**args)
+    g, _ = oracle.backward(dy=L["dy"], **args)
+    return dict(y=y, dx=g["dx"], dlogits=g["dlogits"], dwg=g["dwg"], dwu=g["dwu"], dwd=g["dwd"])
+
+
+def custom(name, mode="bf16", **kw):
+    cfg, L = inputs.custom_layer(dtype=mode, **kw)
+    return pytest.param(cfg.with_(name=name), L, mode, id=name)
+
+
+SMALL = [
+    pytest.param(inputs.CONFIGS["tiny"], None, "fp32", id="tiny_fp32"),
+    pytest.param(inputs.CONFIGS["tiny"].with_(dtype="bf16"), None, "bf16", id="tiny_bf16"),
+    custom("ragged_T333", T=333, H=512, F=256, E=16, k=4, seed=11),
+    custom("ragged_fp32", mode="fp32", T=397, H=256, F=384, E=8, k=3, seed=12),
+    custom("k1", T=200, H=256, F=128, E=4, k=1, seed=13),
+    custom("k_equals_E", T=96, H=256, F=128, E=4, k=4, seed=14),
+    custom("single_token", T=1, H=256, F=128, E=8, k=2, seed=15),
+    custom("zipf_empty_experts", T=300, H=256, F=256, E=32, k=2, zipf_s=3.0, seed=16),
+    custom("expert_share", T=400, H=256, F=128, E=16, k=4, E_local=5, e0=3, seed=17),
+    custom("expert_share_fp32", mode="fp32", T=250, H=256, F=128, E=12, k=3, E_local=4, e0=8, seed=18),
+    custom("many_experts_k32", T=130, H=256, F=128, E=512, k=32, seed=19),
+    custom("wide_H4096_F1536", T=130, H=4096, F=1536, E=4, k=2, seed=20),
+]
+
+
+@pytest.mark.parametrize("cfg,L,mode", SMALL)
+def test_small_layer_parity(cfg, L, mode):
+    if L is None:
+        L = inputs.make_layer(cfg)
+    print(f"case {cfg.name} mode={mode} T={cfg.T} H={cfg.H} F={cfg.F} E={cfg.E} k={cfg.k}", flush=True)
+    got = run_layer(cfg, L, mode)
+    r = check_routing(cfg, L, got["routing"])
+    ref = oracle_full(cfg, L)
+    errs = {n: oracle.rel_frobenius(got[n], ref[n]) for n in OUTS}
+    print(cfg.name, {n: f"{v:.2e}" for n, v in errs.items()}, flush=True)
+    for n in OUTS:
+        assert errs[n] <= TOL[mode], (n, errs[n])
+    empty = np.nonzero(r["counts"] == 0)[0]
+    for e in empty:
+        for n in ("dwg", "dwu", "dwd"):
+            assert not np.any(got[n][e]), (n, e)
+    if cfg.name == "zipf_empty_experts":
+        assert empty.size > 0
+    if cfg.el < cfg.E:                                   # tokens with no local pair: exact zeros
+        none = np.nonzero(np.all(r["pair_pos"].reshape(cfg.T, cfg.k) < 0, axis=1))[0]
+        assert not np.any(got["y"][none]) and not np.any(got["dx"][none])
+
+
+def test_expert_shares_add_up_on_gpu():
+    cfg, L = inputs.custom_layer(T=256, H=256, F=128, E=8, k=2, dtype="bf16", seed=21)
+    full = run_layer(cfg, L)
+    acc = {n: 0.0 for n in ("y", "dx", "dlogits")}
+    for e0 in range(0, 8, 4):
+        sc = cfg.with_(E_local=4, e0=e0)
+        Ls = dict(L, wg=L["wg"][e0:e0 + 4], wu=L["wu"][e0:e0 + 4], wd=L["wd"][e0:e0 + 4])
+        part = run_layer(sc, Ls)
+        for n in acc:
+            acc[n] = acc[n] + part[n]
+        for n in ("dwg", "dwu", "dwd"):
+            assert np.array_equal(part[n], full[n][e0:e0 + 4]), n
+    for n in acc:
+        assert oracle.rel_frobenius(acc[n], full[n]) <= 1e-2, n
+
+
+def test_deterministic_and_poison_independent():
+    cfg, L = inputs.custom_layer(T=300, H=512, F=256, E=16, k=4, dtype="bf16", seed=22)
+    a = run_layer(cfg, L)
+    b = run_layer(cfg, L, poison=True)
+    for n in OUTS:
+        assert a[n].tobytes() == b[n].tobytes(), n
+
+
+# ------------------------------------------------------------------------------ full-size workloads
+
+def sampled_check(cfg, L, got, ntok=24, seed=0):
+    rng = np.random.default_rng(seed)
+    toks = sorted(set([0, cfg.T - 1] + rng.choice(cfg.T, ntok, replace=False).tolist()))
+    r = check_routing(cfg, L, got["routing"])
+    s = oracle.token_rows(toks, L["dy"], L["x"], L["logits"], L["wg"], L["wu"], L["wd"], cfg.k, cfg.e0, cfg.el)
+    errs = {n: oracle.rel_frobenius(got[n][toks], s[n]) for n in ("y", "dx", "dlogits")}
+    counts = r["counts"]
+    experts = sorted(set([0, cfg.el - 1, int(np.argmax(counts)), int(np.argmin(counts))]))
+    for i in experts:
+        dg, du, dd = oracle.expert_grads(i, L["dy"], L["x"], L["logits"], L["wg"][i], L["wu"][i], L["wd"][i],
+                                         cfg.k, cfg.e0, cfg.el, r=r)
+        for n, ref in (("dwg", dg), ("dwu", du), ("dwd", dd)):
+            errs[f"{n}[{i}]"] = oracle.rel_frobenius(got[n][i], ref)
+    print(cfg.name, "counts min/max", counts.min(), counts.max(), {n: f"{v:.2e}" for n, v in errs.items()},
+          flush=True)
+    for n, v in errs.items():
+        assert v <= TOL[cfg.dtype], (n, v)
+    for n in OUTS:
+        assert np.all(np.isfinite(got[n])), n
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(400)
+@pytest.mark.parametrize("name", ["qwen3_30b_a3b", "qwen3_30b_a3b_ep16", "qwen3_235b_a22b_zipf"])
+def test_full_size_sampled(name):
+    cfg = inputs.CONFIGS[name]
+    print(f"case {name}: generating inputs", flush=True)
+    L = inputs.make_layer(cfg)
+    print(f"case {name}: running fwd+bwd on the GPU", flush=True)
+    got = run_layer(cfg, L)
+    sampled_check(cfg, L, got)
+    del got
+    torch.cuda.empty_cache()
