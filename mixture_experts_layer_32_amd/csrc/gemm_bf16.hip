@@ -1,0 +1,636 @@
+// bf16 grouped-GEMM engine for gfx950 and the six expert GEMMs of the fused MoE layer.
+// The SwiGLU experts and the combine are from "A Magia da Fusão" on "IA: MoE Kernel 3x Mais Rápido
+// Chegou!"; the backward pass is from "Afinal, o que é esse Prime Mega MoE?" on the same page;
+// the bf16 precision mode is from "Supporto di precisione e vincoli hardware" on "Prime Mega MoE:
+// il kernel che accelera il training AI del 55%".
+//
+// Engine:
+//  * A workgroup of 4 wavefronts computes a 256x256 output tile, each wave a 128x128 quadrant,
+//    as 4x4 blocks of v_mfma_f32_32x32x16_bf16 with fp32 accumulators (256 per lane, in AGPRs).
+//  * A K-tile is 32 contraction elements. Operand tiles reach LDS with global_load_lds_dwordx4
+//    (no VGPR staging) through a 4-stage ring of 32 KB stages, so three K-tiles are in flight
+//    while one is multiplied. Each wave waits only for its own loads of the current K-tile
+//    (vmcnt with the exact count of younger loads), then a barrier publishes them.
+//  * K-major operand (contraction axis contiguous: x, dY, hw, dab rows, and the weights in the
+//    forward): one 64-byte LDS row per M/N index. Chunk c of row r goes to slot
+//    c ^ ((r >> 2) & 3). ds_read_b128 fragment reads are then conflict-free.
+//  * MN-major operand (M/N axis contiguous: the weights in the dgrad GEMMs, every weight-gradient
+//    operand): one 512-byte LDS row per contraction index. Chunk c of row k goes to slot
+//    c ^ ((k & 3) << 2). Fragments are read with ds_read_b64_tr_b16, which transposes 16x4
+//    blocks on the fly. In each 16-lane group, lane s reads 4 columns of row k0 + s/4; lane i
+//    then receives column i of rows k0..k0+3. The four rows of one read land in disjoint bank
+//    groups.
+//  * Rows outside an expert's segment are clamped to a valid row when they only feed discarded
+//    outputs. When they would contribute to a contraction, they read the zero page. The token
+//    indices of gathered contraction rows come through scalar loads, so that the vector memory
+//    counter tracks nothing but the tile loads.
+//  * The row-tiled kernels are persistent. Each XCD takes one contiguous range of the
+//    expert-major tile list, so the blocks sharing an expert's operands share that XCD's L2.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_t;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int TILE = 256;            // output tile rows and columns
+constexpr int KTILE = 32;            // contraction elements per K-tile
+constexpr int STAGES = 4;            // LDS ring depth
+constexpr int OPB = 16384;           // bytes per operand per stage
+constexpr int STB = 2 * OPB;         // bytes per stage
+constexpr int LOADS = 4;             // global_load_lds per lane per operand per K-tile
+constexpr int NTHR = 256;
+
+// One wave-wide direct-to-LDS load: lane i copies 16 bytes from g into lds + 16*i (lds is
+// wave-uniform). Written as inline assembly so that the compiler neither tracks it nor inserts
+// waits for it. The main loop orders these loads with explicit vmcnt waits and barriers.
+__device__ __forceinline__ void gl2lds(const void* g, char* lds) {
+  const unsigned off = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(off), "v"(g) : "memory", "m0");
+}
+// wait until at most N vector memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// workgroup barrier without a memory fence. The caller has already waited for the loads the
+// barrier publishes; lgkmcnt(0) retires this wave's LDS reads before other waves may overwrite
+// the stage.
+__device__ __forceinline__ void block_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+__device__ __forceinline__ int kswz(int r) { return (r >> 2) & 3; }
+
+__device__ __forceinline__ bf16x8 frag_k(const char* tile, int row0, int ks, int lane) {
+  const int r = row0 + (lane & 31);
+  const int c = 2 * ks + (lane >> 5);
+  return *reinterpret_cast<const bf16x8*>(tile + r * 64 + ((c ^ kswz(r)) << 4));
+}
+
+__device__ __forceinline__ const char* mn_addr(const char* tile, int k, int col) {
+  return tile + k * 512 + ((((col >> 3) ^ ((k & 3) << 2))) << 4) + (col & 7) * 2;
+}
+
+__device__ __forceinline__ bf16x8 frag_mn(const char* tile, int col0, int ks, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int k = 16 * ks + 8 * (g >> 1) + (s >> 2);
+  const int col = col0 + 16 * (g & 1) + 4 * (s & 3);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)mn_addr(tile, k, col));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)mn_addr(tile, k + 4, col));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// ------------------------------------------------------------------------------------------------
+// Operand loaders. issue(stage_tile, kt) starts the LOADS direct-to-LDS loads this lane owns for
+// K-tile kt. prefetch(kt) fetches (into SGPRs) the row indices issue(kt) will need; it runs one
+// K-tile ahead of issue.
+
+// contraction row owned by this lane in load slot j of an MN-major operand (2 rows per slot)
+__device__ __forceinline__ int mn_krow(int j) { return wave_id() * 8 + 2 * j + ((threadIdx.x & 63) >> 5); }
+
+// K-major operand of 256 rows. This lane owns rows w*64 + 16j + lane/4 (j < 4), slot lane&3.
+struct KOp {
+  const char* p[LOADS];   // global address of this lane's chunk in K-tile 0
+  __device__ __forceinline__ void prefetch(int) {}
+  __device__ __forceinline__ void issue(char* tile, int kt) const {
+    const int w = wave_id();
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) gl2lds(p[j] + (size_t)kt * 64, tile + (w * LOADS + j) * 1024);
+  }
+  __device__ __forceinline__ static int row_of(int j) { return wave_id() * 64 + 16 * j + ((threadIdx.x & 63) >> 2); }
+  __device__ __forceinline__ static int chunk_of(int j) { return (threadIdx.x & 3) ^ kswz(row_of(j)); }
+};
+
+// MN-major operand: 32 contraction rows of 256 columns starting at column col0. This lane owns
+// contraction rows w*8 + 2j + lane/32 (j < 4) and slot lane&31.
+template <class Rows>
+struct MNOp {
+  Rows rows;
+  const char* zero;
+  int coff[LOADS];     // byte offset of this lane's column chunk, or -1 if past the last column
+  __device__ __forceinline__ void init(int col0, int ncols) {
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int c = (threadIdx.x & 31) ^ ((mn_krow(j) & 3) << 2);
+      coff[j] = col0 + 8 * c < ncols ? 16 * c : -1;
+    }
+  }
+  __device__ __forceinline__ void prefetch(int kt) { rows.prefetch(kt); }
+  __device__ __forceinline__ void issue(char* tile, int kt) const {
+    const int w = wave_id();
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const char* r = rows.row(kt, j);
+      gl2lds(r && coff[j] >= 0 ? r + coff[j] : zero, tile + (w * LOADS + j) * 1024);
+    }
+  }
+};
+
+// contraction rows of a weight matrix: row k at base + k*ld (k < split) or base2 + (k-split)*ld
+struct WeightRows {
+  const char* base;
+  const char* base2;
+  size_t ld;
+  int split;
+  __device__ __forceinline__ void prefetch(int) {}
+  __device__ __forceinline__ const char* row(int kt, int j) const {
+    const int k = kt * KTILE + mn_krow(j);
+    return k < split ? base + (size_t)k * ld : base2 + (size_t)(k - split) * ld;
+  }
+};
+
+// contraction rows = an expert's pairs seg0 .. seg_end-1: the pair rows of a [rows, ld] tensor
+struct PairRows {
+  const char* base;
+  size_t ld;
+  int seg0, seg_end;
+  __device__ __forceinline__ void prefetch(int) {}
+  __device__ __forceinline__ const char* row(int kt, int j) const {
+    const int r = seg0 + kt * KTILE + mn_krow(j);
+    return r < seg_end ? base + (size_t)r * ld : nullptr;
+  }
+};
+
+// contraction rows = an expert's pairs, as the token rows of a [T, ld] tensor via perm. The
+// wave's 8 token indices of a K-tile arrive through one scalar load.
+struct GatherRows {
+  const char* base;
+  const int* __restrict__ perm;
+  size_t ld;
+  int seg0, seg_end, topk;
+  int tok[8];
+  __device__ __forceinline__ void prefetch(int kt) {
+    const int r0 = seg0 + kt * KTILE + wave_id() * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tok[i] = perm[min(r0 + i, seg_end - 1)] / topk;
+  }
+  __device__ __forceinline__ const char* row(int kt, int j) const {
+    const int hi = (threadIdx.x & 63) >> 5;
+    const int r = seg0 + kt * KTILE + mn_krow(j);
+    const int t = hi ? tok[2 * j + 1] : tok[2 * j];
+    return r < seg_end ? base + (size_t)t * ld : nullptr;
+  }
+};
+
+// ------------------------------------------------------------------------------------------------
+// Main loop: nk K-tiles, accumulating into acc. A rows am0.. of the A tile (wave's quadrant); B
+// fragments from columns bn[ni]. Each K-tile is two 16-deep steps. The fragments of the second
+// step are read while the MFMAs of the first run. The barrier that publishes the next K-tile sits
+// between the two steps, and the next K-tile's first fragments are read while the second step's
+// MFMAs run, so the MFMA pipe stays fed across the barrier. The ring holds 4 K-tiles: at the
+// barrier of K-tile kt, K-tile kt+4 is issued into the stage K-tile kt came from (its fragments are
+// all in registers by then). On return all LDS reads are done (LDS may be reused).
+template <bool AMN, bool BMN>
+__device__ __forceinline__ void read_frags(bf16x8 (&fa)[4], bf16x8 (&fb)[4], const char* st, int ks, int am0,
+                                           const int (&bn)[4], int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fa[i] = AMN ? frag_mn(st, am0 + 32 * i, ks, lane) : frag_k(st, am0 + 32 * i, ks, lane);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) fb[j] = BMN ? frag_mn(st + OPB, bn[j], ks, lane) : frag_k(st + OPB, bn[j], ks, lane);
+}
+
+// The B fragment is passed as the MFMA's first operand, so each accumulator block holds the
+// transposed 32x32 block: lane l keeps row (l & 31) of C and 4 consecutive columns per group of 4.
+__device__ __forceinline__ void mma_step(f32x16 (&acc)[4][4], const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+}
+
+// wait until the K-tile whose loads are followed by `younger` more issued K-tiles has landed
+__device__ __forceinline__ void wait_tile(int younger) {
+  if (younger >= 3) wait_vm<3 * 2 * LOADS>();
+  else if (younger == 2) wait_vm<2 * 2 * LOADS>();
+  else if (younger == 1) wait_vm<2 * LOADS>();
+  else wait_vm<0>();
+}
+
+template <bool AMN, bool BMN, class LA, class LB>
+__device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], char* smem, LA& la, LB& lb, int nk, int am0,
+                                         const int (&bn)[4]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  if (nk <= 0) return;
+  wait_vm<0>();   // stores of the previous tile's epilogue must not count against the ring below
+  block_sync();   // and every wave is done reading its epilogue staging slab
+#pragma unroll
+  for (int s = 0; s < STAGES; ++s) {
+    if (s < nk) {
+      la.prefetch(s);
+      lb.prefetch(s);
+      la.issue(smem + s * STB, s);
+      lb.issue(smem + s * STB + OPB, s);
+    }
+  }
+  if (STAGES < nk) {
+    la.prefetch(STAGES);
+    lb.prefetch(STAGES);
+  }
+  wait_tile(min(nk - 1, STAGES - 1));
+  block_sync();
+  bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+  read_frags<AMN, BMN>(fa0, fb0, smem, 0, am0, bn, lane);
+  for (int kt = 0; kt < nk; ++kt) {
+    const char* cur = smem + (kt % STAGES) * STB;
+    read_frags<AMN, BMN>(fa1, fb1, cur, 1, am0, bn, lane);
+    mma_step(acc, fa0, fb0);
+    if (kt + 1 < nk) {
+      wait_tile(min(nk - 2 - kt, STAGES - 2));
+      block_sync();
+      if (kt + STAGES < nk) {
+        const int t = kt + STAGES;
+        char* st = smem + (t % STAGES) * STB;
+        la.issue(st, t);
+        lb.issue(st + OPB, t);
+        if (t + 1 < nk) {
+          la.prefetch(t + 1);
+          lb.prefetch(t + 1);
+        }
+      }
+      read_frags<AMN, BMN>(fa0, fb0, smem + ((kt + 1) % STAGES) * STB, 0, am0, bn, lane);
+    }
+    mma_step(acc, fa1, fb1);
+  }
+  block_sync();
+}
+
+// Accumulator element q of block (i, j) is C[am0 + 32i + (lane & 31)][bn[j] + 8(q/4) + 4(lane/32) + q%4]:
+// for a = q/4 a lane holds 4 consecutive columns of one row.
+__device__ __forceinline__ int acc_m(int i, int lane) { return 32 * i + (lane & 31); }
+__device__ __forceinline__ int acc_n(int a, int lane) { return 8 * a + 4 * (lane >> 5); }
+
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+  return __builtin_bit_cast(uint2, v);
+}
+__device__ __forceinline__ void st8(void* p, uint2 v) { *reinterpret_cast<uint2*>(p) = v; }
+// ------------------------------------------------------------------------------------------------
+// Epilogue staging. After the main loop the LDS ring is free. Each wave stages 32 rows of its
+// 128x128 quadrant as fp32 (row stride 132 floats, so the 32 rows of one write land in distinct
+// banks). It then reads them back row-contiguous, so that global loads and stores move whole 128- or
+// 256-byte row segments with 16-byte lanes.
+constexpr int SLD = 132;                       // staged row stride (floats)
+constexpr int SLAB = 32 * SLD;                 // floats per wave
+
+__device__ __forceinline__ float* wave_slab(char* smem) {
+  return reinterpret_cast<float*>(smem) + wave_id() * SLAB;
+}
+
+// rows 32i .. 32i+31 of the quadrant; staged column 32j + 8a + 4(lane/32) + b holds block j
+__device__ __forceinline__ void stage_rows(float* slab, const f32x16 (&acc)[4][4], int i, int lane) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      float4 v = make_float4(acc[i][j][4 * a], acc[i][j][4 * a + 1], acc[i][j][4 * a + 2], acc[i][j][4 * a + 3]);
+      *reinterpret_cast<float4*>(slab + (lane & 31) * SLD + 32 * j + acc_n(a, lane)) = v;
+    }
+}
+
+__device__ __forceinline__ void read8(const float* slab, int row, int col, float (&v)[8]) {
+  const float4 x = *reinterpret_cast<const float4*>(slab + row * SLD + col);
+  const float4 y = *reinterpret_cast<const float4*>(slab + row * SLD + col + 4);
+  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w; v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+}
+
+__device__ __forceinline__ uint4 pack8(const float (&v)[8]) {
+  const bf16x8 b = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3], (bf16)v[4], (bf16)v[5], (bf16)v[6], (bf16)v[7]};
+  return __builtin_bit_cast(uint4, b);
+}
+__device__ __forceinline__ void unpack8(uint4 u, float (&v)[8]) {
+  const bf16x8 b = __builtin_bit_cast(bf16x8, u);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (float)b[e];
+}
+
+// Stores the wave's 128x128 quadrant (columns contiguous from the quadrant's first column) as
+// bf16. out_row(m) gives the output row pointer of quadrant row m at the quadrant's first column,
+// or null to skip the row; ncols limits the columns written.
+template <class OutRow>
+__device__ __forceinline__ void store_quadrant(char* smem, const f32x16 (&acc)[4][4], int lane, OutRow out_row,
+                                               int ncols) {
+  float* slab = wave_slab(smem);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    stage_rows(slab, acc, i, lane);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int rl = (lane >> 4) + 4 * s, c0 = (lane & 15) * 8;
+      bf16* o = out_row(32 * i + rl);
+      if (o && c0 < ncols) {
+        float v[8];
+        read8(slab, rl, c0, v);
+        st16(o + c0, pack8(v));
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void unpack4(uint2 v, float (&f)[4]) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const bf16x4 b = __builtin_bit_cast(bf16x4, v);
+  f[0] = (float)b[0]; f[1] = (float)b[1]; f[2] = (float)b[2]; f[3] = (float)b[3];
+}
+
+#define MOE_SMEM __shared__ __attribute__((aligned(1024))) char smem[STAGES * STB];
+
+// ------------------------------------------------------------------------------------------------
+// forward: [a | b] = gather(x) [W_gate; W_up]^T, then ab and hw = w * silu(a) * b
+__global__ __launch_bounds__(NTHR, 1) void k_gateup_bf16(FwdParams p) {
+  MOE_SMEM
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const bf16* __restrict__ x = static_cast<const bf16*>(p.x);
+  const bf16* __restrict__ wg = static_cast<const bf16*>(p.wg);
+  const bf16* __restrict__ wu = static_cast<const bf16*>(p.wu);
+  bf16* __restrict__ ab = static_cast<bf16*>(p.ab);
+  bf16* __restrict__ hw = static_cast<bf16*>(p.hw);
+  const int H = p.H, F = p.F, ntn = F / 128;
+  const XcdRange xr = xcd_range(*p.num_mtiles2 * ntn);
+  const int bn[4] = {64 * wn, 64 * wn + 32, 128 + 64 * wn, 128 + 64 * wn + 32};
+  for (int tile = xr.first; tile < xr.end; tile += xr.stride) {
+    const int mt = tile / ntn, nt = tile - mt * ntn;
+    const int2 me = p.mtile2[mt];
+    const int e = me.x, r0 = me.y, seg_end = p.offsets[e + 1];
+    KOp la, lb;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int row = KOp::row_of(j), c = KOp::chunk_of(j);
+      const int r = min(r0 + row, seg_end - 1);
+      la.p[j] = reinterpret_cast<const char*>(x + (size_t)(p.perm[r] / p.k) * H) + 16 * c;
+      const bf16* wrow = row < 128 ? wg + ((size_t)e * F + nt * 128 + row) * H : wu + ((size_t)e * F + nt * 128 + row - 128) * H;
+      lb.p[j] = reinterpret_cast<const char*>(wrow) + 16 * c;
+    }
+    float wrow[4];   // routing weight of quadrant row 32i + (lane & 31)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wrow[i] = p.weight[p.perm[min(r0 + 128 * wm + acc_m(i, lane), seg_end - 1)]];
+    f32x16 acc[4][4];
+    mainloop<false, false>(acc, smem, la, lb, H / KTILE, 128 * wm, bn);
+    // staged columns 0..63 hold gate columns f0.., 64..127 the matching up columns
+    float* slab = wave_slab(smem);
+    const int f0 = nt * 128 + 64 * wn;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      stage_rows(slab, acc, i, lane);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int rl = (lane >> 3) + 8 * s, c0 = (lane & 7) * 8;
+        const float wt = __shfl(wrow[i], rl);
+        const int r = r0 + 128 * wm + 32 * i + rl;
+        if (r < seg_end) {
+          float av[8], bv[8], hv[8];
+          read8(slab, rl, c0, av);
+          read8(slab, rl, 64 + c0, bv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) hv[e] = wt * (av[e] * sigmoidf_(av[e]) * bv[e]);
+          bf16* abr = ab + (size_t)r * 2 * F + f0 + c0;
+          st16(abr, pack8(av));
+          st16(abr + F, pack8(bv));
+          st16(hw + (size_t)r * F + f0 + c0, pack8(hv));
+        }
+      }
+    }
+  }
+}
+
+// forward: o' = hw W_down[e]^T
+__global__ __launch_bounds__(NTHR, 1) void k_down_bf16(FwdParams p) {
+  MOE_SMEM
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const bf16* __restrict__ hw = static_cast<const bf16*>(p.hw);
+  const bf16* __restrict__ wd = static_cast<const bf16*>(p.wd);
+  bf16* __restrict__ o = static_cast<bf16*>(p.o);
+  const int H = p.H, F = p.F, ntn = H / TILE;
+  const XcdRange xr = xcd_range(*p.num_mtiles2 * ntn);
+  const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
+  for (int tile = xr.first; tile < xr.end; tile += xr.stride) {
+    const int mt = tile / ntn, nt = tile - mt * ntn;
+    const int2 me = p.mtile2[mt];
+    const int e = me.x, r0 = me.y, seg_end = p.offsets[e + 1];
+    KOp la, lb;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int row = KOp::row_of(j), c = KOp::chunk_of(j);
+      const int r = min(r0 + row, seg_end - 1);
+      la.p[j] = reinterpret_cast<const char*>(hw + (size_t)r * F) + 16 * c;
+      lb.p[j] = reinterpret_cast<const char*>(wd + ((size_t)e * H + nt * TILE + row) * F) + 16 * c;
+    }
+    f32x16 acc[4][4];
+    mainloop<false, false>(acc, smem, la, lb, F / KTILE, 128 * wm, bn);
+    const int rq = r0 + 128 * wm;
+    bf16* const oq = o + nt * TILE + 128 * wn;
+    store_quadrant(smem, acc, lane, [&](int m) { return rq + m < seg_end ? oq + (size_t)(rq + m) * H : nullptr; }, 128);
+  }
+}
+
+// backward: u = gather(dY) W_down[e]; epilogue writes g partials, da, db
+__global__ __launch_bounds__(NTHR, 1) void k_bwd_dh_bf16(BwdParams p) {
+  MOE_SMEM
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const bf16* __restrict__ dy = static_cast<const bf16*>(p.dy);
+  const bf16* __restrict__ ab = static_cast<const bf16*>(p.ab);
+  bf16* __restrict__ dab = static_cast<bf16*>(p.dab);
+  const int H = p.H, F = p.F, ntn = (F + TILE - 1) / TILE;
+  const XcdRange xr = xcd_range(*p.num_mtiles2 * ntn);
+  const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
+  for (int tile = xr.first; tile < xr.end; tile += xr.stride) {
+    const int mt = tile / ntn, nt = tile - mt * ntn;
+    const int2 me = p.mtile2[mt];
+    const int e = me.x, r0 = me.y, seg_end = p.offsets[e + 1];
+    KOp la;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int r = min(r0 + KOp::row_of(j), seg_end - 1);
+      la.p[j] = reinterpret_cast<const char*>(dy + (size_t)(p.perm[r] / p.k) * H) + 16 * KOp::chunk_of(j);
+    }
+    MNOp<WeightRows> lb;
+    const char* wbase = reinterpret_cast<const char*>(static_cast<const bf16*>(p.wd) + (size_t)e * H * F + nt * TILE);
+    lb.rows = WeightRows{wbase, wbase, (size_t)F * 2, H};
+    lb.zero = static_cast<const char*>(p.zeros);
+    lb.init(nt * TILE, F);
+    float wrow[4];   // routing weight of quadrant row 32i + (lane & 31)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wrow[i] = p.weight[p.perm[min(r0 + 128 * wm + acc_m(i, lane), seg_end - 1)]];
+    f32x16 acc[4][4];
+    mainloop<false, true>(acc, smem, la, lb, H / KTILE, 128 * wm, bn);
+    // u = dH' staged per 32 rows; each row's 128 columns are read by 16 lanes, 8 columns each
+    float* slab = wave_slab(smem);
+    const int fq = nt * TILE + 128 * wn;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      stage_rows(slab, acc, i, lane);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int rl = (lane >> 4) + 4 * s, c0 = (lane & 15) * 8;
+        const float wt = __shfl(wrow[i], rl);
+        const int r = r0 + 128 * wm + 32 * i + rl, f = fq + c0;
+        float gsum = 0.f;
+        if (r < seg_end && f < F) {
+          float u[8], av[8], bv[8], da[8], db[8];
+          read8(slab, rl, c0, u);
+          const bf16* abr = ab + (size_t)r * 2 * F + f;
+          unpack8(ld16(abr), av);
+          unpack8(ld16(abr + F), bv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float sg = sigmoidf_(av[e]), si = av[e] * sg;
+            gsum += u[e] * (si * bv[e]);
+            const float dh = wt * u[e];
+            da[e] = dh * bv[e] * sg * (1.0f + av[e] * (1.0f - sg));
+            db[e] = dh * si;
+          }
+          bf16* dabr = dab + (size_t)r * 2 * F + f;
+          st16(dabr, pack8(da));
+          st16(dabr + F, pack8(db));
+        }
+        gsum += __shfl_xor(gsum, 1);
+        gsum += __shfl_xor(gsum, 2);
+        gsum += __shfl_xor(gsum, 4);
+        gsum += __shfl_xor(gsum, 8);
+        if (r < seg_end && (lane & 15) == 0) p.gpart[(size_t)(nt * 2 + wn) * p.rows + r] = gsum;
+      }
+    }
+  }
+}
+
+// backward: dX = [da db] [W_gate[e]; W_up[e]] (contraction over 2F)
+__global__ __launch_bounds__(NTHR, 1) void k_dgrad_x_bf16(BwdParams p) {
+  MOE_SMEM
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const bf16* __restrict__ dab = static_cast<const bf16*>(p.dab);
+  bf16* __restrict__ dxp = static_cast<bf16*>(p.dxp);
+  const int H = p.H, F = p.F, ntn = H / TILE;
+  const XcdRange xr = xcd_range(*p.num_mtiles2 * ntn);
+  const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
+  for (int tile = xr.first; tile < xr.end; tile += xr.stride) {
+    const int mt = tile / ntn, nt = tile - mt * ntn;
+    const int2 me = p.mtile2[mt];
+    const int e = me.x, r0 = me.y, seg_end = p.offsets[e + 1];
+    KOp la;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int r = min(r0 + KOp::row_of(j), seg_end - 1);
+      la.p[j] = reinterpret_cast<const char*>(dab + (size_t)r * 2 * F) + 16 * KOp::chunk_of(j);
+    }
+    MNOp<WeightRows> lb;
+    lb.rows = WeightRows{reinterpret_cast<const char*>(static_cast<const bf16*>(p.wg) + (size_t)e * F * H + nt * TILE),
+                         reinterpret_cast<const char*>(static_cast<const bf16*>(p.wu) + (size_t)e * F * H + nt * TILE),
+                         (size_t)H * 2, F};
+    lb.zero = static_cast<const char*>(p.zeros);
+    lb.init(nt * TILE, H);
+    f32x16 acc[4][4];
+    mainloop<false, true>(acc, smem, la, lb, 2 * F / KTILE, 128 * wm, bn);
+    const int rq = r0 + 128 * wm;
+    bf16* const oq = dxp + nt * TILE + 128 * wn;
+    store_quadrant(smem, acc, lane, [&](int m) { return rq + m < seg_end ? oq + (size_t)(rq + m) * H : nullptr; }, 128);
+  }
+}
+
+// backward: dW_down[e] (H x F) = sum over the expert's pairs of dY_t hw_r^T
+__global__ __launch_bounds__(NTHR, 1) void k_wgrad_down_bf16(BwdParams p) {
+  MOE_SMEM
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const int H = p.H, F = p.F, ntn = (F + TILE - 1) / TILE, tpe = (H / TILE) * ntn;
+  const int lid = xcd_logical_block(gridDim.x);
+  const int e = lid / tpe, t = lid - e * tpe, mt = t / ntn, nt = t - mt * ntn;
+  const int seg0 = p.offsets[e], seg_end = p.offsets[e + 1];
+  MNOp<GatherRows> la;
+  la.rows = GatherRows{reinterpret_cast<const char*>(static_cast<const bf16*>(p.dy) + mt * TILE), p.perm,
+                       (size_t)H * 2, seg0, seg_end, p.k, {}};
+  la.zero = static_cast<const char*>(p.zeros);
+  la.init(mt * TILE, H);
+  MNOp<PairRows> lb;
+  lb.rows = PairRows{reinterpret_cast<const char*>(static_cast<const bf16*>(p.hw) + nt * TILE), (size_t)F * 2, seg0,
+                     seg_end};
+  lb.zero = static_cast<const char*>(p.zeros);
+  lb.init(nt * TILE, F);
+  const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
+  f32x16 acc[4][4];
+  mainloop<true, true>(acc, smem, la, lb, (seg_end - seg0 + KTILE - 1) / KTILE, 128 * wm, bn);
+  bf16* __restrict__ out = static_cast<bf16*>(p.dwd) + (size_t)e * H * F;
+  const int mq = mt * TILE + 128 * wm, nq = nt * TILE + 128 * wn;
+  store_quadrant(smem, acc, lane, [&](int m) { return out + (size_t)(mq + m) * F + nq; }, F - nq);
+}
+
+// backward: [dW_gate; dW_up][e] (2F x H) = sum over the expert's pairs of [da; db]_r x_t^T
+__global__ __launch_bounds__(NTHR, 1) void k_wgrad_gateup_bf16(BwdParams p) {
+  MOE_SMEM
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const int H = p.H, F = p.F, ntn = H / TILE, tpe = (2 * F / TILE) * ntn;
+  const int lid = xcd_logical_block(gridDim.x);
+  const int e = lid / tpe, t = lid - e * tpe, mt = t / ntn, nt = t - mt * ntn;
+  const int seg0 = p.offsets[e], seg_end = p.offsets[e + 1];
+  MNOp<PairRows> la;
+  la.rows = PairRows{reinterpret_cast<const char*>(static_cast<const bf16*>(p.dab) + mt * TILE), (size_t)F * 4, seg0,
+                     seg_end};
+  la.zero = static_cast<const char*>(p.zeros);
+  la.init(mt * TILE, 2 * F);
+  MNOp<GatherRows> lb;
+  lb.rows = GatherRows{reinterpret_cast<const char*>(static_cast<const bf16*>(p.x) + nt * TILE), p.perm,
+                       (size_t)H * 2, seg0, seg_end, p.k, {}};
+  lb.zero = static_cast<const char*>(p.zeros);
+  lb.init(nt * TILE, H);
+  const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
+  f32x16 acc[4][4];
+  mainloop<true, true>(acc, smem, la, lb, (seg_end - seg0 + KTILE - 1) / KTILE, 128 * wm, bn);
+  bf16* __restrict__ dwg = static_cast<bf16*>(p.dwg) + (size_t)e * F * H;
+  bf16* __restrict__ dwu = static_cast<bf16*>(p.dwu) + (size_t)e * F * H;
+  const int mq = mt * TILE + 128 * wm, nq = nt * TILE + 128 * wn;
+  store_quadrant(smem, acc, lane, [&](int m) {
+    const int mm = mq + m;
+    return (mm < F ? dwg + (size_t)mm * H : dwu + (size_t)(mm - F) * H) + nq;
+  }, 128);
+}
+
+}  // namespace
+
+hipError_t launch_forward_gemms_bf16(const FwdParams& p, int grid, hipStream_t s) {
+  hipError_t err;
+  prof_mark_begin("gemm_gateup_swiglu", s);
+  k_gateup_bf16<<<grid, NTHR, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+  prof_mark_begin("gemm_down", s);
+  k_down_bf16<<<grid, NTHR, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+  return hipSuccess;
+}
+
+hipError_t launch_backward_gemms_bf16(const BwdParams& p, int grid, hipStream_t s) {
+  hipError_t err;
+  prof_mark_begin("gemm_bwd_dh_dswiglu", s);
+  k_bwd_dh_bf16<<<grid, NTHR, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+  const int nb_wd = p.El * (p.H / TILE) * ((p.F + TILE - 1) / TILE);
+  prof_mark_begin("gemm_wgrad_down", s);
+  k_wgrad_down_bf16<<<nb_wd, NTHR, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+  const int nb_wgu = p.El * (2 * p.F / TILE) * (p.H / TILE);
+  prof_mark_begin("gemm_wgrad_gateup", s);
+  k_wgrad_gateup_bf16<<<nb_wgu, NTHR, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+  prof_mark_begin("gemm_dgrad_x", s);
+  k_dgrad_x_bf16<<<grid, NTHR, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+  return hipSuccess;
+}
+
+}  // namespace moe

@@ -325,15 +325,21 @@ hipError_t launch_backward(const BwdParams& p, int grid, hipStream_t s) {
   k_dgrad_x<T><<<grid, kThreads, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   prof_mark_end(s);
+  return hipSuccess;
+}
 
+template <class T>
+hipError_t launch_combine_bwd(const BwdParams& p, hipStream_t s) {
   prof_mark_begin("combine_bwd", s);
   k_combine_bwd<T><<<(unsigned)p.T, 256, 0, s>>>(p);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
   prof_mark_end(s);
   return hipSuccess;
 }
 
 template hipError_t launch_backward<float>(const BwdParams&, int, hipStream_t);
-template hipError_t launch_backward<bf16>(const BwdParams&, int, hipStream_t);
+template hipError_t launch_combine_bwd<float>(const BwdParams&, hipStream_t);
+template hipError_t launch_combine_bwd<bf16>(const BwdParams&, hipStream_t);
 
 }  // namespace moe

@@ -169,7 +169,6 @@ hipError_t launch_combine(const void* src, const int* pair_pos, void* out, int64
 }
 
 template hipError_t launch_forward_gemms<float>(const FwdParams&, int, hipStream_t);
-template hipError_t launch_forward_gemms<bf16>(const FwdParams&, int, hipStream_t);
 template hipError_t launch_combine<float>(const void*, const int*, void*, int64_t, int, int, hipStream_t);
 template hipError_t launch_combine<bf16>(const void*, const int*, void*, int64_t, int, int, hipStream_t);
 

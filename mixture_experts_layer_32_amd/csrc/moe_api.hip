@@ -26,7 +26,8 @@ Layout make_layout(const moe_desc& d) {
   L.rows = d.T * (int64_t)d.topk;
   L.nblk_route = (int)((d.T + kRouteTokens - 1) / kRouteTokens);
   L.mtile_cap = (int)(L.rows / kBM) + d.E_local + 1;
-  L.np = d.F / 64;
+  L.mtile2_cap = (int)(L.rows / kBM2) + d.E_local + 1;
+  L.np = d.mode == MOE_MODE_FP32 ? d.F / 64 : 2 * ((d.F + 255) / 256);
   L.elem = d.mode == MOE_MODE_FP32 ? 4 : 2;
   const size_t rows = (size_t)L.rows, El = (size_t)d.E_local;
   size_t off = 0;
@@ -43,6 +44,9 @@ Layout make_layout(const moe_desc& d) {
   L.pair_pos = take(rows * 4);
   L.mtile = take((size_t)L.mtile_cap * 8);
   L.num_mtiles = take(4);
+  L.mtile2 = take((size_t)L.mtile2_cap * 8);
+  L.num_mtiles2 = take(4);
+  L.zeros = take(kZeroBytes);
   L.ab = take(rows * 2 * d.F * L.elem);
   L.hw = take(rows * d.F * L.elem);
   L.saved_total = off;
@@ -223,6 +227,9 @@ static RouteParams route_params(const moe_desc& d, const Layout& L, const float*
   p.pair_pos = reinterpret_cast<int*>(sv + L.pair_pos);
   p.mtile = reinterpret_cast<int2*>(sv + L.mtile);
   p.num_mtiles = reinterpret_cast<int*>(sv + L.num_mtiles);
+  p.mtile2 = reinterpret_cast<int2*>(sv + L.mtile2);
+  p.num_mtiles2 = reinterpret_cast<int*>(sv + L.num_mtiles2);
+  p.zeros = reinterpret_cast<uint4*>(sv + L.zeros);
   p.blk_mask = reinterpret_cast<unsigned long long*>(w + L.blk_mask);
   p.blk_count = reinterpret_cast<int*>(w + L.blk_count);
   p.blk_prefix = reinterpret_cast<int*>(w + L.blk_prefix);
@@ -274,6 +281,9 @@ moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits, const 
   fp.offsets = rp.offsets;
   fp.mtile = rp.mtile;
   fp.num_mtiles = rp.num_mtiles;
+  fp.mtile2 = rp.mtile2;
+  fp.num_mtiles2 = rp.num_mtiles2;
+  fp.zeros = rp.zeros;
   fp.weight = rp.weight;
   fp.ab = sv + L.ab;
   fp.hw = sv + L.hw;
@@ -285,13 +295,14 @@ moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits, const 
   fp.F = d->F;
   fp.k = d->topk;
   fp.El = d->E_local;
-  const int grid = persistent_grid(2);
   if (d->mode == MOE_MODE_FP32) {
-    if ((e = launch_forward_gemms<float>(fp, grid, s)) != hipSuccess) return hip_fail(e, "forward GEMM launch");
+    if ((e = launch_forward_gemms<float>(fp, persistent_grid(2), s)) != hipSuccess)
+      return hip_fail(e, "forward GEMM launch");
     if ((e = launch_combine<float>(fp.o, fp.pair_pos, y, d->T, d->topk, d->H, s)) != hipSuccess)
       return hip_fail(e, "combine launch");
   } else {
-    if ((e = launch_forward_gemms<bf16>(fp, grid, s)) != hipSuccess) return hip_fail(e, "forward GEMM launch");
+    if ((e = launch_forward_gemms_bf16(fp, persistent_grid(1), s)) != hipSuccess)
+      return hip_fail(e, "forward GEMM launch");
     if ((e = launch_combine<bf16>(fp.o, fp.pair_pos, y, d->T, d->topk, d->H, s)) != hipSuccess)
       return hip_fail(e, "combine launch");
   }
@@ -327,6 +338,9 @@ moe_status moe_bwd(const moe_desc* d, const void* dy, const void* x, const void*
   p.pair_pos = reinterpret_cast<const int*>(sv + L.pair_pos);
   p.mtile = reinterpret_cast<const int2*>(sv + L.mtile);
   p.num_mtiles = reinterpret_cast<const int*>(sv + L.num_mtiles);
+  p.mtile2 = reinterpret_cast<const int2*>(sv + L.mtile2);
+  p.num_mtiles2 = reinterpret_cast<const int*>(sv + L.num_mtiles2);
+  p.zeros = sv + L.zeros;
   p.ab = sv + L.ab;
   p.hw = sv + L.hw;
   p.dab = w + L.dab;
@@ -346,9 +360,11 @@ moe_status moe_bwd(const moe_desc* d, const void* dy, const void* x, const void*
   p.El = d->E_local;
   p.np = L.np;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int grid = persistent_grid(2);
-  hipError_t e = d->mode == MOE_MODE_FP32 ? launch_backward<float>(p, grid, s) : launch_backward<bf16>(p, grid, s);
-  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  hipError_t e = d->mode == MOE_MODE_FP32 ? launch_backward<float>(p, persistent_grid(2), s)
+                                           : launch_backward_gemms_bf16(p, persistent_grid(1), s);
+  if (e != hipSuccess) return hip_fail(e, "backward GEMM launch");
+  e = d->mode == MOE_MODE_FP32 ? launch_combine_bwd<float>(p, s) : launch_combine_bwd<bf16>(p, s);
+  if (e != hipSuccess) return hip_fail(e, "backward combine launch");
   return MOE_OK;
 }
 

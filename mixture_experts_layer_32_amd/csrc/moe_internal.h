@@ -8,7 +8,9 @@
 
 namespace moe {
 
-constexpr int kBM = 128;            // rows per M-tile of the row-tiled grouped GEMMs
+constexpr int kBM = 128;            // rows per M-tile of the fp32 row-tiled grouped GEMMs
+constexpr int kBM2 = 256;           // rows per M-tile of the bf16 row-tiled grouped GEMMs
+constexpr int kZeroBytes = 1024;    // zero page read by the bf16 GEMMs for out-of-range rows
 constexpr int kRouteTokens = 64;    // tokens per routing block (one 64-bit mask word per expert)
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopk = 32;
@@ -17,11 +19,13 @@ constexpr int kMaxTopk = 32;
 struct Layout {
   int64_t rows;        // T*k: upper bound on routed pairs
   int nblk_route;      // ceil(T / kRouteTokens)
-  int mtile_cap;       // upper bound on M-tiles: rows / kBM + E_local + 1
-  int np;              // partial sums of g per pair (F / 64)
+  int mtile_cap;       // upper bound on 128-row M-tiles: rows / kBM + E_local + 1
+  int mtile2_cap;      // upper bound on 256-row M-tiles
+  int np;              // partial sums of g per pair: F / 64 (fp32 engine), 2*ceil(F/256) (bf16 engine)
   size_t elem;         // bytes per stored element (4 or 2)
   // saved
-  size_t idx, weight, counts, offsets, perm, pair_pos, mtile, num_mtiles, ab, hw, saved_total;
+  size_t idx, weight, counts, offsets, perm, pair_pos, mtile, num_mtiles, mtile2, num_mtiles2, zeros, ab, hw,
+      saved_total;
   // forward workspace
   size_t blk_mask, blk_count, blk_prefix, o, fwd_total;
   // backward workspace
@@ -44,6 +48,9 @@ struct RouteParams {
   int* pair_pos;
   int2* mtile;
   int* num_mtiles;
+  int2* mtile2;
+  int* num_mtiles2;
+  uint4* zeros;
   unsigned long long* blk_mask;
   int* blk_count;
   int* blk_prefix;
@@ -62,6 +69,9 @@ struct FwdParams {
   const int* offsets;
   const int2* mtile;
   const int* num_mtiles;
+  const int2* mtile2;
+  const int* num_mtiles2;
+  const void* zeros;
   const float* weight;
   void* ab;
   void* hw;
@@ -88,6 +98,9 @@ struct BwdParams {
   const int* pair_pos;
   const int2* mtile;
   const int* num_mtiles;
+  const int2* mtile2;
+  const int* num_mtiles2;
+  const void* zeros;
   const void* ab;
   const void* hw;
   void* dab;
@@ -102,6 +115,9 @@ struct BwdParams {
   int H, F, k, E, El, np;
 };
 template <class T> hipError_t launch_backward(const BwdParams& p, int grid, hipStream_t s);
+template <class T> hipError_t launch_combine_bwd(const BwdParams& p, hipStream_t s);
+hipError_t launch_forward_gemms_bf16(const FwdParams& p, int grid, hipStream_t s);
+hipError_t launch_backward_gemms_bf16(const BwdParams& p, int grid, hipStream_t s);
 
 int persistent_grid(int blocks_per_cu);
 

@@ -135,19 +135,23 @@ __global__ __launch_bounds__(512) void k_route_offsets(RouteParams p) {
   __shared__ int lds[8];
   const int e = threadIdx.x;
   const int c = e < p.El ? p.counts[e] : 0;
-  const int nt = (c + kBM - 1) / kBM;
-  int tot_c, tot_t;
+  const int nt = (c + kBM - 1) / kBM, nt2 = (c + kBM2 - 1) / kBM2;
+  int tot_c, tot_t, tot_t2;
   const int inc_c = block_incl_scan<512>(c, lds, tot_c);
   const int inc_t = block_incl_scan<512>(nt, lds, tot_t);
+  const int inc_t2 = block_incl_scan<512>(nt2, lds, tot_t2);
   if (e < p.El) {
-    const int off = inc_c - c, t0 = inc_t - nt;
+    const int off = inc_c - c, t0 = inc_t - nt, t2 = inc_t2 - nt2;
     p.offsets[e] = off;
     for (int i = 0; i < nt; ++i) p.mtile[t0 + i] = make_int2(e, off + i * kBM);
+    for (int i = 0; i < nt2; ++i) p.mtile2[t2 + i] = make_int2(e, off + i * kBM2);
   }
   if (e == 0) {
     p.offsets[p.El] = tot_c;
     *p.num_mtiles = tot_t;
+    *p.num_mtiles2 = tot_t2;
   }
+  if (e < kZeroBytes / 16) p.zeros[e] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 __global__ __launch_bounds__(256) void k_route_scatter(RouteParams p) {
