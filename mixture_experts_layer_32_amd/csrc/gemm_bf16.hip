@@ -146,30 +146,18 @@ struct WeightRows {
   }
 };
 
-// contraction rows = an expert's pairs seg0 .. seg_end-1: the pair rows of a [rows, ld] tensor
-struct PairRows {
-  const char* base;
-  size_t ld;
-  int seg0, seg_end;
-  __device__ __forceinline__ void prefetch(int) {}
-  __device__ __forceinline__ const char* row(int kt, int j) const {
-    const int r = seg0 + kt * KTILE + mn_krow(j);
-    return r < seg_end ? base + (size_t)r * ld : nullptr;
-  }
-};
-
-// contraction rows = an expert's pairs, as the token rows of a [T, ld] tensor via perm. The
-// wave's 8 token indices of a K-tile arrive through one scalar load.
+// contraction rows = an expert's pairs, as the token rows of a [T, ld] tensor (ptok maps a
+// sorted pair to its token). The wave's 8 token indices of a K-tile arrive through one scalar load.
 struct GatherRows {
   const char* base;
-  const int* __restrict__ perm;
+  const int* __restrict__ ptok;
   size_t ld;
-  int seg0, seg_end, topk;
+  int seg0, seg_end;
   int tok[8];
   __device__ __forceinline__ void prefetch(int kt) {
     const int r0 = seg0 + kt * KTILE + wave_id() * 8;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) tok[i] = perm[min(r0 + i, seg_end - 1)] / topk;
+    for (int i = 0; i < 8; ++i) tok[i] = ptok[min(r0 + i, seg_end - 1)];
   }
   __device__ __forceinline__ const char* row(int kt, int j) const {
     const int hi = (threadIdx.x & 63) >> 5;
@@ -340,13 +328,32 @@ __device__ __forceinline__ void store_quadrant(char* smem, const f32x16 (&acc)[4
   }
 }
 
+// Writes staged columns [0, ncol) of the 32 staged rows to a pair-contiguous transposed copy.
+// dst(c) is the copy's row for staged column c, at the pair column of staged row 0 (null: skip).
+// Four lanes cover one column, 8 consecutive pair rows each: one 16-byte store, 64 contiguous bytes
+// per column.
+template <class Dst>
+__device__ __forceinline__ void store_transposed(const float* slab, int lane, int ncol, Dst dst) {
+  for (int cb = 0; cb < ncol; cb += 16) {
+    const int c = cb + (lane >> 2), g8 = 8 * (lane & 3);
+    bf16* o = dst(c);
+    if (o) {
+      float v[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) v[t] = slab[(g8 + t) * SLD + c];
+      st16(o + g8, pack8(v));
+    }
+  }
+}
+
 __device__ __forceinline__ void unpack4(uint2 v, float (&f)[4]) {
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   const bf16x4 b = __builtin_bit_cast(bf16x4, v);
   f[0] = (float)b[0]; f[1] = (float)b[1]; f[2] = (float)b[2]; f[3] = (float)b[3];
 }
 
-#define MOE_SMEM __shared__ __attribute__((aligned(1024))) char smem[STAGES * STB];
+constexpr int SMEM_BYTES = STAGES * STB > 8 * SLAB * 4 ? STAGES * STB : 8 * SLAB * 4;
+#define MOE_SMEM __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
 
 // ------------------------------------------------------------------------------------------------
 // forward: [a | b] = gather(x) [W_gate; W_up]^T, then ab and hw = w * silu(a) * b
@@ -370,7 +377,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_gateup_bf16(FwdParams p) {
     for (int j = 0; j < LOADS; ++j) {
       const int row = KOp::row_of(j), c = KOp::chunk_of(j);
       const int r = min(r0 + row, seg_end - 1);
-      la.p[j] = reinterpret_cast<const char*>(x + (size_t)(p.perm[r] / p.k) * H) + 16 * c;
+      la.p[j] = reinterpret_cast<const char*>(x + (size_t)p.ptok[r] * H) + 16 * c;
       const bf16* wrow = row < 128 ? wg + ((size_t)e * F + nt * 128 + row) * H : wu + ((size_t)e * F + nt * 128 + row - 128) * H;
       lb.p[j] = reinterpret_cast<const char*>(wrow) + 16 * c;
     }
@@ -379,9 +386,14 @@ __global__ __launch_bounds__(NTHR, 1) void k_gateup_bf16(FwdParams p) {
     for (int i = 0; i < 4; ++i) wrow[i] = p.weight[p.perm[min(r0 + 128 * wm + acc_m(i, lane), seg_end - 1)]];
     f32x16 acc[4][4];
     mainloop<false, false>(acc, smem, la, lb, H / KTILE, 128 * wm, bn);
-    // staged columns 0..63 hold gate columns f0.., 64..127 the matching up columns
+    // staged columns 0..63 hold gate columns f0.., 64..127 the matching up columns. After the row
+    // pass the gate columns hold hw (zero on rows past the segment), which is then written to the
+    // pair-contiguous copy hwT[f][qoff[e] + pair - offsets[e]] as well.
     float* slab = wave_slab(smem);
     const int f0 = nt * 128 + 64 * wn;
+    bf16* __restrict__ hwt = static_cast<bf16*>(p.hwt);
+    const int qend = p.qoff[e + 1];
+    const int colq = p.qoff[e] + (r0 - p.offsets[e]) + 128 * wm;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       stage_rows(slab, acc, i, lane);
@@ -390,8 +402,9 @@ __global__ __launch_bounds__(NTHR, 1) void k_gateup_bf16(FwdParams p) {
         const int rl = (lane >> 3) + 8 * s, c0 = (lane & 7) * 8;
         const float wt = __shfl(wrow[i], rl);
         const int r = r0 + 128 * wm + 32 * i + rl;
+        float hv[8];
         if (r < seg_end) {
-          float av[8], bv[8], hv[8];
+          float av[8], bv[8];
           read8(slab, rl, c0, av);
           read8(slab, rl, 64 + c0, bv);
 #pragma unroll
@@ -400,8 +413,15 @@ __global__ __launch_bounds__(NTHR, 1) void k_gateup_bf16(FwdParams p) {
           st16(abr, pack8(av));
           st16(abr + F, pack8(bv));
           st16(hw + (size_t)r * F + f0 + c0, pack8(hv));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) hv[e] = 0.f;
         }
+        *reinterpret_cast<float4*>(slab + rl * SLD + c0) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+        *reinterpret_cast<float4*>(slab + rl * SLD + c0 + 4) = make_float4(hv[4], hv[5], hv[6], hv[7]);
       }
+      const int colb = colq + 32 * i;
+      store_transposed(slab, lane, 64, [&](int c) { return colb < qend ? hwt + (size_t)(f0 + c) * p.qc + colb : nullptr; });
     }
   }
 }
@@ -454,7 +474,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_dh_bf16(BwdParams p) {
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       const int r = min(r0 + KOp::row_of(j), seg_end - 1);
-      la.p[j] = reinterpret_cast<const char*>(dy + (size_t)(p.perm[r] / p.k) * H) + 16 * KOp::chunk_of(j);
+      la.p[j] = reinterpret_cast<const char*>(dy + (size_t)p.ptok[r] * H) + 16 * KOp::chunk_of(j);
     }
     MNOp<WeightRows> lb;
     const char* wbase = reinterpret_cast<const char*>(static_cast<const bf16*>(p.wd) + (size_t)e * H * F + nt * TILE);
@@ -466,9 +486,15 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_dh_bf16(BwdParams p) {
     for (int i = 0; i < 4; ++i) wrow[i] = p.weight[p.perm[min(r0 + 128 * wm + acc_m(i, lane), seg_end - 1)]];
     f32x16 acc[4][4];
     mainloop<false, true>(acc, smem, la, lb, H / KTILE, 128 * wm, bn);
-    // u = dH' staged per 32 rows; each row's 128 columns are read by 16 lanes, 8 columns each
+    // u = dH' staged per 32 rows; each row's 128 columns are read by 16 lanes, 8 columns each. The
+    // row pass overwrites u with da and fills a second slab with db (zero on rows or columns past
+    // the segment); both then go to the pair-contiguous copy dabT.
     float* slab = wave_slab(smem);
+    float* slab2 = slab + 4 * SLAB;
+    bf16* __restrict__ dabt = static_cast<bf16*>(p.dabt);
     const int fq = nt * TILE + 128 * wn;
+    const int qend = p.qoff[e + 1];
+    const int colq = p.qoff[e] + (r0 - p.offsets[e]) + 128 * wm;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       stage_rows(slab, acc, i, lane);
@@ -477,9 +503,9 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_dh_bf16(BwdParams p) {
         const int rl = (lane >> 4) + 4 * s, c0 = (lane & 15) * 8;
         const float wt = __shfl(wrow[i], rl);
         const int r = r0 + 128 * wm + 32 * i + rl, f = fq + c0;
-        float gsum = 0.f;
+        float gsum = 0.f, da[8], db[8];
         if (r < seg_end && f < F) {
-          float u[8], av[8], bv[8], da[8], db[8];
+          float u[8], av[8], bv[8];
           read8(slab, rl, c0, u);
           const bf16* abr = ab + (size_t)r * 2 * F + f;
           unpack8(ld16(abr), av);
@@ -495,13 +521,27 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_dh_bf16(BwdParams p) {
           bf16* dabr = dab + (size_t)r * 2 * F + f;
           st16(dabr, pack8(da));
           st16(dabr + F, pack8(db));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) da[e] = db[e] = 0.f;
         }
+        *reinterpret_cast<float4*>(slab + rl * SLD + c0) = make_float4(da[0], da[1], da[2], da[3]);
+        *reinterpret_cast<float4*>(slab + rl * SLD + c0 + 4) = make_float4(da[4], da[5], da[6], da[7]);
+        *reinterpret_cast<float4*>(slab2 + rl * SLD + c0) = make_float4(db[0], db[1], db[2], db[3]);
+        *reinterpret_cast<float4*>(slab2 + rl * SLD + c0 + 4) = make_float4(db[4], db[5], db[6], db[7]);
         gsum += __shfl_xor(gsum, 1);
         gsum += __shfl_xor(gsum, 2);
         gsum += __shfl_xor(gsum, 4);
         gsum += __shfl_xor(gsum, 8);
         if (r < seg_end && (lane & 15) == 0) p.gpart[(size_t)(nt * 2 + wn) * p.rows + r] = gsum;
       }
+      const int colb = colq + 32 * i;
+      store_transposed(slab, lane, 128, [&](int c) {
+        return colb < qend && fq + c < F ? dabt + (size_t)(fq + c) * p.qc + colb : nullptr;
+      });
+      store_transposed(slab2, lane, 128, [&](int c) {
+        return colb < qend && fq + c < F ? dabt + (size_t)(F + fq + c) * p.qc + colb : nullptr;
+      });
     }
   }
 }
@@ -548,18 +588,21 @@ __global__ __launch_bounds__(NTHR, 1) void k_wgrad_down_bf16(BwdParams p) {
   const int e = lid / tpe, t = lid - e * tpe, mt = t / ntn, nt = t - mt * ntn;
   const int seg0 = p.offsets[e], seg_end = p.offsets[e + 1];
   MNOp<GatherRows> la;
-  la.rows = GatherRows{reinterpret_cast<const char*>(static_cast<const bf16*>(p.dy) + mt * TILE), p.perm,
-                       (size_t)H * 2, seg0, seg_end, p.k, {}};
+  la.rows = GatherRows{reinterpret_cast<const char*>(static_cast<const bf16*>(p.dy) + mt * TILE), p.ptok,
+                       (size_t)H * 2, seg0, seg_end, {}};
   la.zero = static_cast<const char*>(p.zeros);
   la.init(mt * TILE, H);
-  MNOp<PairRows> lb;
-  lb.rows = PairRows{reinterpret_cast<const char*>(static_cast<const bf16*>(p.hw) + nt * TILE), (size_t)F * 2, seg0,
-                     seg_end};
-  lb.zero = static_cast<const char*>(p.zeros);
-  lb.init(nt * TILE, F);
+  // B rows: hwT[n][qoff[e] ..], contiguous along the expert's pairs (zero-padded to 32)
+  KOp lb;
+  const bf16* hwt = static_cast<const bf16*>(p.hwt) + p.qoff[e];
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) {
+    const int n = min(nt * TILE + KOp::row_of(j), F - 1);
+    lb.p[j] = reinterpret_cast<const char*>(hwt + (size_t)n * p.qc) + 16 * KOp::chunk_of(j);
+  }
   const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
   f32x16 acc[4][4];
-  mainloop<true, true>(acc, smem, la, lb, (seg_end - seg0 + KTILE - 1) / KTILE, 128 * wm, bn);
+  mainloop<true, false>(acc, smem, la, lb, (seg_end - seg0 + KTILE - 1) / KTILE, 128 * wm, bn);
   bf16* __restrict__ out = static_cast<bf16*>(p.dwd) + (size_t)e * H * F;
   const int mq = mt * TILE + 128 * wm, nq = nt * TILE + 128 * wn;
   store_quadrant(smem, acc, lane, [&](int m) { return out + (size_t)(mq + m) * F + nq; }, F - nq);
@@ -573,19 +616,22 @@ __global__ __launch_bounds__(NTHR, 1) void k_wgrad_gateup_bf16(BwdParams p) {
   const int lid = xcd_logical_block(gridDim.x);
   const int e = lid / tpe, t = lid - e * tpe, mt = t / ntn, nt = t - mt * ntn;
   const int seg0 = p.offsets[e], seg_end = p.offsets[e + 1];
-  MNOp<PairRows> la;
-  la.rows = PairRows{reinterpret_cast<const char*>(static_cast<const bf16*>(p.dab) + mt * TILE), (size_t)F * 4, seg0,
-                     seg_end};
-  la.zero = static_cast<const char*>(p.zeros);
-  la.init(mt * TILE, 2 * F);
+  // A rows: dabT[m][qoff[e] ..], contiguous along the expert's pairs (zero-padded to 32)
+  KOp la;
+  const bf16* dabt = static_cast<const bf16*>(p.dabt) + p.qoff[e];
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) {
+    const int m = mt * TILE + KOp::row_of(j);
+    la.p[j] = reinterpret_cast<const char*>(dabt + (size_t)m * p.qc) + 16 * KOp::chunk_of(j);
+  }
   MNOp<GatherRows> lb;
-  lb.rows = GatherRows{reinterpret_cast<const char*>(static_cast<const bf16*>(p.x) + nt * TILE), p.perm,
-                       (size_t)H * 2, seg0, seg_end, p.k, {}};
+  lb.rows = GatherRows{reinterpret_cast<const char*>(static_cast<const bf16*>(p.x) + nt * TILE), p.ptok,
+                       (size_t)H * 2, seg0, seg_end, {}};
   lb.zero = static_cast<const char*>(p.zeros);
   lb.init(nt * TILE, H);
   const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
   f32x16 acc[4][4];
-  mainloop<true, true>(acc, smem, la, lb, (seg_end - seg0 + KTILE - 1) / KTILE, 128 * wm, bn);
+  mainloop<false, true>(acc, smem, la, lb, (seg_end - seg0 + KTILE - 1) / KTILE, 128 * wm, bn);
   bf16* __restrict__ dwg = static_cast<bf16*>(p.dwg) + (size_t)e * F * H;
   bf16* __restrict__ dwu = static_cast<bf16*>(p.dwu) + (size_t)e * F * H;
   const int mq = mt * TILE + 128 * wm, nq = nt * TILE + 128 * wn;

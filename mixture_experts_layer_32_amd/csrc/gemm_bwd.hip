@@ -46,11 +46,11 @@ struct GateUpRows {
 template <class T>
 struct GatherRows {
   const T* base;  // tensor + c0
-  const int* perm;
-  int seg0, seg_end, topk, ld;
+  const int* ptok;
+  int seg0, seg_end, ld;
   __device__ __forceinline__ const char* row(int k) const {
     const int r = seg0 + k;
-    return r < seg_end ? reinterpret_cast<const char*>(base + (size_t)(perm[r] / topk) * ld) : nullptr;
+    return r < seg_end ? reinterpret_cast<const char*>(base + (size_t)ptok[r] * ld) : nullptr;
   }
 };
 
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dh(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = r0 + (tid >> 3) + 32 * i;
-      la.p[i] = r < seg_end ? reinterpret_cast<const char*>(dy + (size_t)(p.perm[r] / p.k) * H) + (tid & 7) * 16
+      la.p[i] = r < seg_end ? reinterpret_cast<const char*>(dy + (size_t)p.ptok[r] * H) + (tid & 7) * 16
                             : nullptr;
     }
     MNLoader<T, 128, WdRows<T>> lb;
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_wgrad_down(BwdParams p) {
   const int seg0 = p.offsets[e], seg_end = p.offsets[e + 1];
   const int nk = (seg_end - seg0 + Elem<T>::BK - 1) / Elem<T>::BK;
   MNLoader<T, 128, GatherRows<T>> la;
-  la.src = GatherRows<T>{static_cast<const T*>(p.dy) + mt * 128, p.perm, seg0, seg_end, p.k, H};
+  la.src = GatherRows<T>{static_cast<const T*>(p.dy) + mt * 128, p.ptok, seg0, seg_end, H};
   la.init(tid);
   MNLoader<T, 128, PairRows<T>> lb;
   lb.src = PairRows<T>{static_cast<const T*>(p.hw) + nt * 128, seg0, seg_end, F};
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_wgrad_gateup(BwdParams p) {
   la.src = PairRows<T>{static_cast<const T*>(p.dab) + mt * 128, seg0, seg_end, 2 * F};
   la.init(tid);
   MNLoader<T, 128, GatherRows<T>> lb;
-  lb.src = GatherRows<T>{static_cast<const T*>(p.x) + nt * 128, p.perm, seg0, seg_end, p.k, H};
+  lb.src = GatherRows<T>{static_cast<const T*>(p.x) + nt * 128, p.ptok, seg0, seg_end, H};
   lb.init(tid);
   const int brow[4] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
   f32x4 acc[4][4];

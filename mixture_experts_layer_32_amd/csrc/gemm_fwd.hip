@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gateup(FwdParams p) {
     for (int i = 0; i < 4; ++i) {
       const int row = (tid >> 3) + 32 * i;
       const int r = r0 + row;
-      la.p[i] = r < seg_end ? reinterpret_cast<const char*>(x + (size_t)(p.perm[r] / p.k) * H) + (tid & 7) * 16
+      la.p[i] = r < seg_end ? reinterpret_cast<const char*>(x + (size_t)p.ptok[r] * H) + (tid & 7) * 16
                             : nullptr;
       const T* wrow = row < 64 ? wg + ((size_t)e * F + nt * 64 + row) * H
                                : wu + ((size_t)e * F + nt * 64 + row - 64) * H;

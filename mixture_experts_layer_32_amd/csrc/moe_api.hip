@@ -29,6 +29,8 @@ Layout make_layout(const moe_desc& d) {
   L.mtile2_cap = (int)(L.rows / kBM2) + d.E_local + 1;
   L.np = d.mode == MOE_MODE_FP32 ? d.F / 64 : 2 * ((d.F + 255) / 256);
   L.elem = d.mode == MOE_MODE_FP32 ? 4 : 2;
+  // transposed copies exist only on the bf16 engine; columns: every expert padded to 32
+  L.qc = d.mode == MOE_MODE_FP32 ? 0 : ((L.rows + 32 * (int64_t)d.E_local + 31) & ~int64_t(31));
   const size_t rows = (size_t)L.rows, El = (size_t)d.E_local;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -41,14 +43,17 @@ Layout make_layout(const moe_desc& d) {
   L.counts = take(El * 4);
   L.offsets = take((El + 1) * 4);
   L.perm = take(rows * 4);
+  L.ptok = take(rows * 4);
   L.pair_pos = take(rows * 4);
   L.mtile = take((size_t)L.mtile_cap * 8);
   L.num_mtiles = take(4);
   L.mtile2 = take((size_t)L.mtile2_cap * 8);
   L.num_mtiles2 = take(4);
   L.zeros = take(kZeroBytes);
+  L.qoff = take((El + 1) * 4);
   L.ab = take(rows * 2 * d.F * L.elem);
   L.hw = take(rows * d.F * L.elem);
+  L.hwt = take((size_t)L.qc * d.F * 2);
   L.saved_total = off;
 
   off = 0;
@@ -63,6 +68,7 @@ Layout make_layout(const moe_desc& d) {
   L.dab = take(rows * 2 * d.F * L.elem);
   L.gpart = take((size_t)L.np * rows * 4);
   L.dxp = take(rows * d.H * L.elem);
+  L.dabt = take((size_t)L.qc * 2 * d.F * 2);
   L.bwd_total = off;
   return L;
 }
@@ -224,12 +230,14 @@ static RouteParams route_params(const moe_desc& d, const Layout& L, const float*
   p.counts = reinterpret_cast<int*>(sv + L.counts);
   p.offsets = reinterpret_cast<int*>(sv + L.offsets);
   p.perm = reinterpret_cast<int*>(sv + L.perm);
+  p.ptok = reinterpret_cast<int*>(sv + L.ptok);
   p.pair_pos = reinterpret_cast<int*>(sv + L.pair_pos);
   p.mtile = reinterpret_cast<int2*>(sv + L.mtile);
   p.num_mtiles = reinterpret_cast<int*>(sv + L.num_mtiles);
   p.mtile2 = reinterpret_cast<int2*>(sv + L.mtile2);
   p.num_mtiles2 = reinterpret_cast<int*>(sv + L.num_mtiles2);
   p.zeros = reinterpret_cast<uint4*>(sv + L.zeros);
+  p.qoff = reinterpret_cast<int*>(sv + L.qoff);
   p.blk_mask = reinterpret_cast<unsigned long long*>(w + L.blk_mask);
   p.blk_count = reinterpret_cast<int*>(w + L.blk_count);
   p.blk_prefix = reinterpret_cast<int*>(w + L.blk_prefix);
@@ -278,12 +286,16 @@ moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits, const 
   fp.wu = w_up;
   fp.wd = w_down;
   fp.perm = rp.perm;
+  fp.ptok = rp.ptok;
   fp.offsets = rp.offsets;
   fp.mtile = rp.mtile;
   fp.num_mtiles = rp.num_mtiles;
   fp.mtile2 = rp.mtile2;
   fp.num_mtiles2 = rp.num_mtiles2;
   fp.zeros = rp.zeros;
+  fp.qoff = rp.qoff;
+  fp.qc = L.qc;
+  fp.hwt = sv + L.hwt;
   fp.weight = rp.weight;
   fp.ab = sv + L.ab;
   fp.hw = sv + L.hw;
@@ -334,6 +346,7 @@ moe_status moe_bwd(const moe_desc* d, const void* dy, const void* x, const void*
   p.idx = reinterpret_cast<const int*>(sv + L.idx);
   p.weight = reinterpret_cast<const float*>(sv + L.weight);
   p.perm = reinterpret_cast<const int*>(sv + L.perm);
+  p.ptok = reinterpret_cast<const int*>(sv + L.ptok);
   p.offsets = reinterpret_cast<const int*>(sv + L.offsets);
   p.pair_pos = reinterpret_cast<const int*>(sv + L.pair_pos);
   p.mtile = reinterpret_cast<const int2*>(sv + L.mtile);
@@ -341,8 +354,12 @@ moe_status moe_bwd(const moe_desc* d, const void* dy, const void* x, const void*
   p.mtile2 = reinterpret_cast<const int2*>(sv + L.mtile2);
   p.num_mtiles2 = reinterpret_cast<const int*>(sv + L.num_mtiles2);
   p.zeros = sv + L.zeros;
+  p.qoff = reinterpret_cast<const int*>(sv + L.qoff);
+  p.qc = L.qc;
   p.ab = sv + L.ab;
   p.hw = sv + L.hw;
+  p.hwt = sv + L.hwt;
+  p.dabt = w + L.dabt;
   p.dab = w + L.dab;
   p.gpart = reinterpret_cast<float*>(w + L.gpart);
   p.dxp = w + L.dxp;

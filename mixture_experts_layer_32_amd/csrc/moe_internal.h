@@ -24,12 +24,13 @@ struct Layout {
   int np;              // partial sums of g per pair: F / 64 (fp32 engine), 2*ceil(F/256) (bf16 engine)
   size_t elem;         // bytes per stored element (4 or 2)
   // saved
-  size_t idx, weight, counts, offsets, perm, pair_pos, mtile, num_mtiles, mtile2, num_mtiles2, zeros, ab, hw,
-      saved_total;
+  int64_t qc;          // row stride of the pair-contiguous transposed copies (bf16 engine)
+  size_t idx, weight, counts, offsets, perm, ptok, pair_pos, mtile, num_mtiles, mtile2, num_mtiles2, zeros, qoff, ab, hw,
+      hwt, saved_total;
   // forward workspace
   size_t blk_mask, blk_count, blk_prefix, o, fwd_total;
   // backward workspace
-  size_t dab, gpart, dxp, bwd_total;
+  size_t dab, gpart, dxp, dabt, bwd_total;
 };
 
 Layout make_layout(const moe_desc& d);
@@ -45,12 +46,14 @@ struct RouteParams {
   int* counts;
   int* offsets;
   int* perm;
+  int* ptok;
   int* pair_pos;
   int2* mtile;
   int* num_mtiles;
   int2* mtile2;
   int* num_mtiles2;
   uint4* zeros;
+  int* qoff;
   unsigned long long* blk_mask;
   int* blk_count;
   int* blk_prefix;
@@ -66,15 +69,19 @@ struct FwdParams {
   const void* wu;
   const void* wd;
   const int* perm;
+  const int* ptok;
   const int* offsets;
   const int2* mtile;
   const int* num_mtiles;
   const int2* mtile2;
   const int* num_mtiles2;
   const void* zeros;
+  const int* qoff;
+  int64_t qc;
   const float* weight;
   void* ab;
   void* hw;
+  void* hwt;
   void* o;
   const int* pair_pos;
   void* y;
@@ -94,6 +101,7 @@ struct BwdParams {
   const int* idx;
   const float* weight;
   const int* perm;
+  const int* ptok;
   const int* offsets;
   const int* pair_pos;
   const int2* mtile;
@@ -101,9 +109,13 @@ struct BwdParams {
   const int2* mtile2;
   const int* num_mtiles2;
   const void* zeros;
+  const int* qoff;
+  int64_t qc;
   const void* ab;
   const void* hw;
+  const void* hwt;
   void* dab;
+  void* dabt;
   float* gpart;
   void* dxp;
   void* dx;

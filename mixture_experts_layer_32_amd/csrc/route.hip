@@ -13,7 +13,8 @@
 //                    wave-wide (value desc, index asc) argmax. Per block and local expert, a
 //                    64-bit mask of the tokens that chose it.
 //   k_route_colscan  one block per local expert: exclusive scan of the per-block counts.
-//   k_route_offsets  one block: expert offsets, M-tile table, tile count.
+//   k_route_offsets  one block: expert offsets, M-tile tables and counts, and the offsets of the
+//                    experts' 32-column-padded segments in the pair-contiguous transposed copies.
 //   k_route_scatter  one thread per pair: position = expert offset + earlier blocks' count +
 //                    popcount of earlier tokens in the block's mask.
 #include <math.h>
@@ -136,18 +137,22 @@ __global__ __launch_bounds__(512) void k_route_offsets(RouteParams p) {
   const int e = threadIdx.x;
   const int c = e < p.El ? p.counts[e] : 0;
   const int nt = (c + kBM - 1) / kBM, nt2 = (c + kBM2 - 1) / kBM2;
-  int tot_c, tot_t, tot_t2;
+  const int c32 = (c + 31) & ~31;
+  int tot_c, tot_t, tot_t2, tot_q;
   const int inc_c = block_incl_scan<512>(c, lds, tot_c);
   const int inc_t = block_incl_scan<512>(nt, lds, tot_t);
   const int inc_t2 = block_incl_scan<512>(nt2, lds, tot_t2);
+  const int inc_q = block_incl_scan<512>(c32, lds, tot_q);
   if (e < p.El) {
     const int off = inc_c - c, t0 = inc_t - nt, t2 = inc_t2 - nt2;
     p.offsets[e] = off;
+    p.qoff[e] = inc_q - c32;
     for (int i = 0; i < nt; ++i) p.mtile[t0 + i] = make_int2(e, off + i * kBM);
     for (int i = 0; i < nt2; ++i) p.mtile2[t2 + i] = make_int2(e, off + i * kBM2);
   }
   if (e == 0) {
     p.offsets[p.El] = tot_c;
+    p.qoff[p.El] = tot_q;
     *p.num_mtiles = tot_t;
     *p.num_mtiles2 = tot_t2;
   }
@@ -168,6 +173,7 @@ __global__ __launch_bounds__(256) void k_route_scatter(RouteParams p) {
   const unsigned long long before = p.blk_mask[cell] & ((1ull << tl) - 1ull);
   const int pos = p.offsets[el] + p.blk_prefix[cell] + __popcll(before);
   p.perm[pos] = (int)q;
+  p.ptok[pos] = (int)t;
   p.pair_pos[q] = pos;
 }
 
