@@ -49,26 +49,33 @@ def hbm_bytes(name, cfg, P, elem):
     return None
 
 
-def cpu_baseline(cfg, L, n_experts=16):
-    import numpy as np
+def cpu_baseline(cfg, L, min_seconds=10.0, group=16):
+    """The float64 oracle, as it stands, on whole expert shares of the workload (16 experts at a
+    time, all tokens routed) until at least min_seconds of host time have been spent."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 0) for i in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count()
-    sl = slice(0, n_experts)
-    args = dict(x=L["x"], logits=L["logits"], wg=L["wg"][sl], wu=L["wu"][sl], wd=L["wd"][sl], k=cfg.k, e0=0,
-                e_local=n_experts)
     t0 = time.perf_counter()
-    _, r = oracle.forward(**args)
-    oracle.backward(dy=L["dy"], **args)
+    P, done = 0, 0
+    while done < cfg.el:
+        n = min(group, cfg.el - done)
+        sl = slice(done, done + n)
+        args = dict(x=L["x"], logits=L["logits"], wg=L["wg"][sl], wu=L["wu"][sl], wd=L["wd"][sl], k=cfg.k,
+                    e0=cfg.e0 + done, e_local=n)
+        _, r = oracle.forward(**args)
+        oracle.backward(dy=L["dy"], **args)
+        P += int(r["counts"].sum())
+        done += n
+        if time.perf_counter() - t0 >= min_seconds:
+            break
     dt = time.perf_counter() - t0
-    P = int(r["counts"].sum())
     fl = 18.0 * cfg.H * cfg.F * P
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"experts 0-{n_experts - 1} of {cfg.name} ({P} routed pairs), float64 forward+backward, "
-                      f"{dt:.1f} s wall"}
+            "sample": f"experts {cfg.e0}-{cfg.e0 + done - 1} of {cfg.name} ({P} routed pairs), float64 forward+"
+                      f"backward, {dt:.1f} s wall"}
 
 
 def main():
@@ -79,6 +86,8 @@ def main():
     ap.add_argument("--config", default="qwen3_30b_a3b")
     ap.add_argument("--mode", default=None, help="fp32 or bf16 (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one plain 1 GiB device copy before the timed steps (reference for HBM counters)")
     a = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
@@ -114,6 +123,12 @@ def main():
         step()
     torch.cuda.synchronize()
     P = int(layer.routing()["offsets"][-1])
+    if a.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").normal_()
+        dst = torch.empty_like(src)
+        dst.copy_(src)          # 1 GiB read + 1 GiB write, a plain copy kernel
+        torch.cuda.synchronize()
+        del src, dst
 
     # timed region: K steps, forward/backward split by events on the library's stream
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),

@@ -99,6 +99,8 @@ __device__ __forceinline__ int mn_krow(int j) { return wave_id() * 8 + 2 * j + (
 struct KOp {
   const char* p[LOADS];   // global address of this lane's chunk in K-tile 0
   __device__ __forceinline__ void prefetch(int) {}
+  __device__ __forceinline__ void prologue_prefetch(int) {}
+  __device__ __forceinline__ void prologue_issue(char* tile, int kt) const { issue(tile, kt); }
   __device__ __forceinline__ void issue(char* tile, int kt) const {
     const int w = wave_id();
 #pragma unroll
@@ -131,6 +133,17 @@ struct MNOp {
       gl2lds(r && coff[j] >= 0 ? r + coff[j] : zero, tile + (w * LOADS + j) * 1024);
     }
   }
+  // prologue: the row indices of the first STAGES K-tiles are fetched together (kt is a
+  // compile-time slot after unrolling), then the tiles are issued
+  __device__ __forceinline__ void prologue_prefetch(int kt) { rows.prologue_prefetch(kt); }
+  __device__ __forceinline__ void prologue_issue(char* tile, int kt) const {
+    const int w = wave_id();
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const char* r = rows.prologue_row(kt, j);
+      gl2lds(r && coff[j] >= 0 ? r + coff[j] : zero, tile + (w * LOADS + j) * 1024);
+    }
+  }
 };
 
 // contraction rows of a weight matrix: row k at base + k*ld (k < split) or base2 + (k-split)*ld
@@ -140,10 +153,12 @@ struct WeightRows {
   size_t ld;
   int split;
   __device__ __forceinline__ void prefetch(int) {}
+  __device__ __forceinline__ void prologue_prefetch(int) {}
   __device__ __forceinline__ const char* row(int kt, int j) const {
     const int k = kt * KTILE + mn_krow(j);
     return k < split ? base + (size_t)k * ld : base2 + (size_t)(k - split) * ld;
   }
+  __device__ __forceinline__ const char* prologue_row(int kt, int j) const { return row(kt, j); }
 };
 
 // contraction rows = an expert's pairs, as the token rows of a [T, ld] tensor (ptok maps a
@@ -154,15 +169,27 @@ struct GatherRows {
   size_t ld;
   int seg0, seg_end;
   int tok[8];
+  int tokp[STAGES][8];   // prologue K-tiles
   __device__ __forceinline__ void prefetch(int kt) {
     const int r0 = seg0 + kt * KTILE + wave_id() * 8;
 #pragma unroll
     for (int i = 0; i < 8; ++i) tok[i] = ptok[min(r0 + i, seg_end - 1)];
   }
+  __device__ __forceinline__ void prologue_prefetch(int kt) {
+    const int r0 = seg0 + kt * KTILE + wave_id() * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tokp[kt][i] = ptok[min(r0 + i, seg_end - 1)];
+  }
   __device__ __forceinline__ const char* row(int kt, int j) const {
     const int hi = (threadIdx.x & 63) >> 5;
     const int r = seg0 + kt * KTILE + mn_krow(j);
     const int t = hi ? tok[2 * j + 1] : tok[2 * j];
+    return r < seg_end ? base + (size_t)t * ld : nullptr;
+  }
+  __device__ __forceinline__ const char* prologue_row(int kt, int j) const {
+    const int hi = (threadIdx.x & 63) >> 5;
+    const int r = seg0 + kt * KTILE + mn_krow(j);
+    const int t = hi ? tokp[kt][2 * j + 1] : tokp[kt][2 * j];
     return r < seg_end ? base + (size_t)t * ld : nullptr;
   }
 };
@@ -216,11 +243,14 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], char* smem, LA& la
   block_sync();   // and every wave is done reading its epilogue staging slab
 #pragma unroll
   for (int s = 0; s < STAGES; ++s) {
+    la.prologue_prefetch(s);
+    lb.prologue_prefetch(s);
+  }
+#pragma unroll
+  for (int s = 0; s < STAGES; ++s) {
     if (s < nk) {
-      la.prefetch(s);
-      lb.prefetch(s);
-      la.issue(smem + s * STB, s);
-      lb.issue(smem + s * STB + OPB, s);
+      la.prologue_issue(smem + s * STB, s);
+      lb.prologue_issue(smem + s * STB + OPB, s);
     }
   }
   if (STAGES < nk) {
@@ -498,6 +528,16 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_dh_bf16(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       stage_rows(slab, acc, i, lane);
+      // the 8 rows of this lane: gather every a/b vector first so that the loads overlap
+      uint4 araw[8], braw[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int rl = (lane >> 4) + 4 * s, c0 = (lane & 15) * 8;
+        const int r = r0 + 128 * wm + 32 * i + rl, f = fq + c0;
+        const bf16* abr = ab + (size_t)min(r, seg_end - 1) * 2 * F + min(f, F - 8);
+        araw[s] = ld16(abr);
+        braw[s] = ld16(abr + F);
+      }
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const int rl = (lane >> 4) + 4 * s, c0 = (lane & 15) * 8;
@@ -507,9 +547,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_dh_bf16(BwdParams p) {
         if (r < seg_end && f < F) {
           float u[8], av[8], bv[8];
           read8(slab, rl, c0, u);
-          const bf16* abr = ab + (size_t)r * 2 * F + f;
-          unpack8(ld16(abr), av);
-          unpack8(ld16(abr + F), bv);
+          unpack8(araw[s], av);
+          unpack8(braw[s], bv);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float sg = sigmoidf_(av[e]), si = av[e] * sg;
@@ -584,7 +623,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_wgrad_down_bf16(BwdParams p) {
   MOE_SMEM
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
   const int H = p.H, F = p.F, ntn = (F + TILE - 1) / TILE, tpe = (H / TILE) * ntn;
-  const int lid = xcd_logical_block(gridDim.x);
+  const XcdRange xr = xcd_range(p.El * tpe);
+  for (int lid = xr.first; lid < xr.end; lid += xr.stride) {
   const int e = lid / tpe, t = lid - e * tpe, mt = t / ntn, nt = t - mt * ntn;
   const int seg0 = p.offsets[e], seg_end = p.offsets[e + 1];
   MNOp<GatherRows> la;
@@ -606,6 +646,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_wgrad_down_bf16(BwdParams p) {
   bf16* __restrict__ out = static_cast<bf16*>(p.dwd) + (size_t)e * H * F;
   const int mq = mt * TILE + 128 * wm, nq = nt * TILE + 128 * wn;
   store_quadrant(smem, acc, lane, [&](int m) { return out + (size_t)(mq + m) * F + nq; }, F - nq);
+  }
 }
 
 // backward: [dW_gate; dW_up][e] (2F x H) = sum over the expert's pairs of [da; db]_r x_t^T
@@ -613,7 +654,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_wgrad_gateup_bf16(BwdParams p) {
   MOE_SMEM
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
   const int H = p.H, F = p.F, ntn = H / TILE, tpe = (2 * F / TILE) * ntn;
-  const int lid = xcd_logical_block(gridDim.x);
+  const XcdRange xr = xcd_range(p.El * tpe);
+  for (int lid = xr.first; lid < xr.end; lid += xr.stride) {
   const int e = lid / tpe, t = lid - e * tpe, mt = t / ntn, nt = t - mt * ntn;
   const int seg0 = p.offsets[e], seg_end = p.offsets[e + 1];
   // A rows: dabT[m][qoff[e] ..], contiguous along the expert's pairs (zero-padded to 32)
@@ -639,6 +681,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_wgrad_gateup_bf16(BwdParams p) {
     const int mm = mq + m;
     return (mm < F ? dwg + (size_t)mm * H : dwu + (size_t)(mm - F) * H) + nq;
   }, 128);
+  }
 }
 
 }  // namespace
@@ -662,14 +705,12 @@ hipError_t launch_backward_gemms_bf16(const BwdParams& p, int grid, hipStream_t 
   k_bwd_dh_bf16<<<grid, NTHR, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   prof_mark_end(s);
-  const int nb_wd = p.El * (p.H / TILE) * ((p.F + TILE - 1) / TILE);
   prof_mark_begin("gemm_wgrad_down", s);
-  k_wgrad_down_bf16<<<nb_wd, NTHR, 0, s>>>(p);
+  k_wgrad_down_bf16<<<grid, NTHR, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   prof_mark_end(s);
-  const int nb_wgu = p.El * (2 * p.F / TILE) * (p.H / TILE);
   prof_mark_begin("gemm_wgrad_gateup", s);
-  k_wgrad_gateup_bf16<<<nb_wgu, NTHR, 0, s>>>(p);
+  k_wgrad_gateup_bf16<<<grid, NTHR, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   prof_mark_end(s);
   prof_mark_begin("gemm_dgrad_x", s);

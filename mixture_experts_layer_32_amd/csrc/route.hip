@@ -9,9 +9,11 @@
 // sequence of fp32 operations, so runs are bitwise reproducible.
 //
 // Kernels (one stream, no host round trip):
-//   k_route_topk     64 tokens per block, one wavefront per token at a time. k rounds of a
-//                    wave-wide (value desc, index asc) argmax. Per block and local expert, a
-//                    64-bit mask of the tokens that chose it.
+//   k_route_topk4    k <= 8: 64 tokens per block, 4 lanes per token; each lane keeps a sorted list
+//                    of its quarter of the experts (value desc, index asc), two shuffle steps merge
+//                    the lists.
+//   k_route_topk_wave  k > 8: one wavefront per token, k rounds of a wave-wide argmax.
+//                    Both write, per block and local expert, a 64-bit mask of the tokens that chose it.
 //   k_route_colscan  one block per local expert: exclusive scan of the per-block counts.
 //   k_route_offsets  one block: expert offsets, M-tile tables and counts, and the offsets of the
 //                    experts' 32-column-padded segments in the pair-contiguous transposed copies.
@@ -50,8 +52,101 @@ __device__ __forceinline__ int block_incl_scan(int v, int* lds, int& total) {
   return v + add;
 }
 
+// Insert candidate (cv, ce) into the list t[0..KMAX) kept sorted by better(); the loser of each
+// compare-exchange moves on. Branchless.
+template <int KMAX>
+__device__ __forceinline__ void topk_insert(float (&tv)[KMAX], int (&ti)[KMAX], float cv, int ce) {
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const bool b = better(cv, ce, tv[j], ti[j]);
+    const float nv = b ? cv : tv[j];
+    const int ni = b ? ce : ti[j];
+    cv = b ? tv[j] : cv;
+    ce = b ? ti[j] : ce;
+    tv[j] = nv;
+    ti[j] = ni;
+  }
+}
+
+// k <= 8: 64 tokens per block, 4 lanes per token. Lane q keeps the best KMAX of experts q, q+4, q+8, ...;
+// two butterfly steps merge the four lists, after which every lane of the token holds its top k.
+template <int KMAX>
+__global__ __launch_bounds__(256) void k_route_topk4(RouteParams p) {
+  __shared__ unsigned long long mask[kMaxExperts];
+  const int tid = threadIdx.x, tl = tid >> 2, q = tid & 3;
+  for (int e = tid; e < p.El; e += 256) mask[e] = 0ull;
+  __syncthreads();
+  const int64_t t = (int64_t)blockIdx.x * kRouteTokens + tl;
+  if (t < p.T) {
+    float tv[KMAX];
+    int ti[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      tv[j] = -INFINITY;
+      ti[j] = 0x7fffffff;
+    }
+    const float* row = p.logits + t * p.E;
+#pragma unroll 1
+    for (int e = q; e < p.E; e += 4) topk_insert<KMAX>(tv, ti, row[e], e);
+    // merge with the partner lane's list: the better of tv[j] and the partner's [KMAX-1-j]
+    // leaves the top KMAX of both lists as a bitonic sequence, which three half-cleaner stages sort
+#pragma unroll
+    for (int step = 1; step <= 2; step <<= 1) {
+      float ov[KMAX];
+      int oi[KMAX];
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        ov[j] = __shfl_xor(tv[j], step);
+        oi[j] = __shfl_xor(ti[j], step);
+      }
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        const bool b = better(tv[j], ti[j], ov[KMAX - 1 - j], oi[KMAX - 1 - j]);
+        tv[j] = b ? tv[j] : ov[KMAX - 1 - j];
+        ti[j] = b ? ti[j] : oi[KMAX - 1 - j];
+      }
+#pragma unroll
+      for (int d = KMAX / 2; d >= 1; d >>= 1)
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+          if ((j & d) == 0) {
+            const bool b = better(tv[j], ti[j], tv[j + d], ti[j + d]);
+            const float v0 = b ? tv[j] : tv[j + d], v1 = b ? tv[j + d] : tv[j];
+            const int i0 = b ? ti[j] : ti[j + d], i1 = b ? ti[j + d] : ti[j];
+            tv[j] = v0;
+            tv[j + d] = v1;
+            ti[j] = i0;
+            ti[j + d] = i1;
+          }
+    }
+    // renormalised softmax over the chosen k, summed in slot order
+    float z[KMAX], sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      z[j] = j < p.k ? expf(tv[j] - tv[0]) : 0.f;
+      sum += z[j];
+    }
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j < p.k && (j & 3) == q) {
+        p.idx[t * p.k + j] = ti[j];
+        p.weight[t * p.k + j] = z[j] / sum;
+        const int el = ti[j] - p.e0;
+        if (el >= 0 && el < p.El) atomicOr(&mask[el], 1ull << tl);
+      }
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < p.El; e += 256) {
+    const size_t qq = (size_t)blockIdx.x * p.El + e;
+    p.blk_mask[qq] = mask[e];
+    p.blk_count[qq] = __popcll(mask[e]);
+  }
+}
+
+// k > 8: one wavefront per token, k rounds of a wave-wide (value desc, index asc) argmax.
 template <int PER_LANE>
-__global__ __launch_bounds__(256) void k_route_topk(RouteParams p) {
+__global__ __launch_bounds__(256) void k_route_topk_wave(RouteParams p) {
   __shared__ unsigned long long mask[kMaxExperts];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   for (int e = tid; e < p.El; e += 256) mask[e] = 0ull;
@@ -179,12 +274,13 @@ __global__ __launch_bounds__(256) void k_route_scatter(RouteParams p) {
 
 hipError_t launch_route(const RouteParams& p, hipStream_t s) {
   hipError_t err;
-  const int per_lane = (p.E + 63) / 64;
   prof_mark_begin("route_topk", s);
-  if (per_lane <= 1) k_route_topk<1><<<p.nblk, 256, 0, s>>>(p);
-  else if (per_lane <= 2) k_route_topk<2><<<p.nblk, 256, 0, s>>>(p);
-  else if (per_lane <= 4) k_route_topk<4><<<p.nblk, 256, 0, s>>>(p);
-  else k_route_topk<8><<<p.nblk, 256, 0, s>>>(p);
+  const int per_lane = (p.E + 63) / 64;
+  if (p.k <= 8) k_route_topk4<8><<<p.nblk, 256, 0, s>>>(p);
+  else if (per_lane <= 1) k_route_topk_wave<1><<<p.nblk, 256, 0, s>>>(p);
+  else if (per_lane <= 2) k_route_topk_wave<2><<<p.nblk, 256, 0, s>>>(p);
+  else if (per_lane <= 4) k_route_topk_wave<4><<<p.nblk, 256, 0, s>>>(p);
+  else k_route_topk_wave<8><<<p.nblk, 256, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   prof_mark_end(s);
   prof_mark_begin("route_colscan", s);
