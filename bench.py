@@ -14,7 +14,7 @@ Printed on one JSON line:
   value         whole-layer TFLOP/s = 18*H*F*pairs / (forward+backward time)
   roofline      the dominant kernel: algorithmic flops per launch / its mean duration (HIP events
                 on the launch stream) against the bf16 MFMA peak
-  cpu_baseline  the float64 oracle on a bounded sample (the pairs of 16 experts), host cores
+  cpu_baseline  the float64 oracle on whole expert shares, at least 10 s of host time
 
     python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
 """
@@ -47,6 +47,22 @@ def hbm_bytes(name, cfg, P, elem):
     if name == "route_topk":
         return T * E * 4 + T * k * 8
     return None
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, if it was
+    taken on this workload and the GEMM source has not changed since (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_bf16_hbm_traffic.json")
+    try:
+        doc = json.load(open(path))
+        src = open(os.path.join(ROOT, doc["kernel_source"]), "rb").read()
+        if hashlib.sha256(src).hexdigest() != doc["kernel_source_sha256"]:
+            return None
+        k = doc["kernels"][kernel]
+        return round(k["hbm_read_bytes"] + k["hbm_write_bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(cfg, L, min_seconds=10.0, group=16):
@@ -179,11 +195,14 @@ def main():
     if dom in GEMM_FLOPS_PER_PAIR:
         ach = GEMM_FLOPS_PER_PAIR[dom] * cfg.H * cfg.F * P / (davg * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4), "traffic": None, "kernel": dom, "avg_ms": round(davg, 5)}
+                "frac": round(ach / peak, 4), "traffic": measured_traffic(dom, cfg.name) if mode == "bf16" else None,
+                "traffic_unit": "bytes per launch (HBM read + write, rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
+                "kernel": dom, "avg_ms": round(davg, 5)}
     else:
         ach = hbm_bytes(dom, cfg, P, 4 if mode == "fp32" else 2) / (davg * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom, "avg_ms": round(davg, 5)}
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic(dom, cfg.name),
+                "kernel": dom, "avg_ms": round(davg, 5)}
 
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
