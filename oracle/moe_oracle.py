@@ -32,10 +32,26 @@ Parity status: every function here is pinned by tests that do not go through thi
  * torch's own functional ops and autograd;
  * central finite differences.
 No function is "parity unpinned".
+
+MX precision modes (mode="mxfp8": both passes; mode="fp8_bwd": backward only). Every GEMM operand
+is replaced by its MXFP8 round trip (oracle/mx.py) along that GEMM's contraction axis:
+    gate/up        x rows and W_gate, W_up along H
+    down           (w * h) along F; W_down along F
+    dH             dY rows along H; W_down along H
+    down wgrad     dY and (w * h) along the expert's pairs, in the stable pair order, in blocks of 32
+                   (the last block zero-padded)
+    gate/up wgrad  da, db and x along the expert's pairs
+    dgrad x        da, db along F; W_gate, W_up along F
+Routing, softmax, SwiGLU, the router gradient and the combines stay exact.
+Reading: the routing weight enters before the down projection (o' = W_down (w h)). Without
+quantisation that is the same sum as weighting the expert output. In MX modes it fixes which
+operand is quantised.
 """
 from __future__ import annotations
 
 import numpy as np
+
+from . import mx
 
 
 def _f64(a):
@@ -129,6 +145,20 @@ def expert_forward(xr, wg_e, wu_e, wd_e):
     return a, b, h, o
 
 
+def _qz(on, v, axis):
+    return mx.mx_quantize(v, axis) if on else _f64(v)
+
+
+def expert_forward_q(xr, wr, wg_e, wu_e, wd_e, quant):
+    """One expert with optional MXFP8 operands (quant=True). Returns a, b, h and o' = W_down (w h)."""
+    xq = _qz(quant, xr, 1)
+    a = xq @ _qz(quant, wg_e, 1).T
+    b = xq @ _qz(quant, wu_e, 1).T
+    h = silu(a) * b
+    o = _qz(quant, wr[:, None] * h, 1) @ _qz(quant, wd_e, 1).T
+    return a, b, h, o
+
+
 def _expert_rows(r, i):
     """(pair ids, token ids, weights) of local expert i, in the stable pair order."""
     pairs = r["perm"][r["offsets"][i]:r["offsets"][i + 1]]
@@ -138,7 +168,7 @@ def _expert_rows(r, i):
 # ----------------------------------------------------------------------------------------------
 # forward
 
-def forward(x, logits, wg, wu, wd, k, e0=0, e_local=None):
+def forward(x, logits, wg, wu, wd, k, e0=0, e_local=None, mode=None):
     """y[t] = sum over the local chosen slots j of w_tj * FFN_{S_tj}(x_t).
 
     wg, wu [El,F,H] and wd [El,H,F] hold the local experts e0..e0+El-1. A token with no local
@@ -153,15 +183,19 @@ def forward(x, logits, wg, wu, wd, k, e0=0, e_local=None):
         pairs, toks, wr = _expert_rows(r, i)
         if pairs.size == 0:
             continue
-        _, _, _, o = expert_forward(x[toks], wg[i], wu[i], wd[i])
-        y[toks] += wr[:, None] * o          # a token meets an expert at most once
+        if mode == "mxfp8":
+            _, _, _, o = expert_forward_q(x[toks], wr, wg[i], wu[i], wd[i], True)
+            y[toks] += o                    # the routing weight is inside o'
+        else:
+            _, _, _, o = expert_forward(x[toks], wg[i], wu[i], wd[i])
+            y[toks] += wr[:, None] * o      # a token meets an expert at most once
     return y, r
 
 
 # ----------------------------------------------------------------------------------------------
 # backward
 
-def backward(dy, x, logits, wg, wu, wd, k, e0=0, e_local=None):
+def backward(dy, x, logits, wg, wu, wd, k, e0=0, e_local=None, mode=None):
     """Gradients of L = <dY, y> with respect to x, the router logits and the expert weights.
 
     Per routed pair (t, j) with expert e and weight w = w_tj:
@@ -175,7 +209,8 @@ def backward(dy, x, logits, wg, wu, wd, k, e0=0, e_local=None):
     have g = 0. Unchosen experts get 0. The index selection is piecewise constant and carries no
     gradient.
     Reading: the pages name only a backward pass (dgrad, wgrad, dSwiGLU and the router-weight
-    gradient are the parts any such pass must produce).
+    gradient are the parts any such pass must produce). In the MX modes the backward GEMMs
+    take MXFP8 operands as listed in the module docstring.
     """
     x, dy = _f64(x), _f64(dy)
     T, H = x.shape
@@ -191,19 +226,37 @@ def backward(dy, x, logits, wg, wu, wd, k, e0=0, e_local=None):
         pairs, toks, wr = _expert_rows(r, i)
         if pairs.size == 0:
             continue
-        xe, dye = x[toks], dy[toks]
-        a, b, h, _ = expert_forward(xe, wg[i], wu[i], wd[i])
-        u = dye @ _f64(wd[i])
-        g[pairs] = np.sum(u * h, axis=1)
-        dh = wr[:, None] * u
-        da = dh * b * dsilu(a)
-        db = dh * silu(a)
-        dwd[i] = (wr[:, None] * dye).T @ h
-        dwg[i] = da.T @ xe
-        dwu[i] = db.T @ xe
-        dx[toks] += da @ _f64(wg[i]) + db @ _f64(wu[i])
+        gi, dwg[i], dwu[i], dwd[i], dxe = _expert_backward(x[toks], dy[toks], wr, wg[i], wu[i], wd[i], mode)
+        g[pairs] = gi
+        dx[toks] += dxe
     dlogits = router_grad(r, g.reshape(T, k), E)
     return dict(dx=dx, dlogits=dlogits, dwg=dwg, dwu=dwu, dwd=dwd, g=g.reshape(T, k)), r
+
+
+def _expert_backward(xe, dye, wr, wg_i, wu_i, wd_i, mode):
+    """(g, dWg, dWu, dWd, dx rows) of one expert's pairs, in the stable pair order."""
+    qb = mode in ("mxfp8", "fp8_bwd")
+    if mode == "mxfp8":
+        a, b, h, _ = expert_forward_q(xe, wr, wg_i, wu_i, wd_i, True)
+    else:
+        a, b, h, _ = expert_forward(xe, wg_i, wu_i, wd_i)
+    u = _qz(qb, dye, 1) @ _qz(qb, wd_i, 0)                 # contraction over H
+    g = np.sum(u * h, axis=1)
+    dh = wr[:, None] * u
+    da = dh * b * dsilu(a)
+    db = dh * silu(a)
+    hw = wr[:, None] * h
+    if qb:                                                  # contraction over the pairs
+        dwd = _qz(True, dye, 0).T @ _qz(True, hw, 0)
+        xq = _qz(True, xe, 0)
+        dwg = _qz(True, da, 0).T @ xq
+        dwu = _qz(True, db, 0).T @ xq
+    else:
+        dwd = (wr[:, None] * dye).T @ h
+        dwg = da.T @ xe
+        dwu = db.T @ xe
+    dxe = _qz(qb, da, 1) @ _qz(qb, wg_i, 0) + _qz(qb, db, 1) @ _qz(qb, wu_i, 0)   # contraction over F
+    return g, dwg, dwu, dwd, dxe
 
 
 def router_grad(r, g, E):
@@ -219,8 +272,12 @@ def router_grad(r, g, E):
 # ----------------------------------------------------------------------------------------------
 # sampled evaluation for full-size layers: each quantity below depends only on the pairs named
 
-def token_rows(tokens, dy, x, logits, wg, wu, wd, k, e0=0, e_local=None):
-    """y, dx and dlogits rows of the given tokens. They need only those tokens' own pairs."""
+def token_rows(tokens, dy, x, logits, wg, wu, wd, k, e0=0, e_local=None, mode=None):
+    """y, dx and dlogits rows of the given tokens. They need only those tokens' own pairs.
+
+    In the MX modes, every quantised operand of these rows is blocked along a row (H or F), so
+    the rows are still independent.
+    """
     x, dy = _f64(x), _f64(dy)
     el = e_local if e_local is not None else len(wg)
     lg = _f64(logits)[np.asarray(tokens)]
@@ -230,25 +287,31 @@ def token_rows(tokens, dy, x, logits, wg, wu, wd, k, e0=0, e_local=None):
     y = np.zeros((n, H))
     dx = np.zeros((n, H))
     g = np.zeros((n, k))
+    qb = mode in ("mxfp8", "fp8_bwd")
     for q, t in enumerate(tokens):
         for j in range(k):
             e = int(idx[q, j])
             if not (e0 <= e < e0 + el):
                 continue
             i = e - e0
-            a, b, h, o = expert_forward(x[t:t + 1], wg[i], wu[i], wd[i])
-            y[q] += w[q, j] * o[0]
-            u = dy[t:t + 1] @ _f64(wd[i])
+            wr = np.array([w[q, j]])
+            if mode == "mxfp8":
+                a, b, h, o = expert_forward_q(x[t:t + 1], wr, wg[i], wu[i], wd[i], True)
+                y[q] += o[0]
+            else:
+                a, b, h, o = expert_forward(x[t:t + 1], wg[i], wu[i], wd[i])
+                y[q] += w[q, j] * o[0]
+            u = _qz(qb, dy[t:t + 1], 1) @ _qz(qb, wd[i], 0)
             g[q, j] = np.sum(u * h)
             dh = w[q, j] * u
             da = dh * b * dsilu(a)
             db = dh * silu(a)
-            dx[q] += (da @ _f64(wg[i]) + db @ _f64(wu[i]))[0]
+            dx[q] += (_qz(qb, da, 1) @ _qz(qb, wg[i], 0) + _qz(qb, db, 1) @ _qz(qb, wu[i], 0))[0]
     rr = dict(w=w, idx=idx)
     return dict(y=y, dx=dx, dlogits=router_grad(rr, g, lg.shape[1]), idx=idx, w=w)
 
 
-def expert_grads(i, dy, x, logits, wg_i, wu_i, wd_i, k, e0=0, e_local=None, r=None):
+def expert_grads(i, dy, x, logits, wg_i, wu_i, wd_i, k, e0=0, e_local=None, r=None, mode=None):
     """dW_gate, dW_up, dW_down of local expert i. They need only that expert's rows."""
     x, dy = _f64(x), _f64(dy)
     if r is None:
@@ -257,13 +320,8 @@ def expert_grads(i, dy, x, logits, wg_i, wu_i, wd_i, k, e0=0, e_local=None, r=No
     F, H = np.shape(wg_i)
     if pairs.size == 0:
         return np.zeros((F, H)), np.zeros((F, H)), np.zeros((H, F))
-    xe, dye = x[toks], dy[toks]
-    a, b, h, _ = expert_forward(xe, wg_i, wu_i, wd_i)
-    u = dye @ _f64(wd_i)
-    dh = wr[:, None] * u
-    da = dh * b * dsilu(a)
-    db = dh * silu(a)
-    return da.T @ xe, db.T @ xe, (wr[:, None] * dye).T @ h
+    _, dwg, dwu, dwd, _ = _expert_backward(x[toks], dy[toks], wr, wg_i, wu_i, wd_i, mode)
+    return dwg, dwu, dwd
 
 
 def rel_frobenius(got, ref):
