@@ -60,9 +60,18 @@ extern "C" {
  *   FP32     all storage and arithmetic in fp32 (test mode).
  *   BF16     bf16 storage; GEMMs on bf16 MFMA with fp32 accumulation; routing,
  *            softmax, SwiGLU and combines in fp32.
- *   MXFP8    bf16 storage; every GEMM operand quantised to MXFP8 (e4m3 elements, one e8m0
- *            scale per 32 elements along the contraction axis) in both passes.
- *   FP8_BWD  bf16 forward, MXFP8 backward. */
+ *   MXFP8    bf16 storage; every GEMM operand quantised to MXFP8 in both passes, GEMMs on
+ *            the scaled fp8 MFMA with fp32 accumulation. The format is read as OCP
+ *            microscaling: one e8m0 scale 2^s per 32 consecutive elements along the GEMM's
+ *            contraction axis, s = floor(log2 amax) - 8 clamped to [-127, 127], elements e4m3
+ *            (finite-only, largest 448) of v / 2^s, rounded to nearest even and saturated.
+ *            Quantised operands (contraction axis in brackets):
+ *              forward   x, W_gate, W_up [H]; w*h, W_down [F]
+ *              backward  dy, W_down [H]; da, db, W_gate, W_up [F];
+ *                        dy, w*h, da, db, x [the expert's pairs in sorted order, blocks of 32
+ *                        from the expert's first pair, the last block zero-padded]
+ *            Routing, softmax, SwiGLU, the router gradient and the combines stay fp32.
+ *   FP8_BWD  the BF16 forward; the backward GEMMs quantised as in MXFP8. */
 typedef enum {
   MOE_MODE_FP32 = 0,
   MOE_MODE_BF16 = 1,
@@ -74,7 +83,7 @@ typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1,        /* null pointer, non-positive size, k > E_total, bad share */
   MOE_ERR_UNSUPPORTED_SHAPE = 2,  /* H % 256, F % 128, E_total > 512, k > 32, T*k >= 2^31 */
-  MOE_ERR_UNSUPPORTED_MODE = 3,   /* mode value unknown or not built into this library */
+  MOE_ERR_UNSUPPORTED_MODE = 3,   /* mode value unknown */
   MOE_ERR_WORKSPACE_TOO_SMALL = 4,
   MOE_ERR_HIP = 5                 /* a HIP runtime call failed; see moe_last_error() */
 } moe_status;
@@ -137,6 +146,18 @@ typedef struct {
   size_t idx, weight, counts, offsets, perm, pair_pos;
 } moe_saved_offsets;
 moe_status moe_saved_layout(const moe_desc* d, moe_saved_offsets* out);
+
+/* MXFP8 quantisation of one bf16 matrix in [rows, cols] (row-major), with the element and scale
+ * rules of MOE_MODE_MXFP8. It is the kernel the MX modes use on x, dy and the weights, exposed so
+ * that it can be checked alone.
+ *   axis = 1: blocks of 32 along each row. q [rows, cols] e4m3 bytes, scales [rows, cols/32]
+ *             e8m0 bytes. cols % 32 == 0.
+ *   axis = 0: blocks of 32 down each column, written transposed. q [cols, rows],
+ *             scales [cols, rows/32]. rows % 64 == 0, cols % 128 == 0.
+ * in and q need 16-byte alignment, scales 4-byte alignment; rows*cols < 2^34. Errors as
+ * elsewhere (nothing is enqueued on error). */
+moe_status moe_mx_quantize(const void* in, int64_t rows, int64_t cols, int axis, uint8_t* q,
+                           uint8_t* scales, void* stream);
 
 /* Static description of a status code. */
 const char* moe_status_string(moe_status s);

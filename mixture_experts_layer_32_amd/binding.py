@@ -71,10 +71,12 @@ def lib():
         L.moe_last_error.argtypes = []
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_version.restype = ctypes.c_char_p
+        L.moe_mx_quantize.argtypes = [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, _P, _P, _P]
         L.moe_profile_enable.argtypes = [ctypes.c_int]
         L.moe_profile_kernel.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
                                          ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]
-        for n in ("moe_query_sizes", "moe_route", "moe_fwd", "moe_bwd", "moe_saved_layout", "moe_profile_enable",
+        for n in ("moe_query_sizes", "moe_route", "moe_fwd", "moe_bwd", "moe_saved_layout", "moe_mx_quantize",
+                  "moe_profile_enable",
                   "moe_profile_disable", "moe_profile_collect", "moe_profile_kernel"):
             getattr(L, n).restype = st
         _lib = L
@@ -134,6 +136,10 @@ def moe_bwd(desc, dy, x, w_gate, w_up, w_down, saved, dx, dlogits, dw_gate, dw_u
     _check(lib().moe_bwd(ctypes.byref(desc), ptr(dy), ptr(x), ptr(w_gate), ptr(w_up), ptr(w_down), ptr(saved),
                          ptr(dx), ptr(dlogits), ptr(dw_gate), ptr(dw_up), ptr(dw_down), ptr(ws), ws_bytes,
                          _stream(stream)))
+
+
+def moe_mx_quantize(x, rows, cols, axis, q, scales, stream=None):
+    _check(lib().moe_mx_quantize(ptr(x), rows, cols, axis, ptr(q), ptr(scales), _stream(stream)))
 
 
 def profile_enable(max_launches=4096):

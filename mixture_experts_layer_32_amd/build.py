@@ -38,7 +38,10 @@ def hipcc() -> str:
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    try:
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=1200)
+    except subprocess.TimeoutExpired:
+        raise RuntimeError(f"command timed out after 1200 s: {' '.join(cmd)}")
     out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{out}")

@@ -26,51 +26,15 @@
 //    counter tracks nothing but the tile loads.
 //  * The row-tiled kernels are persistent. Each XCD takes one contiguous range of the
 //    expert-major tile list, so the blocks sharing an expert's operands share that XCD's L2.
-#include "moe_device.h"
+#include "engine.h"
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_t;
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
+using namespace eng;
 
-constexpr int TILE = 256;            // output tile rows and columns
 constexpr int KTILE = 32;            // contraction elements per K-tile
-constexpr int STAGES = 4;            // LDS ring depth
-constexpr int OPB = 16384;           // bytes per operand per stage
-constexpr int STB = 2 * OPB;         // bytes per stage
-constexpr int LOADS = 4;             // global_load_lds per lane per operand per K-tile
-constexpr int NTHR = 256;
-
-// One wave-wide direct-to-LDS load: lane i copies 16 bytes from g into lds + 16*i (lds is
-// wave-uniform). Written as inline assembly so that the compiler neither tracks it nor inserts
-// waits for it. The main loop orders these loads with explicit vmcnt waits and barriers.
-__device__ __forceinline__ void gl2lds(const void* g, char* lds) {
-  const unsigned off = __builtin_amdgcn_readfirstlane(
-      (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(off), "v"(g) : "memory", "m0");
-}
-// wait until at most N vector memory operations of this wave are outstanding
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-// workgroup barrier without a memory fence. The caller has already waited for the loads the
-// barrier publishes; lgkmcnt(0) retires this wave's LDS reads before other waves may overwrite
-// the stage.
-__device__ __forceinline__ void block_sync() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
-__device__ __forceinline__ int kswz(int r) { return (r >> 2) & 3; }
-
-__device__ __forceinline__ bf16x8 frag_k(const char* tile, int row0, int ks, int lane) {
-  const int r = row0 + (lane & 31);
-  const int c = 2 * ks + (lane >> 5);
-  return *reinterpret_cast<const bf16x8*>(tile + r * 64 + ((c ^ kswz(r)) << 4));
-}
 
 __device__ __forceinline__ const char* mn_addr(const char* tile, int k, int col) {
   return tile + k * 512 + ((((col >> 3) ^ ((k & 3) << 2))) << 4) + (col & 7) * 2;
@@ -94,21 +58,6 @@ __device__ __forceinline__ bf16x8 frag_mn(const char* tile, int col0, int ks, in
 
 // contraction row owned by this lane in load slot j of an MN-major operand (2 rows per slot)
 __device__ __forceinline__ int mn_krow(int j) { return wave_id() * 8 + 2 * j + ((threadIdx.x & 63) >> 5); }
-
-// K-major operand of 256 rows. This lane owns rows w*64 + 16j + lane/4 (j < 4), slot lane&3.
-struct KOp {
-  const char* p[LOADS];   // global address of this lane's chunk in K-tile 0
-  __device__ __forceinline__ void prefetch(int) {}
-  __device__ __forceinline__ void prologue_prefetch(int) {}
-  __device__ __forceinline__ void prologue_issue(char* tile, int kt) const { issue(tile, kt); }
-  __device__ __forceinline__ void issue(char* tile, int kt) const {
-    const int w = wave_id();
-#pragma unroll
-    for (int j = 0; j < LOADS; ++j) gl2lds(p[j] + (size_t)kt * 64, tile + (w * LOADS + j) * 1024);
-  }
-  __device__ __forceinline__ static int row_of(int j) { return wave_id() * 64 + 16 * j + ((threadIdx.x & 63) >> 2); }
-  __device__ __forceinline__ static int chunk_of(int j) { return (threadIdx.x & 3) ^ kswz(row_of(j)); }
-};
 
 // MN-major operand: 32 contraction rows of 256 columns starting at column col0. This lane owns
 // contraction rows w*8 + 2j + lane/32 (j < 4) and slot lane&31.
@@ -283,103 +232,6 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], char* smem, LA& la
     mma_step(acc, fa1, fb1);
   }
   block_sync();
-}
-
-// Accumulator element q of block (i, j) is C[am0 + 32i + (lane & 31)][bn[j] + 8(q/4) + 4(lane/32) + q%4]:
-// for a = q/4 a lane holds 4 consecutive columns of one row.
-__device__ __forceinline__ int acc_m(int i, int lane) { return 32 * i + (lane & 31); }
-__device__ __forceinline__ int acc_n(int a, int lane) { return 8 * a + 4 * (lane >> 5); }
-
-__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  const bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
-  return __builtin_bit_cast(uint2, v);
-}
-__device__ __forceinline__ void st8(void* p, uint2 v) { *reinterpret_cast<uint2*>(p) = v; }
-// ------------------------------------------------------------------------------------------------
-// Epilogue staging. After the main loop the LDS ring is free. Each wave stages 32 rows of its
-// 128x128 quadrant as fp32 (row stride 132 floats, so the 32 rows of one write land in distinct
-// banks). It then reads them back row-contiguous, so that global loads and stores move whole 128- or
-// 256-byte row segments with 16-byte lanes.
-constexpr int SLD = 132;                       // staged row stride (floats)
-constexpr int SLAB = 32 * SLD;                 // floats per wave
-
-__device__ __forceinline__ float* wave_slab(char* smem) {
-  return reinterpret_cast<float*>(smem) + wave_id() * SLAB;
-}
-
-// rows 32i .. 32i+31 of the quadrant; staged column 32j + 8a + 4(lane/32) + b holds block j
-__device__ __forceinline__ void stage_rows(float* slab, const f32x16 (&acc)[4][4], int i, int lane) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      float4 v = make_float4(acc[i][j][4 * a], acc[i][j][4 * a + 1], acc[i][j][4 * a + 2], acc[i][j][4 * a + 3]);
-      *reinterpret_cast<float4*>(slab + (lane & 31) * SLD + 32 * j + acc_n(a, lane)) = v;
-    }
-}
-
-__device__ __forceinline__ void read8(const float* slab, int row, int col, float (&v)[8]) {
-  const float4 x = *reinterpret_cast<const float4*>(slab + row * SLD + col);
-  const float4 y = *reinterpret_cast<const float4*>(slab + row * SLD + col + 4);
-  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w; v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
-}
-
-__device__ __forceinline__ uint4 pack8(const float (&v)[8]) {
-  const bf16x8 b = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3], (bf16)v[4], (bf16)v[5], (bf16)v[6], (bf16)v[7]};
-  return __builtin_bit_cast(uint4, b);
-}
-__device__ __forceinline__ void unpack8(uint4 u, float (&v)[8]) {
-  const bf16x8 b = __builtin_bit_cast(bf16x8, u);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = (float)b[e];
-}
-
-// Stores the wave's 128x128 quadrant (columns contiguous from the quadrant's first column) as
-// bf16. out_row(m) gives the output row pointer of quadrant row m at the quadrant's first column,
-// or null to skip the row; ncols limits the columns written.
-template <class OutRow>
-__device__ __forceinline__ void store_quadrant(char* smem, const f32x16 (&acc)[4][4], int lane, OutRow out_row,
-                                               int ncols) {
-  float* slab = wave_slab(smem);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    stage_rows(slab, acc, i, lane);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int rl = (lane >> 4) + 4 * s, c0 = (lane & 15) * 8;
-      bf16* o = out_row(32 * i + rl);
-      if (o && c0 < ncols) {
-        float v[8];
-        read8(slab, rl, c0, v);
-        st16(o + c0, pack8(v));
-      }
-    }
-  }
-}
-
-// Writes staged columns [0, ncol) of the 32 staged rows to a pair-contiguous transposed copy.
-// dst(c) is the copy's row for staged column c, at the pair column of staged row 0 (null: skip).
-// Four lanes cover one column, 8 consecutive pair rows each: one 16-byte store, 64 contiguous bytes
-// per column.
-template <class Dst>
-__device__ __forceinline__ void store_transposed(const float* slab, int lane, int ncol, Dst dst) {
-  for (int cb = 0; cb < ncol; cb += 16) {
-    const int c = cb + (lane >> 2), g8 = 8 * (lane & 3);
-    bf16* o = dst(c);
-    if (o) {
-      float v[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) v[t] = slab[(g8 + t) * SLD + c];
-      st16(o + g8, pack8(v));
-    }
-  }
-}
-
-__device__ __forceinline__ void unpack4(uint2 v, float (&f)[4]) {
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  const bf16x4 b = __builtin_bit_cast(bf16x4, v);
-  f[0] = (float)b[0]; f[1] = (float)b[1]; f[2] = (float)b[2]; f[3] = (float)b[3];
 }
 
 constexpr int SMEM_BYTES = STAGES * STB > 8 * SLAB * 4 ? STAGES * STB : 8 * SLAB * 4;

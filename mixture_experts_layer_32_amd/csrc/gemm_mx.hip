@@ -1,0 +1,543 @@
+// MXFP8 grouped-GEMM engine for gfx950 and the six expert GEMMs of the fused MoE layer in the MX
+// precision modes ("Supporto di precisione e vincoli hardware" on "Prime Mega MoE: il kernel che
+// accelera il training AI del 55%" names MXFP8 among the kernel's modes; the layer itself is the
+// one of "A Magia da Fusão" on "IA: MoE Kernel 3x Mais Rápido Chegou!").
+//
+// Engine:
+//  * v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 operands. Lane l holds row l%32 of an operand:
+//    bytes 0-15 are contraction elements 16(l/32) + 0..15 and bytes 16-31 are elements
+//    32 + 16(l/32) + 0..15. The block scale of (row i, 32-element block b) comes from lane i + 32b.
+//  * A K-tile is 64 fp8 elements = 64 bytes per row, so data tiles, the 4-stage LDS ring, the
+//    swizzle and the K-major loader are those of the bf16 engine (engine.h). A lane's two 16-byte
+//    chunks are the ones the bf16 engine reads for its two 16-deep steps.
+//  * Every operand is K-major. The quantise kernels and the GEMM epilogues write them that way,
+//    with scales in [rows][K/32] byte arrays. Per stage, each thread also moves one scale dword
+//    per operand into LDS (global_load_lds_dword). Dword d of the stage's scale area holds the
+//    row of quadrant half d/128, 32-row block d%4 and row (d%128)/4 of that block. A lane then
+//    reads the scales of its four 32-row blocks with one 16-byte LDS read.
+//  * A K-tile covers scale columns c = cbase + 2kt and c + 1. Scale bases are multiples of 4 (rows
+//    of H/32, F/32, 2F/32 or Q/32 bytes; expert segments padded to 128 pairs) and K-tile counts are
+//    even, so the dword at column c & ~3 holds K-tile kt's scales in bytes 2(kt & 1) and
+//    2(kt & 1) + 1, and lane l takes byte 2(kt & 1) + l/32.
+//  * Main loop per K-tile: 8 MFMAs (row blocks 0-1), wait + barrier, issue K-tile kt+4, read the
+//    next K-tile's fragments, then the other 8 MFMAs. Fragments are double-buffered, so the
+//    next tile's LDS reads overlap this tile's second half.
+//  * Epilogues quantise in registers where the next GEMM needs an fp8 operand. 4 lanes hold a
+//    block of 32 along F (row pass) or along the pairs (transposed pass); two shuffles give its
+//    amax.
+#include <type_traits>
+
+#include "engine.h"
+#include "moe_internal.h"
+#include "mx_device.h"
+
+namespace moe {
+namespace {
+
+using namespace eng;
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int SCB = 1024;                      // scale bytes per operand per stage (256 dwords)
+constexpr int STB_MX = STB + 2 * SCB;          // stage: A data, B data, A scales, B scales
+constexpr int VM_PER_TILE = 2 * LOADS + 2;     // direct-to-LDS loads per lane per K-tile
+constexpr int SMEM_MX = STAGES * STB_MX > 8 * SLAB * 4 ? STAGES * STB_MX : 8 * SLAB * 4;
+#define MX_SMEM __shared__ __attribute__((aligned(1024))) char smem[SMEM_MX];
+
+// lane i copies 4 bytes from g into lds + 4*i (lds wave-uniform); see gl2lds
+__device__ __forceinline__ void gl2lds_dword(const void* g, char* lds) {
+  const unsigned off = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(off), "v"(g) : "memory", "m0");
+}
+
+// The operand-tile row whose scale dword this thread moves: quadrant half h, block j, row l32.
+__device__ __forceinline__ int sc_half() { return threadIdx.x >> 7; }
+__device__ __forceinline__ int sc_blk() { return threadIdx.x & 3; }
+__device__ __forceinline__ int sc_row32() { return (threadIdx.x & 127) >> 2; }
+
+// scale row of this thread, and the scale column of K-tile 0 (a multiple of 4)
+struct SOp {
+  const uint8_t* row;
+  int cbase;
+  __device__ __forceinline__ void issue(char* area, int kt) const {
+    const int c = cbase + 2 * kt;
+    gl2lds_dword(row + (c & ~3), area + wave_id() * 256);
+  }
+};
+
+__device__ __forceinline__ i32x8 frag8(const char* tile, int row0, int lane) {
+  const int r = row0 + (lane & 31), h = lane >> 5, sw = kswz(r);
+  const uint4 lo = *reinterpret_cast<const uint4*>(tile + r * 64 + ((h ^ sw) << 4));
+  const uint4 hi = *reinterpret_cast<const uint4*>(tile + r * 64 + (((2 + h) ^ sw) << 4));
+  const i32x8 v = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  return v;
+}
+
+struct Frags {
+  i32x8 a[4], b[4];
+  uint4 sa, sb;   // scale dwords of the lane's four A blocks and four B blocks
+};
+
+__device__ __forceinline__ void read_frags_mx(Frags& f, const char* st, int am0, const int (&bn)[4], int wm, int wn,
+                                              int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.a[i] = frag8(st, am0 + 32 * i, lane);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f.b[j] = frag8(st + OPB, bn[j], lane);
+  f.sa = *reinterpret_cast<const uint4*>(st + 2 * OPB + (wm * 128 + (lane & 31) * 4) * 4);
+  f.sb = *reinterpret_cast<const uint4*>(st + 2 * OPB + SCB + (wn * 128 + (lane & 31) * 4) * 4);
+}
+
+// MFMAs of row blocks i0, i0+1 (B fragment first: each accumulator block holds the transposed
+// 32x32 block, as in the bf16 engine)
+__device__ __forceinline__ void mma_half(f32x16 (&acc)[4][4], const Frags& f, int i0, int sela, int selb) {
+  const unsigned sa[4] = {f.sa.x, f.sa.y, f.sa.z, f.sa.w};
+  const unsigned sb[4] = {f.sb.x, f.sb.y, f.sb.z, f.sb.w};
+#pragma unroll
+  for (int ii = 0; ii < 2; ++ii) {
+    const int i = i0 + ii;
+    const int as = (int)((sa[i] >> sela) & 0xffu);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int bs = (int)((sb[j] >> selb) & 0xffu);
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], 0, 0, 0, bs, 0, as);
+    }
+  }
+}
+
+__device__ __forceinline__ void wait_tile_mx(int younger) {
+  if (younger >= 3) wait_vm<3 * VM_PER_TILE>();
+  else if (younger == 2) wait_vm<2 * VM_PER_TILE>();
+  else if (younger == 1) wait_vm<VM_PER_TILE>();
+  else wait_vm<0>();
+}
+
+template <class LA, class LB>
+__device__ __forceinline__ void issue_tile(char* st, const LA& la, const LB& lb, const SOp& sa, const SOp& sb, int kt) {
+  la.issue(st, kt);
+  lb.issue(st + OPB, kt);
+  sa.issue(st + 2 * OPB, kt);
+  sb.issue(st + 2 * OPB + SCB, kt);
+}
+
+// One K-tile: MFMAs of row blocks 0-1, then the barrier that publishes K-tile kt+1, the issue of
+// K-tile kt+STAGES into the stage K-tile kt came from, and the reads of K-tile kt+1's fragments, then
+// MFMAs of row blocks 2-3. The wait, barrier and fragment reads run unconditionally: past the last
+// K-tile they reread a stage that is no longer refilled, and the fragments go unused. Keeping
+// them unconditional lets the compiler hold both fragment sets in registers. ODD is the parity of
+// kt: with the scale base a multiple of 4, K-tile kt's scales are bytes 2*ODD + lane/32.
+template <int ODD, class LA, class LB>
+__device__ __forceinline__ void step_mx(f32x16 (&acc)[4][4], char* smem, const LA& la, const LB& lb, const SOp& sa,
+                                        const SOp& sb, int kt, int nk, const Frags& cur, Frags& nxt, int am0,
+                                        const int (&bn)[4], int wm, int wn, int lane) {
+  const int sel = 16 * ODD + 8 * (lane >> 5);
+  mma_half(acc, cur, 0, sel, sel);
+  wait_tile_mx(min(nk - 2 - kt, STAGES - 2));
+  block_sync();
+  if (kt + STAGES < nk) issue_tile(smem + (kt % STAGES) * STB_MX, la, lb, sa, sb, kt + STAGES);
+  read_frags_mx(nxt, smem + ((kt + 1) % STAGES) * STB_MX, am0, bn, wm, wn, lane);
+  mma_half(acc, cur, 2, sel, sel);
+}
+
+// nk K-tiles (nk even; every scale base a multiple of 4 scale columns).
+template <class LA, class LB>
+__device__ __forceinline__ void mainloop_mx(f32x16 (&acc)[4][4], char* smem, const LA& la, const LB& lb, const SOp& sa,
+                                            const SOp& sb, int nk, int am0, const int (&bn)[4], int wm, int wn) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  if (nk <= 0) return;
+  wait_vm<0>();   // stores of the previous tile's epilogue must not count against the ring below
+  block_sync();   // and every wave is done reading its epilogue staging slab
+#pragma unroll
+  for (int s = 0; s < STAGES; ++s)
+    if (s < nk) issue_tile(smem + s * STB_MX, la, lb, sa, sb, s);
+  wait_tile_mx(min(nk - 1, STAGES - 1));
+  block_sync();
+  Frags f0, f1;
+  read_frags_mx(f0, smem, am0, bn, wm, wn, lane);
+  for (int kt = 0; kt < nk; kt += 2) {
+    step_mx<0>(acc, smem, la, lb, sa, sb, kt, nk, f0, f1, am0, bn, wm, wn, lane);
+    step_mx<1>(acc, smem, la, lb, sa, sb, kt + 1, nk, f1, f0, am0, bn, wm, wn, lane);
+  }
+  block_sync();
+}
+
+// Writes staged columns [0, ncol) of the 32 staged rows, quantised along the rows (the pairs), to a
+// pair-contiguous transposed fp8 copy. dst(c) is the copy's row for staged column c at the pair
+// column of staged row 0 (a multiple of 32), null to skip; sdst(c) is its scale byte.
+template <class Dst, class SDst>
+__device__ __forceinline__ void store_transposed_mx(const float* slab, int lane, int ncol, Dst dst, SDst sdst) {
+  for (int cb = 0; cb < ncol; cb += 16) {
+    const int c = cb + (lane >> 2), g8 = 8 * (lane & 3);
+    float v[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = slab[(g8 + t) * SLD + c];
+    const int s = mx_exponent(mx_amax_x4(v));
+    uint8_t* o = dst(c);
+    if (o) {
+      *reinterpret_cast<uint2*>(o + g8) = mx_encode8(v, s);
+      if ((lane & 3) == 0) *sdst(c) = (uint8_t)(s + 127);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// forward: [a | b] = gather(x) [W_gate; W_up]^T; epilogue writes ab (bf16), hw = w silu(a) b as fp8
+// along F (the down GEMM's A operand) and as fp8 along the pairs (the down weight gradient's B)
+__global__ __launch_bounds__(NTHR, 1) void k_gateup_mx(FwdParams p) {
+  MX_SMEM
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  bf16* __restrict__ ab = static_cast<bf16*>(p.ab);
+  const int H = p.H, F = p.F, ntn = F / 128, hs = H / 32;
+  const XcdRange xr = xcd_range(*p.num_mtiles2 * ntn);
+  const int bn[4] = {64 * wn, 64 * wn + 32, 128 + 64 * wn, 128 + 64 * wn + 32};
+  const int arow_s = 128 * sc_half() + 32 * sc_blk() + sc_row32();
+  const int brow_s = 128 * (sc_blk() >> 1) + 64 * sc_half() + 32 * (sc_blk() & 1) + sc_row32();
+  for (int tile = xr.first; tile < xr.end; tile += xr.stride) {
+    const int mt = tile / ntn, nt = tile - mt * ntn;
+    const int2 me = p.mtile2[mt];
+    const int e = me.x, r0 = me.y, seg_end = p.offsets[e + 1];
+    KOp la, lb;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int row = KOp::row_of(j), c = KOp::chunk_of(j);
+      const int r = min(r0 + row, seg_end - 1);
+      la.p[j] = reinterpret_cast<const char*>(p.xq + (size_t)p.ptok[r] * H) + 16 * c;
+      const uint8_t* wrow = row < 128 ? p.wgq + ((size_t)e * F + nt * 128 + row) * H
+                                      : p.wuq + ((size_t)e * F + nt * 128 + row - 128) * H;
+      lb.p[j] = reinterpret_cast<const char*>(wrow) + 16 * c;
+    }
+    const SOp sa{p.xs + (size_t)p.ptok[min(r0 + arow_s, seg_end - 1)] * hs, 0};
+    const SOp sb{brow_s < 128 ? p.wgs + ((size_t)e * F + nt * 128 + brow_s) * hs
+                              : p.wus + ((size_t)e * F + nt * 128 + brow_s - 128) * hs, 0};
+    float wrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wrow[i] = p.weight[p.perm[min(r0 + 128 * wm + acc_m(i, lane), seg_end - 1)]];
+    f32x16 acc[4][4];
+    mainloop_mx(acc, smem, la, lb, sa, sb, H / 64, 128 * wm, bn, wm, wn);
+    float* slab = wave_slab(smem);
+    const int f0 = nt * 128 + 64 * wn;
+    const int qend = p.qoff[e + 1];
+    const int colq = p.qoff[e] + (r0 - p.offsets[e]) + 128 * wm;
+    const int64_t qs = p.qc / 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      stage_rows(slab, acc, i, lane);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int rl = (lane >> 3) + 8 * s, c0 = (lane & 7) * 8;
+        const float wt = __shfl(wrow[i], rl);
+        const int r = r0 + 128 * wm + 32 * i + rl;
+        const bool ok = r < seg_end;
+        float hv[8];
+        if (ok) {
+          float av[8], bv[8];
+          read8(slab, rl, c0, av);
+          read8(slab, rl, 64 + c0, bv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) hv[e] = wt * (av[e] * sigmoidf_(av[e]) * bv[e]);
+          bf16* abr = ab + (size_t)r * 2 * F + f0 + c0;
+          st16(abr, pack8(av));
+          st16(abr + F, pack8(bv));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) hv[e] = 0.f;
+        }
+        const int sx = mx_exponent(mx_amax_x4(hv));
+        if (ok) {
+          *reinterpret_cast<uint2*>(p.hwq + (size_t)r * F + f0 + c0) = mx_encode8(hv, sx);
+          if ((lane & 3) == 0) p.hws[(size_t)r * (F / 32) + (f0 + c0) / 32] = (uint8_t)(sx + 127);
+        }
+        *reinterpret_cast<float4*>(slab + rl * SLD + c0) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+        *reinterpret_cast<float4*>(slab + rl * SLD + c0 + 4) = make_float4(hv[4], hv[5], hv[6], hv[7]);
+      }
+      const int colb = colq + 32 * i;
+      store_transposed_mx(
+          slab, lane, 64, [&](int c) { return colb < qend ? p.hwtq + (size_t)(f0 + c) * p.qc + colb : nullptr; },
+          [&](int c) { return p.hwts + (size_t)(f0 + c) * qs + colb / 32; });
+    }
+  }
+}
+
+// forward: o' = hw W_down[e]^T (contraction over F)
+__global__ __launch_bounds__(NTHR, 1) void k_down_mx(FwdParams p) {
+  MX_SMEM
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  bf16* __restrict__ o = static_cast<bf16*>(p.o);
+  const int H = p.H, F = p.F, ntn = H / TILE, fs = F / 32;
+  const XcdRange xr = xcd_range(*p.num_mtiles2 * ntn);
+  const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
+  const int row_s = 128 * sc_half() + 32 * sc_blk() + sc_row32();
+  for (int tile = xr.first; tile < xr.end; tile += xr.stride) {
+    const int mt = tile / ntn, nt = tile - mt * ntn;
+    const int2 me = p.mtile2[mt];
+    const int e = me.x, r0 = me.y, seg_end = p.offsets[e + 1];
+    KOp la, lb;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int row = KOp::row_of(j), c = KOp::chunk_of(j);
+      const int r = min(r0 + row, seg_end - 1);
+      la.p[j] = reinterpret_cast<const char*>(p.hwq + (size_t)r * F) + 16 * c;
+      lb.p[j] = reinterpret_cast<const char*>(p.wdq + ((size_t)e * H + nt * TILE + row) * F) + 16 * c;
+    }
+    const SOp sa{p.hws + (size_t)min(r0 + row_s, seg_end - 1) * fs, 0};
+    const SOp sb{p.wds + ((size_t)e * H + nt * TILE + row_s) * fs, 0};
+    f32x16 acc[4][4];
+    mainloop_mx(acc, smem, la, lb, sa, sb, F / 64, 128 * wm, bn, wm, wn);
+    const int rq = r0 + 128 * wm;
+    bf16* const oq = o + nt * TILE + 128 * wn;
+    store_quadrant(smem, acc, lane, [&](int m) { return rq + m < seg_end ? oq + (size_t)(rq + m) * H : nullptr; }, 128);
+  }
+}
+
+// backward: u = gather(dY) W_down[e] (contraction over H, B = W_down[e]^T quantised along H);
+// epilogue writes g partials, and da, db as fp8 along F (dgrad A) and along the pairs (wgrad A)
+__global__ __launch_bounds__(NTHR, 1) void k_bwd_dh_mx(BwdParams p) {
+  MX_SMEM
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const bf16* __restrict__ ab = static_cast<const bf16*>(p.ab);
+  const int H = p.H, F = p.F, ntn = (F + TILE - 1) / TILE, hs = H / 32, f2s = 2 * F / 32;
+  const XcdRange xr = xcd_range(*p.num_mtiles2 * ntn);
+  const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
+  const int row_s = 128 * sc_half() + 32 * sc_blk() + sc_row32();
+  for (int tile = xr.first; tile < xr.end; tile += xr.stride) {
+    const int mt = tile / ntn, nt = tile - mt * ntn;
+    const int2 me = p.mtile2[mt];
+    const int e = me.x, r0 = me.y, seg_end = p.offsets[e + 1];
+    KOp la, lb;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int row = KOp::row_of(j), c = KOp::chunk_of(j);
+      const int r = min(r0 + row, seg_end - 1);
+      la.p[j] = reinterpret_cast<const char*>(p.dyq + (size_t)p.ptok[r] * H) + 16 * c;
+      const int f = min(nt * TILE + row, F - 1);
+      lb.p[j] = reinterpret_cast<const char*>(p.wdtq + ((size_t)e * F + f) * H) + 16 * c;
+    }
+    const SOp sa{p.dys + (size_t)p.ptok[min(r0 + row_s, seg_end - 1)] * hs, 0};
+    const SOp sb{p.wdts + ((size_t)e * F + min(nt * TILE + row_s, F - 1)) * hs, 0};
+    float wrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wrow[i] = p.weight[p.perm[min(r0 + 128 * wm + acc_m(i, lane), seg_end - 1)]];
+    f32x16 acc[4][4];
+    mainloop_mx(acc, smem, la, lb, sa, sb, H / 64, 128 * wm, bn, wm, wn);
+    float* slab = wave_slab(smem);
+    float* slab2 = slab + 4 * SLAB;
+    const int fq = nt * TILE + 128 * wn;
+    const int qend = p.qoff[e + 1];
+    const int colq = p.qoff[e] + (r0 - p.offsets[e]) + 128 * wm;
+    const int64_t qs = p.qc / 32;
+    // one 32-row block of the quadrant; i is a compile-time constant so that acc stays in registers
+    auto block = [&](auto I) {
+      constexpr int i = decltype(I)::value;
+      stage_rows(slab, acc, i, lane);
+      uint4 araw[8], braw[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int rl = (lane >> 4) + 4 * s, c0 = (lane & 15) * 8;
+        const int r = r0 + 128 * wm + 32 * i + rl, f = fq + c0;
+        const bf16* abr = ab + (size_t)min(r, seg_end - 1) * 2 * F + min(f, F - 8);
+        araw[s] = ld16(abr);
+        braw[s] = ld16(abr + F);
+      }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int rl = (lane >> 4) + 4 * s, c0 = (lane & 15) * 8;
+        const float wt = __shfl(wrow[i], rl);
+        const int r = r0 + 128 * wm + 32 * i + rl, f = fq + c0;
+        const bool ok = r < seg_end && f < F;
+        float gsum = 0.f, da[8], db[8];
+        if (ok) {
+          float u[8], av[8], bv[8];
+          read8(slab, rl, c0, u);
+          unpack8(araw[s], av);
+          unpack8(braw[s], bv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float sg = sigmoidf_(av[e]), si = av[e] * sg;
+            gsum += u[e] * (si * bv[e]);
+            const float dh = wt * u[e];
+            da[e] = dh * bv[e] * sg * (1.0f + av[e] * (1.0f - sg));
+            db[e] = dh * si;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) da[e] = db[e] = 0.f;
+        }
+        const int sda = mx_exponent(mx_amax_x4(da));
+        const int sdb = mx_exponent(mx_amax_x4(db));
+        if (ok) {
+          uint8_t* qr = p.dabq + (size_t)r * 2 * F + f;
+          *reinterpret_cast<uint2*>(qr) = mx_encode8(da, sda);
+          *reinterpret_cast<uint2*>(qr + F) = mx_encode8(db, sdb);
+          if ((lane & 3) == 0) {
+            uint8_t* sr = p.dabs + (size_t)r * f2s;
+            sr[f / 32] = (uint8_t)(sda + 127);
+            sr[(F + f) / 32] = (uint8_t)(sdb + 127);
+          }
+        }
+        *reinterpret_cast<float4*>(slab + rl * SLD + c0) = make_float4(da[0], da[1], da[2], da[3]);
+        *reinterpret_cast<float4*>(slab + rl * SLD + c0 + 4) = make_float4(da[4], da[5], da[6], da[7]);
+        *reinterpret_cast<float4*>(slab2 + rl * SLD + c0) = make_float4(db[0], db[1], db[2], db[3]);
+        *reinterpret_cast<float4*>(slab2 + rl * SLD + c0 + 4) = make_float4(db[4], db[5], db[6], db[7]);
+        gsum += __shfl_xor(gsum, 1);
+        gsum += __shfl_xor(gsum, 2);
+        gsum += __shfl_xor(gsum, 4);
+        gsum += __shfl_xor(gsum, 8);
+        if (r < seg_end && (lane & 15) == 0) p.gpart[(size_t)(nt * 2 + wn) * p.rows + r] = gsum;
+      }
+      const int colb = colq + 32 * i;
+      store_transposed_mx(
+          slab, lane, 128,
+          [&](int c) { return colb < qend && fq + c < F ? p.dabtq + (size_t)(fq + c) * p.qc + colb : nullptr; },
+          [&](int c) { return p.dabts + (size_t)(fq + c) * qs + colb / 32; });
+      store_transposed_mx(
+          slab2, lane, 128,
+          [&](int c) { return colb < qend && fq + c < F ? p.dabtq + (size_t)(F + fq + c) * p.qc + colb : nullptr; },
+          [&](int c) { return p.dabts + (size_t)(F + fq + c) * qs + colb / 32; });
+    };
+    block(std::integral_constant<int, 0>{});
+    block(std::integral_constant<int, 1>{});
+    block(std::integral_constant<int, 2>{});
+    block(std::integral_constant<int, 3>{});
+  }
+}
+
+// backward: dX' = [da db] [W_gate[e]; W_up[e]] (contraction over 2F; B = [W_gate^T W_up^T] quantised
+// along F, one H x 2F matrix per expert)
+__global__ __launch_bounds__(NTHR, 1) void k_dgrad_x_mx(BwdParams p) {
+  MX_SMEM
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  bf16* __restrict__ dxp = static_cast<bf16*>(p.dxp);
+  const int H = p.H, F = p.F, ntn = H / TILE, f2s = 2 * F / 32;
+  const XcdRange xr = xcd_range(*p.num_mtiles2 * ntn);
+  const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
+  const int row_s = 128 * sc_half() + 32 * sc_blk() + sc_row32();
+  for (int tile = xr.first; tile < xr.end; tile += xr.stride) {
+    const int mt = tile / ntn, nt = tile - mt * ntn;
+    const int2 me = p.mtile2[mt];
+    const int e = me.x, r0 = me.y, seg_end = p.offsets[e + 1];
+    KOp la, lb;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int row = KOp::row_of(j), c = KOp::chunk_of(j);
+      const int r = min(r0 + row, seg_end - 1);
+      la.p[j] = reinterpret_cast<const char*>(p.dabq + (size_t)r * 2 * F) + 16 * c;
+      lb.p[j] = reinterpret_cast<const char*>(p.wgutq + ((size_t)e * H + nt * TILE + row) * 2 * F) + 16 * c;
+    }
+    const SOp sa{p.dabs + (size_t)min(r0 + row_s, seg_end - 1) * f2s, 0};
+    const SOp sb{p.wguts + ((size_t)e * H + nt * TILE + row_s) * f2s, 0};
+    f32x16 acc[4][4];
+    mainloop_mx(acc, smem, la, lb, sa, sb, 2 * F / 64, 128 * wm, bn, wm, wn);
+    const int rq = r0 + 128 * wm;
+    bf16* const oq = dxp + nt * TILE + 128 * wn;
+    store_quadrant(smem, acc, lane, [&](int m) { return rq + m < seg_end ? oq + (size_t)(rq + m) * H : nullptr; }, 128);
+  }
+}
+
+// backward: dW_down[e] (H x F) = sum over the expert's pairs of dY_t hw_r^T. A = dY^T and B = hw^T,
+// both pair-contiguous and quantised along the pairs; the expert's K range is its padded segment.
+__global__ __launch_bounds__(NTHR, 1) void k_wgrad_down_mx(BwdParams p) {
+  MX_SMEM
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const int H = p.H, F = p.F, ntn = (F + TILE - 1) / TILE, tpe = (H / TILE) * ntn;
+  const int64_t qs = p.qc / 32;
+  const XcdRange xr = xcd_range(p.El * tpe);
+  const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
+  const int row_s = 128 * sc_half() + 32 * sc_blk() + sc_row32();
+  for (int lid = xr.first; lid < xr.end; lid += xr.stride) {
+    const int e = lid / tpe, t = lid - e * tpe, mt = t / ntn, nt = t - mt * ntn;
+    const int q0 = p.qoff[e], nk = (p.qoff[e + 1] - q0) / 64;
+    KOp la, lb;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int row = KOp::row_of(j), c = KOp::chunk_of(j);
+      la.p[j] = reinterpret_cast<const char*>(p.dytq + (size_t)(mt * TILE + row) * p.qc + q0) + 16 * c;
+      lb.p[j] = reinterpret_cast<const char*>(p.hwtq + (size_t)min(nt * TILE + row, F - 1) * p.qc + q0) + 16 * c;
+    }
+    const SOp sa{p.dyts + (size_t)(mt * TILE + row_s) * qs, q0 / 32};
+    const SOp sb{p.hwts + (size_t)min(nt * TILE + row_s, F - 1) * qs, q0 / 32};
+    f32x16 acc[4][4];
+    mainloop_mx(acc, smem, la, lb, sa, sb, nk, 128 * wm, bn, wm, wn);
+    bf16* __restrict__ out = static_cast<bf16*>(p.dwd) + (size_t)e * H * F;
+    const int mq = mt * TILE + 128 * wm, nq = nt * TILE + 128 * wn;
+    store_quadrant(smem, acc, lane, [&](int m) { return out + (size_t)(mq + m) * F + nq; }, F - nq);
+  }
+}
+
+// backward: [dW_gate; dW_up][e] (2F x H) = sum over the expert's pairs of [da; db]_r x_t^T. A = [da db]^T
+// and B = x^T, both pair-contiguous and quantised along the pairs.
+__global__ __launch_bounds__(NTHR, 1) void k_wgrad_gateup_mx(BwdParams p) {
+  MX_SMEM
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const int H = p.H, F = p.F, ntn = H / TILE, tpe = (2 * F / TILE) * ntn;
+  const int64_t qs = p.qc / 32;
+  const XcdRange xr = xcd_range(p.El * tpe);
+  const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
+  const int row_s = 128 * sc_half() + 32 * sc_blk() + sc_row32();
+  for (int lid = xr.first; lid < xr.end; lid += xr.stride) {
+    const int e = lid / tpe, t = lid - e * tpe, mt = t / ntn, nt = t - mt * ntn;
+    const int q0 = p.qoff[e], nk = (p.qoff[e + 1] - q0) / 64;
+    KOp la, lb;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int row = KOp::row_of(j), c = KOp::chunk_of(j);
+      la.p[j] = reinterpret_cast<const char*>(p.dabtq + (size_t)(mt * TILE + row) * p.qc + q0) + 16 * c;
+      lb.p[j] = reinterpret_cast<const char*>(p.xtq + (size_t)(nt * TILE + row) * p.qc + q0) + 16 * c;
+    }
+    const SOp sa{p.dabts + (size_t)(mt * TILE + row_s) * qs, q0 / 32};
+    const SOp sb{p.xts + (size_t)(nt * TILE + row_s) * qs, q0 / 32};
+    f32x16 acc[4][4];
+    mainloop_mx(acc, smem, la, lb, sa, sb, nk, 128 * wm, bn, wm, wn);
+    bf16* __restrict__ dwg = static_cast<bf16*>(p.dwg) + (size_t)e * F * H;
+    bf16* __restrict__ dwu = static_cast<bf16*>(p.dwu) + (size_t)e * F * H;
+    const int mq = mt * TILE + 128 * wm, nq = nt * TILE + 128 * wn;
+    store_quadrant(smem, acc, lane, [&](int m) {
+      const int mm = mq + m;
+      return (mm < F ? dwg + (size_t)mm * H : dwu + (size_t)(mm - F) * H) + nq;
+    }, 128);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_forward_gemms_mx(const FwdParams& p, int grid, hipStream_t s) {
+  hipError_t err;
+  prof_mark_begin("gemm_gateup_swiglu", s);
+  k_gateup_mx<<<grid, NTHR, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+  prof_mark_begin("gemm_down", s);
+  k_down_mx<<<grid, NTHR, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+  return hipSuccess;
+}
+
+hipError_t launch_backward_gemms_mx(const BwdParams& p, int grid, hipStream_t s) {
+  hipError_t err;
+  prof_mark_begin("gemm_bwd_dh_dswiglu", s);
+  k_bwd_dh_mx<<<grid, NTHR, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+  prof_mark_begin("gemm_wgrad_down", s);
+  k_wgrad_down_mx<<<grid, NTHR, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+  prof_mark_begin("gemm_wgrad_gateup", s);
+  k_wgrad_gateup_mx<<<grid, NTHR, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+  prof_mark_begin("gemm_dgrad_x", s);
+  k_dgrad_x_mx<<<grid, NTHR, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+  return hipSuccess;
+}
+
+}  // namespace moe

@@ -23,15 +23,21 @@ static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 Layout make_layout(const moe_desc& d) {
   Layout L{};
+  L.mx = d.mode == MOE_MODE_MXFP8 || d.mode == MOE_MODE_FP8_BWD;
   L.rows = d.T * (int64_t)d.topk;
   L.nblk_route = (int)((d.T + kRouteTokens - 1) / kRouteTokens);
   L.mtile_cap = (int)(L.rows / kBM) + d.E_local + 1;
   L.mtile2_cap = (int)(L.rows / kBM2) + d.E_local + 1;
   L.np = d.mode == MOE_MODE_FP32 ? d.F / 64 : 2 * ((d.F + 255) / 256);
   L.elem = d.mode == MOE_MODE_FP32 ? 4 : 2;
-  // transposed copies exist only on the bf16 engine; columns: every expert padded to 32
-  L.qc = d.mode == MOE_MODE_FP32 ? 0 : ((L.rows + 32 * (int64_t)d.E_local + 31) & ~int64_t(31));
-  const size_t rows = (size_t)L.rows, El = (size_t)d.E_local;
+  // Pair-contiguous transposed copies (bf16 and fp8 engines): every expert's segment is padded to
+  // qpad columns. The fp8 engine needs an even number of 64-pair K-tiles per expert and scale rows
+  // of a multiple of 4 bytes, hence 128.
+  L.qpad = L.mx ? 128 : 32;
+  L.qc = d.mode == MOE_MODE_FP32 ? 0 : (L.rows + (int64_t)L.qpad * d.E_local + 127) / 128 * 128;
+  const size_t rows = (size_t)L.rows, El = (size_t)d.E_local, T = (size_t)d.T, H = (size_t)d.H, F = (size_t)d.F;
+  const size_t qc = (size_t)L.qc;
+  const bool mxf = d.mode == MOE_MODE_MXFP8, f8b = d.mode == MOE_MODE_FP8_BWD;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -51,9 +57,10 @@ Layout make_layout(const moe_desc& d) {
   L.num_mtiles2 = take(4);
   L.zeros = take(kZeroBytes);
   L.qoff = take((El + 1) * 4);
-  L.ab = take(rows * 2 * d.F * L.elem);
-  L.hw = take(rows * d.F * L.elem);
-  L.hwt = take((size_t)L.qc * d.F * 2);
+  L.ab = take(rows * 2 * F * L.elem);
+  L.hw = take(L.mx ? 0 : rows * F * L.elem);
+  L.hwt = take(L.mx ? qc * F : qc * F * 2);      // MX: E4M3 bytes along the pairs
+  L.hwts = take(L.mx ? qc / 32 * F : 0);
   L.saved_total = off;
 
   off = 0;
@@ -61,14 +68,40 @@ Layout make_layout(const moe_desc& d) {
   L.blk_mask = take(cells * 8);
   L.blk_count = take(cells * 4);
   L.blk_prefix = take(cells * 4);
-  L.o = take(rows * d.H * L.elem);
+  L.o = take(rows * H * L.elem);
+  L.xq = take(mxf ? T * H : 0);
+  L.xs = take(mxf ? T * H / 32 : 0);
+  L.wgq = take(mxf ? El * F * H : 0);
+  L.wgs = take(mxf ? El * F * H / 32 : 0);
+  L.wuq = take(mxf ? El * F * H : 0);
+  L.wus = take(mxf ? El * F * H / 32 : 0);
+  L.wdq = take(mxf ? El * H * F : 0);
+  L.wds = take(mxf ? El * H * F / 32 : 0);
+  L.hwq = take(mxf ? rows * F : 0);
+  L.hws = take(mxf ? rows * F / 32 : 0);
+  L.hw16 = take(f8b ? rows * F * 2 : 0);
+  L.hwt16 = take(f8b ? qc * F * 2 : 0);
   L.fwd_total = off;
 
   off = 0;
-  L.dab = take(rows * 2 * d.F * L.elem);
+  L.dab = take(L.mx ? 0 : rows * 2 * F * L.elem);
   L.gpart = take((size_t)L.np * rows * 4);
-  L.dxp = take(rows * d.H * L.elem);
-  L.dabt = take((size_t)L.qc * 2 * d.F * 2);
+  L.dxp = take(rows * H * L.elem);
+  L.dabt = take(L.mx ? 0 : qc * 2 * F * 2);
+  L.dyq = take(L.mx ? T * H : 0);
+  L.dys = take(L.mx ? T * H / 32 : 0);
+  L.wdtq = take(L.mx ? El * F * H : 0);
+  L.wdts = take(L.mx ? El * F * H / 32 : 0);
+  L.wgutq = take(L.mx ? El * H * 2 * F : 0);
+  L.wguts = take(L.mx ? El * H * 2 * F / 32 : 0);
+  L.dytq = take(L.mx ? H * qc : 0);
+  L.dyts = take(L.mx ? H * qc / 32 : 0);
+  L.xtq = take(L.mx ? H * qc : 0);
+  L.xts = take(L.mx ? H * qc / 32 : 0);
+  L.dabq = take(L.mx ? rows * 2 * F : 0);
+  L.dabs = take(L.mx ? rows * 2 * F / 32 : 0);
+  L.dabtq = take(L.mx ? 2 * F * qc : 0);
+  L.dabts = take(L.mx ? 2 * F * qc / 32 : 0);
   L.bwd_total = off;
   return L;
 }
@@ -87,11 +120,9 @@ static moe_status validate(const moe_desc* d) {
   if (d->topk > kMaxTopk) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "topk must be <= 32");
   if (d->T * (int64_t)d->topk >= (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "T*topk must be < 2^31");
-  if (d->mode != MOE_MODE_FP32 && d->mode != MOE_MODE_BF16) {
-    if (d->mode == MOE_MODE_MXFP8 || d->mode == MOE_MODE_FP8_BWD)
-      return fail(MOE_ERR_UNSUPPORTED_MODE, "MX modes are not built into this library version");
+  if (d->mode != MOE_MODE_FP32 && d->mode != MOE_MODE_BF16 && d->mode != MOE_MODE_MXFP8 &&
+      d->mode != MOE_MODE_FP8_BWD)
     return fail(MOE_ERR_UNSUPPORTED_MODE, "unknown mode");
-  }
   return MOE_OK;
 }
 
@@ -178,7 +209,9 @@ using namespace moe;
 
 extern "C" {
 
-const char* moe_version(void) { return "libmoe 0.1 (gfx950; fp32/bf16; persistent grouped GEMM 128x128x128B)"; }
+const char* moe_version(void) {
+  return "libmoe 0.2 (gfx950; fp32/bf16/mxfp8/fp8_bwd; persistent grouped GEMM, 256x256 tiles)";
+}
 
 const char* moe_status_string(moe_status s) {
   switch (s) {
@@ -247,6 +280,7 @@ static RouteParams route_params(const moe_desc& d, const Layout& L, const float*
   p.e0 = d.expert_offset;
   p.k = d.topk;
   p.nblk = L.nblk_route;
+  p.qpad = L.qpad;
   return p;
 }
 
@@ -307,16 +341,55 @@ moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits, const 
   fp.F = d->F;
   fp.k = d->topk;
   fp.El = d->E_local;
+  char* w = static_cast<char*>(ws);
   if (d->mode == MOE_MODE_FP32) {
     if ((e = launch_forward_gemms<float>(fp, persistent_grid(2), s)) != hipSuccess)
       return hip_fail(e, "forward GEMM launch");
     if ((e = launch_combine<float>(fp.o, fp.pair_pos, y, d->T, d->topk, d->H, s)) != hipSuccess)
       return hip_fail(e, "combine launch");
-  } else {
+  } else if (d->mode == MOE_MODE_BF16) {
     if ((e = launch_forward_gemms_bf16(fp, persistent_grid(1), s)) != hipSuccess)
       return hip_fail(e, "forward GEMM launch");
     if ((e = launch_combine<bf16>(fp.o, fp.pair_pos, y, d->T, d->topk, d->H, s)) != hipSuccess)
       return hip_fail(e, "combine launch");
+  } else if (d->mode == MOE_MODE_MXFP8) {
+    // every forward GEMM operand as MXFP8 along its contraction axis; hw and its transposed copy
+    // are quantised in the gate/up epilogue
+    auto u8 = [&](size_t o) { return reinterpret_cast<uint8_t*>(w + o); };
+    const size_t El = (size_t)d->E_local, H = (size_t)d->H, F = (size_t)d->F;
+    if ((e = launch_quant_rows(x, u8(L.xq), u8(L.xs), d->T * d->H, "mx_quant_x", s)) != hipSuccess ||
+        (e = launch_quant_rows(w_gate, u8(L.wgq), u8(L.wgs), El * F * H, "mx_quant_w_gate", s)) != hipSuccess ||
+        (e = launch_quant_rows(w_up, u8(L.wuq), u8(L.wus), El * F * H, "mx_quant_w_up", s)) != hipSuccess ||
+        (e = launch_quant_rows(w_down, u8(L.wdq), u8(L.wds), El * H * F, "mx_quant_w_down", s)) != hipSuccess)
+      return hip_fail(e, "quantise launch");
+    fp.xq = u8(L.xq);
+    fp.xs = u8(L.xs);
+    fp.wgq = u8(L.wgq);
+    fp.wgs = u8(L.wgs);
+    fp.wuq = u8(L.wuq);
+    fp.wus = u8(L.wus);
+    fp.wdq = u8(L.wdq);
+    fp.wds = u8(L.wds);
+    fp.hwq = u8(L.hwq);
+    fp.hws = u8(L.hws);
+    fp.hwtq = reinterpret_cast<uint8_t*>(sv + L.hwt);
+    fp.hwts = reinterpret_cast<uint8_t*>(sv + L.hwts);
+    if ((e = launch_forward_gemms_mx(fp, persistent_grid(1), s)) != hipSuccess)
+      return hip_fail(e, "forward GEMM launch");
+    if ((e = launch_combine<bf16>(fp.o, fp.pair_pos, y, d->T, d->topk, d->H, s)) != hipSuccess)
+      return hip_fail(e, "combine launch");
+  } else {
+    // FP8_BWD: the bf16 forward; the transposed hw copy is then quantised along the pairs for the
+    // backward's down weight gradient
+    fp.hw = w + L.hw16;
+    fp.hwt = w + L.hwt16;
+    if ((e = launch_forward_gemms_bf16(fp, persistent_grid(1), s)) != hipSuccess)
+      return hip_fail(e, "forward GEMM launch");
+    if ((e = launch_combine<bf16>(fp.o, fp.pair_pos, y, d->T, d->topk, d->H, s)) != hipSuccess)
+      return hip_fail(e, "combine launch");
+    if ((e = launch_quant_rows(w + L.hwt16, reinterpret_cast<uint8_t*>(sv + L.hwt), reinterpret_cast<uint8_t*>(sv + L.hwts),
+                               L.qc * d->F, "mx_quant_hw_t", s)) != hipSuccess)
+      return hip_fail(e, "quantise launch");
   }
   return MOE_OK;
 }
@@ -377,11 +450,66 @@ moe_status moe_bwd(const moe_desc* d, const void* dy, const void* x, const void*
   p.El = d->E_local;
   p.np = L.np;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = d->mode == MOE_MODE_FP32 ? launch_backward<float>(p, persistent_grid(2), s)
-                                           : launch_backward_gemms_bf16(p, persistent_grid(1), s);
+  hipError_t e;
+  if (L.mx) {
+    // every backward GEMM operand as MXFP8 along its contraction axis; da and db are quantised in
+    // the dH epilogue
+    auto u8 = [&](size_t o) { return reinterpret_cast<uint8_t*>(w + o); };
+    const int El = d->E_local, H = d->H, F = d->F;
+    if ((e = launch_quant_rows(dy, u8(L.dyq), u8(L.dys), d->T * d->H, "mx_quant_dy", s)) != hipSuccess ||
+        (e = launch_quant_cols(w_down, u8(L.wdtq), u8(L.wdts), El, H, F, H, 0, "mx_quant_w_down_t", s)) != hipSuccess ||
+        (e = launch_quant_cols(w_gate, u8(L.wgutq), u8(L.wguts), El, F, H, 2 * F, 0, "mx_quant_w_gate_t", s)) != hipSuccess ||
+        (e = launch_quant_cols(w_up, u8(L.wgutq), u8(L.wguts), El, F, H, 2 * F, F, "mx_quant_w_up_t", s)) != hipSuccess ||
+        (e = launch_gather_t_quant(dy, p.ptok, p.offsets, p.qoff, El, H, L.qc, u8(L.dytq), u8(L.dyts), "mx_quant_dy_t",
+                                   s)) != hipSuccess ||
+        (e = launch_gather_t_quant(x, p.ptok, p.offsets, p.qoff, El, H, L.qc, u8(L.xtq), u8(L.xts), "mx_quant_x_t",
+                                   s)) != hipSuccess)
+      return hip_fail(e, "quantise launch");
+    p.dyq = u8(L.dyq);
+    p.dys = u8(L.dys);
+    p.wdtq = u8(L.wdtq);
+    p.wdts = u8(L.wdts);
+    p.wgutq = u8(L.wgutq);
+    p.wguts = u8(L.wguts);
+    p.dytq = u8(L.dytq);
+    p.dyts = u8(L.dyts);
+    p.xtq = u8(L.xtq);
+    p.xts = u8(L.xts);
+    p.hwtq = reinterpret_cast<const uint8_t*>(sv + L.hwt);
+    p.hwts = reinterpret_cast<const uint8_t*>(sv + L.hwts);
+    p.dabq = u8(L.dabq);
+    p.dabs = u8(L.dabs);
+    p.dabtq = u8(L.dabtq);
+    p.dabts = u8(L.dabts);
+    e = launch_backward_gemms_mx(p, persistent_grid(1), s);
+  } else {
+    e = d->mode == MOE_MODE_FP32 ? launch_backward<float>(p, persistent_grid(2), s)
+                                 : launch_backward_gemms_bf16(p, persistent_grid(1), s);
+  }
   if (e != hipSuccess) return hip_fail(e, "backward GEMM launch");
   e = d->mode == MOE_MODE_FP32 ? launch_combine_bwd<float>(p, s) : launch_combine_bwd<bf16>(p, s);
   if (e != hipSuccess) return hip_fail(e, "backward combine launch");
+  return MOE_OK;
+}
+
+moe_status moe_mx_quantize(const void* in, int64_t rows, int64_t cols, int axis, uint8_t* q, uint8_t* scales,
+                           void* stream) {
+  g_last_error.clear();
+  moe_status st;
+  if ((st = check_ptrs({{in, "in"}, {q, "q"}}, 16)) != MOE_OK) return st;
+  if ((st = check_ptrs({{scales, "scales"}}, 4)) != MOE_OK) return st;
+  if (rows < 1 || cols < 1) return fail(MOE_ERR_INVALID_ARG, "rows and cols must be positive");
+  if (axis != 0 && axis != 1) return fail(MOE_ERR_INVALID_ARG, "axis must be 0 or 1");
+  if (axis == 1 && cols % 32 != 0) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "cols must be a multiple of 32 (axis 1)");
+  if (axis == 0 && (rows % 64 != 0 || cols % 128 != 0))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "rows must be a multiple of 64 and cols of 128 (axis 0)");
+  if (rows * cols >= (int64_t(1) << 34)) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "rows*cols must be < 2^34");
+  if (axis == 0 && (rows > INT32_MAX || cols / 128 > 65535))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "matrix too large for axis 0");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = axis == 1 ? launch_quant_rows(in, q, scales, rows * cols, "mx_quant_rows", s)
+                                 : launch_quant_cols(in, q, scales, 1, (int)rows, (int)cols, rows, 0, "mx_quant_cols", s);
+  if (e != hipSuccess) return hip_fail(e, "quantise launch");
   return MOE_OK;
 }
 

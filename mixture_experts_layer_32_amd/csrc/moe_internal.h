@@ -21,16 +21,19 @@ struct Layout {
   int nblk_route;      // ceil(T / kRouteTokens)
   int mtile_cap;       // upper bound on 128-row M-tiles: rows / kBM + E_local + 1
   int mtile2_cap;      // upper bound on 256-row M-tiles
-  int np;              // partial sums of g per pair: F / 64 (fp32 engine), 2*ceil(F/256) (bf16 engine)
+  int np;              // partial sums of g per pair: F / 64 (fp32 engine), 2*ceil(F/256) (bf16/fp8 engines)
   size_t elem;         // bytes per stored element (4 or 2)
+  int qpad;            // pair-contiguous segments are padded to a multiple of qpad pairs (32, or 64 in MX modes)
+  bool mx;             // MXFP8 or FP8_BWD
   // saved
-  int64_t qc;          // row stride of the pair-contiguous transposed copies (bf16 engine)
+  int64_t qc;          // row stride of the pair-contiguous transposed copies (bf16 and fp8 engines)
   size_t idx, weight, counts, offsets, perm, ptok, pair_pos, mtile, num_mtiles, mtile2, num_mtiles2, zeros, qoff, ab, hw,
-      hwt, saved_total;
-  // forward workspace
-  size_t blk_mask, blk_count, blk_prefix, o, fwd_total;
-  // backward workspace
-  size_t dab, gpart, dxp, dabt, bwd_total;
+      hwt, hwts, saved_total;
+  // forward workspace (MX: quantised operands; FP8_BWD: the bf16 hw and its transposed copy)
+  size_t blk_mask, blk_count, blk_prefix, o, xq, xs, wgq, wgs, wuq, wus, wdq, wds, hwq, hws, hw16, hwt16, fwd_total;
+  // backward workspace (MX: quantised operands)
+  size_t dab, gpart, dxp, dabt, dyq, dys, wdtq, wdts, wgutq, wguts, dytq, dyts, xtq, xts, dabq, dabs, dabtq, dabts,
+      bwd_total;
 };
 
 Layout make_layout(const moe_desc& d);
@@ -58,7 +61,7 @@ struct RouteParams {
   int* blk_count;
   int* blk_prefix;
   int64_t T;
-  int E, El, e0, k, nblk;
+  int E, El, e0, k, nblk, qpad;
 };
 hipError_t launch_route(const RouteParams& p, hipStream_t s);
 
@@ -85,6 +88,9 @@ struct FwdParams {
   void* o;
   const int* pair_pos;
   void* y;
+  // MXFP8 operands: E4M3 bytes and e8m0 scales ([rows][K/32]), all K-major
+  const uint8_t *xq, *xs, *wgq, *wgs, *wuq, *wus, *wdq, *wds;
+  uint8_t *hwq, *hws, *hwtq, *hwts;
   int64_t T;
   int H, F, k, El;
 };
@@ -123,6 +129,9 @@ struct BwdParams {
   void* dwg;
   void* dwu;
   void* dwd;
+  // MXFP8 operands: E4M3 bytes and e8m0 scales ([rows][K/32]), all K-major
+  const uint8_t *dyq, *dys, *wdtq, *wdts, *wgutq, *wguts, *dytq, *dyts, *xtq, *xts, *hwtq, *hwts;
+  uint8_t *dabq, *dabs, *dabtq, *dabts;
   int64_t T, rows;
   int H, F, k, E, El, np;
 };
@@ -130,6 +139,14 @@ template <class T> hipError_t launch_backward(const BwdParams& p, int grid, hipS
 template <class T> hipError_t launch_combine_bwd(const BwdParams& p, hipStream_t s);
 hipError_t launch_forward_gemms_bf16(const FwdParams& p, int grid, hipStream_t s);
 hipError_t launch_backward_gemms_bf16(const BwdParams& p, int grid, hipStream_t s);
+
+hipError_t launch_forward_gemms_mx(const FwdParams& p, int grid, hipStream_t s);
+hipError_t launch_backward_gemms_mx(const BwdParams& p, int grid, hipStream_t s);
+hipError_t launch_quant_rows(const void* in, uint8_t* q, uint8_t* sc, int64_t n, const char* name, hipStream_t s);
+hipError_t launch_quant_cols(const void* in, uint8_t* q, uint8_t* sc, int B, int R, int C, int64_t ldo, int col0,
+                             const char* name, hipStream_t s);
+hipError_t launch_gather_t_quant(const void* x, const int* ptok, const int* offsets, const int* qoff, int El, int H,
+                                 int64_t qc, uint8_t* q, uint8_t* sc, const char* name, hipStream_t s);
 
 int persistent_grid(int blocks_per_cu);
 

@@ -16,7 +16,8 @@
 //                    Both write, per block and local expert, a 64-bit mask of the tokens that chose it.
 //   k_route_colscan  one block per local expert: exclusive scan of the per-block counts.
 //   k_route_offsets  one block: expert offsets, M-tile tables and counts, and the offsets of the
-//                    experts' 32-column-padded segments in the pair-contiguous transposed copies.
+//                    experts' padded segments (32 columns, 64 in the MX modes) in the
+//                    pair-contiguous transposed copies.
 //   k_route_scatter  one thread per pair: position = expert offset + earlier blocks' count +
 //                    popcount of earlier tokens in the block's mask.
 #include <math.h>
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(512) void k_route_offsets(RouteParams p) {
   const int e = threadIdx.x;
   const int c = e < p.El ? p.counts[e] : 0;
   const int nt = (c + kBM - 1) / kBM, nt2 = (c + kBM2 - 1) / kBM2;
-  const int c32 = (c + 31) & ~31;
+  const int c32 = (c + p.qpad - 1) & ~(p.qpad - 1);
   int tot_c, tot_t, tot_t2, tot_q;
   const int inc_c = block_incl_scan<512>(c, lds, tot_c);
   const int inc_t = block_incl_scan<512>(nt, lds, tot_t);

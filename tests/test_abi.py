@@ -38,8 +38,9 @@ def test_library_exports_every_declared_function():
     (dict(E_total=64, topk=33), "MOE_ERR_UNSUPPORTED_SHAPE"),
     (dict(T=1 << 28, topk=8), "MOE_ERR_UNSUPPORTED_SHAPE"),
     (dict(mode=7), "MOE_ERR_UNSUPPORTED_MODE"),
-    (dict(mode="mxfp8"), "MOE_ERR_UNSUPPORTED_MODE"),
-    (dict(mode="fp8_bwd"), "MOE_ERR_UNSUPPORTED_MODE"),
+    (dict(mode=-1), "MOE_ERR_UNSUPPORTED_MODE"),
+    (dict(H=384, mode="mxfp8"), "MOE_ERR_UNSUPPORTED_SHAPE"),
+    (dict(F=192, mode="fp8_bwd"), "MOE_ERR_UNSUPPORTED_SHAPE"),
 ])
 def test_validation_errors(kw, code):
     with pytest.raises(b.MoEError) as ei:
@@ -78,6 +79,42 @@ def test_sizes_cover_the_layout():
     assert off["pair_pos"] + rows * 4 <= saved
     f32 = b.query_sizes(desc(T=1000, H=512, F=256, E_total=16, topk=4, mode="fp32"))
     assert f32[2] > saved                                        # fp32 activations are wider
+
+
+@pytest.mark.parametrize("mode", ["mxfp8", "fp8_bwd"])
+def test_mx_sizes_cover_the_layout(mode):
+    T, H, F, E, k = 1000, 512, 256, 16, 4
+    d = desc(T=T, H=H, F=F, E_total=E, topk=k, mode=mode)
+    fwd, bwd, saved = b.query_sizes(d)
+    rows = T * k
+    qc = -(-(rows + 128 * E) // 128) * 128                    # pair columns, segments padded to 128
+    assert all(v % 256 == 0 for v in (fwd, bwd, saved))
+    # routing + a, b (bf16) + the fp8 pair-contiguous hw copy with its scales
+    assert saved >= rows * (4 * 4) + rows * 2 * F * 2 + qc * F * (1 + 1 / 32)
+    if mode == "mxfp8":    # quantised x, weights and hw, plus the per-pair outputs
+        assert fwd >= rows * H * 2 + T * H * (1 + 1 / 32) + 3 * E * F * H * (1 + 1 / 32) + rows * F * (1 + 1 / 32)
+    else:                  # bf16 hw and its transposed copy, plus the per-pair outputs
+        assert fwd >= rows * H * 2 + rows * F * 2 + qc * F * 2
+    # quantised dy, weights (both orientations), dY^T, x^T, da/db (both orientations), partials, dX'
+    assert bwd >= (T * H + 3 * E * F * H + 2 * H * qc + rows * 2 * F + 2 * F * qc) * (1 + 1 / 32) \
+        + rows * 4 * 2 * ((F + 255) // 256) + rows * H * 2
+
+
+@pytest.mark.parametrize("args,code,msg", [
+    ((None, 64, 64, 1), "MOE_ERR_INVALID_ARG", "in is null"),
+    ((FAKE + 8, 64, 64, 1), "MOE_ERR_INVALID_ARG", "not 16-byte aligned"),
+    ((FAKE, 0, 64, 1), "MOE_ERR_INVALID_ARG", "positive"),
+    ((FAKE, 64, 64, 2), "MOE_ERR_INVALID_ARG", "axis"),
+    ((FAKE, 64, 48, 1), "MOE_ERR_UNSUPPORTED_SHAPE", "multiple of 32"),
+    ((FAKE, 96, 128, 0), "MOE_ERR_UNSUPPORTED_SHAPE", "multiple of 64"),
+    ((FAKE, 64, 64, 0), "MOE_ERR_UNSUPPORTED_SHAPE", "multiple of 64"),
+    ((FAKE, 1 << 17, 1 << 17, 1), "MOE_ERR_UNSUPPORTED_SHAPE", r"2\^34"),
+])
+def test_mx_quantize_validation(args, code, msg):
+    x, rows, cols, axis = args
+    with pytest.raises(b.MoEError, match=msg) as ei:
+        b.moe_mx_quantize(x, rows, cols, axis, FAKE, FAKE, stream=0)
+    assert ei.value.code == code
 
 
 def test_status_strings():

@@ -1,0 +1,165 @@
+"""GPU parity of the MX precision modes (MXFP8, FP8_BWD) against the MX-emulating float64 oracle.
+
+Bar:
+ * The MXFP8 quantise kernel (moe_mx_quantize): bit-exact E4M3 bytes and e8m0 scale bytes, against
+   oracle/mx.py on the same bf16 input.
+ * Routing: bit-exact, as in every mode.
+ * y, dx, dlogits, dW_gate, dW_up, dW_down: relative Frobenius error within 5e-2 against the oracle
+   run in the same mode (every GEMM operand quantised at the same points). The error against the
+   exact oracle is printed for information.
+ * Experts that receive no tokens: weight gradients exactly zero.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_layer_32_amd import binding, inputs
+from gpu_util import OUTS, TOL, run_layer
+
+pytestmark = pytest.mark.gpu
+
+
+def _fp8_values(u8):
+    return torch.from_numpy(np.ascontiguousarray(u8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _quant_input(rows, cols, seed):
+    """bf16-exact values spanning the scale range: per-32-block magnitudes from 2^-140 to 2^120,
+    all-zero blocks, blocks whose amax is an exact power of two, and blocks that saturate."""
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal((rows, cols)).astype(np.float32)
+    exps = rng.integers(-140, 121, size=(rows, cols // 32)).astype(np.float32)
+    v *= np.repeat(np.exp2(exps), 32, axis=1)
+    v[rng.random((rows, cols)) < 0.02] = 0.0
+    flat = v.reshape(rows, cols // 32, 32)
+    pick = rng.random((rows, cols // 32))
+    flat[pick < 0.05] = 0.0                                       # zero blocks
+    pw = (pick >= 0.05) & (pick < 0.10)
+    flat[pw, 0] = np.float32(2.0) ** rng.integers(-20, 20, size=int(pw.sum()))    # amax a power of two
+    flat[pw, 1:] = np.clip(flat[pw, 1:], -np.abs(flat[pw, :1]) * 0.99, np.abs(flat[pw, :1]) * 0.99)
+    sat = (pick >= 0.10) & (pick < 0.15)
+    flat[sat, 0] = np.float32(1.9375) * np.float32(2.0) ** rng.integers(-10, 10, size=int(sat.sum()))
+    v = inputs.round_to_bf16(flat.reshape(rows, cols))
+    v[v == 0] = 0.0                                               # no negative zeros
+    return v
+
+
+@pytest.mark.parametrize("axis,rows,cols", [(1, 96, 416), (1, 1, 32), (0, 192, 256), (0, 64, 128)])
+def test_mx_quantize_bit_exact(axis, rows, cols):
+    print(f"case mx_quantize axis={axis} {rows}x{cols}", flush=True)
+    # blocks are built along the quantisation axis
+    v = _quant_input(rows, cols, 100 + rows + axis) if axis == 1 else \
+        np.ascontiguousarray(_quant_input(cols, rows, 100 + rows + axis).T)
+    x = torch.from_numpy(v).to("cuda").to(torch.bfloat16)
+    qr, qc = (rows, cols) if axis == 1 else (cols, rows)
+    q = torch.empty(qr, qc, dtype=torch.uint8, device="cuda")
+    s = torch.empty(qr, qc // 32, dtype=torch.uint8, device="cuda")
+    binding.moe_mx_quantize(x, rows, cols, axis, q, s)
+    torch.cuda.synchronize()
+    q, s = q.cpu().numpy(), s.cpu().numpy()
+    src = v if axis == 1 else v.T
+    _, el, sx = oracle.mx.mx_quantize(src.astype(np.float64), axis=1, return_parts=True)
+    want_s = (sx + 127).astype(np.uint8)
+    assert np.array_equal(s, want_s), np.argwhere(s != want_s)[:5]
+    want_q = torch.from_numpy(el).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(q, want_q), np.argwhere(q != want_q)[:5]
+    assert np.array_equal(_fp8_values(q), el)
+    if rows * cols >= 8192:   # the input exercised every kind of block
+        assert (sx == -127).any() and (np.abs(el) == 448).any() and (sx > 100).any()
+
+
+def oracle_full(cfg, L, mode):
+    args = dict(x=L["x"], logits=L["logits"], wg=L["wg"], wu=L["wu"], wd=L["wd"], k=cfg.k, e0=cfg.e0,
+                e_local=cfg.el, mode=mode)
+    y, _ = oracle.forward(**args)
+    g, _ = oracle.backward(dy=L["dy"], **args)
+    return dict(y=y, dx=g["dx"], dlogits=g["dlogits"], dwg=g["dwg"], dwu=g["dwu"], dwd=g["dwd"])
+
+
+def mx_case(name, mode, **kw):
+    cfg, L = inputs.custom_layer(dtype="bf16", **kw)
+    return pytest.param(cfg.with_(name=name), L, mode, id=f"{name}_{mode}")
+
+
+MX_SMALL = [
+    mx_case(n, m, **kw) for m in ("mxfp8", "fp8_bwd") for n, kw in [
+        ("basic", dict(T=256, H=256, F=128, E=8, k=2, seed=31)),
+        ("ragged_T333", dict(T=333, H=512, F=256, E=16, k=4, seed=32)),
+        ("F384", dict(T=300, H=256, F=384, E=8, k=3, seed=33)),
+        ("k1", dict(T=200, H=256, F=128, E=4, k=1, seed=34)),
+        ("single_token", dict(T=1, H=256, F=128, E=8, k=2, seed=35)),
+        ("zipf_empty_experts", dict(T=300, H=256, F=256, E=32, k=2, zipf_s=3.0, seed=36)),
+        ("expert_share", dict(T=400, H=256, F=128, E=16, k=4, E_local=5, e0=3, seed=37)),
+        ("long_segments", dict(T=1200, H=256, F=128, E=4, k=2, seed=38)),
+        ("wide_H4096_F1536", dict(T=130, H=4096, F=1536, E=4, k=2, seed=39)),
+    ]
+]
+
+
+@pytest.mark.parametrize("cfg,L,mode", MX_SMALL)
+def test_small_layer_parity_mx(cfg, L, mode):
+    print(f"case {cfg.name} mode={mode} T={cfg.T} H={cfg.H} F={cfg.F} E={cfg.E} k={cfg.k}", flush=True)
+    got = run_layer(cfg, L, mode)
+    r = oracle.route(L["logits"], cfg.k, cfg.e0, cfg.el)
+    rt = got["routing"]
+    for n in ("idx", "counts", "offsets", "perm", "pair_pos"):
+        assert np.array_equal(rt[n], r[n]), n
+    ref = oracle_full(cfg, L, mode)
+    exact = oracle_full(cfg, L, None)
+    errs = {n: oracle.rel_frobenius(got[n], ref[n]) for n in OUTS}
+    info = {n: oracle.rel_frobenius(got[n], exact[n]) for n in OUTS}
+    print(cfg.name, mode, "vs MX oracle", {n: f"{v:.2e}" for n, v in errs.items()},
+          "vs exact", {n: f"{v:.2e}" for n, v in info.items()}, flush=True)
+    for n in OUTS:
+        assert errs[n] <= TOL[mode], (n, errs[n])
+        assert np.all(np.isfinite(got[n])), n
+    for e in np.nonzero(r["counts"] == 0)[0]:
+        for n in ("dwg", "dwu", "dwd"):
+            assert not np.any(got[n][e]), (n, e)
+    if cfg.el < cfg.E:
+        none = np.nonzero(np.all(r["pair_pos"].reshape(cfg.T, cfg.k) < 0, axis=1))[0]
+        assert not np.any(got["y"][none]) and not np.any(got["dx"][none])
+
+
+@pytest.mark.parametrize("mode", ["mxfp8", "fp8_bwd"])
+def test_mx_deterministic_and_poison_independent(mode):
+    cfg, L = inputs.custom_layer(T=300, H=512, F=256, E=16, k=4, dtype="bf16", seed=40)
+    print(f"case determinism mode={mode}", flush=True)
+    a = run_layer(cfg, L, mode)
+    b = run_layer(cfg, L, mode, poison=True)
+    for n in OUTS:
+        assert a[n].tobytes() == b[n].tobytes(), n
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("mode", ["mxfp8", "fp8_bwd"])
+def test_full_size_sampled_mx(mode):
+    cfg = inputs.CONFIGS["qwen3_30b_a3b_mxfp8"]
+    print(f"case {cfg.name} mode={mode}: generating inputs", flush=True)
+    L = inputs.make_layer(cfg)
+    print(f"case {cfg.name} mode={mode}: running fwd+bwd on the GPU", flush=True)
+    got = run_layer(cfg, L, mode)
+    r = oracle.route(L["logits"], cfg.k, cfg.e0, cfg.el)
+    rt = got["routing"]
+    for n in ("idx", "counts", "offsets", "perm", "pair_pos"):
+        assert np.array_equal(rt[n], r[n]), n
+    rng = np.random.default_rng(1)
+    toks = sorted(set([0, cfg.T - 1] + rng.choice(cfg.T, 16, replace=False).tolist()))
+    s = oracle.token_rows(toks, L["dy"], L["x"], L["logits"], L["wg"], L["wu"], L["wd"], cfg.k, cfg.e0, cfg.el,
+                          mode=mode)
+    errs = {n: oracle.rel_frobenius(got[n][toks], s[n]) for n in ("y", "dx", "dlogits")}
+    counts = r["counts"]
+    for i in sorted(set([0, cfg.el - 1, int(np.argmax(counts))])):
+        dg, du, dd = oracle.expert_grads(i, L["dy"], L["x"], L["logits"], L["wg"][i], L["wu"][i], L["wd"][i], cfg.k,
+                                         cfg.e0, cfg.el, r=r, mode=mode)
+        for n, ref in (("dwg", dg), ("dwu", du), ("dwd", dd)):
+            errs[f"{n}[{i}]"] = oracle.rel_frobenius(got[n][i], ref)
+    print(cfg.name, mode, {n: f"{v:.2e}" for n, v in errs.items()}, flush=True)
+    for n, v in errs.items():
+        assert v <= TOL[mode], (n, v)
+    for n in OUTS:
+        assert np.all(np.isfinite(got[n])), n
+    del got
+    torch.cuda.empty_cache()
