@@ -3,9 +3,9 @@
 // loader, and the LDS-staged epilogue helpers.
 //
 // Tile geometry: a workgroup of 4 wavefronts computes a 256x256 output tile, each wave a 128x128
-// quadrant as 4x4 blocks of 32x32 MFMA outputs. A K-tile is 64 bytes of contraction per operand
-// row (32 bf16 or 64 fp8 elements). The operand tiles of a K-tile reach LDS with
-// global_load_lds_dwordx4 through a ring of STAGES stages.
+// quadrant as 4x4 blocks of 32x32 MFMA outputs. Each engine sets its K-tile (the bytes of
+// contraction per operand row) and ring depth. The operand tiles of a K-tile reach LDS with
+// global_load_lds_dwordx4.
 #pragma once
 #include "moe_device.h"
 
@@ -17,10 +17,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int TILE = 256;            // output tile rows and columns
-constexpr int STAGES = 4;            // LDS ring depth
-constexpr int OPB = 16384;           // bytes per operand per stage
-constexpr int STB = 2 * OPB;         // bytes per stage
-constexpr int LOADS = 4;             // global_load_lds per lane per operand per K-tile
 constexpr int NTHR = 256;
 
 // One wave-wide direct-to-LDS load: lane i copies 16 bytes from g into lds + 16*i (lds is
@@ -43,28 +39,38 @@ __device__ __forceinline__ void block_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
-__device__ __forceinline__ int kswz(int r) { return (r >> 2) & 3; }
 
-__device__ __forceinline__ bf16x8 frag_k(const char* tile, int row0, int ks, int lane) {
-  const int r = row0 + (lane & 31);
-  const int c = 2 * ks + (lane >> 5);
-  return *reinterpret_cast<const bf16x8*>(tile + r * 64 + ((c ^ kswz(r)) << 4));
-}
-
-
-// K-major operand of 256 rows. This lane owns rows w*64 + 16j + lane/4 (j < 4), slot lane&3.
-struct KOp {
+// K-major operand of 256 rows with ROWB bytes of contraction per row per K-tile (64 or 128).
+// One wave instruction moves RPI = 64/NCH whole row segments (NCH = ROWB/16 chunks of 16 bytes);
+// this lane owns rows (w*LOADS + j)*RPI + lane/NCH and slot lane%NCH. A 128-byte segment is a
+// whole cache line: the direct-to-LDS path moves twice the bytes per cycle with whole lines as
+// with half lines.
+// LDS: row r at r*ROWB, chunk c at slot c ^ swz(r). A ds_read_b128 serves 16 lanes per pass over
+// the 64 banks (256 bytes). The 16 lanes read 16 consecutive rows at one chunk, and swz spreads
+// them over distinct bank groups:
+//   64-byte rows:  4 rows share 256 bytes, swz = (r >> 2) & 3
+//   128-byte rows: 2 rows share 256 bytes, swz = (r >> 1) & 7
+template <int ROWB>
+struct KRows {
+  static constexpr int NCH = ROWB / 16, RPI = 64 / NCH, LOADS = TILE / (4 * RPI);
   const char* p[LOADS];   // global address of this lane's chunk in K-tile 0
+  __device__ __forceinline__ static int swz(int r) { return ROWB == 64 ? (r >> 2) & 3 : (r >> 1) & 7; }
+  __device__ __forceinline__ static int row_of(int j) {
+    return (wave_id() * LOADS + j) * RPI + (threadIdx.x & 63) / NCH;
+  }
+  __device__ __forceinline__ static int chunk_of(int j) { return (threadIdx.x & (NCH - 1)) ^ swz(row_of(j)); }
   __device__ __forceinline__ void prefetch(int) {}
   __device__ __forceinline__ void prologue_prefetch(int) {}
   __device__ __forceinline__ void prologue_issue(char* tile, int kt) const { issue(tile, kt); }
   __device__ __forceinline__ void issue(char* tile, int kt) const {
     const int w = wave_id();
 #pragma unroll
-    for (int j = 0; j < LOADS; ++j) gl2lds(p[j] + (size_t)kt * 64, tile + (w * LOADS + j) * 1024);
+    for (int j = 0; j < LOADS; ++j) gl2lds(p[j] + (size_t)kt * ROWB, tile + (w * LOADS + j) * 1024);
   }
-  __device__ __forceinline__ static int row_of(int j) { return wave_id() * 64 + 16 * j + ((threadIdx.x & 63) >> 2); }
-  __device__ __forceinline__ static int chunk_of(int j) { return (threadIdx.x & 3) ^ kswz(row_of(j)); }
+  // 16-byte chunk c of row r of the staged tile
+  __device__ __forceinline__ static const char* at(const char* tile, int r, int c) {
+    return tile + r * ROWB + ((c ^ swz(r)) << 4);
+  }
 };
 
 // Accumulator element q of block (i, j) is C[am0 + 32i + (lane & 31)][bn[j] + 8(q/4) + 4(lane/32) + q%4]:

@@ -7,13 +7,13 @@
 // Engine:
 //  * A workgroup of 4 wavefronts computes a 256x256 output tile, each wave a 128x128 quadrant,
 //    as 4x4 blocks of v_mfma_f32_32x32x16_bf16 with fp32 accumulators (256 per lane, in AGPRs).
-//  * A K-tile is 32 contraction elements. Operand tiles reach LDS with global_load_lds_dwordx4
-//    (no VGPR staging) through a 4-stage ring of 32 KB stages, so three K-tiles are in flight
-//    while one is multiplied. Each wave waits only for its own loads of the current K-tile
-//    (vmcnt with the exact count of younger loads), then a barrier publishes them.
+//  * A K-tile is 64 contraction elements. Operand tiles reach LDS with global_load_lds_dwordx4
+//    (no VGPR staging) through a 2-stage ring of 64 KB stages: K-tile kt+1 lands while kt is
+//    multiplied. Each wave waits for its own loads, then a barrier publishes them.
 //  * K-major operand (contraction axis contiguous: x, dY, hw, dab rows, and the weights in the
-//    forward): one 64-byte LDS row per M/N index. Chunk c of row r goes to slot
-//    c ^ ((r >> 2) & 3). ds_read_b128 fragment reads are then conflict-free.
+//    forward): one 128-byte LDS row per M/N index, so every load moves whole cache lines (with
+//    64-byte rows the direct-to-LDS path ran at half the bytes per cycle). Chunk c of row r goes
+//    to slot c ^ ((r >> 1) & 7). ds_read_b128 fragment reads are then conflict-free.
 //  * MN-major operand (M/N axis contiguous: the weights in the dgrad GEMMs, every weight-gradient
 //    operand): one 512-byte LDS row per contraction index. Chunk c of row k goes to slot
 //    c ^ ((k & 3) << 2). Fragments are read with ds_read_b64_tr_b16, which transposes 16x4
@@ -34,7 +34,12 @@ namespace {
 
 using namespace eng;
 
-constexpr int KTILE = 32;            // contraction elements per K-tile
+constexpr int KTILE = 64;            // contraction elements per K-tile: 128 bytes per K-major row
+typedef KRows<128> KOp;              // K-major operand loader (8 rows of 128 bytes per wave instruction)
+constexpr int LOADS = KOp::LOADS;    // 8 direct-to-LDS loads per lane per operand per K-tile
+constexpr int OPB = 32768;           // bytes per operand per stage (256 x 128 B, or 64 x 512 B)
+constexpr int STB = 2 * OPB;         // bytes per stage
+constexpr int STAGES = 2;            // LDS ring depth (2 x 64 KB)
 
 __device__ __forceinline__ const char* mn_addr(const char* tile, int k, int col) {
   return tile + k * 512 + ((((col >> 3) ^ ((k & 3) << 2))) << 4) + (col & 7) * 2;
@@ -57,10 +62,11 @@ __device__ __forceinline__ bf16x8 frag_mn(const char* tile, int col0, int ks, in
 // K-tile ahead of issue.
 
 // contraction row owned by this lane in load slot j of an MN-major operand (2 rows per slot)
-__device__ __forceinline__ int mn_krow(int j) { return wave_id() * 8 + 2 * j + ((threadIdx.x & 63) >> 5); }
+__device__ __forceinline__ int mn_krow(int j) { return wave_id() * 16 + 2 * j + ((threadIdx.x & 63) >> 5); }
 
-// MN-major operand: 32 contraction rows of 256 columns starting at column col0. This lane owns
-// contraction rows w*8 + 2j + lane/32 (j < 4) and slot lane&31.
+// MN-major operand: 64 contraction rows of 256 columns starting at column col0. This lane owns
+// contraction rows w*16 + 2j + lane/32 (j < 8) and slot lane&31. Each wave instruction moves two
+// whole 512-byte rows.
 template <class Rows>
 struct MNOp {
   Rows rows;
@@ -111,23 +117,23 @@ struct WeightRows {
 };
 
 // contraction rows = an expert's pairs, as the token rows of a [T, ld] tensor (ptok maps a
-// sorted pair to its token). The wave's 8 token indices of a K-tile arrive through one scalar load.
+// sorted pair to its token). The wave's 16 token indices of a K-tile arrive through scalar loads.
 struct GatherRows {
   const char* base;
   const int* __restrict__ ptok;
   size_t ld;
   int seg0, seg_end;
-  int tok[8];
-  int tokp[STAGES][8];   // prologue K-tiles
+  int tok[16];
+  int tokp[STAGES][16];   // prologue K-tiles
   __device__ __forceinline__ void prefetch(int kt) {
-    const int r0 = seg0 + kt * KTILE + wave_id() * 8;
+    const int r0 = seg0 + kt * KTILE + wave_id() * 16;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) tok[i] = ptok[min(r0 + i, seg_end - 1)];
+    for (int i = 0; i < 16; ++i) tok[i] = ptok[min(r0 + i, seg_end - 1)];
   }
   __device__ __forceinline__ void prologue_prefetch(int kt) {
-    const int r0 = seg0 + kt * KTILE + wave_id() * 8;
+    const int r0 = seg0 + kt * KTILE + wave_id() * 16;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) tokp[kt][i] = ptok[min(r0 + i, seg_end - 1)];
+    for (int i = 0; i < 16; ++i) tokp[kt][i] = ptok[min(r0 + i, seg_end - 1)];
   }
   __device__ __forceinline__ const char* row(int kt, int j) const {
     const int hi = (threadIdx.x & 63) >> 5;
@@ -145,12 +151,16 @@ struct GatherRows {
 
 // ------------------------------------------------------------------------------------------------
 // Main loop: nk K-tiles, accumulating into acc. A rows am0.. of the A tile (wave's quadrant); B
-// fragments from columns bn[ni]. Each K-tile is two 16-deep steps. The fragments of the second
-// step are read while the MFMAs of the first run. The barrier that publishes the next K-tile sits
-// between the two steps, and the next K-tile's first fragments are read while the second step's
-// MFMAs run, so the MFMA pipe stays fed across the barrier. The ring holds 4 K-tiles: at the
-// barrier of K-tile kt, K-tile kt+4 is issued into the stage K-tile kt came from (its fragments are
-// all in registers by then). On return all LDS reads are done (LDS may be reused).
+// fragments from columns bn[ni]. A K-tile is four 16-deep steps; each step's fragments are read
+// while the previous step's MFMAs run. The ring holds two K-tiles: K-tile kt+1 lands while kt is
+// multiplied. After the last fragments of K-tile kt are read, the wave waits for K-tile kt+1, the
+// barrier publishes it and frees kt's stage, K-tile kt+2 is issued into that stage, and the first
+// fragments of kt+1 are read while the last MFMAs of kt run. On return all LDS reads are done (LDS
+// may be reused).
+__device__ __forceinline__ bf16x8 frag_k(const char* tile, int row0, int ks, int lane) {
+  return *reinterpret_cast<const bf16x8*>(KOp::at(tile, row0 + (lane & 31), 2 * ks + (lane >> 5)));
+}
+
 template <bool AMN, bool BMN>
 __device__ __forceinline__ void read_frags(bf16x8 (&fa)[4], bf16x8 (&fb)[4], const char* st, int ks, int am0,
                                            const int (&bn)[4], int lane) {
@@ -167,14 +177,6 @@ __device__ __forceinline__ void mma_step(f32x16 (&acc)[4][4], const bf16x8 (&fa)
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-}
-
-// wait until the K-tile whose loads are followed by `younger` more issued K-tiles has landed
-__device__ __forceinline__ void wait_tile(int younger) {
-  if (younger >= 3) wait_vm<3 * 2 * LOADS>();
-  else if (younger == 2) wait_vm<2 * 2 * LOADS>();
-  else if (younger == 1) wait_vm<2 * LOADS>();
-  else wait_vm<0>();
 }
 
 template <bool AMN, bool BMN, class LA, class LB>
@@ -195,39 +197,42 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], char* smem, LA& la
     la.prologue_prefetch(s);
     lb.prologue_prefetch(s);
   }
-#pragma unroll
-  for (int s = 0; s < STAGES; ++s) {
-    if (s < nk) {
-      la.prologue_issue(smem + s * STB, s);
-      lb.prologue_issue(smem + s * STB + OPB, s);
+  la.prologue_issue(smem, 0);
+  lb.prologue_issue(smem + OPB, 0);
+  if (nk > 1) {
+    la.prologue_issue(smem + STB, 1);
+    lb.prologue_issue(smem + STB + OPB, 1);
+    if (nk > 2) {
+      la.prefetch(2);
+      lb.prefetch(2);
     }
+    wait_vm<2 * LOADS>();   // K-tile 0 landed; K-tile 1 may still be in flight
+  } else {
+    wait_vm<0>();
   }
-  if (STAGES < nk) {
-    la.prefetch(STAGES);
-    lb.prefetch(STAGES);
-  }
-  wait_tile(min(nk - 1, STAGES - 1));
   block_sync();
   bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
   read_frags<AMN, BMN>(fa0, fb0, smem, 0, am0, bn, lane);
   for (int kt = 0; kt < nk; ++kt) {
-    const char* cur = smem + (kt % STAGES) * STB;
+    char* cur = smem + (kt & 1) * STB;
     read_frags<AMN, BMN>(fa1, fb1, cur, 1, am0, bn, lane);
     mma_step(acc, fa0, fb0);
+    read_frags<AMN, BMN>(fa0, fb0, cur, 2, am0, bn, lane);
+    mma_step(acc, fa1, fb1);
+    read_frags<AMN, BMN>(fa1, fb1, cur, 3, am0, bn, lane);
+    mma_step(acc, fa0, fb0);
     if (kt + 1 < nk) {
-      wait_tile(min(nk - 2 - kt, STAGES - 2));
+      wait_vm<0>();   // K-tile kt+1 (the only tile in flight) has landed
       block_sync();
-      if (kt + STAGES < nk) {
-        const int t = kt + STAGES;
-        char* st = smem + (t % STAGES) * STB;
-        la.issue(st, t);
-        lb.issue(st + OPB, t);
-        if (t + 1 < nk) {
-          la.prefetch(t + 1);
-          lb.prefetch(t + 1);
+      if (kt + 2 < nk) {
+        la.issue(cur, kt + 2);
+        lb.issue(cur + OPB, kt + 2);
+        if (kt + 3 < nk) {
+          la.prefetch(kt + 3);
+          lb.prefetch(kt + 3);
         }
       }
-      read_frags<AMN, BMN>(fa0, fb0, smem + ((kt + 1) % STAGES) * STB, 0, am0, bn, lane);
+      read_frags<AMN, BMN>(fa0, fb0, smem + ((kt + 1) & 1) * STB, 0, am0, bn, lane);
     }
     mma_step(acc, fa1, fb1);
   }

@@ -38,6 +38,11 @@ using namespace eng;
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
+typedef KRows<64> KOp;                         // K-tile: 64 fp8 = 64 bytes per row
+constexpr int LOADS = KOp::LOADS;              // 4 direct-to-LDS loads per lane per operand per K-tile
+constexpr int STAGES = 4;                      // LDS ring depth (4 x 34 KB)
+constexpr int OPB = 16384;                     // data bytes per operand per stage (256 rows x 64 B)
+constexpr int STB = 2 * OPB;
 constexpr int SCB = 1024;                      // scale bytes per operand per stage (256 dwords)
 constexpr int STB_MX = STB + 2 * SCB;          // stage: A data, B data, A scales, B scales
 constexpr int VM_PER_TILE = 2 * LOADS + 2;     // direct-to-LDS loads per lane per K-tile
@@ -67,9 +72,9 @@ struct SOp {
 };
 
 __device__ __forceinline__ i32x8 frag8(const char* tile, int row0, int lane) {
-  const int r = row0 + (lane & 31), h = lane >> 5, sw = kswz(r);
-  const uint4 lo = *reinterpret_cast<const uint4*>(tile + r * 64 + ((h ^ sw) << 4));
-  const uint4 hi = *reinterpret_cast<const uint4*>(tile + r * 64 + (((2 + h) ^ sw) << 4));
+  const int r = row0 + (lane & 31), h = lane >> 5;
+  const uint4 lo = *reinterpret_cast<const uint4*>(KOp::at(tile, r, h));
+  const uint4 hi = *reinterpret_cast<const uint4*>(KOp::at(tile, r, 2 + h));
   const i32x8 v = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   return v;
 }

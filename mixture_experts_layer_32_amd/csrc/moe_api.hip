@@ -31,9 +31,9 @@ Layout make_layout(const moe_desc& d) {
   L.np = d.mode == MOE_MODE_FP32 ? d.F / 64 : 2 * ((d.F + 255) / 256);
   L.elem = d.mode == MOE_MODE_FP32 ? 4 : 2;
   // Pair-contiguous transposed copies (bf16 and fp8 engines): every expert's segment is padded to
-  // qpad columns. The fp8 engine needs an even number of 64-pair K-tiles per expert and scale rows
-  // of a multiple of 4 bytes, hence 128.
-  L.qpad = L.mx ? 128 : 32;
+  // qpad columns. The bf16 engine reads 64-pair K-tiles; the fp8 engine needs an even number of
+  // 64-pair K-tiles per expert and scale rows of a multiple of 4 bytes, hence 128.
+  L.qpad = L.mx ? 128 : 64;
   L.qc = d.mode == MOE_MODE_FP32 ? 0 : (L.rows + (int64_t)L.qpad * d.E_local + 127) / 128 * 128;
   const size_t rows = (size_t)L.rows, El = (size_t)d.E_local, T = (size_t)d.T, H = (size_t)d.H, F = (size_t)d.F;
   const size_t qc = (size_t)L.qc;
