@@ -69,16 +69,16 @@ def hbm_bytes(name, cfg, P, elem):
     return None
 
 
-def measured_traffic(kernel, workload):
+def measured_traffic(kernel, workload, mode):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, if it was
-    taken on this workload and the GEMM source has not changed since (else None)."""
+    taken on this workload and mode and none of the kernel sources has changed since (else None)."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"{workload}_bf16_hbm_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{workload}_{mode}_hbm_traffic.json")
     try:
         doc = json.load(open(path))
-        src = open(os.path.join(ROOT, doc["kernel_source"]), "rb").read()
-        if hashlib.sha256(src).hexdigest() != doc["kernel_source_sha256"]:
-            return None
+        for src, sha in doc["kernel_sources_sha256"].items():
+            if hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest() != sha:
+                return None
         k = doc["kernels"][kernel]
         return round(k["hbm_read_bytes"] + k["hbm_write_bytes"])
     except (OSError, KeyError, ValueError):
@@ -218,13 +218,13 @@ def main():
         peak = kernel_peak(dom, mode)
         ach = GEMM_FLOPS_PER_PAIR[dom] * cfg.H * cfg.F * P / (davg * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4), "traffic": measured_traffic(dom, cfg.name) if mode == "bf16" else None,
+                "frac": round(ach / peak, 4), "traffic": measured_traffic(dom, cfg.name, mode),
                 "traffic_unit": "bytes per launch (HBM read + write, rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
                 "kernel": dom, "avg_ms": round(davg, 5)}
     else:
         ach = hbm_bytes(dom, cfg, P, 4 if mode == "fp32" else 2) / (davg * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic(dom, cfg.name),
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic(dom, cfg.name, mode),
                 "kernel": dom, "avg_ms": round(davg, 5)}
 
     res = {
