@@ -54,6 +54,8 @@ def hbm_bytes(name, cfg, P, elem):
     q = 1 + 1 / 32                                   # one E4M3 byte per element plus its e8m0 scale
     if name in ("mx_quant_x", "mx_quant_dy"):
         return T * H * (2 + q)
+    if name in ("mx_quant_w_gate", "mx_quant_w_up", "mx_quant_w_down"):   # both orientations from one read
+        return el * F * H * (2 + 2 * q)
     if name.startswith("mx_quant_w_"):
         return el * F * H * (2 + q)
     if name in ("mx_quant_x_t", "mx_quant_dy_t"):    # gathered rows of the expert pairs

@@ -122,7 +122,9 @@ moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits,
                    const void* w_gate, const void* w_up, const void* w_down,
                    void* y, void* saved, void* ws, size_t ws_bytes, void* stream);
 
-/* Backward of <dy, y> with the same x, weights and the `saved` of the matching moe_fwd.
+/* Backward of <dy, y> with the same x, weights and the `saved` of the matching moe_fwd (in
+ * MOE_MODE_MXFP8, `saved` also carries the weights quantised for the backward, so the weights
+ * must be unchanged since that moe_fwd).
  * Outputs (all overwritten, never accumulated):
  *   dx                 [T,H]
  *   dlogits            [T,E_total] fp32, zero outside each token's chosen experts
@@ -141,9 +143,20 @@ moe_status moe_bwd(const moe_desc* d, const void* dy, const void* x,
  *   offsets   int32 [E_local+1] exclusive prefix sum of counts (offsets[E_local] = P)
  *   perm      int32 [T*k]      first P entries: pair ids t*k+j sorted by (expert, pair id)
  *   pair_pos  int32 [T*k]      position of pair t*k+j in perm, -1 if its expert is not local
+ * and, in the MX modes (0 in the others), the MXFP8 operands the forward leaves for the backward,
+ * each an e4m3 byte array with its e8m0 scale bytes:
+ *   qoff      int32 [E_local+1] first column of each expert's segment in the pair-contiguous
+ *                              copies; each segment is padded with zeros to a multiple of 128
+ *   qcols     (value)          column count Q of the pair-contiguous copies
+ *   hwt, hwt_scales            w*h transposed, [F, Q] and [F, Q/32]: blocks of 32 along each
+ *                              expert's pairs
+ *   wdt, wdt_scales            (MXFP8) W_down[e] along H, transposed: [E_local, F, H], [E_local, F, H/32]
+ *   wgut, wgut_scales          (MXFP8) [W_gate[e]^T | W_up[e]^T] along F: [E_local, H, 2F],
+ *                              [E_local, H, 2F/32]
  * Host-only pointer arithmetic, for tests and tools. */
 typedef struct {
   size_t idx, weight, counts, offsets, perm, pair_pos;
+  size_t qoff, qcols, hwt, hwt_scales, wdt, wdt_scales, wgut, wgut_scales;
 } moe_saved_offsets;
 moe_status moe_saved_layout(const moe_desc* d, moe_saved_offsets* out);
 
@@ -153,7 +166,7 @@ moe_status moe_saved_layout(const moe_desc* d, moe_saved_offsets* out);
  *   axis = 1: blocks of 32 along each row. q [rows, cols] e4m3 bytes, scales [rows, cols/32]
  *             e8m0 bytes. cols % 32 == 0.
  *   axis = 0: blocks of 32 down each column, written transposed. q [cols, rows],
- *             scales [cols, rows/32]. rows % 64 == 0, cols % 128 == 0.
+ *             scales [cols, rows/32]. rows % 128 == 0, cols % 64 == 0.
  * in and q need 16-byte alignment, scales 4-byte alignment; rows*cols < 2^34. Errors as
  * elsewhere (nothing is enqueued on error). */
 moe_status moe_mx_quantize(const void* in, int64_t rows, int64_t cols, int axis, uint8_t* q,

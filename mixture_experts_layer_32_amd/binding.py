@@ -32,7 +32,8 @@ class Desc(ctypes.Structure):
 
 
 class SavedOffsets(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_size_t) for n in ("idx", "weight", "counts", "offsets", "perm", "pair_pos")]
+    _fields_ = [(n, ctypes.c_size_t) for n in ("idx", "weight", "counts", "offsets", "perm", "pair_pos", "qoff", "qcols",
+                                               "hwt", "hwt_scales", "wdt", "wdt_scales", "wgut", "wgut_scales")]
 
 
 class MoEError(RuntimeError):

@@ -8,6 +8,7 @@
 // global_load_lds_dwordx4.
 #pragma once
 #include "moe_device.h"
+#include "mx_device.h"
 
 namespace moe {
 namespace eng {
@@ -168,6 +169,25 @@ __device__ __forceinline__ void unpack4(uint2 v, float (&f)[4]) {
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   const bf16x4 b = __builtin_bit_cast(bf16x4, v);
   f[0] = (float)b[0]; f[1] = (float)b[1]; f[2] = (float)b[2]; f[3] = (float)b[3];
+}
+
+// Writes staged columns [0, ncol) of the 32 staged rows, quantised along the rows (the pairs), to a
+// pair-contiguous transposed fp8 copy. dst(c) is the copy's row for staged column c at the pair
+// column of staged row 0 (a multiple of 32), null to skip; sdst(c) is its scale byte.
+template <class Dst, class SDst>
+__device__ __forceinline__ void store_transposed_mx(const float* slab, int lane, int ncol, Dst dst, SDst sdst) {
+  for (int cb = 0; cb < ncol; cb += 16) {
+    const int c = cb + (lane >> 2), g8 = 8 * (lane & 3);
+    float v[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = slab[(g8 + t) * SLD + c];
+    const int s = mx_exponent(mx_amax_x4(v));
+    uint8_t* o = dst(c);
+    if (o) {
+      *reinterpret_cast<uint2*>(o + g8) = mx_encode8(v, s);
+      if ((lane & 3) == 0) *sdst(c) = (uint8_t)(s + 127);
+    }
+  }
 }
 
 }  // namespace eng

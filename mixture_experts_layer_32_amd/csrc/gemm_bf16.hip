@@ -244,6 +244,9 @@ constexpr int SMEM_BYTES = STAGES * STB > 8 * SLAB * 4 ? STAGES * STB : 8 * SLAB
 
 // ------------------------------------------------------------------------------------------------
 // forward: [a | b] = gather(x) [W_gate; W_up]^T, then ab and hw = w * silu(a) * b
+// QT: the pair-contiguous copy of hw is written as MXFP8 (blocks of 32 along the pairs, quantised
+// from the fp32 values) for an MXFP8 backward, instead of bf16
+template <bool QT>
 __global__ __launch_bounds__(NTHR, 1) void k_gateup_bf16(FwdParams p) {
   MOE_SMEM
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
@@ -308,7 +311,12 @@ __global__ __launch_bounds__(NTHR, 1) void k_gateup_bf16(FwdParams p) {
         *reinterpret_cast<float4*>(slab + rl * SLD + c0 + 4) = make_float4(hv[4], hv[5], hv[6], hv[7]);
       }
       const int colb = colq + 32 * i;
-      store_transposed(slab, lane, 64, [&](int c) { return colb < qend ? hwt + (size_t)(f0 + c) * p.qc + colb : nullptr; });
+      if (QT)
+        store_transposed_mx(
+            slab, lane, 64, [&](int c) { return colb < qend ? p.hwtq + (size_t)(f0 + c) * p.qc + colb : nullptr; },
+            [&](int c) { return p.hwts + (size_t)(f0 + c) * (p.qc / 32) + colb / 32; });
+      else
+        store_transposed(slab, lane, 64, [&](int c) { return colb < qend ? hwt + (size_t)(f0 + c) * p.qc + colb : nullptr; });
     }
   }
 }
@@ -546,7 +554,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_wgrad_gateup_bf16(BwdParams p) {
 hipError_t launch_forward_gemms_bf16(const FwdParams& p, int grid, hipStream_t s) {
   hipError_t err;
   prof_mark_begin("gemm_gateup_swiglu", s);
-  k_gateup_bf16<<<grid, NTHR, 0, s>>>(p);
+  if (p.hwtq) k_gateup_bf16<true><<<grid, NTHR, 0, s>>>(p);
+  else k_gateup_bf16<false><<<grid, NTHR, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   prof_mark_end(s);
   prof_mark_begin("gemm_down", s);

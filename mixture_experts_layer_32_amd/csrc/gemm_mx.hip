@@ -173,25 +173,6 @@ __device__ __forceinline__ void mainloop_mx(f32x16 (&acc)[4][4], char* smem, con
   block_sync();
 }
 
-// Writes staged columns [0, ncol) of the 32 staged rows, quantised along the rows (the pairs), to a
-// pair-contiguous transposed fp8 copy. dst(c) is the copy's row for staged column c at the pair
-// column of staged row 0 (a multiple of 32), null to skip; sdst(c) is its scale byte.
-template <class Dst, class SDst>
-__device__ __forceinline__ void store_transposed_mx(const float* slab, int lane, int ncol, Dst dst, SDst sdst) {
-  for (int cb = 0; cb < ncol; cb += 16) {
-    const int c = cb + (lane >> 2), g8 = 8 * (lane & 3);
-    float v[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) v[t] = slab[(g8 + t) * SLD + c];
-    const int s = mx_exponent(mx_amax_x4(v));
-    uint8_t* o = dst(c);
-    if (o) {
-      *reinterpret_cast<uint2*>(o + g8) = mx_encode8(v, s);
-      if ((lane & 3) == 0) *sdst(c) = (uint8_t)(s + 127);
-    }
-  }
-}
-
 // ------------------------------------------------------------------------------------------------
 // forward: [a | b] = gather(x) [W_gate; W_up]^T; epilogue writes ab (bf16), hw = w silu(a) b as fp8
 // along F (the down GEMM's A operand) and as fp8 along the pairs (the down weight gradient's B)

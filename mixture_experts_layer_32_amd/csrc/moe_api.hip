@@ -61,6 +61,10 @@ Layout make_layout(const moe_desc& d) {
   L.hw = take(L.mx ? 0 : rows * F * L.elem);
   L.hwt = take(L.mx ? qc * F : qc * F * 2);      // MX: E4M3 bytes along the pairs
   L.hwts = take(L.mx ? qc / 32 * F : 0);
+  L.sv_wdtq = take(mxf ? El * F * H : 0);
+  L.sv_wdts = take(mxf ? El * F * H / 32 : 0);
+  L.sv_wgutq = take(mxf ? El * H * 2 * F : 0);
+  L.sv_wguts = take(mxf ? El * H * 2 * F / 32 : 0);
   L.saved_total = off;
 
   off = 0;
@@ -80,7 +84,6 @@ Layout make_layout(const moe_desc& d) {
   L.hwq = take(mxf ? rows * F : 0);
   L.hws = take(mxf ? rows * F / 32 : 0);
   L.hw16 = take(f8b ? rows * F * 2 : 0);
-  L.hwt16 = take(f8b ? qc * F * 2 : 0);
   L.fwd_total = off;
 
   off = 0;
@@ -90,10 +93,10 @@ Layout make_layout(const moe_desc& d) {
   L.dabt = take(L.mx ? 0 : qc * 2 * F * 2);
   L.dyq = take(L.mx ? T * H : 0);
   L.dys = take(L.mx ? T * H / 32 : 0);
-  L.wdtq = take(L.mx ? El * F * H : 0);
-  L.wdts = take(L.mx ? El * F * H / 32 : 0);
-  L.wgutq = take(L.mx ? El * H * 2 * F : 0);
-  L.wguts = take(L.mx ? El * H * 2 * F / 32 : 0);
+  L.wdtq = take(f8b ? El * F * H : 0);
+  L.wdts = take(f8b ? El * F * H / 32 : 0);
+  L.wgutq = take(f8b ? El * H * 2 * F : 0);
+  L.wguts = take(f8b ? El * H * 2 * F / 32 : 0);
   L.dytq = take(L.mx ? H * qc : 0);
   L.dyts = take(L.mx ? H * qc / 32 : 0);
   L.xtq = take(L.mx ? H * qc : 0);
@@ -250,6 +253,15 @@ moe_status moe_saved_layout(const moe_desc* d, moe_saved_offsets* out) {
   out->offsets = L.offsets;
   out->perm = L.perm;
   out->pair_pos = L.pair_pos;
+  const bool mxf = d->mode == MOE_MODE_MXFP8;
+  out->qoff = L.mx ? L.qoff : 0;
+  out->qcols = L.mx ? (size_t)L.qc : 0;
+  out->hwt = L.mx ? L.hwt : 0;
+  out->hwt_scales = L.mx ? L.hwts : 0;
+  out->wdt = mxf ? L.sv_wdtq : 0;
+  out->wdt_scales = mxf ? L.sv_wdts : 0;
+  out->wgut = mxf ? L.sv_wgutq : 0;
+  out->wgut_scales = mxf ? L.sv_wguts : 0;
   return MOE_OK;
 }
 
@@ -354,13 +366,18 @@ moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits, const 
       return hip_fail(e, "combine launch");
   } else if (d->mode == MOE_MODE_MXFP8) {
     // every forward GEMM operand as MXFP8 along its contraction axis; hw and its transposed copy
-    // are quantised in the gate/up epilogue
+    // are quantised in the gate/up epilogue. Each weight is read once and quantised along both
+    // axes: the other orientation is the backward's operand and goes to `saved`.
     auto u8 = [&](size_t o) { return reinterpret_cast<uint8_t*>(w + o); };
-    const size_t El = (size_t)d->E_local, H = (size_t)d->H, F = (size_t)d->F;
+    auto s8 = [&](size_t o) { return reinterpret_cast<uint8_t*>(sv + o); };
+    const int El = d->E_local, H = d->H, F = d->F;
     if ((e = launch_quant_rows(x, u8(L.xq), u8(L.xs), d->T * d->H, "mx_quant_x", s)) != hipSuccess ||
-        (e = launch_quant_rows(w_gate, u8(L.wgq), u8(L.wgs), El * F * H, "mx_quant_w_gate", s)) != hipSuccess ||
-        (e = launch_quant_rows(w_up, u8(L.wuq), u8(L.wus), El * F * H, "mx_quant_w_up", s)) != hipSuccess ||
-        (e = launch_quant_rows(w_down, u8(L.wdq), u8(L.wds), El * H * F, "mx_quant_w_down", s)) != hipSuccess)
+        (e = launch_quant_both(w_gate, u8(L.wgq), u8(L.wgs), s8(L.sv_wgutq), s8(L.sv_wguts), El, F, H, 2 * F, 0,
+                               "mx_quant_w_gate", s)) != hipSuccess ||
+        (e = launch_quant_both(w_up, u8(L.wuq), u8(L.wus), s8(L.sv_wgutq), s8(L.sv_wguts), El, F, H, 2 * F, F,
+                               "mx_quant_w_up", s)) != hipSuccess ||
+        (e = launch_quant_both(w_down, u8(L.wdq), u8(L.wds), s8(L.sv_wdtq), s8(L.sv_wdts), El, H, F, H, 0,
+                               "mx_quant_w_down", s)) != hipSuccess)
       return hip_fail(e, "quantise launch");
     fp.xq = u8(L.xq);
     fp.xs = u8(L.xs);
@@ -379,17 +396,15 @@ moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits, const 
     if ((e = launch_combine<bf16>(fp.o, fp.pair_pos, y, d->T, d->topk, d->H, s)) != hipSuccess)
       return hip_fail(e, "combine launch");
   } else {
-    // FP8_BWD: the bf16 forward; the transposed hw copy is then quantised along the pairs for the
+    // FP8_BWD: the bf16 forward; its epilogue writes the pair-contiguous hw copy as MXFP8 for the
     // backward's down weight gradient
     fp.hw = w + L.hw16;
-    fp.hwt = w + L.hwt16;
+    fp.hwtq = reinterpret_cast<uint8_t*>(sv + L.hwt);
+    fp.hwts = reinterpret_cast<uint8_t*>(sv + L.hwts);
     if ((e = launch_forward_gemms_bf16(fp, persistent_grid(1), s)) != hipSuccess)
       return hip_fail(e, "forward GEMM launch");
     if ((e = launch_combine<bf16>(fp.o, fp.pair_pos, y, d->T, d->topk, d->H, s)) != hipSuccess)
       return hip_fail(e, "combine launch");
-    if ((e = launch_quant_rows(w + L.hwt16, reinterpret_cast<uint8_t*>(sv + L.hwt), reinterpret_cast<uint8_t*>(sv + L.hwts),
-                               L.qc * d->F, "mx_quant_hw_t", s)) != hipSuccess)
-      return hip_fail(e, "quantise launch");
   }
   return MOE_OK;
 }
@@ -453,13 +468,21 @@ moe_status moe_bwd(const moe_desc* d, const void* dy, const void* x, const void*
   hipError_t e;
   if (L.mx) {
     // every backward GEMM operand as MXFP8 along its contraction axis; da and db are quantised in
-    // the dH epilogue
+    // the dH epilogue. MXFP8: the weights' backward orientation comes from the forward (`saved`);
+    // FP8_BWD quantises it here.
     auto u8 = [&](size_t o) { return reinterpret_cast<uint8_t*>(w + o); };
     const int El = d->E_local, H = d->H, F = d->F;
+    const bool f8b = d->mode == MOE_MODE_FP8_BWD;
+    const uint8_t* wdtq = f8b ? u8(L.wdtq) : reinterpret_cast<const uint8_t*>(sv + L.sv_wdtq);
+    const uint8_t* wdts = f8b ? u8(L.wdts) : reinterpret_cast<const uint8_t*>(sv + L.sv_wdts);
+    const uint8_t* wgutq = f8b ? u8(L.wgutq) : reinterpret_cast<const uint8_t*>(sv + L.sv_wgutq);
+    const uint8_t* wguts = f8b ? u8(L.wguts) : reinterpret_cast<const uint8_t*>(sv + L.sv_wguts);
+    if (f8b &&
+        ((e = launch_quant_cols(w_down, u8(L.wdtq), u8(L.wdts), El, H, F, H, 0, "mx_quant_w_down_t", s)) != hipSuccess ||
+         (e = launch_quant_cols(w_gate, u8(L.wgutq), u8(L.wguts), El, F, H, 2 * F, 0, "mx_quant_w_gate_t", s)) != hipSuccess ||
+         (e = launch_quant_cols(w_up, u8(L.wgutq), u8(L.wguts), El, F, H, 2 * F, F, "mx_quant_w_up_t", s)) != hipSuccess))
+      return hip_fail(e, "quantise launch");
     if ((e = launch_quant_rows(dy, u8(L.dyq), u8(L.dys), d->T * d->H, "mx_quant_dy", s)) != hipSuccess ||
-        (e = launch_quant_cols(w_down, u8(L.wdtq), u8(L.wdts), El, H, F, H, 0, "mx_quant_w_down_t", s)) != hipSuccess ||
-        (e = launch_quant_cols(w_gate, u8(L.wgutq), u8(L.wguts), El, F, H, 2 * F, 0, "mx_quant_w_gate_t", s)) != hipSuccess ||
-        (e = launch_quant_cols(w_up, u8(L.wgutq), u8(L.wguts), El, F, H, 2 * F, F, "mx_quant_w_up_t", s)) != hipSuccess ||
         (e = launch_gather_t_quant(dy, p.ptok, p.offsets, p.qoff, El, H, L.qc, u8(L.dytq), u8(L.dyts), "mx_quant_dy_t",
                                    s)) != hipSuccess ||
         (e = launch_gather_t_quant(x, p.ptok, p.offsets, p.qoff, El, H, L.qc, u8(L.xtq), u8(L.xts), "mx_quant_x_t",
@@ -467,10 +490,10 @@ moe_status moe_bwd(const moe_desc* d, const void* dy, const void* x, const void*
       return hip_fail(e, "quantise launch");
     p.dyq = u8(L.dyq);
     p.dys = u8(L.dys);
-    p.wdtq = u8(L.wdtq);
-    p.wdts = u8(L.wdts);
-    p.wgutq = u8(L.wgutq);
-    p.wguts = u8(L.wguts);
+    p.wdtq = wdtq;
+    p.wdts = wdts;
+    p.wgutq = wgutq;
+    p.wguts = wguts;
     p.dytq = u8(L.dytq);
     p.dyts = u8(L.dyts);
     p.xtq = u8(L.xtq);
@@ -501,10 +524,10 @@ moe_status moe_mx_quantize(const void* in, int64_t rows, int64_t cols, int axis,
   if (rows < 1 || cols < 1) return fail(MOE_ERR_INVALID_ARG, "rows and cols must be positive");
   if (axis != 0 && axis != 1) return fail(MOE_ERR_INVALID_ARG, "axis must be 0 or 1");
   if (axis == 1 && cols % 32 != 0) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "cols must be a multiple of 32 (axis 1)");
-  if (axis == 0 && (rows % 64 != 0 || cols % 128 != 0))
-    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "rows must be a multiple of 64 and cols of 128 (axis 0)");
+  if (axis == 0 && (rows % 128 != 0 || cols % 64 != 0))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "rows must be a multiple of 128 and cols of 64 (axis 0)");
   if (rows * cols >= (int64_t(1) << 34)) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "rows*cols must be < 2^34");
-  if (axis == 0 && (rows > INT32_MAX || cols / 128 > 65535))
+  if (axis == 0 && (rows / 128 > 65535 || cols / 64 > INT32_MAX))
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "matrix too large for axis 0");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = axis == 1 ? launch_quant_rows(in, q, scales, rows * cols, "mx_quant_rows", s)

@@ -29,8 +29,11 @@ struct Layout {
   int64_t qc;          // row stride of the pair-contiguous transposed copies (bf16 and fp8 engines)
   size_t idx, weight, counts, offsets, perm, ptok, pair_pos, mtile, num_mtiles, mtile2, num_mtiles2, zeros, qoff, ab, hw,
       hwt, hwts, saved_total;
-  // forward workspace (MX: quantised operands; FP8_BWD: the bf16 hw and its transposed copy)
-  size_t blk_mask, blk_count, blk_prefix, o, xq, xs, wgq, wgs, wuq, wus, wdq, wds, hwq, hws, hw16, hwt16, fwd_total;
+  // MXFP8: the weights quantised along their other axis by the forward, for the backward (in
+  // saved); FP8_BWD: the backward quantises them into its workspace (wdtq.. below)
+  size_t sv_wdtq, sv_wdts, sv_wgutq, sv_wguts;
+  // forward workspace (MXFP8: quantised operands; FP8_BWD: the bf16 hw)
+  size_t blk_mask, blk_count, blk_prefix, o, xq, xs, wgq, wgs, wuq, wus, wdq, wds, hwq, hws, hw16, fwd_total;
   // backward workspace (MX: quantised operands)
   size_t dab, gpart, dxp, dabt, dyq, dys, wdtq, wdts, wgutq, wguts, dytq, dyts, xtq, xts, dabq, dabs, dabtq, dabts,
       bwd_total;
@@ -145,6 +148,8 @@ hipError_t launch_backward_gemms_mx(const BwdParams& p, int grid, hipStream_t s)
 hipError_t launch_quant_rows(const void* in, uint8_t* q, uint8_t* sc, int64_t n, const char* name, hipStream_t s);
 hipError_t launch_quant_cols(const void* in, uint8_t* q, uint8_t* sc, int B, int R, int C, int64_t ldo, int col0,
                              const char* name, hipStream_t s);
+hipError_t launch_quant_both(const void* in, uint8_t* qr, uint8_t* sr, uint8_t* qc, uint8_t* scc, int B, int R, int C,
+                             int64_t ldo, int col0, const char* name, hipStream_t s);
 hipError_t launch_gather_t_quant(const void* x, const int* ptok, const int* offsets, const int* qoff, int El, int H,
                                  int64_t qc, uint8_t* q, uint8_t* sc, const char* name, hipStream_t s);
 

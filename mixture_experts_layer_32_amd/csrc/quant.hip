@@ -7,9 +7,13 @@
 //                     One lane per 8 elements; 4 lanes per block of 32.
 //   k_quant_cols      along the strided axis, transposing: W_down[e] (H x F) along H into F x H,
 //                     and W_gate[e], W_up[e] (F x H) along F into the two halves of H x 2F.
+//   k_quant_both      both orientations of one weight tensor from one read (the MXFP8 forward
+//                     quantises each weight once per step for both passes).
 //   k_gather_t_quant  along an expert's pairs, transposing and gathering: dY and x rows of the
 //                     expert's tokens, in the sorted pair order, into [H][Q] where the expert's
-//                     pairs occupy columns qoff[e] .. qoff[e+1] (zero-padded to a multiple of 64).
+//                     pairs occupy columns qoff[e] .. qoff[e+1] (zero-padded to a multiple of 128).
+// The transposing kernels stage 128 x 64 tiles in LDS, so that every row segment they read or
+// write is one whole 128-byte line.
 // The quantised element and scale formulas are in mx_device.h.
 #include "moe_device.h"
 #include "moe_internal.h"
@@ -42,16 +46,17 @@ __global__ __launch_bounds__(256) void k_quant_rows(const bf16* __restrict__ in,
   }
 }
 
-// Column pass shared by the transposing kernels: the block's LDS tile holds 64 source rows of 128
-// columns (bf16). Thread t quantises column t & 127 over rows 32 (t >> 7) .. +31 into 32 output
-// bytes at out_row + 32 (t >> 7) and one scale byte at sc_row + (t >> 7).
-__device__ __forceinline__ void column_pass(const bf16 (*tile)[128], uint8_t* out_row, uint8_t* sc_row) {
-  const int c = threadIdx.x & 127, half = threadIdx.x >> 7;
+// Column pass shared by the transposing kernels: the block's LDS tile holds 128 source rows of 64
+// columns (bf16). Thread t quantises column t & 63 over rows 32 (t >> 6) .. +31 into 32 output
+// bytes at out_row + 32 (t >> 6) and one scale byte at sc_row + (t >> 6). The four threads of a
+// column write one whole 128-byte line.
+__device__ __forceinline__ void column_pass(const bf16 (*tile)[64], uint8_t* out_row, uint8_t* sc_row) {
+  const int c = threadIdx.x & 63, blk = threadIdx.x >> 6;
   float v[32];
   float m = 0.f;
 #pragma unroll
   for (int r = 0; r < 32; ++r) {
-    v[r] = (float)tile[32 * half + r][c];
+    v[r] = (float)tile[32 * blk + r][c];
     m = fmaxf(m, fabsf(v[r]));
   }
   const int s = mx_exponent(m);
@@ -60,37 +65,76 @@ __device__ __forceinline__ void column_pass(const bf16 (*tile)[128], uint8_t* ou
 #pragma unroll
   for (int g = 0; g < 8; ++g)
     w[g] = mx_cvt4(mx_sat(v[4 * g] * sm), mx_sat(v[4 * g + 1] * sm), mx_sat(v[4 * g + 2] * sm), mx_sat(v[4 * g + 3] * sm));
-  uint4* o = reinterpret_cast<uint4*>(out_row + 32 * half);
+  uint4* o = reinterpret_cast<uint4*>(out_row + 32 * blk);
   o[0] = make_uint4(w[0], w[1], w[2], w[3]);
   o[1] = make_uint4(w[4], w[5], w[6], w[7]);
-  sc_row[half] = (uint8_t)(s + 127);
+  sc_row[blk] = (uint8_t)(s + 127);
+}
+
+// Loads rows r0..r0+127, columns c0..c0+63 of a row-major bf16 matrix (row pointers from row_ptr)
+// into the LDS tile: 8 lanes per row, one whole 128-byte line each. Load i of thread t covers row
+// (t >> 3) + 32i, columns 8 (t & 7) .. +7, and is also returned in raw[i].
+template <class RowPtr>
+__device__ __forceinline__ void load_tile(bf16 (*tile)[64], RowPtr row_ptr, uint4 (&raw)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ch = threadIdx.x + 256 * i, row = ch >> 3, c8 = (ch & 7) * 8;
+    const bf16* src = row_ptr(row);
+    raw[i] = src ? ld16(src + c8) : make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint4*>(&tile[row][c8]) = raw[i];
+  }
 }
 
 // in [B][R][C] -> out[b][c][col0 + r] (row stride ldo bytes), scales [b][c][(col0 + r) / 32]
-// (row stride ldo / 32). Grid (C / 128, R / 64, B).
+// (row stride ldo / 32). Grid (C / 64, R / 128, B).
 __global__ __launch_bounds__(256) void k_quant_cols(const bf16* __restrict__ in, uint8_t* __restrict__ q,
                                                     uint8_t* __restrict__ sc, int R, int C, int64_t ldo, int col0) {
-  __shared__ __attribute__((aligned(16))) bf16 tile[64][128];
-  const int b = blockIdx.z, r0 = blockIdx.y * 64, c0 = blockIdx.x * 128, t = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) bf16 tile[128][64];
+  const int b = blockIdx.z, r0 = blockIdx.y * 128, c0 = blockIdx.x * 64;
   const bf16* src = in + ((size_t)b * R + r0) * C + c0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int ch = t + 256 * i, row = ch >> 4, c8 = (ch & 15) * 8;
-    *reinterpret_cast<uint4*>(&tile[row][c8]) = ld16(src + (size_t)row * C + c8);
-  }
+  uint4 raw[4];
+  load_tile(tile, [&](int row) { return src + (size_t)row * C; }, raw);
   __syncthreads();
-  const size_t orow = (size_t)b * C + c0 + (t & 127);
+  const size_t orow = (size_t)b * C + c0 + (threadIdx.x & 63);
   column_pass(tile, q + orow * ldo + col0 + r0, sc + orow * (ldo / 32) + (col0 + r0) / 32);
 }
 
-// Grid (qc / 64, H / 128). Window w covers columns 64w .. 64w+63 of [H][qc], inside one expert's
-// padded segment.
+// Both orientations of one weight tensor in one read: in [B][R][C] ->
+//   rows: qr [B][R][C] with blocks of 32 along C, scales sr [B][R][C/32]
+//   cols: as k_quant_cols (blocks of 32 along R, written transposed at column col0 of rows of ldo)
+// Grid (C / 64, R / 128, B).
+__global__ __launch_bounds__(256) void k_quant_both(const bf16* __restrict__ in, uint8_t* __restrict__ qr,
+                                                    uint8_t* __restrict__ sr, uint8_t* __restrict__ qc,
+                                                    uint8_t* __restrict__ scc, int R, int C, int64_t ldo, int col0) {
+  __shared__ __attribute__((aligned(16))) bf16 tile[128][64];
+  const int b = blockIdx.z, r0 = blockIdx.y * 128, c0 = blockIdx.x * 64;
+  const bf16* src = in + ((size_t)b * R + r0) * C + c0;
+  uint4 raw[4];
+  load_tile(tile, [&](int row) { return src + (size_t)row * C; }, raw);
+  // row pass from registers: the 4 lanes 4g..4g+3 hold one row's block of 32 along C
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v[8];
+    unpack8f(raw[i], v);
+    const int s = mx_exponent(mx_amax_x4(v));
+    const int row = (threadIdx.x >> 3) + 32 * i, c8 = (threadIdx.x & 7) * 8;
+    const size_t grow = (size_t)b * R + r0 + row;
+    *reinterpret_cast<uint2*>(qr + grow * C + c0 + c8) = mx_encode8(v, s);
+    if ((threadIdx.x & 3) == 0) sr[grow * (C / 32) + (c0 + c8) / 32] = (uint8_t)(s + 127);
+  }
+  __syncthreads();
+  const size_t orow = (size_t)b * C + c0 + (threadIdx.x & 63);
+  column_pass(tile, qc + orow * ldo + col0 + r0, scc + orow * (ldo / 32) + (col0 + r0) / 32);
+}
+
+// Grid (qc / 128, H / 64). Window w covers columns 128w .. 128w+127 of [H][qc], inside one
+// expert's padded segment (segments are multiples of 128 columns).
 __global__ __launch_bounds__(256) void k_gather_t_quant(const bf16* __restrict__ x, const int* __restrict__ ptok,
                                                         const int* __restrict__ offsets, const int* __restrict__ qoff,
                                                         int El, int H, int64_t qc, uint8_t* __restrict__ q,
                                                         uint8_t* __restrict__ sc) {
-  __shared__ __attribute__((aligned(16))) bf16 tile[64][128];
-  const int q0 = blockIdx.x * 64, h0 = blockIdx.y * 128, t = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) bf16 tile[128][64];
+  const int q0 = blockIdx.x * 128, h0 = blockIdx.y * 64;
   if (q0 >= qoff[El]) return;   // past the last expert's segment: nothing reads these columns
   int lo = 0, hi = El - 1;      // the expert whose segment holds q0: the last e with qoff[e] <= q0
   while (lo < hi) {
@@ -99,15 +143,10 @@ __global__ __launch_bounds__(256) void k_gather_t_quant(const bf16* __restrict__
     else hi = mid - 1;
   }
   const int base = offsets[lo] + (q0 - qoff[lo]), end = offsets[lo + 1];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int ch = t + 256 * i, row = ch >> 4, c8 = (ch & 15) * 8;
-    const int r = base + row;
-    *reinterpret_cast<uint4*>(&tile[row][c8]) =
-        r < end ? ld16(x + (size_t)ptok[r] * H + h0 + c8) : make_uint4(0u, 0u, 0u, 0u);
-  }
+  uint4 raw[4];
+  load_tile(tile, [&](int row) { return base + row < end ? x + (size_t)ptok[base + row] * H + h0 : nullptr; }, raw);
   __syncthreads();
-  const size_t orow = (size_t)h0 + (t & 127);
+  const size_t orow = (size_t)h0 + (threadIdx.x & 63);
   column_pass(tile, q + orow * qc + q0, sc + orow * (qc / 32) + q0 / 32);
 }
 
@@ -126,7 +165,17 @@ hipError_t launch_quant_rows(const void* in, uint8_t* q, uint8_t* sc, int64_t n,
 hipError_t launch_quant_cols(const void* in, uint8_t* q, uint8_t* sc, int B, int R, int C, int64_t ldo, int col0,
                              const char* name, hipStream_t s) {
   prof_mark_begin(name, s);
-  k_quant_cols<<<dim3(C / 128, R / 64, B), 256, 0, s>>>(static_cast<const bf16*>(in), q, sc, R, C, ldo, col0);
+  k_quant_cols<<<dim3(C / 64, R / 128, B), 256, 0, s>>>(static_cast<const bf16*>(in), q, sc, R, C, ldo, col0);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  prof_mark_end(s);
+  return hipSuccess;
+}
+
+hipError_t launch_quant_both(const void* in, uint8_t* qr, uint8_t* sr, uint8_t* qc, uint8_t* scc, int B, int R, int C,
+                             int64_t ldo, int col0, const char* name, hipStream_t s) {
+  prof_mark_begin(name, s);
+  k_quant_both<<<dim3(C / 64, R / 128, B), 256, 0, s>>>(static_cast<const bf16*>(in), qr, sr, qc, scc, R, C, ldo, col0);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   prof_mark_end(s);
@@ -136,7 +185,7 @@ hipError_t launch_quant_cols(const void* in, uint8_t* q, uint8_t* sc, int B, int
 hipError_t launch_gather_t_quant(const void* x, const int* ptok, const int* offsets, const int* qoff, int El, int H,
                                  int64_t qc, uint8_t* q, uint8_t* sc, const char* name, hipStream_t s) {
   prof_mark_begin(name, s);
-  k_gather_t_quant<<<dim3((unsigned)(qc / 64), H / 128), 256, 0, s>>>(static_cast<const bf16*>(x), ptok, offsets,
+  k_gather_t_quant<<<dim3((unsigned)(qc / 128), H / 64), 256, 0, s>>>(static_cast<const bf16*>(x), ptok, offsets,
                                                                      qoff, El, H, qc, q, sc);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

@@ -91,12 +91,16 @@ def test_mx_sizes_cover_the_layout(mode):
     assert all(v % 256 == 0 for v in (fwd, bwd, saved))
     # routing + a, b (bf16) + the fp8 pair-contiguous hw copy with its scales
     assert saved >= rows * (4 * 4) + rows * 2 * F * 2 + qc * F * (1 + 1 / 32)
-    if mode == "mxfp8":    # quantised x, weights and hw, plus the per-pair outputs
+    if mode == "mxfp8":    # quantised x, weights and hw, plus the per-pair outputs; the weights'
+        # backward orientation is kept in saved
         assert fwd >= rows * H * 2 + T * H * (1 + 1 / 32) + 3 * E * F * H * (1 + 1 / 32) + rows * F * (1 + 1 / 32)
-    else:                  # bf16 hw and its transposed copy, plus the per-pair outputs
-        assert fwd >= rows * H * 2 + rows * F * 2 + qc * F * 2
-    # quantised dy, weights (both orientations), dY^T, x^T, da/db (both orientations), partials, dX'
-    assert bwd >= (T * H + 3 * E * F * H + 2 * H * qc + rows * 2 * F + 2 * F * qc) * (1 + 1 / 32) \
+        assert saved >= rows * 2 * F * 2 + (qc * F + 3 * E * F * H) * (1 + 1 / 32)
+        wq = 0
+    else:                  # bf16 hw (its fp8 transposed copy is in saved), plus the per-pair outputs
+        assert fwd >= rows * H * 2 + rows * F * 2
+        wq = 3 * E * F * H
+    # quantised dy, weights (FP8_BWD), dY^T, x^T, da/db (both orientations), partials, dX'
+    assert bwd >= (T * H + wq + 2 * H * qc + rows * 2 * F + 2 * F * qc) * (1 + 1 / 32) \
         + rows * 4 * 2 * ((F + 255) // 256) + rows * H * 2
 
 
@@ -106,8 +110,8 @@ def test_mx_sizes_cover_the_layout(mode):
     ((FAKE, 0, 64, 1), "MOE_ERR_INVALID_ARG", "positive"),
     ((FAKE, 64, 64, 2), "MOE_ERR_INVALID_ARG", "axis"),
     ((FAKE, 64, 48, 1), "MOE_ERR_UNSUPPORTED_SHAPE", "multiple of 32"),
-    ((FAKE, 96, 128, 0), "MOE_ERR_UNSUPPORTED_SHAPE", "multiple of 64"),
-    ((FAKE, 64, 64, 0), "MOE_ERR_UNSUPPORTED_SHAPE", "multiple of 64"),
+    ((FAKE, 192, 128, 0), "MOE_ERR_UNSUPPORTED_SHAPE", "multiple of 128"),
+    ((FAKE, 128, 96, 0), "MOE_ERR_UNSUPPORTED_SHAPE", "multiple of 128"),
     ((FAKE, 1 << 17, 1 << 17, 1), "MOE_ERR_UNSUPPORTED_SHAPE", r"2\^34"),
 ])
 def test_mx_quantize_validation(args, code, msg):

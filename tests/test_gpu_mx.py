@@ -45,7 +45,7 @@ def _quant_input(rows, cols, seed):
     return v
 
 
-@pytest.mark.parametrize("axis,rows,cols", [(1, 96, 416), (1, 1, 32), (0, 192, 256), (0, 64, 128)])
+@pytest.mark.parametrize("axis,rows,cols", [(1, 96, 416), (1, 1, 32), (0, 256, 192), (0, 128, 64)])
 def test_mx_quantize_bit_exact(axis, rows, cols):
     print(f"case mx_quantize axis={axis} {rows}x{cols}", flush=True)
     # blocks are built along the quantisation axis
@@ -163,3 +163,61 @@ def test_full_size_sampled_mx(mode):
         assert np.all(np.isfinite(got[n])), n
     del got
     torch.cuda.empty_cache()
+
+
+def _e4m3_bytes(el):
+    return torch.from_numpy(np.ascontiguousarray(el)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+@pytest.mark.parametrize("mode", ["mxfp8", "fp8_bwd"])
+def test_mx_operands_left_in_saved(mode):
+    """The forward's MXFP8 operands for the backward: the weights' transposed copies (MXFP8) bit-exact
+    against the oracle's quantiser; w*h along each expert's pairs within 2e-2 of the oracle's (the
+    GPU quantises fp32 h, the oracle float64 h), with zero padding up to the 128-pair boundary."""
+    cfg, L = inputs.custom_layer(T=300, H=256, F=256, E=8, k=2, dtype="bf16", seed=41)
+    print(f"case saved MX operands mode={mode}", flush=True)
+    got = run_layer(cfg, L, mode, keep_layer=True)
+    layer = got.pop("_layer")
+    off = binding.saved_layout(layer.desc)
+    sv = layer.saved.cpu().numpy()
+    El, H, F = cfg.el, cfg.H, cfg.F
+    r = oracle.route(L["logits"], cfg.k, cfg.e0, cfg.el)
+    qc = off["qcols"]
+    qoff = sv[off["qoff"]:off["qoff"] + 4 * (El + 1)].view(np.int32)
+    want_qoff = np.concatenate([[0], np.cumsum(-(-r["counts"] // 128) * 128)])
+    assert np.array_equal(qoff, want_qoff) and qc % 128 == 0 and qc >= qoff[-1]
+    if mode == "mxfp8":
+        wdt = sv[off["wdt"]:off["wdt"] + El * F * H].reshape(El, F, H)
+        wdts = sv[off["wdt_scales"]:off["wdt_scales"] + El * F * H // 32].reshape(El, F, H // 32)
+        wgut = sv[off["wgut"]:off["wgut"] + El * H * 2 * F].reshape(El, H, 2 * F)
+        wguts = sv[off["wgut_scales"]:off["wgut_scales"] + El * H * 2 * F // 32].reshape(El, H, 2 * F // 32)
+        for e in range(El):
+            _, el_, sx = oracle.mx.mx_quantize(L["wd"][e].astype(np.float64), axis=0, return_parts=True)
+            assert np.array_equal(wdt[e], _e4m3_bytes(el_.T)), e
+            assert np.array_equal(wdts[e], (sx + 127).astype(np.uint8)), e     # scales come blocks-last
+            for half, w in ((0, L["wg"][e]), (1, L["wu"][e])):
+                _, el_, sx = oracle.mx.mx_quantize(w.astype(np.float64), axis=0, return_parts=True)
+                assert np.array_equal(wgut[e][:, half * F:(half + 1) * F], _e4m3_bytes(el_.T)), (e, half)
+                assert np.array_equal(wguts[e][:, half * F // 32:(half + 1) * F // 32],
+                                      (sx + 127).astype(np.uint8)), (e, half)
+    else:
+        assert off["wdt"] == 0 and off["wgut"] == 0
+    hwt = sv[off["hwt"]:off["hwt"] + F * qc].reshape(F, qc)
+    hws = sv[off["hwt_scales"]:off["hwt_scales"] + F * qc // 32].reshape(F, qc // 32)
+    x64 = L["x"].astype(np.float64)
+    for e in range(El):
+        pairs = r["perm"][r["offsets"][e]:r["offsets"][e + 1]]
+        n = len(pairs)
+        seg = slice(qoff[e], qoff[e + 1])
+        if n == 0:
+            continue
+        toks, wr = pairs // cfg.k, r["w"].reshape(-1)[pairs]
+        if mode == "mxfp8":
+            _, _, h, _ = oracle.expert_forward_q(x64[toks], wr, L["wg"][e], L["wu"][e], L["wd"][e], True)
+        else:
+            _, _, h, _ = oracle.expert_forward(x64[toks], L["wg"][e], L["wu"][e], L["wd"][e])
+        want = oracle.mx.mx_quantize(wr[:, None] * h, axis=0).T            # [F, n], blocks along the pairs
+        dec = _fp8_values(hwt[:, seg]) * np.repeat(2.0 ** (hws[:, qoff[e] // 32:qoff[e + 1] // 32].astype(np.int64) - 127),
+                                                   32, axis=1)
+        assert oracle.rel_frobenius(dec[:, :n], want) <= 2e-2, e
+        assert not np.any(hwt[:, qoff[e] + n:qoff[e + 1]]), e            # zero padding
