@@ -154,8 +154,9 @@ struct GatherRows {
 // fragments from columns bn[ni]. A K-tile is four 16-deep steps; each step's fragments are read
 // while the previous step's MFMAs run. The ring holds two K-tiles: K-tile kt+1 lands while kt is
 // multiplied. After the last fragments of K-tile kt are read, the wave waits for K-tile kt+1, the
-// barrier publishes it and frees kt's stage, K-tile kt+2 is issued into that stage, and the first
-// fragments of kt+1 are read while the last MFMAs of kt run. On return all LDS reads are done (LDS
+// barrier publishes it and frees kt's stage, A's part of K-tile kt+2 is issued into that stage,
+// and the first fragments of kt+1 are read while the last MFMAs of kt run; B's part of K-tile
+// kt+2 follows those MFMAs. On return all LDS reads are done (LDS
 // may be reused).
 __device__ __forceinline__ bf16x8 frag_k(const char* tile, int row0, int ks, int lane) {
   return *reinterpret_cast<const bf16x8*>(KOp::at(tile, row0 + (lane & 31), 2 * ks + (lane >> 5)));
@@ -226,15 +227,17 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], char* smem, LA& la
       block_sync();
       if (kt + 2 < nk) {
         la.issue(cur, kt + 2);
-        lb.issue(cur + OPB, kt + 2);
-        if (kt + 3 < nk) {
-          la.prefetch(kt + 3);
-          lb.prefetch(kt + 3);
-        }
+        if (kt + 3 < nk) la.prefetch(kt + 3);
       }
       read_frags<AMN, BMN>(fa0, fb0, smem + ((kt + 1) & 1) * STB, 0, am0, bn, lane);
     }
     mma_step(acc, fa1, fb1);
+    // B's loads of K-tile kt+2 go out after the last MFMA step: one burst of all 16 loads per lane
+    // right after the barrier stalled the waves' MFMA issue (measured 2-6 % slower per GEMM)
+    if (kt + 2 < nk) {
+      lb.issue(cur + OPB, kt + 2);
+      if (kt + 3 < nk) lb.prefetch(kt + 3);
+    }
   }
   block_sync();
 }
