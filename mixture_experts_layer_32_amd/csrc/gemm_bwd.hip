@@ -251,53 +251,75 @@ __global__ __launch_bounds__(kThreads, 2) void k_wgrad_gateup(BwdParams p) {
     }
 }
 
+// One wavefront per token, 4 tokens per block. Lane j < k holds slot j: its pair position,
+// weight, expert and g = the sum of its partials. Slot values reach every lane through readlane, so
+// the token's k source rows are addressed from scalar registers.
 template <class T>
 __global__ __launch_bounds__(256) void k_combine_bwd(BwdParams p) {
   constexpr int VEC = Elem<T>::VEC;
-  __shared__ float gs[kMaxTopk];
-  __shared__ float gbar;
-  const int64_t t = blockIdx.x;
-  const int tid = threadIdx.x, k = p.k, H = p.H;
-  if (tid < k) {
-    const int pp = p.pair_pos[t * k + tid];
-    float g = 0.f;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= p.T) return;   // the whole wave leaves
+  const int k = p.k, H = p.H;
+  int pp = -1, ex = -1;
+  float w = 0.f, g = 0.f;
+  if (lane < k) {
+    pp = p.pair_pos[t * k + lane];
+    w = p.weight[t * k + lane];
+    ex = p.idx[t * k + lane];
     if (pp >= 0)
       for (int q = 0; q < p.np; ++q) g += p.gpart[(size_t)q * p.rows + pp];
-    gs[tid] = g;
   }
-  __syncthreads();
-  if (tid == 0) {
-    float s = 0.f;
-    for (int j = 0; j < k; ++j) s += p.weight[t * k + j] * gs[j];
-    gbar = s;
-  }
-  __syncthreads();
-  for (int e = tid; e < p.E; e += 256) {
+  // gbar = sum_j w_j g_j, in slot order
+  const float wg = w * g;
+  float gbar = 0.f;
+  for (int j = 0; j < k; ++j) gbar += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wg), j));
+  const float val = w * (g - gbar);   // dlogits of slot j's expert (lane j)
+  for (int e = lane; e < p.E; e += 64) {
     float v = 0.f;
     for (int j = 0; j < k; ++j)
-      if (p.idx[t * k + j] == e) v = p.weight[t * k + j] * (gs[j] - gbar);
+      if (__builtin_amdgcn_readlane(ex, j) == e) v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, val), j));
     p.dlogits[t * p.E + e] = v;
   }
+  // dx_t = sum over the local slots of dX' rows, fp32 in slot order; 8 slot rows in flight per chunk
   const T* __restrict__ src = static_cast<const T*>(p.dxp);
   T* __restrict__ out = static_cast<T*>(p.dx);
   const int nch = H / VEC;
-  for (int c = tid; c < nch; c += 256) {
-    float acc[VEC];
+  // two chunks per lane at a time (c0 and c0 + 64, the second only if it exists): 16 slot rows in
+  // flight
+  for (int c0 = lane; c0 < nch; c0 += 128) {
+    float acc[2][VEC];
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int pp = p.pair_pos[t * k + j];
-      if (pp < 0) continue;
-      const uint4 raw = ld16(src + (size_t)pp * H + (size_t)c * VEC);
-      const T* ev = reinterpret_cast<const T*>(&raw);
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) acc[v] += (float)ev[v];
+      for (int v = 0; v < VEC; ++v) acc[h][v] = 0.f;
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      uint4 raw[2][8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int ps = j0 + u < k ? __builtin_amdgcn_readlane(pp, j0 + u) : -1;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          raw[h][u] = ps >= 0 && c0 + 64 * h < nch ? ld16(src + (size_t)ps * H + (size_t)(c0 + 64 * h) * VEC)
+                                                   : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const T* ev = reinterpret_cast<const T*>(&raw[h][u]);
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) acc[h][v] += (float)ev[v];
+        }
     }
-    uint4 res;
-    T* r = reinterpret_cast<T*>(&res);
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) r[v] = cvt_out<T>(acc[v]);
-    st16(out + (size_t)t * H + (size_t)c * VEC, res);
+    for (int h = 0; h < 2; ++h) {
+      uint4 res;
+      T* r = reinterpret_cast<T*>(&res);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) r[v] = cvt_out<T>(acc[h][v]);
+      if (c0 + 64 * h < nch) st16(out + (size_t)t * H + (size_t)(c0 + 64 * h) * VEC, res);
+    }
   }
 }
 
@@ -331,7 +353,7 @@ hipError_t launch_backward(const BwdParams& p, int grid, hipStream_t s) {
 template <class T>
 hipError_t launch_combine_bwd(const BwdParams& p, hipStream_t s) {
   prof_mark_begin("combine_bwd", s);
-  k_combine_bwd<T><<<(unsigned)p.T, 256, 0, s>>>(p);
+  k_combine_bwd<T><<<(unsigned)((p.T + 3) / 4), 256, 0, s>>>(p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   prof_mark_end(s);

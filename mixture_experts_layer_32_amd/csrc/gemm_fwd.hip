@@ -9,7 +9,7 @@
 //   k_down     persistent grouped GEMM: o'[r] = hw[r] W_down[e]^T. The routing weight is
 //              already in hw.
 //   k_combine  y_t = sum over the token's local slots of o'[pair_pos]. Gather-sum, fp32
-//              accumulation, one block per token, 16-byte coalesced row reads.
+//              accumulation, one wavefront per token, 16-byte coalesced row reads.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -116,30 +116,53 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(FwdParams p) {
 }
 
 // out[t] = sum over j with pair_pos[t*k+j] >= 0 of src[pair_pos[t*k+j]]; fp32 accumulation in
-// slot order. A token with no local slot gets zeros.
+// slot order. A token with no local slot gets zeros. One wavefront per token, 4 tokens per block;
+// the slots' pair positions reach every lane through readlane, and each chunk keeps 8 slot rows
+// in flight.
 template <class T>
 __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ src, const int* __restrict__ pair_pos,
-                                                 T* __restrict__ out, int k, int H) {
+                                                 T* __restrict__ out, int64_t ntok, int k, int H) {
   constexpr int VEC = Elem<T>::VEC;
-  const int64_t t = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= ntok) return;   // the whole wave leaves
+  const int pp = lane < k ? pair_pos[t * k + lane] : -1;
   const int nch = H / VEC;
-  for (int c = threadIdx.x; c < nch; c += 256) {
-    float acc[VEC];
+  // two chunks per lane at a time (c0 and c0 + 64, the second only if it exists): 16 slot rows in
+  // flight
+  for (int c0 = lane; c0 < nch; c0 += 128) {
+    float acc[2][VEC];
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int pp = pair_pos[t * k + j];
-      if (pp < 0) continue;
-      const uint4 raw = ld16(src + (size_t)pp * H + (size_t)c * VEC);
-      const T* e = reinterpret_cast<const T*>(&raw);
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) acc[v] += (float)e[v];
+      for (int v = 0; v < VEC; ++v) acc[h][v] = 0.f;
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      uint4 raw[2][8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int ps = j0 + u < k ? __builtin_amdgcn_readlane(pp, j0 + u) : -1;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          raw[h][u] = ps >= 0 && c0 + 64 * h < nch ? ld16(src + (size_t)ps * H + (size_t)(c0 + 64 * h) * VEC)
+                                                   : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const T* ev = reinterpret_cast<const T*>(&raw[h][u]);
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) acc[h][v] += (float)ev[v];
+        }
     }
-    uint4 res;
-    T* r = reinterpret_cast<T*>(&res);
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) r[v] = cvt_out<T>(acc[v]);
-    st16(out + (size_t)t * H + (size_t)c * VEC, res);
+    for (int h = 0; h < 2; ++h) {
+      uint4 res;
+      T* r = reinterpret_cast<T*>(&res);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) r[v] = cvt_out<T>(acc[h][v]);
+      if (c0 + 64 * h < nch) st16(out + (size_t)t * H + (size_t)(c0 + 64 * h) * VEC, res);
+    }
   }
 }
 
@@ -161,7 +184,8 @@ template <class T>
 hipError_t launch_combine(const void* src, const int* pair_pos, void* out, int64_t T_, int k, int H,
                           hipStream_t s) {
   prof_mark_begin("combine", s);
-  k_combine<T><<<(unsigned)T_, 256, 0, s>>>(static_cast<const T*>(src), pair_pos, static_cast<T*>(out), k, H);
+  k_combine<T><<<(unsigned)((T_ + 3) / 4), 256, 0, s>>>(static_cast<const T*>(src), pair_pos, static_cast<T*>(out), T_, k,
+                                                      H);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   prof_mark_end(s);
