@@ -2,10 +2,10 @@
 // direct-to-LDS loads and their waits, the K-major LDS layout and fragment reads, the K-major operand
 // loader, and the LDS-staged epilogue helpers.
 //
-// Tile geometry: a workgroup of 4 wavefronts computes a 256x256 output tile, each wave a 128x128
-// quadrant as 4x4 blocks of 32x32 MFMA outputs. Each engine sets its K-tile (the bytes of
-// contraction per operand row) and ring depth. The operand tiles of a K-tile reach LDS with
-// global_load_lds_dwordx4.
+// Tile geometry: a workgroup computes a 256x256 output tile as 32x32 MFMA output blocks. Each wave
+// owns an MI x NJ grid of blocks: with 4 waves a 128x128 quadrant (4x4), with 8 waves a 64x128 or
+// 128x64 eighth. Each engine sets its wave count, K-tile (the bytes of contraction per operand row)
+// and ring depth. The operand tiles of a K-tile reach LDS with global_load_lds_dwordx4.
 #pragma once
 #include "moe_device.h"
 #include "mx_device.h"
@@ -18,7 +18,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int TILE = 256;            // output tile rows and columns
-constexpr int NTHR = 256;
+constexpr int NTHR = 256;            // threads of a 4-wave workgroup
 
 // One wave-wide direct-to-LDS load: lane i copies 16 bytes from g into lds + 16*i (lds is
 // wave-uniform). Written as inline assembly so that the compiler neither tracks it nor inserts
@@ -43,7 +43,7 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 
 // K-major operand of 256 rows with ROWB bytes of contraction per row per K-tile (64 or 128).
 // One wave instruction moves RPI = 64/NCH whole row segments (NCH = ROWB/16 chunks of 16 bytes);
-// this lane owns rows (w*LOADS + j)*RPI + lane/NCH and slot lane%NCH. A 128-byte segment is a
+// with NW waves sharing the tile, this lane owns rows (w*LOADS + j)*RPI + lane/NCH and slot lane%NCH. A 128-byte segment is a
 // whole cache line: the direct-to-LDS path moves twice the bytes per cycle with whole lines as
 // with half lines.
 // LDS: row r at r*ROWB, chunk c at slot c ^ swz(r). A ds_read_b128 serves 16 lanes per pass over
@@ -51,9 +51,9 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 // them over distinct bank groups:
 //   64-byte rows:  4 rows share 256 bytes, swz = (r >> 2) & 3
 //   128-byte rows: 2 rows share 256 bytes, swz = (r >> 1) & 7
-template <int ROWB>
+template <int ROWB, int NW = 4>
 struct KRows {
-  static constexpr int NCH = ROWB / 16, RPI = 64 / NCH, LOADS = TILE / (4 * RPI);
+  static constexpr int NCH = ROWB / 16, RPI = 64 / NCH, LOADS = TILE / (NW * RPI);
   const char* p[LOADS];   // global address of this lane's chunk in K-tile 0
   __device__ __forceinline__ static int swz(int r) { return ROWB == 64 ? (r >> 2) & 3 : (r >> 1) & 7; }
   __device__ __forceinline__ static int row_of(int j) {
@@ -87,30 +87,38 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
 __device__ __forceinline__ void st8(void* p, uint2 v) { *reinterpret_cast<uint2*>(p) = v; }
 // ------------------------------------------------------------------------------------------------
 // Epilogue staging. After the main loop the LDS ring is free. Each wave stages 32 rows of its
-// 128x128 quadrant as fp32 (row stride 132 floats, so the 32 rows of one write land in distinct
-// banks). It then reads them back row-contiguous, so that global loads and stores move whole 128- or
-// 256-byte row segments with 16-byte lanes.
-constexpr int SLD = 132;                       // staged row stride (floats)
-constexpr int SLAB = 32 * SLD;                 // floats per wave
+// NJ blocks of 32 columns as fp32 (row stride 32 NJ + 4 floats, so the 32 rows of one write land in
+// distinct banks). It then reads them back row-contiguous, so that global loads and stores move
+// whole 128- or 256-byte row segments with 16-byte lanes.
+template <int NJ>
+struct Stage {
+  static constexpr int LD = 32 * NJ + 4;       // staged row stride (floats)
+  static constexpr int SIZE = 32 * LD;         // floats per wave
+};
+constexpr int SLD = Stage<4>::LD;
+constexpr int SLAB = Stage<4>::SIZE;
 
+template <int NJ = 4>
 __device__ __forceinline__ float* wave_slab(char* smem) {
-  return reinterpret_cast<float*>(smem) + wave_id() * SLAB;
+  return reinterpret_cast<float*>(smem) + wave_id() * Stage<NJ>::SIZE;
 }
 
-// rows 32i .. 32i+31 of the quadrant; staged column 32j + 8a + 4(lane/32) + b holds block j
-__device__ __forceinline__ void stage_rows(float* slab, const f32x16 (&acc)[4][4], int i, int lane) {
+// rows 32i .. 32i+31 of the wave's blocks; staged column 32j + 8a + 4(lane/32) + b holds block j
+template <int MI, int NJ>
+__device__ __forceinline__ void stage_rows(float* slab, const f32x16 (&acc)[MI][NJ], int i, int lane) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < NJ; ++j)
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       float4 v = make_float4(acc[i][j][4 * a], acc[i][j][4 * a + 1], acc[i][j][4 * a + 2], acc[i][j][4 * a + 3]);
-      *reinterpret_cast<float4*>(slab + (lane & 31) * SLD + 32 * j + acc_n(a, lane)) = v;
+      *reinterpret_cast<float4*>(slab + (lane & 31) * Stage<NJ>::LD + 32 * j + acc_n(a, lane)) = v;
     }
 }
 
+template <int NJ = 4>
 __device__ __forceinline__ void read8(const float* slab, int row, int col, float (&v)[8]) {
-  const float4 x = *reinterpret_cast<const float4*>(slab + row * SLD + col);
-  const float4 y = *reinterpret_cast<const float4*>(slab + row * SLD + col + 4);
+  const float4 x = *reinterpret_cast<const float4*>(slab + row * Stage<NJ>::LD + col);
+  const float4 y = *reinterpret_cast<const float4*>(slab + row * Stage<NJ>::LD + col + 4);
   v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w; v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
 }
 
@@ -124,23 +132,24 @@ __device__ __forceinline__ void unpack8(uint4 u, float (&v)[8]) {
   for (int e = 0; e < 8; ++e) v[e] = (float)b[e];
 }
 
-// Stores the wave's 128x128 quadrant (columns contiguous from the quadrant's first column) as
-// bf16. out_row(m) gives the output row pointer of quadrant row m at the quadrant's first column,
-// or null to skip the row; ncols limits the columns written.
-template <class OutRow>
-__device__ __forceinline__ void store_quadrant(char* smem, const f32x16 (&acc)[4][4], int lane, OutRow out_row,
+// Stores the wave's 32 MI x 32 NJ block of C (columns contiguous from its first column) as bf16.
+// out_row(m) gives the output row pointer of the wave's row m at its first column, or null to skip
+// the row; ncols limits the columns written. A row is read by 4 NJ lanes, 8 columns each.
+template <int MI, int NJ, class OutRow>
+__device__ __forceinline__ void store_quadrant(char* smem, const f32x16 (&acc)[MI][NJ], int lane, OutRow out_row,
                                                int ncols) {
-  float* slab = wave_slab(smem);
+  constexpr int LPR = 4 * NJ, RPP = 64 / LPR;   // lanes per row, rows per pass
+  float* slab = wave_slab<NJ>(smem);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < MI; ++i) {
     stage_rows(slab, acc, i, lane);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int rl = (lane >> 4) + 4 * s, c0 = (lane & 15) * 8;
+    for (int s = 0; s < 32 / RPP; ++s) {
+      const int rl = lane / LPR + RPP * s, c0 = (lane % LPR) * 8;
       bf16* o = out_row(32 * i + rl);
       if (o && c0 < ncols) {
         float v[8];
-        read8(slab, rl, c0, v);
+        read8<NJ>(slab, rl, c0, v);
         st16(o + c0, pack8(v));
       }
     }
@@ -151,7 +160,7 @@ __device__ __forceinline__ void store_quadrant(char* smem, const f32x16 (&acc)[4
 // dst(c) is the copy's row for staged column c, at the pair column of staged row 0 (null: skip).
 // Four lanes cover one column, 8 consecutive pair rows each: one 16-byte store, 64 contiguous bytes
 // per column.
-template <class Dst>
+template <int NJ = 4, class Dst>
 __device__ __forceinline__ void store_transposed(const float* slab, int lane, int ncol, Dst dst) {
   for (int cb = 0; cb < ncol; cb += 16) {
     const int c = cb + (lane >> 2), g8 = 8 * (lane & 3);
@@ -159,7 +168,7 @@ __device__ __forceinline__ void store_transposed(const float* slab, int lane, in
     if (o) {
       float v[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) v[t] = slab[(g8 + t) * SLD + c];
+      for (int t = 0; t < 8; ++t) v[t] = slab[(g8 + t) * Stage<NJ>::LD + c];
       st16(o + g8, pack8(v));
     }
   }
@@ -174,13 +183,13 @@ __device__ __forceinline__ void unpack4(uint2 v, float (&f)[4]) {
 // Writes staged columns [0, ncol) of the 32 staged rows, quantised along the rows (the pairs), to a
 // pair-contiguous transposed fp8 copy. dst(c) is the copy's row for staged column c at the pair
 // column of staged row 0 (a multiple of 32), null to skip; sdst(c) is its scale byte.
-template <class Dst, class SDst>
+template <int NJ = 4, class Dst, class SDst>
 __device__ __forceinline__ void store_transposed_mx(const float* slab, int lane, int ncol, Dst dst, SDst sdst) {
   for (int cb = 0; cb < ncol; cb += 16) {
     const int c = cb + (lane >> 2), g8 = 8 * (lane & 3);
     float v[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) v[t] = slab[(g8 + t) * SLD + c];
+    for (int t = 0; t < 8; ++t) v[t] = slab[(g8 + t) * Stage<NJ>::LD + c];
     const int s = mx_exponent(mx_amax_x4(v));
     uint8_t* o = dst(c);
     if (o) {

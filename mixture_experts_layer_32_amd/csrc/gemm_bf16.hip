@@ -5,8 +5,12 @@
 // il kernel che accelera il training AI del 55%".
 //
 // Engine:
-//  * A workgroup of 4 wavefronts computes a 256x256 output tile, each wave a 128x128 quadrant,
-//    as 4x4 blocks of v_mfma_f32_32x32x16_bf16 with fp32 accumulators (256 per lane, in AGPRs).
+//  * A workgroup of 8 wavefronts (2 per SIMD) computes a 256x256 output tile. Each wave owns a
+//    64x128 eighth as 2x4 blocks of v_mfma_f32_32x32x16_bf16 with fp32 accumulators (128 per
+//    lane), or a 128x64 eighth (4x2 blocks) in the dgrad of h, whose epilogue stages two fp32
+//    slabs. With two waves per SIMD one issues MFMAs while the other waits on LDS, its loads or the
+//    barrier; this outweighs the extra fragment reads (a wave reads 6 fragments per 8 MFMAs instead
+//    of 8 per 16): measured 9 % faster on a dense 8192x8192x2048 product and 20 % at K = 768.
 //  * A K-tile is 64 contraction elements. Operand tiles reach LDS with global_load_lds_dwordx4
 //    (no VGPR staging) through a 2-stage ring of 64 KB stages: K-tile kt+1 lands while kt is
 //    multiplied. Each wave waits for its own loads, then a barrier publishes them.
@@ -34,9 +38,12 @@ namespace {
 
 using namespace eng;
 
+constexpr int NWAVE = 8;             // wavefronts per workgroup
+constexpr int NTHR8 = 64 * NWAVE;
 constexpr int KTILE = 64;            // contraction elements per K-tile: 128 bytes per K-major row
-typedef KRows<128> KOp;              // K-major operand loader (8 rows of 128 bytes per wave instruction)
-constexpr int LOADS = KOp::LOADS;    // 8 direct-to-LDS loads per lane per operand per K-tile
+typedef KRows<128, NWAVE> KOp;       // K-major operand loader (8 rows of 128 bytes per wave instruction)
+constexpr int LOADS = KOp::LOADS;    // 4 direct-to-LDS loads per lane per operand per K-tile
+constexpr int KPW = KTILE / NWAVE;   // contraction rows of an MN-major operand loaded by one wave
 constexpr int OPB = 32768;           // bytes per operand per stage (256 x 128 B, or 64 x 512 B)
 constexpr int STB = 2 * OPB;         // bytes per stage
 constexpr int STAGES = 2;            // LDS ring depth (2 x 64 KB)
@@ -62,10 +69,10 @@ __device__ __forceinline__ bf16x8 frag_mn(const char* tile, int col0, int ks, in
 // K-tile ahead of issue.
 
 // contraction row owned by this lane in load slot j of an MN-major operand (2 rows per slot)
-__device__ __forceinline__ int mn_krow(int j) { return wave_id() * 16 + 2 * j + ((threadIdx.x & 63) >> 5); }
+__device__ __forceinline__ int mn_krow(int j) { return wave_id() * KPW + 2 * j + ((threadIdx.x & 63) >> 5); }
 
 // MN-major operand: 64 contraction rows of 256 columns starting at column col0. This lane owns
-// contraction rows w*16 + 2j + lane/32 (j < 8) and slot lane&31. Each wave instruction moves two
+// contraction rows w*8 + 2j + lane/32 (j < 4) and slot lane&31. Each wave instruction moves two
 // whole 512-byte rows.
 template <class Rows>
 struct MNOp {
@@ -117,23 +124,23 @@ struct WeightRows {
 };
 
 // contraction rows = an expert's pairs, as the token rows of a [T, ld] tensor (ptok maps a
-// sorted pair to its token). The wave's 16 token indices of a K-tile arrive through scalar loads.
+// sorted pair to its token). The wave's 8 token indices of a K-tile arrive through scalar loads.
 struct GatherRows {
   const char* base;
   const int* __restrict__ ptok;
   size_t ld;
   int seg0, seg_end;
-  int tok[16];
-  int tokp[STAGES][16];   // prologue K-tiles
+  int tok[KPW];
+  int tokp[STAGES][KPW];   // prologue K-tiles
   __device__ __forceinline__ void prefetch(int kt) {
-    const int r0 = seg0 + kt * KTILE + wave_id() * 16;
+    const int r0 = seg0 + kt * KTILE + wave_id() * KPW;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) tok[i] = ptok[min(r0 + i, seg_end - 1)];
+    for (int i = 0; i < KPW; ++i) tok[i] = ptok[min(r0 + i, seg_end - 1)];
   }
   __device__ __forceinline__ void prologue_prefetch(int kt) {
-    const int r0 = seg0 + kt * KTILE + wave_id() * 16;
+    const int r0 = seg0 + kt * KTILE + wave_id() * KPW;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) tokp[kt][i] = ptok[min(r0 + i, seg_end - 1)];
+    for (int i = 0; i < KPW; ++i) tokp[kt][i] = ptok[min(r0 + i, seg_end - 1)];
   }
   __device__ __forceinline__ const char* row(int kt, int j) const {
     const int hi = (threadIdx.x & 63) >> 5;
@@ -150,8 +157,8 @@ struct GatherRows {
 };
 
 // ------------------------------------------------------------------------------------------------
-// Main loop: nk K-tiles, accumulating into acc. A rows am0.. of the A tile (wave's quadrant); B
-// fragments from columns bn[ni]. A K-tile is four 16-deep steps; each step's fragments are read
+// Main loop: nk K-tiles, accumulating into the wave's MI x NJ blocks acc. A fragments from rows
+// am0 + 32i of the A tile; B fragments from columns bn[j]. A K-tile is four 16-deep steps; each step's fragments are read
 // while the previous step's MFMAs run. The ring holds two K-tiles: K-tile kt+1 lands while kt is
 // multiplied. After the last fragments of K-tile kt are read, the wave waits for K-tile kt+1, the
 // barrier publishes it and frees kt's stage, A's part of K-tile kt+2 is issued into that stage,
@@ -162,32 +169,33 @@ __device__ __forceinline__ bf16x8 frag_k(const char* tile, int row0, int ks, int
   return *reinterpret_cast<const bf16x8*>(KOp::at(tile, row0 + (lane & 31), 2 * ks + (lane >> 5)));
 }
 
-template <bool AMN, bool BMN>
-__device__ __forceinline__ void read_frags(bf16x8 (&fa)[4], bf16x8 (&fb)[4], const char* st, int ks, int am0,
-                                           const int (&bn)[4], int lane) {
+template <bool AMN, bool BMN, int MI, int NJ>
+__device__ __forceinline__ void read_frags(bf16x8 (&fa)[MI], bf16x8 (&fb)[NJ], const char* st, int ks, int am0,
+                                           const int (&bn)[NJ], int lane) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) fa[i] = AMN ? frag_mn(st, am0 + 32 * i, ks, lane) : frag_k(st, am0 + 32 * i, ks, lane);
+  for (int i = 0; i < MI; ++i) fa[i] = AMN ? frag_mn(st, am0 + 32 * i, ks, lane) : frag_k(st, am0 + 32 * i, ks, lane);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) fb[j] = BMN ? frag_mn(st + OPB, bn[j], ks, lane) : frag_k(st + OPB, bn[j], ks, lane);
+  for (int j = 0; j < NJ; ++j) fb[j] = BMN ? frag_mn(st + OPB, bn[j], ks, lane) : frag_k(st + OPB, bn[j], ks, lane);
 }
 
 // The B fragment is passed as the MFMA's first operand, so each accumulator block holds the
 // transposed 32x32 block: lane l keeps row (l & 31) of C and 4 consecutive columns per group of 4.
-__device__ __forceinline__ void mma_step(f32x16 (&acc)[4][4], const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) {
+template <int MI, int NJ>
+__device__ __forceinline__ void mma_step(f32x16 (&acc)[MI][NJ], const bf16x8 (&fa)[MI], const bf16x8 (&fb)[NJ]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
 }
 
-template <bool AMN, bool BMN, class LA, class LB>
-__device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], char* smem, LA& la, LB& lb, int nk, int am0,
-                                         const int (&bn)[4]) {
+template <bool AMN, bool BMN, int MI, int NJ, class LA, class LB>
+__device__ __forceinline__ void mainloop(f32x16 (&acc)[MI][NJ], char* smem, LA& la, LB& lb, int nk, int am0,
+                                         const int (&bn)[NJ]) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
   if (nk <= 0) return;
@@ -212,7 +220,7 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], char* smem, LA& la
     wait_vm<0>();
   }
   block_sync();
-  bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+  bf16x8 fa0[MI], fb0[NJ], fa1[MI], fb1[NJ];
   read_frags<AMN, BMN>(fa0, fb0, smem, 0, am0, bn, lane);
   for (int kt = 0; kt < nk; ++kt) {
     char* cur = smem + (kt & 1) * STB;
@@ -232,8 +240,8 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], char* smem, LA& la
       read_frags<AMN, BMN>(fa0, fb0, smem + ((kt + 1) & 1) * STB, 0, am0, bn, lane);
     }
     mma_step(acc, fa1, fb1);
-    // B's loads of K-tile kt+2 go out after the last MFMA step: one burst of all 16 loads per lane
-    // right after the barrier stalled the waves' MFMA issue (measured 2-6 % slower per GEMM)
+    // B's loads of K-tile kt+2 go out after the last MFMA step: one burst of all loads right after
+    // the barrier stalled the waves' MFMA issue (measured 2-6 % slower per GEMM with 4 waves)
     if (kt + 2 < nk) {
       lb.issue(cur + OPB, kt + 2);
       if (kt + 3 < nk) lb.prefetch(kt + 3);
@@ -242,7 +250,11 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], char* smem, LA& la
   block_sync();
 }
 
-constexpr int SMEM_BYTES = STAGES * STB > 8 * SLAB * 4 ? STAGES * STB : 8 * SLAB * 4;
+// epilogue staging: one 64-column slab per wave plus a second one (dgrad of h), or one 128-column slab
+constexpr int SLABS_BYTES = 2 * NWAVE * Stage<2>::SIZE * 4 > NWAVE * Stage<4>::SIZE * 4 ? 2 * NWAVE * Stage<2>::SIZE * 4
+                                                                                      : NWAVE * Stage<4>::SIZE * 4;
+constexpr int SMEM_BYTES = STAGES * STB > SLABS_BYTES ? STAGES * STB : SLABS_BYTES;
+static_assert(SMEM_BYTES <= 160 * 1024, "LDS");
 #define MOE_SMEM __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
 
 // ------------------------------------------------------------------------------------------------
@@ -250,9 +262,9 @@ constexpr int SMEM_BYTES = STAGES * STB > 8 * SLAB * 4 ? STAGES * STB : 8 * SLAB
 // QT: the pair-contiguous copy of hw is written as MXFP8 (blocks of 32 along the pairs, quantised
 // from the fp32 values) for an MXFP8 backward, instead of bf16
 template <bool QT>
-__global__ __launch_bounds__(NTHR, 1) void k_gateup_bf16(FwdParams p) {
+__global__ __launch_bounds__(NTHR8, 1) void k_gateup_bf16(FwdParams p) {
   MOE_SMEM
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;   // 64x128 per wave
   const bf16* __restrict__ x = static_cast<const bf16*>(p.x);
   const bf16* __restrict__ wg = static_cast<const bf16*>(p.wg);
   const bf16* __restrict__ wu = static_cast<const bf16*>(p.wu);
@@ -274,11 +286,11 @@ __global__ __launch_bounds__(NTHR, 1) void k_gateup_bf16(FwdParams p) {
       const bf16* wrow = row < 128 ? wg + ((size_t)e * F + nt * 128 + row) * H : wu + ((size_t)e * F + nt * 128 + row - 128) * H;
       lb.p[j] = reinterpret_cast<const char*>(wrow) + 16 * c;
     }
-    float wrow[4];   // routing weight of quadrant row 32i + (lane & 31)
+    float wrow[2];   // routing weight of the wave's row 32i + (lane & 31)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wrow[i] = p.weight[p.perm[min(r0 + 128 * wm + acc_m(i, lane), seg_end - 1)]];
-    f32x16 acc[4][4];
-    mainloop<false, false>(acc, smem, la, lb, H / KTILE, 128 * wm, bn);
+    for (int i = 0; i < 2; ++i) wrow[i] = p.weight[p.perm[min(r0 + 64 * wm + acc_m(i, lane), seg_end - 1)]];
+    f32x16 acc[2][4];
+    mainloop<false, false>(acc, smem, la, lb, H / KTILE, 64 * wm, bn);
     // staged columns 0..63 hold gate columns f0.., 64..127 the matching up columns. After the row
     // pass the gate columns hold hw (zero on rows past the segment), which is then written to the
     // pair-contiguous copy hwT[f][qoff[e] + pair - offsets[e]] as well.
@@ -286,15 +298,15 @@ __global__ __launch_bounds__(NTHR, 1) void k_gateup_bf16(FwdParams p) {
     const int f0 = nt * 128 + 64 * wn;
     bf16* __restrict__ hwt = static_cast<bf16*>(p.hwt);
     const int qend = p.qoff[e + 1];
-    const int colq = p.qoff[e] + (r0 - p.offsets[e]) + 128 * wm;
+    const int colq = p.qoff[e] + (r0 - p.offsets[e]) + 64 * wm;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       stage_rows(slab, acc, i, lane);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int rl = (lane >> 3) + 8 * s, c0 = (lane & 7) * 8;
         const float wt = __shfl(wrow[i], rl);
-        const int r = r0 + 128 * wm + 32 * i + rl;
+        const int r = r0 + 64 * wm + 32 * i + rl;
         float hv[8];
         if (r < seg_end) {
           float av[8], bv[8];
@@ -325,9 +337,9 @@ __global__ __launch_bounds__(NTHR, 1) void k_gateup_bf16(FwdParams p) {
 }
 
 // forward: o' = hw W_down[e]^T
-__global__ __launch_bounds__(NTHR, 1) void k_down_bf16(FwdParams p) {
+__global__ __launch_bounds__(NTHR8, 1) void k_down_bf16(FwdParams p) {
   MOE_SMEM
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;   // 64x128 per wave
   const bf16* __restrict__ hw = static_cast<const bf16*>(p.hw);
   const bf16* __restrict__ wd = static_cast<const bf16*>(p.wd);
   bf16* __restrict__ o = static_cast<bf16*>(p.o);
@@ -346,24 +358,24 @@ __global__ __launch_bounds__(NTHR, 1) void k_down_bf16(FwdParams p) {
       la.p[j] = reinterpret_cast<const char*>(hw + (size_t)r * F) + 16 * c;
       lb.p[j] = reinterpret_cast<const char*>(wd + ((size_t)e * H + nt * TILE + row) * F) + 16 * c;
     }
-    f32x16 acc[4][4];
-    mainloop<false, false>(acc, smem, la, lb, F / KTILE, 128 * wm, bn);
-    const int rq = r0 + 128 * wm;
+    f32x16 acc[2][4];
+    mainloop<false, false>(acc, smem, la, lb, F / KTILE, 64 * wm, bn);
+    const int rq = r0 + 64 * wm;
     bf16* const oq = o + nt * TILE + 128 * wn;
     store_quadrant(smem, acc, lane, [&](int m) { return rq + m < seg_end ? oq + (size_t)(rq + m) * H : nullptr; }, 128);
   }
 }
 
 // backward: u = gather(dY) W_down[e]; epilogue writes g partials, da, db
-__global__ __launch_bounds__(NTHR, 1) void k_bwd_dh_bf16(BwdParams p) {
+__global__ __launch_bounds__(NTHR8, 1) void k_bwd_dh_bf16(BwdParams p) {
   MOE_SMEM
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;   // 128x64 per wave
   const bf16* __restrict__ dy = static_cast<const bf16*>(p.dy);
   const bf16* __restrict__ ab = static_cast<const bf16*>(p.ab);
   bf16* __restrict__ dab = static_cast<bf16*>(p.dab);
   const int H = p.H, F = p.F, ntn = (F + TILE - 1) / TILE;
   const XcdRange xr = xcd_range(*p.num_mtiles2 * ntn);
-  const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
+  const int bn[2] = {64 * wn, 64 * wn + 32};
   for (int tile = xr.first; tile < xr.end; tile += xr.stride) {
     const int mt = tile / ntn, nt = tile - mt * ntn;
     const int2 me = p.mtile2[mt];
@@ -379,42 +391,43 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_dh_bf16(BwdParams p) {
     lb.rows = WeightRows{wbase, wbase, (size_t)F * 2, H};
     lb.zero = static_cast<const char*>(p.zeros);
     lb.init(nt * TILE, F);
-    float wrow[4];   // routing weight of quadrant row 32i + (lane & 31)
+    float wrow[4];   // routing weight of the wave's row 32i + (lane & 31)
 #pragma unroll
     for (int i = 0; i < 4; ++i) wrow[i] = p.weight[p.perm[min(r0 + 128 * wm + acc_m(i, lane), seg_end - 1)]];
-    f32x16 acc[4][4];
+    f32x16 acc[4][2];
     mainloop<false, true>(acc, smem, la, lb, H / KTILE, 128 * wm, bn);
-    // u = dH' staged per 32 rows; each row's 128 columns are read by 16 lanes, 8 columns each. The
+    // u = dH' staged per 32 rows; each row's 64 columns are read by 8 lanes, 8 columns each. The
     // row pass overwrites u with da and fills a second slab with db (zero on rows or columns past
-    // the segment); both then go to the pair-contiguous copy dabT.
-    float* slab = wave_slab(smem);
-    float* slab2 = slab + 4 * SLAB;
+    // the segment); both then go to the pair-contiguous copy dabT. The wave's partial of g over its
+    // 64 columns is partial nt*4 + wn of the row.
+    float* slab = wave_slab<2>(smem);
+    float* slab2 = slab + NWAVE * Stage<2>::SIZE;
     bf16* __restrict__ dabt = static_cast<bf16*>(p.dabt);
-    const int fq = nt * TILE + 128 * wn;
+    const int fq = nt * TILE + 64 * wn;
     const int qend = p.qoff[e + 1];
     const int colq = p.qoff[e] + (r0 - p.offsets[e]) + 128 * wm;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       stage_rows(slab, acc, i, lane);
-      // the 8 rows of this lane: gather every a/b vector first so that the loads overlap
-      uint4 araw[8], braw[8];
+      // the 4 rows of this lane: gather every a/b vector first so that the loads overlap
+      uint4 araw[4], braw[4];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int rl = (lane >> 4) + 4 * s, c0 = (lane & 15) * 8;
+      for (int s = 0; s < 4; ++s) {
+        const int rl = (lane >> 3) + 8 * s, c0 = (lane & 7) * 8;
         const int r = r0 + 128 * wm + 32 * i + rl, f = fq + c0;
         const bf16* abr = ab + (size_t)min(r, seg_end - 1) * 2 * F + min(f, F - 8);
         araw[s] = ld16(abr);
         braw[s] = ld16(abr + F);
       }
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int rl = (lane >> 4) + 4 * s, c0 = (lane & 15) * 8;
+      for (int s = 0; s < 4; ++s) {
+        const int rl = (lane >> 3) + 8 * s, c0 = (lane & 7) * 8;
         const float wt = __shfl(wrow[i], rl);
         const int r = r0 + 128 * wm + 32 * i + rl, f = fq + c0;
         float gsum = 0.f, da[8], db[8];
         if (r < seg_end && f < F) {
           float u[8], av[8], bv[8];
-          read8(slab, rl, c0, u);
+          read8<2>(slab, rl, c0, u);
           unpack8(araw[s], av);
           unpack8(braw[s], bv);
 #pragma unroll
@@ -432,21 +445,21 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_dh_bf16(BwdParams p) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) da[e] = db[e] = 0.f;
         }
-        *reinterpret_cast<float4*>(slab + rl * SLD + c0) = make_float4(da[0], da[1], da[2], da[3]);
-        *reinterpret_cast<float4*>(slab + rl * SLD + c0 + 4) = make_float4(da[4], da[5], da[6], da[7]);
-        *reinterpret_cast<float4*>(slab2 + rl * SLD + c0) = make_float4(db[0], db[1], db[2], db[3]);
-        *reinterpret_cast<float4*>(slab2 + rl * SLD + c0 + 4) = make_float4(db[4], db[5], db[6], db[7]);
+        constexpr int LD = Stage<2>::LD;
+        *reinterpret_cast<float4*>(slab + rl * LD + c0) = make_float4(da[0], da[1], da[2], da[3]);
+        *reinterpret_cast<float4*>(slab + rl * LD + c0 + 4) = make_float4(da[4], da[5], da[6], da[7]);
+        *reinterpret_cast<float4*>(slab2 + rl * LD + c0) = make_float4(db[0], db[1], db[2], db[3]);
+        *reinterpret_cast<float4*>(slab2 + rl * LD + c0 + 4) = make_float4(db[4], db[5], db[6], db[7]);
         gsum += __shfl_xor(gsum, 1);
         gsum += __shfl_xor(gsum, 2);
         gsum += __shfl_xor(gsum, 4);
-        gsum += __shfl_xor(gsum, 8);
-        if (r < seg_end && (lane & 15) == 0) p.gpart[(size_t)(nt * 2 + wn) * p.rows + r] = gsum;
+        if (r < seg_end && (lane & 7) == 0) p.gpart[(size_t)(nt * 4 + wn) * p.rows + r] = gsum;
       }
       const int colb = colq + 32 * i;
-      store_transposed(slab, lane, 128, [&](int c) {
+      store_transposed<2>(slab, lane, 64, [&](int c) {
         return colb < qend && fq + c < F ? dabt + (size_t)(fq + c) * p.qc + colb : nullptr;
       });
-      store_transposed(slab2, lane, 128, [&](int c) {
+      store_transposed<2>(slab2, lane, 64, [&](int c) {
         return colb < qend && fq + c < F ? dabt + (size_t)(F + fq + c) * p.qc + colb : nullptr;
       });
     }
@@ -454,9 +467,9 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_dh_bf16(BwdParams p) {
 }
 
 // backward: dX = [da db] [W_gate[e]; W_up[e]] (contraction over 2F)
-__global__ __launch_bounds__(NTHR, 1) void k_dgrad_x_bf16(BwdParams p) {
+__global__ __launch_bounds__(NTHR8, 1) void k_dgrad_x_bf16(BwdParams p) {
   MOE_SMEM
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;   // 64x128 per wave
   const bf16* __restrict__ dab = static_cast<const bf16*>(p.dab);
   bf16* __restrict__ dxp = static_cast<bf16*>(p.dxp);
   const int H = p.H, F = p.F, ntn = H / TILE;
@@ -478,18 +491,18 @@ __global__ __launch_bounds__(NTHR, 1) void k_dgrad_x_bf16(BwdParams p) {
                          (size_t)H * 2, F};
     lb.zero = static_cast<const char*>(p.zeros);
     lb.init(nt * TILE, H);
-    f32x16 acc[4][4];
-    mainloop<false, true>(acc, smem, la, lb, 2 * F / KTILE, 128 * wm, bn);
-    const int rq = r0 + 128 * wm;
+    f32x16 acc[2][4];
+    mainloop<false, true>(acc, smem, la, lb, 2 * F / KTILE, 64 * wm, bn);
+    const int rq = r0 + 64 * wm;
     bf16* const oq = dxp + nt * TILE + 128 * wn;
     store_quadrant(smem, acc, lane, [&](int m) { return rq + m < seg_end ? oq + (size_t)(rq + m) * H : nullptr; }, 128);
   }
 }
 
 // backward: dW_down[e] (H x F) = sum over the expert's pairs of dY_t hw_r^T
-__global__ __launch_bounds__(NTHR, 1) void k_wgrad_down_bf16(BwdParams p) {
+__global__ __launch_bounds__(NTHR8, 1) void k_wgrad_down_bf16(BwdParams p) {
   MOE_SMEM
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;   // 64x128 per wave
   const int H = p.H, F = p.F, ntn = (F + TILE - 1) / TILE, tpe = (H / TILE) * ntn;
   const XcdRange xr = xcd_range(p.El * tpe);
   for (int lid = xr.first; lid < xr.end; lid += xr.stride) {
@@ -509,18 +522,18 @@ __global__ __launch_bounds__(NTHR, 1) void k_wgrad_down_bf16(BwdParams p) {
     lb.p[j] = reinterpret_cast<const char*>(hwt + (size_t)n * p.qc) + 16 * KOp::chunk_of(j);
   }
   const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
-  f32x16 acc[4][4];
-  mainloop<true, false>(acc, smem, la, lb, (seg_end - seg0 + KTILE - 1) / KTILE, 128 * wm, bn);
+  f32x16 acc[2][4];
+  mainloop<true, false>(acc, smem, la, lb, (seg_end - seg0 + KTILE - 1) / KTILE, 64 * wm, bn);
   bf16* __restrict__ out = static_cast<bf16*>(p.dwd) + (size_t)e * H * F;
-  const int mq = mt * TILE + 128 * wm, nq = nt * TILE + 128 * wn;
+  const int mq = mt * TILE + 64 * wm, nq = nt * TILE + 128 * wn;
   store_quadrant(smem, acc, lane, [&](int m) { return out + (size_t)(mq + m) * F + nq; }, F - nq);
   }
 }
 
 // backward: [dW_gate; dW_up][e] (2F x H) = sum over the expert's pairs of [da; db]_r x_t^T
-__global__ __launch_bounds__(NTHR, 1) void k_wgrad_gateup_bf16(BwdParams p) {
+__global__ __launch_bounds__(NTHR8, 1) void k_wgrad_gateup_bf16(BwdParams p) {
   MOE_SMEM
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;   // 64x128 per wave
   const int H = p.H, F = p.F, ntn = H / TILE, tpe = (2 * F / TILE) * ntn;
   const XcdRange xr = xcd_range(p.El * tpe);
   for (int lid = xr.first; lid < xr.end; lid += xr.stride) {
@@ -540,11 +553,11 @@ __global__ __launch_bounds__(NTHR, 1) void k_wgrad_gateup_bf16(BwdParams p) {
   lb.zero = static_cast<const char*>(p.zeros);
   lb.init(nt * TILE, H);
   const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
-  f32x16 acc[4][4];
-  mainloop<false, true>(acc, smem, la, lb, (seg_end - seg0 + KTILE - 1) / KTILE, 128 * wm, bn);
+  f32x16 acc[2][4];
+  mainloop<false, true>(acc, smem, la, lb, (seg_end - seg0 + KTILE - 1) / KTILE, 64 * wm, bn);
   bf16* __restrict__ dwg = static_cast<bf16*>(p.dwg) + (size_t)e * F * H;
   bf16* __restrict__ dwu = static_cast<bf16*>(p.dwu) + (size_t)e * F * H;
-  const int mq = mt * TILE + 128 * wm, nq = nt * TILE + 128 * wn;
+  const int mq = mt * TILE + 64 * wm, nq = nt * TILE + 128 * wn;
   store_quadrant(smem, acc, lane, [&](int m) {
     const int mm = mq + m;
     return (mm < F ? dwg + (size_t)mm * H : dwu + (size_t)(mm - F) * H) + nq;
@@ -557,12 +570,12 @@ __global__ __launch_bounds__(NTHR, 1) void k_wgrad_gateup_bf16(BwdParams p) {
 hipError_t launch_forward_gemms_bf16(const FwdParams& p, int grid, hipStream_t s) {
   hipError_t err;
   prof_mark_begin("gemm_gateup_swiglu", s);
-  if (p.hwtq) k_gateup_bf16<true><<<grid, NTHR, 0, s>>>(p);
-  else k_gateup_bf16<false><<<grid, NTHR, 0, s>>>(p);
+  if (p.hwtq) k_gateup_bf16<true><<<grid, NTHR8, 0, s>>>(p);
+  else k_gateup_bf16<false><<<grid, NTHR8, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   prof_mark_end(s);
   prof_mark_begin("gemm_down", s);
-  k_down_bf16<<<grid, NTHR, 0, s>>>(p);
+  k_down_bf16<<<grid, NTHR8, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   prof_mark_end(s);
   return hipSuccess;
@@ -571,19 +584,19 @@ hipError_t launch_forward_gemms_bf16(const FwdParams& p, int grid, hipStream_t s
 hipError_t launch_backward_gemms_bf16(const BwdParams& p, int grid, hipStream_t s) {
   hipError_t err;
   prof_mark_begin("gemm_bwd_dh_dswiglu", s);
-  k_bwd_dh_bf16<<<grid, NTHR, 0, s>>>(p);
+  k_bwd_dh_bf16<<<grid, NTHR8, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   prof_mark_end(s);
   prof_mark_begin("gemm_wgrad_down", s);
-  k_wgrad_down_bf16<<<grid, NTHR, 0, s>>>(p);
+  k_wgrad_down_bf16<<<grid, NTHR8, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   prof_mark_end(s);
   prof_mark_begin("gemm_wgrad_gateup", s);
-  k_wgrad_gateup_bf16<<<grid, NTHR, 0, s>>>(p);
+  k_wgrad_gateup_bf16<<<grid, NTHR8, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   prof_mark_end(s);
   prof_mark_begin("gemm_dgrad_x", s);
-  k_dgrad_x_bf16<<<grid, NTHR, 0, s>>>(p);
+  k_dgrad_x_bf16<<<grid, NTHR8, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   prof_mark_end(s);
   return hipSuccess;

@@ -28,7 +28,9 @@ Layout make_layout(const moe_desc& d) {
   L.nblk_route = (int)((d.T + kRouteTokens - 1) / kRouteTokens);
   L.mtile_cap = (int)(L.rows / kBM) + d.E_local + 1;
   L.mtile2_cap = (int)(L.rows / kBM2) + d.E_local + 1;
-  L.np = d.mode == MOE_MODE_FP32 ? d.F / 64 : 2 * ((d.F + 255) / 256);
+  // partial sums of g per pair, one per wave and 256-column tile of the dgrad of h: the fp32 engine's
+  // 64-column tiles, the bf16 engine's 4 waves across a tile, the fp8 engine's 2
+  L.np = d.mode == MOE_MODE_FP32 ? d.F / 64 : (L.mx ? 2 : 4) * ((d.F + 255) / 256);
   L.elem = d.mode == MOE_MODE_FP32 ? 4 : 2;
   // Pair-contiguous transposed copies (bf16 and fp8 engines): every expert's segment is padded to
   // qpad columns. The bf16 engine reads 64-pair K-tiles; the fp8 engine needs an even number of

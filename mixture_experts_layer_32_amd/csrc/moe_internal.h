@@ -21,7 +21,7 @@ struct Layout {
   int nblk_route;      // ceil(T / kRouteTokens)
   int mtile_cap;       // upper bound on 128-row M-tiles: rows / kBM + E_local + 1
   int mtile2_cap;      // upper bound on 256-row M-tiles
-  int np;              // partial sums of g per pair: F / 64 (fp32 engine), 2*ceil(F/256) (bf16/fp8 engines)
+  int np;              // partial sums of g per pair: F / 64 (fp32), 4*ceil(F/256) (bf16), 2*ceil(F/256) (fp8)
   size_t elem;         // bytes per stored element (4 or 2)
   int qpad;            // pair-contiguous segments are padded to a multiple of qpad pairs (32, or 64 in MX modes)
   bool mx;             // MXFP8 or FP8_BWD
