@@ -315,9 +315,9 @@ __global__ __launch_bounds__(NTHR8, 1) void k_gateup_bf16(FwdParams p) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) hv[e] = wt * (av[e] * sigmoidf_(av[e]) * bv[e]);
           bf16* abr = ab + (size_t)r * 2 * F + f0 + c0;
-          st16(abr, pack8(av));
-          st16(abr + F, pack8(bv));
-          st16(hw + (size_t)r * F + f0 + c0, pack8(hv));
+          st16_nt(abr, pack8(av));
+          st16_nt(abr + F, pack8(bv));
+          st16_nt(hw + (size_t)r * F + f0 + c0, pack8(hv));
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) hv[e] = 0.f;
@@ -439,8 +439,8 @@ __global__ __launch_bounds__(NTHR8, 1) void k_bwd_dh_bf16(BwdParams p) {
             db[e] = dh * si;
           }
           bf16* dabr = dab + (size_t)r * 2 * F + f;
-          st16(dabr, pack8(da));
-          st16(dabr + F, pack8(db));
+          st16_nt(dabr, pack8(da));
+          st16_nt(dabr + F, pack8(db));
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) da[e] = db[e] = 0.f;

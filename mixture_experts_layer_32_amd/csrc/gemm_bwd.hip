@@ -300,7 +300,7 @@ __global__ __launch_bounds__(256) void k_combine_bwd(BwdParams p) {
         const int ps = j0 + u < k ? __builtin_amdgcn_readlane(pp, j0 + u) : -1;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          raw[h][u] = ps >= 0 && c0 + 64 * h < nch ? ld16(src + (size_t)ps * H + (size_t)(c0 + 64 * h) * VEC)
+          raw[h][u] = ps >= 0 && c0 + 64 * h < nch ? ld16_nt(src + (size_t)ps * H + (size_t)(c0 + 64 * h) * VEC)
                                                    : make_uint4(0u, 0u, 0u, 0u);
       }
 #pragma unroll

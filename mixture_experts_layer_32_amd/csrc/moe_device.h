@@ -35,6 +35,13 @@ __device__ __forceinline__ int lds_off(int row, int c) { return row * kRowBytes 
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+// 16-byte load of data read once (the combine's per-pair rows): non-temporal, so that it does not
+// stay in L2
+__device__ __forceinline__ uint4 ld16_nt(const void* p) {
+  typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+  const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // ---------------------------------------------------------------------------------------------
 // MFMA micro-step on one 16x16 output block. Lane l supplies row (l & 15) of A and column
