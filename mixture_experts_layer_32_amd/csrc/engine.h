@@ -41,6 +41,47 @@ __device__ __forceinline__ void block_sync() {
 }
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// Dynamic tile scheduler of the persistent kernels. The tile list is cut into 8 contiguous ranges,
+// one per XCD (workgroups are dispatched to the XCDs round-robin: workgroup b runs on XCD b % 8), so
+// that the workgroups sharing an XCD's L2 work on neighbouring tiles, which share operands. Within
+// its range, an XCD's workgroups take tiles in order from a counter, one atomic increment per tile,
+// so that a workgroup that drew cheaper tiles (an expert's half tile) takes more of them. ctr points
+// at the kernel's 8 per-XCD counters, zero at launch. Every thread of the workgroup calls first()
+// and next(); both contain a barrier, and return the next tile, or -1 once the range is exhausted.
+// Between them the tile's work calls fetch() once, after its main loop (so that the returned
+// counter does not occupy a register through the loop, and its latency hides behind the epilogue);
+// the work must contain a barrier before next(), which overwrites the LDS slot. Without fetch(),
+// next() ends the loop.
+struct TileSched {
+  int* ctr;
+  int begin, end, nxt;
+  __device__ __forceinline__ TileSched(int* counters, int total) {
+    const int xcd = blockIdx.x & 7, per = (total + 7) >> 3;
+    begin = min(total, xcd * per);
+    end = min(total, begin + per);
+    ctr = counters + xcd;
+    nxt = 0;
+  }
+  __device__ __forceinline__ int take(int t) {
+    nxt = end - begin;   // past the range unless fetch() runs
+    const int tile = begin + t;
+    return tile < end ? tile : -1;
+  }
+  __device__ __forceinline__ void fetch() {
+    if (threadIdx.x == 0) nxt = atomicAdd(ctr, 1);
+  }
+  __device__ __forceinline__ int first(int* slot) {
+    if (threadIdx.x == 0) *slot = atomicAdd(ctr, 1);
+    block_sync();
+    return take(*slot);
+  }
+  __device__ __forceinline__ int next(int* slot) {
+    if (threadIdx.x == 0) *slot = nxt;
+    block_sync();
+    return take(*slot);
+  }
+};
+
 // K-major operand of 256 rows with ROWB bytes of contraction per row per K-tile (64 or 128).
 // One wave instruction moves RPI = 64/NCH whole row segments (NCH = ROWB/16 chunks of 16 bytes);
 // with NW waves sharing the tile, this lane owns rows (w*LOADS + j)*RPI + lane/NCH and slot lane%NCH. A 128-byte segment is a

@@ -28,8 +28,12 @@
 //    outputs. When they would contribute to a contraction, they read the zero page. The token
 //    indices of gathered contraction rows come through scalar loads, so that the vector memory
 //    counter tracks nothing but the tile loads.
-//  * The row-tiled kernels are persistent. Each XCD takes one contiguous range of the
-//    expert-major tile list, so the blocks sharing an expert's operands share that XCD's L2.
+//  * The kernels are persistent. Each XCD takes one contiguous range of the expert-major tile list,
+//    so the blocks sharing an expert's operands share that XCD's L2. The row-tiled kernels hand out
+//    the tiles of a range dynamically (TileSched), since an expert's last tile may be a half tile;
+//    the others assign them round-robin (the weight-gradient tiles cost the same within an expert,
+//    and the dynamic order measured 3-5 % slower there; the dgrad of h, with its 128x64 waves, ran
+//    its half-tile form 15 % slower, through register pressure).
 #include "engine.h"
 #include "moe_internal.h"
 
@@ -169,28 +173,36 @@ __device__ __forceinline__ bf16x8 frag_k(const char* tile, int row0, int ks, int
   return *reinterpret_cast<const bf16x8*>(KOp::at(tile, row0 + (lane & 31), 2 * ks + (lane >> 5)));
 }
 
-template <bool AMN, bool BMN, int MI, int NJ>
+// A fragments of the first NA row blocks (rows am0 + AST i), B fragments of every column block
+template <bool AMN, bool BMN, int AST, int NA, int MI, int NJ>
 __device__ __forceinline__ void read_frags(bf16x8 (&fa)[MI], bf16x8 (&fb)[NJ], const char* st, int ks, int am0,
                                            const int (&bn)[NJ], int lane) {
 #pragma unroll
-  for (int i = 0; i < MI; ++i) fa[i] = AMN ? frag_mn(st, am0 + 32 * i, ks, lane) : frag_k(st, am0 + 32 * i, ks, lane);
+  for (int i = 0; i < NA; ++i) fa[i] = AMN ? frag_mn(st, am0 + AST * i, ks, lane) : frag_k(st, am0 + AST * i, ks, lane);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) fb[j] = BMN ? frag_mn(st + OPB, bn[j], ks, lane) : frag_k(st + OPB, bn[j], ks, lane);
 }
 
 // The B fragment is passed as the MFMA's first operand, so each accumulator block holds the
 // transposed 32x32 block: lane l keeps row (l & 31) of C and 4 consecutive columns per group of 4.
-template <int MI, int NJ>
+template <int NA, int MI, int NJ>
 __device__ __forceinline__ void mma_step(f32x16 (&acc)[MI][NJ], const bf16x8 (&fa)[MI], const bf16x8 (&fb)[NJ]) {
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+  for (int i = 0; i < NA; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
 }
 
-template <bool AMN, bool BMN, int MI, int NJ, class LA, class LB>
+// Row block i of the wave's A rows starts at am0 + AST i. Only the first NA row blocks run (NA < MI:
+// the rows of the others are known to be past the segment; their accumulators stay zero).
+// With NA < MI (half tile) the A rows from 128 on are not needed: the waves that load them (waves
+// 4-7, K-major A) skip those loads, and wait for their B loads only.
+template <bool AMN, bool BMN, int AST = 32, int NA = 0, int MI, int NJ, class LA, class LB>
 __device__ __forceinline__ void mainloop(f32x16 (&acc)[MI][NJ], char* smem, LA& la, LB& lb, int nk, int am0,
                                          const int (&bn)[NJ]) {
+  constexpr int ACT = NA ? NA : MI;
+  static_assert(ACT == MI || !AMN, "half tiles take a K-major A");
+  const bool skip_a = ACT < MI && wave_id() >= NWAVE / 2;
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < MI; ++i)
@@ -206,40 +218,42 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[MI][NJ], char* smem, LA& 
     la.prologue_prefetch(s);
     lb.prologue_prefetch(s);
   }
-  la.prologue_issue(smem, 0);
+  if (!skip_a) la.prologue_issue(smem, 0);
   lb.prologue_issue(smem + OPB, 0);
   if (nk > 1) {
-    la.prologue_issue(smem + STB, 1);
+    if (!skip_a) la.prologue_issue(smem + STB, 1);
     lb.prologue_issue(smem + STB + OPB, 1);
     if (nk > 2) {
       la.prefetch(2);
       lb.prefetch(2);
     }
-    wait_vm<2 * LOADS>();   // K-tile 0 landed; K-tile 1 may still be in flight
+    // K-tile 0 landed; K-tile 1 may still be in flight
+    if (skip_a) wait_vm<LOADS>();
+    else wait_vm<2 * LOADS>();
   } else {
     wait_vm<0>();
   }
   block_sync();
   bf16x8 fa0[MI], fb0[NJ], fa1[MI], fb1[NJ];
-  read_frags<AMN, BMN>(fa0, fb0, smem, 0, am0, bn, lane);
+  read_frags<AMN, BMN, AST, ACT>(fa0, fb0, smem, 0, am0, bn, lane);
   for (int kt = 0; kt < nk; ++kt) {
     char* cur = smem + (kt & 1) * STB;
-    read_frags<AMN, BMN>(fa1, fb1, cur, 1, am0, bn, lane);
-    mma_step(acc, fa0, fb0);
-    read_frags<AMN, BMN>(fa0, fb0, cur, 2, am0, bn, lane);
-    mma_step(acc, fa1, fb1);
-    read_frags<AMN, BMN>(fa1, fb1, cur, 3, am0, bn, lane);
-    mma_step(acc, fa0, fb0);
+    read_frags<AMN, BMN, AST, ACT>(fa1, fb1, cur, 1, am0, bn, lane);
+    mma_step<ACT>(acc, fa0, fb0);
+    read_frags<AMN, BMN, AST, ACT>(fa0, fb0, cur, 2, am0, bn, lane);
+    mma_step<ACT>(acc, fa1, fb1);
+    read_frags<AMN, BMN, AST, ACT>(fa1, fb1, cur, 3, am0, bn, lane);
+    mma_step<ACT>(acc, fa0, fb0);
     if (kt + 1 < nk) {
       wait_vm<0>();   // K-tile kt+1 (the only tile in flight) has landed
       block_sync();
       if (kt + 2 < nk) {
-        la.issue(cur, kt + 2);
+        if (!skip_a) la.issue(cur, kt + 2);
         if (kt + 3 < nk) la.prefetch(kt + 3);
       }
-      read_frags<AMN, BMN>(fa0, fb0, smem + ((kt + 1) & 1) * STB, 0, am0, bn, lane);
+      read_frags<AMN, BMN, AST, ACT>(fa0, fb0, smem + ((kt + 1) & 1) * STB, 0, am0, bn, lane);
     }
-    mma_step(acc, fa1, fb1);
+    mma_step<ACT>(acc, fa1, fb1);
     // B's loads of K-tile kt+2 go out after the last MFMA step: one burst of all loads right after
     // the barrier stalled the waves' MFMA issue (measured 2-6 % slower per GEMM with 4 waves)
     if (kt + 2 < nk) {
@@ -253,6 +267,18 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[MI][NJ], char* smem, LA& 
 // epilogue staging: one 64-column slab per wave plus a second one (dgrad of h), or one 128-column slab
 constexpr int SLABS_BYTES = 2 * NWAVE * Stage<2>::SIZE * 4 > NWAVE * Stage<4>::SIZE * 4 ? 2 * NWAVE * Stage<2>::SIZE * 4
                                                                                       : NWAVE * Stage<4>::SIZE * 4;
+// Row-tiled kernels: the wave's row blocks are interleaved (block i at tile row am0 + AST i, with
+// AST x MI = 256), so that the first 128 rows of the tile are the first MI/2 blocks of every wave.
+// An expert's last tile with at most 128 valid rows (half tile) runs only those: each wave does
+// half the MFMAs.
+template <bool AMN, bool BMN, int AST, int MI, int NJ, class LA, class LB>
+__device__ __forceinline__ void mainloop_rows(f32x16 (&acc)[MI][NJ], char* smem, LA& la, LB& lb, int nk, int am0,
+                                              const int (&bn)[NJ], bool half) {
+  static_assert(AST * MI == TILE, "row blocks");
+  if (half) mainloop<AMN, BMN, AST, MI / 2>(acc, smem, la, lb, nk, am0, bn);
+  else mainloop<AMN, BMN, AST, MI>(acc, smem, la, lb, nk, am0, bn);
+}
+
 constexpr int SMEM_BYTES = STAGES * STB > SLABS_BYTES ? STAGES * STB : SLABS_BYTES;
 static_assert(SMEM_BYTES <= 160 * 1024, "LDS");
 #define MOE_SMEM __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
@@ -271,9 +297,10 @@ __global__ __launch_bounds__(NTHR8, 1) void k_gateup_bf16(FwdParams p) {
   bf16* __restrict__ ab = static_cast<bf16*>(p.ab);
   bf16* __restrict__ hw = static_cast<bf16*>(p.hw);
   const int H = p.H, F = p.F, ntn = F / 128;
-  const XcdRange xr = xcd_range(*p.num_mtiles2 * ntn);
+  __shared__ int s_tile;
+  TileSched ts(p.sched + 0 * kSchedInts, *p.num_mtiles2 * ntn);
   const int bn[4] = {64 * wn, 64 * wn + 32, 128 + 64 * wn, 128 + 64 * wn + 32};
-  for (int tile = xr.first; tile < xr.end; tile += xr.stride) {
+  for (int tile = ts.first(&s_tile); tile >= 0; tile = ts.next(&s_tile)) {
     const int mt = tile / ntn, nt = tile - mt * ntn;
     const int2 me = p.mtile2[mt];
     const int e = me.x, r0 = me.y, seg_end = p.offsets[e + 1];
@@ -286,11 +313,12 @@ __global__ __launch_bounds__(NTHR8, 1) void k_gateup_bf16(FwdParams p) {
       const bf16* wrow = row < 128 ? wg + ((size_t)e * F + nt * 128 + row) * H : wu + ((size_t)e * F + nt * 128 + row - 128) * H;
       lb.p[j] = reinterpret_cast<const char*>(wrow) + 16 * c;
     }
-    float wrow[2];   // routing weight of the wave's row 32i + (lane & 31)
+    float wrow[2];   // routing weight of tile row 32 wm + 128 i + (lane & 31)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) wrow[i] = p.weight[p.perm[min(r0 + 64 * wm + acc_m(i, lane), seg_end - 1)]];
+    for (int i = 0; i < 2; ++i) wrow[i] = p.weight[p.perm[min(r0 + 32 * wm + 128 * i + (lane & 31), seg_end - 1)]];
     f32x16 acc[2][4];
-    mainloop<false, false>(acc, smem, la, lb, H / KTILE, 64 * wm, bn);
+    mainloop_rows<false, false, 128>(acc, smem, la, lb, H / KTILE, 32 * wm, bn, seg_end - r0 <= 128);
+    ts.fetch();
     // staged columns 0..63 hold gate columns f0.., 64..127 the matching up columns. After the row
     // pass the gate columns hold hw (zero on rows past the segment), which is then written to the
     // pair-contiguous copy hwT[f][qoff[e] + pair - offsets[e]] as well.
@@ -298,7 +326,7 @@ __global__ __launch_bounds__(NTHR8, 1) void k_gateup_bf16(FwdParams p) {
     const int f0 = nt * 128 + 64 * wn;
     bf16* __restrict__ hwt = static_cast<bf16*>(p.hwt);
     const int qend = p.qoff[e + 1];
-    const int colq = p.qoff[e] + (r0 - p.offsets[e]) + 64 * wm;
+    const int colq = p.qoff[e] + (r0 - p.offsets[e]) + 32 * wm;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       stage_rows(slab, acc, i, lane);
@@ -306,7 +334,7 @@ __global__ __launch_bounds__(NTHR8, 1) void k_gateup_bf16(FwdParams p) {
       for (int s = 0; s < 4; ++s) {
         const int rl = (lane >> 3) + 8 * s, c0 = (lane & 7) * 8;
         const float wt = __shfl(wrow[i], rl);
-        const int r = r0 + 64 * wm + 32 * i + rl;
+        const int r = r0 + 32 * wm + 128 * i + rl;
         float hv[8];
         if (r < seg_end) {
           float av[8], bv[8];
@@ -325,7 +353,7 @@ __global__ __launch_bounds__(NTHR8, 1) void k_gateup_bf16(FwdParams p) {
         *reinterpret_cast<float4*>(slab + rl * SLD + c0) = make_float4(hv[0], hv[1], hv[2], hv[3]);
         *reinterpret_cast<float4*>(slab + rl * SLD + c0 + 4) = make_float4(hv[4], hv[5], hv[6], hv[7]);
       }
-      const int colb = colq + 32 * i;
+      const int colb = colq + 128 * i;
       if (QT)
         store_transposed_mx(
             slab, lane, 64, [&](int c) { return colb < qend ? p.hwtq + (size_t)(f0 + c) * p.qc + colb : nullptr; },
@@ -344,9 +372,10 @@ __global__ __launch_bounds__(NTHR8, 1) void k_down_bf16(FwdParams p) {
   const bf16* __restrict__ wd = static_cast<const bf16*>(p.wd);
   bf16* __restrict__ o = static_cast<bf16*>(p.o);
   const int H = p.H, F = p.F, ntn = H / TILE;
-  const XcdRange xr = xcd_range(*p.num_mtiles2 * ntn);
+  __shared__ int s_tile;
+  TileSched ts(p.sched + 1 * kSchedInts, *p.num_mtiles2 * ntn);
   const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
-  for (int tile = xr.first; tile < xr.end; tile += xr.stride) {
+  for (int tile = ts.first(&s_tile); tile >= 0; tile = ts.next(&s_tile)) {
     const int mt = tile / ntn, nt = tile - mt * ntn;
     const int2 me = p.mtile2[mt];
     const int e = me.x, r0 = me.y, seg_end = p.offsets[e + 1];
@@ -359,10 +388,14 @@ __global__ __launch_bounds__(NTHR8, 1) void k_down_bf16(FwdParams p) {
       lb.p[j] = reinterpret_cast<const char*>(wd + ((size_t)e * H + nt * TILE + row) * F) + 16 * c;
     }
     f32x16 acc[2][4];
-    mainloop<false, false>(acc, smem, la, lb, F / KTILE, 64 * wm, bn);
-    const int rq = r0 + 64 * wm;
+    mainloop_rows<false, false, 128>(acc, smem, la, lb, F / KTILE, 32 * wm, bn, seg_end - r0 <= 128);
+    ts.fetch();
+    const int rq = r0 + 32 * wm;   // the wave's row m is tile row 32 wm + 128 (m / 32) + m % 32
     bf16* const oq = o + nt * TILE + 128 * wn;
-    store_quadrant(smem, acc, lane, [&](int m) { return rq + m < seg_end ? oq + (size_t)(rq + m) * H : nullptr; }, 128);
+    store_quadrant(smem, acc, lane, [&](int m) {
+      const int r = rq + 128 * (m >> 5) + (m & 31);
+      return r < seg_end ? oq + (size_t)r * H : nullptr;
+    }, 128);
   }
 }
 
@@ -473,9 +506,10 @@ __global__ __launch_bounds__(NTHR8, 1) void k_dgrad_x_bf16(BwdParams p) {
   const bf16* __restrict__ dab = static_cast<const bf16*>(p.dab);
   bf16* __restrict__ dxp = static_cast<bf16*>(p.dxp);
   const int H = p.H, F = p.F, ntn = H / TILE;
-  const XcdRange xr = xcd_range(*p.num_mtiles2 * ntn);
+  __shared__ int s_tile;
+  TileSched ts(p.sched + 1 * kSchedInts, *p.num_mtiles2 * ntn);
   const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
-  for (int tile = xr.first; tile < xr.end; tile += xr.stride) {
+  for (int tile = ts.first(&s_tile); tile >= 0; tile = ts.next(&s_tile)) {
     const int mt = tile / ntn, nt = tile - mt * ntn;
     const int2 me = p.mtile2[mt];
     const int e = me.x, r0 = me.y, seg_end = p.offsets[e + 1];
@@ -492,10 +526,14 @@ __global__ __launch_bounds__(NTHR8, 1) void k_dgrad_x_bf16(BwdParams p) {
     lb.zero = static_cast<const char*>(p.zeros);
     lb.init(nt * TILE, H);
     f32x16 acc[2][4];
-    mainloop<false, true>(acc, smem, la, lb, 2 * F / KTILE, 64 * wm, bn);
-    const int rq = r0 + 64 * wm;
+    mainloop_rows<false, true, 128>(acc, smem, la, lb, 2 * F / KTILE, 32 * wm, bn, seg_end - r0 <= 128);
+    ts.fetch();
+    const int rq = r0 + 32 * wm;   // the wave's row m is tile row 32 wm + 128 (m / 32) + m % 32
     bf16* const oq = dxp + nt * TILE + 128 * wn;
-    store_quadrant(smem, acc, lane, [&](int m) { return rq + m < seg_end ? oq + (size_t)(rq + m) * H : nullptr; }, 128);
+    store_quadrant(smem, acc, lane, [&](int m) {
+      const int r = rq + 128 * (m >> 5) + (m & 31);
+      return r < seg_end ? oq + (size_t)r * H : nullptr;
+    }, 128);
   }
 }
 
@@ -565,6 +603,11 @@ __global__ __launch_bounds__(NTHR8, 1) void k_wgrad_gateup_bf16(BwdParams p) {
   }
 }
 
+// zeroes the backward GEMMs' tile-scheduler counters (the workspace is the caller's)
+__global__ __launch_bounds__(64) void k_sched_reset(int* sched) {
+  for (int i = threadIdx.x; i < kSchedSlots * kSchedInts; i += 64) sched[i] = 0;
+}
+
 }  // namespace
 
 hipError_t launch_forward_gemms_bf16(const FwdParams& p, int grid, hipStream_t s) {
@@ -583,6 +626,10 @@ hipError_t launch_forward_gemms_bf16(const FwdParams& p, int grid, hipStream_t s
 
 hipError_t launch_backward_gemms_bf16(const BwdParams& p, int grid, hipStream_t s) {
   hipError_t err;
+  prof_mark_begin("sched_reset", s);
+  k_sched_reset<<<1, 64, 0, s>>>(p.sched);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
   prof_mark_begin("gemm_bwd_dh_dswiglu", s);
   k_bwd_dh_bf16<<<grid, NTHR8, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;

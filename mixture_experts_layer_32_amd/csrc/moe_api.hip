@@ -71,6 +71,7 @@ Layout make_layout(const moe_desc& d) {
 
   off = 0;
   const size_t cells = (size_t)L.nblk_route * El;
+  L.sched_f = take(kSchedSlots * kSchedInts * 4);
   L.blk_mask = take(cells * 8);
   L.blk_count = take(cells * 4);
   L.blk_prefix = take(cells * 4);
@@ -89,6 +90,7 @@ Layout make_layout(const moe_desc& d) {
   L.fwd_total = off;
 
   off = 0;
+  L.sched_b = take(kSchedSlots * kSchedInts * 4);
   L.dab = take(L.mx ? 0 : rows * 2 * F * L.elem);
   L.gpart = take((size_t)L.np * rows * 4);
   L.dxp = take(rows * H * L.elem);
@@ -288,6 +290,7 @@ static RouteParams route_params(const moe_desc& d, const Layout& L, const float*
   p.blk_mask = reinterpret_cast<unsigned long long*>(w + L.blk_mask);
   p.blk_count = reinterpret_cast<int*>(w + L.blk_count);
   p.blk_prefix = reinterpret_cast<int*>(w + L.blk_prefix);
+  p.sched = reinterpret_cast<int*>(w + L.sched_f);
   p.T = d.T;
   p.E = d.E_total;
   p.El = d.E_local;
@@ -341,6 +344,7 @@ moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits, const 
   fp.mtile2 = rp.mtile2;
   fp.num_mtiles2 = rp.num_mtiles2;
   fp.zeros = rp.zeros;
+  fp.sched = rp.sched;
   fp.qoff = rp.qoff;
   fp.qc = L.qc;
   fp.hwt = sv + L.hwt;
@@ -452,6 +456,7 @@ moe_status moe_bwd(const moe_desc* d, const void* dy, const void* x, const void*
   p.dabt = w + L.dabt;
   p.dab = w + L.dab;
   p.gpart = reinterpret_cast<float*>(w + L.gpart);
+  p.sched = reinterpret_cast<int*>(w + L.sched_b);
   p.dxp = w + L.dxp;
   p.dx = dx;
   p.dlogits = dlogits;

@@ -14,6 +14,8 @@ constexpr int kZeroBytes = 1024;    // zero page read by the bf16 GEMMs for out-
 constexpr int kRouteTokens = 64;    // tokens per routing block (one 64-bit mask word per expert)
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopk = 32;
+constexpr int kSchedInts = 16;      // ints per GEMM's tile-scheduler slot (8 per-XCD counters, padded to 64 B)
+constexpr int kSchedSlots = 8;      // scheduler slots per workspace
 
 // Byte offsets of every region inside the three caller-provided buffers.
 struct Layout {
@@ -33,9 +35,9 @@ struct Layout {
   // saved); FP8_BWD: the backward quantises them into its workspace (wdtq.. below)
   size_t sv_wdtq, sv_wdts, sv_wgutq, sv_wguts;
   // forward workspace (MXFP8: quantised operands; FP8_BWD: the bf16 hw)
-  size_t blk_mask, blk_count, blk_prefix, o, xq, xs, wgq, wgs, wuq, wus, wdq, wds, hwq, hws, hw16, fwd_total;
+  size_t sched_f, blk_mask, blk_count, blk_prefix, o, xq, xs, wgq, wgs, wuq, wus, wdq, wds, hwq, hws, hw16, fwd_total;
   // backward workspace (MX: quantised operands)
-  size_t dab, gpart, dxp, dabt, dyq, dys, wdtq, wdts, wgutq, wguts, dytq, dyts, xtq, xts, dabq, dabs, dabtq, dabts,
+  size_t sched_b, dab, gpart, dxp, dabt, dyq, dys, wdtq, wdts, wgutq, wguts, dytq, dyts, xtq, xts, dabq, dabs, dabtq, dabts,
       bwd_total;
 };
 
@@ -63,6 +65,7 @@ struct RouteParams {
   unsigned long long* blk_mask;
   int* blk_count;
   int* blk_prefix;
+  int* sched;          // the forward GEMMs' tile-scheduler counters, zeroed by the routing
   int64_t T;
   int E, El, e0, k, nblk, qpad;
 };
@@ -94,6 +97,7 @@ struct FwdParams {
   // MXFP8 operands: E4M3 bytes and e8m0 scales ([rows][K/32]), all K-major
   const uint8_t *xq, *xs, *wgq, *wgs, *wuq, *wus, *wdq, *wds;
   uint8_t *hwq, *hws, *hwtq, *hwts;
+  int* sched;          // tile-scheduler counters (kSchedSlots slots), zero at launch
   int64_t T;
   int H, F, k, El;
 };
@@ -135,6 +139,7 @@ struct BwdParams {
   // MXFP8 operands: E4M3 bytes and e8m0 scales ([rows][K/32]), all K-major
   const uint8_t *dyq, *dys, *wdtq, *wdts, *wgutq, *wguts, *dytq, *dyts, *xtq, *xts, *hwtq, *hwts;
   uint8_t *dabq, *dabs, *dabtq, *dabts;
+  int* sched;          // tile-scheduler counters (kSchedSlots slots), zeroed before the GEMMs
   int64_t T, rows;
   int H, F, k, E, El, np;
 };

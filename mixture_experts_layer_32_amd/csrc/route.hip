@@ -253,6 +253,7 @@ __global__ __launch_bounds__(512) void k_route_offsets(RouteParams p) {
     *p.num_mtiles2 = tot_t2;
   }
   if (e < kZeroBytes / 16) p.zeros[e] = make_uint4(0u, 0u, 0u, 0u);
+  if (e < kSchedSlots * kSchedInts) p.sched[e] = 0;
 }
 
 __global__ __launch_bounds__(256) void k_route_scatter(RouteParams p) {
