@@ -502,13 +502,15 @@ __global__ __launch_bounds__(NTHR8, 1) void k_bwd_dh_bf16(BwdParams p) {
 // backward: dX = [da db] [W_gate[e]; W_up[e]] (contraction over 2F)
 __global__ __launch_bounds__(NTHR8, 1) void k_dgrad_x_bf16(BwdParams p) {
   MOE_SMEM
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;   // 64x128 per wave
+  // 128x64 per wave: B (the weights, MN-major) goes through the slower transposing LDS read, so
+  // each wave takes 2 B blocks and 4 A blocks rather than 4 and 2
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
   const bf16* __restrict__ dab = static_cast<const bf16*>(p.dab);
   bf16* __restrict__ dxp = static_cast<bf16*>(p.dxp);
   const int H = p.H, F = p.F, ntn = H / TILE;
   __shared__ int s_tile;
   TileSched ts(p.sched + 1 * kSchedInts, *p.num_mtiles2 * ntn);
-  const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
+  const int bn[2] = {64 * wn, 64 * wn + 32};
   for (int tile = ts.first(&s_tile); tile >= 0; tile = ts.next(&s_tile)) {
     const int mt = tile / ntn, nt = tile - mt * ntn;
     const int2 me = p.mtile2[mt];
@@ -525,15 +527,15 @@ __global__ __launch_bounds__(NTHR8, 1) void k_dgrad_x_bf16(BwdParams p) {
                          (size_t)H * 2, F};
     lb.zero = static_cast<const char*>(p.zeros);
     lb.init(nt * TILE, H);
-    f32x16 acc[2][4];
-    mainloop_rows<false, true, 128>(acc, smem, la, lb, 2 * F / KTILE, 32 * wm, bn, seg_end - r0 <= 128);
+    f32x16 acc[4][2];
+    mainloop_rows<false, true, 64>(acc, smem, la, lb, 2 * F / KTILE, 32 * wm, bn, seg_end - r0 <= 128);
     ts.fetch();
-    const int rq = r0 + 32 * wm;   // the wave's row m is tile row 32 wm + 128 (m / 32) + m % 32
-    bf16* const oq = dxp + nt * TILE + 128 * wn;
+    const int rq = r0 + 32 * wm;   // the wave's row m is tile row 32 wm + 64 (m / 32) + m % 32
+    bf16* const oq = dxp + nt * TILE + 64 * wn;
     store_quadrant(smem, acc, lane, [&](int m) {
-      const int r = rq + 128 * (m >> 5) + (m & 31);
+      const int r = rq + 64 * (m >> 5) + (m & 31);
       return r < seg_end ? oq + (size_t)r * H : nullptr;
-    }, 128);
+    }, 64);
   }
 }
 
@@ -571,7 +573,8 @@ __global__ __launch_bounds__(NTHR8, 1) void k_wgrad_down_bf16(BwdParams p) {
 // backward: [dW_gate; dW_up][e] (2F x H) = sum over the expert's pairs of [da; db]_r x_t^T
 __global__ __launch_bounds__(NTHR8, 1) void k_wgrad_gateup_bf16(BwdParams p) {
   MOE_SMEM
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;   // 64x128 per wave
+  // 128x64 per wave: B (x, MN-major) goes through the slower transposing LDS read
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
   const int H = p.H, F = p.F, ntn = H / TILE, tpe = (2 * F / TILE) * ntn;
   const XcdRange xr = xcd_range(p.El * tpe);
   for (int lid = xr.first; lid < xr.end; lid += xr.stride) {
@@ -590,16 +593,16 @@ __global__ __launch_bounds__(NTHR8, 1) void k_wgrad_gateup_bf16(BwdParams p) {
                        (size_t)H * 2, seg0, seg_end, {}};
   lb.zero = static_cast<const char*>(p.zeros);
   lb.init(nt * TILE, H);
-  const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
-  f32x16 acc[2][4];
-  mainloop<false, true>(acc, smem, la, lb, (seg_end - seg0 + KTILE - 1) / KTILE, 64 * wm, bn);
+  const int bn[2] = {64 * wn, 64 * wn + 32};
+  f32x16 acc[4][2];
+  mainloop<false, true>(acc, smem, la, lb, (seg_end - seg0 + KTILE - 1) / KTILE, 128 * wm, bn);
   bf16* __restrict__ dwg = static_cast<bf16*>(p.dwg) + (size_t)e * F * H;
   bf16* __restrict__ dwu = static_cast<bf16*>(p.dwu) + (size_t)e * F * H;
-  const int mq = mt * TILE + 64 * wm, nq = nt * TILE + 128 * wn;
+  const int mq = mt * TILE + 128 * wm, nq = nt * TILE + 64 * wn;
   store_quadrant(smem, acc, lane, [&](int m) {
     const int mm = mq + m;
     return (mm < F ? dwg + (size_t)mm * H : dwu + (size_t)(mm - F) * H) + nq;
-  }, 128);
+  }, 64);
   }
 }
 
