@@ -26,6 +26,9 @@ Each function states its reading.
 Arrays may arrive as float32, including bf16-exact values. Every computation converts them to
 float64 before any arithmetic.
 
+The router projection (router_forward, router_backward) produces the logits the layer consumes,
+and takes its dlogits back.
+
 Parity status: every function here is pinned by tests that do not go through this code:
  * brute-force loops;
  * closed forms;
@@ -257,6 +260,28 @@ def _expert_backward(xe, dye, wr, wg_i, wu_i, wd_i, mode):
         dwu = db.T @ xe
     dxe = _qz(qb, da, 1) @ _qz(qb, wg_i, 0) + _qz(qb, db, 1) @ _qz(qb, wu_i, 0)   # contraction over F
     return g, dwg, dwu, dwd, dxe
+
+
+# ----------------------------------------------------------------------------------------------
+# router projection in front of the layer
+
+def router_forward(x, wr):
+    """Router logits l = x W_r^T, [T, E], with W_r [E, H] (out x in, like the experts' weights).
+
+    The pages fold the routing into the fused call ("Prime Mega MoE: kernel fuso per
+    l'addestramento MoE" on "Prime Mega MoE: il kernel che accelera il training AI del 55%") but
+    do not say how the logits arise. Reading: the usual linear router, without bias. The routing
+    above consumes fp32 logits; this returns them in float64, and the caller rounds them where it
+    needs fp32 bits.
+    """
+    return _f64(x) @ _f64(wr).T
+
+
+def router_backward(dlogits, x, wr):
+    """Gradients of the router projection for dlogits [T, E]: dW_r = dlogits^T x [E, H], and the
+    router's part of dx, dlogits W_r [T, H], which adds to the layer's own dx."""
+    dl = _f64(dlogits)
+    return dl.T @ _f64(x), dl @ _f64(wr)
 
 
 def router_grad(r, g, E):
