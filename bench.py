@@ -116,6 +116,55 @@ def cpu_baseline(cfg, L, min_seconds=10.0, group=16):
                       f"backward, {dt:.1f} s wall"}
 
 
+def router_bench(cfg, layer, x, grads, steps):
+    """The router projection in front of the layer (logits = x W_r^T; dW_r and dx += dlogits W_r),
+    timed on its own with HIP events on the library's stream. It is not part of `value`, which is
+    the layer's metric. The backward takes the layer's last dlogits (k nonzeros per row) and
+    accumulates into its dx."""
+    import numpy as np
+    import torch
+    from mixture_experts_layer_32_amd import binding, inputs
+
+    wr = torch.from_numpy(inputs.router_weight(cfg)).to("cuda").to(torch.bfloat16)
+    lg = torch.empty(cfg.T, cfg.E, dtype=torch.float32, device="cuda")
+    dl, dx = grads["dlogits"], grads["dx"]
+    dwr = torch.empty(cfg.E, cfg.H, dtype=torch.bfloat16, device="cuda")
+    for _ in range(2):
+        layer.router_forward(x, wr, lg)
+        layer.router_backward(x, wr, dl, dx, dwr)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1, e2 in evs:
+        e0.record()
+        layer.router_forward(x, wr, lg)
+        e1.record()
+        layer.router_backward(x, wr, dl, dx, dwr)
+        e2.record()
+    torch.cuda.synchronize()
+    fwd_ms = float(np.median([e0.elapsed_time(e1) for e0, e1, _ in evs]))
+    bwd_ms = float(np.median([e1.elapsed_time(e2) for _, e1, e2 in evs]))
+    binding.profile_enable(16 * steps)
+    for _ in range(steps):
+        layer.router_forward(x, wr, lg)
+        layer.router_backward(x, wr, dl, dx, dwr)
+    kern = binding.profile_collect()
+    binding.profile_disable()
+    fl = 2.0 * cfg.T * cfg.H * cfg.E
+    gemm_fl = {"router_fwd_gemm": fl, "router_dx_gemm": fl, "router_dw_gemm": fl}
+    per_kernel = {}
+    for name, (n, tot) in kern.items():
+        ent = {"avg_ms": round(tot / n, 5), "launches": n}
+        if name in gemm_fl:
+            tf = gemm_fl[name] / (tot / n * 1e-3) / 1e12
+            ent["tflops"] = round(tf, 2)
+            ent["pct_peak"] = round(100 * tf / PEAK_TFLOPS["bf16"], 2)
+        per_kernel[name] = ent
+    return {"what": "logits = x W_r^T [T, E] fp32; backward dW_r = dlogits^T x and dx += dlogits W_r (bf16 MFMA)",
+            "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+            "fwd_tflops": round(fl / (fwd_ms * 1e-3) / 1e12, 2),
+            "bwd_tflops": round(2 * fl / (bwd_ms * 1e-3) / 1e12, 2), "kernels": per_kernel}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,6 +292,9 @@ def main():
         "ms_per_step_with_kernel_events": round(ms_step_prof, 4),
         "kernels": per_kernel, "roofline": roof,
     }
+    if mode != "fp32":
+        print("[bench] router projection", file=sys.stderr, flush=True)
+        res["router"] = router_bench(cfg, layer, x, grads, a.steps)
     if not a.no_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, L)

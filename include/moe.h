@@ -136,6 +136,34 @@ moe_status moe_bwd(const moe_desc* d, const void* dy, const void* x,
                    void* dx, float* dlogits, void* dw_gate, void* dw_up, void* dw_down,
                    void* ws, size_t ws_bytes, void* stream);
 
+/* Router projection in front of the layer: the linear router whose fp32 logits moe_fwd and
+ * moe_route consume, and its backward. The pages fold the routing into the fused operation
+ * ("Prime Mega MoE: kernel fuso per l'addestramento MoE" on "Prime Mega MoE: il kernel che
+ * accelera il training AI del 55%") without saying how the logits arise; the library reads it as
+ * the usual linear router without bias:
+ *    logits[t, e]     = sum_h x[t, h] * w_router[e, h]        moe_router_fwd
+ *    dw_router[e, h]  = sum_t dlogits[t, e] * x[t, h]         moe_router_bwd (overwritten)
+ *    dx[t, h]        += sum_e dlogits[t, e] * w_router[e, h]  moe_router_bwd (accumulated)
+ * w_router and dw_router are [E_total, H] (out x in, like the experts' weights); x and dx as in
+ * the layer; logits and dlogits [T, E_total] fp32. Passing moe_bwd's dx and dlogits to
+ * moe_router_bwd gives the gradient of the whole x -> router -> layer composition. In an expert
+ * share, dlogits is the share's contribution and the call is linear in it, so the shares' calls
+ * add up to the full gradient.
+ * Arithmetic: bf16 MFMA with fp32 accumulation. The contractions over H (forward) and over the
+ * tokens (dw_router) are split into slices whose fp32 partial sums are added in a fixed order; the
+ * backward multiplies a bf16 copy of dlogits, and dx is read, added to in fp32 and rounded once.
+ * No atomics: results are bitwise reproducible.
+ * Modes: BF16, MXFP8 and FP8_BWD (bf16 I/O; the projection itself stays bf16). MOE_MODE_FP32
+ * returns MOE_ERR_UNSUPPORTED_MODE. Every tensor pointer needs 16-byte alignment except dlogits
+ * (4 bytes); ws needs 256. The workspace sizes come from moe_query_router_sizes (host-only); its
+ * contents need not be preserved. */
+moe_status moe_query_router_sizes(const moe_desc* d, size_t* fwd_ws, size_t* bwd_ws);
+moe_status moe_router_fwd(const moe_desc* d, const void* x, const void* w_router, float* logits,
+                          void* ws, size_t ws_bytes, void* stream);
+moe_status moe_router_bwd(const moe_desc* d, const void* x, const void* w_router,
+                          const float* dlogits, void* dx, void* dw_router, void* ws,
+                          size_t ws_bytes, void* stream);
+
 /* Byte offsets of the routing results inside `saved`.
  *   idx       int32 [T*k]      chosen experts, slot order (logit desc, index asc)
  *   weight    float [T*k]      renormalised routing weights

@@ -73,11 +73,14 @@ def lib():
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_version.restype = ctypes.c_char_p
         L.moe_mx_quantize.argtypes = [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, _P, _P, _P]
+        L.moe_query_router_sizes.argtypes = [_D, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_router_fwd.argtypes = [_D, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.moe_router_bwd.argtypes = [_D, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_profile_enable.argtypes = [ctypes.c_int]
         L.moe_profile_kernel.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
                                          ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]
         for n in ("moe_query_sizes", "moe_route", "moe_fwd", "moe_bwd", "moe_saved_layout", "moe_mx_quantize",
-                  "moe_profile_enable",
+                  "moe_query_router_sizes", "moe_router_fwd", "moe_router_bwd", "moe_profile_enable",
                   "moe_profile_disable", "moe_profile_collect", "moe_profile_kernel"):
             getattr(L, n).restype = st
         _lib = L
@@ -137,6 +140,22 @@ def moe_bwd(desc, dy, x, w_gate, w_up, w_down, saved, dx, dlogits, dw_gate, dw_u
     _check(lib().moe_bwd(ctypes.byref(desc), ptr(dy), ptr(x), ptr(w_gate), ptr(w_up), ptr(w_down), ptr(saved),
                          ptr(dx), ptr(dlogits), ptr(dw_gate), ptr(dw_up), ptr(dw_down), ptr(ws), ws_bytes,
                          _stream(stream)))
+
+
+def query_router_sizes(desc: Desc):
+    f, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().moe_query_router_sizes(ctypes.byref(desc), ctypes.byref(f), ctypes.byref(b)))
+    return f.value, b.value
+
+
+def moe_router_fwd(desc, x, w_router, logits, ws, ws_bytes, stream=None):
+    _check(lib().moe_router_fwd(ctypes.byref(desc), ptr(x), ptr(w_router), ptr(logits), ptr(ws), ws_bytes,
+                                _stream(stream)))
+
+
+def moe_router_bwd(desc, x, w_router, dlogits, dx, dw_router, ws, ws_bytes, stream=None):
+    _check(lib().moe_router_bwd(ctypes.byref(desc), ptr(x), ptr(w_router), ptr(dlogits), ptr(dx), ptr(dw_router),
+                                ptr(ws), ws_bytes, _stream(stream)))
 
 
 def moe_mx_quantize(x, rows, cols, axis, q, scales, stream=None):

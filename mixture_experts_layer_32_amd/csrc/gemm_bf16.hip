@@ -606,6 +606,217 @@ __global__ __launch_bounds__(NTHR8, 1) void k_wgrad_gateup_bf16(BwdParams p) {
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// Router projection in front of the layer: logits = x W_r^T (fp32), and in the backward
+// dW_r = dlogits^T x and dx += dlogits W_r. The pages fold the routing into the fused call ("Prime
+// Mega MoE: kernel fuso per l'addestramento MoE" on "Prime Mega MoE: il kernel che accelera il
+// training AI del 55%"); the projection is read as the usual linear router without bias. E is small
+// (128 at the benchmark shape), so the two GEMMs with a long contraction (over H in the forward,
+// over T for dW_r) split it p.S ways and add the fp32 partial sums in a fixed order afterwards: no
+// atomics, so results stay bitwise reproducible. The backward multiplies a bf16 copy of dlogits.
+
+// contraction rows k0 .. kend-1 of a row-major matrix (row k at base + k*ld); rows at or past kend
+// read the zero page
+struct DenseRows {
+  const char* base;
+  size_t ld;
+  int k0, kend;
+  __device__ __forceinline__ void prefetch(int) {}
+  __device__ __forceinline__ void prologue_prefetch(int) {}
+  __device__ __forceinline__ const char* row(int kt, int j) const {
+    const int k = k0 + kt * KTILE + mn_krow(j);
+    return k < kend ? base + (size_t)k * ld : nullptr;
+  }
+  __device__ __forceinline__ const char* prologue_row(int kt, int j) const { return row(kt, j); }
+};
+
+// Stores the wave's block as fp32: out_row(m) is the output row of the wave's row m at its first
+// column, or null to skip the row; ncols limits the columns (in steps of 8).
+template <int MI, int NJ, class OutRow>
+__device__ __forceinline__ void store_block_f32(char* smem, const f32x16 (&acc)[MI][NJ], int lane, OutRow out_row,
+                                                int ncols) {
+  constexpr int LPR = 4 * NJ, RPP = 64 / LPR;
+  float* slab = wave_slab<NJ>(smem);
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    stage_rows(slab, acc, i, lane);
+#pragma unroll
+    for (int s = 0; s < 32 / RPP; ++s) {
+      const int rl = lane / LPR + RPP * s, c0 = (lane % LPR) * 8;
+      float* o = out_row(32 * i + rl);
+      if (o && c0 < ncols) {
+        float v[8];
+        read8<NJ>(slab, rl, c0, v);
+        st16_nt(o + c0, make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                   __float_as_uint(v[3])));
+        st16_nt(o + c0 + 4, make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]),
+                                       __float_as_uint(v[7])));
+      }
+    }
+  }
+}
+
+// Adds the wave's block to bf16 rows (read, add in fp32, round once, write); out_row as above, all
+// 32 NJ columns.
+template <int MI, int NJ, class OutRow>
+__device__ __forceinline__ void add_block_bf16(char* smem, const f32x16 (&acc)[MI][NJ], int lane, OutRow out_row) {
+  constexpr int LPR = 4 * NJ, RPP = 64 / LPR;
+  float* slab = wave_slab<NJ>(smem);
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    stage_rows(slab, acc, i, lane);
+#pragma unroll
+    for (int s = 0; s < 32 / RPP; ++s) {
+      const int rl = lane / LPR + RPP * s, c0 = (lane % LPR) * 8;
+      bf16* o = out_row(32 * i + rl);
+      if (o) {
+        float v[8], u[8];
+        read8<NJ>(slab, rl, c0, v);
+        unpack8(ld16(o + c0), u);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += u[e];
+        st16(o + c0, pack8(v));
+      }
+    }
+  }
+}
+
+// forward: part[s][t][e] = sum over the s-th kc-element slice of H of x[t][h] W_r[e][h]
+__global__ __launch_bounds__(NTHR8, 1) void k_router_fwd_bf16(RouterParams p) {
+  MOE_SMEM
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;   // 64x128 per wave
+  const bf16* __restrict__ x = static_cast<const bf16*>(p.x);
+  const bf16* __restrict__ wr = static_cast<const bf16*>(p.wr);
+  const int T = (int)p.T, H = p.H, E = p.E, Ep = p.Ep;
+  const int mtn = (T + TILE - 1) / TILE, ntn = (E + TILE - 1) / TILE, per = mtn * ntn;
+  const XcdRange xr = xcd_range(per * p.S);
+  const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
+  for (int tile = xr.first; tile < xr.end; tile += xr.stride) {
+    const int sp = tile / per, t = tile - sp * per, mt = t / ntn, nt = t - mt * ntn;
+    KOp la, lb;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int row = KOp::row_of(j), c = KOp::chunk_of(j);
+      const size_t k0 = (size_t)sp * p.kc;
+      la.p[j] = reinterpret_cast<const char*>(x + (size_t)min(mt * TILE + row, T - 1) * H + k0) + 16 * c;
+      lb.p[j] = reinterpret_cast<const char*>(wr + (size_t)min(nt * TILE + row, E - 1) * H + k0) + 16 * c;
+    }
+    f32x16 acc[2][4];
+    mainloop<false, false>(acc, smem, la, lb, p.kc / KTILE, 64 * wm, bn);
+    float* out = p.part + (size_t)sp * T * Ep;
+    const int m0 = mt * TILE + 64 * wm, n0 = nt * TILE + 128 * wn;
+    store_block_f32(smem, acc, lane, [&](int m) { return m0 + m < T ? out + (size_t)(m0 + m) * Ep + n0 : nullptr; },
+                    Ep - n0);
+  }
+}
+
+// forward: logits[t][e] = sum over s (S <= 4), in order, of part[s][t][e]; 4 columns of the padded rows per
+// thread (the loads of all slices are issued before the adds)
+__global__ __launch_bounds__(256) void k_router_sum_logits(RouterParams p) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nq = p.T * (p.Ep / 4);
+  if (q >= nq) return;
+  const int64_t t = q / (p.Ep / 4), e = (q - t * (p.Ep / 4)) * 4;
+  float4 v[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    v[s] = s < p.S ? *reinterpret_cast<const float4*>(p.part + ((size_t)s * p.T + t) * p.Ep + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+  float r[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
+#pragma unroll
+  for (int s = 1; s < 4; ++s) {
+    r[0] += v[s].x; r[1] += v[s].y; r[2] += v[s].z; r[3] += v[s].w;
+  }
+  float* out = p.logits + t * p.E;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    if (e + c < p.E) out[e + c] = r[c];
+}
+
+// backward: dlb = bf16(dlogits), zero-padded to Ep columns; the zero page
+__global__ __launch_bounds__(256) void k_router_dl_bf16(RouterParams p) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (blockIdx.x == 0 && threadIdx.x < kZeroBytes / 16) static_cast<uint4*>(p.zeros)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+  if (i >= p.T * p.Ep) return;
+  const int64_t t = i / p.Ep, c = i - t * p.Ep;
+  static_cast<bf16*>(p.dlb)[i] = (bf16)(c < p.E ? p.dlogits[t * p.E + c] : 0.f);
+}
+
+// backward: dx[t][h] += sum_e dlb[t][e] W_r[e][h] (contraction over E; W_r is MN-major here)
+__global__ __launch_bounds__(NTHR8, 1) void k_router_dx_bf16(RouterParams p) {
+  MOE_SMEM
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;   // 64x128 per wave
+  const bf16* __restrict__ dlb = static_cast<const bf16*>(p.dlb);
+  bf16* __restrict__ dx = static_cast<bf16*>(p.dx);
+  const int T = (int)p.T, H = p.H, Ep = p.Ep;
+  const int mtn = (T + TILE - 1) / TILE, ntn = H / TILE;
+  const XcdRange xr = xcd_range(mtn * ntn);
+  const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
+  for (int tile = xr.first; tile < xr.end; tile += xr.stride) {
+    const int mt = tile / ntn, nt = tile - mt * ntn;
+    KOp la;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j)
+      la.p[j] = reinterpret_cast<const char*>(dlb + (size_t)min(mt * TILE + KOp::row_of(j), T - 1) * Ep) +
+                16 * KOp::chunk_of(j);
+    MNOp<DenseRows> lb;
+    lb.rows = DenseRows{reinterpret_cast<const char*>(static_cast<const bf16*>(p.wr) + nt * TILE), (size_t)H * 2, 0, p.E};
+    lb.zero = static_cast<const char*>(p.zeros);
+    lb.init(nt * TILE, H);
+    f32x16 acc[2][4];
+    mainloop<false, true>(acc, smem, la, lb, Ep / KTILE, 64 * wm, bn);
+    const int m0 = mt * TILE + 64 * wm;
+    bf16* const oq = dx + nt * TILE + 128 * wn;
+    add_block_bf16(smem, acc, lane, [&](int m) { return m0 + m < T ? oq + (size_t)(m0 + m) * H : nullptr; });
+  }
+}
+
+// backward: part[s][e][h] = sum over the s-th kc-token slice of dlb[t][e] x[t][h] (both operands
+// MN-major: the contraction runs over the tokens)
+__global__ __launch_bounds__(NTHR8, 1) void k_router_dw_bf16(RouterParams p) {
+  MOE_SMEM
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;   // 64x128 per wave
+  const int T = (int)p.T, H = p.H, E = p.E, Ep = p.Ep;
+  const int mtn = (E + TILE - 1) / TILE, ntn = H / TILE, per = mtn * ntn;
+  const XcdRange xr = xcd_range(per * p.S);
+  const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
+  for (int tile = xr.first; tile < xr.end; tile += xr.stride) {
+    const int sp = tile / per, t = tile - sp * per, mt = t / ntn, nt = t - mt * ntn;
+    const int k0 = sp * p.kc, kend = min(T, k0 + p.kc);
+    MNOp<DenseRows> la, lb;
+    la.rows = DenseRows{reinterpret_cast<const char*>(static_cast<const bf16*>(p.dlb) + mt * TILE), (size_t)Ep * 2, k0, kend};
+    la.zero = static_cast<const char*>(p.zeros);
+    la.init(mt * TILE, Ep);
+    lb.rows = DenseRows{reinterpret_cast<const char*>(static_cast<const bf16*>(p.x) + nt * TILE), (size_t)H * 2, k0, kend};
+    lb.zero = la.zero;
+    lb.init(nt * TILE, H);
+    f32x16 acc[2][4];
+    mainloop<true, true>(acc, smem, la, lb, (kend - k0 + KTILE - 1) / KTILE, 64 * wm, bn);
+    float* out = p.part + (size_t)sp * E * H;
+    const int m0 = mt * TILE + 64 * wm, n0 = nt * TILE + 128 * wn;
+    store_block_f32(smem, acc, lane, [&](int m) { return m0 + m < E ? out + (size_t)(m0 + m) * H + n0 : nullptr; }, 128);
+  }
+}
+
+// backward: dW_r[e][h] = bf16(sum over s, in order, of part[s][e][h]); 4 elements per thread, the
+// slices' loads issued 8 at a time ahead of their adds
+__global__ __launch_bounds__(256) void k_router_sum_dw(RouterParams p) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  const int64_t n = (int64_t)p.E * p.H;
+  if (i >= n) return;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < p.S; s0 += 8) {
+    float4 q[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      q[u] = s0 + u < p.S ? *reinterpret_cast<const float4*>(p.part + (size_t)(s0 + u) * n + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      v.x += q[u].x; v.y += q[u].y; v.z += q[u].z; v.w += q[u].w;
+    }
+  }
+  st8(static_cast<bf16*>(p.dwr) + i, pack4(v.x, v.y, v.z, v.w));
+}
+
 // zeroes the backward GEMMs' tile-scheduler counters (the workspace is the caller's)
 __global__ __launch_bounds__(64) void k_sched_reset(int* sched) {
   for (int i = threadIdx.x; i < kSchedSlots * kSchedInts; i += 64) sched[i] = 0;
@@ -622,6 +833,40 @@ hipError_t launch_forward_gemms_bf16(const FwdParams& p, int grid, hipStream_t s
   prof_mark_end(s);
   prof_mark_begin("gemm_down", s);
   k_down_bf16<<<grid, NTHR8, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+  return hipSuccess;
+}
+
+hipError_t launch_router_fwd_bf16(const RouterParams& p, int grid, hipStream_t s) {
+  hipError_t err;
+  prof_mark_begin("router_fwd_gemm", s);
+  k_router_fwd_bf16<<<grid, NTHR8, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+  prof_mark_begin("router_fwd_sum", s);
+  k_router_sum_logits<<<(unsigned)((p.T * (p.Ep / 4) + 255) / 256), 256, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+  return hipSuccess;
+}
+
+hipError_t launch_router_bwd_bf16(const RouterParams& p, int grid, hipStream_t s) {
+  hipError_t err;
+  prof_mark_begin("router_dlogits_bf16", s);
+  k_router_dl_bf16<<<(unsigned)((p.T * p.Ep + 255) / 256), 256, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+  prof_mark_begin("router_dx_gemm", s);
+  k_router_dx_bf16<<<grid, NTHR8, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+  prof_mark_begin("router_dw_gemm", s);
+  k_router_dw_bf16<<<grid, NTHR8, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+  prof_mark_begin("router_dw_sum", s);
+  k_router_sum_dw<<<(unsigned)(((int64_t)p.E * p.H / 4 + 255) / 256), 256, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   prof_mark_end(s);
   return hipSuccess;

@@ -3,6 +3,7 @@
 // allocates device memory and never synchronises the host inside moe_route/moe_fwd/moe_bwd.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -519,6 +520,123 @@ moe_status moe_bwd(const moe_desc* d, const void* dy, const void* x, const void*
   if (e != hipSuccess) return hip_fail(e, "backward GEMM launch");
   e = d->mode == MOE_MODE_FP32 ? launch_combine_bwd<float>(p, s) : launch_combine_bwd<bf16>(p, s);
   if (e != hipSuccess) return hip_fail(e, "backward combine launch");
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------------------------------------------
+// Router projection in front of the layer
+
+namespace {
+struct RouterLayout {
+  int Ep;          // E_total rounded up to 64 (the bf16 copy of dlogits and the partial rows)
+  int Sf, kcf;     // forward: H split Sf ways, kcf elements each
+  int Sb, kcb;     // dW_r: T split Sb ways, kcb tokens each (a multiple of 64)
+  size_t fwd_part, fwd_total;
+  size_t bwd_zero, bwd_dlb, bwd_part, bwd_total;
+};
+
+RouterLayout router_layout(const moe_desc& d) {
+  RouterLayout R{};
+  const int64_t T = d.T;
+  const int64_t H = d.H, E = d.E_total;
+  R.Ep = (int)((E + 63) / 64 * 64);
+  const int64_t mtn = (T + 255) / 256, etn = (E + 255) / 256, htn = H / 256;
+  // about one 256x256 tile per CU or more: split H (S in {1, 2, 4}; H is a multiple of 256)
+  R.Sf = 1;
+  while (R.Sf < 4 && mtn * etn * R.Sf * 2 <= 256) R.Sf *= 2;
+  R.kcf = (int)(H / R.Sf);
+  const int64_t want = std::max<int64_t>(1, 256 / (etn * htn));
+  R.kcb = (int)(((T + want - 1) / want + 63) / 64 * 64);
+  R.Sb = (int)((T + R.kcb - 1) / R.kcb);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  R.fwd_part = take((size_t)R.Sf * T * R.Ep * 4);
+  R.fwd_total = off;
+  off = 0;
+  R.bwd_zero = take(kZeroBytes);
+  R.bwd_dlb = take((size_t)T * R.Ep * 2);
+  R.bwd_part = take((size_t)R.Sb * E * H * 4);
+  R.bwd_total = off;
+  return R;
+}
+
+moe_status router_checks(const moe_desc* d) {
+  moe_status st = validate(d);
+  if (st != MOE_OK) return st;
+  if (d->mode == MOE_MODE_FP32)
+    return fail(MOE_ERR_UNSUPPORTED_MODE, "the router projection runs in the bf16-I/O modes (BF16, MXFP8, FP8_BWD)");
+  return MOE_OK;
+}
+}  // namespace
+
+moe_status moe_query_router_sizes(const moe_desc* d, size_t* fwd_ws, size_t* bwd_ws) {
+  g_last_error.clear();
+  moe_status st = router_checks(d);
+  if (st != MOE_OK) return st;
+  const RouterLayout R = router_layout(*d);
+  if (fwd_ws) *fwd_ws = R.fwd_total;
+  if (bwd_ws) *bwd_ws = R.bwd_total;
+  return MOE_OK;
+}
+
+moe_status moe_router_fwd(const moe_desc* d, const void* x, const void* w_router, float* logits, void* ws,
+                          size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  moe_status st = router_checks(d);
+  if (st != MOE_OK) return st;
+  if ((st = check_ptrs({{x, "x"}, {w_router, "w_router"}, {logits, "logits"}}, 16)) != MOE_OK) return st;
+  if ((st = check_ptrs({{ws, "ws"}}, 256)) != MOE_OK) return st;
+  const RouterLayout R = router_layout(*d);
+  if (ws_bytes < R.fwd_total) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "router forward workspace too small");
+  RouterParams p{};
+  p.x = x;
+  p.wr = w_router;
+  p.part = reinterpret_cast<float*>(static_cast<char*>(ws) + R.fwd_part);
+  p.logits = logits;
+  p.T = d->T;
+  p.H = d->H;
+  p.E = d->E_total;
+  p.Ep = R.Ep;
+  p.S = R.Sf;
+  p.kc = R.kcf;
+  hipError_t e = launch_router_fwd_bf16(p, persistent_grid(1), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "router forward launch");
+  return MOE_OK;
+}
+
+moe_status moe_router_bwd(const moe_desc* d, const void* x, const void* w_router, const float* dlogits, void* dx,
+                          void* dw_router, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  moe_status st = router_checks(d);
+  if (st != MOE_OK) return st;
+  if ((st = check_ptrs({{x, "x"}, {w_router, "w_router"}, {dx, "dx"}, {dw_router, "dw_router"}}, 16)) != MOE_OK)
+    return st;
+  if ((st = check_ptrs({{dlogits, "dlogits"}}, 4)) != MOE_OK) return st;
+  if ((st = check_ptrs({{ws, "ws"}}, 256)) != MOE_OK) return st;
+  const RouterLayout R = router_layout(*d);
+  if (ws_bytes < R.bwd_total) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "router backward workspace too small");
+  char* w = static_cast<char*>(ws);
+  RouterParams p{};
+  p.x = x;
+  p.wr = w_router;
+  p.part = reinterpret_cast<float*>(w + R.bwd_part);
+  p.dlogits = dlogits;
+  p.dlb = w + R.bwd_dlb;
+  p.dx = dx;
+  p.dwr = dw_router;
+  p.zeros = w + R.bwd_zero;
+  p.T = d->T;
+  p.H = d->H;
+  p.E = d->E_total;
+  p.Ep = R.Ep;
+  p.S = R.Sb;
+  p.kc = R.kcb;
+  hipError_t e = launch_router_bwd_bf16(p, persistent_grid(1), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "router backward launch");
   return MOE_OK;
 }
 

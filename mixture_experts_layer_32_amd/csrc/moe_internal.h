@@ -148,6 +148,25 @@ template <class T> hipError_t launch_combine_bwd(const BwdParams& p, hipStream_t
 hipError_t launch_forward_gemms_bf16(const FwdParams& p, int grid, hipStream_t s);
 hipError_t launch_backward_gemms_bf16(const BwdParams& p, int grid, hipStream_t s);
 
+// Router projection in front of the layer (bf16 engine): logits = x W_r^T; backward dW_r and the
+// router's part of dx. The GEMMs with a long contraction split it S ways (kc elements per split)
+// and add the fp32 partial sums in a fixed order.
+struct RouterParams {
+  const void* x;         // [T, H] bf16
+  const void* wr;        // [E, H] bf16
+  float* part;           // split partial sums: [S][T][Ep] (forward), [S][E][H] (backward)
+  float* logits;         // [T, E] fp32 (forward output)
+  const float* dlogits;  // [T, E] fp32 (backward input)
+  void* dlb;             // [T, Ep] bf16 copy of dlogits, zero-padded (backward)
+  void* dx;              // [T, H] bf16, accumulated into (backward)
+  void* dwr;             // [E, H] bf16 (backward output)
+  void* zeros;           // zero page of kZeroBytes (backward)
+  int64_t T;
+  int H, E, Ep, S, kc;   // Ep = E rounded up to 64; S splits of kc elements of H (fwd) or T (bwd)
+};
+hipError_t launch_router_fwd_bf16(const RouterParams& p, int grid, hipStream_t s);
+hipError_t launch_router_bwd_bf16(const RouterParams& p, int grid, hipStream_t s);
+
 hipError_t launch_forward_gemms_mx(const FwdParams& p, int grid, hipStream_t s);
 hipError_t launch_backward_gemms_mx(const BwdParams& p, int grid, hipStream_t s);
 hipError_t launch_quant_rows(const void* in, uint8_t* q, uint8_t* sc, int64_t n, const char* name, hipStream_t s);

@@ -141,12 +141,24 @@ def _rows(cfg, tid, ncols, std, threads, chunk=1024):
     return out
 
 
+def _router_draw(cfg: LayerConfig):
+    wr = np.random.default_rng([cfg.seed, _TID_WR, 0]).standard_normal((cfg.H, cfg.E), dtype=np.float32)
+    wr *= np.float32(0.02)
+    return wr
+
+
+def router_weight(cfg: LayerConfig):
+    """W_r [E, H] (out x in) for the router projection in front of the layer: the draw the logits
+    of make_tokens come from, transposed, and rounded to bf16 for bf16 workloads."""
+    wr = np.ascontiguousarray(_router_draw(cfg).T)
+    return round_to_bf16(wr) if cfg.dtype == "bf16" else wr
+
+
 def make_tokens(cfg: LayerConfig, threads: int = 16):
     """(x [T,H], logits [T,E] fp32, dy [T,H]); x and dy are bf16-exact for bf16 workloads."""
     x = _rows(cfg, _TID_X, cfg.H, 1.0, threads)
     dy = _rows(cfg, _TID_DY, cfg.H, 1.0, threads)
-    wr = np.random.default_rng([cfg.seed, _TID_WR, 0]).standard_normal((cfg.H, cfg.E), dtype=np.float32)
-    wr *= np.float32(0.02)
+    wr = _router_draw(cfg)
     # router projection in float64 from the stored x, then fp32 logits
     logits = x.astype(np.float64) @ wr.astype(np.float64)
     if cfg.zipf_s > 0:

@@ -1,7 +1,8 @@
 """Device-memory plumbing around the C ABI: torch allocates the caller-owned buffers.
 
-MoELayer holds the workspace and saved buffers for one layer shape, and calls moe_fwd/moe_bwd
-through the binding. No arithmetic happens here.
+MoELayer holds the workspace and saved buffers for one layer shape, and calls moe_fwd/moe_bwd (and
+the router projection's moe_router_fwd/moe_router_bwd) through the binding. No arithmetic happens
+here.
 """
 from __future__ import annotations
 
@@ -48,6 +49,30 @@ class MoELayer:
         binding.moe_bwd(d, dy, x, w_gate, w_up, w_down, self.saved, out["dx"], out["dlogits"], out["dw_gate"],
                         out["dw_up"], out["dw_down"], self.ws, self.ws.numel(), stream)
         return out
+
+    def _router_ws(self):
+        if getattr(self, "router_ws", None) is None:
+            f, b = binding.query_router_sizes(self.desc)
+            self.router_ws = torch.empty(max(f, b, 256), dtype=torch.uint8, device=self.device)
+        return self.router_ws
+
+    def router_forward(self, x, w_router, logits=None, stream=None):
+        """logits = x w_router^T (fp32) through moe_router_fwd; w_router [E_total, H]."""
+        d = self.desc
+        if logits is None:
+            logits = torch.empty(d.T, d.E_total, dtype=torch.float32, device=self.device)
+        ws = self._router_ws()
+        binding.moe_router_fwd(d, x, w_router, logits, ws, ws.numel(), stream)
+        return logits
+
+    def router_backward(self, x, w_router, dlogits, dx, dw_router=None, stream=None):
+        """dw_router = dlogits^T x (returned), and dx += dlogits w_router in place."""
+        d = self.desc
+        if dw_router is None:
+            dw_router = torch.empty(d.E_total, d.H, dtype=self.dtype, device=self.device)
+        ws = self._router_ws()
+        binding.moe_router_bwd(d, x, w_router, dlogits, dx, dw_router, ws, ws.numel(), stream)
+        return dw_router
 
     def routing(self):
         """Routing results from `saved` as CPU tensors: idx, weight, counts, offsets, perm, pair_pos."""

@@ -126,3 +126,33 @@ def test_status_strings():
     for code in range(6):
         assert L.moe_status_string(code)
     assert L.moe_profile_kernel(10 ** 6, None, None, None) != 0
+
+
+def test_router_validation_without_launching():
+    d = desc(T=300, E_total=40, topk=2)
+    fwd, bwd = b.query_router_sizes(d)
+    with pytest.raises(b.MoEError, match="MOE_ERR_UNSUPPORTED_MODE"):
+        b.query_router_sizes(desc(mode="fp32"))
+    with pytest.raises(b.MoEError, match="MOE_ERR_UNSUPPORTED_MODE"):
+        b.moe_router_fwd(desc(mode="fp32"), FAKE, FAKE, FAKE, FAKE, fwd, stream=0)
+    with pytest.raises(b.MoEError, match="w_router is null"):
+        b.moe_router_fwd(d, FAKE, None, FAKE, FAKE, fwd, stream=0)
+    with pytest.raises(b.MoEError, match="logits is not 16-byte aligned"):
+        b.moe_router_fwd(d, FAKE, FAKE, FAKE + 4, FAKE, fwd, stream=0)
+    with pytest.raises(b.MoEError, match="MOE_ERR_WORKSPACE_TOO_SMALL"):
+        b.moe_router_fwd(d, FAKE, FAKE, FAKE, FAKE, fwd - 1, stream=0)
+    with pytest.raises(b.MoEError, match="dw_router is null"):
+        b.moe_router_bwd(d, FAKE, FAKE, FAKE, FAKE, None, FAKE, bwd, stream=0)
+    with pytest.raises(b.MoEError, match="MOE_ERR_WORKSPACE_TOO_SMALL"):
+        b.moe_router_bwd(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, bwd - 256, stream=0)
+    with pytest.raises(b.MoEError, match="ws is not 256-byte aligned"):
+        b.moe_router_bwd(d, FAKE, FAKE, FAKE + 4, FAKE, FAKE, FAKE + 16, bwd, stream=0)
+
+
+@pytest.mark.parametrize("T,H,E", [(300, 256, 40), (16384, 2048, 128), (5, 512, 512), (70000, 1024, 64)])
+def test_router_sizes_cover_the_partials(T, H, E):
+    fwd, bwd = b.query_router_sizes(desc(T=T, H=H, E_total=E, topk=2))
+    Ep = (E + 63) // 64 * 64
+    assert fwd % 256 == 0 and bwd % 256 == 0
+    assert fwd >= T * Ep * 4                        # at least one slice of fp32 partial logits
+    assert bwd >= 1024 + T * Ep * 2 + E * H * 4     # zero page, bf16 dlogits, at least one dW_r slice

@@ -1,0 +1,157 @@
+"""GPU parity of the router projection in front of the layer (moe_router_fwd, moe_router_bwd)
+against the float64 oracle (oracle.router_forward, oracle.router_backward).
+
+Bar (relative Frobenius error per output, as for the layer):
+ * logits <= 1e-5. Products of bf16 values are exact in fp32, and the fp32 sums (MFMA blocks of the
+   H-slices, then at most 4 slice partials in a fixed order) stay within a few 2^-24 sqrt(H) of
+   the float64 values relative to the row's scale: about 4e-6 at H = 4096.
+ * dW_r and the router's part of dx <= 1e-2 (the bf16 bar): the backward multiplies a bf16 copy of
+   dlogits (relative rounding 2^-9) and rounds its outputs to bf16 once.
+ * Bitwise reproducible across calls.
+The composition test runs x, W_r -> router -> layer -> router backward on the GPU and compares the
+total dx and dW_r with the oracle's chain on the same fp32 logits (so that both route alike).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_layer_32_amd import inputs
+from mixture_experts_layer_32_amd.layer import MoELayer
+from gpu_util import to_dev, run_layer
+
+pytestmark = pytest.mark.gpu
+
+TOL_LOGITS = 1e-5
+TOL_BWD = 1e-2
+
+
+def sparse_dlogits(T, E, k, seed):
+    """k nonzero entries per row, like the layer's dlogits."""
+    rng = np.random.default_rng(seed)
+    dl = np.zeros((T, E), np.float32)
+    for t in range(T):
+        dl[t, rng.choice(E, size=min(k, E), replace=False)] = rng.standard_normal(min(k, E)).astype(np.float32)
+    return dl
+
+
+CASES = [
+    ("basic", dict(T=256, H=256, E=8, k=2), "bf16"),
+    ("ragged_T300_E40", dict(T=300, H=256, E=40, k=3), "bf16"),
+    ("E128_T513_H512", dict(T=513, H=512, E=128, k=8), "bf16"),
+    ("E200_H768", dict(T=1000, H=768, E=200, k=4), "bf16"),
+    ("E512_T70", dict(T=70, H=256, E=512, k=8), "bf16"),
+    ("single_token", dict(T=1, H=256, E=8, k=2), "bf16"),
+    ("wide_H4096", dict(T=130, H=4096, E=64, k=4), "bf16"),
+    ("mxfp8_mode", dict(T=300, H=512, E=40, k=3), "mxfp8"),
+]
+
+
+def router_inputs(T, H, E, k, seed):
+    cfg, L = inputs.custom_layer(T=T, H=H, F=128, E=E, k=k, seed=seed)
+    return cfg, L["x"], inputs.router_weight(cfg)
+
+
+@pytest.mark.parametrize("name,shape,mode", CASES, ids=[c[0] for c in CASES])
+def test_router_parity(name, shape, mode):
+    print(f"case router {name} mode={mode} {shape}", flush=True)
+    cfg, x, wr = router_inputs(**shape, seed=51)
+    T, H, E = cfg.T, cfg.H, cfg.E
+    layer = MoELayer(T, H, 128, E, cfg.k, mode)
+    xd, wrd = to_dev(x, torch.bfloat16), to_dev(wr, torch.bfloat16)
+    lg = layer.router_forward(xd, wrd)
+    torch.cuda.synchronize()
+    ref = oracle.router_forward(x, wr)
+    e_fwd = oracle.rel_frobenius(lg.cpu().numpy(), ref)
+    for dense in (False, True):
+        dl = np.random.default_rng(52).standard_normal((T, E)).astype(np.float32) if dense \
+            else sparse_dlogits(T, E, cfg.k, 53)
+        dwr_ref, dxr_ref = oracle.router_backward(dl, x, wr)
+        dx0 = np.zeros((T, H), np.float32)
+        dx = to_dev(dx0, torch.bfloat16)
+        dwr = layer.router_backward(xd, wrd, to_dev(dl, torch.float32), dx)
+        torch.cuda.synchronize()
+        e_dw = oracle.rel_frobenius(dwr.float().cpu().numpy(), dwr_ref)
+        e_dx = oracle.rel_frobenius(dx.float().cpu().numpy(), dxr_ref)
+        # dx is accumulated into: start from a nonzero dx of the same scale
+        dx1 = inputs.round_to_bf16((np.random.default_rng(54).standard_normal((T, H)) *
+                                    np.sqrt(np.mean(dxr_ref ** 2))).astype(np.float32))
+        dxt = to_dev(dx1, torch.bfloat16)
+        layer.router_backward(xd, wrd, to_dev(dl, torch.float32), dxt)
+        torch.cuda.synchronize()
+        e_acc = oracle.rel_frobenius(dxt.float().cpu().numpy(), dx1.astype(np.float64) + dxr_ref)
+        print(name, "dense" if dense else "sparse", f"logits {e_fwd:.2e} dW_r {e_dw:.2e} dx {e_dx:.2e} "
+              f"dx accumulated {e_acc:.2e}", flush=True)
+        assert e_dw <= TOL_BWD and e_dx <= TOL_BWD and e_acc <= TOL_BWD
+    assert e_fwd <= TOL_LOGITS
+
+
+def test_router_deterministic():
+    print("case router determinism", flush=True)
+    cfg, x, wr = router_inputs(T=700, H=512, E=96, k=4, seed=61)
+    layer = MoELayer(cfg.T, cfg.H, 128, cfg.E, cfg.k, "bf16")
+    xd, wrd = to_dev(x, torch.bfloat16), to_dev(wr, torch.bfloat16)
+    dl = to_dev(sparse_dlogits(cfg.T, cfg.E, cfg.k, 62), torch.float32)
+    outs = []
+    ws = layer._router_ws()
+    for rep in range(2):
+        ws.fill_(0xFF if rep == 0 else 0x00)     # results must not depend on stale workspace bytes
+        lg = layer.router_forward(xd, wrd)
+        dx = torch.zeros(cfg.T, cfg.H, dtype=torch.bfloat16, device="cuda")
+        dwr = layer.router_backward(xd, wrd, dl, dx)
+        torch.cuda.synchronize()
+        outs.append([t.cpu().numpy().tobytes() for t in (lg, dx.view(torch.int16), dwr.view(torch.int16))])
+    assert outs[0] == outs[1]
+
+
+def test_router_then_layer_composition():
+    """x, W_r -> logits -> layer forward/backward -> router backward, all on the GPU."""
+    print("case router composition", flush=True)
+    cfg, L = inputs.custom_layer(T=400, H=256, F=128, E=16, k=4, seed=71)
+    wr = inputs.router_weight(cfg)
+    layer = MoELayer(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, "bf16")
+    xd, wrd = to_dev(L["x"], torch.bfloat16), to_dev(wr, torch.bfloat16)
+    lg = layer.router_forward(xd, wrd)
+    torch.cuda.synchronize()
+    lg_np = lg.cpu().numpy()
+    assert oracle.rel_frobenius(lg_np, oracle.router_forward(L["x"], wr)) <= TOL_LOGITS
+    # the layer on the GPU's logits (both sides route on the same fp32 bits)
+    L2 = dict(L, logits=lg_np)
+    got = run_layer(cfg, L2, keep_layer=True)
+    gl = got["_layer"]
+    r = oracle.route(lg_np, cfg.k)
+    assert np.array_equal(got["routing"]["idx"], r["idx"])
+    dx = to_dev(got["dx"].astype(np.float32), torch.bfloat16)
+    dwr = gl.router_backward(xd, wrd, to_dev(got["dlogits"].astype(np.float32), torch.float32), dx)
+    torch.cuda.synchronize()
+    args = dict(x=L["x"], logits=lg_np, wg=L["wg"], wu=L["wu"], wd=L["wd"], k=cfg.k)
+    g, _ = oracle.backward(dy=L["dy"], **args)
+    dwr_ref, dxr_ref = oracle.router_backward(g["dlogits"], L["x"], wr)
+    e_dx = oracle.rel_frobenius(dx.float().cpu().numpy(), g["dx"] + dxr_ref)
+    e_dw = oracle.rel_frobenius(dwr.float().cpu().numpy(), dwr_ref)
+    print(f"composition dx {e_dx:.2e} dW_r {e_dw:.2e}", flush=True)
+    assert e_dx <= TOL_BWD and e_dw <= TOL_BWD
+
+
+@pytest.mark.slow
+def test_router_full_size_sampled():
+    """The benchmark shape (T=16384, H=2048, E=128): sampled logits rows, dx rows and dW_r rows."""
+    cfg = inputs.CONFIGS["qwen3_30b_a3b"]
+    print(f"case router full size {cfg.name}", flush=True)
+    x, _, _ = inputs.make_tokens(cfg)
+    wr = inputs.router_weight(cfg)
+    layer = MoELayer(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, "bf16")
+    xd, wrd = to_dev(x, torch.bfloat16), to_dev(wr, torch.bfloat16)
+    lg = layer.router_forward(xd, wrd)
+    dl = sparse_dlogits(cfg.T, cfg.E, cfg.k, 81)
+    dx = torch.zeros(cfg.T, cfg.H, dtype=torch.bfloat16, device="cuda")
+    dwr = layer.router_backward(xd, wrd, to_dev(dl, torch.float32), dx)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(82).choice(cfg.T, size=64, replace=False)
+    experts = np.random.default_rng(83).choice(cfg.E, size=8, replace=False)
+    e_l = oracle.rel_frobenius(lg.cpu().numpy()[rows], oracle.router_forward(x[rows], wr))
+    e_x = oracle.rel_frobenius(dx.float().cpu().numpy()[rows], oracle.router_backward(dl[rows], x[rows], wr)[1])
+    dw_ref = dl[:, experts].astype(np.float64).T @ x.astype(np.float64)
+    e_w = oracle.rel_frobenius(dwr.float().cpu().numpy()[experts], dw_ref)
+    print(f"full size: logits {e_l:.2e} dx {e_x:.2e} dW_r {e_w:.2e}", flush=True)
+    assert e_l <= TOL_LOGITS and e_x <= TOL_BWD and e_w <= TOL_BWD
