@@ -7,21 +7,22 @@
 //  * v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 operands. Lane l holds row l%32 of an operand:
 //    bytes 0-15 are contraction elements 16(l/32) + 0..15 and bytes 16-31 are elements
 //    32 + 16(l/32) + 0..15. The block scale of (row i, 32-element block b) comes from lane i + 32b.
-//  * A K-tile is 64 fp8 elements = 64 bytes per row, so data tiles, the 4-stage LDS ring, the
-//    swizzle and the K-major loader are those of the bf16 engine (engine.h). A lane's two 16-byte
-//    chunks are the ones the bf16 engine reads for its two 16-deep steps.
+//  * A K-tile is 128 fp8 elements = 128 bytes per row (whole cache lines, as in the bf16 engine),
+//    two 64-deep MFMA steps. The data tiles, the swizzle and the K-major loader are the bf16
+//    engine's (engine.h); step s reads chunks 4s + l/32 and 4s + 2 + l/32 of each row. The ring
+//    has 2 stages of 66 KB.
 //  * Every operand is K-major. The quantise kernels and the GEMM epilogues write them that way,
-//    with scales in [rows][K/32] byte arrays. Per stage, each thread also moves one scale dword
-//    per operand into LDS (global_load_lds_dword). Dword d of the stage's scale area holds the
-//    row of quadrant half d/128, 32-row block d%4 and row (d%128)/4 of that block. A lane then
-//    reads the scales of its four 32-row blocks with one 16-byte LDS read.
-//  * A K-tile covers scale columns c = cbase + 2kt and c + 1. Scale bases are multiples of 4 (rows
-//    of H/32, F/32, 2F/32 or Q/32 bytes; expert segments padded to 128 pairs) and K-tile counts are
-//    even, so the dword at column c & ~3 holds K-tile kt's scales in bytes 2(kt & 1) and
-//    2(kt & 1) + 1, and lane l takes byte 2(kt & 1) + l/32.
-//  * Main loop per K-tile: 8 MFMAs (row blocks 0-1), wait + barrier, issue K-tile kt+4, read the
-//    next K-tile's fragments, then the other 8 MFMAs. Fragments are double-buffered, so the
-//    next tile's LDS reads overlap this tile's second half.
+//    with scales in [rows][K/32] byte arrays. A K-tile's 4 scale bytes of a row are one dword at
+//    column cbase + 4kt (scale bases and row lengths are multiples of 4 bytes: rows of H/32, F/32,
+//    2F/32 or Q/32 bytes, expert segments padded to 128 pairs). Per stage, each thread moves one
+//    scale dword per operand into LDS (global_load_lds_dword). Dword d of the stage's scale area
+//    holds the row of quadrant half d/128, 32-row block d%4 and row (d%128)/4 of that block. A lane
+//    reads the scales of its four 32-row blocks with one 16-byte LDS read, and takes byte
+//    2s + l/32 in step s.
+//  * Main loop per K-tile: step 0's MFMAs of row blocks 0-1, the reads of step 1's fragments, step
+//    0's MFMAs of row blocks 2-3 and step 1's of blocks 0-1; then wait + barrier, the issue of
+//    K-tile kt+2, the reads of the next K-tile's step-0 fragments, and step 1's MFMAs of blocks
+//    2-3. Fragments are double-buffered, so LDS reads overlap MFMAs.
 //  * Epilogues quantise in registers where the next GEMM needs an fp8 operand. 4 lanes hold a
 //    block of 32 along F (row pass) or along the pairs (transposed pass); two shuffles give its
 //    amax.
@@ -38,10 +39,11 @@ using namespace eng;
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-typedef KRows<64> KOp;                         // K-tile: 64 fp8 = 64 bytes per row
-constexpr int LOADS = KOp::LOADS;              // 4 direct-to-LDS loads per lane per operand per K-tile
-constexpr int STAGES = 4;                      // LDS ring depth (4 x 34 KB)
-constexpr int OPB = 16384;                     // data bytes per operand per stage (256 rows x 64 B)
+constexpr int KTILE = 128;                     // fp8 contraction elements per K-tile
+typedef KRows<128> KOp;                        // 128 bytes per row per K-tile
+constexpr int LOADS = KOp::LOADS;              // 8 direct-to-LDS loads per lane per operand per K-tile
+constexpr int STAGES = 2;                      // LDS ring depth (2 x 66 KB)
+constexpr int OPB = 32768;                     // data bytes per operand per stage (256 rows x 128 B)
 constexpr int STB = 2 * OPB;
 constexpr int SCB = 1024;                      // scale bytes per operand per stage (256 dwords)
 constexpr int STB_MX = STB + 2 * SCB;          // stage: A data, B data, A scales, B scales
@@ -66,15 +68,14 @@ struct SOp {
   const uint8_t* row;
   int cbase;
   __device__ __forceinline__ void issue(char* area, int kt) const {
-    const int c = cbase + 2 * kt;
-    gl2lds_dword(row + (c & ~3), area + wave_id() * 256);
+    gl2lds_dword(row + cbase + 4 * kt, area + wave_id() * 256);
   }
 };
 
-__device__ __forceinline__ i32x8 frag8(const char* tile, int row0, int lane) {
+__device__ __forceinline__ i32x8 frag8(const char* tile, int row0, int s, int lane) {
   const int r = row0 + (lane & 31), h = lane >> 5;
-  const uint4 lo = *reinterpret_cast<const uint4*>(KOp::at(tile, r, h));
-  const uint4 hi = *reinterpret_cast<const uint4*>(KOp::at(tile, r, 2 + h));
+  const uint4 lo = *reinterpret_cast<const uint4*>(KOp::at(tile, r, 4 * s + h));
+  const uint4 hi = *reinterpret_cast<const uint4*>(KOp::at(tile, r, 4 * s + 2 + h));
   const i32x8 v = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   return v;
 }
@@ -84,12 +85,13 @@ struct Frags {
   uint4 sa, sb;   // scale dwords of the lane's four A blocks and four B blocks
 };
 
-__device__ __forceinline__ void read_frags_mx(Frags& f, const char* st, int am0, const int (&bn)[4], int wm, int wn,
-                                              int lane) {
+// step s of the K-tile staged at st
+__device__ __forceinline__ void read_frags_mx(Frags& f, const char* st, int s, int am0, const int (&bn)[4], int wm,
+                                              int wn, int lane) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f.a[i] = frag8(st, am0 + 32 * i, lane);
+  for (int i = 0; i < 4; ++i) f.a[i] = frag8(st, am0 + 32 * i, s, lane);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) f.b[j] = frag8(st + OPB, bn[j], lane);
+  for (int j = 0; j < 4; ++j) f.b[j] = frag8(st + OPB, bn[j], s, lane);
   f.sa = *reinterpret_cast<const uint4*>(st + 2 * OPB + (wm * 128 + (lane & 31) * 4) * 4);
   f.sb = *reinterpret_cast<const uint4*>(st + 2 * OPB + SCB + (wn * 128 + (lane & 31) * 4) * 4);
 }
@@ -126,26 +128,27 @@ __device__ __forceinline__ void issue_tile(char* st, const LA& la, const LB& lb,
   sb.issue(st + 2 * OPB + SCB, kt);
 }
 
-// One K-tile: MFMAs of row blocks 0-1, then the barrier that publishes K-tile kt+1, the issue of
-// K-tile kt+STAGES into the stage K-tile kt came from, and the reads of K-tile kt+1's fragments, then
-// MFMAs of row blocks 2-3. The wait, barrier and fragment reads run unconditionally: past the last
-// K-tile they reread a stage that is no longer refilled, and the fragments go unused. Keeping
-// them unconditional lets the compiler hold both fragment sets in registers. ODD is the parity of
-// kt: with the scale base a multiple of 4, K-tile kt's scales are bytes 2*ODD + lane/32.
-template <int ODD, class LA, class LB>
-__device__ __forceinline__ void step_mx(f32x16 (&acc)[4][4], char* smem, const LA& la, const LB& lb, const SOp& sa,
-                                        const SOp& sb, int kt, int nk, const Frags& cur, Frags& nxt, int am0,
-                                        const int (&bn)[4], int wm, int wn, int lane) {
-  const int sel = 16 * ODD + 8 * (lane >> 5);
-  mma_half(acc, cur, 0, sel, sel);
+// One K-tile (see the engine notes above). The wait, barrier and fragment reads run unconditionally:
+// past the last K-tile they reread a stage that is no longer refilled, and the fragments go unused.
+// Keeping them unconditional lets the compiler hold both fragment sets in registers.
+template <class LA, class LB>
+__device__ __forceinline__ void ktile_mx(f32x16 (&acc)[4][4], char* smem, const LA& la, const LB& lb, const SOp& sa,
+                                         const SOp& sb, int kt, int nk, Frags& f0, Frags& f1, int am0,
+                                         const int (&bn)[4], int wm, int wn, int lane) {
+  char* cur = smem + (kt % STAGES) * STB_MX;
+  const int h8 = 8 * (lane >> 5);
+  mma_half(acc, f0, 0, h8, h8);
+  read_frags_mx(f1, cur, 1, am0, bn, wm, wn, lane);
+  mma_half(acc, f0, 2, h8, h8);
+  mma_half(acc, f1, 0, 16 + h8, 16 + h8);
   wait_tile_mx(min(nk - 2 - kt, STAGES - 2));
   block_sync();
-  if (kt + STAGES < nk) issue_tile(smem + (kt % STAGES) * STB_MX, la, lb, sa, sb, kt + STAGES);
-  read_frags_mx(nxt, smem + ((kt + 1) % STAGES) * STB_MX, am0, bn, wm, wn, lane);
-  mma_half(acc, cur, 2, sel, sel);
+  if (kt + STAGES < nk) issue_tile(cur, la, lb, sa, sb, kt + STAGES);
+  read_frags_mx(f0, smem + ((kt + 1) % STAGES) * STB_MX, 0, am0, bn, wm, wn, lane);
+  mma_half(acc, f1, 2, 16 + h8, 16 + h8);
 }
 
-// nk K-tiles (nk even; every scale base a multiple of 4 scale columns).
+// nk K-tiles of 128 elements (every scale base a multiple of 4 scale columns).
 template <class LA, class LB>
 __device__ __forceinline__ void mainloop_mx(f32x16 (&acc)[4][4], char* smem, const LA& la, const LB& lb, const SOp& sa,
                                             const SOp& sb, int nk, int am0, const int (&bn)[4], int wm, int wn) {
@@ -165,11 +168,8 @@ __device__ __forceinline__ void mainloop_mx(f32x16 (&acc)[4][4], char* smem, con
   wait_tile_mx(min(nk - 1, STAGES - 1));
   block_sync();
   Frags f0, f1;
-  read_frags_mx(f0, smem, am0, bn, wm, wn, lane);
-  for (int kt = 0; kt < nk; kt += 2) {
-    step_mx<0>(acc, smem, la, lb, sa, sb, kt, nk, f0, f1, am0, bn, wm, wn, lane);
-    step_mx<1>(acc, smem, la, lb, sa, sb, kt + 1, nk, f1, f0, am0, bn, wm, wn, lane);
-  }
+  read_frags_mx(f0, smem, 0, am0, bn, wm, wn, lane);
+  for (int kt = 0; kt < nk; ++kt) ktile_mx(acc, smem, la, lb, sa, sb, kt, nk, f0, f1, am0, bn, wm, wn, lane);
   block_sync();
 }
 
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_gateup_mx(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) wrow[i] = p.weight[p.perm[min(r0 + 128 * wm + acc_m(i, lane), seg_end - 1)]];
     f32x16 acc[4][4];
-    mainloop_mx(acc, smem, la, lb, sa, sb, H / 64, 128 * wm, bn, wm, wn);
+    mainloop_mx(acc, smem, la, lb, sa, sb, H / KTILE, 128 * wm, bn, wm, wn);
     float* slab = wave_slab(smem);
     const int f0 = nt * 128 + 64 * wn;
     const int qend = p.qoff[e + 1];
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_down_mx(FwdParams p) {
     const SOp sa{p.hws + (size_t)min(r0 + row_s, seg_end - 1) * fs, 0};
     const SOp sb{p.wds + ((size_t)e * H + nt * TILE + row_s) * fs, 0};
     f32x16 acc[4][4];
-    mainloop_mx(acc, smem, la, lb, sa, sb, F / 64, 128 * wm, bn, wm, wn);
+    mainloop_mx(acc, smem, la, lb, sa, sb, F / KTILE, 128 * wm, bn, wm, wn);
     const int rq = r0 + 128 * wm;
     bf16* const oq = o + nt * TILE + 128 * wn;
     store_quadrant(smem, acc, lane, [&](int m) { return rq + m < seg_end ? oq + (size_t)(rq + m) * H : nullptr; }, 128);
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_dh_mx(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) wrow[i] = p.weight[p.perm[min(r0 + 128 * wm + acc_m(i, lane), seg_end - 1)]];
     f32x16 acc[4][4];
-    mainloop_mx(acc, smem, la, lb, sa, sb, H / 64, 128 * wm, bn, wm, wn);
+    mainloop_mx(acc, smem, la, lb, sa, sb, H / KTILE, 128 * wm, bn, wm, wn);
     float* slab = wave_slab(smem);
     float* slab2 = slab + 4 * SLAB;
     const int fq = nt * TILE + 128 * wn;
@@ -419,7 +419,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_dgrad_x_mx(BwdParams p) {
     const SOp sa{p.dabs + (size_t)min(r0 + row_s, seg_end - 1) * f2s, 0};
     const SOp sb{p.wguts + ((size_t)e * H + nt * TILE + row_s) * f2s, 0};
     f32x16 acc[4][4];
-    mainloop_mx(acc, smem, la, lb, sa, sb, 2 * F / 64, 128 * wm, bn, wm, wn);
+    mainloop_mx(acc, smem, la, lb, sa, sb, 2 * F / KTILE, 128 * wm, bn, wm, wn);
     const int rq = r0 + 128 * wm;
     bf16* const oq = dxp + nt * TILE + 128 * wn;
     store_quadrant(smem, acc, lane, [&](int m) { return rq + m < seg_end ? oq + (size_t)(rq + m) * H : nullptr; }, 128);
@@ -438,7 +438,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_wgrad_down_mx(BwdParams p) {
   const int row_s = 128 * sc_half() + 32 * sc_blk() + sc_row32();
   for (int lid = xr.first; lid < xr.end; lid += xr.stride) {
     const int e = lid / tpe, t = lid - e * tpe, mt = t / ntn, nt = t - mt * ntn;
-    const int q0 = p.qoff[e], nk = (p.qoff[e + 1] - q0) / 64;
+    const int q0 = p.qoff[e], nk = (p.qoff[e + 1] - q0) / KTILE;
     KOp la, lb;
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
@@ -468,7 +468,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_wgrad_gateup_mx(BwdParams p) {
   const int row_s = 128 * sc_half() + 32 * sc_blk() + sc_row32();
   for (int lid = xr.first; lid < xr.end; lid += xr.stride) {
     const int e = lid / tpe, t = lid - e * tpe, mt = t / ntn, nt = t - mt * ntn;
-    const int q0 = p.qoff[e], nk = (p.qoff[e + 1] - q0) / 64;
+    const int q0 = p.qoff[e], nk = (p.qoff[e + 1] - q0) / KTILE;
     KOp la, lb;
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
