@@ -126,18 +126,6 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
   return __builtin_bit_cast(uint2, v);
 }
 __device__ __forceinline__ void st8(void* p, uint2 v) { *reinterpret_cast<uint2*>(p) = v; }
-// Epilogue outputs are written once and read by a later kernel. Non-temporal stores keep them from
-// displacing, in L2, the operand tiles that other workgroups still reuse (measured 2-5 % per GEMM).
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void st16_nt(void* p, uint4 v) {
-  const u32x4 w = {v.x, v.y, v.z, v.w};
-  __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
-}
-__device__ __forceinline__ void st8_nt(void* p, uint2 v) {
-  const u32x2 w = {v.x, v.y};
-  __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
-}
 // ------------------------------------------------------------------------------------------------
 // Epilogue staging. After the main loop the LDS ring is free. Each wave stages 32 rows of its
 // NJ blocks of 32 columns as fp32 (row stride 32 NJ + 4 floats, so the 32 rows of one write land in
@@ -222,7 +210,7 @@ __device__ __forceinline__ void store_transposed(const float* slab, int lane, in
       float v[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) v[t] = slab[(g8 + t) * Stage<NJ>::LD + c];
-      st16_nt(o + g8, pack8(v));
+      st16(o + g8, pack8(v));   // 64 bytes per column: ordinary store (non-temporal partial lines are slow)
     }
   }
 }
@@ -246,7 +234,7 @@ __device__ __forceinline__ void store_transposed_mx(const float* slab, int lane,
     const int s = mx_exponent(mx_amax_x4(v));
     uint8_t* o = dst(c);
     if (o) {
-      st8_nt(o + g8, mx_encode8(v, s));
+      *reinterpret_cast<uint2*>(o + g8) = mx_encode8(v, s);
       if ((lane & 3) == 0) *sdst(c) = (uint8_t)(s + 127);
     }
   }

@@ -647,10 +647,10 @@ __device__ __forceinline__ void store_block_f32(char* smem, const f32x16 (&acc)[
       if (o && c0 < ncols) {
         float v[8];
         read8<NJ>(slab, rl, c0, v);
-        st16_nt(o + c0, make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                                   __float_as_uint(v[3])));
-        st16_nt(o + c0 + 4, make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]),
-                                       __float_as_uint(v[7])));
+        st16(o + c0, make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                __float_as_uint(v[3])));
+        st16(o + c0 + 4, make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]),
+                                    __float_as_uint(v[7])));
       }
     }
   }

@@ -237,7 +237,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_gateup_mx(FwdParams p) {
         }
         const int sx = mx_exponent(mx_amax_x4(hv));
         if (ok) {
-          st8_nt(p.hwq + (size_t)r * F + f0 + c0, mx_encode8(hv, sx));
+          *reinterpret_cast<uint2*>(p.hwq + (size_t)r * F + f0 + c0) = mx_encode8(hv, sx);
           if ((lane & 3) == 0) p.hws[(size_t)r * (F / 32) + (f0 + c0) / 32] = (uint8_t)(sx + 127);
         }
         *reinterpret_cast<float4*>(slab + rl * SLD + c0) = make_float4(hv[0], hv[1], hv[2], hv[3]);
@@ -359,8 +359,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_dh_mx(BwdParams p) {
         const int sdb = mx_exponent(mx_amax_x4(db));
         if (ok) {
           uint8_t* qr = p.dabq + (size_t)r * 2 * F + f;
-          st8_nt(qr, mx_encode8(da, sda));
-          st8_nt(qr + F, mx_encode8(db, sdb));
+          *reinterpret_cast<uint2*>(qr) = mx_encode8(da, sda);
+          *reinterpret_cast<uint2*>(qr + F) = mx_encode8(db, sdb);
           if ((lane & 3) == 0) {
             uint8_t* sr = p.dabs + (size_t)r * f2s;
             sr[f / 32] = (uint8_t)(sda + 127);

@@ -8,12 +8,12 @@
 //   k_quant_cols      along the strided axis, transposing: W_down[e] (H x F) along H into F x H,
 //                     and W_gate[e], W_up[e] (F x H) along F into the two halves of H x 2F.
 //   k_quant_both      both orientations of one weight tensor from one read (the MXFP8 forward
-//                     quantises each weight once per step for both passes).
+//                     quantises each weight once per step for both passes); 128 x 128 tiles.
 //   k_gather_t_quant  along an expert's pairs, transposing and gathering: dY and x rows of the
 //                     expert's tokens, in the sorted pair order, into [H][Q] where the expert's
 //                     pairs occupy columns qoff[e] .. qoff[e+1] (zero-padded to a multiple of 128).
-// The transposing kernels stage 128 x 64 tiles in LDS, so that every row segment they read or
-// write is one whole 128-byte line.
+// The transposing kernels stage 128 x 64 (k_quant_both: 128 x 128) tiles in LDS, so that every row
+// segment they read or write is one whole 128-byte line.
 // The quantised element and scale formulas are in mx_device.h.
 #include "moe_device.h"
 #include "moe_internal.h"
@@ -101,30 +101,62 @@ __global__ __launch_bounds__(256) void k_quant_cols(const bf16* __restrict__ in,
 
 // Both orientations of one weight tensor in one read: in [B][R][C] ->
 //   rows: qr [B][R][C] with blocks of 32 along C, scales sr [B][R][C/32]
-//   cols: as k_quant_cols (blocks of 32 along R, written transposed at column col0 of rows of ldo)
-// Grid (C / 64, R / 128, B).
+//   cols: blocks of 32 along R, written transposed at column col0 of rows of ldo bytes:
+//         qc [B][C][ldo], scales scc [B][C][ldo/32]
+// Grid (C / 128, R / 128, B). A block stages a 128 x 128 bf16 tile (32 KB), so that the row pass
+// writes whole 128-byte lines of fp8 (16 lanes per row, quantised from the registers that loaded
+// the tile) and the column pass too (each thread quantises two blocks of 32 of one column). The
+// input is read once: non-temporal loads. The stores stay ordinary: each instruction writes less
+// than a whole line per row, and non-temporal partial-line stores ran 3.4x slower.
 __global__ __launch_bounds__(256) void k_quant_both(const bf16* __restrict__ in, uint8_t* __restrict__ qr,
                                                     uint8_t* __restrict__ sr, uint8_t* __restrict__ qc,
                                                     uint8_t* __restrict__ scc, int R, int C, int64_t ldo, int col0) {
-  __shared__ __attribute__((aligned(16))) bf16 tile[128][64];
-  const int b = blockIdx.z, r0 = blockIdx.y * 128, c0 = blockIdx.x * 64;
+  __shared__ __attribute__((aligned(16))) bf16 tile[128][128];
+  const int t = threadIdx.x, b = blockIdx.z, r0 = blockIdx.y * 128, c0 = blockIdx.x * 128;
   const bf16* src = in + ((size_t)b * R + r0) * C + c0;
-  uint4 raw[4];
-  load_tile(tile, [&](int row) { return src + (size_t)row * C; }, raw);
-  // row pass from registers: the 4 lanes 4g..4g+3 hold one row's block of 32 along C
+  const int col8 = (t & 15) * 8;
+  uint4 raw[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
+    const int row = (t >> 4) + 16 * i;
+    raw[i] = ld16_nt(src + (size_t)row * C + col8);
+    *reinterpret_cast<uint4*>(&tile[row][col8]) = raw[i];
+  }
+  // row pass: the 4 lanes 4g..4g+3 hold one row's block of 32 along C
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
     float v[8];
     unpack8f(raw[i], v);
     const int s = mx_exponent(mx_amax_x4(v));
-    const int row = (threadIdx.x >> 3) + 32 * i, c8 = (threadIdx.x & 7) * 8;
-    const size_t grow = (size_t)b * R + r0 + row;
-    *reinterpret_cast<uint2*>(qr + grow * C + c0 + c8) = mx_encode8(v, s);
-    if ((threadIdx.x & 3) == 0) sr[grow * (C / 32) + (c0 + c8) / 32] = (uint8_t)(s + 127);
+    const size_t grow = (size_t)b * R + r0 + (t >> 4) + 16 * i;
+    *reinterpret_cast<uint2*>(qr + grow * C + c0 + col8) = mx_encode8(v, s);
+    if ((t & 3) == 0) sr[grow * (C / 32) + (c0 + col8) / 32] = (uint8_t)(s + 127);
   }
   __syncthreads();
-  const size_t orow = (size_t)b * C + c0 + (threadIdx.x & 63);
-  column_pass(tile, qc + orow * ldo + col0 + r0, scc + orow * (ldo / 32) + (col0 + r0) / 32);
+  // column pass: thread t quantises column t & 127, blocks of 32 rows 2 (t >> 7) and 2 (t >> 7) + 1
+  const int c = t & 127;
+  const size_t orow = (size_t)b * C + c0 + c;
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) {
+    const int blk = 2 * (t >> 7) + bb;
+    float v[32];
+    float m = 0.f;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      v[r] = (float)tile[32 * blk + r][c];
+      m = fmaxf(m, fabsf(v[r]));
+    }
+    const int s = mx_exponent(m);
+    const float sm = mx_inv_scale(s);
+    unsigned w[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g)
+      w[g] = mx_cvt4(mx_sat(v[4 * g] * sm), mx_sat(v[4 * g + 1] * sm), mx_sat(v[4 * g + 2] * sm), mx_sat(v[4 * g + 3] * sm));
+    uint8_t* o = qc + orow * ldo + col0 + r0 + 32 * blk;
+    st16(o, make_uint4(w[0], w[1], w[2], w[3]));
+    st16(o + 16, make_uint4(w[4], w[5], w[6], w[7]));
+    scc[orow * (ldo / 32) + (col0 + r0) / 32 + blk] = (uint8_t)(s + 127);
+  }
 }
 
 // Grid (qc / 128, H / 64). Window w covers columns 128w .. 128w+127 of [H][qc], inside one
@@ -175,7 +207,7 @@ hipError_t launch_quant_cols(const void* in, uint8_t* q, uint8_t* sc, int B, int
 hipError_t launch_quant_both(const void* in, uint8_t* qr, uint8_t* sr, uint8_t* qc, uint8_t* scc, int B, int R, int C,
                              int64_t ldo, int col0, const char* name, hipStream_t s) {
   prof_mark_begin(name, s);
-  k_quant_both<<<dim3(C / 64, R / 128, B), 256, 0, s>>>(static_cast<const bf16*>(in), qr, sr, qc, scc, R, C, ldo, col0);
+  k_quant_both<<<dim3(C / 128, R / 128, B), 256, 0, s>>>(static_cast<const bf16*>(in), qr, sr, qc, scc, R, C, ldo, col0);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   prof_mark_end(s);
