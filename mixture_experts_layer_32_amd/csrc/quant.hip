@@ -12,8 +12,8 @@
 //   k_gather_t_quant  along an expert's pairs, transposing and gathering: dY and x rows of the
 //                     expert's tokens, in the sorted pair order, into [H][Q] where the expert's
 //                     pairs occupy columns qoff[e] .. qoff[e+1] (zero-padded to a multiple of 128).
-// The transposing kernels stage 128 x 64 (k_quant_both: 128 x 128) tiles in LDS, so that every row
-// segment they read or write is one whole 128-byte line.
+// The transposing kernels stage 128 x 64 tiles (k_quant_both: 128 x 128) in LDS, so that every
+// row segment they read or write is one or two whole 128-byte lines.
 // The quantised element and scale formulas are in mx_device.h.
 #include "moe_device.h"
 #include "moe_internal.h"
@@ -99,6 +99,33 @@ __global__ __launch_bounds__(256) void k_quant_cols(const bf16* __restrict__ in,
   column_pass(tile, q + orow * ldo + col0 + r0, sc + orow * (ldo / 32) + (col0 + r0) / 32);
 }
 
+// Column pass on a 128 x 128 LDS tile: thread t quantises column t & 127 over the blocks of 32 rows
+// 2 (t >> 7) and 2 (t >> 7) + 1, into the 32-byte segments out_row + 32 blk and the scale bytes
+// sc_row[blk]. The two threads of a column write one whole 128-byte line.
+__device__ __forceinline__ void column_pass128(const bf16 (*tile)[128], uint8_t* out_row, uint8_t* sc_row) {
+  const int t = threadIdx.x, c = t & 127;
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) {
+    const int blk = 2 * (t >> 7) + bb;
+    float v[32];
+    float m = 0.f;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      v[r] = (float)tile[32 * blk + r][c];
+      m = fmaxf(m, fabsf(v[r]));
+    }
+    const int s = mx_exponent(m);
+    const float sm = mx_inv_scale(s);
+    unsigned w[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g)
+      w[g] = mx_cvt4(mx_sat(v[4 * g] * sm), mx_sat(v[4 * g + 1] * sm), mx_sat(v[4 * g + 2] * sm), mx_sat(v[4 * g + 3] * sm));
+    st16(out_row + 32 * blk, make_uint4(w[0], w[1], w[2], w[3]));
+    st16(out_row + 32 * blk + 16, make_uint4(w[4], w[5], w[6], w[7]));
+    sc_row[blk] = (uint8_t)(s + 127);
+  }
+}
+
 // Both orientations of one weight tensor in one read: in [B][R][C] ->
 //   rows: qr [B][R][C] with blocks of 32 along C, scales sr [B][R][C/32]
 //   cols: blocks of 32 along R, written transposed at column col0 of rows of ldo bytes:
@@ -133,34 +160,13 @@ __global__ __launch_bounds__(256) void k_quant_both(const bf16* __restrict__ in,
     if ((t & 3) == 0) sr[grow * (C / 32) + (c0 + col8) / 32] = (uint8_t)(s + 127);
   }
   __syncthreads();
-  // column pass: thread t quantises column t & 127, blocks of 32 rows 2 (t >> 7) and 2 (t >> 7) + 1
-  const int c = t & 127;
-  const size_t orow = (size_t)b * C + c0 + c;
-#pragma unroll
-  for (int bb = 0; bb < 2; ++bb) {
-    const int blk = 2 * (t >> 7) + bb;
-    float v[32];
-    float m = 0.f;
-#pragma unroll
-    for (int r = 0; r < 32; ++r) {
-      v[r] = (float)tile[32 * blk + r][c];
-      m = fmaxf(m, fabsf(v[r]));
-    }
-    const int s = mx_exponent(m);
-    const float sm = mx_inv_scale(s);
-    unsigned w[8];
-#pragma unroll
-    for (int g = 0; g < 8; ++g)
-      w[g] = mx_cvt4(mx_sat(v[4 * g] * sm), mx_sat(v[4 * g + 1] * sm), mx_sat(v[4 * g + 2] * sm), mx_sat(v[4 * g + 3] * sm));
-    uint8_t* o = qc + orow * ldo + col0 + r0 + 32 * blk;
-    st16(o, make_uint4(w[0], w[1], w[2], w[3]));
-    st16(o + 16, make_uint4(w[4], w[5], w[6], w[7]));
-    scc[orow * (ldo / 32) + (col0 + r0) / 32 + blk] = (uint8_t)(s + 127);
-  }
+  const size_t orow = (size_t)b * C + c0 + (t & 127);
+  column_pass128(tile, qc + orow * ldo + col0 + r0, scc + orow * (ldo / 32) + (col0 + r0) / 32);
 }
 
 // Grid (qc / 128, H / 64). Window w covers columns 128w .. 128w+127 of [H][qc], inside one
-// expert's padded segment (segments are multiples of 128 columns).
+// expert's padded segment (segments are multiples of 128 columns). (128 x 128 tiles measured 10-15 %
+// slower here.)
 __global__ __launch_bounds__(256) void k_gather_t_quant(const bf16* __restrict__ x, const int* __restrict__ ptok,
                                                         const int* __restrict__ offsets, const int* __restrict__ qoff,
                                                         int El, int H, int64_t qc, uint8_t* __restrict__ q,
