@@ -6,7 +6,8 @@
 //                     (along H), W_down rows (along F), and the transposed hw copy (along pairs).
 //                     One lane per 8 elements; 4 lanes per block of 32.
 //   k_quant_cols      along the strided axis, transposing: W_down[e] (H x F) along H into F x H,
-//                     and W_gate[e], W_up[e] (F x H) along F into the two halves of H x 2F.
+//                     and W_gate[e], W_up[e] (F x H) along F into the two halves of H x 2F
+//                     (k_quant_cols128 when the column count is a multiple of 128).
 //   k_quant_both      both orientations of one weight tensor from one read (the MXFP8 forward
 //                     quantises each weight once per step for both passes); 128 x 128 tiles.
 //   k_gather_t_quant  along an expert's pairs, transposing and gathering: dY and x rows of the
@@ -126,6 +127,24 @@ __device__ __forceinline__ void column_pass128(const bf16 (*tile)[128], uint8_t*
   }
 }
 
+// As k_quant_cols on 128 x 128 tiles (C a multiple of 128): grid (C / 128, R / 128, B). The two
+// threads of a column write one whole 128-byte line; the input is read once (non-temporal loads).
+__global__ __launch_bounds__(256) void k_quant_cols128(const bf16* __restrict__ in, uint8_t* __restrict__ q,
+                                                       uint8_t* __restrict__ sc, int R, int C, int64_t ldo, int col0) {
+  __shared__ __attribute__((aligned(16))) bf16 tile[128][128];
+  const int t = threadIdx.x, b = blockIdx.z, r0 = blockIdx.y * 128, c0 = blockIdx.x * 128;
+  const bf16* src = in + ((size_t)b * R + r0) * C + c0;
+  const int col8 = (t & 15) * 8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = (t >> 4) + 16 * i;
+    *reinterpret_cast<uint4*>(&tile[row][col8]) = ld16_nt(src + (size_t)row * C + col8);
+  }
+  __syncthreads();
+  const size_t orow = (size_t)b * C + c0 + (t & 127);
+  column_pass128(tile, q + orow * ldo + col0 + r0, sc + orow * (ldo / 32) + (col0 + r0) / 32);
+}
+
 // Both orientations of one weight tensor in one read: in [B][R][C] ->
 //   rows: qr [B][R][C] with blocks of 32 along C, scales sr [B][R][C/32]
 //   cols: blocks of 32 along R, written transposed at column col0 of rows of ldo bytes:
@@ -203,7 +222,10 @@ hipError_t launch_quant_rows(const void* in, uint8_t* q, uint8_t* sc, int64_t n,
 hipError_t launch_quant_cols(const void* in, uint8_t* q, uint8_t* sc, int B, int R, int C, int64_t ldo, int col0,
                              const char* name, hipStream_t s) {
   prof_mark_begin(name, s);
-  k_quant_cols<<<dim3(C / 64, R / 128, B), 256, 0, s>>>(static_cast<const bf16*>(in), q, sc, R, C, ldo, col0);
+  if (C % 128 == 0)
+    k_quant_cols128<<<dim3(C / 128, R / 128, B), 256, 0, s>>>(static_cast<const bf16*>(in), q, sc, R, C, ldo, col0);
+  else
+    k_quant_cols<<<dim3(C / 64, R / 128, B), 256, 0, s>>>(static_cast<const bf16*>(in), q, sc, R, C, ldo, col0);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   prof_mark_end(s);

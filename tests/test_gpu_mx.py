@@ -45,7 +45,8 @@ def _quant_input(rows, cols, seed):
     return v
 
 
-@pytest.mark.parametrize("axis,rows,cols", [(1, 96, 416), (1, 1, 32), (0, 256, 192), (0, 128, 64)])
+@pytest.mark.parametrize("axis,rows,cols", [(1, 96, 416), (1, 1, 32), (0, 256, 192), (0, 128, 64), (0, 256, 384),
+                                            (0, 128, 128)])
 def test_mx_quantize_bit_exact(axis, rows, cols):
     print(f"case mx_quantize axis={axis} {rows}x{cols}", flush=True)
     # blocks are built along the quantisation axis
