@@ -177,7 +177,7 @@ __device__ __forceinline__ void unpack8(uint4 u, float (&v)[8]) {
 // out_row(m) gives the output row pointer of the wave's row m at its first column, or null to skip
 // the row; ncols limits the columns written. A row is read by 4 NJ lanes, 8 columns each.
 template <int MI, int NJ, class OutRow>
-__device__ __forceinline__ void store_quadrant(char* smem, const f32x16 (&acc)[MI][NJ], int lane, OutRow out_row,
+__device__ __forceinline__ void store_wave_block(char* smem, const f32x16 (&acc)[MI][NJ], int lane, OutRow out_row,
                                                int ncols) {
   constexpr int LPR = 4 * NJ, RPP = 64 / LPR;   // lanes per row, rows per pass
   float* slab = wave_slab<NJ>(smem);

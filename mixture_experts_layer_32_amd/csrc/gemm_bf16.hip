@@ -392,7 +392,7 @@ __global__ __launch_bounds__(NTHR8, 1) void k_down_bf16(FwdParams p) {
     ts.fetch();
     const int rq = r0 + 32 * wm;   // the wave's row m is tile row 32 wm + 128 (m / 32) + m % 32
     bf16* const oq = o + nt * TILE + 128 * wn;
-    store_quadrant(smem, acc, lane, [&](int m) {
+    store_wave_block(smem, acc, lane, [&](int m) {
       const int r = rq + 128 * (m >> 5) + (m & 31);
       return r < seg_end ? oq + (size_t)r * H : nullptr;
     }, 128);
@@ -532,7 +532,7 @@ __global__ __launch_bounds__(NTHR8, 1) void k_dgrad_x_bf16(BwdParams p) {
     ts.fetch();
     const int rq = r0 + 32 * wm;   // the wave's row m is tile row 32 wm + 64 (m / 32) + m % 32
     bf16* const oq = dxp + nt * TILE + 64 * wn;
-    store_quadrant(smem, acc, lane, [&](int m) {
+    store_wave_block(smem, acc, lane, [&](int m) {
       const int r = rq + 64 * (m >> 5) + (m & 31);
       return r < seg_end ? oq + (size_t)r * H : nullptr;
     }, 64);
@@ -566,7 +566,7 @@ __global__ __launch_bounds__(NTHR8, 1) void k_wgrad_down_bf16(BwdParams p) {
   mainloop<true, false>(acc, smem, la, lb, (seg_end - seg0 + KTILE - 1) / KTILE, 64 * wm, bn);
   bf16* __restrict__ out = static_cast<bf16*>(p.dwd) + (size_t)e * H * F;
   const int mq = mt * TILE + 64 * wm, nq = nt * TILE + 128 * wn;
-  store_quadrant(smem, acc, lane, [&](int m) { return out + (size_t)(mq + m) * F + nq; }, F - nq);
+  store_wave_block(smem, acc, lane, [&](int m) { return out + (size_t)(mq + m) * F + nq; }, F - nq);
   }
 }
 
@@ -599,7 +599,7 @@ __global__ __launch_bounds__(NTHR8, 1) void k_wgrad_gateup_bf16(BwdParams p) {
   bf16* __restrict__ dwg = static_cast<bf16*>(p.dwg) + (size_t)e * F * H;
   bf16* __restrict__ dwu = static_cast<bf16*>(p.dwu) + (size_t)e * F * H;
   const int mq = mt * TILE + 128 * wm, nq = nt * TILE + 64 * wn;
-  store_quadrant(smem, acc, lane, [&](int m) {
+  store_wave_block(smem, acc, lane, [&](int m) {
     const int mm = mq + m;
     return (mm < F ? dwg + (size_t)mm * H : dwu + (size_t)(mm - F) * H) + nq;
   }, 64);

@@ -278,7 +278,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_down_mx(FwdParams p) {
     mainloop_mx(acc, smem, la, lb, sa, sb, F / KTILE, 128 * wm, bn, wm, wn);
     const int rq = r0 + 128 * wm;
     bf16* const oq = o + nt * TILE + 128 * wn;
-    store_quadrant(smem, acc, lane, [&](int m) { return rq + m < seg_end ? oq + (size_t)(rq + m) * H : nullptr; }, 128);
+    store_wave_block(smem, acc, lane, [&](int m) { return rq + m < seg_end ? oq + (size_t)(rq + m) * H : nullptr; }, 128);
   }
 }
 
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_dgrad_x_mx(BwdParams p) {
     mainloop_mx(acc, smem, la, lb, sa, sb, 2 * F / KTILE, 128 * wm, bn, wm, wn);
     const int rq = r0 + 128 * wm;
     bf16* const oq = dxp + nt * TILE + 128 * wn;
-    store_quadrant(smem, acc, lane, [&](int m) { return rq + m < seg_end ? oq + (size_t)(rq + m) * H : nullptr; }, 128);
+    store_wave_block(smem, acc, lane, [&](int m) { return rq + m < seg_end ? oq + (size_t)(rq + m) * H : nullptr; }, 128);
   }
 }
 
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_wgrad_down_mx(BwdParams p) {
     mainloop_mx(acc, smem, la, lb, sa, sb, nk, 128 * wm, bn, wm, wn);
     bf16* __restrict__ out = static_cast<bf16*>(p.dwd) + (size_t)e * H * F;
     const int mq = mt * TILE + 128 * wm, nq = nt * TILE + 128 * wn;
-    store_quadrant(smem, acc, lane, [&](int m) { return out + (size_t)(mq + m) * F + nq; }, F - nq);
+    store_wave_block(smem, acc, lane, [&](int m) { return out + (size_t)(mq + m) * F + nq; }, F - nq);
   }
 }
 
@@ -483,7 +483,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_wgrad_gateup_mx(BwdParams p) {
     bf16* __restrict__ dwg = static_cast<bf16*>(p.dwg) + (size_t)e * F * H;
     bf16* __restrict__ dwu = static_cast<bf16*>(p.dwu) + (size_t)e * F * H;
     const int mq = mt * TILE + 128 * wm, nq = nt * TILE + 128 * wn;
-    store_quadrant(smem, acc, lane, [&](int m) {
+    store_wave_block(smem, acc, lane, [&](int m) {
       const int mm = mq + m;
       return (mm < F ? dwg + (size_t)mm * H : dwu + (size_t)(mm - F) * H) + nq;
     }, 128);
