@@ -200,7 +200,8 @@ __device__ __forceinline__ void store_wave_block(char* smem, const f32x16 (&acc)
 // Writes staged columns [0, ncol) of the 32 staged rows to a pair-contiguous transposed copy.
 // dst(c) is the copy's row for staged column c, at the pair column of staged row 0 (null: skip).
 // Four lanes cover one column, 8 consecutive pair rows each: one 16-byte store, 64 contiguous bytes
-// per column.
+// per column, 16 columns per instruction. (One lane per column, with conflict-free LDS reads but 64
+// lines per store instruction, made the dgrad of h 9 % slower.)
 template <int NJ = 4, class Dst>
 __device__ __forceinline__ void store_transposed(const float* slab, int lane, int ncol, Dst dst) {
   for (int cb = 0; cb < ncol; cb += 16) {
@@ -226,16 +227,27 @@ __device__ __forceinline__ void unpack4(uint2 v, float (&f)[4]) {
 // column of staged row 0 (a multiple of 32), null to skip; sdst(c) is its scale byte.
 template <int NJ = 4, class Dst, class SDst>
 __device__ __forceinline__ void store_transposed_mx(const float* slab, int lane, int ncol, Dst dst, SDst sdst) {
-  for (int cb = 0; cb < ncol; cb += 16) {
-    const int c = cb + (lane >> 2), g8 = 8 * (lane & 3);
-    float v[8];
+  // one lane per column: the 32 staged rows of the column are one block of 32, so no shuffles for
+  // its amax, and the LDS reads are conflict-free (the 64 lanes read 64 consecutive columns of one
+  // row). Measured 3-6 % faster on the MX gate/up and dH GEMMs than four lanes per column.
+  for (int c = lane; c < ncol; c += 64) {
+    float m = 0.f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) v[t] = slab[(g8 + t) * Stage<NJ>::LD + c];
-    const int s = mx_exponent(mx_amax_x4(v));
+    for (int r = 0; r < 32; ++r) m = fmaxf(m, fabsf(slab[r * Stage<NJ>::LD + c]));
+    const int s = mx_exponent(m);
+    const float sm = mx_inv_scale(s);
+    unsigned w[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const float* col = slab + 4 * g * Stage<NJ>::LD + c;
+      w[g] = mx_cvt4(mx_sat(col[0] * sm), mx_sat(col[Stage<NJ>::LD] * sm), mx_sat(col[2 * Stage<NJ>::LD] * sm),
+                     mx_sat(col[3 * Stage<NJ>::LD] * sm));
+    }
     uint8_t* o = dst(c);
     if (o) {
-      *reinterpret_cast<uint2*>(o + g8) = mx_encode8(v, s);
-      if ((lane & 3) == 0) *sdst(c) = (uint8_t)(s + 127);
+      st16(o, make_uint4(w[0], w[1], w[2], w[3]));
+      st16(o + 16, make_uint4(w[4], w[5], w[6], w[7]));
+      *sdst(c) = (uint8_t)(s + 127);
     }
   }
 }
