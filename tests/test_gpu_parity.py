@@ -142,3 +142,38 @@ def test_full_size_sampled(name):
     sampled_check(cfg, L, got)
     del got
     torch.cuda.empty_cache()
+
+
+# rows per expert at the edges of the 128-row (half) and 256-row tiles, and an empty expert
+TILE_COUNTS = [128, 129, 255, 256, 257, 1, 0, 127, 384, 385]
+
+
+@pytest.mark.parametrize("mode", ["bf16", "mxfp8", "fp8_bwd"])
+def test_tile_boundary_counts(mode):
+    """k = 1 routing forced onto chosen experts (the chosen logit is 6 above the others), so that the
+    expert segments end exactly at, just before and just after the tile edges: half tiles, whole
+    tiles, one-row tails and an empty expert."""
+    E, T = len(TILE_COUNTS), sum(TILE_COUNTS)
+    cfg, L = inputs.custom_layer(T=T, H=256, F=128, E=E, k=1, seed=23)
+    rng = np.random.default_rng(24)
+    assign = np.repeat(np.arange(E), TILE_COUNTS)
+    rng.shuffle(assign)
+    lg = (0.1 * rng.standard_normal((T, E))).astype(np.float32)
+    lg[np.arange(T), assign] += np.float32(6.0)
+    L = dict(L, logits=lg)
+    print(f"case tile_boundary_counts mode={mode} counts={TILE_COUNTS}", flush=True)
+    got = run_layer(cfg, L, mode)
+    r = check_routing(cfg, L, got["routing"])
+    assert list(r["counts"]) == TILE_COUNTS
+    args = dict(x=L["x"], logits=lg, wg=L["wg"], wu=L["wu"], wd=L["wd"], k=1, mode=None if mode == "bf16" else mode)
+    y, _ = oracle.forward(**args)
+    g, _ = oracle.backward(dy=L["dy"], **args)
+    ref = dict(y=y, dx=g["dx"], dlogits=g["dlogits"], dwg=g["dwg"], dwu=g["dwu"], dwd=g["dwd"])
+    errs = {n: oracle.rel_frobenius(got[n], ref[n]) for n in OUTS if n != "dlogits"}
+    print("tile_boundary_counts", mode, {n: f"{v:.2e}" for n, v in errs.items()}, flush=True)
+    for n, v in errs.items():
+        assert v <= TOL[mode], (n, v)
+    # k = 1: the weights are 1 and dlogits is exactly zero
+    assert not np.any(got["dlogits"])
+    for n in ("dwg", "dwu", "dwd"):
+        assert not np.any(got[n][TILE_COUNTS.index(0)]), n
