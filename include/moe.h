@@ -152,11 +152,11 @@ moe_status moe_bwd(const moe_desc* d, const void* dy, const void* x,
  * Arithmetic: bf16 MFMA with fp32 accumulation. The contractions over H (forward) and over the
  * tokens (dw_router) are split into slices whose fp32 partial sums are added in a fixed order; the
  * backward multiplies a bf16 copy of dlogits, and dx is read, added to in fp32 and rounded once.
- * No atomics: results are bitwise reproducible.
- * Modes: BF16, MXFP8 and FP8_BWD (bf16 I/O; the projection itself stays bf16). MOE_MODE_FP32
- * returns MOE_ERR_UNSUPPORTED_MODE. Every tensor pointer needs 16-byte alignment except dlogits
- * (4 bytes); ws needs 256. The workspace sizes come from moe_query_router_sizes (host-only); its
- * contents need not be preserved. */
+ * In MOE_MODE_FP32 (the test mode) x, w_router, dx and dw_router are fp32 and every output is a
+ * plain fp32 sum in a fixed order. No atomics: results are bitwise reproducible.
+ * Modes: all four (MXFP8 and FP8_BWD take bf16 I/O; the projection itself stays bf16). Every
+ * tensor pointer needs 16-byte alignment except dlogits (4 bytes); ws needs 256. The workspace
+ * sizes come from moe_query_router_sizes (host-only); its contents need not be preserved. */
 moe_status moe_query_router_sizes(const moe_desc* d, size_t* fwd_ws, size_t* bwd_ws);
 moe_status moe_router_fwd(const moe_desc* d, const void* x, const void* w_router, float* logits,
                           void* ws, size_t ws_bytes, void* stream);

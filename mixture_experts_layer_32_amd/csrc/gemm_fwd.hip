@@ -192,6 +192,64 @@ hipError_t launch_combine(const void* src, const int* pair_pos, void* out, int64
   return hipSuccess;
 }
 
+// Router projection in the fp32 test mode: plain fp32 sums, one thread per output, in a fixed order
+// (performance is not the point of this mode; the bf16 engine has the MFMA form).
+//   logits[t][e]  = sum_h x[t][h] W_r[e][h]
+//   dW_r[e][h]    = sum_t dlogits[t][e] x[t][h]
+//   dx[t][h]     += sum_e dlogits[t][e] W_r[e][h]
+__global__ __launch_bounds__(256) void k_router_fwd_f32(RouterParams p) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= p.T * p.E) return;
+  const int64_t t = i / p.E, e = i - t * p.E;
+  const float* x = static_cast<const float*>(p.x) + t * p.H;
+  const float* w = static_cast<const float*>(p.wr) + e * p.H;
+  float v = 0.f;
+  for (int h = 0; h < p.H; ++h) v = fmaf(x[h], w[h], v);
+  p.logits[i] = v;
+}
+
+__global__ __launch_bounds__(256) void k_router_dw_f32(RouterParams p) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)p.E * p.H) return;
+  const int64_t e = i / p.H, h = i - e * p.H;
+  const float* x = static_cast<const float*>(p.x);
+  float v = 0.f;
+  for (int64_t t = 0; t < p.T; ++t) v = fmaf(p.dlogits[t * p.E + e], x[t * p.H + h], v);
+  static_cast<float*>(p.dwr)[i] = v;
+}
+
+__global__ __launch_bounds__(256) void k_router_dx_f32(RouterParams p) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= p.T * p.H) return;
+  const int64_t t = i / p.H, h = i - t * p.H;
+  const float* w = static_cast<const float*>(p.wr);
+  float v = 0.f;
+  for (int e = 0; e < p.E; ++e) v = fmaf(p.dlogits[t * p.E + e], w[(int64_t)e * p.H + h], v);
+  static_cast<float*>(p.dx)[i] += v;
+}
+
+hipError_t launch_router_fwd_f32(const RouterParams& p, hipStream_t s) {
+  prof_mark_begin("router_fwd_f32", s);
+  k_router_fwd_f32<<<(unsigned)((p.T * p.E + 255) / 256), 256, 0, s>>>(p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  prof_mark_end(s);
+  return hipSuccess;
+}
+
+hipError_t launch_router_bwd_f32(const RouterParams& p, hipStream_t s) {
+  hipError_t err;
+  prof_mark_begin("router_dw_f32", s);
+  k_router_dw_f32<<<(unsigned)(((int64_t)p.E * p.H + 255) / 256), 256, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+  prof_mark_begin("router_dx_f32", s);
+  k_router_dx_f32<<<(unsigned)((p.T * p.H + 255) / 256), 256, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(s);
+  return hipSuccess;
+}
+
 template hipError_t launch_forward_gemms<float>(const FwdParams&, int, hipStream_t);
 template hipError_t launch_combine<float>(const void*, const int*, void*, int64_t, int, int, hipStream_t);
 template hipError_t launch_combine<bf16>(const void*, const int*, void*, int64_t, int, int, hipStream_t);

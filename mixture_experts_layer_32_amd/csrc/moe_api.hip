@@ -554,23 +554,18 @@ RouterLayout router_layout(const moe_desc& d) {
     off = align256(off + bytes);
     return at;
   };
-  R.fwd_part = take((size_t)R.Sf * T * R.Ep * 4);
-  R.fwd_total = off;
+  const bool f32 = d.mode == MOE_MODE_FP32;   // the fp32 test mode's kernels need no workspace
+  R.fwd_part = take(f32 ? 0 : (size_t)R.Sf * T * R.Ep * 4);
+  R.fwd_total = std::max<size_t>(off, 256);
   off = 0;
-  R.bwd_zero = take(kZeroBytes);
-  R.bwd_dlb = take((size_t)T * R.Ep * 2);
-  R.bwd_part = take((size_t)R.Sb * E * H * 4);
-  R.bwd_total = off;
+  R.bwd_zero = take(f32 ? 0 : kZeroBytes);
+  R.bwd_dlb = take(f32 ? 0 : (size_t)T * R.Ep * 2);
+  R.bwd_part = take(f32 ? 0 : (size_t)R.Sb * E * H * 4);
+  R.bwd_total = std::max<size_t>(off, 256);
   return R;
 }
 
-moe_status router_checks(const moe_desc* d) {
-  moe_status st = validate(d);
-  if (st != MOE_OK) return st;
-  if (d->mode == MOE_MODE_FP32)
-    return fail(MOE_ERR_UNSUPPORTED_MODE, "the router projection runs in the bf16-I/O modes (BF16, MXFP8, FP8_BWD)");
-  return MOE_OK;
-}
+moe_status router_checks(const moe_desc* d) { return validate(d); }
 }  // namespace
 
 moe_status moe_query_router_sizes(const moe_desc* d, size_t* fwd_ws, size_t* bwd_ws) {
@@ -603,7 +598,8 @@ moe_status moe_router_fwd(const moe_desc* d, const void* x, const void* w_router
   p.Ep = R.Ep;
   p.S = R.Sf;
   p.kc = R.kcf;
-  hipError_t e = launch_router_fwd_bf16(p, persistent_grid(1), static_cast<hipStream_t>(stream));
+  hipError_t e = d->mode == MOE_MODE_FP32 ? launch_router_fwd_f32(p, static_cast<hipStream_t>(stream))
+                                          : launch_router_fwd_bf16(p, persistent_grid(1), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "router forward launch");
   return MOE_OK;
 }
@@ -635,7 +631,8 @@ moe_status moe_router_bwd(const moe_desc* d, const void* x, const void* w_router
   p.Ep = R.Ep;
   p.S = R.Sb;
   p.kc = R.kcb;
-  hipError_t e = launch_router_bwd_bf16(p, persistent_grid(1), static_cast<hipStream_t>(stream));
+  hipError_t e = d->mode == MOE_MODE_FP32 ? launch_router_bwd_f32(p, static_cast<hipStream_t>(stream))
+                                          : launch_router_bwd_bf16(p, persistent_grid(1), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "router backward launch");
   return MOE_OK;
 }

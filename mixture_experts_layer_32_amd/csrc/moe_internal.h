@@ -152,7 +152,7 @@ hipError_t launch_backward_gemms_bf16(const BwdParams& p, int grid, hipStream_t 
 // router's part of dx. The GEMMs with a long contraction split it S ways (kc elements per split)
 // and add the fp32 partial sums in a fixed order.
 struct RouterParams {
-  const void* x;         // [T, H] bf16
+  const void* x;         // [T, H] bf16 (fp32 in the fp32 test mode, likewise wr, dx, dwr)
   const void* wr;        // [E, H] bf16
   float* part;           // split partial sums: [S][T][Ep] (forward), [S][E][H] (backward)
   float* logits;         // [T, E] fp32 (forward output)
@@ -166,6 +166,8 @@ struct RouterParams {
 };
 hipError_t launch_router_fwd_bf16(const RouterParams& p, int grid, hipStream_t s);
 hipError_t launch_router_bwd_bf16(const RouterParams& p, int grid, hipStream_t s);
+hipError_t launch_router_fwd_f32(const RouterParams& p, hipStream_t s);   // fp32 test mode
+hipError_t launch_router_bwd_f32(const RouterParams& p, hipStream_t s);
 
 hipError_t launch_forward_gemms_mx(const FwdParams& p, int grid, hipStream_t s);
 hipError_t launch_backward_gemms_mx(const BwdParams& p, int grid, hipStream_t s);

@@ -8,6 +8,7 @@ Bar (relative Frobenius error per output, as for the layer):
  * dW_r and the router's part of dx <= 1e-2 (the bf16 bar): the backward multiplies a bf16 copy of
    dlogits (relative rounding 2^-9) and rounds its outputs to bf16 once.
  * Bitwise reproducible across calls.
+ * The fp32 test mode (fp32 tensors, plain fp32 sums): every output <= 1e-5.
 The composition test runs x, W_r -> router -> layer -> router backward on the GPU and compares the
 total dx and dW_r with the oracle's chain on the same fp32 logits (so that both route alike).
 """
@@ -24,6 +25,7 @@ pytestmark = pytest.mark.gpu
 
 TOL_LOGITS = 1e-5
 TOL_BWD = 1e-2
+TOL_FP32 = 1e-5   # the fp32 test mode: plain fp32 sums of at most 16384 terms
 
 
 def sparse_dlogits(T, E, k, seed):
@@ -44,21 +46,26 @@ CASES = [
     ("single_token", dict(T=1, H=256, E=8, k=2), "bf16"),
     ("wide_H4096", dict(T=130, H=4096, E=64, k=4), "bf16"),
     ("mxfp8_mode", dict(T=300, H=512, E=40, k=3), "mxfp8"),
+    ("fp32_mode", dict(T=300, H=256, E=40, k=3), "fp32"),
+    ("fp32_mode_E200", dict(T=517, H=512, E=200, k=4), "fp32"),
 ]
 
 
-def router_inputs(T, H, E, k, seed):
-    cfg, L = inputs.custom_layer(T=T, H=H, F=128, E=E, k=k, seed=seed)
+def router_inputs(T, H, E, k, seed, dtype="bf16"):
+    cfg, L = inputs.custom_layer(T=T, H=H, F=128, E=E, k=k, seed=seed, dtype=dtype)
     return cfg, L["x"], inputs.router_weight(cfg)
 
 
 @pytest.mark.parametrize("name,shape,mode", CASES, ids=[c[0] for c in CASES])
 def test_router_parity(name, shape, mode):
     print(f"case router {name} mode={mode} {shape}", flush=True)
-    cfg, x, wr = router_inputs(**shape, seed=51)
+    f32 = mode == "fp32"
+    dt = torch.float32 if f32 else torch.bfloat16
+    tol_bwd = TOL_FP32 if f32 else TOL_BWD
+    cfg, x, wr = router_inputs(**shape, seed=51, dtype="fp32" if f32 else "bf16")
     T, H, E = cfg.T, cfg.H, cfg.E
     layer = MoELayer(T, H, 128, E, cfg.k, mode)
-    xd, wrd = to_dev(x, torch.bfloat16), to_dev(wr, torch.bfloat16)
+    xd, wrd = to_dev(x, dt), to_dev(wr, dt)
     lg = layer.router_forward(xd, wrd)
     torch.cuda.synchronize()
     ref = oracle.router_forward(x, wr)
@@ -68,21 +75,22 @@ def test_router_parity(name, shape, mode):
             else sparse_dlogits(T, E, cfg.k, 53)
         dwr_ref, dxr_ref = oracle.router_backward(dl, x, wr)
         dx0 = np.zeros((T, H), np.float32)
-        dx = to_dev(dx0, torch.bfloat16)
+        dx = to_dev(dx0, dt)
         dwr = layer.router_backward(xd, wrd, to_dev(dl, torch.float32), dx)
         torch.cuda.synchronize()
         e_dw = oracle.rel_frobenius(dwr.float().cpu().numpy(), dwr_ref)
         e_dx = oracle.rel_frobenius(dx.float().cpu().numpy(), dxr_ref)
         # dx is accumulated into: start from a nonzero dx of the same scale
-        dx1 = inputs.round_to_bf16((np.random.default_rng(54).standard_normal((T, H)) *
-                                    np.sqrt(np.mean(dxr_ref ** 2))).astype(np.float32))
-        dxt = to_dev(dx1, torch.bfloat16)
+        dx1 = (np.random.default_rng(54).standard_normal((T, H)) * np.sqrt(np.mean(dxr_ref ** 2))).astype(np.float32)
+        if not f32:
+            dx1 = inputs.round_to_bf16(dx1)
+        dxt = to_dev(dx1, dt)
         layer.router_backward(xd, wrd, to_dev(dl, torch.float32), dxt)
         torch.cuda.synchronize()
         e_acc = oracle.rel_frobenius(dxt.float().cpu().numpy(), dx1.astype(np.float64) + dxr_ref)
         print(name, "dense" if dense else "sparse", f"logits {e_fwd:.2e} dW_r {e_dw:.2e} dx {e_dx:.2e} "
               f"dx accumulated {e_acc:.2e}", flush=True)
-        assert e_dw <= TOL_BWD and e_dx <= TOL_BWD and e_acc <= TOL_BWD
+        assert e_dw <= tol_bwd and e_dx <= tol_bwd and e_acc <= tol_bwd
     assert e_fwd <= TOL_LOGITS
 
 
