@@ -40,6 +40,13 @@ __device__ __forceinline__ void block_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+// p[i] for a wave-uniform i, through the scalar unit. Read through the constant address space, the
+// data is known not to change during the kernel, so the compiler emits s_load_dword: the value counts
+// against lgkmcnt, not vmcnt. A plain load here becomes a vector load whose compiler-inserted
+// vmcnt waits also wait for the direct-to-LDS tile loads in flight, which the compiler does not see.
+__device__ __forceinline__ int ld_uniform(const int* p, int i) {
+  return ((const __attribute__((address_space(4))) int*)p)[i];
+}
 
 // Dynamic tile scheduler of the persistent kernels. The tile list is cut into 8 contiguous ranges,
 // one per XCD (workgroups are dispatched to the XCDs round-robin: workgroup b runs on XCD b % 8), so

@@ -139,12 +139,12 @@ struct GatherRows {
   __device__ __forceinline__ void prefetch(int kt) {
     const int r0 = seg0 + kt * KTILE + wave_id() * KPW;
 #pragma unroll
-    for (int i = 0; i < KPW; ++i) tok[i] = ptok[min(r0 + i, seg_end - 1)];
+    for (int i = 0; i < KPW; ++i) tok[i] = ld_uniform(ptok, min(r0 + i, seg_end - 1));
   }
   __device__ __forceinline__ void prologue_prefetch(int kt) {
     const int r0 = seg0 + kt * KTILE + wave_id() * KPW;
 #pragma unroll
-    for (int i = 0; i < KPW; ++i) tokp[kt][i] = ptok[min(r0 + i, seg_end - 1)];
+    for (int i = 0; i < KPW; ++i) tokp[kt][i] = ld_uniform(ptok, min(r0 + i, seg_end - 1));
   }
   __device__ __forceinline__ const char* row(int kt, int j) const {
     const int hi = (threadIdx.x & 63) >> 5;
