@@ -439,19 +439,22 @@ __global__ __launch_bounds__(NTHR8, 1) void k_bwd_dh_bf16(BwdParams p) {
     const int fq = nt * TILE + 64 * wn;
     const int qend = p.qoff[e + 1];
     const int colq = p.qoff[e] + (r0 - p.offsets[e]) + 128 * wm;
+    // a/b of the lane's 4 rows of a 32-row block. Row s of block i+1 is loaded into the registers of
+    // row s of block i as soon as those are unpacked, so the next block's loads run during the rest
+    // of this block (no extra registers).
+    uint4 araw[4], braw[4];
+    auto load_ab = [&](int i, int s) {
+      const int rl = (lane >> 3) + 8 * s, c0 = (lane & 7) * 8;
+      const int r = r0 + 128 * wm + 32 * i + rl, f = fq + c0;
+      const bf16* abr = ab + (size_t)min(r, seg_end - 1) * 2 * F + min(f, F - 8);
+      araw[s] = ld16(abr);
+      braw[s] = ld16(abr + F);
+    };
+#pragma unroll
+    for (int s = 0; s < 4; ++s) load_ab(0, s);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       stage_rows(slab, acc, i, lane);
-      // the 4 rows of this lane: gather every a/b vector first so that the loads overlap
-      uint4 araw[4], braw[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int rl = (lane >> 3) + 8 * s, c0 = (lane & 7) * 8;
-        const int r = r0 + 128 * wm + 32 * i + rl, f = fq + c0;
-        const bf16* abr = ab + (size_t)min(r, seg_end - 1) * 2 * F + min(f, F - 8);
-        araw[s] = ld16(abr);
-        braw[s] = ld16(abr + F);
-      }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int rl = (lane >> 3) + 8 * s, c0 = (lane & 7) * 8;
@@ -478,6 +481,7 @@ __global__ __launch_bounds__(NTHR8, 1) void k_bwd_dh_bf16(BwdParams p) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) da[e] = db[e] = 0.f;
         }
+        if (i < 3) load_ab(i + 1, s);
         constexpr int LD = Stage<2>::LD;
         *reinterpret_cast<float4*>(slab + rl * LD + c0) = make_float4(da[0], da[1], da[2], da[3]);
         *reinterpret_cast<float4*>(slab + rl * LD + c0 + 4) = make_float4(da[4], da[5], da[6], da[7]);

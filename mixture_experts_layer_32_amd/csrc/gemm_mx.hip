@@ -319,18 +319,22 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_dh_mx(BwdParams p) {
     const int colq = p.qoff[e] + (r0 - p.offsets[e]) + 128 * wm;
     const int64_t qs = p.qc / 32;
     // one 32-row block of the quadrant; i is a compile-time constant so that acc stays in registers
+    // a/b of the lane's 8 rows of a 32-row block. Row s of block i+1 is loaded into the registers of
+    // row s of block i as soon as those are unpacked, so the next block's loads run during the rest
+    // of this block (no extra registers).
+    uint4 araw[8], braw[8];
+    auto load_ab = [&](int i, int s) {
+      const int rl = (lane >> 4) + 4 * s, c0 = (lane & 15) * 8;
+      const int r = r0 + 128 * wm + 32 * i + rl, f = fq + c0;
+      const bf16* abr = ab + (size_t)min(r, seg_end - 1) * 2 * F + min(f, F - 8);
+      araw[s] = ld16(abr);
+      braw[s] = ld16(abr + F);
+    };
+#pragma unroll
+    for (int s = 0; s < 8; ++s) load_ab(0, s);
     auto block = [&](auto I) {
       constexpr int i = decltype(I)::value;
       stage_rows(slab, acc, i, lane);
-      uint4 araw[8], braw[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int rl = (lane >> 4) + 4 * s, c0 = (lane & 15) * 8;
-        const int r = r0 + 128 * wm + 32 * i + rl, f = fq + c0;
-        const bf16* abr = ab + (size_t)min(r, seg_end - 1) * 2 * F + min(f, F - 8);
-        araw[s] = ld16(abr);
-        braw[s] = ld16(abr + F);
-      }
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const int rl = (lane >> 4) + 4 * s, c0 = (lane & 15) * 8;
@@ -355,6 +359,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_dh_mx(BwdParams p) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) da[e] = db[e] = 0.f;
         }
+        if (i < 3) load_ab(i + 1, s);
         const int sda = mx_exponent(mx_amax_x4(da));
         const int sdb = mx_exponent(mx_amax_x4(db));
         if (ok) {
