@@ -183,15 +183,18 @@ __global__ __launch_bounds__(256) void k_quant_both(const bf16* __restrict__ in,
   column_pass128(tile, qc + orow * ldo + col0 + r0, scc + orow * (ldo / 32) + (col0 + r0) / 32);
 }
 
-// Grid (qc / 128, H / 64). Window w covers columns 128w .. 128w+127 of [H][qc], inside one
-// expert's padded segment (segments are multiples of 128 columns). (128 x 128 tiles measured 10-15 %
-// slower here.)
+// Grid (qc / 128, GT_SPLIT). Window w covers columns 128w .. 128w+127 of [H][qc], inside one
+// expert's padded segment (segments are multiples of 128 columns). A block finds its expert and the
+// window's 128 token indices once, then walks the 64-column tiles h0 = 64 (blockIdx.y + GT_SPLIT j)
+// of H: the next tile's rows load while the current one is quantised. (128 x 128 tiles measured
+// 10-15 % slower here.)
+constexpr int GT_SPLIT = 4;
 __global__ __launch_bounds__(256) void k_gather_t_quant(const bf16* __restrict__ x, const int* __restrict__ ptok,
                                                         const int* __restrict__ offsets, const int* __restrict__ qoff,
                                                         int El, int H, int64_t qc, uint8_t* __restrict__ q,
                                                         uint8_t* __restrict__ sc) {
   __shared__ __attribute__((aligned(16))) bf16 tile[128][64];
-  const int q0 = blockIdx.x * 128, h0 = blockIdx.y * 64;
+  const int q0 = blockIdx.x * 128;
   if (q0 >= qoff[El]) return;   // past the last expert's segment: nothing reads these columns
   int lo = 0, hi = El - 1;      // the expert whose segment holds q0: the last e with qoff[e] <= q0
   while (lo < hi) {
@@ -200,11 +203,33 @@ __global__ __launch_bounds__(256) void k_gather_t_quant(const bf16* __restrict__
     else hi = mid - 1;
   }
   const int base = offsets[lo] + (q0 - qoff[lo]), end = offsets[lo + 1];
-  uint4 raw[4];
-  load_tile(tile, [&](int row) { return base + row < end ? x + (size_t)ptok[base + row] * H + h0 : nullptr; }, raw);
-  __syncthreads();
-  const size_t orow = (size_t)h0 + (threadIdx.x & 63);
-  column_pass(tile, q + orow * qc + q0, sc + orow * (qc / 32) + q0 / 32);
+  // load i of this thread covers tile row (t >> 3) + 32 i, columns 8 (t & 7) .. +7
+  const bf16* src[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (threadIdx.x >> 3) + 32 * i;
+    src[i] = base + row < end ? x + (size_t)ptok[base + row] * H + (threadIdx.x & 7) * 8 : nullptr;
+  }
+  auto load = [&](int h0, uint4 (&raw)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw[i] = src[i] ? ld16(src[i] + h0) : make_uint4(0u, 0u, 0u, 0u);
+  };
+  uint4 raw[4], nxt[4];
+  int h0 = 64 * blockIdx.y;
+  if (h0 >= H) return;
+  load(h0, nxt);
+  for (; h0 < H; h0 += 64 * GT_SPLIT) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      raw[i] = nxt[i];
+      *reinterpret_cast<uint4*>(&tile[(threadIdx.x >> 3) + 32 * i][(threadIdx.x & 7) * 8]) = raw[i];
+    }
+    __syncthreads();
+    if (h0 + 64 * GT_SPLIT < H) load(h0 + 64 * GT_SPLIT, nxt);
+    const size_t orow = (size_t)h0 + (threadIdx.x & 63);
+    column_pass(tile, q + orow * qc + q0, sc + orow * (qc / 32) + q0 / 32);
+    __syncthreads();   // the tile is overwritten next
+  }
 }
 
 }  // namespace
@@ -245,8 +270,8 @@ hipError_t launch_quant_both(const void* in, uint8_t* qr, uint8_t* sr, uint8_t* 
 hipError_t launch_gather_t_quant(const void* x, const int* ptok, const int* offsets, const int* qoff, int El, int H,
                                  int64_t qc, uint8_t* q, uint8_t* sc, const char* name, hipStream_t s) {
   prof_mark_begin(name, s);
-  k_gather_t_quant<<<dim3((unsigned)(qc / 128), H / 64), 256, 0, s>>>(static_cast<const bf16*>(x), ptok, offsets,
-                                                                     qoff, El, H, qc, q, sc);
+  k_gather_t_quant<<<dim3((unsigned)(qc / 128), GT_SPLIT), 256, 0, s>>>(static_cast<const bf16*>(x), ptok, offsets,
+                                                                        qoff, El, H, qc, q, sc);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   prof_mark_end(s);
