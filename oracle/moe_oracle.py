@@ -36,15 +36,19 @@ Parity status: every function here is pinned by tests that do not go through thi
  * central finite differences.
 No function is "parity unpinned".
 
-MX precision modes (mode="mxfp8": both passes; mode="fp8_bwd": backward only). Every GEMM operand
-is replaced by its MXFP8 round trip (oracle/mx.py) along that GEMM's contraction axis:
+Quantised precision modes (mode="mxfp8": MXFP8 in both passes; mode="fp8_bwd": MXFP8 in the
+backward only; mode="fp8": blockwise FP8 in both passes). Every GEMM operand is replaced by its
+round trip (oracle/mx.py) along that GEMM's contraction axis:
     gate/up        x rows and W_gate, W_up along H
     down           (w * h) along F; W_down along F
     dH             dY rows along H; W_down along H
     down wgrad     dY and (w * h) along the expert's pairs, in the stable pair order, in blocks of 32
-                   (the last block zero-padded)
+                   (fp8: 128) from the expert's first pair (the last block zero-padded)
     gate/up wgrad  da, db and x along the expert's pairs
     dgrad x        da, db along F; W_gate, W_up along F
+MXFP8 blocks are 32 elements along the contraction axis. Blockwise FP8 uses blocks of 128 for the
+activation operands and one scale per 128 x 128 tile of each expert weight matrix, whichever axis
+the GEMM contracts, with a power-of-two scale that never saturates (oracle/mx.py).
 Routing, softmax, SwiGLU, the router gradient and the combines stay exact.
 Reading: the routing weight enters before the down projection (o' = W_down (w h)). Without
 quantisation that is the same sum as weighting the expert output. In MX modes it fixes which
@@ -148,17 +152,36 @@ def expert_forward(xr, wg_e, wu_e, wd_e):
     return a, b, h, o
 
 
-def _qz(on, v, axis):
-    return mx.mx_quantize(v, axis) if on else _f64(v)
+def _fwd_quant(mode):
+    """Operand quantiser kind of the forward GEMMs in `mode`: None (exact), "mx" or "blk"."""
+    return {"mxfp8": "mx", "fp8": "blk"}.get(mode)
+
+
+def _bwd_quant(mode):
+    """Operand quantiser kind of the backward GEMMs in `mode`."""
+    return {"mxfp8": "mx", "fp8_bwd": "mx", "fp8": "blk"}.get(mode)
+
+
+def _qz(kind, v, axis, weight=False):
+    """GEMM operand v quantised along `axis`, its contraction axis. kind None leaves it exact; "mx" is
+    MXFP8 (blocks of 32); "blk" is blockwise FP8: blocks of 128 along the axis for an activation
+    operand, 128 x 128 tiles for an expert's weight matrix (the same in both orientations)."""
+    if not kind:
+        return _f64(v)
+    if kind == "blk":
+        return mx.fp8_tile_quantize(v) if weight else mx.fp8_block_quantize(v, axis)
+    return mx.mx_quantize(v, axis)
 
 
 def expert_forward_q(xr, wr, wg_e, wu_e, wd_e, quant):
-    """One expert with optional MXFP8 operands (quant=True). Returns a, b, h and o' = W_down (w h)."""
+    """One expert with quantised operands (quant: "mx" or "blk"; True means "mx"). Returns a, b, h
+    and o' = W_down (w h)."""
+    quant = "mx" if quant is True else quant
     xq = _qz(quant, xr, 1)
-    a = xq @ _qz(quant, wg_e, 1).T
-    b = xq @ _qz(quant, wu_e, 1).T
+    a = xq @ _qz(quant, wg_e, 1, weight=True).T
+    b = xq @ _qz(quant, wu_e, 1, weight=True).T
     h = silu(a) * b
-    o = _qz(quant, wr[:, None] * h, 1) @ _qz(quant, wd_e, 1).T
+    o = _qz(quant, wr[:, None] * h, 1) @ _qz(quant, wd_e, 1, weight=True).T
     return a, b, h, o
 
 
@@ -186,8 +209,8 @@ def forward(x, logits, wg, wu, wd, k, e0=0, e_local=None, mode=None):
         pairs, toks, wr = _expert_rows(r, i)
         if pairs.size == 0:
             continue
-        if mode == "mxfp8":
-            _, _, _, o = expert_forward_q(x[toks], wr, wg[i], wu[i], wd[i], True)
+        if _fwd_quant(mode):
+            _, _, _, o = expert_forward_q(x[toks], wr, wg[i], wu[i], wd[i], _fwd_quant(mode))
             y[toks] += o                    # the routing weight is inside o'
         else:
             _, _, _, o = expert_forward(x[toks], wg[i], wu[i], wd[i])
@@ -238,27 +261,28 @@ def backward(dy, x, logits, wg, wu, wd, k, e0=0, e_local=None, mode=None):
 
 def _expert_backward(xe, dye, wr, wg_i, wu_i, wd_i, mode):
     """(g, dWg, dWu, dWd, dx rows) of one expert's pairs, in the stable pair order."""
-    qb = mode in ("mxfp8", "fp8_bwd")
-    if mode == "mxfp8":
-        a, b, h, _ = expert_forward_q(xe, wr, wg_i, wu_i, wd_i, True)
+    qb = _bwd_quant(mode)
+    if _fwd_quant(mode):
+        a, b, h, _ = expert_forward_q(xe, wr, wg_i, wu_i, wd_i, _fwd_quant(mode))
     else:
         a, b, h, _ = expert_forward(xe, wg_i, wu_i, wd_i)
-    u = _qz(qb, dye, 1) @ _qz(qb, wd_i, 0)                 # contraction over H
+    u = _qz(qb, dye, 1) @ _qz(qb, wd_i, 0, weight=True)    # contraction over H
     g = np.sum(u * h, axis=1)
     dh = wr[:, None] * u
     da = dh * b * dsilu(a)
     db = dh * silu(a)
     hw = wr[:, None] * h
     if qb:                                                  # contraction over the pairs
-        dwd = _qz(True, dye, 0).T @ _qz(True, hw, 0)
-        xq = _qz(True, xe, 0)
-        dwg = _qz(True, da, 0).T @ xq
-        dwu = _qz(True, db, 0).T @ xq
+        dwd = _qz(qb, dye, 0).T @ _qz(qb, hw, 0)
+        xq = _qz(qb, xe, 0)
+        dwg = _qz(qb, da, 0).T @ xq
+        dwu = _qz(qb, db, 0).T @ xq
     else:
         dwd = (wr[:, None] * dye).T @ h
         dwg = da.T @ xe
         dwu = db.T @ xe
-    dxe = _qz(qb, da, 1) @ _qz(qb, wg_i, 0) + _qz(qb, db, 1) @ _qz(qb, wu_i, 0)   # contraction over F
+    dxe = (_qz(qb, da, 1) @ _qz(qb, wg_i, 0, weight=True)
+           + _qz(qb, db, 1) @ _qz(qb, wu_i, 0, weight=True))                # contraction over F
     return g, dwg, dwu, dwd, dxe
 
 
@@ -312,7 +336,7 @@ def token_rows(tokens, dy, x, logits, wg, wu, wd, k, e0=0, e_local=None, mode=No
     y = np.zeros((n, H))
     dx = np.zeros((n, H))
     g = np.zeros((n, k))
-    qb = mode in ("mxfp8", "fp8_bwd")
+    qb, qf = _bwd_quant(mode), _fwd_quant(mode)
     for q, t in enumerate(tokens):
         for j in range(k):
             e = int(idx[q, j])
@@ -320,18 +344,19 @@ def token_rows(tokens, dy, x, logits, wg, wu, wd, k, e0=0, e_local=None, mode=No
                 continue
             i = e - e0
             wr = np.array([w[q, j]])
-            if mode == "mxfp8":
-                a, b, h, o = expert_forward_q(x[t:t + 1], wr, wg[i], wu[i], wd[i], True)
+            if qf:
+                a, b, h, o = expert_forward_q(x[t:t + 1], wr, wg[i], wu[i], wd[i], qf)
                 y[q] += o[0]
             else:
                 a, b, h, o = expert_forward(x[t:t + 1], wg[i], wu[i], wd[i])
                 y[q] += w[q, j] * o[0]
-            u = _qz(qb, dy[t:t + 1], 1) @ _qz(qb, wd[i], 0)
+            u = _qz(qb, dy[t:t + 1], 1) @ _qz(qb, wd[i], 0, weight=True)
             g[q, j] = np.sum(u * h)
             dh = w[q, j] * u
             da = dh * b * dsilu(a)
             db = dh * silu(a)
-            dx[q] += (_qz(qb, da, 1) @ _qz(qb, wg[i], 0) + _qz(qb, db, 1) @ _qz(qb, wu[i], 0))[0]
+            dx[q] += (_qz(qb, da, 1) @ _qz(qb, wg[i], 0, weight=True)
+                      + _qz(qb, db, 1) @ _qz(qb, wu[i], 0, weight=True))[0]
     rr = dict(w=w, idx=idx)
     return dict(y=y, dx=dx, dlogits=router_grad(rr, g, lg.shape[1]), idx=idx, w=w)
 

@@ -14,6 +14,17 @@ microscaling one:
 
 Quantisation only replaces GEMM operands (quantise, then dequantise in float64). Every other step
 stays exact.
+
+Blockwise FP8 (the "fp8" mode). The same pages list a blockwise-scaled FP8 mode for Hopper and give
+no block sizes. The reading here is the usual one for FP8 training of this kind of layer, with the
+scale restricted to a power of two (an e8m0 byte), which is what the gfx950 scaled MFMA consumes:
+ * activation operands: one scale per 128 consecutive elements along the GEMM's contraction axis
+   (1 x 128 along a row, or 128 x 1 down an expert's pairs for the weight gradients);
+ * weights: one scale per 128 x 128 tile of each expert's matrix, so that both orientations of a
+   weight share every scale;
+ * the scale is the smallest power of two 2^s with amax <= 448 * 2^s (s clamped to [-127, 127],
+   s = -127 for an all-zero block), so no element saturates;
+ * elements are E4M3 of v / 2^s, rounded to nearest with ties to even.
 """
 from __future__ import annotations
 
@@ -46,21 +57,27 @@ def block_scale_exponent(amax):
     return np.where(amax == 0, -127, s).astype(np.int64)
 
 
-def mx_quantize(v, axis=-1, return_parts=False):
-    """MXFP8 round trip of v along `axis` in blocks of 32.
+def ceil_scale_exponent(amax):
+    """Blockwise FP8 scale exponent: the smallest s with amax <= 448 * 2^s, clamped to [-127, 127];
+    -127 if amax == 0."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, ex = np.frexp(amax)
+    s = ex - 1 - E4M3_EMAX                          # floor(log2 amax) - 8: amax / 2^s lies in [256, 512)
+    s = s + (amax > np.ldexp(E4M3_MAX, s))          # past 448 * 2^s: the next power of two
+    s = np.clip(s, -127, 127)
+    return np.where(amax == 0, -127, s).astype(np.int64)
 
-    A last block shorter than 32 is padded with zeros. Returns the dequantised float64 array,
-    plus (elements, scale exponents) if return_parts.
-    """
+
+def _quantize_blocks(v, axis, block, scale_exponent, return_parts):
     v = np.asarray(v, dtype=np.float64)
     x = np.moveaxis(v, axis, -1)
     n = x.shape[-1]
-    nb = -(-n // BLOCK)
-    pad = nb * BLOCK - n
+    nb = -(-n // block)
+    pad = nb * block - n
     if pad:
         x = np.concatenate([x, np.zeros(x.shape[:-1] + (pad,))], axis=-1)
-    blocks = x.reshape(x.shape[:-1] + (nb, BLOCK))
-    s = block_scale_exponent(np.max(np.abs(blocks), axis=-1))
+    blocks = x.reshape(x.shape[:-1] + (nb, block))
+    s = scale_exponent(np.max(np.abs(blocks), axis=-1))
     scale = np.ldexp(1.0, s)[..., None]
     elems = e4m3_round(blocks / scale)
     deq = (elems * scale).reshape(x.shape)[..., :n]
@@ -68,6 +85,42 @@ def mx_quantize(v, axis=-1, return_parts=False):
     if return_parts:
         return out, np.moveaxis(elems.reshape(x.shape)[..., :n], -1, axis), s
     return out
+
+
+def mx_quantize(v, axis=-1, return_parts=False):
+    """MXFP8 round trip of v along `axis` in blocks of 32.
+
+    A last block shorter than 32 is padded with zeros. Returns the dequantised float64 array,
+    plus (elements, scale exponents) if return_parts.
+    """
+    return _quantize_blocks(v, axis, BLOCK, block_scale_exponent, return_parts)
+
+
+FP8_BLOCK = 128
+
+
+def fp8_block_quantize(v, axis=-1, return_parts=False):
+    """Blockwise FP8 round trip of an activation operand along `axis`, in blocks of 128 (the last
+    one zero-padded), with the scale rule of ceil_scale_exponent."""
+    return _quantize_blocks(v, axis, FP8_BLOCK, ceil_scale_exponent, return_parts)
+
+
+def fp8_tile_quantize(w, return_parts=False):
+    """Blockwise FP8 round trip of a 2-D weight in 128 x 128 tiles, one scale per tile (edge tiles
+    are zero-padded). Returns the dequantised array, plus (elements, scale exponents per tile)."""
+    w = np.asarray(w, dtype=np.float64)
+    R, C = w.shape
+    nr, nc = -(-R // FP8_BLOCK), -(-C // FP8_BLOCK)
+    pad = np.zeros((nr * FP8_BLOCK, nc * FP8_BLOCK))
+    pad[:R, :C] = w
+    tiles = pad.reshape(nr, FP8_BLOCK, nc, FP8_BLOCK)
+    s = ceil_scale_exponent(np.max(np.abs(tiles), axis=(1, 3)))
+    scale = np.ldexp(1.0, s)[:, None, :, None]
+    elems = e4m3_round(tiles / scale)
+    deq = (elems * scale).reshape(pad.shape)[:R, :C]
+    if return_parts:
+        return deq, elems.reshape(pad.shape)[:R, :C], s
+    return deq
 
 
 def e4m3_table():

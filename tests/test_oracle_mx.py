@@ -255,10 +255,10 @@ def test_planted_wrong_axis_is_caught(monkeypatch):
     ref = _brute_mx(x, dy, lg, wg, wu, wd, k, False, True)
     orig = oracle.moe_oracle._qz
 
-    def wrong(on, v, axis):
+    def wrong(on, v, axis, **kw):
         if on and np.ndim(v) == 2 and np.shape(v) == wd[0].shape and axis == 0:
             axis = 1
-        return orig(on, v, axis)
+        return orig(on, v, axis, **kw)
     monkeypatch.setattr(oracle.moe_oracle, "_qz", wrong)
     gr, _ = oracle.backward(dy, x, lg, wg, wu, wd, k, mode="fp8_bwd")
     assert not np.allclose(gr["dx"], ref[1], rtol=1e-9, atol=1e-9)
