@@ -43,7 +43,7 @@ def kernel_peak(name, mode):
     """Dense MFMA peak (TFLOP/s) of the arithmetic a GEMM kernel runs in."""
     if mode == "fp32":
         return PEAK_TFLOPS["fp32"]
-    if mode == "mxfp8" or (mode == "fp8_bwd" and name not in FWD_GEMMS):
+    if mode in ("mxfp8", "fp8") or (mode == "fp8_bwd" and name not in FWD_GEMMS):
         return PEAK_TFLOPS["fp8"]
     return PEAK_TFLOPS["bf16"]
 
@@ -171,7 +171,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="qwen3_30b_a3b")
-    ap.add_argument("--mode", default=None, help="fp32, bf16, mxfp8 or fp8_bwd (default: the workload's)")
+    ap.add_argument("--mode", default=None, help="fp32, bf16, mxfp8, fp8_bwd or fp8 (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain 1 GiB device copy before the timed steps (reference for HBM counters)")
@@ -287,7 +287,7 @@ def main():
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
         "full_layer_2f_b_ms": round(2 * fwd_ms + bwd_ms, 4),
         "pct_mfma_peak": round(100 * ideal_ms / ms_step, 2),
-        "mfma_peak_basis": {"mxfp8": "fp8 5033.2 TFLOP/s", "fp8_bwd": "bf16 forward, fp8 backward GEMMs",
+        "mfma_peak_basis": {"mxfp8": "fp8 5033.2 TFLOP/s", "fp8": "fp8 5033.2 TFLOP/s", "fp8_bwd": "bf16 forward, fp8 backward GEMMs",
                             "fp32": "fp32 157.3 TFLOP/s"}.get(mode, "bf16 2516.6 TFLOP/s"),
         "ms_per_step_with_kernel_events": round(ms_step_prof, 4),
         "kernels": per_kernel, "roofline": roof,

@@ -71,12 +71,24 @@ extern "C" {
  *                        dy, w*h, da, db, x [the expert's pairs in sorted order, blocks of 32
  *                        from the expert's first pair, the last block zero-padded]
  *            Routing, softmax, SwiGLU, the router gradient and the combines stay fp32.
- *   FP8_BWD  the BF16 forward; the backward GEMMs quantised as in MXFP8. */
+ *   FP8_BWD  the BF16 forward; the backward GEMMs quantised as in MXFP8.
+ *   FP8      blockwise-scaled FP8 in both passes (the pages list it without block sizes). The
+ *            same operands and axes as MXFP8, on the same scaled fp8 MFMA, with larger blocks and
+ *            a scale that never saturates:
+ *              activation operands (x, dy, w*h, da, db): one scale per 128 consecutive elements
+ *                along the contraction axis (for the weight gradients, 128 pairs from the expert's
+ *                first pair, the last block zero-padded);
+ *              weights: one scale per 128 x 128 tile of each expert's matrix, the same for both
+ *                orientations;
+ *              scale 2^s with s the smallest integer such that amax <= 448 * 2^s, clamped to
+ *                [-127, 127] (-127 for an all-zero block); elements e4m3 of v / 2^s, rounded to
+ *                nearest even. */
 typedef enum {
   MOE_MODE_FP32 = 0,
   MOE_MODE_BF16 = 1,
   MOE_MODE_MXFP8 = 2,
-  MOE_MODE_FP8_BWD = 3
+  MOE_MODE_FP8_BWD = 3,
+  MOE_MODE_FP8 = 4
 } moe_mode;
 
 typedef enum {
@@ -199,6 +211,21 @@ moe_status moe_saved_layout(const moe_desc* d, moe_saved_offsets* out);
  * elsewhere (nothing is enqueued on error). */
 moe_status moe_mx_quantize(const void* in, int64_t rows, int64_t cols, int axis, uint8_t* q,
                            uint8_t* scales, void* stream);
+
+/* Blockwise FP8 quantisation of one bf16 matrix in [rows, cols] (row-major) with the rules of
+ * MOE_MODE_FP8: the kernels that mode uses on x, dy and the weights, exposed so that they can be
+ * checked alone. Scales keep the MXFP8 layout, one e8m0 byte per 32 elements along the blocked
+ * axis, each block's scale repeated over its 32-element groups.
+ *   weight = 0: an activation operand, blocks of 128 along each row. q [rows, cols] e4m3 bytes,
+ *               scales [rows, cols/32]; qt and scales_t are unused (may be null). cols % 128 == 0.
+ *   weight = 1: a weight matrix, one scale per 128 x 128 tile. q [rows, cols] and
+ *               scales [rows, cols/32] hold the row orientation; qt [cols, rows] and
+ *               scales_t [cols, rows/32] the transposed one, with the same scales.
+ *               rows % 128 == 0, cols % 128 == 0.
+ * in, q and qt need 16-byte alignment, the scale arrays 4-byte alignment; rows*cols < 2^34.
+ * Errors as elsewhere (nothing is enqueued on error). */
+moe_status moe_fp8_block_quantize(const void* in, int64_t rows, int64_t cols, int weight, uint8_t* q,
+                                  uint8_t* scales, uint8_t* qt, uint8_t* scales_t, void* stream);
 
 /* Static description of a status code. */
 const char* moe_status_string(moe_status s);

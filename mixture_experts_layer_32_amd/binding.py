@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "moe.h")
 
-MODES = {"fp32": 0, "bf16": 1, "mxfp8": 2, "fp8_bwd": 3}
+MODES = {"fp32": 0, "bf16": 1, "mxfp8": 2, "fp8_bwd": 3, "fp8": 4}
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED_SHAPE",
           3: "MOE_ERR_UNSUPPORTED_MODE", 4: "MOE_ERR_WORKSPACE_TOO_SMALL", 5: "MOE_ERR_HIP"}
 
@@ -73,6 +73,7 @@ def lib():
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_version.restype = ctypes.c_char_p
         L.moe_mx_quantize.argtypes = [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, _P, _P, _P]
+        L.moe_fp8_block_quantize.argtypes = [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, _P, _P, _P, _P, _P]
         L.moe_query_router_sizes.argtypes = [_D, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
         L.moe_router_fwd.argtypes = [_D, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_router_bwd.argtypes = [_D, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
@@ -80,6 +81,7 @@ def lib():
         L.moe_profile_kernel.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
                                          ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]
         for n in ("moe_query_sizes", "moe_route", "moe_fwd", "moe_bwd", "moe_saved_layout", "moe_mx_quantize",
+                  "moe_fp8_block_quantize",
                   "moe_query_router_sizes", "moe_router_fwd", "moe_router_bwd", "moe_profile_enable",
                   "moe_profile_disable", "moe_profile_collect", "moe_profile_kernel"):
             getattr(L, n).restype = st
@@ -160,6 +162,11 @@ def moe_router_bwd(desc, x, w_router, dlogits, dx, dw_router, ws, ws_bytes, stre
 
 def moe_mx_quantize(x, rows, cols, axis, q, scales, stream=None):
     _check(lib().moe_mx_quantize(ptr(x), rows, cols, axis, ptr(q), ptr(scales), _stream(stream)))
+
+
+def moe_fp8_block_quantize(x, rows, cols, weight, q, scales, qt=None, scales_t=None, stream=None):
+    _check(lib().moe_fp8_block_quantize(ptr(x), rows, cols, int(weight), ptr(q), ptr(scales), ptr(qt), ptr(scales_t),
+                                        _stream(stream)))
 
 
 def profile_enable(max_launches=4096):

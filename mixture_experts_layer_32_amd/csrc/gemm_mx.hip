@@ -173,9 +173,131 @@ __device__ __forceinline__ void mainloop_mx(f32x16 (&acc)[4][4], char* smem, con
   block_sync();
 }
 
+// Blockwise FP8 form of store_transposed_mx: the staged column c (one lane per column) is written
+// with the exponent sx(c) of its whole block of pairs, found beforehand.
+template <class Dst, class SDst, class Sx>
+__device__ __forceinline__ void store_transposed_fixed(const float* slab, int lane, int ncol, Dst dst, SDst sdst,
+                                                       Sx sx) {
+  for (int c = lane; c < ncol; c += 64) {
+    const int s = sx(c);
+    const float sm = mx_inv_scale(s);
+    unsigned w[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const float* col = slab + 4 * g * SLD + c;
+      w[g] = mx_cvt4(mx_sat(col[0] * sm), mx_sat(col[SLD] * sm), mx_sat(col[2 * SLD] * sm), mx_sat(col[3 * SLD] * sm));
+    }
+    uint8_t* o = dst(c);
+    if (o) {
+      st16(o, make_uint4(w[0], w[1], w[2], w[3]));
+      st16(o + 16, make_uint4(w[4], w[5], w[6], w[7]));
+      *sdst(c) = (uint8_t)(s + 127);
+    }
+  }
+}
+
+// largest magnitude of staged column c over the 32 staged rows (8 reads in flight at a time: fully
+// unrolled, the compiler issued all of them at once and spilled the values)
+__device__ __forceinline__ float column_amax(const float* slab, int c) {
+  float m = 0.f;
+#pragma unroll 8
+  for (int r = 0; r < 32; ++r) m = fmaxf(m, fabsf(slab[r * SLD + c]));
+  return m;
+}
+
 // ------------------------------------------------------------------------------------------------
 // forward: [a | b] = gather(x) [W_gate; W_up]^T; epilogue writes ab (bf16), hw = w silu(a) b as fp8
 // along F (the down GEMM's A operand) and as fp8 along the pairs (the down weight gradient's B)
+// Blockwise FP8 epilogue of the gate/up GEMM. w h is quantised along F in blocks of 128 columns,
+// which the two waves wn = 0, 1 of a row share (64 columns each), and along the pairs in blocks of
+// the wave's 128 rows. Pass 1 computes h, writes a and b, each row's maximum over the wave's 64
+// columns (into LDS past the four staging slabs, for the partner wave) and each column's maximum
+// over the 128 rows. After a barrier, pass 2 recomputes h (the same operations on the same values)
+// and writes both fp8 copies with those scales.
+__device__ __forceinline__ void epilogue_gateup_blk(const FwdParams& p, const f32x16 (&acc)[4][4], char* smem,
+                                                    float* slab, const float (&wrow)[4], int lane, int w, int wm,
+                                                    int r0, int seg_end, int f0, int qend, int colq, int64_t qs) {
+  bf16* __restrict__ ab = static_cast<bf16*>(p.ab);
+  const int F = p.F;
+  float* rmax = reinterpret_cast<float*>(smem) + 4 * SLAB;   // [4 waves][128 rows]
+  auto hrow = [&](int i, int s, float (&hv)[8], bool write_ab) {
+    const int rl = (lane >> 3) + 8 * s, c0 = (lane & 7) * 8;
+    const float wt = __shfl(wrow[i], rl);
+    const int r = r0 + 128 * wm + 32 * i + rl;
+    if (r < seg_end) {
+      float av[8], bv[8];
+      read8(slab, rl, c0, av);
+      read8(slab, rl, 64 + c0, bv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv[e] = wt * (av[e] * sigmoidf_(av[e]) * bv[e]);
+      if (write_ab) {
+        bf16* abr = ab + (size_t)r * 2 * F + f0 + c0;
+        st16_nt(abr, pack8(av));
+        st16_nt(abr + F, pack8(bv));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv[e] = 0.f;
+    }
+  };
+  auto put_slab = [&](int s, const float (&hv)[8]) {
+    const int rl = (lane >> 3) + 8 * s, c0 = (lane & 7) * 8;
+    *reinterpret_cast<float4*>(slab + rl * SLD + c0) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+    *reinterpret_cast<float4*>(slab + rl * SLD + c0 + 4) = make_float4(hv[4], hv[5], hv[6], hv[7]);
+  };
+  float cmax = 0.f;   // column `lane` of the wave's 64, over its 128 rows
+  auto pass1 = [&](auto I) {
+    constexpr int i = decltype(I)::value;
+    stage_rows(slab, acc, i, lane);
+#pragma unroll 1
+    for (int s = 0; s < 4; ++s) {
+      float hv[8];
+      hrow(i, s, hv, true);
+      float m = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(hv[e]));
+      m = fmaxf(m, __shfl_xor(m, 1));
+      m = fmaxf(m, __shfl_xor(m, 2));
+      m = fmaxf(m, __shfl_xor(m, 4));
+      if ((lane & 7) == 0) rmax[w * 128 + 32 * i + (lane >> 3) + 8 * s] = m;
+      put_slab(s, hv);
+    }
+    cmax = fmaxf(cmax, column_amax(slab, lane));
+  };
+  pass1(std::integral_constant<int, 0>{});
+  pass1(std::integral_constant<int, 1>{});
+  pass1(std::integral_constant<int, 2>{});
+  pass1(std::integral_constant<int, 3>{});
+  block_sync();   // the partner wave's row maxima
+  const int scol = fp8b_exponent(cmax);
+  auto pass2 = [&](auto I) {
+    constexpr int i = decltype(I)::value;
+    stage_rows(slab, acc, i, lane);
+#pragma unroll 1
+    for (int s = 0; s < 4; ++s) {
+      float hv[8];
+      hrow(i, s, hv, false);
+      const int rl = (lane >> 3) + 8 * s, c0 = (lane & 7) * 8;
+      const int r = r0 + 128 * wm + 32 * i + rl;
+      const int sx = fp8b_exponent(fmaxf(rmax[w * 128 + 32 * i + rl], rmax[(w ^ 1) * 128 + 32 * i + rl]));
+      if (r < seg_end) {
+        *reinterpret_cast<uint2*>(p.hwq + (size_t)r * F + f0 + c0) = mx_encode8(hv, sx);
+        if ((lane & 3) == 0) p.hws[(size_t)r * (F / 32) + (f0 + c0) / 32] = (uint8_t)(sx + 127);
+      }
+      put_slab(s, hv);
+    }
+    const int colb = colq + 32 * i;
+    store_transposed_fixed(
+        slab, lane, 64, [&](int c) { return colb < qend ? p.hwtq + (size_t)(f0 + c) * p.qc + colb : nullptr; },
+        [&](int c) { return p.hwts + (size_t)(f0 + c) * qs + colb / 32; }, [&](int) { return scol; });
+  };
+  pass2(std::integral_constant<int, 0>{});
+  pass2(std::integral_constant<int, 1>{});
+  pass2(std::integral_constant<int, 2>{});
+  pass2(std::integral_constant<int, 3>{});
+}
+
+template <bool BLK>
 __global__ __launch_bounds__(NTHR, 1) void k_gateup_mx(FwdParams p) {
   MX_SMEM
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
@@ -212,6 +334,10 @@ __global__ __launch_bounds__(NTHR, 1) void k_gateup_mx(FwdParams p) {
     const int qend = p.qoff[e + 1];
     const int colq = p.qoff[e] + (r0 - p.offsets[e]) + 128 * wm;
     const int64_t qs = p.qc / 32;
+    if constexpr (BLK) {
+      epilogue_gateup_blk(p, acc, smem, slab, wrow, lane, w, wm, r0, seg_end, f0, qend, colq, qs);
+      continue;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       stage_rows(slab, acc, i, lane);
@@ -284,6 +410,113 @@ __global__ __launch_bounds__(NTHR, 1) void k_down_mx(FwdParams p) {
 
 // backward: u = gather(dY) W_down[e] (contraction over H, B = W_down[e]^T quantised along H);
 // epilogue writes g partials, and da, db as fp8 along F (dgrad A) and along the pairs (wgrad A)
+// Blockwise FP8 epilogue of the dH GEMM. A row's 128 columns of da (and of db) in this wave are one
+// block along F (16 lanes: four shuffles give its amax), so the row copies are written in pass 1
+// together with the g partials. Along the pairs, a column's block is the wave's 128 rows: pass 1 also
+// takes each column's maximum, and pass 2 recomputes da and db (the same operations on the same
+// values) and writes the transposed copies with those scales.
+__device__ __forceinline__ void epilogue_dh_blk(const BwdParams& p, const f32x16 (&acc)[4][4], float* slab,
+                                                float* slab2, const float (&wrow)[4], int lane, int wm, int wn,
+                                                int nt, int r0, int seg_end, int fq, int qend, int colq, int64_t qs) {
+  const bf16* __restrict__ ab = static_cast<const bf16*>(p.ab);
+  const int F = p.F, f2s = 2 * F / 32;
+  auto dswiglu = [&](int i, int s, float (&da)[8], float (&db)[8], float& gsum) {
+    const int rl = (lane >> 4) + 4 * s, c0 = (lane & 15) * 8;
+    const float wt = __shfl(wrow[i], rl);
+    const int r = r0 + 128 * wm + 32 * i + rl, f = fq + c0;
+    // branch-free: rows past the segment and columns past F read a clamped row and are then zeroed
+    // (a branch around the array writes made the compiler keep da and db in scratch memory)
+    const bool ok = r < seg_end && f < F;
+    float u[8], av[8], bv[8];
+    read8(slab, rl, c0, u);
+    const bf16* abr = ab + (size_t)min(r, seg_end - 1) * 2 * F + min(f, F - 8);
+    unpack8(ld16(abr), av);
+    unpack8(ld16(abr + F), bv);
+    gsum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float sg = sigmoidf_(av[e]), si = av[e] * sg;
+      gsum += u[e] * (si * bv[e]);
+      const float dh = wt * u[e];
+      da[e] = ok ? dh * bv[e] * sg * (1.0f + av[e] * (1.0f - sg)) : 0.f;
+      db[e] = ok ? dh * si : 0.f;
+    }
+    gsum = ok ? gsum : 0.f;
+  };
+  auto put_slabs = [&](int s, const float (&da)[8], const float (&db)[8]) {
+    const int rl = (lane >> 4) + 4 * s, c0 = (lane & 15) * 8;
+    *reinterpret_cast<float4*>(slab + rl * SLD + c0) = make_float4(da[0], da[1], da[2], da[3]);
+    *reinterpret_cast<float4*>(slab + rl * SLD + c0 + 4) = make_float4(da[4], da[5], da[6], da[7]);
+    *reinterpret_cast<float4*>(slab2 + rl * SLD + c0) = make_float4(db[0], db[1], db[2], db[3]);
+    *reinterpret_cast<float4*>(slab2 + rl * SLD + c0 + 4) = make_float4(db[4], db[5], db[6], db[7]);
+  };
+  // columns lane and lane + 64 of the da and db slabs, over the wave's 128 rows
+  float cm[4] = {0.f, 0.f, 0.f, 0.f};
+  auto pass1 = [&](auto I) {
+    constexpr int i = decltype(I)::value;
+    stage_rows(slab, acc, i, lane);
+#pragma unroll 1
+    for (int s = 0; s < 8; ++s) {
+      float da[8], db[8], gsum;
+      dswiglu(i, s, da, db, gsum);
+      const int rl = (lane >> 4) + 4 * s, c0 = (lane & 15) * 8;
+      const int r = r0 + 128 * wm + 32 * i + rl, f = fq + c0;
+      const int sda = fp8b_exponent(mx_amax_x16(da));
+      const int sdb = fp8b_exponent(mx_amax_x16(db));
+      if (r < seg_end && f < F) {
+        uint8_t* qr = p.dabq + (size_t)r * 2 * F + f;
+        *reinterpret_cast<uint2*>(qr) = mx_encode8(da, sda);
+        *reinterpret_cast<uint2*>(qr + F) = mx_encode8(db, sdb);
+        if ((lane & 3) == 0) {
+          uint8_t* sr = p.dabs + (size_t)r * f2s;
+          sr[f / 32] = (uint8_t)(sda + 127);
+          sr[(F + f) / 32] = (uint8_t)(sdb + 127);
+        }
+      }
+      put_slabs(s, da, db);
+      gsum += __shfl_xor(gsum, 1);
+      gsum += __shfl_xor(gsum, 2);
+      gsum += __shfl_xor(gsum, 4);
+      gsum += __shfl_xor(gsum, 8);
+      if (r < seg_end && (lane & 15) == 0) p.gpart[(size_t)(nt * 2 + wn) * p.rows + r] = gsum;
+    }
+    cm[0] = fmaxf(cm[0], column_amax(slab, lane));
+    cm[1] = fmaxf(cm[1], column_amax(slab, lane + 64));
+    cm[2] = fmaxf(cm[2], column_amax(slab2, lane));
+    cm[3] = fmaxf(cm[3], column_amax(slab2, lane + 64));
+  };
+  pass1(std::integral_constant<int, 0>{});
+  pass1(std::integral_constant<int, 1>{});
+  pass1(std::integral_constant<int, 2>{});
+  pass1(std::integral_constant<int, 3>{});
+  const int sc[4] = {fp8b_exponent(cm[0]), fp8b_exponent(cm[1]), fp8b_exponent(cm[2]), fp8b_exponent(cm[3])};
+  auto pass2 = [&](auto I) {
+    constexpr int i = decltype(I)::value;
+    stage_rows(slab, acc, i, lane);
+#pragma unroll 1
+    for (int s = 0; s < 8; ++s) {
+      float da[8], db[8], gsum;
+      dswiglu(i, s, da, db, gsum);
+      put_slabs(s, da, db);
+    }
+    const int colb = colq + 32 * i;
+    store_transposed_fixed(
+        slab, lane, 128,
+        [&](int c) { return colb < qend && fq + c < F ? p.dabtq + (size_t)(fq + c) * p.qc + colb : nullptr; },
+        [&](int c) { return p.dabts + (size_t)(fq + c) * qs + colb / 32; }, [&](int c) { return c < 64 ? sc[0] : sc[1]; });
+    store_transposed_fixed(
+        slab2, lane, 128,
+        [&](int c) { return colb < qend && fq + c < F ? p.dabtq + (size_t)(F + fq + c) * p.qc + colb : nullptr; },
+        [&](int c) { return p.dabts + (size_t)(F + fq + c) * qs + colb / 32; },
+        [&](int c) { return c < 64 ? sc[2] : sc[3]; });
+  };
+  pass2(std::integral_constant<int, 0>{});
+  pass2(std::integral_constant<int, 1>{});
+  pass2(std::integral_constant<int, 2>{});
+  pass2(std::integral_constant<int, 3>{});
+}
+
+template <bool BLK>
 __global__ __launch_bounds__(NTHR, 1) void k_bwd_dh_mx(BwdParams p) {
   MX_SMEM
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
@@ -318,6 +551,10 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_dh_mx(BwdParams p) {
     const int qend = p.qoff[e + 1];
     const int colq = p.qoff[e] + (r0 - p.offsets[e]) + 128 * wm;
     const int64_t qs = p.qc / 32;
+    if constexpr (BLK) {
+      epilogue_dh_blk(p, acc, slab, slab2, wrow, lane, wm, wn, nt, r0, seg_end, fq, qend, colq, qs);
+      continue;
+    }
     // one 32-row block of the quadrant; i is a compile-time constant so that acc stays in registers
     // a/b of the lane's 8 rows of a 32-row block. Row s of block i+1 is loaded into the registers of
     // row s of block i as soon as those are unpacked, so the next block's loads run during the rest
@@ -500,7 +737,10 @@ __global__ __launch_bounds__(NTHR, 1) void k_wgrad_gateup_mx(BwdParams p) {
 hipError_t launch_forward_gemms_mx(const FwdParams& p, int grid, hipStream_t s) {
   hipError_t err;
   prof_mark_begin("gemm_gateup_swiglu", s);
-  k_gateup_mx<<<grid, NTHR, 0, s>>>(p);
+  if (p.blk)
+    k_gateup_mx<true><<<grid, NTHR, 0, s>>>(p);
+  else
+    k_gateup_mx<false><<<grid, NTHR, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   prof_mark_end(s);
   prof_mark_begin("gemm_down", s);
@@ -513,7 +753,10 @@ hipError_t launch_forward_gemms_mx(const FwdParams& p, int grid, hipStream_t s) 
 hipError_t launch_backward_gemms_mx(const BwdParams& p, int grid, hipStream_t s) {
   hipError_t err;
   prof_mark_begin("gemm_bwd_dh_dswiglu", s);
-  k_bwd_dh_mx<<<grid, NTHR, 0, s>>>(p);
+  if (p.blk)
+    k_bwd_dh_mx<true><<<grid, NTHR, 0, s>>>(p);
+  else
+    k_bwd_dh_mx<false><<<grid, NTHR, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   prof_mark_end(s);
   prof_mark_begin("gemm_wgrad_down", s);

@@ -24,7 +24,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 Layout make_layout(const moe_desc& d) {
   Layout L{};
-  L.mx = d.mode == MOE_MODE_MXFP8 || d.mode == MOE_MODE_FP8_BWD;
+  L.mx = d.mode == MOE_MODE_MXFP8 || d.mode == MOE_MODE_FP8_BWD || d.mode == MOE_MODE_FP8;
   L.rows = d.T * (int64_t)d.topk;
   L.nblk_route = (int)((d.T + kRouteTokens - 1) / kRouteTokens);
   L.mtile_cap = (int)(L.rows / kBM) + d.E_local + 1;
@@ -40,7 +40,8 @@ Layout make_layout(const moe_desc& d) {
   L.qc = d.mode == MOE_MODE_FP32 ? 0 : (L.rows + (int64_t)L.qpad * d.E_local + 127) / 128 * 128;
   const size_t rows = (size_t)L.rows, El = (size_t)d.E_local, T = (size_t)d.T, H = (size_t)d.H, F = (size_t)d.F;
   const size_t qc = (size_t)L.qc;
-  const bool mxf = d.mode == MOE_MODE_MXFP8, f8b = d.mode == MOE_MODE_FP8_BWD;
+  // fp8 forward (MXFP8 and blockwise FP8 share every buffer; only the scales' grouping differs)
+  const bool mxf = d.mode == MOE_MODE_MXFP8 || d.mode == MOE_MODE_FP8, f8b = d.mode == MOE_MODE_FP8_BWD;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -129,7 +130,7 @@ static moe_status validate(const moe_desc* d) {
   if (d->T * (int64_t)d->topk >= (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "T*topk must be < 2^31");
   if (d->mode != MOE_MODE_FP32 && d->mode != MOE_MODE_BF16 && d->mode != MOE_MODE_MXFP8 &&
-      d->mode != MOE_MODE_FP8_BWD)
+      d->mode != MOE_MODE_FP8_BWD && d->mode != MOE_MODE_FP8)
     return fail(MOE_ERR_UNSUPPORTED_MODE, "unknown mode");
   return MOE_OK;
 }
@@ -218,7 +219,7 @@ using namespace moe;
 extern "C" {
 
 const char* moe_version(void) {
-  return "libmoe 0.2 (gfx950; fp32/bf16/mxfp8/fp8_bwd; persistent grouped GEMM, 256x256 tiles)";
+  return "libmoe 0.2 (gfx950; fp32/bf16/mxfp8/fp8_bwd/fp8; persistent grouped GEMM, 256x256 tiles)";
 }
 
 const char* moe_status_string(moe_status s) {
@@ -258,7 +259,7 @@ moe_status moe_saved_layout(const moe_desc* d, moe_saved_offsets* out) {
   out->offsets = L.offsets;
   out->perm = L.perm;
   out->pair_pos = L.pair_pos;
-  const bool mxf = d->mode == MOE_MODE_MXFP8;
+  const bool mxf = d->mode == MOE_MODE_MXFP8 || d->mode == MOE_MODE_FP8;
   out->qoff = L.mx ? L.qoff : 0;
   out->qcols = L.mx ? (size_t)L.qc : 0;
   out->hwt = L.mx ? L.hwt : 0;
@@ -371,21 +372,23 @@ moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits, const 
       return hip_fail(e, "forward GEMM launch");
     if ((e = launch_combine<bf16>(fp.o, fp.pair_pos, y, d->T, d->topk, d->H, s)) != hipSuccess)
       return hip_fail(e, "combine launch");
-  } else if (d->mode == MOE_MODE_MXFP8) {
-    // every forward GEMM operand as MXFP8 along its contraction axis; hw and its transposed copy
-    // are quantised in the gate/up epilogue. Each weight is read once and quantised along both
-    // axes: the other orientation is the backward's operand and goes to `saved`.
+  } else if (d->mode == MOE_MODE_MXFP8 || d->mode == MOE_MODE_FP8) {
+    // every forward GEMM operand as MXFP8 (blockwise FP8) along its contraction axis; hw and its
+    // transposed copy are quantised in the gate/up epilogue. Each weight is read once and quantised
+    // along both axes: the other orientation is the backward's operand and goes to `saved`.
     auto u8 = [&](size_t o) { return reinterpret_cast<uint8_t*>(w + o); };
     auto s8 = [&](size_t o) { return reinterpret_cast<uint8_t*>(sv + o); };
     const int El = d->E_local, H = d->H, F = d->F;
-    if ((e = launch_quant_rows(x, u8(L.xq), u8(L.xs), d->T * d->H, "mx_quant_x", s)) != hipSuccess ||
+    const bool blk = d->mode == MOE_MODE_FP8;
+    if ((e = launch_quant_rows(x, u8(L.xq), u8(L.xs), d->T * d->H, "mx_quant_x", s, blk)) != hipSuccess ||
         (e = launch_quant_both(w_gate, u8(L.wgq), u8(L.wgs), s8(L.sv_wgutq), s8(L.sv_wguts), El, F, H, 2 * F, 0,
-                               "mx_quant_w_gate", s)) != hipSuccess ||
+                               "mx_quant_w_gate", s, blk)) != hipSuccess ||
         (e = launch_quant_both(w_up, u8(L.wuq), u8(L.wus), s8(L.sv_wgutq), s8(L.sv_wguts), El, F, H, 2 * F, F,
-                               "mx_quant_w_up", s)) != hipSuccess ||
+                               "mx_quant_w_up", s, blk)) != hipSuccess ||
         (e = launch_quant_both(w_down, u8(L.wdq), u8(L.wds), s8(L.sv_wdtq), s8(L.sv_wdts), El, H, F, H, 0,
-                               "mx_quant_w_down", s)) != hipSuccess)
+                               "mx_quant_w_down", s, blk)) != hipSuccess)
       return hip_fail(e, "quantise launch");
+    fp.blk = blk;
     fp.xq = u8(L.xq);
     fp.xs = u8(L.xs);
     fp.wgq = u8(L.wgq);
@@ -480,7 +483,7 @@ moe_status moe_bwd(const moe_desc* d, const void* dy, const void* x, const void*
     // FP8_BWD quantises it here.
     auto u8 = [&](size_t o) { return reinterpret_cast<uint8_t*>(w + o); };
     const int El = d->E_local, H = d->H, F = d->F;
-    const bool f8b = d->mode == MOE_MODE_FP8_BWD;
+    const bool f8b = d->mode == MOE_MODE_FP8_BWD, blk = d->mode == MOE_MODE_FP8;
     const uint8_t* wdtq = f8b ? u8(L.wdtq) : reinterpret_cast<const uint8_t*>(sv + L.sv_wdtq);
     const uint8_t* wdts = f8b ? u8(L.wdts) : reinterpret_cast<const uint8_t*>(sv + L.sv_wdts);
     const uint8_t* wgutq = f8b ? u8(L.wgutq) : reinterpret_cast<const uint8_t*>(sv + L.sv_wgutq);
@@ -490,12 +493,13 @@ moe_status moe_bwd(const moe_desc* d, const void* dy, const void* x, const void*
          (e = launch_quant_cols(w_gate, u8(L.wgutq), u8(L.wguts), El, F, H, 2 * F, 0, "mx_quant_w_gate_t", s)) != hipSuccess ||
          (e = launch_quant_cols(w_up, u8(L.wgutq), u8(L.wguts), El, F, H, 2 * F, F, "mx_quant_w_up_t", s)) != hipSuccess))
       return hip_fail(e, "quantise launch");
-    if ((e = launch_quant_rows(dy, u8(L.dyq), u8(L.dys), d->T * d->H, "mx_quant_dy", s)) != hipSuccess ||
+    if ((e = launch_quant_rows(dy, u8(L.dyq), u8(L.dys), d->T * d->H, "mx_quant_dy", s, blk)) != hipSuccess ||
         (e = launch_gather_t_quant(dy, p.ptok, p.offsets, p.qoff, El, H, L.qc, u8(L.dytq), u8(L.dyts), "mx_quant_dy_t",
-                                   s)) != hipSuccess ||
+                                   s, blk)) != hipSuccess ||
         (e = launch_gather_t_quant(x, p.ptok, p.offsets, p.qoff, El, H, L.qc, u8(L.xtq), u8(L.xts), "mx_quant_x_t",
-                                   s)) != hipSuccess)
+                                   s, blk)) != hipSuccess)
       return hip_fail(e, "quantise launch");
+    p.blk = blk;
     p.dyq = u8(L.dyq);
     p.dys = u8(L.dys);
     p.wdtq = wdtq;
@@ -654,6 +658,32 @@ moe_status moe_mx_quantize(const void* in, int64_t rows, int64_t cols, int axis,
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = axis == 1 ? launch_quant_rows(in, q, scales, rows * cols, "mx_quant_rows", s)
                                  : launch_quant_cols(in, q, scales, 1, (int)rows, (int)cols, rows, 0, "mx_quant_cols", s);
+  if (e != hipSuccess) return hip_fail(e, "quantise launch");
+  return MOE_OK;
+}
+
+moe_status moe_fp8_block_quantize(const void* in, int64_t rows, int64_t cols, int weight, uint8_t* q,
+                                  uint8_t* scales, uint8_t* qt, uint8_t* scales_t, void* stream) {
+  g_last_error.clear();
+  moe_status st;
+  if ((st = check_ptrs({{in, "in"}, {q, "q"}}, 16)) != MOE_OK) return st;
+  if ((st = check_ptrs({{scales, "scales"}}, 4)) != MOE_OK) return st;
+  if (rows < 1 || cols < 1) return fail(MOE_ERR_INVALID_ARG, "rows and cols must be positive");
+  if (weight != 0 && weight != 1) return fail(MOE_ERR_INVALID_ARG, "weight must be 0 or 1");
+  if (weight == 1) {
+    if ((st = check_ptrs({{qt, "qt"}}, 16)) != MOE_OK) return st;
+    if ((st = check_ptrs({{scales_t, "scales_t"}}, 4)) != MOE_OK) return st;
+    if (rows % 128 != 0) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "rows must be a multiple of 128 (weight)");
+    if (rows / 128 > 65535) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "matrix too large for the weight form");
+  }
+  if (cols % 128 != 0) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "cols must be a multiple of 128");
+  if (rows * cols >= (int64_t(1) << 34)) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "rows*cols must be < 2^34");
+  if (cols > INT32_MAX || rows > INT32_MAX) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "matrix too large");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e =
+      weight == 0 ? launch_quant_rows(in, q, scales, rows * cols, "fp8b_quant_rows", s, true)
+                  : launch_quant_both(in, q, scales, qt, scales_t, 1, (int)rows, (int)cols, rows, 0, "fp8b_quant_weight",
+                                      s, true);
   if (e != hipSuccess) return hip_fail(e, "quantise launch");
   return MOE_OK;
 }

@@ -97,6 +97,7 @@ struct FwdParams {
   // MXFP8 operands: E4M3 bytes and e8m0 scales ([rows][K/32]), all K-major
   const uint8_t *xq, *xs, *wgq, *wgs, *wuq, *wus, *wdq, *wds;
   uint8_t *hwq, *hws, *hwtq, *hwts;
+  bool blk;            // blockwise FP8 scales instead of MXFP8 (fp8 engine only)
   int* sched;          // tile-scheduler counters (kSchedSlots slots), zero at launch
   int64_t T;
   int H, F, k, El;
@@ -139,6 +140,7 @@ struct BwdParams {
   // MXFP8 operands: E4M3 bytes and e8m0 scales ([rows][K/32]), all K-major
   const uint8_t *dyq, *dys, *wdtq, *wdts, *wgutq, *wguts, *dytq, *dyts, *xtq, *xts, *hwtq, *hwts;
   uint8_t *dabq, *dabs, *dabtq, *dabts;
+  bool blk;            // blockwise FP8 scales instead of MXFP8 (fp8 engine only)
   int* sched;          // tile-scheduler counters (kSchedSlots slots), zeroed before the GEMMs
   int64_t T, rows;
   int H, F, k, E, El, np;
@@ -171,13 +173,15 @@ hipError_t launch_router_bwd_f32(const RouterParams& p, hipStream_t s);
 
 hipError_t launch_forward_gemms_mx(const FwdParams& p, int grid, hipStream_t s);
 hipError_t launch_backward_gemms_mx(const BwdParams& p, int grid, hipStream_t s);
-hipError_t launch_quant_rows(const void* in, uint8_t* q, uint8_t* sc, int64_t n, const char* name, hipStream_t s);
+hipError_t launch_quant_rows(const void* in, uint8_t* q, uint8_t* sc, int64_t n, const char* name, hipStream_t s,
+                             bool blk = false);
 hipError_t launch_quant_cols(const void* in, uint8_t* q, uint8_t* sc, int B, int R, int C, int64_t ldo, int col0,
                              const char* name, hipStream_t s);
 hipError_t launch_quant_both(const void* in, uint8_t* qr, uint8_t* sr, uint8_t* qc, uint8_t* scc, int B, int R, int C,
-                             int64_t ldo, int col0, const char* name, hipStream_t s);
+                             int64_t ldo, int col0, const char* name, hipStream_t s, bool blk = false);
 hipError_t launch_gather_t_quant(const void* x, const int* ptok, const int* offsets, const int* qoff, int El, int H,
-                                 int64_t qc, uint8_t* q, uint8_t* sc, const char* name, hipStream_t s);
+                                 int64_t qc, uint8_t* q, uint8_t* sc, const char* name, hipStream_t s,
+                                 bool blk = false);
 
 int persistent_grid(int blocks_per_cu);
 

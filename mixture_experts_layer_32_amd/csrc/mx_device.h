@@ -40,6 +40,22 @@ __device__ __forceinline__ uint2 mx_encode8(const float (&v)[8], int s) {
                     mx_cvt4(mx_sat(v[4] * m), mx_sat(v[5] * m), mx_sat(v[6] * m), mx_sat(v[7] * m)));
 }
 
+// Blockwise FP8 (the FP8 mode; the same pages list a blockwise-scaled FP8 without block sizes). The
+// library reads it with power-of-two scales, the form the scaled MFMA consumes: the scale of a block
+// is the smallest 2^s with amax <= 448 * 2^s, s clamped to [-127, 127], so no element saturates.
+// With amax = m 2^e (m in [1, 2)), 448 2^(e-8) = 1.75 2^e: s = e - 8, plus one when m > 1.75, i.e.
+// when the fp32 mantissa field exceeds 0x600000. Zero and subnormal amax give s = -127.
+__device__ __forceinline__ int fp8b_exponent(float amax) {
+  const unsigned u = __float_as_uint(amax);
+  const int be = (int)((u >> 23) & 0xffu);
+  return max(be - 127 - 8 + ((u & 0x7fffffu) > 0x600000u ? 1 : 0), -127);
+}
+
+template <bool BLK>
+__device__ __forceinline__ int block_exponent(float amax) {
+  return BLK ? fp8b_exponent(amax) : mx_exponent(amax);
+}
+
 // Largest magnitude of a block of 32 held as 8 values by each of 4 consecutive lanes (lanes 4g..4g+3).
 // Every lane of the wave must execute it.
 __device__ __forceinline__ float mx_amax_x4(const float (&v)[8]) {
@@ -49,6 +65,20 @@ __device__ __forceinline__ float mx_amax_x4(const float (&v)[8]) {
   m = fmaxf(m, __shfl_xor(m, 1));
   m = fmaxf(m, __shfl_xor(m, 2));
   return m;
+}
+
+// Largest magnitude of a block of 128 held as 8 values by each of 16 consecutive lanes.
+// Every lane of the wave must execute it.
+__device__ __forceinline__ float mx_amax_x16(const float (&v)[8]) {
+  float m = mx_amax_x4(v);
+  m = fmaxf(m, __shfl_xor(m, 4));
+  m = fmaxf(m, __shfl_xor(m, 8));
+  return m;
+}
+
+template <bool BLK>
+__device__ __forceinline__ float block_amax(const float (&v)[8]) {
+  return BLK ? mx_amax_x16(v) : mx_amax_x4(v);
 }
 
 }  // namespace moe

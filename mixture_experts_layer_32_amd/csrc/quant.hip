@@ -16,6 +16,11 @@
 // The transposing kernels stage 128 x 64 tiles (k_quant_both: 128 x 128) in LDS, so that every
 // row segment they read or write is one or two whole 128-byte lines.
 // The quantised element and scale formulas are in mx_device.h.
+//
+// Blockwise FP8 (template flag BLK): k_quant_rows takes blocks of 128 along the row (16 lanes),
+// k_quant_both one scale per 128 x 128 tile for both orientations, and k_gather_t_quant blocks of
+// the 128 pairs of a window. The scale arrays keep the MXFP8 layout (one byte per 32 elements), with
+// each block's scale repeated over its 32-element groups, so the fp8 GEMMs read both forms alike.
 #include "moe_device.h"
 #include "moe_internal.h"
 #include "mx_device.h"
@@ -29,7 +34,8 @@ __device__ __forceinline__ void unpack8f(uint4 u, float (&v)[8]) {
   for (int e = 0; e < 8; ++e) v[e] = (float)b[e];
 }
 
-// n8 = elements / 8 (a multiple of 4: blocks never straddle a thread group)
+// n8 = elements / 8 (a multiple of 4, of 16 with BLK: blocks never straddle a thread group)
+template <bool BLK>
 __global__ __launch_bounds__(256) void k_quant_rows(const bf16* __restrict__ in, uint8_t* __restrict__ q,
                                                     uint8_t* __restrict__ sc, int64_t n8) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -40,7 +46,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const bf16* __restrict__ in,
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = 0.f;
   }
-  const int s = mx_exponent(mx_amax_x4(v));
+  const int s = block_exponent<BLK>(block_amax<BLK>(v));
   if (i < n8) {
     *reinterpret_cast<uint2*>(q + i * 8) = mx_encode8(v, s);
     if ((i & 3) == 0) sc[i >> 2] = (uint8_t)(s + 127);
@@ -50,8 +56,10 @@ __global__ __launch_bounds__(256) void k_quant_rows(const bf16* __restrict__ in,
 // Column pass shared by the transposing kernels: the block's LDS tile holds 128 source rows of 64
 // columns (bf16). Thread t quantises column t & 63 over rows 32 (t >> 6) .. +31 into 32 output
 // bytes at out_row + 32 (t >> 6) and one scale byte at sc_row + (t >> 6). The four threads of a
-// column write one whole 128-byte line.
-__device__ __forceinline__ void column_pass(const bf16 (*tile)[64], uint8_t* out_row, uint8_t* sc_row) {
+// column write one whole 128-byte line. With BLK the column's 128 rows are one block: the four
+// threads (one per wave) exchange their maxima through cmax [4][64] (a barrier every thread reaches).
+template <bool BLK>
+__device__ __forceinline__ void column_pass(const bf16 (*tile)[64], uint8_t* out_row, uint8_t* sc_row, float* cmax) {
   const int c = threadIdx.x & 63, blk = threadIdx.x >> 6;
   float v[32];
   float m = 0.f;
@@ -60,7 +68,12 @@ __device__ __forceinline__ void column_pass(const bf16 (*tile)[64], uint8_t* out
     v[r] = (float)tile[32 * blk + r][c];
     m = fmaxf(m, fabsf(v[r]));
   }
-  const int s = mx_exponent(m);
+  if constexpr (BLK) {
+    cmax[threadIdx.x] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(cmax[c], cmax[64 + c]), fmaxf(cmax[128 + c], cmax[192 + c]));
+  }
+  const int s = block_exponent<BLK>(m);
   const float sm = mx_inv_scale(s);
   unsigned w[8];
 #pragma unroll
@@ -97,13 +110,16 @@ __global__ __launch_bounds__(256) void k_quant_cols(const bf16* __restrict__ in,
   load_tile(tile, [&](int row) { return src + (size_t)row * C; }, raw);
   __syncthreads();
   const size_t orow = (size_t)b * C + c0 + (threadIdx.x & 63);
-  column_pass(tile, q + orow * ldo + col0 + r0, sc + orow * (ldo / 32) + (col0 + r0) / 32);
+  column_pass<false>(tile, q + orow * ldo + col0 + r0, sc + orow * (ldo / 32) + (col0 + r0) / 32, nullptr);
 }
 
 // Column pass on a 128 x 128 LDS tile: thread t quantises column t & 127 over the blocks of 32 rows
 // 2 (t >> 7) and 2 (t >> 7) + 1, into the 32-byte segments out_row + 32 blk and the scale bytes
-// sc_row[blk]. The two threads of a column write one whole 128-byte line.
-__device__ __forceinline__ void column_pass128(const bf16 (*tile)[128], uint8_t* out_row, uint8_t* sc_row) {
+// sc_row[blk]. The two threads of a column write one whole 128-byte line. With BLK every block takes
+// the tile's exponent s_tile.
+template <bool BLK>
+__device__ __forceinline__ void column_pass128(const bf16 (*tile)[128], uint8_t* out_row, uint8_t* sc_row,
+                                               int s_tile) {
   const int t = threadIdx.x, c = t & 127;
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
@@ -115,7 +131,7 @@ __device__ __forceinline__ void column_pass128(const bf16 (*tile)[128], uint8_t*
       v[r] = (float)tile[32 * blk + r][c];
       m = fmaxf(m, fabsf(v[r]));
     }
-    const int s = mx_exponent(m);
+    const int s = BLK ? s_tile : mx_exponent(m);
     const float sm = mx_inv_scale(s);
     unsigned w[8];
 #pragma unroll
@@ -142,7 +158,7 @@ __global__ __launch_bounds__(256) void k_quant_cols128(const bf16* __restrict__ 
   }
   __syncthreads();
   const size_t orow = (size_t)b * C + c0 + (t & 127);
-  column_pass128(tile, q + orow * ldo + col0 + r0, sc + orow * (ldo / 32) + (col0 + r0) / 32);
+  column_pass128<false>(tile, q + orow * ldo + col0 + r0, sc + orow * (ldo / 32) + (col0 + r0) / 32, 0);
 }
 
 // Both orientations of one weight tensor in one read: in [B][R][C] ->
@@ -154,6 +170,8 @@ __global__ __launch_bounds__(256) void k_quant_cols128(const bf16* __restrict__ 
 // the tile) and the column pass too (each thread quantises two blocks of 32 of one column). The
 // input is read once: non-temporal loads. The stores stay ordinary: each instruction writes less
 // than a whole line per row, and non-temporal partial-line stores ran 3.4x slower.
+// BLK: one exponent for the whole tile (its amax over the 4 waves), in both orientations.
+template <bool BLK>
 __global__ __launch_bounds__(256) void k_quant_both(const bf16* __restrict__ in, uint8_t* __restrict__ qr,
                                                     uint8_t* __restrict__ sr, uint8_t* __restrict__ qc,
                                                     uint8_t* __restrict__ scc, int R, int C, int64_t ldo, int col0) {
@@ -168,19 +186,36 @@ __global__ __launch_bounds__(256) void k_quant_both(const bf16* __restrict__ in,
     raw[i] = ld16_nt(src + (size_t)row * C + col8);
     *reinterpret_cast<uint4*>(&tile[row][col8]) = raw[i];
   }
+  int s_tile = 0;
+  if constexpr (BLK) {
+    __shared__ float wmax[4];
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float v[8];
+      unpack8f(raw[i], v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+    }
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) m = fmaxf(m, __shfl_xor(m, d));
+    if ((t & 63) == 0) wmax[t >> 6] = m;
+    __syncthreads();
+    s_tile = fp8b_exponent(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
+  }
   // row pass: the 4 lanes 4g..4g+3 hold one row's block of 32 along C
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     float v[8];
     unpack8f(raw[i], v);
-    const int s = mx_exponent(mx_amax_x4(v));
+    const int s = BLK ? s_tile : mx_exponent(mx_amax_x4(v));
     const size_t grow = (size_t)b * R + r0 + (t >> 4) + 16 * i;
     *reinterpret_cast<uint2*>(qr + grow * C + c0 + col8) = mx_encode8(v, s);
     if ((t & 3) == 0) sr[grow * (C / 32) + (c0 + col8) / 32] = (uint8_t)(s + 127);
   }
   __syncthreads();
   const size_t orow = (size_t)b * C + c0 + (t & 127);
-  column_pass128(tile, qc + orow * ldo + col0 + r0, scc + orow * (ldo / 32) + (col0 + r0) / 32);
+  column_pass128<BLK>(tile, qc + orow * ldo + col0 + r0, scc + orow * (ldo / 32) + (col0 + r0) / 32, s_tile);
 }
 
 // Grid (qc / 128, GT_SPLIT). Window w covers columns 128w .. 128w+127 of [H][qc], inside one
@@ -189,11 +224,13 @@ __global__ __launch_bounds__(256) void k_quant_both(const bf16* __restrict__ in,
 // of H: the next tile's rows load while the current one is quantised. (128 x 128 tiles measured
 // 10-15 % slower here.)
 constexpr int GT_SPLIT = 4;
+template <bool BLK>
 __global__ __launch_bounds__(256) void k_gather_t_quant(const bf16* __restrict__ x, const int* __restrict__ ptok,
                                                         const int* __restrict__ offsets, const int* __restrict__ qoff,
                                                         int El, int H, int64_t qc, uint8_t* __restrict__ q,
                                                         uint8_t* __restrict__ sc) {
   __shared__ __attribute__((aligned(16))) bf16 tile[128][64];
+  __shared__ float cmax[BLK ? 256 : 1];
   const int q0 = blockIdx.x * 128;
   if (q0 >= qoff[El]) return;   // past the last expert's segment: nothing reads these columns
   int lo = 0, hi = El - 1;      // the expert whose segment holds q0: the last e with qoff[e] <= q0
@@ -227,17 +264,21 @@ __global__ __launch_bounds__(256) void k_gather_t_quant(const bf16* __restrict__
     __syncthreads();
     if (h0 + 64 * GT_SPLIT < H) load(h0 + 64 * GT_SPLIT, nxt);
     const size_t orow = (size_t)h0 + (threadIdx.x & 63);
-    column_pass(tile, q + orow * qc + q0, sc + orow * (qc / 32) + q0 / 32);
-    __syncthreads();   // the tile is overwritten next
+    column_pass<BLK>(tile, q + orow * qc + q0, sc + orow * (qc / 32) + q0 / 32, cmax);
+    __syncthreads();   // the tile (and cmax) are overwritten next
   }
 }
 
 }  // namespace
 
-hipError_t launch_quant_rows(const void* in, uint8_t* q, uint8_t* sc, int64_t n, const char* name, hipStream_t s) {
+hipError_t launch_quant_rows(const void* in, uint8_t* q, uint8_t* sc, int64_t n, const char* name, hipStream_t s,
+                             bool blk) {
   const int64_t n8 = n / 8;
   prof_mark_begin(name, s);
-  k_quant_rows<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(static_cast<const bf16*>(in), q, sc, n8);
+  if (blk)
+    k_quant_rows<true><<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(static_cast<const bf16*>(in), q, sc, n8);
+  else
+    k_quant_rows<false><<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(static_cast<const bf16*>(in), q, sc, n8);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   prof_mark_end(s);
@@ -258,9 +299,13 @@ hipError_t launch_quant_cols(const void* in, uint8_t* q, uint8_t* sc, int B, int
 }
 
 hipError_t launch_quant_both(const void* in, uint8_t* qr, uint8_t* sr, uint8_t* qc, uint8_t* scc, int B, int R, int C,
-                             int64_t ldo, int col0, const char* name, hipStream_t s) {
+                             int64_t ldo, int col0, const char* name, hipStream_t s, bool blk) {
   prof_mark_begin(name, s);
-  k_quant_both<<<dim3(C / 128, R / 128, B), 256, 0, s>>>(static_cast<const bf16*>(in), qr, sr, qc, scc, R, C, ldo, col0);
+  const dim3 grid(C / 128, R / 128, B);
+  if (blk)
+    k_quant_both<true><<<grid, 256, 0, s>>>(static_cast<const bf16*>(in), qr, sr, qc, scc, R, C, ldo, col0);
+  else
+    k_quant_both<false><<<grid, 256, 0, s>>>(static_cast<const bf16*>(in), qr, sr, qc, scc, R, C, ldo, col0);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   prof_mark_end(s);
@@ -268,10 +313,13 @@ hipError_t launch_quant_both(const void* in, uint8_t* qr, uint8_t* sr, uint8_t* 
 }
 
 hipError_t launch_gather_t_quant(const void* x, const int* ptok, const int* offsets, const int* qoff, int El, int H,
-                                 int64_t qc, uint8_t* q, uint8_t* sc, const char* name, hipStream_t s) {
+                                 int64_t qc, uint8_t* q, uint8_t* sc, const char* name, hipStream_t s, bool blk) {
   prof_mark_begin(name, s);
-  k_gather_t_quant<<<dim3((unsigned)(qc / 128), GT_SPLIT), 256, 0, s>>>(static_cast<const bf16*>(x), ptok, offsets,
-                                                                        qoff, El, H, qc, q, sc);
+  const dim3 grid((unsigned)(qc / 128), GT_SPLIT);
+  if (blk)
+    k_gather_t_quant<true><<<grid, 256, 0, s>>>(static_cast<const bf16*>(x), ptok, offsets, qoff, El, H, qc, q, sc);
+  else
+    k_gather_t_quant<false><<<grid, 256, 0, s>>>(static_cast<const bf16*>(x), ptok, offsets, qoff, El, H, qc, q, sc);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   prof_mark_end(s);

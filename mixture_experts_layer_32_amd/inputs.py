@@ -15,7 +15,7 @@ top-8 routing, 16,384-token sequences; "Os Números que Impressionam" on the pag
   qwen3_30b_a3b        T=16384, H=2048, E=128, F=768,  k=8, bf16
   qwen3_30b_a3b_ep16   the same inputs, experts 0..15 only (one rank's expert share)
   qwen3_235b_a22b_zipf T=16384, H=4096, E=128, F=1536, k=8, bf16, Zipf-skewed router prior
-  qwen3_30b_a3b_mxfp8  the qwen3_30b_a3b inputs, for the MX precision modes
+  qwen3_30b_a3b_mxfp8  the qwen3_30b_a3b inputs, for the fp8 precision modes (MXFP8, FP8_BWD, FP8)
 
 Distributions: x ~ N(0,1); W_gate, W_up ~ N(0, 1/H); W_down ~ N(0, 1/F) (variance 1/fan_in);
 W_r ~ N(0, 0.02^2) (standard deviation 0.02); dY ~ N(0,1). Every tensor is drawn from its

@@ -41,6 +41,8 @@ def test_library_exports_every_declared_function():
     (dict(mode=-1), "MOE_ERR_UNSUPPORTED_MODE"),
     (dict(H=384, mode="mxfp8"), "MOE_ERR_UNSUPPORTED_SHAPE"),
     (dict(F=192, mode="fp8_bwd"), "MOE_ERR_UNSUPPORTED_SHAPE"),
+    (dict(H=384, mode="fp8"), "MOE_ERR_UNSUPPORTED_SHAPE"),
+    (dict(mode=5), "MOE_ERR_UNSUPPORTED_MODE"),
 ])
 def test_validation_errors(kw, code):
     with pytest.raises(b.MoEError) as ei:
@@ -81,7 +83,7 @@ def test_sizes_cover_the_layout():
     assert f32[2] > saved                                        # fp32 activations are wider
 
 
-@pytest.mark.parametrize("mode", ["mxfp8", "fp8_bwd"])
+@pytest.mark.parametrize("mode", ["mxfp8", "fp8_bwd", "fp8"])
 def test_mx_sizes_cover_the_layout(mode):
     T, H, F, E, k = 1000, 512, 256, 16, 4
     d = desc(T=T, H=H, F=F, E_total=E, topk=k, mode=mode)
@@ -91,8 +93,8 @@ def test_mx_sizes_cover_the_layout(mode):
     assert all(v % 256 == 0 for v in (fwd, bwd, saved))
     # routing + a, b (bf16) + the fp8 pair-contiguous hw copy with its scales
     assert saved >= rows * (4 * 4) + rows * 2 * F * 2 + qc * F * (1 + 1 / 32)
-    if mode == "mxfp8":    # quantised x, weights and hw, plus the per-pair outputs; the weights'
-        # backward orientation is kept in saved
+    if mode in ("mxfp8", "fp8"):    # quantised x, weights and hw, plus the per-pair outputs; the
+        # weights' backward orientation is kept in saved
         assert fwd >= rows * H * 2 + T * H * (1 + 1 / 32) + 3 * E * F * H * (1 + 1 / 32) + rows * F * (1 + 1 / 32)
         assert saved >= rows * 2 * F * 2 + (qc * F + 3 * E * F * H) * (1 + 1 / 32)
         wq = 0
@@ -119,6 +121,24 @@ def test_mx_quantize_validation(args, code, msg):
     with pytest.raises(b.MoEError, match=msg) as ei:
         b.moe_mx_quantize(x, rows, cols, axis, FAKE, FAKE, stream=0)
     assert ei.value.code == code
+
+
+@pytest.mark.parametrize("args,code,msg", [
+    ((None, 128, 128, 0), "MOE_ERR_INVALID_ARG", "in is null"),
+    ((FAKE + 8, 128, 128, 0), "MOE_ERR_INVALID_ARG", "not 16-byte aligned"),
+    ((FAKE, 0, 128, 0), "MOE_ERR_INVALID_ARG", "positive"),
+    ((FAKE, 128, 128, 2), "MOE_ERR_INVALID_ARG", "weight"),
+    ((FAKE, 64, 96, 0), "MOE_ERR_UNSUPPORTED_SHAPE", "cols must be a multiple of 128"),
+    ((FAKE, 64, 128, 1), "MOE_ERR_UNSUPPORTED_SHAPE", "rows must be a multiple of 128"),
+    ((FAKE, 1 << 17, 1 << 17, 0), "MOE_ERR_UNSUPPORTED_SHAPE", r"2\^34"),
+])
+def test_fp8_block_quantize_validation(args, code, msg):
+    x, rows, cols, weight = args
+    with pytest.raises(b.MoEError, match=msg) as ei:
+        b.moe_fp8_block_quantize(x, rows, cols, weight, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert ei.value.code == code
+    with pytest.raises(b.MoEError, match="qt is null"):
+        b.moe_fp8_block_quantize(FAKE, 128, 128, 1, FAKE, FAKE, None, FAKE, stream=0)
 
 
 def test_status_strings():

@@ -1,8 +1,9 @@
-"""GPU parity of the MX precision modes (MXFP8, FP8_BWD) against the MX-emulating float64 oracle.
+"""GPU parity of the fp8 precision modes (MXFP8, FP8_BWD, blockwise FP8) against the float64 oracle
+run in the same mode.
 
 Bar:
- * The MXFP8 quantise kernel (moe_mx_quantize): bit-exact E4M3 bytes and e8m0 scale bytes, against
-   oracle/mx.py on the same bf16 input.
+ * The MXFP8 quantise kernel (moe_mx_quantize) and the blockwise FP8 ones (moe_fp8_block_quantize):
+   bit-exact E4M3 bytes and e8m0 scale bytes, against oracle/mx.py on the same bf16 input.
  * Routing: bit-exact, as in every mode.
  * y, dx, dlogits, dW_gate, dW_up, dW_down: relative Frobenius error within 5e-2 against the oracle
    run in the same mode (every GEMM operand quantised at the same points). The error against the
@@ -18,6 +19,10 @@ from mixture_experts_layer_32_amd import binding, inputs
 from gpu_util import OUTS, TOL, run_layer
 
 pytestmark = pytest.mark.gpu
+
+
+def _e4m3_bytes(el):
+    return torch.from_numpy(np.ascontiguousarray(el)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
 def _fp8_values(u8):
@@ -70,6 +75,66 @@ def test_mx_quantize_bit_exact(axis, rows, cols):
         assert (sx == -127).any() and (np.abs(el) == 448).any() and (sx > 100).any()
 
 
+def _blk_input(rows, cols, seed, tile_rows):
+    """bf16-exact values with one magnitude per block of tile_rows x 128 (exponents 2^-140 .. 2^120),
+    all-zero blocks, and blocks whose amax sits on the scale boundaries: exactly 448 * 2^j, one bf16
+    step above it (the scale moves up), and exactly 2^j."""
+    rng = np.random.default_rng(seed)
+    nbr, nbc = rows // tile_rows, cols // 128
+    v = rng.standard_normal((rows, cols)).astype(np.float32)
+    v *= np.repeat(np.repeat(np.exp2(rng.integers(-140, 121, size=(nbr, nbc))).astype(np.float32), tile_rows, 0),
+                   128, 1)
+    v = inputs.round_to_bf16(v)
+    blocks = v.reshape(nbr, tile_rows, nbc, 128)
+    pick = rng.random((nbr, nbc))
+    for bi, bj in zip(*np.nonzero(pick < 0.3)):
+        blk = blocks[bi, :, bj, :]
+        j = int(rng.integers(-20, 20))
+        kind = int(rng.integers(0, 4))
+        if kind == 0:
+            blk[...] = 0.0
+            continue
+        top = [448.0, 452.0, 256.0][kind - 1] * 2.0 ** j             # 452: just above 448 in bf16
+        blk *= np.float32(0.99 * top / max(float(np.abs(blk).max()), 1e-30))
+        blk[...] = inputs.round_to_bf16(np.clip(blk, -0.99 * top, 0.99 * top))
+        blk[0, 0] = np.float32(top) * (1 if rng.random() < 0.5 else -1)
+    v = blocks.reshape(rows, cols)
+    v[rng.random((rows, cols)) < 0.02] = 0.0
+    v[v == 0] = 0.0                                               # no negative zeros
+    return v
+
+
+@pytest.mark.parametrize("weight,rows,cols", [(0, 96, 512), (0, 1, 128), (0, 300, 2048), (1, 128, 128),
+                                              (1, 256, 384), (1, 768, 2048)])
+def test_fp8_block_quantize_bit_exact(weight, rows, cols):
+    print(f"case fp8_block_quantize weight={weight} {rows}x{cols}", flush=True)
+    v = _blk_input(rows, cols, 200 + rows + weight, 128 if weight else 1)
+    x = torch.from_numpy(v).to("cuda").to(torch.bfloat16)
+    q = torch.empty(rows, cols, dtype=torch.uint8, device="cuda")
+    s = torch.empty(rows, cols // 32, dtype=torch.uint8, device="cuda")
+    qt = torch.empty(cols, rows, dtype=torch.uint8, device="cuda") if weight else None
+    st = torch.empty(cols, rows // 32, dtype=torch.uint8, device="cuda") if weight else None
+    binding.moe_fp8_block_quantize(x, rows, cols, weight, q, s, qt, st)
+    torch.cuda.synchronize()
+    q, s = q.cpu().numpy(), s.cpu().numpy()
+    v64 = v.astype(np.float64)
+    if weight:
+        _, el, sx = oracle.mx.fp8_tile_quantize(v64, return_parts=True)        # sx per 128 x 128 tile
+        want_s = np.repeat(np.repeat(sx + 127, 128, 0), 4, 1).astype(np.uint8)  # [rows, cols / 32]
+        want_st = np.repeat(np.repeat(sx.T + 127, 128, 0), 4, 1).astype(np.uint8)
+        qt, st = qt.cpu().numpy(), st.cpu().numpy()
+        assert np.array_equal(st, want_st), np.argwhere(st != want_st)[:5]
+        assert np.array_equal(qt, _e4m3_bytes(el.T)), np.argwhere(qt != _e4m3_bytes(el.T))[:5]
+    else:
+        _, el, sx = oracle.mx.fp8_block_quantize(v64, axis=1, return_parts=True)  # sx per row and block of 128
+        want_s = np.repeat(sx + 127, 4, axis=1).astype(np.uint8)
+    assert np.array_equal(s, want_s), np.argwhere(s != want_s)[:5]
+    assert np.array_equal(q, _e4m3_bytes(el)), np.argwhere(q != _e4m3_bytes(el))[:5]
+    assert np.abs(el).max() <= 448
+    if rows * cols >= 500000:  # the input reached the boundaries it was built for
+        assert (sx == -127).any() and (np.abs(el) == 448).any() and (sx > 100).any()
+
+
 def oracle_full(cfg, L, mode):
     args = dict(x=L["x"], logits=L["logits"], wg=L["wg"], wu=L["wu"], wd=L["wd"], k=cfg.k, e0=cfg.e0,
                 e_local=cfg.el, mode=mode)
@@ -84,7 +149,7 @@ def mx_case(name, mode, **kw):
 
 
 MX_SMALL = [
-    mx_case(n, m, **kw) for m in ("mxfp8", "fp8_bwd") for n, kw in [
+    mx_case(n, m, **kw) for m in ("mxfp8", "fp8_bwd", "fp8") for n, kw in [
         ("basic", dict(T=256, H=256, F=128, E=8, k=2, seed=31)),
         ("ragged_T333", dict(T=333, H=512, F=256, E=16, k=4, seed=32)),
         ("F384", dict(T=300, H=256, F=384, E=8, k=3, seed=33)),
@@ -123,7 +188,7 @@ def test_small_layer_parity_mx(cfg, L, mode):
         assert not np.any(got["y"][none]) and not np.any(got["dx"][none])
 
 
-@pytest.mark.parametrize("mode", ["mxfp8", "fp8_bwd"])
+@pytest.mark.parametrize("mode", ["mxfp8", "fp8_bwd", "fp8"])
 def test_mx_deterministic_and_poison_independent(mode):
     cfg, L = inputs.custom_layer(T=300, H=512, F=256, E=16, k=4, dtype="bf16", seed=40)
     print(f"case determinism mode={mode}", flush=True)
@@ -135,7 +200,7 @@ def test_mx_deterministic_and_poison_independent(mode):
 
 @pytest.mark.slow
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("mode", ["mxfp8", "fp8_bwd"])
+@pytest.mark.parametrize("mode", ["mxfp8", "fp8_bwd", "fp8"])
 def test_full_size_sampled_mx(mode):
     cfg = inputs.CONFIGS["qwen3_30b_a3b_mxfp8"]
     print(f"case {cfg.name} mode={mode}: generating inputs", flush=True)
@@ -166,11 +231,7 @@ def test_full_size_sampled_mx(mode):
     torch.cuda.empty_cache()
 
 
-def _e4m3_bytes(el):
-    return torch.from_numpy(np.ascontiguousarray(el)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-
-
-@pytest.mark.parametrize("mode", ["mxfp8", "fp8_bwd"])
+@pytest.mark.parametrize("mode", ["mxfp8", "fp8_bwd", "fp8"])
 def test_mx_operands_left_in_saved(mode):
     """The forward's MXFP8 operands for the backward: the weights' transposed copies (MXFP8) bit-exact
     against the oracle's quantiser; w*h along each expert's pairs within 2e-2 of the oracle's (the
@@ -187,7 +248,21 @@ def test_mx_operands_left_in_saved(mode):
     qoff = sv[off["qoff"]:off["qoff"] + 4 * (El + 1)].view(np.int32)
     want_qoff = np.concatenate([[0], np.cumsum(-(-r["counts"] // 128) * 128)])
     assert np.array_equal(qoff, want_qoff) and qc % 128 == 0 and qc >= qoff[-1]
-    if mode == "mxfp8":
+    if mode == "fp8":
+        wdt = sv[off["wdt"]:off["wdt"] + El * F * H].reshape(El, F, H)
+        wdts = sv[off["wdt_scales"]:off["wdt_scales"] + El * F * H // 32].reshape(El, F, H // 32)
+        wgut = sv[off["wgut"]:off["wgut"] + El * H * 2 * F].reshape(El, H, 2 * F)
+        wguts = sv[off["wgut_scales"]:off["wgut_scales"] + El * H * 2 * F // 32].reshape(El, H, 2 * F // 32)
+        for e in range(El):       # 128 x 128 tiles: the transposed copies carry the same tile scales
+            _, el_, sx = oracle.mx.fp8_tile_quantize(L["wd"][e].astype(np.float64), return_parts=True)
+            assert np.array_equal(wdt[e], _e4m3_bytes(el_.T)), e
+            assert np.array_equal(wdts[e], np.repeat(np.repeat(sx.T + 127, 128, 0), 4, 1).astype(np.uint8)), e
+            for half, w in ((0, L["wg"][e]), (1, L["wu"][e])):
+                _, el_, sx = oracle.mx.fp8_tile_quantize(w.astype(np.float64), return_parts=True)
+                assert np.array_equal(wgut[e][:, half * F:(half + 1) * F], _e4m3_bytes(el_.T)), (e, half)
+                assert np.array_equal(wguts[e][:, half * F // 32:(half + 1) * F // 32],
+                                      np.repeat(np.repeat(sx.T + 127, 128, 0), 4, 1).astype(np.uint8)), (e, half)
+    elif mode == "mxfp8":
         wdt = sv[off["wdt"]:off["wdt"] + El * F * H].reshape(El, F, H)
         wdts = sv[off["wdt_scales"]:off["wdt_scales"] + El * F * H // 32].reshape(El, F, H // 32)
         wgut = sv[off["wgut"]:off["wgut"] + El * H * 2 * F].reshape(El, H, 2 * F)
@@ -213,11 +288,13 @@ def test_mx_operands_left_in_saved(mode):
         if n == 0:
             continue
         toks, wr = pairs // cfg.k, r["w"].reshape(-1)[pairs]
-        if mode == "mxfp8":
-            _, _, h, _ = oracle.expert_forward_q(x64[toks], wr, L["wg"][e], L["wu"][e], L["wd"][e], True)
+        if mode in ("mxfp8", "fp8"):
+            _, _, h, _ = oracle.expert_forward_q(x64[toks], wr, L["wg"][e], L["wu"][e], L["wd"][e],
+                                                 "blk" if mode == "fp8" else "mx")
         else:
             _, _, h, _ = oracle.expert_forward(x64[toks], L["wg"][e], L["wu"][e], L["wd"][e])
-        want = oracle.mx.mx_quantize(wr[:, None] * h, axis=0).T            # [F, n], blocks along the pairs
+        quant = oracle.mx.fp8_block_quantize if mode == "fp8" else oracle.mx.mx_quantize
+        want = quant(wr[:, None] * h, axis=0).T                              # [F, n], blocks along the pairs
         dec = _fp8_values(hwt[:, seg]) * np.repeat(2.0 ** (hws[:, qoff[e] // 32:qoff[e + 1] // 32].astype(np.int64) - 127),
                                                    32, axis=1)
         assert oracle.rel_frobenius(dec[:, :n], want) <= 2e-2, e

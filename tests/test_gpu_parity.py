@@ -148,7 +148,7 @@ def test_full_size_sampled(name):
 TILE_COUNTS = [128, 129, 255, 256, 257, 1, 0, 127, 384, 385]
 
 
-@pytest.mark.parametrize("mode", ["bf16", "mxfp8", "fp8_bwd"])
+@pytest.mark.parametrize("mode", ["bf16", "mxfp8", "fp8_bwd", "fp8"])
 def test_tile_boundary_counts(mode):
     """k = 1 routing forced onto chosen experts (the chosen logit is 6 above the others), so that the
     expert segments end exactly at, just before and just after the tile edges: half tiles, whole
