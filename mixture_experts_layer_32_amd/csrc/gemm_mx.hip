@@ -420,18 +420,28 @@ __device__ __forceinline__ void epilogue_dh_blk(const BwdParams& p, const f32x16
                                                 int nt, int r0, int seg_end, int fq, int qend, int colq, int64_t qs) {
   const bf16* __restrict__ ab = static_cast<const bf16*>(p.ab);
   const int F = p.F, f2s = 2 * F / 32;
-  auto dswiglu = [&](int i, int s, float (&da)[8], float (&db)[8], float& gsum) {
+  // a and b of the lane's 8 rows of a 32-row block. The 8 blocks (4 per pass) are processed in
+  // order, and row s of the next block is loaded into row s's registers as soon as they are
+  // unpacked, so those loads run during the rest of the current block.
+  uint4 araw[8], braw[8];
+  auto load_ab = [&](int i, int s) {
+    const int rl = (lane >> 4) + 4 * s, c0 = (lane & 15) * 8;
+    const int r = r0 + 128 * wm + 32 * i + rl, f = fq + c0;
+    const bf16* abr = ab + (size_t)min(r, seg_end - 1) * 2 * F + min(f, F - 8);
+    araw[s] = ld16(abr);
+    braw[s] = ld16(abr + F);
+  };
+  // rows past the segment and columns past F computed from clamped loads, then zeroed
+  auto dswiglu = [&](int i, int s, int inext, float (&da)[8], float (&db)[8], float& gsum) {
     const int rl = (lane >> 4) + 4 * s, c0 = (lane & 15) * 8;
     const float wt = __shfl(wrow[i], rl);
     const int r = r0 + 128 * wm + 32 * i + rl, f = fq + c0;
-    // branch-free: rows past the segment and columns past F read a clamped row and are then zeroed
-    // (a branch around the array writes made the compiler keep da and db in scratch memory)
     const bool ok = r < seg_end && f < F;
     float u[8], av[8], bv[8];
     read8(slab, rl, c0, u);
-    const bf16* abr = ab + (size_t)min(r, seg_end - 1) * 2 * F + min(f, F - 8);
-    unpack8(ld16(abr), av);
-    unpack8(ld16(abr + F), bv);
+    unpack8(araw[s], av);
+    unpack8(braw[s], bv);
+    if (inext >= 0) load_ab(inext, s);
     gsum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -452,13 +462,15 @@ __device__ __forceinline__ void epilogue_dh_blk(const BwdParams& p, const f32x16
   };
   // columns lane and lane + 64 of the da and db slabs, over the wave's 128 rows
   float cm[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 8; ++s) load_ab(0, s);
   auto pass1 = [&](auto I) {
     constexpr int i = decltype(I)::value;
     stage_rows(slab, acc, i, lane);
-#pragma unroll 1
+#pragma unroll
     for (int s = 0; s < 8; ++s) {
       float da[8], db[8], gsum;
-      dswiglu(i, s, da, db, gsum);
+      dswiglu(i, s, (i + 1) & 3, da, db, gsum);   // after block 3 come pass 2's blocks from 0
       const int rl = (lane >> 4) + 4 * s, c0 = (lane & 15) * 8;
       const int r = r0 + 128 * wm + 32 * i + rl, f = fq + c0;
       const int sda = fp8b_exponent(mx_amax_x16(da));
@@ -493,10 +505,10 @@ __device__ __forceinline__ void epilogue_dh_blk(const BwdParams& p, const f32x16
   auto pass2 = [&](auto I) {
     constexpr int i = decltype(I)::value;
     stage_rows(slab, acc, i, lane);
-#pragma unroll 1
+#pragma unroll
     for (int s = 0; s < 8; ++s) {
       float da[8], db[8], gsum;
-      dswiglu(i, s, da, db, gsum);
+      dswiglu(i, s, i < 3 ? i + 1 : -1, da, db, gsum);
       put_slabs(s, da, db);
     }
     const int colb = colq + 32 * i;
