@@ -89,6 +89,18 @@ struct TileSched {
   }
 };
 
+// Static per-XCD tile range whose 9 boundaries b[0..8] were written by a previous kernel (the
+// weight-gradient GEMMs' cost-balanced split); within it the XCD's workgroups take tiles round-robin.
+__device__ __forceinline__ XcdRange xcd_range_split(const int* b) {
+  const int xcd = blockIdx.x & 7;
+  XcdRange r;
+  r.begin = ld_uniform(b, xcd);
+  r.end = ld_uniform(b, xcd + 1);
+  r.stride = gridDim.x >> 3;
+  r.first = r.begin + (blockIdx.x >> 3);
+  return r;
+}
+
 // K-major operand of 256 rows with ROWB bytes of contraction per row per K-tile (64 or 128).
 // One wave instruction moves RPI = 64/NCH whole row segments (NCH = ROWB/16 chunks of 16 bytes);
 // with NW waves sharing the tile, this lane owns rows (w*LOADS + j)*RPI + lane/NCH and slot lane%NCH. A 128-byte segment is a

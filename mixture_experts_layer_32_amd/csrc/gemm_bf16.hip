@@ -548,7 +548,7 @@ __global__ __launch_bounds__(NTHR8, 1) void k_wgrad_down_bf16(BwdParams p) {
   MOE_SMEM
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;   // 64x128 per wave
   const int H = p.H, F = p.F, ntn = (F + TILE - 1) / TILE, tpe = (H / TILE) * ntn;
-  const XcdRange xr = xcd_range(p.El * tpe);
+  const XcdRange xr = xcd_range_split(p.sched + kSchedWgradDown * kSchedInts);
   for (int lid = xr.first; lid < xr.end; lid += xr.stride) {
   const int e = lid / tpe, t = lid - e * tpe, mt = t / ntn, nt = t - mt * ntn;
   const int seg0 = p.offsets[e], seg_end = p.offsets[e + 1];
@@ -580,7 +580,7 @@ __global__ __launch_bounds__(NTHR8, 1) void k_wgrad_gateup_bf16(BwdParams p) {
   // 128x64 per wave: B (x, MN-major) goes through the slower transposing LDS read
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
   const int H = p.H, F = p.F, ntn = H / TILE, tpe = (2 * F / TILE) * ntn;
-  const XcdRange xr = xcd_range(p.El * tpe);
+  const XcdRange xr = xcd_range_split(p.sched + kSchedWgradGateup * kSchedInts);
   for (int lid = xr.first; lid < xr.end; lid += xr.stride) {
   const int e = lid / tpe, t = lid - e * tpe, mt = t / ntn, nt = t - mt * ntn;
   const int seg0 = p.offsets[e], seg_end = p.offsets[e + 1];
@@ -821,12 +821,92 @@ __global__ __launch_bounds__(256) void k_router_sum_dw(RouterParams p) {
   st8(static_cast<bf16*>(p.dwr) + i, pack4(v.x, v.y, v.z, v.w));
 }
 
-// zeroes the backward GEMMs' tile-scheduler counters (the workspace is the caller's)
-__global__ __launch_bounds__(64) void k_sched_reset(int* sched) {
-  for (int i = threadIdx.x; i < kSchedSlots * kSchedInts; i += 64) sched[i] = 0;
+// One workgroup before the backward GEMMs: zeroes the tile-scheduler counters (the workspace is the
+// caller's) and cuts each weight-gradient GEMM's tile list (expert-major, tpe tiles per expert) into
+// 8 contiguous per-XCD ranges, whose tiles the XCD's workgroups then take round-robin. Every tile of
+// expert e contracts over the expert's c_e pairs: u_e = ceil(c_e / ktile) K-tiles, plus
+// kTileOverhead K-tiles' worth of prologue and epilogue. Ranges of equal tile count are kept while
+// their estimated costs stay within 10 % of each other (then every workgroup also gets the same
+// number of tiles); otherwise, as under a skewed load, where equal counts gave the XCD holding the
+// most loaded experts several times the others' work, boundary x (1..7) moves to the first tile whose
+// preceding tiles cost at least x/8 of the total. El <= kMaxExperts = 512: 2 experts per thread.
+constexpr int kTileOverhead = 2;
+__global__ __launch_bounds__(256) void k_sched_setup(int* sched, const int* offsets, int El, int tpe_d, int tpe_g,
+                                                     int ktile) {
+  __shared__ long long part[256];   // inclusive prefix of the per-thread cost sums
+  __shared__ int uu[2 * 256];       // u_e
+  __shared__ int even[2];           // equal-count ranges within 10 %
+  const int t = threadIdx.x;
+  for (int i = t; i < kSchedSlots * kSchedInts; i += 256) sched[i] = 0;
+  long long own = 0;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = 2 * t + q;
+    const int u = e < El ? (offsets[e + 1] - offsets[e] + ktile - 1) / ktile + kTileOverhead : 0;
+    uu[e] = u;
+    own += u;
+  }
+  part[t] = own;
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {
+    const long long v = t >= d ? part[t - d] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  const long long total = part[255];
+  const int slots[2] = {kSchedWgradDown, kSchedWgradGateup}, tpes[2] = {tpe_d, tpe_g};
+  // cost of tiles [0, L): the experts before e = L / tpe, then L % tpe tiles of e
+  auto cum = [&](int tpe, int L) -> long long {
+    const int e = L / tpe, j = L - e * tpe;
+    long long U = e >= 2 ? part[e / 2 - 1] : 0;
+    if (e & 1) U += uu[e - 1];
+    return tpe * U + (e < El ? (long long)j * uu[e] : 0);
+  };
+  if (t < 2) {
+    const int tpe = tpes[t], per = (El * tpe + 7) >> 3;
+    long long mx = 0;
+    for (int x = 0; x < 8; ++x)
+      mx = max(mx, cum(tpe, min((x + 1) * per, El * tpe)) - cum(tpe, min(x * per, El * tpe)));
+    even[t] = 10 * 8 * mx <= 11 * tpe * total;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int tpe = tpes[g], per = (El * tpe + 7) >> 3;
+    int* b = sched + slots[g] * kSchedInts;
+    if (even[g]) {
+      if (t < 8) b[t + 1] = min((t + 1) * per, El * tpe);
+      continue;
+    }
+    long long pre = part[t] - own;      // cost units of the experts before 2t
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = 2 * t + q;
+      if (e < El) {
+        const long long u = uu[e], lo = tpe * pre, hi = tpe * (pre + u);
+        for (int x = 1; x < 8; ++x) {
+          const long long target = tpe * total * x / 8;
+          if (lo <= target && target < hi) b[x] = e * tpe + (int)((target - lo + u - 1) / u);
+        }
+        pre += u;
+      }
+    }
+    if (t == 0) b[8] = El * tpe;
+  }
 }
 
 }  // namespace
+
+hipError_t launch_sched_setup(const BwdParams& p, int ktile, hipStream_t s) {
+  const int tpe_d = (p.H / TILE) * ((p.F + TILE - 1) / TILE), tpe_g = (2 * p.F / TILE) * (p.H / TILE);
+  prof_mark_begin("sched_setup", s);
+  k_sched_setup<<<1, 256, 0, s>>>(p.sched, p.offsets, p.El, tpe_d, tpe_g, ktile);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  prof_mark_end(s);
+  return hipSuccess;
+}
 
 hipError_t launch_forward_gemms_bf16(const FwdParams& p, int grid, hipStream_t s) {
   hipError_t err;
@@ -878,10 +958,7 @@ hipError_t launch_router_bwd_bf16(const RouterParams& p, int grid, hipStream_t s
 
 hipError_t launch_backward_gemms_bf16(const BwdParams& p, int grid, hipStream_t s) {
   hipError_t err;
-  prof_mark_begin("sched_reset", s);
-  k_sched_reset<<<1, 64, 0, s>>>(p.sched);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  prof_mark_end(s);
+  if ((err = launch_sched_setup(p, KTILE, s)) != hipSuccess) return err;
   prof_mark_begin("gemm_bwd_dh_dswiglu", s);
   k_bwd_dh_bf16<<<grid, NTHR8, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;

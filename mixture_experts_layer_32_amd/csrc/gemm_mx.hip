@@ -687,7 +687,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_wgrad_down_mx(BwdParams p) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
   const int H = p.H, F = p.F, ntn = (F + TILE - 1) / TILE, tpe = (H / TILE) * ntn;
   const int64_t qs = p.qc / 32;
-  const XcdRange xr = xcd_range(p.El * tpe);
+  const XcdRange xr = xcd_range_split(p.sched + kSchedWgradDown * kSchedInts);
   const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
   const int row_s = 128 * sc_half() + 32 * sc_blk() + sc_row32();
   for (int lid = xr.first; lid < xr.end; lid += xr.stride) {
@@ -717,7 +717,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_wgrad_gateup_mx(BwdParams p) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
   const int H = p.H, F = p.F, ntn = H / TILE, tpe = (2 * F / TILE) * ntn;
   const int64_t qs = p.qc / 32;
-  const XcdRange xr = xcd_range(p.El * tpe);
+  const XcdRange xr = xcd_range_split(p.sched + kSchedWgradGateup * kSchedInts);
   const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
   const int row_s = 128 * sc_half() + 32 * sc_blk() + sc_row32();
   for (int lid = xr.first; lid < xr.end; lid += xr.stride) {
@@ -764,6 +764,7 @@ hipError_t launch_forward_gemms_mx(const FwdParams& p, int grid, hipStream_t s) 
 
 hipError_t launch_backward_gemms_mx(const BwdParams& p, int grid, hipStream_t s) {
   hipError_t err;
+  if ((err = launch_sched_setup(p, KTILE, s)) != hipSuccess) return err;
   prof_mark_begin("gemm_bwd_dh_dswiglu", s);
   if (p.blk)
     k_bwd_dh_mx<true><<<grid, NTHR, 0, s>>>(p);

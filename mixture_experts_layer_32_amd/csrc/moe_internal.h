@@ -16,6 +16,8 @@ constexpr int kMaxExperts = 512;
 constexpr int kMaxTopk = 32;
 constexpr int kSchedInts = 16;      // ints per GEMM's tile-scheduler slot (8 per-XCD counters, padded to 64 B)
 constexpr int kSchedSlots = 8;      // scheduler slots per workspace
+// backward slots holding the weight-gradient GEMMs' per-XCD tile ranges (9 boundaries each)
+constexpr int kSchedWgradDown = 2, kSchedWgradGateup = 3;
 
 // Byte offsets of every region inside the three caller-provided buffers.
 struct Layout {
@@ -149,6 +151,9 @@ template <class T> hipError_t launch_backward(const BwdParams& p, int grid, hipS
 template <class T> hipError_t launch_combine_bwd(const BwdParams& p, hipStream_t s);
 hipError_t launch_forward_gemms_bf16(const FwdParams& p, int grid, hipStream_t s);
 hipError_t launch_backward_gemms_bf16(const BwdParams& p, int grid, hipStream_t s);
+// zeroes the backward's tile counters and splits the weight-gradient tile lists over the XCDs by
+// cost (ktile: pairs per K-tile of the engine)
+hipError_t launch_sched_setup(const BwdParams& p, int ktile, hipStream_t s);
 
 // Router projection in front of the layer (bf16 engine): logits = x W_r^T; backward dW_r and the
 // router's part of dx. The GEMMs with a long contraction split it S ways (kc elements per split)
