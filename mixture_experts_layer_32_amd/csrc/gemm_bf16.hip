@@ -179,8 +179,10 @@ __device__ __forceinline__ void read_frags(bf16x8 (&fa)[MI], bf16x8 (&fb)[NJ], c
                                            const int (&bn)[NJ], int lane) {
 #pragma unroll
   for (int i = 0; i < NA; ++i) fa[i] = AMN ? frag_mn(st, am0 + AST * i, ks, lane) : frag_k(st, am0 + AST * i, ks, lane);
+  if (NA > 0) {   // a wave with no active row block multiplies nothing
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) fb[j] = BMN ? frag_mn(st + OPB, bn[j], ks, lane) : frag_k(st + OPB, bn[j], ks, lane);
+    for (int j = 0; j < NJ; ++j) fb[j] = BMN ? frag_mn(st + OPB, bn[j], ks, lane) : frag_k(st + OPB, bn[j], ks, lane);
+  }
 }
 
 // The B fragment is passed as the MFMA's first operand, so each accumulator block holds the
@@ -194,15 +196,17 @@ __device__ __forceinline__ void mma_step(f32x16 (&acc)[MI][NJ], const bf16x8 (&f
 }
 
 // Row block i of the wave's A rows starts at am0 + AST i. Only the first NA row blocks run (NA < MI:
-// the rows of the others are known to be past the segment; their accumulators stay zero).
-// With NA < MI (half tile) the A rows from 128 on are not needed: the waves that load them (waves
-// 4-7, K-major A) skip those loads, and wait for their B loads only.
+// the rows of the others are known to be past the segment; their accumulators stay zero); NA = 0
+// runs all MI, NA = -1 none (the wave still loads its share of the operand tiles).
+// The waves 4-7 load the A rows from 128 on (K-major A). When no wave needs them they skip those
+// loads and wait for their B loads only: skip_hi = 1 or 0 says whether that is so; by default
+// (skip_hi = -1) it is taken to be so whenever NA < MI (the row-tiled kernels' half tiles).
 template <bool AMN, bool BMN, int AST = 32, int NA = 0, int MI, int NJ, class LA, class LB>
 __device__ __forceinline__ void mainloop(f32x16 (&acc)[MI][NJ], char* smem, LA& la, LB& lb, int nk, int am0,
-                                         const int (&bn)[NJ]) {
-  constexpr int ACT = NA ? NA : MI;
+                                         const int (&bn)[NJ], int skip_hi = -1) {
+  constexpr int ACT = NA == 0 ? MI : (NA < 0 ? 0 : NA);
   static_assert(ACT == MI || !AMN, "half tiles take a K-major A");
-  const bool skip_a = ACT < MI && wave_id() >= NWAVE / 2;
+  const bool skip_a = (skip_hi < 0 ? ACT < MI : skip_hi > 0) && wave_id() >= NWAVE / 2;
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < MI; ++i)
@@ -407,9 +411,10 @@ __global__ __launch_bounds__(NTHR8, 1) void k_bwd_dh_bf16(BwdParams p) {
   const bf16* __restrict__ ab = static_cast<const bf16*>(p.ab);
   bf16* __restrict__ dab = static_cast<bf16*>(p.dab);
   const int H = p.H, F = p.F, ntn = (F + TILE - 1) / TILE;
-  const XcdRange xr = xcd_range(*p.num_mtiles2 * ntn);
+  __shared__ int s_tile;
+  TileSched ts(p.sched + 0 * kSchedInts, *p.num_mtiles2 * ntn);
   const int bn[2] = {64 * wn, 64 * wn + 32};
-  for (int tile = xr.first; tile < xr.end; tile += xr.stride) {
+  for (int tile = ts.first(&s_tile); tile >= 0; tile = ts.next(&s_tile)) {
     const int mt = tile / ntn, nt = tile - mt * ntn;
     const int2 me = p.mtile2[mt];
     const int e = me.x, r0 = me.y, seg_end = p.offsets[e + 1];
@@ -428,7 +433,17 @@ __global__ __launch_bounds__(NTHR8, 1) void k_bwd_dh_bf16(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) wrow[i] = p.weight[p.perm[min(r0 + 128 * wm + acc_m(i, lane), seg_end - 1)]];
     f32x16 acc[4][2];
-    mainloop<false, true>(acc, smem, la, lb, H / KTILE, 128 * wm, bn);
+    // An expert's last tile often holds a few rows only: each wave multiplies just its 32-row blocks
+    // that reach into the segment (none, 1, 2 or all 4), and with at most 128 valid rows the waves
+    // 4-7 skip the A loads of rows 128-255. Tiles then differ in cost: the XCD's workgroups take
+    // them from a counter.
+    const int valid = seg_end - r0 - 128 * wm;   // the wave's rows inside the segment
+    const int skip_hi = seg_end - r0 <= 128;
+    if (valid <= 0) mainloop<false, true, 32, -1>(acc, smem, la, lb, H / KTILE, 128 * wm, bn, skip_hi);
+    else if (valid <= 32) mainloop<false, true, 32, 1>(acc, smem, la, lb, H / KTILE, 128 * wm, bn, skip_hi);
+    else if (valid <= 64) mainloop<false, true, 32, 2>(acc, smem, la, lb, H / KTILE, 128 * wm, bn, skip_hi);
+    else mainloop<false, true, 32, 0>(acc, smem, la, lb, H / KTILE, 128 * wm, bn, skip_hi);
+    ts.fetch();
     // u = dH' staged per 32 rows; each row's 64 columns are read by 8 lanes, 8 columns each. The
     // row pass overwrites u with da and fills a second slab with db (zero on rows or columns past
     // the segment); both then go to the pair-contiguous copy dabT. The wave's partial of g over its
