@@ -11,7 +11,9 @@ It runs on one batch of synthetic inputs already resident in HBM. The default wo
 Qwen3-30B-A3B-shaped layer: T=16384, H=2048, 128 experts, F=768, top-8, bf16.
 
 Printed on one JSON line:
-  value         whole-layer TFLOP/s = 18*H*F*pairs / (forward+backward time)
+  value         whole-layer TFLOP/s = 18*H*F*pairs / (forward+backward time, wall clock over K steps)
+  fwd_ms, bwd_ms  medians of the per-step HIP-event times; step_ms_events: median, p10 and p90 of
+                the per-step forward+backward event times
   roofline      the dominant kernel: algorithmic flops per launch / its mean duration (HIP events
                 on the launch stream) against the bf16 MFMA peak
   cpu_baseline  the float64 oracle on whole expert shares, at least 10 s of host time
@@ -232,6 +234,7 @@ def main():
     ms_step = (time.perf_counter() - t0) * 1e3 / a.steps
     fwd_ms = float(np.median([e0.elapsed_time(e1) for e0, e1, _ in evs]))
     bwd_ms = float(np.median([e1.elapsed_time(e2) for _, e1, e2 in evs]))
+    step_ev = np.array([e0.elapsed_time(e2) for e0, _, e2 in evs])   # GPU time of each fwd+bwd step
 
     # per-kernel durations: the same K steps again with every launch bracketed by HIP events
     binding.profile_enable(64 * a.steps)
@@ -286,6 +289,10 @@ def main():
                    "topk": cfg.k, "routed_pairs": P},
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
         "full_layer_2f_b_ms": round(2 * fwd_ms + bwd_ms, 4),
+        "step_ms_events": {"median": round(float(np.median(step_ev)), 4),
+                           "p10": round(float(np.percentile(step_ev, 10)), 4),
+                           "p90": round(float(np.percentile(step_ev, 90)), 4),
+                           "caches": "not flushed between steps; inputs resident in HBM"},
         "pct_mfma_peak": round(100 * ideal_ms / ms_step, 2),
         "mfma_peak_basis": {"mxfp8": "fp8 5033.2 TFLOP/s", "fp8": "fp8 5033.2 TFLOP/s", "fp8_bwd": "bf16 forward, fp8 backward GEMMs",
                             "fp32": "fp32 157.3 TFLOP/s"}.get(mode, "bf16 2516.6 TFLOP/s"),

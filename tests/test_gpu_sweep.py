@@ -1,0 +1,57 @@
+"""Seeded sweep of small layers over every precision mode, against the oracle run in the same mode.
+
+Each case draws its shape from a fixed seed: T, H (a multiple of 256), F (a multiple of 128), E, k,
+an expert share (E_local, e0) and sometimes a Zipf-like skew of the expert loads, so that the
+kernels meet shapes and routing outcomes the hand-picked cases do not name. Bar: routing bit-exact,
+every output within the mode's relative Frobenius tolerance, experts with no rows exactly zero.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from mixture_experts_layer_32_amd import inputs
+from gpu_util import OUTS, TOL, run_layer
+
+pytestmark = pytest.mark.gpu
+
+MODES = ("bf16", "mxfp8", "fp8_bwd", "fp8", "fp32")
+
+
+def _case(i):
+    rng = np.random.default_rng(1000 + i)
+    mode = MODES[i % len(MODES)]
+    E = int(rng.integers(2, 41))
+    k = int(rng.integers(1, min(8, E) + 1))
+    share = rng.random() < 0.3
+    el = int(rng.integers(1, E + 1)) if share else E
+    e0 = int(rng.integers(0, E - el + 1)) if share else 0
+    kw = dict(T=int(rng.integers(1, 700)), H=int(rng.choice([256, 512])), F=int(rng.choice([128, 256, 384, 512, 640])),
+              E=E, k=k, seed=2000 + i, E_local=el if share else -1, e0=e0,
+              zipf_s=float(rng.choice([0.0, 0.0, 1.1, 2.5])))
+    return mode, kw
+
+
+CASES = [pytest.param(*_case(i), id=f"sweep{i}") for i in range(20)]
+
+
+@pytest.mark.parametrize("mode,kw", CASES)
+def test_sweep_parity(mode, kw):
+    print(f"case sweep mode={mode} {kw}", flush=True)
+    cfg, L = inputs.custom_layer(dtype="fp32" if mode == "fp32" else "bf16", **kw)
+    got = run_layer(cfg, L, mode)
+    r = oracle.route(L["logits"], cfg.k, cfg.e0, cfg.el)
+    for n in ("idx", "counts", "offsets", "perm", "pair_pos"):
+        assert np.array_equal(got["routing"][n], r[n]), n
+    args = dict(x=L["x"], logits=L["logits"], wg=L["wg"], wu=L["wu"], wd=L["wd"], k=cfg.k, e0=cfg.e0,
+                e_local=cfg.el, mode=None if mode in ("bf16", "fp32") else mode)
+    y, _ = oracle.forward(**args)
+    g, _ = oracle.backward(dy=L["dy"], **args)
+    ref = dict(y=y, dx=g["dx"], dlogits=g["dlogits"], dwg=g["dwg"], dwu=g["dwu"], dwd=g["dwd"])
+    errs = {n: oracle.rel_frobenius(got[n], ref[n]) for n in OUTS}
+    print(f"sweep {mode}", {n: f"{v:.2e}" for n, v in errs.items()}, flush=True)
+    for n in OUTS:
+        assert np.all(np.isfinite(got[n])), n
+        assert errs[n] <= TOL[mode], (n, errs[n])
+    for e in np.nonzero(r["counts"] == 0)[0]:
+        for n in ("dwg", "dwu", "dwd"):
+            assert not np.any(got[n][e]), (n, e)
