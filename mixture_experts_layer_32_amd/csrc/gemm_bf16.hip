@@ -195,6 +195,10 @@ __device__ __forceinline__ void mma_step(f32x16 (&acc)[MI][NJ], const bf16x8 (&f
     for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
 }
 
+template <bool AMN, bool BMN, int AST, int ACT, int MI, int NJ, class LA, class LB>
+__device__ __forceinline__ void mainloop_body(f32x16 (&acc)[MI][NJ], char* smem, LA& la, LB& lb, int nk, int am0,
+                                              const int (&bn)[NJ], bool skip_a);
+
 // Row block i of the wave's A rows starts at am0 + AST i. Only the first NA row blocks run (NA < MI:
 // the rows of the others are known to be past the segment; their accumulators stay zero); NA = 0
 // runs all MI, NA = -1 none (the wave still loads its share of the operand tiles).
@@ -238,6 +242,15 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[MI][NJ], char* smem, LA& 
     wait_vm<0>();
   }
   block_sync();
+  mainloop_body<AMN, BMN, AST, ACT>(acc, smem, la, lb, nk, am0, bn, skip_a);
+}
+
+// The K-tile loop once K-tiles 0 and 1 are issued (and K-tile 2's indices prefetched) and K-tile 0
+// is published: ACT active row blocks, A's loads skipped when skip_a.
+template <bool AMN, bool BMN, int AST, int ACT, int MI, int NJ, class LA, class LB>
+__device__ __forceinline__ void mainloop_body(f32x16 (&acc)[MI][NJ], char* smem, LA& la, LB& lb, int nk, int am0,
+                                              const int (&bn)[NJ], bool skip_a) {
+  const int lane = threadIdx.x & 63;
   bf16x8 fa0[MI], fb0[NJ], fa1[MI], fb1[NJ];
   read_frags<AMN, BMN, AST, ACT>(fa0, fb0, smem, 0, am0, bn, lane);
   for (int kt = 0; kt < nk; ++kt) {
@@ -589,6 +602,75 @@ __global__ __launch_bounds__(NTHR8, 1) void k_wgrad_down_bf16(BwdParams p) {
   }
 }
 
+// Persistent tiles with the next tile's first K-tile issued before the current tile's epilogue:
+// the caller issues K-tile 0 of a tile into stage 0 (after the previous main loop's last barrier,
+// before the previous epilogue), and stages that epilogue in bf16 in stage 1. mainloop_pre then
+// waits for every wave's staging reads, issues K-tile 1 into stage 1 and waits for K-tile 0 only,
+// so K-tile 0's latency and the epilogue's stores overlap. ns_prev is the number of stores this wave
+// issued after K-tile 0 (the vector-memory counter completes in order; 0 for a wave's first tile).
+template <int NS, bool AMN, bool BMN, int MI, int NJ, class LA, class LB>
+__device__ __forceinline__ void mainloop_pre(f32x16 (&acc)[MI][NJ], char* smem, LA& la, LB& lb, int nk, int am0,
+                                             const int (&bn)[NJ], bool after_stores) {
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  if (nk <= 0) return;
+  block_sync();   // every wave is done reading its staging area in stage 1
+  if (nk > 1) {
+    la.prologue_prefetch(1);
+    lb.prologue_prefetch(1);
+    la.prologue_issue(smem + STB, 1);
+    lb.prologue_issue(smem + STB + OPB, 1);
+    if (nk > 2) {
+      la.prefetch(2);
+      lb.prefetch(2);
+    }
+    if (after_stores) wait_vm<NS + 2 * LOADS>();
+    else wait_vm<2 * LOADS>();
+  } else {
+    if (after_stores) wait_vm<NS>();
+    else wait_vm<0>();
+  }
+  block_sync();
+  mainloop_body<AMN, BMN, 32, MI>(acc, smem, la, lb, nk, am0, bn, false);
+}
+
+// K-tile 0 of a tile into stage 0 (its row indices first)
+template <class LA, class LB>
+__device__ __forceinline__ void issue_k0(char* smem, LA& la, LB& lb) {
+  la.prologue_prefetch(0);
+  lb.prologue_prefetch(0);
+  la.prologue_issue(smem, 0);
+  lb.prologue_issue(smem + OPB, 0);
+}
+
+// store_wave_block with the rows staged as bf16 in ring stage 1 (4.6 KB per wave for NJ = 2), so
+// that stage 0 can take the next tile's first K-tile meanwhile. The values are rounded to bf16 once,
+// as in store_wave_block. Every row is stored: MI * 32 * 4 NJ / 64 stores per lane.
+template <int MI, int NJ, class OutRow>
+__device__ __forceinline__ void store_wave_block_s1(char* smem, const f32x16 (&acc)[MI][NJ], int lane, OutRow out_row) {
+  constexpr int LDB = 32 * NJ + 8;               // staged row stride (bf16)
+  constexpr int LPR = 4 * NJ, RPP = 64 / LPR;    // lanes per row, rows per pass
+  bf16* st = reinterpret_cast<bf16*>(smem + STB) + wave_id() * 32 * LDB;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        st8(st + (lane & 31) * LDB + 32 * j + acc_n(a, lane),
+            pack4(acc[i][j][4 * a], acc[i][j][4 * a + 1], acc[i][j][4 * a + 2], acc[i][j][4 * a + 3]));
+#pragma unroll
+    for (int s = 0; s < 32 / RPP; ++s) {
+      const int rl = lane / LPR + RPP * s, c0 = (lane % LPR) * 8;
+      st16_nt(out_row(32 * i + rl) + c0, *reinterpret_cast<const uint4*>(st + rl * LDB + c0));
+    }
+  }
+}
+
 // backward: [dW_gate; dW_up][e] (2F x H) = sum over the expert's pairs of [da; db]_r x_t^T
 __global__ __launch_bounds__(NTHR8, 1) void k_wgrad_gateup_bf16(BwdParams p) {
   MOE_SMEM
@@ -596,32 +678,59 @@ __global__ __launch_bounds__(NTHR8, 1) void k_wgrad_gateup_bf16(BwdParams p) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
   const int H = p.H, F = p.F, ntn = H / TILE, tpe = (2 * F / TILE) * ntn;
   const XcdRange xr = xcd_range_split(p.sched + kSchedWgradGateup * kSchedInts);
-  for (int lid = xr.first; lid < xr.end; lid += xr.stride) {
-  const int e = lid / tpe, t = lid - e * tpe, mt = t / ntn, nt = t - mt * ntn;
-  const int seg0 = p.offsets[e], seg_end = p.offsets[e + 1];
-  // A rows: dabT[m][qoff[e] ..], contiguous along the expert's pairs (zero-padded to 32)
+  const bf16* dabt0 = static_cast<const bf16*>(p.dabt);
   KOp la;
-  const bf16* dabt = static_cast<const bf16*>(p.dabt) + p.qoff[e];
-#pragma unroll
-  for (int j = 0; j < LOADS; ++j) {
-    const int m = mt * TILE + KOp::row_of(j);
-    la.p[j] = reinterpret_cast<const char*>(dabt + (size_t)m * p.qc) + 16 * KOp::chunk_of(j);
-  }
   MNOp<GatherRows> lb;
-  lb.rows = GatherRows{reinterpret_cast<const char*>(static_cast<const bf16*>(p.x) + nt * TILE), p.ptok,
-                       (size_t)H * 2, seg0, seg_end, {}};
-  lb.zero = static_cast<const char*>(p.zeros);
-  lb.init(nt * TILE, H);
+  int e = 0, mt = 0, nt = 0, nk = 0;
+  // loaders of tile lid: A rows dabT[m][qoff[e] ..], contiguous along the expert's pairs (zero-padded
+  // to 64); B the expert's gathered x rows
+  auto setup = [&](int lid) {
+    e = lid / tpe;
+    const int t = lid - e * tpe;
+    mt = t / ntn;
+    nt = t - mt * ntn;
+    // scalar loads: after a vector load the compiler would wait for every vector memory operation
+    // in flight before using the value
+    const int seg0 = ld_uniform(p.offsets, e), seg_end = ld_uniform(p.offsets, e + 1);
+    nk = (seg_end - seg0 + KTILE - 1) / KTILE;
+    const bf16* dabt = dabt0 + ld_uniform(p.qoff, e);
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int m = mt * TILE + KOp::row_of(j);
+      la.p[j] = reinterpret_cast<const char*>(dabt + (size_t)m * p.qc) + 16 * KOp::chunk_of(j);
+    }
+    lb.rows = GatherRows{reinterpret_cast<const char*>(static_cast<const bf16*>(p.x) + nt * TILE), p.ptok,
+                         (size_t)H * 2, seg0, seg_end, {}};
+    lb.zero = static_cast<const char*>(p.zeros);
+    lb.init(nt * TILE, H);
+  };
   const int bn[2] = {64 * wn, 64 * wn + 32};
-  f32x16 acc[4][2];
-  mainloop<false, true>(acc, smem, la, lb, (seg_end - seg0 + KTILE - 1) / KTILE, 128 * wm, bn);
-  bf16* __restrict__ dwg = static_cast<bf16*>(p.dwg) + (size_t)e * F * H;
-  bf16* __restrict__ dwu = static_cast<bf16*>(p.dwu) + (size_t)e * F * H;
-  const int mq = mt * TILE + 128 * wm, nq = nt * TILE + 64 * wn;
-  store_wave_block(smem, acc, lane, [&](int m) {
-    const int mm = mq + m;
-    return (mm < F ? dwg + (size_t)mm * H : dwu + (size_t)(mm - F) * H) + nq;
-  }, 64);
+  constexpr int NS = 4 * 32 * 8 / 64;   // epilogue stores per lane (MI = 4, NJ = 2)
+  int lid = xr.first;
+  if (lid >= xr.end) return;
+  setup(lid);
+  if (nk > 0) issue_k0(smem, la, lb);
+  bool after_stores = false;
+  for (; lid < xr.end; lid += xr.stride) {
+    f32x16 acc[4][2];
+    mainloop_pre<NS, false, true>(acc, smem, la, lb, nk, 128 * wm, bn, after_stores);
+    const int ce = e, cmt = mt, cnt = nt;
+    // every wave is past the main loop's last barrier (or the tile had no K-tile): stage 0 is free
+    after_stores = false;
+    if (lid + xr.stride < xr.end) {
+      setup(lid + xr.stride);
+      if (nk > 0) {
+        issue_k0(smem, la, lb);
+        after_stores = true;
+      }
+    }
+    bf16* __restrict__ dwg = static_cast<bf16*>(p.dwg) + (size_t)ce * F * H;
+    bf16* __restrict__ dwu = static_cast<bf16*>(p.dwu) + (size_t)ce * F * H;
+    const int mq = cmt * TILE + 128 * wm, nq = cnt * TILE + 64 * wn;
+    store_wave_block_s1(smem, acc, lane, [&](int m) {
+      const int mm = mq + m;
+      return (mm < F ? dwg + (size_t)mm * H : dwu + (size_t)(mm - F) * H) + nq;
+    });
   }
 }
 
