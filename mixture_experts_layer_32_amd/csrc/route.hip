@@ -9,8 +9,8 @@
 // sequence of fp32 operations, so runs are bitwise reproducible.
 //
 // Kernels (one stream, no host round trip):
-//   k_route_topk4    k <= 8: 64 tokens per block, 4 lanes per token; each lane keeps a sorted list
-//                    of its quarter of the experts (value desc, index asc), two shuffle steps merge
+//   k_route_topk     k <= 8: 64 tokens per block, 8 lanes per token; each lane keeps a sorted list
+//                    of its eighth of the experts (value desc, index asc), three shuffle steps merge
 //                    the lists.
 //   k_route_topk_wave  k > 8: one wavefront per token, k rounds of a wave-wide argmax.
 //                    Both write, per block and local expert, a 64-bit mask of the tokens that chose it.
@@ -69,13 +69,16 @@ __device__ __forceinline__ void topk_insert(float (&tv)[KMAX], int (&ti)[KMAX], 
   }
 }
 
-// k <= 8: 64 tokens per block, 4 lanes per token. Lane q keeps the best KMAX of experts q, q+4, q+8, ...;
-// two butterfly steps merge the four lists, after which every lane of the token holds its top k.
-template <int KMAX>
-__global__ __launch_bounds__(256) void k_route_topk4(RouteParams p) {
+// k <= 8: 64 tokens per block, LPT lanes per token. Lane q keeps the best KMAX of experts q, q+LPT,
+// q+2 LPT, ...; log2(LPT) butterfly steps merge the lists, after which every lane of the token holds
+// its top k. LPT = 8 took 20 us against 23 us with 4 at T = 16384, E = 128; LPT = 16 sent the
+// compiler into a build of more than 15 minutes.
+template <int KMAX, int LPT>
+__global__ __launch_bounds__(64 * LPT) void k_route_topk(RouteParams p) {
+  constexpr int NT = 64 * LPT;
   __shared__ unsigned long long mask[kMaxExperts];
-  const int tid = threadIdx.x, tl = tid >> 2, q = tid & 3;
-  for (int e = tid; e < p.El; e += 256) mask[e] = 0ull;
+  const int tid = threadIdx.x, tl = tid / LPT, q = tid % LPT;
+  for (int e = tid; e < p.El; e += NT) mask[e] = 0ull;
   __syncthreads();
   const int64_t t = (int64_t)blockIdx.x * kRouteTokens + tl;
   if (t < p.T) {
@@ -88,11 +91,11 @@ __global__ __launch_bounds__(256) void k_route_topk4(RouteParams p) {
     }
     const float* row = p.logits + t * p.E;
 #pragma unroll 1
-    for (int e = q; e < p.E; e += 4) topk_insert<KMAX>(tv, ti, row[e], e);
+    for (int e = q; e < p.E; e += LPT) topk_insert<KMAX>(tv, ti, row[e], e);
     // merge with the partner lane's list: the better of tv[j] and the partner's [KMAX-1-j]
     // leaves the top KMAX of both lists as a bitonic sequence, which three half-cleaner stages sort
 #pragma unroll
-    for (int step = 1; step <= 2; step <<= 1) {
+    for (int step = 1; step < LPT; step <<= 1) {
       float ov[KMAX];
       int oi[KMAX];
 #pragma unroll
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(256) void k_route_topk4(RouteParams p) {
     }
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
-      if (j < p.k && (j & 3) == q) {
+      if (j < p.k && (j & (LPT - 1)) == q) {
         p.idx[t * p.k + j] = ti[j];
         p.weight[t * p.k + j] = z[j] / sum;
         const int el = ti[j] - p.e0;
@@ -138,7 +141,7 @@ __global__ __launch_bounds__(256) void k_route_topk4(RouteParams p) {
     }
   }
   __syncthreads();
-  for (int e = tid; e < p.El; e += 256) {
+  for (int e = tid; e < p.El; e += NT) {
     const size_t qq = (size_t)blockIdx.x * p.El + e;
     p.blk_mask[qq] = mask[e];
     p.blk_count[qq] = __popcll(mask[e]);
@@ -278,7 +281,7 @@ hipError_t launch_route(const RouteParams& p, hipStream_t s) {
   hipError_t err;
   prof_mark_begin("route_topk", s);
   const int per_lane = (p.E + 63) / 64;
-  if (p.k <= 8) k_route_topk4<8><<<p.nblk, 256, 0, s>>>(p);
+  if (p.k <= 8) k_route_topk<8, 8><<<p.nblk, 64 * 8, 0, s>>>(p);
   else if (per_lane <= 1) k_route_topk_wave<1><<<p.nblk, 256, 0, s>>>(p);
   else if (per_lane <= 2) k_route_topk_wave<2><<<p.nblk, 256, 0, s>>>(p);
   else if (per_lane <= 4) k_route_topk_wave<4><<<p.nblk, 256, 0, s>>>(p);
