@@ -606,8 +606,9 @@ __global__ __launch_bounds__(NTHR8, 1) void k_wgrad_down_bf16(BwdParams p) {
 // the caller issues K-tile 0 of a tile into stage 0 (after the previous main loop's last barrier,
 // before the previous epilogue), and stages that epilogue in bf16 in stage 1. mainloop_pre then
 // waits for every wave's staging reads, issues K-tile 1 into stage 1 and waits for K-tile 0 only,
-// so K-tile 0's latency and the epilogue's stores overlap. ns_prev is the number of stores this wave
-// issued after K-tile 0 (the vector-memory counter completes in order; 0 for a wave's first tile).
+// so K-tile 0's latency and the epilogue's stores overlap. after_stores says whether this wave
+// issued its NS epilogue stores after K-tile 0 (false for its first tile): the vector-memory counter
+// completes in order, so K-tile 0 has landed once at most NS stores and K-tile 1's loads remain.
 template <int NS, bool AMN, bool BMN, int MI, int NJ, class LA, class LB>
 __device__ __forceinline__ void mainloop_pre(f32x16 (&acc)[MI][NJ], char* smem, LA& la, LB& lb, int nk, int am0,
                                              const int (&bn)[NJ], bool after_stores) {
