@@ -170,8 +170,8 @@ def router_bench(cfg, layer, x, grads, steps):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="qwen3_30b_a3b")
     ap.add_argument("--mode", default=None, help="fp32, bf16, mxfp8, fp8_bwd or fp8 (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

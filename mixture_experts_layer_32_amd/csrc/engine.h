@@ -220,17 +220,30 @@ __device__ __forceinline__ void store_wave_block(char* smem, const f32x16 (&acc)
 // dst(c) is the copy's row for staged column c, at the pair column of staged row 0 (null: skip).
 // Four lanes cover one column, 8 consecutive pair rows each: one 16-byte store, 64 contiguous bytes
 // per column, 16 columns per instruction. (One lane per column, with conflict-free LDS reads but 64
-// lines per store instruction, made the dgrad of h 9 % slower.)
+// lines per store instruction, made the dgrad of h 9 % slower.) The row stride is 4 banks mod 64,
+// so rows 16 apart share banks: lane groups q = 2, 3 (rows 16-31) read their 8 rows starting from
+// the fifth, which puts the four groups of a read on bank offsets 0, 32, 16, 48 (no conflicts; the
+// in-order form conflicted 2-way on every read).
 template <int NJ = 4, class Dst>
 __device__ __forceinline__ void store_transposed(const float* slab, int lane, int ncol, Dst dst) {
+  static_assert(Stage<NJ>::LD % 64 == 4, "the read order assumes a row stride of 4 banks mod 64");
+  const int rot = 4 * ((lane >> 1) & 1);
   for (int cb = 0; cb < ncol; cb += 16) {
     const int c = cb + (lane >> 2), g8 = 8 * (lane & 3);
     bf16* o = dst(c);
     if (o) {
-      float v[8];
+      // r[t] = row g8 + ((t + rot) & 7): two base addresses with constant offsets
+      const float* lo = slab + (g8 + rot) * Stage<NJ>::LD + c;
+      const float* hi = slab + (g8 + 4 - rot) * Stage<NJ>::LD + c;
+      float r[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) v[t] = slab[(g8 + t) * Stage<NJ>::LD + c];
-      st16(o + g8, pack8(v));   // 64 bytes per column: ordinary store (non-temporal partial lines are slow)
+      for (int t = 0; t < 4; ++t) {
+        r[t] = lo[t * Stage<NJ>::LD];
+        r[t + 4] = hi[t * Stage<NJ>::LD];
+      }
+      const uint4 w = pack8(r);   // rotated groups hold rows 4-7 in the low half: swap the halves
+      const uint4 out = rot ? make_uint4(w.z, w.w, w.x, w.y) : w;
+      st16(o + g8, out);   // 64 bytes per column: ordinary store (non-temporal partial lines are slow)
     }
   }
 }
