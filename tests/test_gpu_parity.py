@@ -177,3 +177,27 @@ def test_tile_boundary_counts(mode):
     assert not np.any(got["dlogits"])
     for n in ("dwg", "dwu", "dwd"):
         assert not np.any(got[n][TILE_COUNTS.index(0)]), n
+
+
+def test_wgrad_xcd_split_balances_a_skewed_load():
+    """The weight-gradient tile lists are cut into 8 per-XCD ranges of equal estimated cost when equal
+    tile counts would be out of balance (a Zipf-like skew here). White-box: the ranges sit in the
+    backward workspace's scheduler slots 2 (down) and 3 (gate/up), 9 boundaries each."""
+    H, F, E, k = 1024, 512, 32, 2
+    cfg, L = inputs.custom_layer(T=3000, H=H, F=F, E=E, k=k, zipf_s=2.5, seed=77)
+    print("case wgrad_xcd_split zipf_s=2.5", flush=True)
+    got = run_layer(cfg, L, "bf16", keep_layer=True)
+    layer = got["_layer"]
+    ws = layer.ws[:8 * 16 * 4].cpu().numpy().view(np.int32).reshape(8, 16)
+    counts = got["routing"]["counts"].astype(np.int64)
+    u = -(-counts // 64) + 2                                    # K-tiles per tile, plus its fixed cost
+    for slot, tpe in ((2, (H // 256) * -(-F // 256)), (3, (2 * F // 256) * (H // 256))):
+        b = ws[slot, :9]
+        assert b[0] == 0 and b[8] == E * tpe and np.all(np.diff(b) >= 0), b
+        tile_cost = np.repeat(u, tpe)
+        cost = np.array([tile_cost[b[x]:b[x + 1]].sum() for x in range(8)])
+        per = -(-E * tpe // 8)
+        even = np.array([tile_cost[x * per:(x + 1) * per].sum() for x in range(8)])
+        assert even.max() > 1.1 * even.mean()                   # the skew defeats equal counts
+        assert cost.max() <= cost.sum() / 8 + tile_cost.max(), (cost, b)
+        assert cost.max() < even.max()
