@@ -251,43 +251,26 @@ __global__ __launch_bounds__(kThreads, 2) void k_wgrad_gateup(BwdParams p) {
     }
 }
 
-// One wavefront per token, 4 tokens per block. Lane j < k holds slot j: its pair position,
-// weight, expert and g = the sum of its partials. Slot values reach every lane through readlane, so
-// the token's k source rows are addressed from scalar registers.
+// One wavefront per part of a token's row (128 chunks of 16 bytes), 4 parts per block, as in the
+// forward combine; part 0 also writes the token's dlogits. Lane j < k holds slot j: its pair
+// position, weight, expert and g = the sum of its partials. Slot values reach every lane through
+// readlane, so the token's k source rows are addressed from scalar registers.
 template <class T>
 __global__ __launch_bounds__(256) void k_combine_bwd(BwdParams p) {
   constexpr int VEC = Elem<T>::VEC;
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nch = p.H / VEC, nparts = (nch + 127) / 128;
+  const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t t = u / nparts;
+  const int part = (int)(u - t * nparts);
   if (t >= p.T) return;   // the whole wave leaves
   const int k = p.k, H = p.H;
-  int pp = -1, ex = -1;
-  float w = 0.f, g = 0.f;
-  if (lane < k) {
-    pp = p.pair_pos[t * k + lane];
-    w = p.weight[t * k + lane];
-    ex = p.idx[t * k + lane];
-    if (pp >= 0)
-      for (int q = 0; q < p.np; ++q) g += p.gpart[(size_t)q * p.rows + pp];
-  }
-  // gbar = sum_j w_j g_j, in slot order
-  const float wg = w * g;
-  float gbar = 0.f;
-  for (int j = 0; j < k; ++j) gbar += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wg), j));
-  const float val = w * (g - gbar);   // dlogits of slot j's expert (lane j)
-  for (int e = lane; e < p.E; e += 64) {
-    float v = 0.f;
-    for (int j = 0; j < k; ++j)
-      if (__builtin_amdgcn_readlane(ex, j) == e) v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, val), j));
-    p.dlogits[t * p.E + e] = v;
-  }
+  const int pp = lane < k ? p.pair_pos[t * k + lane] : -1;
   // dx_t = sum over the local slots of dX' rows, fp32 in slot order; 8 slot rows in flight per chunk
   const T* __restrict__ src = static_cast<const T*>(p.dxp);
   T* __restrict__ out = static_cast<T*>(p.dx);
-  const int nch = H / VEC;
-  // two chunks per lane at a time (c0 and c0 + 64, the second only if it exists): 16 slot rows in
-  // flight
-  for (int c0 = lane; c0 < nch; c0 += 128) {
+  // two chunks per lane (c0 and c0 + 64, the second only if it exists): 16 slot rows in flight
+  for (int c0 = lane + 128 * part; c0 < nch; c0 += 128 * nparts) {
     float acc[2][VEC];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -321,6 +304,27 @@ __global__ __launch_bounds__(256) void k_combine_bwd(BwdParams p) {
       if (c0 + 64 * h < nch) st16(out + (size_t)t * H + (size_t)(c0 + 64 * h) * VEC, res);
     }
   }
+  // dlogits of the token, by part 0, after its share of dx (the other parts skip the partials)
+  if (part != 0) return;
+  int ex = -1;
+  float w = 0.f, g = 0.f;
+  if (lane < k) {
+    w = p.weight[t * k + lane];
+    ex = p.idx[t * k + lane];
+    if (pp >= 0)
+      for (int q = 0; q < p.np; ++q) g += p.gpart[(size_t)q * p.rows + pp];
+  }
+  // gbar = sum_j w_j g_j, in slot order
+  const float wg = w * g;
+  float gbar = 0.f;
+  for (int j = 0; j < k; ++j) gbar += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wg), j));
+  const float val = w * (g - gbar);   // dlogits of slot j's expert (lane j)
+  for (int e = lane; e < p.E; e += 64) {
+    float v = 0.f;
+    for (int j = 0; j < k; ++j)
+      if (__builtin_amdgcn_readlane(ex, j) == e) v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, val), j));
+    p.dlogits[t * p.E + e] = v;
+  }
 }
 
 template <class T>
@@ -353,7 +357,8 @@ hipError_t launch_backward(const BwdParams& p, int grid, hipStream_t s) {
 template <class T>
 hipError_t launch_combine_bwd(const BwdParams& p, hipStream_t s) {
   prof_mark_begin("combine_bwd", s);
-  k_combine_bwd<T><<<(unsigned)((p.T + 3) / 4), 256, 0, s>>>(p);
+  const int64_t nparts = (p.H / Elem<T>::VEC + 127) / 128;
+  k_combine_bwd<T><<<(unsigned)((p.T * nparts + 3) / 4), 256, 0, s>>>(p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   prof_mark_end(s);

@@ -116,21 +116,23 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(FwdParams p) {
 }
 
 // out[t] = sum over j with pair_pos[t*k+j] >= 0 of src[pair_pos[t*k+j]]; fp32 accumulation in
-// slot order. A token with no local slot gets zeros. One wavefront per token, 4 tokens per block;
-// the slots' pair positions reach every lane through readlane, and each chunk keeps 8 slot rows
-// in flight.
+// slot order. A token with no local slot gets zeros. One wavefront per part of a token's row (128
+// chunks of 16 bytes: 2048 bf16), 4 parts per block; the slots' pair positions reach every lane
+// through readlane, and each chunk keeps 8 slot rows in flight. (One wavefront per whole token left
+// the last of its ~3 rounds of waves per CU mostly empty.)
 template <class T>
 __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ src, const int* __restrict__ pair_pos,
                                                  T* __restrict__ out, int64_t ntok, int k, int H) {
   constexpr int VEC = Elem<T>::VEC;
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nch = H / VEC, nparts = (nch + 127) / 128;
+  const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t t = u / nparts;
+  const int part = (int)(u - t * nparts);
   if (t >= ntok) return;   // the whole wave leaves
   const int pp = lane < k ? pair_pos[t * k + lane] : -1;
-  const int nch = H / VEC;
-  // two chunks per lane at a time (c0 and c0 + 64, the second only if it exists): 16 slot rows in
-  // flight
-  for (int c0 = lane; c0 < nch; c0 += 128) {
+  // two chunks per lane (c0 and c0 + 64, the second only if it exists): 16 slot rows in flight
+  for (int c0 = lane + 128 * part; c0 < nch; c0 += 128 * nparts) {
     float acc[2][VEC];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -184,8 +186,9 @@ template <class T>
 hipError_t launch_combine(const void* src, const int* pair_pos, void* out, int64_t T_, int k, int H,
                           hipStream_t s) {
   prof_mark_begin("combine", s);
-  k_combine<T><<<(unsigned)((T_ + 3) / 4), 256, 0, s>>>(static_cast<const T*>(src), pair_pos, static_cast<T*>(out), T_, k,
-                                                      H);
+  const int64_t nparts = (H / Elem<T>::VEC + 127) / 128;
+  k_combine<T><<<(unsigned)((T_ * nparts + 3) / 4), 256, 0, s>>>(static_cast<const T*>(src), pair_pos,
+                                                                 static_cast<T*>(out), T_, k, H);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   prof_mark_end(s);
