@@ -193,6 +193,14 @@ __device__ __forceinline__ void mma_step(f32x16 (&acc)[MI][NJ], const bf16x8 (&f
   for (int i = 0; i < NA; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+  // issue order: one MFMA, then one of the next step's LDS fragment reads, and so on, so that the
+  // reads spread over the step instead of reaching the LDS port in one burst (the weight gradients
+  // and the dgrad measured 2-4 % faster than with the compiler's own grouping)
+#pragma unroll
+  for (int q = 0; q < NA * NJ; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
 }
 
 template <bool AMN, bool BMN, int AST, int ACT, int MI, int NJ, class LA, class LB>

@@ -97,7 +97,9 @@ __device__ __forceinline__ void read_frags_mx(Frags& f, const char* st, int s, i
 }
 
 // MFMAs of row blocks i0, i0+1 (B fragment first: each accumulator block holds the transposed
-// 32x32 block, as in the bf16 engine)
+// 32x32 block, as in the bf16 engine). Each MFMA is followed in issue order by RPM of the LDS
+// fragment reads around it, so that one wave per SIMD keeps its matrix core fed while it reads.
+template <int RPM = 1>
 __device__ __forceinline__ void mma_half(f32x16 (&acc)[4][4], const Frags& f, int i0, int sela, int selb) {
   const unsigned sa[4] = {f.sa.x, f.sa.y, f.sa.z, f.sa.w};
   const unsigned sb[4] = {f.sb.x, f.sb.y, f.sb.z, f.sb.w};
@@ -110,6 +112,11 @@ __device__ __forceinline__ void mma_half(f32x16 (&acc)[4][4], const Frags& f, in
       const int bs = (int)((sb[j] >> selb) & 0xffu);
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], 0, 0, 0, bs, 0, as);
     }
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
   }
 }
 
@@ -145,7 +152,7 @@ __device__ __forceinline__ void ktile_mx(f32x16 (&acc)[4][4], char* smem, const 
   block_sync();
   if (kt + STAGES < nk) issue_tile(cur, la, lb, sa, sb, kt + STAGES);
   read_frags_mx(f0, smem + ((kt + 1) % STAGES) * STB_MX, 0, am0, bn, wm, wn, lane);
-  mma_half(acc, f1, 2, 16 + h8, 16 + h8);
+  mma_half<2>(acc, f1, 2, 16 + h8, 16 + h8);
 }
 
 // nk K-tiles of 128 elements (every scale base a multiple of 4 scale columns).
