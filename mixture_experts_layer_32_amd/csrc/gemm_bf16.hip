@@ -165,10 +165,10 @@ struct GatherRows {
 // am0 + 32i of the A tile; B fragments from columns bn[j]. A K-tile is four 16-deep steps; each step's fragments are read
 // while the previous step's MFMAs run. The ring holds two K-tiles: K-tile kt+1 lands while kt is
 // multiplied. After the last fragments of K-tile kt are read, the wave waits for K-tile kt+1, the
-// barrier publishes it and frees kt's stage, A's part of K-tile kt+2 is issued into that stage,
-// and the first fragments of kt+1 are read while the last MFMAs of kt run; B's part of K-tile
-// kt+2 follows those MFMAs. On return all LDS reads are done (LDS
-// may be reused).
+// barrier publishes it and frees kt's stage, A's part of K-tile kt+2 is issued into that stage
+// (with B's part when B is K-major), and the first fragments of kt+1 are read while the last MFMAs
+// of kt run; an MN-major B's part of K-tile kt+2 follows those MFMAs. On return all LDS reads are
+// done (LDS may be reused).
 __device__ __forceinline__ bf16x8 frag_k(const char* tile, int row0, int ks, int lane) {
   return *reinterpret_cast<const bf16x8*>(KOp::at(tile, row0 + (lane & 31), 2 * ks + (lane >> 5)));
 }
@@ -275,13 +275,18 @@ __device__ __forceinline__ void mainloop_body(f32x16 (&acc)[MI][NJ], char* smem,
       if (kt + 2 < nk) {
         if (!skip_a) la.issue(cur, kt + 2);
         if (kt + 3 < nk) la.prefetch(kt + 3);
+        if (!BMN) {
+          lb.issue(cur + OPB, kt + 2);
+          if (kt + 3 < nk) lb.prefetch(kt + 3);
+        }
       }
       read_frags<AMN, BMN, AST, ACT>(fa0, fb0, smem + ((kt + 1) & 1) * STB, 0, am0, bn, lane);
     }
     mma_step<ACT>(acc, fa1, fb1);
-    // B's loads of K-tile kt+2 go out after the last MFMA step: one burst of all loads right after
-    // the barrier stalled the waves' MFMA issue (measured 2-6 % slower per GEMM with 4 waves)
-    if (kt + 2 < nk) {
+    // A K-major B's loads of K-tile kt+2 go out with A's, right after the barrier; an MN-major B's
+    // after the last MFMA step. Each order measured 3-5 % faster on the GEMMs it is used for than
+    // the other (MN-major B fragments come through the slower transposing LDS read).
+    if (BMN && kt + 2 < nk) {
       lb.issue(cur + OPB, kt + 2);
       if (kt + 3 < nk) lb.prefetch(kt + 3);
     }
