@@ -343,12 +343,18 @@ __global__ __launch_bounds__(NTHR8, 1) void k_gateup_bf16(FwdParams p) {
       const bf16* wrow = row < 128 ? wg + ((size_t)e * F + nt * 128 + row) * H : wu + ((size_t)e * F + nt * 128 + row - 128) * H;
       lb.p[j] = reinterpret_cast<const char*>(wrow) + 16 * c;
     }
-    float wrow[2];   // routing weight of tile row 32 wm + 128 i + (lane & 31)
+    // routing weight of tile row 32 wm + 128 i + (lane & 31): the slot index is loaded before the
+    // main loop, the weight it selects after it, so that no dependent pair of loads sits ahead of
+    // the first K-tile's loads (the MXFP8 gate/up GEMM measured 0.8 % faster; bf16 unchanged)
+    int prow[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) wrow[i] = p.weight[p.perm[min(r0 + 32 * wm + 128 * i + (lane & 31), seg_end - 1)]];
+    for (int i = 0; i < 2; ++i) prow[i] = p.perm[min(r0 + 32 * wm + 128 * i + (lane & 31), seg_end - 1)];
     f32x16 acc[2][4];
     mainloop_rows<false, false, 128>(acc, smem, la, lb, H / KTILE, 32 * wm, bn, seg_end - r0 <= 128);
     ts.fetch();
+    float wrow[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) wrow[i] = p.weight[prow[i]];
     // staged columns 0..63 hold gate columns f0.., 64..127 the matching up columns. After the row
     // pass the gate columns hold hw (zero on rows past the segment), which is then written to the
     // pair-contiguous copy hwT[f][qoff[e] + pair - offsets[e]] as well.
@@ -455,9 +461,9 @@ __global__ __launch_bounds__(NTHR8, 1) void k_bwd_dh_bf16(BwdParams p) {
     lb.rows = WeightRows{wbase, wbase, (size_t)F * 2, H};
     lb.zero = static_cast<const char*>(p.zeros);
     lb.init(nt * TILE, F);
-    float wrow[4];   // routing weight of the wave's row 32i + (lane & 31)
+    int prow[4];   // slot of the wave's row 32i + (lane & 31); its routing weight is loaded after the main loop
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wrow[i] = p.weight[p.perm[min(r0 + 128 * wm + acc_m(i, lane), seg_end - 1)]];
+    for (int i = 0; i < 4; ++i) prow[i] = p.perm[min(r0 + 128 * wm + acc_m(i, lane), seg_end - 1)];
     f32x16 acc[4][2];
     // An expert's last tile often holds a few rows only: each wave multiplies just its 32-row blocks
     // that reach into the segment (none, 1, 2 or all 4), and with at most 128 valid rows the waves
@@ -470,6 +476,9 @@ __global__ __launch_bounds__(NTHR8, 1) void k_bwd_dh_bf16(BwdParams p) {
     else if (valid <= 64) mainloop<false, true, 32, 2>(acc, smem, la, lb, H / KTILE, 128 * wm, bn, skip_hi);
     else mainloop<false, true, 32, 0>(acc, smem, la, lb, H / KTILE, 128 * wm, bn, skip_hi);
     ts.fetch();
+    float wrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wrow[i] = p.weight[prow[i]];
     // u = dH' staged per 32 rows; each row's 64 columns are read by 8 lanes, 8 columns each. The
     // row pass overwrites u with da and fills a second slab with db (zero on rows or columns past
     // the segment); both then go to the pair-contiguous copy dabT. The wave's partial of g over its

@@ -331,11 +331,14 @@ __global__ __launch_bounds__(NTHR, 1) void k_gateup_mx(FwdParams p) {
     const SOp sa{p.xs + (size_t)p.ptok[min(r0 + arow_s, seg_end - 1)] * hs, 0};
     const SOp sb{brow_s < 128 ? p.wgs + ((size_t)e * F + nt * 128 + brow_s) * hs
                               : p.wus + ((size_t)e * F + nt * 128 + brow_s - 128) * hs, 0};
-    float wrow[4];
+    int prow[4];   // slots of the wave's rows; their routing weights are loaded after the main loop
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wrow[i] = p.weight[p.perm[min(r0 + 128 * wm + acc_m(i, lane), seg_end - 1)]];
+    for (int i = 0; i < 4; ++i) prow[i] = p.perm[min(r0 + 128 * wm + acc_m(i, lane), seg_end - 1)];
     f32x16 acc[4][4];
     mainloop_mx(acc, smem, la, lb, sa, sb, H / KTILE, 128 * wm, bn, wm, wn);
+    float wrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wrow[i] = p.weight[prow[i]];
     float* slab = wave_slab(smem);
     const int f0 = nt * 128 + 64 * wn;
     const int qend = p.qoff[e + 1];
@@ -559,11 +562,14 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_dh_mx(BwdParams p) {
     }
     const SOp sa{p.dys + (size_t)p.ptok[min(r0 + row_s, seg_end - 1)] * hs, 0};
     const SOp sb{p.wdts + ((size_t)e * F + min(nt * TILE + row_s, F - 1)) * hs, 0};
-    float wrow[4];
+    int prow[4];   // slots of the wave's rows; their routing weights are loaded after the main loop
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wrow[i] = p.weight[p.perm[min(r0 + 128 * wm + acc_m(i, lane), seg_end - 1)]];
+    for (int i = 0; i < 4; ++i) prow[i] = p.perm[min(r0 + 128 * wm + acc_m(i, lane), seg_end - 1)];
     f32x16 acc[4][4];
     mainloop_mx(acc, smem, la, lb, sa, sb, H / KTILE, 128 * wm, bn, wm, wn);
+    float wrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wrow[i] = p.weight[prow[i]];
     float* slab = wave_slab(smem);
     float* slab2 = slab + 4 * SLAB;
     const int fq = nt * TILE + 128 * wn;
