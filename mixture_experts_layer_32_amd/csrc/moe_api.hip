@@ -62,7 +62,9 @@ Layout make_layout(const moe_desc& d) {
   L.zeros = take(kZeroBytes);
   L.qoff = take((El + 1) * 4);
   L.ab = take(rows * 2 * F * L.elem);
-  L.hw = take(L.mx ? 0 : rows * F * L.elem);
+  // w*h row-major: the forward's down GEMM reads it; only the fp32 engine's backward does too, so it
+  // stays in `saved` in that mode alone (bf16 modes: forward workspace, hw16 below)
+  L.hw = take(d.mode == MOE_MODE_FP32 ? rows * F * 4 : 0);
   L.hwt = take(L.mx ? qc * F : qc * F * 2);      // MX: E4M3 bytes along the pairs
   L.hwts = take(L.mx ? qc / 32 * F : 0);
   L.sv_wdtq = take(mxf ? El * F * H : 0);
@@ -88,7 +90,7 @@ Layout make_layout(const moe_desc& d) {
   L.wds = take(mxf ? El * H * F / 32 : 0);
   L.hwq = take(mxf ? rows * F : 0);
   L.hws = take(mxf ? rows * F / 32 : 0);
-  L.hw16 = take(f8b ? rows * F * 2 : 0);
+  L.hw16 = take(d.mode == MOE_MODE_BF16 || f8b ? rows * F * 2 : 0);
   L.fwd_total = off;
 
   off = 0;
@@ -368,6 +370,7 @@ moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits, const 
     if ((e = launch_combine<float>(fp.o, fp.pair_pos, y, d->T, d->topk, d->H, s)) != hipSuccess)
       return hip_fail(e, "combine launch");
   } else if (d->mode == MOE_MODE_BF16) {
+    fp.hw = w + L.hw16;
     if ((e = launch_forward_gemms_bf16(fp, persistent_grid(1), s)) != hipSuccess)
       return hip_fail(e, "forward GEMM launch");
     if ((e = launch_combine<bf16>(fp.o, fp.pair_pos, y, d->T, d->topk, d->H, s)) != hipSuccess)

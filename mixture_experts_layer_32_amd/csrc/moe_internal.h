@@ -36,7 +36,7 @@ struct Layout {
   // MXFP8: the weights quantised along their other axis by the forward, for the backward (in
   // saved); FP8_BWD: the backward quantises them into its workspace (wdtq.. below)
   size_t sv_wdtq, sv_wdts, sv_wgutq, sv_wguts;
-  // forward workspace (MXFP8: quantised operands; FP8_BWD: the bf16 hw)
+  // forward workspace (MXFP8: quantised operands; BF16 and FP8_BWD: the bf16 hw)
   size_t sched_f, blk_mask, blk_count, blk_prefix, o, xq, xs, wgq, wgs, wuq, wus, wdq, wds, hwq, hws, hw16, fwd_total;
   // backward workspace (MX: quantised operands)
   size_t sched_b, dab, gpart, dxp, dabt, dyq, dys, wdtq, wdts, wgutq, wguts, dytq, dyts, xtq, xts, dabq, dabs, dabtq, dabts,

@@ -6,6 +6,9 @@ from mixture_experts_layer_32_amd.layer import MoELayer
 
 # relative Frobenius error per output tensor; the MX modes are judged against the MX-emulating oracle
 TOL = {"fp32": 1e-5, "bf16": 1e-2, "mxfp8": 5e-2, "fp8_bwd": 5e-2, "fp8": 5e-2}
+# per-row bound on y, dx and dlogits in the full-size checks (a fault confined to some tiles gives
+# rows with errors of order 1)
+ROW_TOL = {"fp32": 1e-4, "bf16": 5e-2, "mxfp8": 0.25, "fp8_bwd": 0.25, "fp8": 0.25}
 OUTS = ("y", "dx", "dlogits", "dwg", "dwu", "dwd")
 
 

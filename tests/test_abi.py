@@ -175,3 +175,23 @@ def test_router_sizes_cover_the_partials(T, H, E):
     assert fwd % 256 == 0 and bwd % 256 == 0
     assert fwd >= T * Ep * 4                        # at least one slice of fp32 partial logits
     assert bwd >= 1024 + T * Ep * 2 + E * H * 4     # zero page, bf16 dlogits, at least one dW_r slice
+
+
+def test_layer_rejects_mismatched_tensors_before_the_library():
+    """layer.py checks device, dtype, shape and contiguity of every tensor it hands to the C ABI,
+    which receives bare pointers (a host pointer or a wrong-sized buffer would reach the kernels)."""
+    import torch
+    from mixture_experts_layer_32_amd.layer import _expect
+    cpu = torch.device("cpu")
+    ok = torch.zeros(4, 8, dtype=torch.bfloat16)
+    _expect(ok, "x", (4, 8), torch.bfloat16, cpu)
+    with pytest.raises(ValueError, match="dtype"):
+        _expect(ok.float(), "x", (4, 8), torch.bfloat16, cpu)
+    with pytest.raises(ValueError, match="shape"):
+        _expect(ok, "x", (4, 16), torch.bfloat16, cpu)
+    with pytest.raises(ValueError, match="contiguous"):
+        _expect(torch.zeros(8, 4, dtype=torch.bfloat16).t(), "x", (4, 8), torch.bfloat16, cpu)
+    with pytest.raises(ValueError, match="tensor on"):
+        _expect(ok, "x", (4, 8), torch.bfloat16, torch.device("cuda", 0))
+    with pytest.raises(ValueError, match="torch.Tensor"):
+        _expect(12345, "x", (4, 8), torch.bfloat16, cpu)

@@ -6,8 +6,11 @@ Bar:
    bit-exact E4M3 bytes and e8m0 scale bytes, against oracle/mx.py on the same bf16 input.
  * Routing: bit-exact, as in every mode.
  * y, dx, dlogits, dW_gate, dW_up, dW_down: relative Frobenius error within 5e-2 against the oracle
-   run in the same mode (every GEMM operand quantised at the same points). The error against the
-   exact oracle is printed for information.
+   run in the same mode (every GEMM operand quantised at the same points).
+ * The same outputs against the exact (unquantised) float64 oracle: within EXACT_TOL. MXFP8 itself
+   moves every output 6-8 % away from exact arithmetic (blockwise FP8 6.5-7 %, FP8_BWD's backward
+   4-7 %), so these modes do not meet 5e-2 against exact arithmetic; the bound is there to catch a
+   rounding or scale-rule error that the GPU and the MX-emulating oracle would share.
  * Experts that receive no tokens: weight gradients exactly zero.
 """
 import numpy as np
@@ -19,6 +22,10 @@ from mixture_experts_layer_32_amd import binding, inputs
 from gpu_util import OUTS, TOL, run_layer
 
 pytestmark = pytest.mark.gpu
+
+# relative Frobenius error against the exact float64 oracle (measured: MXFP8 6.2-8.3e-2, blockwise
+# FP8 5.3-7.0e-2, FP8_BWD 3.0-6.9e-2 over the small layers below)
+EXACT_TOL = {"mxfp8": 0.095, "fp8": 0.09, "fp8_bwd": 0.09}
 
 
 def _e4m3_bytes(el):
@@ -179,6 +186,7 @@ def test_small_layer_parity_mx(cfg, L, mode):
           "vs exact", {n: f"{v:.2e}" for n, v in info.items()}, flush=True)
     for n in OUTS:
         assert errs[n] <= TOL[mode], (n, errs[n])
+        assert info[n] <= EXACT_TOL[mode], (n, "vs exact", info[n])
         assert np.all(np.isfinite(got[n])), n
     for e in np.nonzero(r["counts"] == 0)[0]:
         for n in ("dwg", "dwu", "dwd"):

@@ -6,8 +6,10 @@ Bar:
  * y, dx, dlogits, dW_gate, dW_up, dW_down: relative Frobenius error within 1e-2 for bf16 and
    1e-5 for fp32.
  * Experts that receive no tokens: weight gradients exactly zero.
-Full-size workloads are checked on sampled tokens (y, dx, dlogits rows) and sampled experts
-(dW). The oracle recomputes those from the token's or the expert's own pairs.
+Full-size workloads are checked element by element against the full oracle: the whole-tensor bar
+on every output, a per-row bound on y, dx and dlogits (5e-2 for bf16, against the row's norm or a
+floor: 5 % of the typical row norm for y and dx, the typical row norm for dlogits), and the
+whole-tensor bar on every expert's weight gradients.
 """
 import numpy as np
 import pytest
@@ -15,7 +17,7 @@ import torch
 
 import oracle
 from mixture_experts_layer_32_amd import inputs
-from gpu_util import OUTS, TOL, run_layer
+from gpu_util import OUTS, ROW_TOL, TOL, run_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -109,39 +111,66 @@ def test_deterministic_and_poison_independent():
 
 # ------------------------------------------------------------------------------ full-size workloads
 
-def sampled_check(cfg, L, got, ntok=24, seed=0):
-    rng = np.random.default_rng(seed)
-    toks = sorted(set([0, cfg.T - 1] + rng.choice(cfg.T, ntok, replace=False).tolist()))
+def row_errors(got, ref, floor_frac=0.05):
+    """Per-row relative error ||got_t - ref_t|| / max(||ref_t||, floor), with floor = floor_frac times
+    the root-mean-square norm of the reference's rows: a row whose reference is far below the typical
+    row norm (a dlogits row whose router gradients nearly cancel) is judged against that floor."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    d = np.linalg.norm(got - ref, axis=1)
+    n = np.linalg.norm(ref, axis=1)
+    rms = np.sqrt(np.mean(n ** 2))
+    return d / np.maximum(n, floor_frac * rms)
+
+
+def full_check(cfg, L, got, mode="bf16"):
+    """Every output element against the full float64 oracle: the whole-tensor bar, a per-row bound on
+    y, dx and dlogits, and the whole-tensor bar on every expert's dW_gate, dW_up and dW_down."""
     r = check_routing(cfg, L, got["routing"])
-    s = oracle.token_rows(toks, L["dy"], L["x"], L["logits"], L["wg"], L["wu"], L["wd"], cfg.k, cfg.e0, cfg.el)
-    errs = {n: oracle.rel_frobenius(got[n][toks], s[n]) for n in ("y", "dx", "dlogits")}
-    counts = r["counts"]
-    experts = sorted(set([0, cfg.el - 1, int(np.argmax(counts)), int(np.argmin(counts))]))
-    for i in experts:
-        dg, du, dd = oracle.expert_grads(i, L["dy"], L["x"], L["logits"], L["wg"][i], L["wu"][i], L["wd"][i],
-                                         cfg.k, cfg.e0, cfg.el, r=r)
-        for n, ref in (("dwg", dg), ("dwu", du), ("dwd", dd)):
-            errs[f"{n}[{i}]"] = oracle.rel_frobenius(got[n][i], ref)
-    print(cfg.name, "counts min/max", counts.min(), counts.max(), {n: f"{v:.2e}" for n, v in errs.items()},
-          flush=True)
-    for n, v in errs.items():
-        assert v <= TOL[cfg.dtype], (n, v)
+    print(f"case {cfg.name}: float64 oracle on the host", flush=True)
+    ref = oracle_full(cfg, L)
+    errs = {n: oracle.rel_frobenius(got[n], ref[n]) for n in OUTS}
+    # A dlogits row is w_j (g_j - sum_i w_i g_i) over the token's chosen experts, with g_j = <dY_t, o_tj>:
+    # its size follows how far the router gradients cancel (in an expert share a row can hang on one
+    # g), while the rounding error of each g follows |dY_t| |o_tj|. Its rows are therefore judged
+    # against at least the typical row norm; y and dx rows against 5 % of it.
+    rows = {n: row_errors(got[n], ref[n], 1.0 if n == "dlogits" else 0.05) for n in ("y", "dx", "dlogits")}
+    per_e = {n: np.array([oracle.rel_frobenius(got[n][e], ref[n][e]) if r["counts"][e] else 0.0
+                          for e in range(cfg.el)]) for n in ("dwg", "dwu", "dwd")}
+    print(cfg.name, "counts min/max", r["counts"].min(), r["counts"].max(),
+          {n: f"{v:.2e}" for n, v in errs.items()},
+          {f"{n} rows max/p99.9": f"{v.max():.2e}/{np.percentile(v, 99.9):.2e}" for n, v in rows.items()},
+          {f"{n} experts max": f"{v.max():.2e}" for n, v in per_e.items()}, flush=True)
     for n in OUTS:
+        assert errs[n] <= TOL[mode], (n, errs[n])
         assert np.all(np.isfinite(got[n])), n
+    for n, v in rows.items():
+        worst = int(np.argmax(v))
+        assert v[worst] <= ROW_TOL[mode], (n, "row", worst, v[worst])
+    for n, v in per_e.items():
+        worst = int(np.argmax(v))
+        assert v[worst] <= TOL[mode], (n, "expert", worst, v[worst])
+    for e in np.nonzero(r["counts"] == 0)[0]:
+        for n in ("dwg", "dwu", "dwd"):
+            assert not np.any(got[n][e]), (n, e)
+    # rows of tokens with no pair on the computed experts are exactly zero
+    none = np.nonzero(np.all(r["pair_pos"].reshape(cfg.T, cfg.k) < 0, axis=1))[0]
+    for n in ("y", "dx", "dlogits"):
+        assert not np.any(got[n][none]), n
 
 
 @pytest.mark.slow
-@pytest.mark.timeout(400)
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["qwen3_30b_a3b", "qwen3_30b_a3b_ep16", "qwen3_235b_a22b_zipf"])
-def test_full_size_sampled(name):
+def test_full_size_every_output(name):
+    """The full-size workloads, every row of y, dx and dlogits and every expert's weight gradients
+    compared with the float64 oracle (no sampling)."""
     cfg = inputs.CONFIGS[name]
     print(f"case {name}: generating inputs", flush=True)
     L = inputs.make_layer(cfg)
     print(f"case {name}: running fwd+bwd on the GPU", flush=True)
     got = run_layer(cfg, L)
-    sampled_check(cfg, L, got)
-    del got
     torch.cuda.empty_cache()
+    full_check(cfg, L, got)
 
 
 # rows per expert at the edges of the 128-row (half) and 256-row tiles, and an empty expert

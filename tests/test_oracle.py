@@ -383,3 +383,50 @@ def test_planted_mistake_tie_break_is_caught(monkeypatch):
     monkeypatch.setattr(om, "topk_select", high_index_first)
     lg = np.array([[0.0, 1.0, 1.0, 0.0, 1.0]])
     assert list(om.route(lg, 2)["idx"][0]) != brute_topk(lg[0].tolist(), 2)
+
+
+# ---------------------------------------------------------------------------- the parity metric
+# rel_frobenius decides every parity verdict, so it is pinned against values worked out by hand.
+
+def test_rel_frobenius_hand_values():
+    # ref = [3, 4] (norm 5), got = [3, 5]: the difference [0, 1] has norm 1, so the error is 1/5.
+    # Dividing by ||got|| = sqrt(34) would give 0.1715, the squared ratio 0.04.
+    assert oracle.rel_frobenius(np.array([3.0, 5.0]), np.array([3.0, 4.0])) == pytest.approx(0.2, abs=1e-15)
+    # the arguments are not symmetric: got = [3, 4], ref = [3, 5] gives 1/sqrt(34)
+    assert oracle.rel_frobenius(np.array([3.0, 4.0]), np.array([3.0, 5.0])) == pytest.approx(1 / math.sqrt(34),
+                                                                                              abs=1e-15)
+    # a matrix takes the Frobenius norm, not the spectral one: ref = diag(3, 4) has Frobenius norm 5
+    # (spectral 4); a difference of 1 in one element gives 0.2 (0.25 with spectral norms)
+    ref = np.diag([3.0, 4.0])
+    got = ref + np.array([[1.0, 0.0], [0.0, 0.0]])
+    assert oracle.rel_frobenius(got, ref) == pytest.approx(0.2, abs=1e-15)
+    # every element counts: ref all ones in 2x3 (norm sqrt 6), got off by 1 in two places -> sqrt(2/6)
+    ref = np.ones((2, 3))
+    got = ref.copy()
+    got[0, 2] = 2.0
+    got[1, 0] = 0.0
+    assert oracle.rel_frobenius(got, ref) == pytest.approx(math.sqrt(2.0 / 6.0), abs=1e-15)
+    # scale-free: the same relative difference at 2^40 and 2^-40
+    for s in (2.0 ** 40, 2.0 ** -40):
+        assert oracle.rel_frobenius(s * np.array([3.0, 5.0]), s * np.array([3.0, 4.0])) == pytest.approx(0.2)
+
+
+def test_rel_frobenius_zero_reference():
+    z = np.zeros((3, 4))
+    assert oracle.rel_frobenius(z, z) == 0.0
+    # -0.0 counts as zero
+    assert oracle.rel_frobenius(-z, z) == 0.0
+    got = z.copy()
+    got[1, 2] = 1e-30
+    assert oracle.rel_frobenius(got, z) == float("inf")
+
+
+def test_rel_frobenius_reads_float32_and_bf16_bits_exactly():
+    # float32 inputs are widened to float64 before any arithmetic: 1 + 2^-23 vs 1 differs by 2^-23
+    got = np.array([1.0 + 2.0 ** -23], dtype=np.float32)
+    ref = np.array([1.0], dtype=np.float32)
+    assert oracle.rel_frobenius(got, ref) == 2.0 ** -23
+    # a torch bf16 tensor converted through float32 keeps its value
+    t = torch.tensor([1.0078125, 2.0], dtype=torch.bfloat16)       # 1 + 2^-7 is exact in bf16
+    assert oracle.rel_frobenius(t.float().numpy(), np.array([1.0, 2.0])) == pytest.approx(
+        2.0 ** -7 / math.sqrt(5.0), rel=1e-15)
