@@ -93,7 +93,8 @@ typedef enum {
 
 typedef enum {
   MOE_OK = 0,
-  MOE_ERR_INVALID_ARG = 1,        /* null pointer, non-positive size, k > E_total, bad share */
+  MOE_ERR_INVALID_ARG = 1,        /* null pointer, non-positive size, k > E_total, bad share,
+                                     recompute not 0 or 1 */
   MOE_ERR_UNSUPPORTED_SHAPE = 2,  /* H % 256, F % 128, E_total > 512, k > 32, T*k >= 2^31 */
   MOE_ERR_UNSUPPORTED_MODE = 3,   /* mode value unknown */
   MOE_ERR_WORKSPACE_TOO_SMALL = 4,
@@ -110,7 +111,24 @@ typedef struct {
   int32_t expert_offset;  /* first computed expert; expert_offset + E_local <= E_total */
   int32_t topk;           /* experts per token, 1..min(E_total, 32) */
   int32_t mode;           /* moe_mode */
+  int32_t recompute;      /* 0 or 1: activation checkpointing (see below) */
 } moe_desc;
+
+/* Activation checkpointing (desc.recompute). The pages quote the layer's cost under full
+ * activation checkpointing as two forwards plus one backward ("Analisi dei kernel layer: forward vs
+ * backward" and "Benchmark di training end-to-end: velocità o illusione?" on "Prime Mega MoE: il
+ * kernel che accelera il training AI del 55%"): the training step runs the forward once, keeps only
+ * its input, and runs it again inside the backward.
+ *   recompute = 0  moe_fwd leaves the gate/up activations (a, b and w*h; in MXFP8 and FP8 also the
+ *                  weights quantised for the backward) in `saved`, and moe_bwd reads them.
+ *   recompute = 1  moe_fwd keeps only the routing results in `saved` and writes no activation for
+ *                  the backward. moe_bwd first recomputes a, b and w*h (and, in the fp8 modes, the
+ *                  quantised x and weights) from x with the forward's own gate/up kernel, into its
+ *                  workspace, then runs the backward. Only the gate/up GEMM is recomputed: the down
+ *                  GEMM and the combine do not feed the backward.
+ * The recomputed values are the same bits as the forward's (same kernels, same inputs), so every
+ * output of moe_bwd is bitwise identical to recompute = 0. moe_query_sizes gives the smaller
+ * `saved` and the larger backward workspace of the chosen form. */
 
 /* Byte sizes of the caller-allocated buffers for the description (host pointers out; any may
  * be NULL). Each size is a multiple of 256. The base pointers must be 256-byte aligned.
@@ -135,8 +153,9 @@ moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits,
                    void* y, void* saved, void* ws, size_t ws_bytes, void* stream);
 
 /* Backward of <dy, y> with the same x, weights and the `saved` of the matching moe_fwd (in
- * MOE_MODE_MXFP8, `saved` also carries the weights quantised for the backward, so the weights
- * must be unchanged since that moe_fwd).
+ * MOE_MODE_MXFP8 and MOE_MODE_FP8 without recompute, `saved` also carries the weights quantised for
+ * the backward, and with recompute the activations are recomputed from x and the weights, so in
+ * either case x and the weights must be unchanged since that moe_fwd).
  * Outputs (all overwritten, never accumulated):
  *   dx                 [T,H]
  *   dlogits            [T,E_total] fp32, zero outside each token's chosen experts
@@ -183,8 +202,8 @@ moe_status moe_router_bwd(const moe_desc* d, const void* x, const void* w_router
  *   offsets   int32 [E_local+1] exclusive prefix sum of counts (offsets[E_local] = P)
  *   perm      int32 [T*k]      first P entries: pair ids t*k+j sorted by (expert, pair id)
  *   pair_pos  int32 [T*k]      position of pair t*k+j in perm, -1 if its expert is not local
- * and, in the MX modes (0 in the others), the MXFP8 operands the forward leaves for the backward,
- * each an e4m3 byte array with its e8m0 scale bytes:
+ * and, in the MX modes without recompute (0 in the others), the MXFP8 operands the forward leaves
+ * for the backward, each an e4m3 byte array with its e8m0 scale bytes:
  *   qoff      int32 [E_local+1] first column of each expert's segment in the pair-contiguous
  *                              copies; each segment is padded with zeros to a multiple of 128
  *   qcols     (value)          column count Q of the pair-contiguous copies

@@ -22,13 +22,14 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED_SHAPE",
 class Desc(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int32), ("F", ctypes.c_int32),
                 ("E_total", ctypes.c_int32), ("E_local", ctypes.c_int32),
-                ("expert_offset", ctypes.c_int32), ("topk", ctypes.c_int32), ("mode", ctypes.c_int32)]
+                ("expert_offset", ctypes.c_int32), ("topk", ctypes.c_int32), ("mode", ctypes.c_int32),
+                ("recompute", ctypes.c_int32)]
 
     @classmethod
-    def make(cls, T, H, F, E_total, topk, mode="bf16", E_local=None, expert_offset=0):
+    def make(cls, T, H, F, E_total, topk, mode="bf16", E_local=None, expert_offset=0, recompute=False):
         m = MODES[mode] if isinstance(mode, str) else int(mode)
         return cls(T, H, F, E_total, E_total - expert_offset if E_local is None else E_local,
-                   expert_offset, topk, m)
+                   expert_offset, topk, m, int(recompute))
 
 
 class SavedOffsets(ctypes.Structure):

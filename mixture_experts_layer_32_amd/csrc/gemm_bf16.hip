@@ -317,6 +317,8 @@ static_assert(SMEM_BYTES <= 160 * 1024, "LDS");
 // forward: [a | b] = gather(x) [W_gate; W_up]^T, then ab and hw = w * silu(a) * b
 // QT: the pair-contiguous copy of hw is written as MXFP8 (blocks of 32 along the pairs, quantised
 // from the fp32 values) for an MXFP8 backward, instead of bf16
+// Each output may be null, and is then not written: under activation checkpointing the forward
+// writes hw alone (for the down GEMM), and the backward's recompute ab and the transposed copy.
 template <bool QT>
 __global__ __launch_bounds__(NTHR8, 1) void k_gateup_bf16(FwdParams p) {
   MOE_SMEM
@@ -378,10 +380,12 @@ __global__ __launch_bounds__(NTHR8, 1) void k_gateup_bf16(FwdParams p) {
           read8(slab, rl, 64 + c0, bv);
 #pragma unroll
           for (int e = 0; e < 8; ++e) hv[e] = wt * (av[e] * sigmoidf_(av[e]) * bv[e]);
-          bf16* abr = ab + (size_t)r * 2 * F + f0 + c0;
-          st16_nt(abr, pack8(av));
-          st16_nt(abr + F, pack8(bv));
-          st16_nt(hw + (size_t)r * F + f0 + c0, pack8(hv));
+          if (ab) {
+            bf16* abr = ab + (size_t)r * 2 * F + f0 + c0;
+            st16_nt(abr, pack8(av));
+            st16_nt(abr + F, pack8(bv));
+          }
+          if (hw) st16_nt(hw + (size_t)r * F + f0 + c0, pack8(hv));
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) hv[e] = 0.f;
@@ -390,11 +394,11 @@ __global__ __launch_bounds__(NTHR8, 1) void k_gateup_bf16(FwdParams p) {
         *reinterpret_cast<float4*>(slab + rl * SLD + c0 + 4) = make_float4(hv[4], hv[5], hv[6], hv[7]);
       }
       const int colb = colq + 128 * i;
-      if (QT)
+      if (QT)   // (selected only with a copy to write)
         store_transposed_mx(
             slab, lane, 64, [&](int c) { return colb < qend ? p.hwtq + (size_t)(f0 + c) * p.qc + colb : nullptr; },
             [&](int c) { return p.hwts + (size_t)(f0 + c) * (p.qc / 32) + colb / 32; });
-      else
+      else if (hwt)
         store_transposed(slab, lane, 64, [&](int c) { return colb < qend ? hwt + (size_t)(f0 + c) * p.qc + colb : nullptr; });
     }
   }
@@ -1044,6 +1048,12 @@ __global__ __launch_bounds__(256) void k_sched_setup(int* sched, const int* offs
   }
 }
 
+// zeroes the kSchedSlots tile-scheduler slots at sched (a kernel rather than a memset: the call may be
+// captured in a graph)
+__global__ __launch_bounds__(256) void k_zero_sched(int* sched) {
+  for (int i = threadIdx.x; i < kSchedSlots * kSchedInts; i += 256) sched[i] = 0;
+}
+
 }  // namespace
 
 hipError_t launch_sched_setup(const BwdParams& p, int ktile, hipStream_t s) {
@@ -1056,13 +1066,18 @@ hipError_t launch_sched_setup(const BwdParams& p, int ktile, hipStream_t s) {
   return hipSuccess;
 }
 
-hipError_t launch_forward_gemms_bf16(const FwdParams& p, int grid, hipStream_t s) {
+hipError_t launch_forward_gemms_bf16(const FwdParams& p, int grid, hipStream_t s, bool recompute) {
   hipError_t err;
-  prof_mark_begin("gemm_gateup_swiglu", s);
+  if (recompute) {   // the backward's recompute: its own tile counters, zeroed here
+    k_zero_sched<<<1, 256, 0, s>>>(p.sched);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  prof_mark_begin(recompute ? "gemm_gateup_recompute" : "gemm_gateup_swiglu", s);
   if (p.hwtq) k_gateup_bf16<true><<<grid, NTHR8, 0, s>>>(p);
   else k_gateup_bf16<false><<<grid, NTHR8, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   prof_mark_end(s);
+  if (recompute) return hipSuccess;
   prof_mark_begin("gemm_down", s);
   k_down_bf16<<<grid, NTHR8, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;

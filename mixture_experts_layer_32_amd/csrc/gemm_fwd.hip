@@ -169,12 +169,13 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ src, cons
 }
 
 template <class T>
-hipError_t launch_forward_gemms(const FwdParams& p, int grid, hipStream_t s) {
+hipError_t launch_forward_gemms(const FwdParams& p, int grid, hipStream_t s, bool recompute) {
   hipError_t err;
-  prof_mark_begin("gemm_gateup_swiglu", s);
+  prof_mark_begin(recompute ? "gemm_gateup_recompute" : "gemm_gateup_swiglu", s);
   k_gateup<T><<<grid, kThreads, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   prof_mark_end(s);
+  if (recompute) return hipSuccess;
   prof_mark_begin("gemm_down", s);
   k_down<T><<<grid, kThreads, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -253,7 +254,7 @@ hipError_t launch_router_bwd_f32(const RouterParams& p, hipStream_t s) {
   return hipSuccess;
 }
 
-template hipError_t launch_forward_gemms<float>(const FwdParams&, int, hipStream_t);
+template hipError_t launch_forward_gemms<float>(const FwdParams&, int, hipStream_t, bool);
 template hipError_t launch_combine<float>(const void*, const int*, void*, int64_t, int, int, hipStream_t);
 template hipError_t launch_combine<bf16>(const void*, const int*, void*, int64_t, int, int, hipStream_t);
 

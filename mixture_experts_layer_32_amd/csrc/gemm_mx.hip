@@ -214,7 +214,9 @@ __device__ __forceinline__ float column_amax(const float* slab, int c) {
 
 // ------------------------------------------------------------------------------------------------
 // forward: [a | b] = gather(x) [W_gate; W_up]^T; epilogue writes ab (bf16), hw = w silu(a) b as fp8
-// along F (the down GEMM's A operand) and as fp8 along the pairs (the down weight gradient's B)
+// along F (the down GEMM's A operand) and as fp8 along the pairs (the down weight gradient's B).
+// Each output may be null, and is then not written (activation checkpointing: the forward writes
+// the fp8 hw along F alone, the backward's recompute ab and the copy along the pairs).
 // Blockwise FP8 epilogue of the gate/up GEMM. w h is quantised along F in blocks of 128 columns,
 // which the two waves wn = 0, 1 of a row share (64 columns each), and along the pairs in blocks of
 // the wave's 128 rows. Pass 1 computes h, writes a and b, each row's maximum over the wave's 64
@@ -237,7 +239,7 @@ __device__ __forceinline__ void epilogue_gateup_blk(const FwdParams& p, const f3
       read8(slab, rl, 64 + c0, bv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) hv[e] = wt * (av[e] * sigmoidf_(av[e]) * bv[e]);
-      if (write_ab) {
+      if (write_ab && ab) {
         bf16* abr = ab + (size_t)r * 2 * F + f0 + c0;
         st16_nt(abr, pack8(av));
         st16_nt(abr + F, pack8(bv));
@@ -287,14 +289,15 @@ __device__ __forceinline__ void epilogue_gateup_blk(const FwdParams& p, const f3
       const int rl = (lane >> 3) + 8 * s, c0 = (lane & 7) * 8;
       const int r = r0 + 128 * wm + 32 * i + rl;
       const int sx = fp8b_exponent(fmaxf(rmax[w * 128 + 32 * i + rl], rmax[(w ^ 1) * 128 + 32 * i + rl]));
-      if (r < seg_end) {
+      if (r < seg_end && p.hwq) {
         *reinterpret_cast<uint2*>(p.hwq + (size_t)r * F + f0 + c0) = mx_encode8(hv, sx);
         if ((lane & 3) == 0) p.hws[(size_t)r * (F / 32) + (f0 + c0) / 32] = (uint8_t)(sx + 127);
       }
       put_slab(s, hv);
     }
     const int colb = colq + 32 * i;
-    store_transposed_fixed(
+    if (p.hwtq)
+      store_transposed_fixed(
         slab, lane, 64, [&](int c) { return colb < qend ? p.hwtq + (size_t)(f0 + c) * p.qc + colb : nullptr; },
         [&](int c) { return p.hwts + (size_t)(f0 + c) * qs + colb / 32; }, [&](int) { return scol; });
   };
@@ -364,15 +367,17 @@ __global__ __launch_bounds__(NTHR, 1) void k_gateup_mx(FwdParams p) {
           read8(slab, rl, 64 + c0, bv);
 #pragma unroll
           for (int e = 0; e < 8; ++e) hv[e] = wt * (av[e] * sigmoidf_(av[e]) * bv[e]);
-          bf16* abr = ab + (size_t)r * 2 * F + f0 + c0;
-          st16_nt(abr, pack8(av));
-          st16_nt(abr + F, pack8(bv));
+          if (ab) {
+            bf16* abr = ab + (size_t)r * 2 * F + f0 + c0;
+            st16_nt(abr, pack8(av));
+            st16_nt(abr + F, pack8(bv));
+          }
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) hv[e] = 0.f;
         }
         const int sx = mx_exponent(mx_amax_x4(hv));
-        if (ok) {
+        if (ok && p.hwq) {
           *reinterpret_cast<uint2*>(p.hwq + (size_t)r * F + f0 + c0) = mx_encode8(hv, sx);
           if ((lane & 3) == 0) p.hws[(size_t)r * (F / 32) + (f0 + c0) / 32] = (uint8_t)(sx + 127);
         }
@@ -380,9 +385,10 @@ __global__ __launch_bounds__(NTHR, 1) void k_gateup_mx(FwdParams p) {
         *reinterpret_cast<float4*>(slab + rl * SLD + c0 + 4) = make_float4(hv[4], hv[5], hv[6], hv[7]);
       }
       const int colb = colq + 32 * i;
-      store_transposed_mx(
-          slab, lane, 64, [&](int c) { return colb < qend ? p.hwtq + (size_t)(f0 + c) * p.qc + colb : nullptr; },
-          [&](int c) { return p.hwts + (size_t)(f0 + c) * qs + colb / 32; });
+      if (p.hwtq)
+        store_transposed_mx(
+            slab, lane, 64, [&](int c) { return colb < qend ? p.hwtq + (size_t)(f0 + c) * p.qc + colb : nullptr; },
+            [&](int c) { return p.hwts + (size_t)(f0 + c) * qs + colb / 32; });
     }
   }
 }
@@ -759,15 +765,16 @@ __global__ __launch_bounds__(NTHR, 1) void k_wgrad_gateup_mx(BwdParams p) {
 
 }  // namespace
 
-hipError_t launch_forward_gemms_mx(const FwdParams& p, int grid, hipStream_t s) {
+hipError_t launch_forward_gemms_mx(const FwdParams& p, int grid, hipStream_t s, bool recompute) {
   hipError_t err;
-  prof_mark_begin("gemm_gateup_swiglu", s);
+  prof_mark_begin(recompute ? "gemm_gateup_recompute" : "gemm_gateup_swiglu", s);
   if (p.blk)
     k_gateup_mx<true><<<grid, NTHR, 0, s>>>(p);
   else
     k_gateup_mx<false><<<grid, NTHR, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   prof_mark_end(s);
+  if (recompute) return hipSuccess;
   prof_mark_begin("gemm_down", s);
   k_down_mx<<<grid, NTHR, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;

@@ -25,6 +25,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 Layout make_layout(const moe_desc& d) {
   Layout L{};
   L.mx = d.mode == MOE_MODE_MXFP8 || d.mode == MOE_MODE_FP8_BWD || d.mode == MOE_MODE_FP8;
+  L.rc = d.recompute != 0;
   L.rows = d.T * (int64_t)d.topk;
   L.nblk_route = (int)((d.T + kRouteTokens - 1) / kRouteTokens);
   L.mtile_cap = (int)(L.rows / kBM) + d.E_local + 1;
@@ -42,6 +43,8 @@ Layout make_layout(const moe_desc& d) {
   const size_t qc = (size_t)L.qc;
   // fp8 forward (MXFP8 and blockwise FP8 share every buffer; only the scales' grouping differs)
   const bool mxf = d.mode == MOE_MODE_MXFP8 || d.mode == MOE_MODE_FP8, f8b = d.mode == MOE_MODE_FP8_BWD;
+  const bool f32 = d.mode == MOE_MODE_FP32;
+  const bool keep = !L.rc;   // the forward leaves its activations in `saved`
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -61,16 +64,16 @@ Layout make_layout(const moe_desc& d) {
   L.num_mtiles2 = take(4);
   L.zeros = take(kZeroBytes);
   L.qoff = take((El + 1) * 4);
-  L.ab = take(rows * 2 * F * L.elem);
+  L.ab = take(keep ? rows * 2 * F * L.elem : 0);
   // w*h row-major: the forward's down GEMM reads it; only the fp32 engine's backward does too, so it
   // stays in `saved` in that mode alone (bf16 modes: forward workspace, hw16 below)
-  L.hw = take(d.mode == MOE_MODE_FP32 ? rows * F * 4 : 0);
-  L.hwt = take(L.mx ? qc * F : qc * F * 2);      // MX: E4M3 bytes along the pairs
-  L.hwts = take(L.mx ? qc / 32 * F : 0);
-  L.sv_wdtq = take(mxf ? El * F * H : 0);
-  L.sv_wdts = take(mxf ? El * F * H / 32 : 0);
-  L.sv_wgutq = take(mxf ? El * H * 2 * F : 0);
-  L.sv_wguts = take(mxf ? El * H * 2 * F / 32 : 0);
+  L.hw = take(keep && f32 ? rows * F * 4 : 0);
+  L.hwt = take(keep ? (L.mx ? qc * F : qc * F * 2) : 0);      // MX: E4M3 bytes along the pairs
+  L.hwts = take(keep && L.mx ? qc / 32 * F : 0);
+  L.sv_wdtq = take(keep && mxf ? El * F * H : 0);
+  L.sv_wdts = take(keep && mxf ? El * F * H / 32 : 0);
+  L.sv_wgutq = take(keep && mxf ? El * H * 2 * F : 0);
+  L.sv_wguts = take(keep && mxf ? El * H * 2 * F / 32 : 0);
   L.saved_total = off;
 
   off = 0;
@@ -91,6 +94,8 @@ Layout make_layout(const moe_desc& d) {
   L.hwq = take(mxf ? rows * F : 0);
   L.hws = take(mxf ? rows * F / 32 : 0);
   L.hw16 = take(d.mode == MOE_MODE_BF16 || f8b ? rows * F * 2 : 0);
+  L.f_ab = take(L.rc && f32 ? rows * 2 * F * 4 : 0);    // the fp32 engine writes a, b unconditionally
+  L.f_hw = take(L.rc && f32 ? rows * F * 4 : 0);
   L.fwd_total = off;
 
   off = 0;
@@ -101,10 +106,12 @@ Layout make_layout(const moe_desc& d) {
   L.dabt = take(L.mx ? 0 : qc * 2 * F * 2);
   L.dyq = take(L.mx ? T * H : 0);
   L.dys = take(L.mx ? T * H / 32 : 0);
-  L.wdtq = take(f8b ? El * F * H : 0);
-  L.wdts = take(f8b ? El * F * H / 32 : 0);
-  L.wgutq = take(f8b ? El * H * 2 * F : 0);
-  L.wguts = take(f8b ? El * H * 2 * F / 32 : 0);
+  // the weights quantised along their other axis, when the forward has not left them in `saved`
+  const bool wq_here = f8b || (L.rc && mxf);
+  L.wdtq = take(wq_here ? El * F * H : 0);
+  L.wdts = take(wq_here ? El * F * H / 32 : 0);
+  L.wgutq = take(wq_here ? El * H * 2 * F : 0);
+  L.wguts = take(wq_here ? El * H * 2 * F / 32 : 0);
   L.dytq = take(L.mx ? H * qc : 0);
   L.dyts = take(L.mx ? H * qc / 32 : 0);
   L.xtq = take(L.mx ? H * qc : 0);
@@ -113,6 +120,17 @@ Layout make_layout(const moe_desc& d) {
   L.dabs = take(L.mx ? rows * 2 * F / 32 : 0);
   L.dabtq = take(L.mx ? 2 * F * qc : 0);
   L.dabts = take(L.mx ? 2 * F * qc / 32 : 0);
+  L.r_sched = take(L.rc ? kSchedSlots * kSchedInts * 4 : 0);
+  L.r_ab = take(L.rc ? rows * 2 * F * L.elem : 0);
+  L.r_hw = take(L.rc && f32 ? rows * F * 4 : 0);
+  L.r_hwt = take(L.rc ? (L.mx ? qc * F : qc * F * 2) : 0);
+  L.r_hwts = take(L.rc && L.mx ? qc / 32 * F : 0);
+  L.r_xq = take(L.rc && mxf ? T * H : 0);
+  L.r_xs = take(L.rc && mxf ? T * H / 32 : 0);
+  L.r_wgq = take(L.rc && mxf ? El * F * H : 0);
+  L.r_wgs = take(L.rc && mxf ? El * F * H / 32 : 0);
+  L.r_wuq = take(L.rc && mxf ? El * F * H : 0);
+  L.r_wus = take(L.rc && mxf ? El * F * H / 32 : 0);
   L.bwd_total = off;
   return L;
 }
@@ -134,6 +152,7 @@ static moe_status validate(const moe_desc* d) {
   if (d->mode != MOE_MODE_FP32 && d->mode != MOE_MODE_BF16 && d->mode != MOE_MODE_MXFP8 &&
       d->mode != MOE_MODE_FP8_BWD && d->mode != MOE_MODE_FP8)
     return fail(MOE_ERR_UNSUPPORTED_MODE, "unknown mode");
+  if (d->recompute != 0 && d->recompute != 1) return fail(MOE_ERR_INVALID_ARG, "recompute must be 0 or 1");
   return MOE_OK;
 }
 
@@ -261,11 +280,13 @@ moe_status moe_saved_layout(const moe_desc* d, moe_saved_offsets* out) {
   out->offsets = L.offsets;
   out->perm = L.perm;
   out->pair_pos = L.pair_pos;
-  const bool mxf = d->mode == MOE_MODE_MXFP8 || d->mode == MOE_MODE_FP8;
+  // with activation checkpointing `saved` holds the routing results alone
+  const bool act = L.mx && !L.rc;
+  const bool mxf = act && (d->mode == MOE_MODE_MXFP8 || d->mode == MOE_MODE_FP8);
   out->qoff = L.mx ? L.qoff : 0;
   out->qcols = L.mx ? (size_t)L.qc : 0;
-  out->hwt = L.mx ? L.hwt : 0;
-  out->hwt_scales = L.mx ? L.hwts : 0;
+  out->hwt = act ? L.hwt : 0;
+  out->hwt_scales = act ? L.hwts : 0;
   out->wdt = mxf ? L.sv_wdtq : 0;
   out->wdt_scales = mxf ? L.sv_wdts : 0;
   out->wgut = mxf ? L.sv_wgutq : 0;
@@ -351,9 +372,11 @@ moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits, const 
   fp.sched = rp.sched;
   fp.qoff = rp.qoff;
   fp.qc = L.qc;
-  fp.hwt = sv + L.hwt;
+  // activation checkpointing: nothing for the backward (it recomputes a, b and hw); only hw, the
+  // down GEMM's operand, is written, into the workspace
+  fp.hwt = L.rc ? nullptr : sv + L.hwt;
   fp.weight = rp.weight;
-  fp.ab = sv + L.ab;
+  fp.ab = L.rc ? nullptr : sv + L.ab;
   fp.hw = sv + L.hw;
   fp.o = static_cast<char*>(ws) + L.o;
   fp.pair_pos = rp.pair_pos;
@@ -365,6 +388,10 @@ moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits, const 
   fp.El = d->E_local;
   char* w = static_cast<char*>(ws);
   if (d->mode == MOE_MODE_FP32) {
+    if (L.rc) {   // the fp32 engine writes a, b and hw unconditionally: workspace scratch
+      fp.ab = w + L.f_ab;
+      fp.hw = w + L.f_hw;
+    }
     if ((e = launch_forward_gemms<float>(fp, persistent_grid(2), s)) != hipSuccess)
       return hip_fail(e, "forward GEMM launch");
     if ((e = launch_combine<float>(fp.o, fp.pair_pos, y, d->T, d->topk, d->H, s)) != hipSuccess)
@@ -383,12 +410,14 @@ moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits, const 
     auto s8 = [&](size_t o) { return reinterpret_cast<uint8_t*>(sv + o); };
     const int El = d->E_local, H = d->H, F = d->F;
     const bool blk = d->mode == MOE_MODE_FP8;
+    // with activation checkpointing the backward quantises the weights' other orientation itself
+    auto sv8 = [&](size_t o) { return L.rc ? nullptr : s8(o); };
     if ((e = launch_quant_rows(x, u8(L.xq), u8(L.xs), d->T * d->H, "mx_quant_x", s, blk)) != hipSuccess ||
-        (e = launch_quant_both(w_gate, u8(L.wgq), u8(L.wgs), s8(L.sv_wgutq), s8(L.sv_wguts), El, F, H, 2 * F, 0,
+        (e = launch_quant_both(w_gate, u8(L.wgq), u8(L.wgs), sv8(L.sv_wgutq), sv8(L.sv_wguts), El, F, H, 2 * F, 0,
                                "mx_quant_w_gate", s, blk)) != hipSuccess ||
-        (e = launch_quant_both(w_up, u8(L.wuq), u8(L.wus), s8(L.sv_wgutq), s8(L.sv_wguts), El, F, H, 2 * F, F,
+        (e = launch_quant_both(w_up, u8(L.wuq), u8(L.wus), sv8(L.sv_wgutq), sv8(L.sv_wguts), El, F, H, 2 * F, F,
                                "mx_quant_w_up", s, blk)) != hipSuccess ||
-        (e = launch_quant_both(w_down, u8(L.wdq), u8(L.wds), s8(L.sv_wdtq), s8(L.sv_wdts), El, H, F, H, 0,
+        (e = launch_quant_both(w_down, u8(L.wdq), u8(L.wds), sv8(L.sv_wdtq), sv8(L.sv_wdts), El, H, F, H, 0,
                                "mx_quant_w_down", s, blk)) != hipSuccess)
       return hip_fail(e, "quantise launch");
     fp.blk = blk;
@@ -402,8 +431,8 @@ moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits, const 
     fp.wds = u8(L.wds);
     fp.hwq = u8(L.hwq);
     fp.hws = u8(L.hws);
-    fp.hwtq = reinterpret_cast<uint8_t*>(sv + L.hwt);
-    fp.hwts = reinterpret_cast<uint8_t*>(sv + L.hwts);
+    fp.hwtq = L.rc ? nullptr : reinterpret_cast<uint8_t*>(sv + L.hwt);
+    fp.hwts = L.rc ? nullptr : reinterpret_cast<uint8_t*>(sv + L.hwts);
     if ((e = launch_forward_gemms_mx(fp, persistent_grid(1), s)) != hipSuccess)
       return hip_fail(e, "forward GEMM launch");
     if ((e = launch_combine<bf16>(fp.o, fp.pair_pos, y, d->T, d->topk, d->H, s)) != hipSuccess)
@@ -412,14 +441,83 @@ moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits, const 
     // FP8_BWD: the bf16 forward; its epilogue writes the pair-contiguous hw copy as MXFP8 for the
     // backward's down weight gradient
     fp.hw = w + L.hw16;
-    fp.hwtq = reinterpret_cast<uint8_t*>(sv + L.hwt);
-    fp.hwts = reinterpret_cast<uint8_t*>(sv + L.hwts);
+    fp.hwtq = L.rc ? nullptr : reinterpret_cast<uint8_t*>(sv + L.hwt);   // null: the bf16 kernel without it
+    fp.hwts = L.rc ? nullptr : reinterpret_cast<uint8_t*>(sv + L.hwts);
     if ((e = launch_forward_gemms_bf16(fp, persistent_grid(1), s)) != hipSuccess)
       return hip_fail(e, "forward GEMM launch");
     if ((e = launch_combine<bf16>(fp.o, fp.pair_pos, y, d->T, d->topk, d->H, s)) != hipSuccess)
       return hip_fail(e, "combine launch");
   }
   return MOE_OK;
+}
+
+// Activation checkpointing: the gate/up GEMM of the forward again, from x and the weights, with its
+// outputs (a and b, and w*h along the pairs: the backward's operands) in the backward workspace. In
+// the fp8 modes x and the gate/up weights are quantised again first, and the weights' backward
+// orientation is quantised here, since the forward left nothing in `saved`. The same kernels on the
+// same inputs give the forward's bits. Points p (the backward's parameters) at the results.
+static hipError_t recompute_activations(const moe_desc& d, const Layout& L, BwdParams& p, char* w,
+                                        hipStream_t s) {
+  auto u8 = [&](size_t o) { return reinterpret_cast<uint8_t*>(w + o); };
+  const int El = d.E_local, H = d.H, F = d.F;
+  FwdParams fp{};
+  fp.x = p.x;
+  fp.wg = p.wg;
+  fp.wu = p.wu;
+  fp.wd = p.wd;
+  fp.perm = p.perm;
+  fp.ptok = p.ptok;
+  fp.offsets = p.offsets;
+  fp.mtile = p.mtile;
+  fp.num_mtiles = p.num_mtiles;
+  fp.mtile2 = p.mtile2;
+  fp.num_mtiles2 = p.num_mtiles2;
+  fp.zeros = p.zeros;
+  fp.qoff = p.qoff;
+  fp.qc = L.qc;
+  fp.weight = p.weight;
+  fp.pair_pos = p.pair_pos;
+  fp.sched = reinterpret_cast<int*>(w + L.r_sched);
+  fp.ab = w + L.r_ab;
+  fp.T = d.T;
+  fp.H = H;
+  fp.F = F;
+  fp.k = d.topk;
+  fp.El = El;
+  p.ab = fp.ab;
+  hipError_t e;
+  if (d.mode == MOE_MODE_FP32) {
+    fp.hw = w + L.r_hw;
+    p.hw = fp.hw;
+    return launch_forward_gemms<float>(fp, persistent_grid(2), s, true);
+  }
+  if (d.mode == MOE_MODE_BF16) {
+    fp.hwt = w + L.r_hwt;
+    p.hwt = fp.hwt;
+    return launch_forward_gemms_bf16(fp, persistent_grid(1), s, true);
+  }
+  fp.hwtq = u8(L.r_hwt);
+  fp.hwts = u8(L.r_hwts);
+  if (d.mode == MOE_MODE_FP8_BWD) return launch_forward_gemms_bf16(fp, persistent_grid(1), s, true);
+  // MXFP8 / blockwise FP8: x and the gate/up weights along H, and the weights' backward orientation
+  const bool blk = d.mode == MOE_MODE_FP8;
+  if ((e = launch_quant_rows(p.x, u8(L.r_xq), u8(L.r_xs), d.T * H, "mx_quant_x_recompute", s, blk)) != hipSuccess ||
+      (e = launch_quant_both(p.wg, u8(L.r_wgq), u8(L.r_wgs), u8(L.wgutq), u8(L.wguts), El, F, H, 2 * F, 0,
+                             "mx_quant_w_gate_recompute", s, blk)) != hipSuccess ||
+      (e = launch_quant_both(p.wu, u8(L.r_wuq), u8(L.r_wus), u8(L.wgutq), u8(L.wguts), El, F, H, 2 * F, F,
+                             "mx_quant_w_up_recompute", s, blk)) != hipSuccess)
+    return e;
+  e = blk ? launch_quant_both(p.wd, nullptr, nullptr, u8(L.wdtq), u8(L.wdts), El, H, F, H, 0, "mx_quant_w_down_t", s, true)
+          : launch_quant_cols(p.wd, u8(L.wdtq), u8(L.wdts), El, H, F, H, 0, "mx_quant_w_down_t", s);
+  if (e != hipSuccess) return e;
+  fp.blk = blk;
+  fp.xq = u8(L.r_xq);
+  fp.xs = u8(L.r_xs);
+  fp.wgq = u8(L.r_wgq);
+  fp.wgs = u8(L.r_wgs);
+  fp.wuq = u8(L.r_wuq);
+  fp.wus = u8(L.r_wus);
+  return launch_forward_gemms_mx(fp, persistent_grid(1), s, true);
 }
 
 moe_status moe_bwd(const moe_desc* d, const void* dy, const void* x, const void* w_gate, const void* w_up,
@@ -480,17 +578,19 @@ moe_status moe_bwd(const moe_desc* d, const void* dy, const void* x, const void*
   p.np = L.np;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
+  if (L.rc && (e = recompute_activations(*d, L, p, w, s)) != hipSuccess) return hip_fail(e, "recompute launch");
   if (L.mx) {
     // every backward GEMM operand as MXFP8 along its contraction axis; da and db are quantised in
     // the dH epilogue. MXFP8: the weights' backward orientation comes from the forward (`saved`);
-    // FP8_BWD quantises it here.
+    // FP8_BWD quantises it here, and with activation checkpointing the recompute did.
     auto u8 = [&](size_t o) { return reinterpret_cast<uint8_t*>(w + o); };
     const int El = d->E_local, H = d->H, F = d->F;
     const bool f8b = d->mode == MOE_MODE_FP8_BWD, blk = d->mode == MOE_MODE_FP8;
-    const uint8_t* wdtq = f8b ? u8(L.wdtq) : reinterpret_cast<const uint8_t*>(sv + L.sv_wdtq);
-    const uint8_t* wdts = f8b ? u8(L.wdts) : reinterpret_cast<const uint8_t*>(sv + L.sv_wdts);
-    const uint8_t* wgutq = f8b ? u8(L.wgutq) : reinterpret_cast<const uint8_t*>(sv + L.sv_wgutq);
-    const uint8_t* wguts = f8b ? u8(L.wguts) : reinterpret_cast<const uint8_t*>(sv + L.sv_wguts);
+    const bool wq_here = f8b || L.rc;
+    const uint8_t* wdtq = wq_here ? u8(L.wdtq) : reinterpret_cast<const uint8_t*>(sv + L.sv_wdtq);
+    const uint8_t* wdts = wq_here ? u8(L.wdts) : reinterpret_cast<const uint8_t*>(sv + L.sv_wdts);
+    const uint8_t* wgutq = wq_here ? u8(L.wgutq) : reinterpret_cast<const uint8_t*>(sv + L.sv_wgutq);
+    const uint8_t* wguts = wq_here ? u8(L.wguts) : reinterpret_cast<const uint8_t*>(sv + L.sv_wguts);
     if (f8b &&
         ((e = launch_quant_cols(w_down, u8(L.wdtq), u8(L.wdts), El, H, F, H, 0, "mx_quant_w_down_t", s)) != hipSuccess ||
          (e = launch_quant_cols(w_gate, u8(L.wgutq), u8(L.wguts), El, F, H, 2 * F, 0, "mx_quant_w_gate_t", s)) != hipSuccess ||
@@ -513,8 +613,8 @@ moe_status moe_bwd(const moe_desc* d, const void* dy, const void* x, const void*
     p.dyts = u8(L.dyts);
     p.xtq = u8(L.xtq);
     p.xts = u8(L.xts);
-    p.hwtq = reinterpret_cast<const uint8_t*>(sv + L.hwt);
-    p.hwts = reinterpret_cast<const uint8_t*>(sv + L.hwts);
+    p.hwtq = reinterpret_cast<const uint8_t*>(L.rc ? w + L.r_hwt : sv + L.hwt);
+    p.hwts = reinterpret_cast<const uint8_t*>(L.rc ? w + L.r_hwts : sv + L.hwts);
     p.dabq = u8(L.dabq);
     p.dabs = u8(L.dabs);
     p.dabtq = u8(L.dabtq);

@@ -29,6 +29,7 @@ struct Layout {
   size_t elem;         // bytes per stored element (4 or 2)
   int qpad;            // pair-contiguous segments are padded to a multiple of qpad pairs (32, or 64 in MX modes)
   bool mx;             // MXFP8 or FP8_BWD
+  bool rc;             // activation checkpointing: the backward recomputes the gate/up activations
   // saved
   int64_t qc;          // row stride of the pair-contiguous transposed copies (bf16 and fp8 engines)
   size_t idx, weight, counts, offsets, perm, ptok, pair_pos, mtile, num_mtiles, mtile2, num_mtiles2, zeros, qoff, ab, hw,
@@ -39,8 +40,10 @@ struct Layout {
   // forward workspace (MXFP8: quantised operands; BF16 and FP8_BWD: the bf16 hw)
   size_t sched_f, blk_mask, blk_count, blk_prefix, o, xq, xs, wgq, wgs, wuq, wus, wdq, wds, hwq, hws, hw16, fwd_total;
   // backward workspace (MX: quantised operands)
-  size_t sched_b, dab, gpart, dxp, dabt, dyq, dys, wdtq, wdts, wgutq, wguts, dytq, dyts, xtq, xts, dabq, dabs, dabtq, dabts,
-      bwd_total;
+  size_t sched_b, dab, gpart, dxp, dabt, dyq, dys, wdtq, wdts, wgutq, wguts, dytq, dyts, xtq, xts, dabq, dabs, dabtq, dabts;
+  // activation checkpointing: the forward's scratch for the fp32 engine's a, b and hw (the forward
+  // workspace), and the backward's recomputed activations and quantised forward operands
+  size_t f_ab, f_hw, r_sched, r_ab, r_hw, r_hwt, r_hwts, r_xq, r_xs, r_wgq, r_wgs, r_wuq, r_wus, bwd_total;
 };
 
 Layout make_layout(const moe_desc& d);
@@ -104,7 +107,7 @@ struct FwdParams {
   int64_t T;
   int H, F, k, El;
 };
-template <class T> hipError_t launch_forward_gemms(const FwdParams& p, int grid, hipStream_t s);
+template <class T> hipError_t launch_forward_gemms(const FwdParams& p, int grid, hipStream_t s, bool recompute = false);
 template <class T> hipError_t launch_combine(const void* src, const int* pair_pos, void* out, int64_t ntok,
                                              int k, int H, hipStream_t s);
 
@@ -149,7 +152,9 @@ struct BwdParams {
 };
 template <class T> hipError_t launch_backward(const BwdParams& p, int grid, hipStream_t s);
 template <class T> hipError_t launch_combine_bwd(const BwdParams& p, hipStream_t s);
-hipError_t launch_forward_gemms_bf16(const FwdParams& p, int grid, hipStream_t s);
+// gate/up and down GEMMs; recompute: the gate/up GEMM alone, as the backward's recompute under
+// activation checkpointing (bf16: with its tile counters at p.sched zeroed first)
+hipError_t launch_forward_gemms_bf16(const FwdParams& p, int grid, hipStream_t s, bool recompute = false);
 hipError_t launch_backward_gemms_bf16(const BwdParams& p, int grid, hipStream_t s);
 // zeroes the backward's tile counters and splits the weight-gradient tile lists over the XCDs by
 // cost (ktile: pairs per K-tile of the engine)
@@ -176,7 +181,7 @@ hipError_t launch_router_bwd_bf16(const RouterParams& p, int grid, hipStream_t s
 hipError_t launch_router_fwd_f32(const RouterParams& p, hipStream_t s);   // fp32 test mode
 hipError_t launch_router_bwd_f32(const RouterParams& p, hipStream_t s);
 
-hipError_t launch_forward_gemms_mx(const FwdParams& p, int grid, hipStream_t s);
+hipError_t launch_forward_gemms_mx(const FwdParams& p, int grid, hipStream_t s, bool recompute = false);
 hipError_t launch_backward_gemms_mx(const BwdParams& p, int grid, hipStream_t s);
 hipError_t launch_quant_rows(const void* in, uint8_t* q, uint8_t* sc, int64_t n, const char* name, hipStream_t s,
                              bool blk = false);

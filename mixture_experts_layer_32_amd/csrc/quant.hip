@@ -10,6 +10,7 @@
 //                     (k_quant_cols128 when the column count is a multiple of 128).
 //   k_quant_both      both orientations of one weight tensor from one read (the MXFP8 forward
 //                     quantises each weight once per step for both passes); 128 x 128 tiles.
+//                     Either orientation is skipped when its output is null.
 //   k_gather_t_quant  along an expert's pairs, transposing and gathering: dY and x rows of the
 //                     expert's tokens, in the sorted pair order, into [H][Q] where the expert's
 //                     pairs occupy columns qoff[e] .. qoff[e+1] (zero-padded to a multiple of 128).
@@ -203,16 +204,19 @@ __global__ __launch_bounds__(256) void k_quant_both(const bf16* __restrict__ in,
     __syncthreads();
     s_tile = fp8b_exponent(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
   }
-  // row pass: the 4 lanes 4g..4g+3 hold one row's block of 32 along C
+  // row pass: the 4 lanes 4g..4g+3 hold one row's block of 32 along C (skipped when qr is null)
+  if (qr) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float v[8];
-    unpack8f(raw[i], v);
-    const int s = BLK ? s_tile : mx_exponent(mx_amax_x4(v));
-    const size_t grow = (size_t)b * R + r0 + (t >> 4) + 16 * i;
-    *reinterpret_cast<uint2*>(qr + grow * C + c0 + col8) = mx_encode8(v, s);
-    if ((t & 3) == 0) sr[grow * (C / 32) + (c0 + col8) / 32] = (uint8_t)(s + 127);
+    for (int i = 0; i < 8; ++i) {
+      float v[8];
+      unpack8f(raw[i], v);
+      const int s = BLK ? s_tile : mx_exponent(mx_amax_x4(v));
+      const size_t grow = (size_t)b * R + r0 + (t >> 4) + 16 * i;
+      *reinterpret_cast<uint2*>(qr + grow * C + c0 + col8) = mx_encode8(v, s);
+      if ((t & 3) == 0) sr[grow * (C / 32) + (c0 + col8) / 32] = (uint8_t)(s + 127);
+    }
   }
+  if (!qc) return;   // no column pass (the whole block takes this branch)
   __syncthreads();
   const size_t orow = (size_t)b * C + c0 + (t & 127);
   column_pass128<BLK>(tile, qc + orow * ldo + col0 + r0, scc + orow * (ldo / 32) + (col0 + r0) / 32, s_tile);

@@ -27,8 +27,11 @@ def _expect(t, name, shape, dtype, device):
 
 
 class MoELayer:
-    def __init__(self, T, H, F, E_total, topk, mode="bf16", E_local=None, expert_offset=0, device="cuda"):
-        self.desc = binding.Desc.make(T, H, F, E_total, topk, mode, E_local, expert_offset)
+    def __init__(self, T, H, F, E_total, topk, mode="bf16", E_local=None, expert_offset=0, device="cuda",
+                 recompute=False):
+        """recompute=True: activation checkpointing (the backward recomputes the gate/up activations
+        from x instead of reading them from the saved buffer)."""
+        self.desc = binding.Desc.make(T, H, F, E_total, topk, mode, E_local, expert_offset, recompute)
         self.mode = mode
         self.dtype = torch.float32 if mode == "fp32" else torch.bfloat16
         self.device = torch.device(device)

@@ -16,11 +16,12 @@ def to_dev(a, dtype):
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dtype)
 
 
-def run_layer(cfg, L, mode=None, poison=False, keep_layer=False):
-    """Forward + backward on the GPU. Returns float64 numpy outputs and the routing results."""
+def run_layer(cfg, L, mode=None, poison=False, keep_layer=False, recompute=False):
+    """Forward + backward on the GPU. Returns float64 numpy outputs and the routing results.
+    recompute: activation checkpointing (the backward recomputes the gate/up activations)."""
     mode = mode or cfg.dtype
     dt = torch.float32 if mode == "fp32" else torch.bfloat16
-    layer = MoELayer(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, mode, cfg.el, cfg.e0)
+    layer = MoELayer(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, mode, cfg.el, cfg.e0, recompute=recompute)
     if poison:                              # NaN bit patterns in every scratch byte
         layer.ws.fill_(0xFF)
         layer.saved.fill_(0xFF)
@@ -38,7 +39,7 @@ def run_layer(cfg, L, mode=None, poison=False, keep_layer=False):
     return res
 
 
-def raw_bits(cfg, L, mode=None, poison=False):
+def raw_bits(cfg, L, mode=None, poison=False, recompute=False):
     """Output tensors as raw bytes (for bitwise comparisons)."""
-    r = run_layer(cfg, L, mode, poison)
+    r = run_layer(cfg, L, mode, poison, recompute=recompute)
     return {n: r[n].tobytes() for n in OUTS}

@@ -43,6 +43,8 @@ def test_library_exports_every_declared_function():
     (dict(F=192, mode="fp8_bwd"), "MOE_ERR_UNSUPPORTED_SHAPE"),
     (dict(H=384, mode="fp8"), "MOE_ERR_UNSUPPORTED_SHAPE"),
     (dict(mode=5), "MOE_ERR_UNSUPPORTED_MODE"),
+    (dict(recompute=2), "MOE_ERR_INVALID_ARG"),
+    (dict(recompute=-1), "MOE_ERR_INVALID_ARG"),
 ])
 def test_validation_errors(kw, code):
     with pytest.raises(b.MoEError) as ei:
@@ -73,7 +75,7 @@ def test_sizes_cover_the_layout():
     fwd, bwd, saved = b.query_sizes(d)
     rows = 1000 * 4
     assert all(v % 256 == 0 for v in (fwd, bwd, saved))
-    assert saved >= rows * (4 * 4) + rows * 3 * 256 * 2           # routing + a, b, hw (bf16)
+    assert saved >= rows * (4 * 4) + rows * 3 * 256 * 2           # routing + a, b and the copy of hw (bf16)
     assert fwd >= rows * 512 * 2                                  # per-pair expert outputs
     assert bwd >= rows * 512 * 2 + rows * 2 * 256 * 2 + rows * 4 * (256 // 64)
     off = b.saved_layout(d)
@@ -195,3 +197,26 @@ def test_layer_rejects_mismatched_tensors_before_the_library():
         _expect(ok, "x", (4, 8), torch.bfloat16, torch.device("cuda", 0))
     with pytest.raises(ValueError, match="torch.Tensor"):
         _expect(12345, "x", (4, 8), torch.bfloat16, cpu)
+
+
+@pytest.mark.parametrize("mode", ["fp32", "bf16", "mxfp8", "fp8_bwd", "fp8"])
+def test_recompute_keeps_only_routing_in_saved(mode):
+    """Activation checkpointing: `saved` shrinks to the routing results (no activation, no quantised
+    weight), and the backward workspace grows by the recomputed activations."""
+    T, H, F, E, k = 1000, 512, 256, 16, 4
+    rows = T * k
+    kw = dict(T=T, H=H, F=F, E_total=E, topk=k, mode=mode)
+    fwd0, bwd0, saved0 = b.query_sizes(desc(**kw))
+    fwd1, bwd1, saved1 = b.query_sizes(desc(recompute=1, **kw))
+    elem = 4 if mode == "fp32" else 2
+    # routing: idx, weight, perm, ptok, pair_pos, M-tile tables, counts, offsets, zero page, qoff
+    routing = rows * 4 * 5 + (rows // 128 + E + 1) * 8 + (rows // 256 + E + 1) * 8 + 1024 + 4 * 256
+    assert saved1 <= routing + 16 * 256
+    assert saved0 - saved1 >= rows * 2 * F * elem                 # a and b at least
+    assert bwd1 - bwd0 >= rows * 2 * F * elem                     # recomputed a and b
+    off0, off1 = b.saved_layout(desc(**kw)), b.saved_layout(desc(recompute=1, **kw))
+    for n in ("idx", "weight", "counts", "offsets", "perm", "pair_pos", "qoff", "qcols"):
+        assert off1[n] == off0[n], n
+    for n in ("hwt", "hwt_scales", "wdt", "wdt_scales", "wgut", "wgut_scales"):
+        assert off1[n] == 0, n
+    assert fwd1 >= fwd0 - 256
