@@ -145,6 +145,17 @@ moe_status moe_query_sizes(const moe_desc* d, size_t* fwd_ws, size_t* bwd_ws, si
 moe_status moe_route(const moe_desc* d, const float* logits, void* saved, void* ws,
                      size_t ws_bytes, void* stream);
 
+/* moe_route without a workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation). Same results in `saved` as
+ * moe_route. The routing scratch (per 64 tokens and local expert 16 bytes of token masks, counts and
+ * prefixes, plus 512 bytes of tile counters) lives in a static device array of 8 MiB inside the
+ * library, one per GPU, held until the process ends; a description needing more returns
+ * MOE_ERR_UNSUPPORTED_SHAPE (up to 262,080 tokens at 128 local experts). Nothing is allocated or
+ * freed. Every call on one GPU shares that GPU's array: calls that overlap on one GPU (different
+ * streams, or host threads) race, and must be ordered by the caller. The first call on a device
+ * looks up the array's address there (a host-side runtime query, no device work). */
+moe_status moe_route_static(const moe_desc* d, const float* logits, void* saved, void* stream);
+
 /* Forward: routing, dispatch (gathered inside the gate/up GEMM's operand loads), gate/up GEMM
  * with the SwiGLU epilogue, down GEMM, and the weighted combine into y. y is overwritten.
  * `saved` receives what moe_bwd needs. */

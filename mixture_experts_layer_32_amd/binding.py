@@ -65,6 +65,7 @@ def lib():
         L.moe_query_sizes.argtypes = [_D, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t),
                                       ctypes.POINTER(ctypes.c_size_t)]
         L.moe_route.argtypes = [_D, _P, _P, _P, ctypes.c_size_t, _P]
+        L.moe_route_static.argtypes = [_D, _P, _P, _P]
         L.moe_fwd.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_bwd.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_saved_layout.argtypes = [_D, ctypes.POINTER(SavedOffsets)]
@@ -81,7 +82,7 @@ def lib():
         L.moe_profile_enable.argtypes = [ctypes.c_int]
         L.moe_profile_kernel.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
                                          ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]
-        for n in ("moe_query_sizes", "moe_route", "moe_fwd", "moe_bwd", "moe_saved_layout", "moe_mx_quantize",
+        for n in ("moe_query_sizes", "moe_route", "moe_route_static", "moe_fwd", "moe_bwd", "moe_saved_layout", "moe_mx_quantize",
                   "moe_fp8_block_quantize",
                   "moe_query_router_sizes", "moe_router_fwd", "moe_router_bwd", "moe_profile_enable",
                   "moe_profile_disable", "moe_profile_collect", "moe_profile_kernel"):
@@ -131,6 +132,10 @@ def saved_layout(desc: Desc) -> dict:
 
 def moe_route(desc, logits, saved, ws, ws_bytes, stream=None):
     _check(lib().moe_route(ctypes.byref(desc), ptr(logits), ptr(saved), ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_route_static(desc, logits, saved, stream=None):
+    _check(lib().moe_route_static(ctypes.byref(desc), ptr(logits), ptr(saved), _stream(stream)))
 
 
 def moe_fwd(desc, x, logits, w_gate, w_up, w_down, y, saved, ws, ws_bytes, stream=None):

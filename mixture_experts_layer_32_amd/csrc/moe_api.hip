@@ -340,6 +340,82 @@ moe_status moe_route(const moe_desc* d, const float* logits, void* saved, void* 
   return MOE_OK;
 }
 
+// ------------------------------------------------------------------ routing without a workspace
+// moe_route_static: moe_route with its scratch (the per-block token masks, counts and prefixes, and
+// the tile-scheduler counters it zeroes) in one file-scope device array instead of a workspace
+// argument, for callers that cannot allocate. Every call on a GPU shares that GPU's copy.
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+// Byte offsets of the routing scratch inside the static array, and the bytes it needs.
+struct RouteScratch {
+  size_t sched, blk_mask, blk_count, blk_prefix, total;
+};
+static RouteScratch route_scratch(const moe_desc& d) {
+  RouteScratch R{};
+  const size_t cells = (size_t)((d.T + kRouteTokens - 1) / kRouteTokens) * (size_t)d.E_local;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  R.sched = take(kSchedSlots * kSchedInts * 4);
+  R.blk_mask = take(cells * 8);
+  R.blk_count = take(cells * 4);
+  R.blk_prefix = take(cells * 4);
+  R.total = off;
+  return R;
+}
+
+// Device address of `scratch` on the current device, looked up once per device (with that device
+// current) and kept: each GPU holds its own copy of the array at its own address. The array's name
+// is a host-side stand-in in host code; only this address may reach a kernel.
+static moe_status static_scratch(char** out) {
+  static std::mutex mu;
+  static std::vector<char*> per_device;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> g(mu);
+  if ((size_t)dev >= per_device.size()) per_device.resize(dev + 1, nullptr);
+  if (!per_device[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) returned a null address");
+    per_device[dev] = static_cast<char*>(ptr);
+  }
+  *out = per_device[dev];
+  return MOE_OK;
+}
+
+moe_status moe_route_static(const moe_desc* d, const float* logits, void* saved, void* stream) {
+  g_last_error.clear();
+  moe_status st = validate(d);
+  if (st != MOE_OK) return st;
+  if ((st = check_ptrs({{logits, "logits"}}, 4)) != MOE_OK) return st;
+  if ((st = check_ptrs({{saved, "saved"}}, 256)) != MOE_OK) return st;
+  const RouteScratch R = route_scratch(*d);
+  if (R.total > kStaticScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_route_static needs " + std::to_string(R.total) +
+                                               " bytes of scratch (16 per 64 tokens and local expert, plus 512); "
+                                               "the static scratch holds " + std::to_string(kStaticScratchBytes));
+  char* sc = nullptr;
+  if ((st = static_scratch(&sc)) != MOE_OK) return st;
+  const Layout L = make_layout(*d);
+  // the layout's workspace offsets are replaced by the scratch's; every scratch word the routing
+  // reads is written earlier in the same call, so nothing needs clearing
+  RouteParams p = route_params(*d, L, logits, saved, sc);
+  p.sched = reinterpret_cast<int*>(sc + R.sched);
+  p.blk_mask = reinterpret_cast<unsigned long long*>(sc + R.blk_mask);
+  p.blk_count = reinterpret_cast<int*>(sc + R.blk_count);
+  p.blk_prefix = reinterpret_cast<int*>(sc + R.blk_prefix);
+  hipError_t e = launch_route(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "route launch");
+  return MOE_OK;
+}
+
 moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits, const void* w_gate, const void* w_up,
                    const void* w_down, void* y, void* saved, void* ws, size_t ws_bytes, void* stream) {
   g_last_error.clear();
