@@ -256,6 +256,10 @@ __device__ __forceinline__ int xcd_logical_block(int nblocks) {
 
 template <class T> __device__ __forceinline__ T cvt_out(float v) { return (T)v; }
 
-__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// sigma(z) = 1 / (1 + e^-z), with the hardware reciprocal (v_rcp_f32, about 1 ulp) instead of an
+// IEEE division: the division's scale/Newton/fixup sequence was about ten instructions per element
+// in the SwiGLU and dSwiGLU epilogues, whose VALU work the matrix cores wait on. For large -z the
+// exponential overflows to +inf and the reciprocal gives 0, as the division does.
+__device__ __forceinline__ float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 }  // namespace moe
