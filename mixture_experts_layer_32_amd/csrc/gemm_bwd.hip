@@ -251,79 +251,54 @@ __global__ __launch_bounds__(kThreads, 2) void k_wgrad_gateup(BwdParams p) {
     }
 }
 
-// One wavefront per part of a token's row (128 chunks of 16 bytes), 4 parts per block, as in the
-// forward combine; part 0 also writes the token's dlogits. Lane j < k holds slot j: its pair
-// position, weight, expert and g = the sum of its partials. Slot values reach every lane through
-// readlane, so the token's k source rows are addressed from scalar registers.
+// One wavefront per part of a row (128 chunks of 16 bytes) of tpw consecutive tokens (combine_tpw), 4
+// wavefronts per block, as in the forward combine; part 0 also writes those tokens' dlogits. Lane
+// q < (tokens) k holds slot q % k of token q / k: its pair position, weight, expert and g = the sum of
+// its partials. Slot values reach every lane through readlane, so a token's k source rows are
+// addressed from scalar registers.
 template <class T>
-__global__ __launch_bounds__(256) void k_combine_bwd(BwdParams p) {
+__global__ __launch_bounds__(256) void k_combine_bwd(BwdParams p, int tpw) {
   constexpr int VEC = Elem<T>::VEC;
   const int lane = threadIdx.x & 63;
-  const int nch = p.H / VEC, nparts = (nch + 127) / 128;
-  const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t t = u / nparts;
-  const int part = (int)(u - t * nparts);
-  if (t >= p.T) return;   // the whole wave leaves
   const int k = p.k, H = p.H;
-  const int pp = lane < k ? p.pair_pos[t * k + lane] : -1;
-  // dx_t = sum over the local slots of dX' rows, fp32 in slot order; 8 slot rows in flight per chunk
-  const T* __restrict__ src = static_cast<const T*>(p.dxp);
-  T* __restrict__ out = static_cast<T*>(p.dx);
-  // two chunks per lane (c0 and c0 + 64, the second only if it exists): 16 slot rows in flight
-  for (int c0 = lane + 128 * part; c0 < nch; c0 += 128 * nparts) {
-    float acc[2][VEC];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) acc[h][v] = 0.f;
-    for (int j0 = 0; j0 < k; j0 += 8) {
-      uint4 raw[2][8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int ps = j0 + u < k ? __builtin_amdgcn_readlane(pp, j0 + u) : -1;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          raw[h][u] = ps >= 0 && c0 + 64 * h < nch ? ld16_nt(src + (size_t)ps * H + (size_t)(c0 + 64 * h) * VEC)
-                                                   : make_uint4(0u, 0u, 0u, 0u);
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const T* ev = reinterpret_cast<const T*>(&raw[h][u]);
-#pragma unroll
-          for (int v = 0; v < VEC; ++v) acc[h][v] += (float)ev[v];
-        }
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint4 res;
-      T* r = reinterpret_cast<T*>(&res);
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) r[v] = cvt_out<T>(acc[h][v]);
-      if (c0 + 64 * h < nch) st16(out + (size_t)t * H + (size_t)(c0 + 64 * h) * VEC, res);
-    }
-  }
-  // dlogits of the token, by part 0, after its share of dx (the other parts skip the partials)
+  const int nch = H / VEC, nparts = (nch + 127) / 128;
+  const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t tg = u / nparts;
+  const int part = (int)(u - tg * nparts);
+  const int64_t t0 = tg * tpw;
+  if (t0 >= p.T) return;   // the whole wave leaves
+  const int nt = (int)min((int64_t)tpw, p.T - t0);
+  const bool mine = lane < nt * k;
+  const int pp = mine ? p.pair_pos[t0 * k + lane] : -1;
+  // dx_t = sum over the local slots of dX' rows, fp32 in slot order
+  for (int tt = 0; tt < nt; ++tt)
+    combine_row_part<T, VEC>(static_cast<const T*>(p.dxp), pp, tt * k, k, H, nch, part, nparts, lane,
+                             static_cast<T*>(p.dx) + (t0 + tt) * H);
+  // dlogits of the tokens, by part 0, after its share of dx (the other parts skip the partials)
   if (part != 0) return;
   int ex = -1;
   float w = 0.f, g = 0.f;
-  if (lane < k) {
-    w = p.weight[t * k + lane];
-    ex = p.idx[t * k + lane];
+  if (mine) {
+    w = p.weight[t0 * k + lane];
+    ex = p.idx[t0 * k + lane];
     if (pp >= 0)
       for (int q = 0; q < p.np; ++q) g += p.gpart[(size_t)q * p.rows + pp];
   }
-  // gbar = sum_j w_j g_j, in slot order
   const float wg = w * g;
-  float gbar = 0.f;
-  for (int j = 0; j < k; ++j) gbar += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wg), j));
-  const float val = w * (g - gbar);   // dlogits of slot j's expert (lane j)
-  for (int e = lane; e < p.E; e += 64) {
-    float v = 0.f;
+  for (int tt = 0; tt < nt; ++tt) {
+    // gbar = sum_j w_j g_j over the token's slots, in slot order
+    float gbar = 0.f;
     for (int j = 0; j < k; ++j)
-      if (__builtin_amdgcn_readlane(ex, j) == e) v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, val), j));
-    p.dlogits[t * p.E + e] = v;
+      gbar += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wg), tt * k + j));
+    const float val = w * (g - gbar);   // dlogits of slot q's expert, meaningful in the token's lanes
+    float* row = p.dlogits + (t0 + tt) * p.E;
+    for (int e = lane; e < p.E; e += 64) {
+      float v = 0.f;
+      for (int j = 0; j < k; ++j)
+        if (__builtin_amdgcn_readlane(ex, tt * k + j) == e)
+          v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, val), tt * k + j));
+      row[e] = v;
+    }
   }
 }
 
@@ -357,8 +332,9 @@ hipError_t launch_backward(const BwdParams& p, int grid, hipStream_t s) {
 template <class T>
 hipError_t launch_combine_bwd(const BwdParams& p, hipStream_t s) {
   prof_mark_begin("combine_bwd", s);
-  const int64_t nparts = (p.H / Elem<T>::VEC + 127) / 128;
-  k_combine_bwd<T><<<(unsigned)((p.T * nparts + 3) / 4), 256, 0, s>>>(p);
+  const int64_t nparts = (p.H / Elem<T>::VEC + 127) / 128, tpw = combine_tpw(p.k, p.El, p.E);
+  const int64_t waves = (p.T + tpw - 1) / tpw * nparts;
+  k_combine_bwd<T><<<(unsigned)((waves + 3) / 4), 256, 0, s>>>(p, (int)tpw);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   prof_mark_end(s);

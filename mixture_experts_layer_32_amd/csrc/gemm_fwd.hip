@@ -116,56 +116,25 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(FwdParams p) {
 }
 
 // out[t] = sum over j with pair_pos[t*k+j] >= 0 of src[pair_pos[t*k+j]]; fp32 accumulation in
-// slot order. A token with no local slot gets zeros. One wavefront per part of a token's row (128
-// chunks of 16 bytes: 2048 bf16), 4 parts per block; the slots' pair positions reach every lane
-// through readlane, and each chunk keeps 8 slot rows in flight. (One wavefront per whole token left
-// the last of its ~3 rounds of waves per CU mostly empty.)
+// slot order. A token with no local slot gets zeros. One wavefront per part of a row (128 chunks of
+// 16 bytes: 2048 bf16) of tpw consecutive tokens (combine_tpw), 4 wavefronts per block (the parts of
+// a token in neighbouring wavefronts); the slots' pair positions reach every lane through readlane.
+// (One wavefront per whole token left the last of its ~3 rounds of waves per CU mostly empty.)
 template <class T>
 __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ src, const int* __restrict__ pair_pos,
-                                                 T* __restrict__ out, int64_t ntok, int k, int H) {
+                                                 T* __restrict__ out, int64_t ntok, int k, int H, int tpw) {
   constexpr int VEC = Elem<T>::VEC;
   const int lane = threadIdx.x & 63;
   const int nch = H / VEC, nparts = (nch + 127) / 128;
   const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t t = u / nparts;
-  const int part = (int)(u - t * nparts);
-  if (t >= ntok) return;   // the whole wave leaves
-  const int pp = lane < k ? pair_pos[t * k + lane] : -1;
-  // two chunks per lane (c0 and c0 + 64, the second only if it exists): 16 slot rows in flight
-  for (int c0 = lane + 128 * part; c0 < nch; c0 += 128 * nparts) {
-    float acc[2][VEC];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) acc[h][v] = 0.f;
-    for (int j0 = 0; j0 < k; j0 += 8) {
-      uint4 raw[2][8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int ps = j0 + u < k ? __builtin_amdgcn_readlane(pp, j0 + u) : -1;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          raw[h][u] = ps >= 0 && c0 + 64 * h < nch ? ld16_nt(src + (size_t)ps * H + (size_t)(c0 + 64 * h) * VEC)
-                                                   : make_uint4(0u, 0u, 0u, 0u);
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const T* ev = reinterpret_cast<const T*>(&raw[h][u]);
-#pragma unroll
-          for (int v = 0; v < VEC; ++v) acc[h][v] += (float)ev[v];
-        }
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint4 res;
-      T* r = reinterpret_cast<T*>(&res);
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) r[v] = cvt_out<T>(acc[h][v]);
-      if (c0 + 64 * h < nch) st16(out + (size_t)t * H + (size_t)(c0 + 64 * h) * VEC, res);
-    }
-  }
+  const int64_t tg = u / nparts;
+  const int part = (int)(u - tg * nparts);
+  const int64_t t0 = tg * tpw;
+  if (t0 >= ntok) return;   // the whole wave leaves
+  const int nt = (int)min((int64_t)tpw, ntok - t0);
+  const int ppv = lane < nt * k ? pair_pos[t0 * k + lane] : -1;
+  for (int tt = 0; tt < nt; ++tt)
+    combine_row_part<T, VEC>(src, ppv, tt * k, k, H, nch, part, nparts, lane, out + (t0 + tt) * H);
 }
 
 template <class T>
@@ -184,12 +153,13 @@ hipError_t launch_forward_gemms(const FwdParams& p, int grid, hipStream_t s, boo
 }
 
 template <class T>
-hipError_t launch_combine(const void* src, const int* pair_pos, void* out, int64_t T_, int k, int H,
+hipError_t launch_combine(const void* src, const int* pair_pos, void* out, int64_t T_, int k, int H, int tpw,
                           hipStream_t s) {
   prof_mark_begin("combine", s);
   const int64_t nparts = (H / Elem<T>::VEC + 127) / 128;
-  k_combine<T><<<(unsigned)((T_ * nparts + 3) / 4), 256, 0, s>>>(static_cast<const T*>(src), pair_pos,
-                                                                 static_cast<T*>(out), T_, k, H);
+  const int64_t waves = (T_ + tpw - 1) / tpw * nparts;
+  k_combine<T><<<(unsigned)((waves + 3) / 4), 256, 0, s>>>(static_cast<const T*>(src), pair_pos,
+                                                           static_cast<T*>(out), T_, k, H, tpw);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   prof_mark_end(s);
@@ -255,7 +225,7 @@ hipError_t launch_router_bwd_f32(const RouterParams& p, hipStream_t s) {
 }
 
 template hipError_t launch_forward_gemms<float>(const FwdParams&, int, hipStream_t, bool);
-template hipError_t launch_combine<float>(const void*, const int*, void*, int64_t, int, int, hipStream_t);
-template hipError_t launch_combine<bf16>(const void*, const int*, void*, int64_t, int, int, hipStream_t);
+template hipError_t launch_combine<float>(const void*, const int*, void*, int64_t, int, int, int, hipStream_t);
+template hipError_t launch_combine<bf16>(const void*, const int*, void*, int64_t, int, int, int, hipStream_t);
 
 }  // namespace moe

@@ -463,6 +463,7 @@ moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits, const 
   fp.k = d->topk;
   fp.El = d->E_local;
   char* w = static_cast<char*>(ws);
+  const int tpw = combine_tpw(d->topk, d->E_local, d->E_total);
   if (d->mode == MOE_MODE_FP32) {
     if (L.rc) {   // the fp32 engine writes a, b and hw unconditionally: workspace scratch
       fp.ab = w + L.f_ab;
@@ -470,13 +471,13 @@ moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits, const 
     }
     if ((e = launch_forward_gemms<float>(fp, persistent_grid(2), s)) != hipSuccess)
       return hip_fail(e, "forward GEMM launch");
-    if ((e = launch_combine<float>(fp.o, fp.pair_pos, y, d->T, d->topk, d->H, s)) != hipSuccess)
+    if ((e = launch_combine<float>(fp.o, fp.pair_pos, y, d->T, d->topk, d->H, tpw, s)) != hipSuccess)
       return hip_fail(e, "combine launch");
   } else if (d->mode == MOE_MODE_BF16) {
     fp.hw = w + L.hw16;
     if ((e = launch_forward_gemms_bf16(fp, persistent_grid(1), s)) != hipSuccess)
       return hip_fail(e, "forward GEMM launch");
-    if ((e = launch_combine<bf16>(fp.o, fp.pair_pos, y, d->T, d->topk, d->H, s)) != hipSuccess)
+    if ((e = launch_combine<bf16>(fp.o, fp.pair_pos, y, d->T, d->topk, d->H, tpw, s)) != hipSuccess)
       return hip_fail(e, "combine launch");
   } else if (d->mode == MOE_MODE_MXFP8 || d->mode == MOE_MODE_FP8) {
     // every forward GEMM operand as MXFP8 (blockwise FP8) along its contraction axis; hw and its
@@ -511,7 +512,7 @@ moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits, const 
     fp.hwts = L.rc ? nullptr : reinterpret_cast<uint8_t*>(sv + L.hwts);
     if ((e = launch_forward_gemms_mx(fp, persistent_grid(1), s)) != hipSuccess)
       return hip_fail(e, "forward GEMM launch");
-    if ((e = launch_combine<bf16>(fp.o, fp.pair_pos, y, d->T, d->topk, d->H, s)) != hipSuccess)
+    if ((e = launch_combine<bf16>(fp.o, fp.pair_pos, y, d->T, d->topk, d->H, tpw, s)) != hipSuccess)
       return hip_fail(e, "combine launch");
   } else {
     // FP8_BWD: the bf16 forward; its epilogue writes the pair-contiguous hw copy as MXFP8 for the
@@ -521,7 +522,7 @@ moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits, const 
     fp.hwts = L.rc ? nullptr : reinterpret_cast<uint8_t*>(sv + L.hwts);
     if ((e = launch_forward_gemms_bf16(fp, persistent_grid(1), s)) != hipSuccess)
       return hip_fail(e, "forward GEMM launch");
-    if ((e = launch_combine<bf16>(fp.o, fp.pair_pos, y, d->T, d->topk, d->H, s)) != hipSuccess)
+    if ((e = launch_combine<bf16>(fp.o, fp.pair_pos, y, d->T, d->topk, d->H, tpw, s)) != hipSuccess)
       return hip_fail(e, "combine launch");
   }
   return MOE_OK;

@@ -256,6 +256,59 @@ __device__ __forceinline__ int xcd_logical_block(int nblocks) {
 
 template <class T> __device__ __forceinline__ T cvt_out(float v) { return (T)v; }
 
+// The combines (forward y, backward dx): a wavefront sums one part of a row (128 chunks of 16 bytes:
+// 2048 bf16) for tpw consecutive tokens, loading all their pair positions with one instruction (lane
+// q holds slot q % k of token q / k), then gathering token after token. Where few of a token's slots
+// are local (an expert share of at most a quarter of the experts), several tokens per wavefront
+// spend one pair-position round trip on several short gathers (forward combine 8 %, backward 18 %
+// faster on a 16-of-128 share); with every slot local, the gathers are long and one token per
+// wavefront keeps more of them in flight (4 tokens: 4-7 % slower).
+__host__ __device__ constexpr int combine_tpw(int k, int E_local, int E_total) {
+  return 4 * E_local > E_total ? 1 : (64 / k < 4 ? 64 / k : 4);
+}
+
+// dst row part `part` (of nparts) = the sum, in slot order and fp32, of the source rows src[pp] of the
+// k slots whose pair positions pp sit in lanes slot0 .. slot0+k-1 of ppv (pp < 0: not local). Each
+// lane takes two chunks, so 16 slot rows are in flight per lane.
+template <class T, int VEC>
+__device__ __forceinline__ void combine_row_part(const T* __restrict__ src, int ppv, int slot0, int k, int H, int nch,
+                                                 int part, int nparts, int lane, T* __restrict__ dst) {
+  for (int c0 = lane + 128 * part; c0 < nch; c0 += 128 * nparts) {
+    float acc[2][VEC];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) acc[h][v] = 0.f;
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      uint4 raw[2][8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int ps = j0 + u < k ? __builtin_amdgcn_readlane(ppv, slot0 + j0 + u) : -1;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          raw[h][u] = ps >= 0 && c0 + 64 * h < nch ? ld16_nt(src + (size_t)ps * H + (size_t)(c0 + 64 * h) * VEC)
+                                                   : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const T* ev = reinterpret_cast<const T*>(&raw[h][u]);
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) acc[h][v] += (float)ev[v];
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint4 res;
+      T* r = reinterpret_cast<T*>(&res);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) r[v] = cvt_out<T>(acc[h][v]);
+      if (c0 + 64 * h < nch) st16(dst + (size_t)(c0 + 64 * h) * VEC, res);
+    }
+  }
+}
+
 // sigma(z) = 1 / (1 + e^-z), with the hardware reciprocal (v_rcp_f32, about 1 ulp) instead of an
 // IEEE division: the division's scale/Newton/fixup sequence was about ten instructions per element
 // in the SwiGLU and dSwiGLU epilogues, whose VALU work the matrix cores wait on. For large -z the

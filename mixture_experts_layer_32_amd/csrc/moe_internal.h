@@ -108,8 +108,9 @@ struct FwdParams {
   int H, F, k, El;
 };
 template <class T> hipError_t launch_forward_gemms(const FwdParams& p, int grid, hipStream_t s, bool recompute = false);
+// tpw: tokens per wavefront (combine_tpw)
 template <class T> hipError_t launch_combine(const void* src, const int* pair_pos, void* out, int64_t ntok,
-                                             int k, int H, hipStream_t s);
+                                             int k, int H, int tpw, hipStream_t s);
 
 struct BwdParams {
   const void* dy;

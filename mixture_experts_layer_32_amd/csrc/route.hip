@@ -90,8 +90,16 @@ __global__ __launch_bounds__(64 * LPT) void k_route_topk(RouteParams p) {
       ti[j] = 0x7fffffff;
     }
     const float* row = p.logits + t * p.E;
-#pragma unroll 1
-    for (int e = q; e < p.E; e += LPT) topk_insert<KMAX>(tv, ti, row[e], e);
+    // 8 of the lane's logits are loaded at a time, then inserted: the loads of a batch are in flight
+    // together (one at a time, each insertion waited for its own load)
+    for (int e0 = q; e0 < p.E; e0 += 8 * LPT) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = e0 + i * LPT < p.E ? row[e0 + i * LPT] : -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (e0 + i * LPT < p.E) topk_insert<KMAX>(tv, ti, v[i], e0 + i * LPT);
+    }
     // merge with the partner lane's list: the better of tv[j] and the partner's [KMAX-1-j]
     // leaves the top KMAX of both lists as a bitonic sequence, which three half-cleaner stages sort
 #pragma unroll
