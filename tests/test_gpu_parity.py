@@ -58,6 +58,9 @@ SMALL = [
     custom("expert_share", T=400, H=256, F=128, E=16, k=4, E_local=5, e0=3, seed=17),
     custom("expert_share_fp32", mode="fp32", T=250, H=256, F=128, E=12, k=3, E_local=4, e0=8, seed=18),
     custom("many_experts_k32", T=130, H=256, F=128, E=512, k=32, seed=19),
+    # shares of at most a quarter of the experts: the backward runs two GEMMs per launch
+    custom("share_quarter", T=700, H=512, F=384, E=32, k=4, E_local=8, e0=12, seed=25),
+    custom("share_with_empty_experts", T=500, H=256, F=256, E=64, k=2, E_local=12, e0=14, zipf_s=0.3, seed=26),
     custom("wide_H4096_F1536", T=130, H=4096, F=1536, E=4, k=2, seed=20),
 ]
 
