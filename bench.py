@@ -124,7 +124,7 @@ def cpu_baseline(cfg, L, min_seconds=10.0, group=16):
                       f"backward, {dt:.1f} s wall"}
 
 
-def router_bench(cfg, layer, x, grads, steps):
+def router_bench(cfg, layer, x, grads, steps, wg=None, wu=None, wd=None, y=None):
     """The router projection in front of the layer (logits = x W_r^T; dW_r and dx += dlogits W_r),
     timed on its own with HIP events on the library's stream. It is not part of `value`, which is
     the layer's metric. The backward takes the layer's last dlogits (k nonzeros per row) and
@@ -157,6 +157,35 @@ def router_bench(cfg, layer, x, grads, steps):
         layer.router_backward(x, wr, dl, dx, dwr)
     kern = binding.profile_collect()
     binding.profile_disable()
+    fused = None
+    if wg is not None and cfg.E <= 256 and cfg.k <= 8:
+        # the layer's forward from x: moe_fwd_router (router projection fused with the routing) against
+        # moe_router_fwd followed by moe_fwd
+        for _ in range(2):
+            layer.forward_router(x, wr, wg, wu, wd, y, lg)
+        ev3 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for e in ev3:
+            e[0].record()
+            layer.router_forward(x, wr, lg)
+            layer.forward(x, lg, wg, wu, wd, y)
+            e[1].record()
+            layer.forward_router(x, wr, wg, wu, wd, y, lg)
+            e[2].record()
+        torch.cuda.synchronize()
+        binding.profile_enable(16 * steps)
+        for _ in range(steps):
+            layer.forward_router(x, wr, wg, wu, wd, y, lg)
+        kf = binding.profile_collect()
+        binding.profile_disable()
+        n_, tot = kf["router_topk_fused"]
+        fk = tot / n_
+        by = cfg.T * cfg.H * 2 + cfg.E * cfg.H * 2 + cfg.T * cfg.E * 4 + cfg.T * cfg.k * 8
+        fused = {"what": "layer forward from x: moe_fwd_router vs moe_router_fwd + moe_fwd",
+                 "separate_ms": round(float(np.median([e[0].elapsed_time(e[1]) for e in ev3])), 4),
+                 "fused_ms": round(float(np.median([e[1].elapsed_time(e[2]) for e in ev3])), 4),
+                 "router_topk_fused_avg_ms": round(fk, 5),
+                 "router_topk_fused_gbs": round(by / (fk * 1e-3) / 1e9, 1),
+                 "router_topk_fused_algorithmic_bytes": by}
     fl = 2.0 * cfg.T * cfg.H * cfg.E
     gemm_fl = {"router_fwd_gemm": fl, "router_dx_gemm": fl, "router_dw_gemm": fl}
     per_kernel = {}
@@ -170,7 +199,8 @@ def router_bench(cfg, layer, x, grads, steps):
     return {"what": "logits = x W_r^T [T, E] fp32; backward dW_r = dlogits^T x and dx += dlogits W_r (bf16 MFMA)",
             "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
             "fwd_tflops": round(fl / (fwd_ms * 1e-3) / 1e12, 2),
-            "bwd_tflops": round(2 * fl / (bwd_ms * 1e-3) / 1e12, 2), "kernels": per_kernel}
+            "bwd_tflops": round(2 * fl / (bwd_ms * 1e-3) / 1e12, 2), "kernels": per_kernel,
+            "fused_forward": fused}
 
 
 def full_layer_bench(cfg, mode, layer, x, lg, wg, wu, wd, y, dy, grads, steps):
@@ -373,7 +403,7 @@ def main():
     res["full_layer_2f_b_ms"] = fl["two_forwards_one_backward"]["ms"]
     if mode != "fp32":
         print("[bench] router projection", file=sys.stderr, flush=True)
-        res["router"] = router_bench(cfg, layer, x, grads, a.steps)
+        res["router"] = router_bench(cfg, layer, x, grads, a.steps, wg, wu, wd, y)
     if not a.no_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, L)

@@ -163,6 +163,21 @@ moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits,
                    const void* w_gate, const void* w_up, const void* w_down,
                    void* y, void* saved, void* ws, size_t ws_bytes, void* stream);
 
+/* The forward from x: the router projection logits = x w_router^T fused with the routing (top-k,
+ * weights and the per-block expert masks in one kernel), then the layer as moe_fwd. The pages fold the
+ * routing into the fused operation ("Prime Mega MoE: kernel fuso per l'addestramento MoE" on "Prime
+ * Mega MoE: il kernel che accelera il training AI del 55%"); the projection is the linear router of
+ * moe_router_fwd. `logits` [T, E_total] fp32 is an output here: the logits the routing used (their
+ * bits are those of this kernel's fp32 accumulation over H, which is not moe_router_fwd's order), so
+ * that the routing is exactly oracle routing of `logits`. w_router [E_total, H] bf16, 16-byte aligned.
+ * The backward is moe_bwd, then moe_router_bwd with moe_bwd's dlogits.
+ * Bf16 I/O modes only (MOE_ERR_UNSUPPORTED_MODE in MOE_MODE_FP32), E_total <= 256 and topk <= 8
+ * (MOE_ERR_UNSUPPORTED_SHAPE otherwise: use moe_router_fwd, then moe_fwd). Workspace and `saved` as
+ * for moe_fwd. */
+moe_status moe_fwd_router(const moe_desc* d, const void* x, const void* w_router, float* logits,
+                          const void* w_gate, const void* w_up, const void* w_down, void* y,
+                          void* saved, void* ws, size_t ws_bytes, void* stream);
+
 /* Backward of <dy, y> with the same x, weights and the `saved` of the matching moe_fwd (in
  * MOE_MODE_MXFP8 and MOE_MODE_FP8 without recompute, `saved` also carries the weights quantised for
  * the backward, and with recompute the activations are recomputed from x and the weights, so in

@@ -67,6 +67,7 @@ def lib():
         L.moe_route.argtypes = [_D, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_route_static.argtypes = [_D, _P, _P, _P]
         L.moe_fwd.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.moe_fwd_router.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_bwd.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_saved_layout.argtypes = [_D, ctypes.POINTER(SavedOffsets)]
         L.moe_status_string.argtypes = [st]
@@ -82,7 +83,7 @@ def lib():
         L.moe_profile_enable.argtypes = [ctypes.c_int]
         L.moe_profile_kernel.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
                                          ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]
-        for n in ("moe_query_sizes", "moe_route", "moe_route_static", "moe_fwd", "moe_bwd", "moe_saved_layout", "moe_mx_quantize",
+        for n in ("moe_query_sizes", "moe_route", "moe_route_static", "moe_fwd", "moe_fwd_router", "moe_bwd", "moe_saved_layout", "moe_mx_quantize",
                   "moe_fp8_block_quantize",
                   "moe_query_router_sizes", "moe_router_fwd", "moe_router_bwd", "moe_profile_enable",
                   "moe_profile_disable", "moe_profile_collect", "moe_profile_kernel"):
@@ -141,6 +142,11 @@ def moe_route_static(desc, logits, saved, stream=None):
 def moe_fwd(desc, x, logits, w_gate, w_up, w_down, y, saved, ws, ws_bytes, stream=None):
     _check(lib().moe_fwd(ctypes.byref(desc), ptr(x), ptr(logits), ptr(w_gate), ptr(w_up), ptr(w_down), ptr(y),
                          ptr(saved), ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_fwd_router(desc, x, w_router, logits, w_gate, w_up, w_down, y, saved, ws, ws_bytes, stream=None):
+    _check(lib().moe_fwd_router(ctypes.byref(desc), ptr(x), ptr(w_router), ptr(logits), ptr(w_gate), ptr(w_up),
+                                ptr(w_down), ptr(y), ptr(saved), ptr(ws), ws_bytes, _stream(stream)))
 
 
 def moe_bwd(desc, dy, x, w_gate, w_up, w_down, saved, dx, dlogits, dw_gate, dw_up, dw_down, ws, ws_bytes,

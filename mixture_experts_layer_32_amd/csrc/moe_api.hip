@@ -416,20 +416,23 @@ moe_status moe_route_static(const moe_desc* d, const float* logits, void* saved,
   return MOE_OK;
 }
 
-moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits, const void* w_gate, const void* w_up,
-                   const void* w_down, void* y, void* saved, void* ws, size_t ws_bytes, void* stream) {
-  g_last_error.clear();
-  moe_status st = validate(d);
-  if (st != MOE_OK) return st;
+// The forward after validation: routing (from the given logits, or the router projection fused with
+// the top-k when w_router is given, writing the logits to logits_out), then the expert GEMMs and the
+// combine.
+static moe_status fwd_impl(const moe_desc* d, const void* x, const float* logits, const void* w_router,
+                           float* logits_out, const void* w_gate, const void* w_up, const void* w_down, void* y,
+                           void* saved, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st;
   if ((st = check_ptrs({{x, "x"}, {w_gate, "w_gate"}, {w_up, "w_up"}, {w_down, "w_down"}, {y, "y"}}, 16)) != MOE_OK)
     return st;
-  if ((st = check_ptrs({{logits, "logits"}}, 4)) != MOE_OK) return st;
+  if ((st = check_ptrs({{w_router ? logits_out : logits, "logits"}}, 4)) != MOE_OK) return st;
+  if (w_router && (st = check_ptrs({{w_router, "w_router"}}, 16)) != MOE_OK) return st;
   if ((st = check_ptrs({{saved, "saved"}, {ws, "ws"}}, 256)) != MOE_OK) return st;
   const Layout L = make_layout(*d);
   if (ws_bytes < L.fwd_total) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "forward workspace too small");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const RouteParams rp = route_params(*d, L, logits, saved, ws);
-  hipError_t e = launch_route(rp, s);
+  const RouteParams rp = route_params(*d, L, w_router ? logits_out : logits, saved, ws);
+  hipError_t e = w_router ? launch_router_route_bf16(rp, x, w_router, logits_out, d->H, s) : launch_route(rp, s);
   if (e != hipSuccess) return hip_fail(e, "route launch");
   char* sv = static_cast<char*>(saved);
   FwdParams fp{};
@@ -526,6 +529,27 @@ moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits, const 
       return hip_fail(e, "combine launch");
   }
   return MOE_OK;
+}
+
+moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits, const void* w_gate, const void* w_up,
+                   const void* w_down, void* y, void* saved, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  moe_status st = validate(d);
+  if (st != MOE_OK) return st;
+  return fwd_impl(d, x, logits, nullptr, nullptr, w_gate, w_up, w_down, y, saved, ws, ws_bytes, stream);
+}
+
+moe_status moe_fwd_router(const moe_desc* d, const void* x, const void* w_router, float* logits, const void* w_gate,
+                          const void* w_up, const void* w_down, void* y, void* saved, void* ws, size_t ws_bytes,
+                          void* stream) {
+  g_last_error.clear();
+  moe_status st = validate(d);
+  if (st != MOE_OK) return st;
+  if (d->mode == MOE_MODE_FP32) return fail(MOE_ERR_UNSUPPORTED_MODE, "moe_fwd_router takes bf16 x and w_router");
+  if (d->E_total > 256 || d->topk > 8)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_fwd_router needs E_total <= 256 and topk <= 8 "
+                                           "(else moe_router_fwd, then moe_fwd)");
+  return fwd_impl(d, x, nullptr, w_router, logits, w_gate, w_up, w_down, y, saved, ws, ws_bytes, stream);
 }
 
 // Activation checkpointing: the gate/up GEMM of the forward again, from x and the weights, with its

@@ -77,6 +77,12 @@ struct RouteParams {
   int E, El, e0, k, nblk, qpad;
 };
 hipError_t launch_route(const RouteParams& p, hipStream_t s);
+// the routing after the top-k (its per-block masks and counts in place): scans, offsets, permutation
+hipError_t launch_route_tail(const RouteParams& p, hipStream_t s);
+// the router projection fused with the top-k (bf16 x and W_r, E <= 256, k <= 8), then the routing
+// tail; the logits [T, E] fp32 are written to `logits`
+hipError_t launch_router_route_bf16(const RouteParams& p, const void* x, const void* w_router, float* logits, int H,
+                                    hipStream_t s);
 
 // Row-tiled grouped GEMMs and wgrad GEMMs; T = float or bf16.
 struct FwdParams {

@@ -24,12 +24,9 @@
 
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "route_device.h"
 
 namespace moe {
-
-__device__ __forceinline__ bool better(float av, int ae, float bv, int be) {
-  return av > bv || (av == bv && ae < be);
-}
 
 template <int NT>
 __device__ __forceinline__ int block_incl_scan(int v, int* lds, int& total) {
@@ -53,26 +50,8 @@ __device__ __forceinline__ int block_incl_scan(int v, int* lds, int& total) {
   return v + add;
 }
 
-// Insert candidate (cv, ce) into the list t[0..KMAX) kept sorted by better(); the loser of each
-// compare-exchange moves on. Branchless.
-template <int KMAX>
-__device__ __forceinline__ void topk_insert(float (&tv)[KMAX], int (&ti)[KMAX], float cv, int ce) {
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    const bool b = better(cv, ce, tv[j], ti[j]);
-    const float nv = b ? cv : tv[j];
-    const int ni = b ? ce : ti[j];
-    cv = b ? tv[j] : cv;
-    ce = b ? ti[j] : ce;
-    tv[j] = nv;
-    ti[j] = ni;
-  }
-}
-
-// k <= 8: 64 tokens per block, LPT lanes per token. Lane q keeps the best KMAX of experts q, q+LPT,
-// q+2 LPT, ...; log2(LPT) butterfly steps merge the lists, after which every lane of the token holds
-// its top k. LPT = 8 took 20 us against 23 us with 4 at T = 16384, E = 128; LPT = 16 sent the
-// compiler into a build of more than 15 minutes.
+// k <= 8: 64 tokens per block, LPT lanes per token (route_token). LPT = 8 took 20 us against 23 us
+// with 4 at T = 16384, E = 128; LPT = 16 sent the compiler into a build of more than 15 minutes.
 template <int KMAX, int LPT>
 __global__ __launch_bounds__(64 * LPT) void k_route_topk(RouteParams p) {
   constexpr int NT = 64 * LPT;
@@ -82,71 +61,8 @@ __global__ __launch_bounds__(64 * LPT) void k_route_topk(RouteParams p) {
   __syncthreads();
   const int64_t t = (int64_t)blockIdx.x * kRouteTokens + tl;
   if (t < p.T) {
-    float tv[KMAX];
-    int ti[KMAX];
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      tv[j] = -INFINITY;
-      ti[j] = 0x7fffffff;
-    }
     const float* row = p.logits + t * p.E;
-    // 8 of the lane's logits are loaded at a time, then inserted: the loads of a batch are in flight
-    // together (one at a time, each insertion waited for its own load)
-    for (int e0 = q; e0 < p.E; e0 += 8 * LPT) {
-      float v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = e0 + i * LPT < p.E ? row[e0 + i * LPT] : -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (e0 + i * LPT < p.E) topk_insert<KMAX>(tv, ti, v[i], e0 + i * LPT);
-    }
-    // merge with the partner lane's list: the better of tv[j] and the partner's [KMAX-1-j]
-    // leaves the top KMAX of both lists as a bitonic sequence, which three half-cleaner stages sort
-#pragma unroll
-    for (int step = 1; step < LPT; step <<= 1) {
-      float ov[KMAX];
-      int oi[KMAX];
-#pragma unroll
-      for (int j = 0; j < KMAX; ++j) {
-        ov[j] = __shfl_xor(tv[j], step);
-        oi[j] = __shfl_xor(ti[j], step);
-      }
-#pragma unroll
-      for (int j = 0; j < KMAX; ++j) {
-        const bool b = better(tv[j], ti[j], ov[KMAX - 1 - j], oi[KMAX - 1 - j]);
-        tv[j] = b ? tv[j] : ov[KMAX - 1 - j];
-        ti[j] = b ? ti[j] : oi[KMAX - 1 - j];
-      }
-#pragma unroll
-      for (int d = KMAX / 2; d >= 1; d >>= 1)
-#pragma unroll
-        for (int j = 0; j < KMAX; ++j)
-          if ((j & d) == 0) {
-            const bool b = better(tv[j], ti[j], tv[j + d], ti[j + d]);
-            const float v0 = b ? tv[j] : tv[j + d], v1 = b ? tv[j + d] : tv[j];
-            const int i0 = b ? ti[j] : ti[j + d], i1 = b ? ti[j + d] : ti[j];
-            tv[j] = v0;
-            tv[j + d] = v1;
-            ti[j] = i0;
-            ti[j + d] = i1;
-          }
-    }
-    // renormalised softmax over the chosen k, summed in slot order
-    float z[KMAX], sum = 0.f;
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      z[j] = j < p.k ? expf(tv[j] - tv[0]) : 0.f;
-      sum += z[j];
-    }
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      if (j < p.k && (j & (LPT - 1)) == q) {
-        p.idx[t * p.k + j] = ti[j];
-        p.weight[t * p.k + j] = z[j] / sum;
-        const int el = ti[j] - p.e0;
-        if (el >= 0 && el < p.El) atomicOr(&mask[el], 1ull << tl);
-      }
-    }
+    route_token<KMAX, LPT>(p, t, tl, q, [&](int e) { return row[e]; }, mask);
   }
   __syncthreads();
   for (int e = tid; e < p.El; e += NT) {
@@ -296,6 +212,12 @@ hipError_t launch_route(const RouteParams& p, hipStream_t s) {
   else k_route_topk_wave<8><<<p.nblk, 256, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   prof_mark_end(s);
+  return launch_route_tail(p, s);
+}
+
+// after the top-k: per-expert scans, offsets and M-tile tables, and the permutation
+hipError_t launch_route_tail(const RouteParams& p, hipStream_t s) {
+  hipError_t err;
   prof_mark_begin("route_colscan", s);
   k_route_colscan<<<p.El, 256, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;

@@ -67,6 +67,19 @@ class MoELayer:
         binding.moe_fwd(d, x, logits, w_gate, w_up, w_down, y, self.saved, self.ws, self.ws.numel(), stream)
         return y
 
+    def forward_router(self, x, w_router, w_gate, w_up, w_down, y=None, logits=None, stream=None):
+        """The forward from x through moe_fwd_router (router projection fused with the routing);
+        returns (y, logits)."""
+        d = self.desc
+        if y is None:
+            y = torch.empty(d.T, d.H, dtype=self.dtype, device=self.device)
+        if logits is None:
+            logits = torch.empty(d.T, d.E_total, dtype=torch.float32, device=self.device)
+        self._check(x=x, w_router=w_router, logits=logits, w_gate=w_gate, w_up=w_up, w_down=w_down, y=y)
+        binding.moe_fwd_router(d, x, w_router, logits, w_gate, w_up, w_down, y, self.saved, self.ws, self.ws.numel(),
+                               stream)
+        return y, logits
+
     def route(self, logits, stream=None):
         self._check(logits=logits)
         binding.moe_route(self.desc, logits, self.saved, self.ws, self.ws.numel(), stream)

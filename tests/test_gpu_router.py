@@ -163,3 +163,65 @@ def test_router_full_size_sampled():
     e_w = oracle.rel_frobenius(dwr.float().cpu().numpy()[experts], dw_ref)
     print(f"full size: logits {e_l:.2e} dx {e_x:.2e} dW_r {e_w:.2e}", flush=True)
     assert e_l <= TOL_LOGITS and e_x <= TOL_BWD and e_w <= TOL_BWD
+
+
+# ------------------------------------------------------------- router projection fused with routing
+FUSED = [
+    # name, T, H, F, E, k, E_local, e0, mode
+    ("E8_k2", 256, 256, 128, 8, 2, None, 0, "bf16"),
+    ("E128_k8_ragged", 777, 512, 256, 128, 8, None, 0, "bf16"),
+    ("E160_k6_two_blocks", 300, 256, 128, 160, 6, None, 0, "bf16"),
+    ("E256_k8", 200, 768, 128, 256, 8, None, 0, "bf16"),
+    ("E128_share", 500, 256, 128, 128, 8, 16, 32, "bf16"),
+    ("E64_k1", 129, 256, 128, 64, 1, None, 0, "bf16"),
+    ("E128_mxfp8", 300, 512, 256, 128, 8, None, 0, "mxfp8"),
+]
+
+
+@pytest.mark.parametrize("name,T,H,F,E,k,el,e0,mode", FUSED, ids=[c[0] for c in FUSED])
+def test_fwd_router_fused(name, T, H, F, E, k, el, e0, mode):
+    """moe_fwd_router: the routing is exactly the oracle's routing of the logits the call returns, those
+    logits are the router projection within 1e-5, and y is bitwise moe_fwd's on those logits."""
+    print(f"case fwd_router {name} T={T} H={H} E={E} k={k} mode={mode}", flush=True)
+    cfg, L = inputs.custom_layer(T=T, H=H, F=F, E=E, k=k, E_local=-1 if el is None else el, e0=e0, seed=61)
+    wr = inputs.router_weight(cfg)
+    dt = torch.bfloat16
+    x, wrd = to_dev(L["x"], dt), to_dev(wr, dt)
+    wg, wu, wd = to_dev(L["wg"], dt), to_dev(L["wu"], dt), to_dev(L["wd"], dt)
+    layer = MoELayer(T, H, F, E, k, mode, cfg.el, cfg.e0)
+    y, lg = layer.forward_router(x, wrd, wg, wu, wd)
+    torch.cuda.synchronize()
+    lg_np = lg.cpu().numpy()
+    rt = {n: t.numpy() for n, t in layer.routing().items()}
+    r = oracle.route(lg_np, k, cfg.e0, cfg.el)
+    for n in ("idx", "counts", "offsets", "perm", "pair_pos"):
+        assert np.array_equal(rt[n], r[n]), n
+    assert np.max(np.abs(rt["weight"] - r["w"])) <= 1e-6
+    assert oracle.rel_frobenius(lg_np, oracle.router_forward(L["x"], wr)) <= TOL_LOGITS
+    ref = MoELayer(T, H, F, E, k, mode, cfg.el, cfg.e0)
+    y2 = ref.forward(x, lg, wg, wu, wd)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "y differs from moe_fwd on the same logits"
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(300)
+def test_fwd_router_fused_benchmark_shape():
+    cfg = inputs.CONFIGS["qwen3_30b_a3b"]
+    print("case fwd_router qwen3_30b_a3b", flush=True)
+    x_np, _, _ = inputs.make_tokens(cfg)
+    wr = inputs.router_weight(cfg)
+    x, wrd = to_dev(x_np, torch.bfloat16), to_dev(wr, torch.bfloat16)
+    layer = MoELayer(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, "bf16")
+    lg = torch.empty(cfg.T, cfg.E, dtype=torch.float32, device="cuda")
+    # the routing alone (the expert weights do not matter for it): zero weights keep the call cheap
+    z = torch.zeros(cfg.E, cfg.F, cfg.H, dtype=torch.bfloat16, device="cuda")
+    zd = torch.zeros(cfg.E, cfg.H, cfg.F, dtype=torch.bfloat16, device="cuda")
+    layer.forward_router(x, wrd, z, z, zd, logits=lg)
+    torch.cuda.synchronize()
+    lg_np = lg.cpu().numpy()
+    rt = {n: t.numpy() for n, t in layer.routing().items()}
+    r = oracle.route(lg_np, cfg.k)
+    for n in ("idx", "counts", "offsets", "perm", "pair_pos"):
+        assert np.array_equal(rt[n], r[n]), n
+    assert oracle.rel_frobenius(lg_np, oracle.router_forward(x_np, wr)) <= TOL_LOGITS
