@@ -15,77 +15,95 @@ __device__ __forceinline__ bool better(float av, int ae, float bv, int be) {
   return av > bv || (av == bv && ae < be);
 }
 
-// Insert candidate (cv, ce) into the list t[0..KMAX) kept sorted by better(); the loser of each
-// compare-exchange moves on. Branchless.
-template <int KMAX>
-__device__ __forceinline__ void topk_insert(float (&tv)[KMAX], int (&ti)[KMAX], float cv, int ce) {
+// Order-preserving 64-bit key of (logit v, expert e): a larger key is a better candidate (larger logit,
+// then lower index). The high word maps the fp32 bits monotonically to unsigned order, with -0 taken
+// as +0 so that the two zeros tie as equal logits do; the low word is ~e. Finite logits only.
+__device__ __forceinline__ unsigned long long topk_key(float v, int e) {
+  unsigned u = __float_as_uint(v);
+  u = u == 0x80000000u ? 0u : u;
+  const unsigned o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)o << 32) | (unsigned)~e;
+}
+__device__ __forceinline__ float key_value(unsigned long long k) {
+  const unsigned o = (unsigned)(k >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ __forceinline__ int key_expert(unsigned long long k) { return (int)~(unsigned)k; }
+
+// compare-exchange into descending order
+__device__ __forceinline__ void key_ce(unsigned long long& a, unsigned long long& b) {
+  const bool s = b > a;
+  const unsigned long long hi = s ? b : a, lo = s ? a : b;
+  a = hi;
+  b = lo;
+}
+// sorts 8 keys into descending order: Knuth's 19-comparator network for 8 inputs, in 6 parallel rounds
+__device__ __forceinline__ void key_sort8(unsigned long long (&k)[8]) {
+  key_ce(k[0], k[2]); key_ce(k[1], k[3]); key_ce(k[4], k[6]); key_ce(k[5], k[7]);
+  key_ce(k[0], k[4]); key_ce(k[1], k[5]); key_ce(k[2], k[6]); key_ce(k[3], k[7]);
+  key_ce(k[0], k[1]); key_ce(k[2], k[3]); key_ce(k[4], k[5]); key_ce(k[6], k[7]);
+  key_ce(k[2], k[4]); key_ce(k[3], k[5]);
+  key_ce(k[1], k[4]); key_ce(k[3], k[6]);
+  key_ce(k[1], k[2]); key_ce(k[3], k[4]); key_ce(k[5], k[6]);
+}
+// t (descending) becomes the best 8 of t and c (both descending): the larger of t[j] and c[7-j] leaves
+// the best 8 as a bitonic sequence, which three half-cleaner rounds sort
+__device__ __forceinline__ void key_merge8(unsigned long long (&t)[8], const unsigned long long (&c)[8]) {
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    const bool b = better(cv, ce, tv[j], ti[j]);
-    const float nv = b ? cv : tv[j];
-    const int ni = b ? ce : ti[j];
-    cv = b ? tv[j] : cv;
-    ce = b ? ti[j] : ce;
-    tv[j] = nv;
-    ti[j] = ni;
+  for (int j = 0; j < 8; ++j) t[j] = t[j] > c[7 - j] ? t[j] : c[7 - j];
+#pragma unroll
+  for (int d = 4; d >= 1; d >>= 1)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if ((j & d) == 0) key_ce(t[j], t[j + d]);
+}
+
+// Best 8 of experts 0..E-1 (logit e from get(e)) by LPT lanes of a token, lane q taking experts q,
+// q + LPT, ...: each lane sorts its candidates 8 at a time and merges them into its list, then log2(LPT)
+// butterfly steps merge the lanes' lists, after which every lane of the token holds the token's best 8
+// (slots past E hold key 0 and come last).
+template <int LPT, class Get>
+__device__ __forceinline__ void select_top8(int E, int q, Get get, float (&tv)[8], int (&ti)[8]) {
+  unsigned long long t[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) t[j] = 0ull;
+  for (int e0 = q; e0 < E; e0 += 8 * LPT) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = e0 + i * LPT < E ? get(e0 + i * LPT) : 0.f;
+    unsigned long long c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = e0 + i * LPT < E ? topk_key(v[i], e0 + i * LPT) : 0ull;
+    key_sort8(c);
+    key_merge8(t, c);
+  }
+#pragma unroll
+  for (int step = 1; step < LPT; step <<= 1) {
+    unsigned long long o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const unsigned lo = __shfl_xor((unsigned)t[j], step), hi = __shfl_xor((unsigned)(t[j] >> 32), step);
+      o[j] = ((unsigned long long)hi << 32) | lo;
+    }
+    key_merge8(t, o);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    tv[j] = key_value(t[j]);
+    ti[j] = key_expert(t[j]);
   }
 }
 
-// Top-k of token t (k <= KMAX) by its LPT lanes: lane q keeps the best KMAX of experts q, q+LPT,
-// q+2 LPT, ... (logit e from get(e)); log2(LPT) butterfly steps merge the lists, after which every lane
-// of the token holds its top k. Writes the token's expert indices and renormalised softmax weights
+// Top-k of token t (k <= KMAX = 8) by its LPT lanes (select_top8), after which every lane of the
+// token holds its top k. Writes the token's expert indices and renormalised softmax weights
 // (summed in slot order) and sets its bit (tl) in the block's per-local-expert masks.
 template <int KMAX, int LPT, class Get>
 __device__ __forceinline__ void route_token(const RouteParams& p, int64_t t, int tl, int q, Get get,
                                             unsigned long long* mask) {
+  static_assert(KMAX == 8, "the selection keeps the best 8");
   float tv[KMAX];
   int ti[KMAX];
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    tv[j] = -INFINITY;
-    ti[j] = 0x7fffffff;
-  }
-  // 8 of the lane's logits are read at a time, then inserted: the loads of a batch are in flight
-  // together (one at a time, each insertion waited for its own load)
-  for (int e0 = q; e0 < p.E; e0 += 8 * LPT) {
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = e0 + i * LPT < p.E ? get(e0 + i * LPT) : -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (e0 + i * LPT < p.E) topk_insert<KMAX>(tv, ti, v[i], e0 + i * LPT);
-  }
-  // merge with the partner lane's list: the better of tv[j] and the partner's [KMAX-1-j]
-  // leaves the top KMAX of both lists as a bitonic sequence, which three half-cleaner stages sort
-#pragma unroll
-  for (int step = 1; step < LPT; step <<= 1) {
-    float ov[KMAX];
-    int oi[KMAX];
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      ov[j] = __shfl_xor(tv[j], step);
-      oi[j] = __shfl_xor(ti[j], step);
-    }
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      const bool b = better(tv[j], ti[j], ov[KMAX - 1 - j], oi[KMAX - 1 - j]);
-      tv[j] = b ? tv[j] : ov[KMAX - 1 - j];
-      ti[j] = b ? ti[j] : oi[KMAX - 1 - j];
-    }
-#pragma unroll
-    for (int d = KMAX / 2; d >= 1; d >>= 1)
-#pragma unroll
-      for (int j = 0; j < KMAX; ++j)
-        if ((j & d) == 0) {
-          const bool b = better(tv[j], ti[j], tv[j + d], ti[j + d]);
-          const float v0 = b ? tv[j] : tv[j + d], v1 = b ? tv[j + d] : tv[j];
-          const int i0 = b ? ti[j] : ti[j + d], i1 = b ? ti[j + d] : ti[j];
-          tv[j] = v0;
-          tv[j + d] = v1;
-          ti[j] = i0;
-          ti[j + d] = i1;
-        }
-  }
+  select_top8<LPT>(p.E, q, get, tv, ti);
   // renormalised softmax over the chosen k, summed in slot order
   float z[KMAX], sum = 0.f;
 #pragma unroll
