@@ -267,13 +267,12 @@ __device__ __forceinline__ void store_transposed_mx(const float* slab, int lane,
 #pragma unroll
     for (int r = 0; r < 32; ++r) m = fmaxf(m, fabsf(slab[r * Stage<NJ>::LD + c]));
     const int s = mx_exponent(m);
-    const float sm = mx_inv_scale(s);
+    const MxScale sc = mx_scale(s);
     unsigned w[8];
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       const float* col = slab + 4 * g * Stage<NJ>::LD + c;
-      w[g] = mx_cvt4(mx_sat(col[0] * sm), mx_sat(col[Stage<NJ>::LD] * sm), mx_sat(col[2 * Stage<NJ>::LD] * sm),
-                     mx_sat(col[3 * Stage<NJ>::LD] * sm));
+      w[g] = mx_cvt4(col[0], col[Stage<NJ>::LD], col[2 * Stage<NJ>::LD], col[3 * Stage<NJ>::LD], sc);
     }
     uint8_t* o = dst(c);
     if (o) {

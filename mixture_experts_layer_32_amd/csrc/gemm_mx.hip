@@ -187,12 +187,12 @@ __device__ __forceinline__ void store_transposed_fixed(const float* slab, int la
                                                        Sx sx) {
   for (int c = lane; c < ncol; c += 64) {
     const int s = sx(c);
-    const float sm = mx_inv_scale(s);
+    const MxScale sc = mx_scale(s);
     unsigned w[8];
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       const float* col = slab + 4 * g * SLD + c;
-      w[g] = mx_cvt4(mx_sat(col[0] * sm), mx_sat(col[SLD] * sm), mx_sat(col[2 * SLD] * sm), mx_sat(col[3 * SLD] * sm));
+      w[g] = mx_cvt4(col[0], col[SLD], col[2 * SLD], col[3 * SLD], sc);
     }
     uint8_t* o = dst(c);
     if (o) {

@@ -9,9 +9,8 @@
 //    even and saturated to +-448.
 // floor(log2 amax) of a normal fp32 amax is its biased exponent minus 127. Zero and subnormal amax
 // (below 2^-126) give biased exponent 0, and the clamp then yields -127, which is the value the
-// formula gives for them too. v * 2^-s is exact in fp32: the power of two is a normal number and
-// |v| 2^-s < 512. The hardware convert rounds to nearest even, but it turns values of magnitude
-// 464 or more into NaN, so values are clamped to +-448 before it.
+// formula gives for them too. v * 2^-s is exact: scaling by a power of two only moves the exponent
+// (|v| 2^-s < 512).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -23,21 +22,37 @@ __device__ __forceinline__ int mx_exponent(float amax) {
   return max(be - 127 - 8, -127);   // finite amax has be <= 254, so s <= 119
 }
 
-// 2^-s for s in [-127, 119]: biased exponent 127 - s lies in [8, 254]
-__device__ __forceinline__ float mx_inv_scale(int s) { return __uint_as_float((unsigned)(127 - s) << 23); }
+// The element encoding of a block with exponent s, on the hardware's scaled convert
+// (v_cvt_scalef32_pk_fp8_f32), which divides by its scale operand 2^s and rounds to nearest even. It
+// turns magnitudes of 464 2^s or more into NaN, so values are first clamped to +-448 2^s, in the
+// input's units (448 2^s is exact in fp32 for every s). One clamp and half a convert per element,
+// where scaling first took a multiply more. The quantiser tests hold it to the oracle's encoding byte
+// for byte, over block magnitudes 2^-140 .. 2^120 (subnormal blocks: s = -127), zero blocks and
+// saturating blocks.
+struct MxScale {
+  float up;    // 2^s; 2^-127 is the subnormal 0x00400000
+  float lim;   // 448 2^s
+};
+__device__ __forceinline__ MxScale mx_scale(int s) {
+  const float up = s > -127 ? __uint_as_float((unsigned)(127 + s) << 23) : __uint_as_float(0x00400000u);
+  return {up, 448.f * up};
+}
 
-__device__ __forceinline__ float mx_sat(float v) { return fminf(fmaxf(v, -448.f), 448.f); }
+// the median of v, -lim and lim: one v_med3_f32
+__device__ __forceinline__ float mx_clamp(float v, const MxScale& c) { return __builtin_amdgcn_fmed3f(v, -c.lim, c.lim); }
 
-// four fp32 values (already scaled and saturated) -> four E4M3 bytes, first value in the low byte
-__device__ __forceinline__ unsigned mx_cvt4(float a, float b, float c, float d) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+// four fp32 values of a block -> four E4M3 bytes, first value in the low byte
+__device__ __forceinline__ unsigned mx_cvt4(float a, float b, float c, float d, const MxScale& sc) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  v2s o = {0, 0};
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, mx_clamp(a, sc), mx_clamp(b, sc), sc.up, false);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, mx_clamp(c, sc), mx_clamp(d, sc), sc.up, true);
+  return __builtin_bit_cast(unsigned, o);
 }
 
 __device__ __forceinline__ uint2 mx_encode8(const float (&v)[8], int s) {
-  const float m = mx_inv_scale(s);
-  return make_uint2(mx_cvt4(mx_sat(v[0] * m), mx_sat(v[1] * m), mx_sat(v[2] * m), mx_sat(v[3] * m)),
-                    mx_cvt4(mx_sat(v[4] * m), mx_sat(v[5] * m), mx_sat(v[6] * m), mx_sat(v[7] * m)));
+  const MxScale sc = mx_scale(s);
+  return make_uint2(mx_cvt4(v[0], v[1], v[2], v[3], sc), mx_cvt4(v[4], v[5], v[6], v[7], sc));
 }
 
 // Blockwise FP8 (the FP8 mode; the same pages list a blockwise-scaled FP8 without block sizes). The

@@ -75,11 +75,10 @@ __device__ __forceinline__ void column_pass(const bf16 (*tile)[64], uint8_t* out
     m = fmaxf(fmaxf(cmax[c], cmax[64 + c]), fmaxf(cmax[128 + c], cmax[192 + c]));
   }
   const int s = block_exponent<BLK>(m);
-  const float sm = mx_inv_scale(s);
+  const MxScale sc = mx_scale(s);
   unsigned w[8];
 #pragma unroll
-  for (int g = 0; g < 8; ++g)
-    w[g] = mx_cvt4(mx_sat(v[4 * g] * sm), mx_sat(v[4 * g + 1] * sm), mx_sat(v[4 * g + 2] * sm), mx_sat(v[4 * g + 3] * sm));
+  for (int g = 0; g < 8; ++g) w[g] = mx_cvt4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3], sc);
   uint4* o = reinterpret_cast<uint4*>(out_row + 32 * blk);
   o[0] = make_uint4(w[0], w[1], w[2], w[3]);
   o[1] = make_uint4(w[4], w[5], w[6], w[7]);
@@ -133,11 +132,10 @@ __device__ __forceinline__ void column_pass128(const bf16 (*tile)[128], uint8_t*
       m = fmaxf(m, fabsf(v[r]));
     }
     const int s = BLK ? s_tile : mx_exponent(m);
-    const float sm = mx_inv_scale(s);
+    const MxScale sc = mx_scale(s);
     unsigned w[8];
 #pragma unroll
-    for (int g = 0; g < 8; ++g)
-      w[g] = mx_cvt4(mx_sat(v[4 * g] * sm), mx_sat(v[4 * g + 1] * sm), mx_sat(v[4 * g + 2] * sm), mx_sat(v[4 * g + 3] * sm));
+    for (int g = 0; g < 8; ++g) w[g] = mx_cvt4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3], sc);
     st16(out_row + 32 * blk, make_uint4(w[0], w[1], w[2], w[3]));
     st16(out_row + 32 * blk + 16, make_uint4(w[4], w[5], w[6], w[7]));
     sc_row[blk] = (uint8_t)(s + 127);
