@@ -13,8 +13,8 @@
 // at E = 128, H = 2048) stays in L2. A stage carries little arithmetic per wave (RB / 32 MFMA steps
 // of NB blocks), so even and odd steps accumulate into two sets of registers (two dependency chains
 // instead of one), added at the end, and the fragments of the next step are read while the current
-// one multiplies. The first form of this kernel, 64-byte-deep stages with two barriers each and one
-// chain, took 36 us at the 30B-A3B shape.
+// one multiplies. At the 30B-A3B shape this takes 32 us (22 us without the top-k), against 36 us for
+// the first form of the kernel (128-byte-deep stages with two barriers each and one chain).
 #include "engine.h"
 #include "moe_internal.h"
 #include "route_device.h"
