@@ -225,3 +225,39 @@ def test_fwd_router_fused_benchmark_shape():
     for n in ("idx", "counts", "offsets", "perm", "pair_pos"):
         assert np.array_equal(rt[n], r[n]), n
     assert oracle.rel_frobenius(lg_np, oracle.router_forward(x_np, wr)) <= TOL_LOGITS
+
+
+@pytest.mark.parametrize("mode", ["bf16", "mxfp8"])
+def test_fwd_router_then_recomputing_backward(mode):
+    """moe_fwd_router under activation checkpointing (recompute = 1), then moe_bwd: every gradient is
+    bitwise the one of the stored-activation layer run on the same logits, and the layer matches the
+    oracle on the logits the fused call returned."""
+    T, H, F, E, k = 333, 512, 256, 64, 4
+    print(f"case fwd_router + recompute mode={mode}", flush=True)
+    cfg, L = inputs.custom_layer(T=T, H=H, F=F, E=E, k=k, seed=71)
+    wr = inputs.router_weight(cfg)
+    dt = torch.bfloat16
+    x, wrd, dy = to_dev(L["x"], dt), to_dev(wr, dt), to_dev(L["dy"], dt)
+    wg, wu, wd = to_dev(L["wg"], dt), to_dev(L["wu"], dt), to_dev(L["wd"], dt)
+    ck = MoELayer(T, H, F, E, k, mode, recompute=True)
+    y, lg = ck.forward_router(x, wrd, wg, wu, wd)
+    g = ck.backward(dy, x, wg, wu, wd)
+    ref = MoELayer(T, H, F, E, k, mode)
+    y2 = ref.forward(x, lg, wg, wu, wd)
+    g2 = ref.backward(dy, x, wg, wu, wd)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    for n in ("dx", "dw_gate", "dw_up", "dw_down"):
+        assert torch.equal(g[n].view(torch.int16), g2[n].view(torch.int16)), n
+    assert torch.equal(g["dlogits"], g2["dlogits"])
+    lg_np = lg.cpu().numpy()
+    args = dict(x=L["x"], logits=lg_np, wg=L["wg"], wu=L["wu"], wd=L["wd"], k=k,
+                mode=None if mode == "bf16" else mode)
+    ry, _ = oracle.forward(**args)
+    rg, _ = oracle.backward(dy=L["dy"], **args)
+    tol = 1e-2 if mode == "bf16" else 5e-2
+    for n, got, want in (("y", y, ry), ("dx", g["dx"], rg["dx"]), ("dlogits", g["dlogits"], rg["dlogits"]),
+                         ("dw_gate", g["dw_gate"], rg["dwg"]), ("dw_up", g["dw_up"], rg["dwu"]),
+                         ("dw_down", g["dw_down"], rg["dwd"])):
+        err = oracle.rel_frobenius(got.float().cpu().numpy(), want)
+        assert err <= tol, (n, err)
