@@ -9,9 +9,9 @@
 // sequence of fp32 operations, so runs are bitwise reproducible.
 //
 // Kernels (one stream, no host round trip):
-//   k_route_topk     k <= 8: 64 tokens per block, 8 lanes per token; each lane keeps a sorted list
-//                    of its eighth of the experts (value desc, index asc), three shuffle steps merge
-//                    the lists.
+//   k_route_topk     k <= 8: 64 tokens per block, 8 lanes per token; each lane sorts its eighth of
+//                    the experts 8 at a time by sorting networks on 64-bit (logit, index) keys into
+//                    a top-8 list, three shuffle steps merge the lists (route_device.h).
 //   k_route_topk_wave  k > 8: one wavefront per token, k rounds of a wave-wide argmax.
 //                    Both write, per block and local expert, a 64-bit mask of the tokens that chose it.
 //   k_route_colscan  one block per local expert: exclusive scan of the per-block counts.
@@ -51,7 +51,8 @@ __device__ __forceinline__ int block_incl_scan(int v, int* lds, int& total) {
 }
 
 // k <= 8: 64 tokens per block, LPT lanes per token (route_token). LPT = 8 took 20 us against 23 us
-// with 4 at T = 16384, E = 128; LPT = 16 sent the compiler into a build of more than 15 minutes.
+// with 4 at T = 16384, E = 128 (one candidate inserted at a time; the sorting networks then took it
+// to 14.5 us); LPT = 16 sent the compiler into a build of more than 15 minutes.
 template <int KMAX, int LPT>
 __global__ __launch_bounds__(64 * LPT) void k_route_topk(RouteParams p) {
   constexpr int NT = 64 * LPT;
