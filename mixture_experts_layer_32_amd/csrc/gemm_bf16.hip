@@ -542,9 +542,7 @@ __device__ __forceinline__ void dh_tile(const BwdParams& p, char* smem, int tile
         *reinterpret_cast<float4*>(slab + rl * LD + c0 + 4) = make_float4(da[4], da[5], da[6], da[7]);
         *reinterpret_cast<float4*>(slab2 + rl * LD + c0) = make_float4(db[0], db[1], db[2], db[3]);
         *reinterpret_cast<float4*>(slab2 + rl * LD + c0 + 4) = make_float4(db[4], db[5], db[6], db[7]);
-        gsum += __shfl_xor(gsum, 1);
-        gsum += __shfl_xor(gsum, 2);
-        gsum += __shfl_xor(gsum, 4);
+        gsum = group_sum8(gsum);
         if (r < seg_end && (lane & 7) == 0) p.gpart[(size_t)(nt * 4 + wn) * p.rows + r] = gsum;
       }
       const int colb = colq + 32 * i;

@@ -265,9 +265,7 @@ __device__ __forceinline__ void epilogue_gateup_blk(const FwdParams& p, const f3
       float m = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(hv[e]));
-      m = fmaxf(m, __shfl_xor(m, 1));
-      m = fmaxf(m, __shfl_xor(m, 2));
-      m = fmaxf(m, __shfl_xor(m, 4));
+      m = group_max8(m);
       if ((lane & 7) == 0) rmax[w * 128 + 32 * i + (lane >> 3) + 8 * s] = m;
       put_slab(s, hv);
     }
@@ -502,10 +500,7 @@ __device__ __forceinline__ void epilogue_dh_blk(const BwdParams& p, const f32x16
         }
       }
       put_slabs(s, da, db);
-      gsum += __shfl_xor(gsum, 1);
-      gsum += __shfl_xor(gsum, 2);
-      gsum += __shfl_xor(gsum, 4);
-      gsum += __shfl_xor(gsum, 8);
+      gsum = group_sum16(gsum);
       if (r < seg_end && (lane & 15) == 0) p.gpart[(size_t)(nt * 2 + wn) * p.rows + r] = gsum;
     }
     cm[0] = fmaxf(cm[0], column_amax(slab, lane));
@@ -644,10 +639,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_dh_mx(BwdParams p) {
         *reinterpret_cast<float4*>(slab + rl * SLD + c0 + 4) = make_float4(da[4], da[5], da[6], da[7]);
         *reinterpret_cast<float4*>(slab2 + rl * SLD + c0) = make_float4(db[0], db[1], db[2], db[3]);
         *reinterpret_cast<float4*>(slab2 + rl * SLD + c0 + 4) = make_float4(db[4], db[5], db[6], db[7]);
-        gsum += __shfl_xor(gsum, 1);
-        gsum += __shfl_xor(gsum, 2);
-        gsum += __shfl_xor(gsum, 4);
-        gsum += __shfl_xor(gsum, 8);
+        gsum = group_sum16(gsum);
         if (r < seg_end && (lane & 15) == 0) p.gpart[(size_t)(nt * 2 + wn) * p.rows + r] = gsum;
       }
       const int colb = colq + 32 * i;

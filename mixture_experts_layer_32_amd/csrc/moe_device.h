@@ -309,6 +309,41 @@ __device__ __forceinline__ void combine_row_part(const T* __restrict__ src, int 
   }
 }
 
+// Cross-lane moves inside a 16-lane row through DPP (a VALU source modifier: no LDS round trip, unlike
+// __shfl, which compiles to ds_bpermute_b32). Every lane of the row must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp_mov(unsigned v) {
+  return (unsigned)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, false);
+}
+constexpr int kDppXor1 = 0xb1;         // quad_perm [1,0,3,2]: the lane's xor-1 partner
+constexpr int kDppXor2 = 0x4e;         // quad_perm [2,3,0,1]: xor 2
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror: lane i of each 8 takes lane 7 - i
+constexpr int kDppMirror = 0x140;      // row_mirror: lane i of each 16 takes lane 15 - i
+// Sum over aligned groups of 8 (16) lanes, every lane getting the group's sum. The last step takes
+// the mirrored lane instead of the xor-4 (xor-8) one: after the quad steps all lanes of a quad hold
+// the same bits, so the additions are the ones of a xor butterfly, bit for bit.
+__device__ __forceinline__ float group_sum8(float v) {
+  v += dpp_mov<kDppXor1>(v);
+  v += dpp_mov<kDppXor2>(v);
+  return v + dpp_mov<kDppHalfMirror>(v);
+}
+__device__ __forceinline__ float group_sum16(float v) {
+  v = group_sum8(v);
+  return v + dpp_mov<kDppMirror>(v);
+}
+__device__ __forceinline__ float quad_max(float m) {
+  m = fmaxf(m, dpp_mov<kDppXor1>(m));
+  return fmaxf(m, dpp_mov<kDppXor2>(m));
+}
+__device__ __forceinline__ float group_max8(float m) {
+  m = quad_max(m);
+  return fmaxf(m, dpp_mov<kDppHalfMirror>(m));
+}
+
 // sigma(z) = 1 / (1 + e^-z), with the hardware reciprocal (v_rcp_f32, about 1 ulp) instead of an
 // IEEE division: the division's scale/Newton/fixup sequence was about ten instructions per element
 // in the SwiGLU and dSwiGLU epilogues, whose VALU work the matrix cores wait on. For large -z the

@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "moe_device.h"
+
 namespace moe {
 
 __device__ __forceinline__ int mx_exponent(float amax) {
@@ -77,17 +79,15 @@ __device__ __forceinline__ float mx_amax_x4(const float (&v)[8]) {
   float m = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
-  m = fmaxf(m, __shfl_xor(m, 1));
-  m = fmaxf(m, __shfl_xor(m, 2));
-  return m;
+  return quad_max(m);
 }
 
 // Largest magnitude of a block of 128 held as 8 values by each of 16 consecutive lanes.
 // Every lane of the wave must execute it.
 __device__ __forceinline__ float mx_amax_x16(const float (&v)[8]) {
   float m = mx_amax_x4(v);
-  m = fmaxf(m, __shfl_xor(m, 4));
-  m = fmaxf(m, __shfl_xor(m, 8));
+  m = fmaxf(m, dpp_mov<kDppHalfMirror>(m));   // the quads of the group hold their maxima
+  m = fmaxf(m, dpp_mov<kDppMirror>(m));
   return m;
 }
 

@@ -58,10 +58,23 @@ __device__ __forceinline__ void key_merge8(unsigned long long (&t)[8], const uns
       if ((j & d) == 0) key_ce(t[j], t[j + d]);
 }
 
+// t becomes the merge of t and the list of the lane that DPP control CTRL selects (a butterfly step:
+// the merge is symmetric, so both lanes end with the same list)
+template <int CTRL>
+__device__ __forceinline__ void merge_partner(unsigned long long (&t)[8]) {
+  unsigned long long o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    o[j] = ((unsigned long long)dpp_mov<CTRL>((unsigned)(t[j] >> 32)) << 32) | dpp_mov<CTRL>((unsigned)t[j]);
+  key_merge8(t, o);
+}
+
 // Best 8 of experts 0..E-1 (logit e from get(e)) by LPT lanes of a token, lane q taking experts q,
 // q + LPT, ...: each lane sorts its candidates 8 at a time and merges them into its list, then log2(LPT)
-// butterfly steps merge the lanes' lists, after which every lane of the token holds the token's best 8
-// (slots past E hold key 0 and come last).
+// butterfly steps merge the lanes' lists (DPP moves: partners xor 1, xor 2, then the mirrored lane of
+// the 8, which after the quad steps holds the same list as the xor-4 one), after which every lane of
+// the token holds the token's best 8 (slots past E hold key 0 and come last). The token's lanes must
+// all be active.
 template <int LPT, class Get>
 __device__ __forceinline__ void select_top8(int E, int q, Get get, float (&tv)[8], int (&ti)[8]) {
   unsigned long long t[8];
@@ -77,16 +90,10 @@ __device__ __forceinline__ void select_top8(int E, int q, Get get, float (&tv)[8
     key_sort8(c);
     key_merge8(t, c);
   }
-#pragma unroll
-  for (int step = 1; step < LPT; step <<= 1) {
-    unsigned long long o[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const unsigned lo = __shfl_xor((unsigned)t[j], step), hi = __shfl_xor((unsigned)(t[j] >> 32), step);
-      o[j] = ((unsigned long long)hi << 32) | lo;
-    }
-    key_merge8(t, o);
-  }
+  static_assert(LPT == 1 || LPT == 2 || LPT == 4 || LPT == 8, "lanes per token");
+  if constexpr (LPT > 1) merge_partner<kDppXor1>(t);
+  if constexpr (LPT > 2) merge_partner<kDppXor2>(t);
+  if constexpr (LPT > 4) merge_partner<kDppHalfMirror>(t);   // the quads' lists are merged by now
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     tv[j] = key_value(t[j]);
