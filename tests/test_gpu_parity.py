@@ -33,9 +33,10 @@ def check_routing(cfg, L, rt):
     return r
 
 
-def oracle_full(cfg, L):
+def oracle_full(cfg, L, mode="bf16"):
+    """The float64 oracle's outputs; in the fp8 modes it quantises at the kernels' points (mode=...)."""
     args = dict(x=L["x"], logits=L["logits"], wg=L["wg"], wu=L["wu"], wd=L["wd"], k=cfg.k, e0=cfg.e0,
-                e_local=cfg.el)
+                e_local=cfg.el, mode=None if mode in ("fp32", "bf16") else mode)
     y, _ = oracle.forward(**args)
     g, _ = oracle.backward(dy=L["dy"], **args)
     return dict(y=y, dx=g["dx"], dlogits=g["dlogits"], dwg=g["dwg"], dwu=g["dwu"], dwd=g["dwd"])
@@ -130,7 +131,7 @@ def full_check(cfg, L, got, mode="bf16"):
     y, dx and dlogits, and the whole-tensor bar on every expert's dW_gate, dW_up and dW_down."""
     r = check_routing(cfg, L, got["routing"])
     print(f"case {cfg.name}: float64 oracle on the host", flush=True)
-    ref = oracle_full(cfg, L)
+    ref = oracle_full(cfg, L, mode)
     errs = {n: oracle.rel_frobenius(got[n], ref[n]) for n in OUTS}
     # A dlogits row is w_j (g_j - sum_i w_i g_i) over the token's chosen experts, with g_j = <dY_t, o_tj>:
     # its size follows how far the router gradients cancel (in an expert share a row can hang on one
