@@ -15,7 +15,10 @@
 //                     expert's tokens, in the sorted pair order, into [H][Q] where the expert's
 //                     pairs occupy columns qoff[e] .. qoff[e+1] (zero-padded to a multiple of 128).
 // The transposing kernels stage 128 x 64 tiles (k_quant_both: 128 x 128) in LDS, so that every
-// row segment they read or write is one or two whole 128-byte lines.
+// row segment they read or write is one or two whole 128-byte lines. Their scale bytes are the
+// exception: a tile writes 4 of them per row, so a 128-byte line of scales is filled by many
+// blocks. Their grids are one-dimensional with consecutive tiles on one XCD (xcd_logical_block),
+// so that those blocks meet in one L2, which merges the line before writing it back.
 // The quantised element and scale formulas are in mx_device.h.
 //
 // Blockwise FP8 (template flag BLK): k_quant_rows takes blocks of 128 along the row (16 lanes),
@@ -28,6 +31,20 @@
 
 namespace moe {
 namespace {
+
+// tile (x, y, b) of a grid of nx x ny x B tiles run as a one-dimensional grid: logical tile ids, x
+// fastest, then y, then b, in contiguous ranges per XCD
+struct Tile3 {
+  int x, y, b;
+};
+__device__ __forceinline__ Tile3 tile_of_block(int nx, int ny) {
+  const int n = xcd_logical_block(gridDim.x);
+  Tile3 t;
+  t.x = n % nx;
+  t.y = (n / nx) % ny;
+  t.b = n / (nx * ny);
+  return t;
+}
 
 __device__ __forceinline__ void unpack8f(uint4 u, float (&v)[8]) {
   const bf16x8 b = __builtin_bit_cast(bf16x8, u);
@@ -100,11 +117,12 @@ __device__ __forceinline__ void load_tile(bf16 (*tile)[64], RowPtr row_ptr, uint
 }
 
 // in [B][R][C] -> out[b][c][col0 + r] (row stride ldo bytes), scales [b][c][(col0 + r) / 32]
-// (row stride ldo / 32). Grid (C / 64, R / 128, B).
+// (row stride ldo / 32). Tiles (C / 64, R / 128, B).
 __global__ __launch_bounds__(256) void k_quant_cols(const bf16* __restrict__ in, uint8_t* __restrict__ q,
                                                     uint8_t* __restrict__ sc, int R, int C, int64_t ldo, int col0) {
   __shared__ __attribute__((aligned(16))) bf16 tile[128][64];
-  const int b = blockIdx.z, r0 = blockIdx.y * 128, c0 = blockIdx.x * 64;
+  const Tile3 tt = tile_of_block(C / 64, R / 128);
+  const int b = tt.b, r0 = tt.y * 128, c0 = tt.x * 64;
   const bf16* src = in + ((size_t)b * R + r0) * C + c0;
   uint4 raw[4];
   load_tile(tile, [&](int row) { return src + (size_t)row * C; }, raw);
@@ -142,12 +160,13 @@ __device__ __forceinline__ void column_pass128(const bf16 (*tile)[128], uint8_t*
   }
 }
 
-// As k_quant_cols on 128 x 128 tiles (C a multiple of 128): grid (C / 128, R / 128, B). The two
+// As k_quant_cols on 128 x 128 tiles (C a multiple of 128): tiles (C / 128, R / 128, B). The two
 // threads of a column write one whole 128-byte line; the input is read once (non-temporal loads).
 __global__ __launch_bounds__(256) void k_quant_cols128(const bf16* __restrict__ in, uint8_t* __restrict__ q,
                                                        uint8_t* __restrict__ sc, int R, int C, int64_t ldo, int col0) {
   __shared__ __attribute__((aligned(16))) bf16 tile[128][128];
-  const int t = threadIdx.x, b = blockIdx.z, r0 = blockIdx.y * 128, c0 = blockIdx.x * 128;
+  const Tile3 tt = tile_of_block(C / 128, R / 128);
+  const int t = threadIdx.x, b = tt.b, r0 = tt.y * 128, c0 = tt.x * 128;
   const bf16* src = in + ((size_t)b * R + r0) * C + c0;
   const int col8 = (t & 15) * 8;
 #pragma unroll
@@ -164,7 +183,7 @@ __global__ __launch_bounds__(256) void k_quant_cols128(const bf16* __restrict__ 
 //   rows: qr [B][R][C] with blocks of 32 along C, scales sr [B][R][C/32]
 //   cols: blocks of 32 along R, written transposed at column col0 of rows of ldo bytes:
 //         qc [B][C][ldo], scales scc [B][C][ldo/32]
-// Grid (C / 128, R / 128, B). A block stages a 128 x 128 bf16 tile (32 KB), so that the row pass
+// Tiles (C / 128, R / 128, B). A block stages a 128 x 128 bf16 tile (32 KB), so that the row pass
 // writes whole 128-byte lines of fp8 (16 lanes per row, quantised from the registers that loaded
 // the tile) and the column pass too (each thread quantises two blocks of 32 of one column). The
 // input is read once: non-temporal loads. The stores stay ordinary: each instruction writes less
@@ -175,7 +194,8 @@ __global__ __launch_bounds__(256) void k_quant_both(const bf16* __restrict__ in,
                                                     uint8_t* __restrict__ sr, uint8_t* __restrict__ qc,
                                                     uint8_t* __restrict__ scc, int R, int C, int64_t ldo, int col0) {
   __shared__ __attribute__((aligned(16))) bf16 tile[128][128];
-  const int t = threadIdx.x, b = blockIdx.z, r0 = blockIdx.y * 128, c0 = blockIdx.x * 128;
+  const Tile3 tt = tile_of_block(C / 128, R / 128);
+  const int t = threadIdx.x, b = tt.b, r0 = tt.y * 128, c0 = tt.x * 128;
   const bf16* src = in + ((size_t)b * R + r0) * C + c0;
   const int col8 = (t & 15) * 8;
   uint4 raw[8];
@@ -220,11 +240,11 @@ __global__ __launch_bounds__(256) void k_quant_both(const bf16* __restrict__ in,
   column_pass128<BLK>(tile, qc + orow * ldo + col0 + r0, scc + orow * (ldo / 32) + (col0 + r0) / 32, s_tile);
 }
 
-// Grid (qc / 128, GT_SPLIT). Window w covers columns 128w .. 128w+127 of [H][qc], inside one
-// expert's padded segment (segments are multiples of 128 columns). A block finds its expert and the
-// window's 128 token indices once, then walks the 64-column tiles h0 = 64 (blockIdx.y + GT_SPLIT j)
-// of H: the next tile's rows load while the current one is quantised. (128 x 128 tiles measured
-// 10-15 % slower here.)
+// Blocks (window w, split s) for w < qc / 128, s < GT_SPLIT, logical id s (qc / 128) + w. Window w
+// covers columns 128w .. 128w+127 of [H][qc], inside one expert's padded segment (segments are
+// multiples of 128 columns). A block finds its expert and the window's 128 token indices once, then
+// walks the 64-column tiles h0 = 64 (s + GT_SPLIT j) of H: the next tile's rows load while the
+// current one is quantised. (128 x 128 tiles measured 10-15 % slower here.)
 constexpr int GT_SPLIT = 4;
 template <bool BLK>
 __global__ __launch_bounds__(256) void k_gather_t_quant(const bf16* __restrict__ x, const int* __restrict__ ptok,
@@ -233,7 +253,8 @@ __global__ __launch_bounds__(256) void k_gather_t_quant(const bf16* __restrict__
                                                         uint8_t* __restrict__ sc) {
   __shared__ __attribute__((aligned(16))) bf16 tile[128][64];
   __shared__ float cmax[BLK ? 256 : 1];
-  const int q0 = blockIdx.x * 128;
+  const int nwin = (int)(qc / 128), n = xcd_logical_block(gridDim.x), split = n / nwin;
+  const int q0 = (n - split * nwin) * 128;
   if (q0 >= qoff[El]) return;   // past the last expert's segment: nothing reads these columns
   int lo = 0, hi = El - 1;      // the expert whose segment holds q0: the last e with qoff[e] <= q0
   while (lo < hi) {
@@ -254,7 +275,7 @@ __global__ __launch_bounds__(256) void k_gather_t_quant(const bf16* __restrict__
     for (int i = 0; i < 4; ++i) raw[i] = src[i] ? ld16(src[i] + h0) : make_uint4(0u, 0u, 0u, 0u);
   };
   uint4 raw[4], nxt[4];
-  int h0 = 64 * blockIdx.y;
+  int h0 = 64 * split;
   if (h0 >= H) return;
   load(h0, nxt);
   for (; h0 < H; h0 += 64 * GT_SPLIT) {
@@ -291,9 +312,9 @@ hipError_t launch_quant_cols(const void* in, uint8_t* q, uint8_t* sc, int B, int
                              const char* name, hipStream_t s) {
   prof_mark_begin(name, s);
   if (C % 128 == 0)
-    k_quant_cols128<<<dim3(C / 128, R / 128, B), 256, 0, s>>>(static_cast<const bf16*>(in), q, sc, R, C, ldo, col0);
+    k_quant_cols128<<<(C / 128) * (R / 128) * B, 256, 0, s>>>(static_cast<const bf16*>(in), q, sc, R, C, ldo, col0);
   else
-    k_quant_cols<<<dim3(C / 64, R / 128, B), 256, 0, s>>>(static_cast<const bf16*>(in), q, sc, R, C, ldo, col0);
+    k_quant_cols<<<(C / 64) * (R / 128) * B, 256, 0, s>>>(static_cast<const bf16*>(in), q, sc, R, C, ldo, col0);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   prof_mark_end(s);
@@ -303,7 +324,7 @@ hipError_t launch_quant_cols(const void* in, uint8_t* q, uint8_t* sc, int B, int
 hipError_t launch_quant_both(const void* in, uint8_t* qr, uint8_t* sr, uint8_t* qc, uint8_t* scc, int B, int R, int C,
                              int64_t ldo, int col0, const char* name, hipStream_t s, bool blk) {
   prof_mark_begin(name, s);
-  const dim3 grid(C / 128, R / 128, B);
+  const unsigned grid = (C / 128) * (R / 128) * B;
   if (blk)
     k_quant_both<true><<<grid, 256, 0, s>>>(static_cast<const bf16*>(in), qr, sr, qc, scc, R, C, ldo, col0);
   else
@@ -317,7 +338,7 @@ hipError_t launch_quant_both(const void* in, uint8_t* qr, uint8_t* sr, uint8_t* 
 hipError_t launch_gather_t_quant(const void* x, const int* ptok, const int* offsets, const int* qoff, int El, int H,
                                  int64_t qc, uint8_t* q, uint8_t* sc, const char* name, hipStream_t s, bool blk) {
   prof_mark_begin(name, s);
-  const dim3 grid((unsigned)(qc / 128), GT_SPLIT);
+  const unsigned grid = (unsigned)(qc / 128) * GT_SPLIT;
   if (blk)
     k_gather_t_quant<true><<<grid, 256, 0, s>>>(static_cast<const bf16*>(x), ptok, offsets, qoff, El, H, qc, q, sc);
   else
