@@ -233,8 +233,9 @@ moe_status moe_router_bwd(const moe_desc* d, const void* x, const void* w_router
  *   qoff      int32 [E_local+1] first column of each expert's segment in the pair-contiguous
  *                              copies; each segment is padded with zeros to a multiple of 128
  *   qcols     (value)          column count Q of the pair-contiguous copies
- *   hwt, hwt_scales            w*h transposed, [F, Q] and [F, Q/32]: blocks of 32 along each
- *                              expert's pairs
+ *   hwt, hwt_scales            w*h transposed, [F, Q], blocks of 32 along each expert's pairs;
+ *                              scales K-tile-major, [Q/128, F, 4]: the byte of row f, pair
+ *                              column q at ((q/128) F + f) 4 + (q/32) % 4
  *   wdt, wdt_scales            (MXFP8) W_down[e] along H, transposed: [E_local, F, H], [E_local, F, H/32]
  *   wgut, wgut_scales          (MXFP8) [W_gate[e]^T | W_up[e]^T] along F: [E_local, H, 2F],
  *                              [E_local, H, 2F/32]

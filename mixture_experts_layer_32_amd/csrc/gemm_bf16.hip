@@ -397,7 +397,7 @@ __global__ __launch_bounds__(NTHR8, 1) void k_gateup_bf16(FwdParams p) {
       if (QT)   // (selected only with a copy to write)
         store_transposed_mx(
             slab, lane, 64, [&](int c) { return colb < qend ? p.hwtq + (size_t)(f0 + c) * p.qc + colb : nullptr; },
-            [&](int c) { return p.hwts + (size_t)(f0 + c) * (p.qc / 32) + colb / 32; });
+            [&](int c) { return p.hwts + tscale_at(F, f0 + c, colb); });
       else if (hwt)
         store_transposed(slab, lane, 64, [&](int c) { return colb < qend ? hwt + (size_t)(f0 + c) * p.qc + colb : nullptr; });
     }

@@ -12,9 +12,11 @@
 //    engine's (engine.h); step s reads chunks 4s + l/32 and 4s + 2 + l/32 of each row. The ring
 //    has 2 stages of 66 KB.
 //  * Every operand is K-major. The quantise kernels and the GEMM epilogues write them that way,
-//    with scales in [rows][K/32] byte arrays. A K-tile's 4 scale bytes of a row are one dword at
-//    column cbase + 4kt (scale bases and row lengths are multiples of 4 bytes: rows of H/32, F/32,
-//    2F/32 or Q/32 bytes, expert segments padded to 128 pairs). Per stage, each thread moves one
+//    with scales in [rows][K/32] byte arrays, except the pair-contiguous copies (K = the pairs),
+//    whose scales are K-tile-major, [Q/128][rows][4] (tscale_at). Either way a K-tile's 4 scale
+//    bytes of a row are one dword, kstride bytes after the previous K-tile's (4, or 4 rows; scale
+//    bases and row lengths are multiples of 4 bytes: rows of H/32, F/32 or 2F/32 bytes, expert
+//    segments padded to 128 pairs). Per stage, each thread moves one
 //    scale dword per operand into LDS (global_load_lds_dword). Dword d of the stage's scale area
 //    holds the row of quadrant half d/128, 32-row block d%4 and row (d%128)/4 of that block. A lane
 //    reads the scales of its four 32-row blocks with one 16-byte LDS read, and takes byte
@@ -67,8 +69,9 @@ __device__ __forceinline__ int sc_row32() { return (threadIdx.x & 127) >> 2; }
 struct SOp {
   const uint8_t* row;
   int cbase;
+  int kstride = 4;   // bytes from one K-tile's scale dword to the next: 4 in [rows][K/32] arrays
   __device__ __forceinline__ void issue(char* area, int kt) const {
-    gl2lds_dword(row + cbase + 4 * kt, area + wave_id() * 256);
+    gl2lds_dword(row + cbase + (size_t)kstride * kt, area + wave_id() * 256);
   }
 };
 
@@ -225,7 +228,7 @@ __device__ __forceinline__ float column_amax(const float* slab, int c) {
 // and writes both fp8 copies with those scales.
 __device__ __forceinline__ void epilogue_gateup_blk(const FwdParams& p, const f32x16 (&acc)[4][4], char* smem,
                                                     float* slab, const float (&wrow)[4], int lane, int w, int wm,
-                                                    int r0, int seg_end, int f0, int qend, int colq, int64_t qs) {
+                                                    int r0, int seg_end, int f0, int qend, int colq) {
   bf16* __restrict__ ab = static_cast<bf16*>(p.ab);
   const int F = p.F;
   float* rmax = reinterpret_cast<float*>(smem) + 4 * SLAB;   // [4 waves][128 rows]
@@ -297,7 +300,7 @@ __device__ __forceinline__ void epilogue_gateup_blk(const FwdParams& p, const f3
     if (p.hwtq)
       store_transposed_fixed(
         slab, lane, 64, [&](int c) { return colb < qend ? p.hwtq + (size_t)(f0 + c) * p.qc + colb : nullptr; },
-        [&](int c) { return p.hwts + (size_t)(f0 + c) * qs + colb / 32; }, [&](int) { return scol; });
+        [&](int c) { return p.hwts + tscale_at(F, f0 + c, colb); }, [&](int) { return scol; });
   };
   pass2(std::integral_constant<int, 0>{});
   pass2(std::integral_constant<int, 1>{});
@@ -344,9 +347,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_gateup_mx(FwdParams p) {
     const int f0 = nt * 128 + 64 * wn;
     const int qend = p.qoff[e + 1];
     const int colq = p.qoff[e] + (r0 - p.offsets[e]) + 128 * wm;
-    const int64_t qs = p.qc / 32;
     if constexpr (BLK) {
-      epilogue_gateup_blk(p, acc, smem, slab, wrow, lane, w, wm, r0, seg_end, f0, qend, colq, qs);
+      epilogue_gateup_blk(p, acc, smem, slab, wrow, lane, w, wm, r0, seg_end, f0, qend, colq);
       continue;
     }
 #pragma unroll
@@ -386,7 +388,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_gateup_mx(FwdParams p) {
       if (p.hwtq)
         store_transposed_mx(
             slab, lane, 64, [&](int c) { return colb < qend ? p.hwtq + (size_t)(f0 + c) * p.qc + colb : nullptr; },
-            [&](int c) { return p.hwts + (size_t)(f0 + c) * qs + colb / 32; });
+            [&](int c) { return p.hwts + tscale_at(F, f0 + c, colb); });
     }
   }
 }
@@ -431,7 +433,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_down_mx(FwdParams p) {
 // values) and writes the transposed copies with those scales.
 __device__ __forceinline__ void epilogue_dh_blk(const BwdParams& p, const f32x16 (&acc)[4][4], float* slab,
                                                 float* slab2, const float (&wrow)[4], int lane, int wm, int wn,
-                                                int nt, int r0, int seg_end, int fq, int qend, int colq, int64_t qs) {
+                                                int nt, int r0, int seg_end, int fq, int qend, int colq) {
   const bf16* __restrict__ ab = static_cast<const bf16*>(p.ab);
   const int F = p.F, f2s = 2 * F / 32;
   // a and b of the lane's 8 rows of a 32-row block. The 8 blocks (4 per pass) are processed in
@@ -526,11 +528,11 @@ __device__ __forceinline__ void epilogue_dh_blk(const BwdParams& p, const f32x16
     store_transposed_fixed(
         slab, lane, 128,
         [&](int c) { return colb < qend && fq + c < F ? p.dabtq + (size_t)(fq + c) * p.qc + colb : nullptr; },
-        [&](int c) { return p.dabts + (size_t)(fq + c) * qs + colb / 32; }, [&](int c) { return c < 64 ? sc[0] : sc[1]; });
+        [&](int c) { return p.dabts + tscale_at(2 * F, fq + c, colb); }, [&](int c) { return c < 64 ? sc[0] : sc[1]; });
     store_transposed_fixed(
         slab2, lane, 128,
         [&](int c) { return colb < qend && fq + c < F ? p.dabtq + (size_t)(F + fq + c) * p.qc + colb : nullptr; },
-        [&](int c) { return p.dabts + (size_t)(F + fq + c) * qs + colb / 32; },
+        [&](int c) { return p.dabts + tscale_at(2 * F, F + fq + c, colb); },
         [&](int c) { return c < 64 ? sc[2] : sc[3]; });
   };
   pass2(std::integral_constant<int, 0>{});
@@ -576,9 +578,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_dh_mx(BwdParams p) {
     const int fq = nt * TILE + 128 * wn;
     const int qend = p.qoff[e + 1];
     const int colq = p.qoff[e] + (r0 - p.offsets[e]) + 128 * wm;
-    const int64_t qs = p.qc / 32;
     if constexpr (BLK) {
-      epilogue_dh_blk(p, acc, slab, slab2, wrow, lane, wm, wn, nt, r0, seg_end, fq, qend, colq, qs);
+      epilogue_dh_blk(p, acc, slab, slab2, wrow, lane, wm, wn, nt, r0, seg_end, fq, qend, colq);
       continue;
     }
     // one 32-row block of the quadrant; i is a compile-time constant so that acc stays in registers
@@ -646,11 +647,11 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_dh_mx(BwdParams p) {
       store_transposed_mx(
           slab, lane, 128,
           [&](int c) { return colb < qend && fq + c < F ? p.dabtq + (size_t)(fq + c) * p.qc + colb : nullptr; },
-          [&](int c) { return p.dabts + (size_t)(fq + c) * qs + colb / 32; });
+          [&](int c) { return p.dabts + tscale_at(2 * F, fq + c, colb); });
       store_transposed_mx(
           slab2, lane, 128,
           [&](int c) { return colb < qend && fq + c < F ? p.dabtq + (size_t)(F + fq + c) * p.qc + colb : nullptr; },
-          [&](int c) { return p.dabts + (size_t)(F + fq + c) * qs + colb / 32; });
+          [&](int c) { return p.dabts + tscale_at(2 * F, F + fq + c, colb); });
     };
     block(std::integral_constant<int, 0>{});
     block(std::integral_constant<int, 1>{});
@@ -697,7 +698,6 @@ __global__ __launch_bounds__(NTHR, 1) void k_wgrad_down_mx(BwdParams p) {
   MX_SMEM
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
   const int H = p.H, F = p.F, ntn = (F + TILE - 1) / TILE, tpe = (H / TILE) * ntn;
-  const int64_t qs = p.qc / 32;
   const XcdRange xr = xcd_range_split(p.sched + kSchedWgradDown * kSchedInts);
   const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
   const int row_s = 128 * sc_half() + 32 * sc_blk() + sc_row32();
@@ -711,8 +711,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_wgrad_down_mx(BwdParams p) {
       la.p[j] = reinterpret_cast<const char*>(p.dytq + (size_t)(mt * TILE + row) * p.qc + q0) + 16 * c;
       lb.p[j] = reinterpret_cast<const char*>(p.hwtq + (size_t)min(nt * TILE + row, F - 1) * p.qc + q0) + 16 * c;
     }
-    const SOp sa{p.dyts + (size_t)(mt * TILE + row_s) * qs, q0 / 32};
-    const SOp sb{p.hwts + (size_t)min(nt * TILE + row_s, F - 1) * qs, q0 / 32};
+    const SOp sa{p.dyts + tscale_at(H, mt * TILE + row_s, q0), 0, 4 * H};
+    const SOp sb{p.hwts + tscale_at(F, min(nt * TILE + row_s, F - 1), q0), 0, 4 * F};
     f32x16 acc[4][4];
     mainloop_mx(acc, smem, la, lb, sa, sb, nk, 128 * wm, bn, wm, wn);
     bf16* __restrict__ out = static_cast<bf16*>(p.dwd) + (size_t)e * H * F;
@@ -727,7 +727,6 @@ __global__ __launch_bounds__(NTHR, 1) void k_wgrad_gateup_mx(BwdParams p) {
   MX_SMEM
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
   const int H = p.H, F = p.F, ntn = H / TILE, tpe = (2 * F / TILE) * ntn;
-  const int64_t qs = p.qc / 32;
   const XcdRange xr = xcd_range_split(p.sched + kSchedWgradGateup * kSchedInts);
   const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
   const int row_s = 128 * sc_half() + 32 * sc_blk() + sc_row32();
@@ -741,8 +740,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_wgrad_gateup_mx(BwdParams p) {
       la.p[j] = reinterpret_cast<const char*>(p.dabtq + (size_t)(mt * TILE + row) * p.qc + q0) + 16 * c;
       lb.p[j] = reinterpret_cast<const char*>(p.xtq + (size_t)(nt * TILE + row) * p.qc + q0) + 16 * c;
     }
-    const SOp sa{p.dabts + (size_t)(mt * TILE + row_s) * qs, q0 / 32};
-    const SOp sb{p.xts + (size_t)(nt * TILE + row_s) * qs, q0 / 32};
+    const SOp sa{p.dabts + tscale_at(2 * F, mt * TILE + row_s, q0), 0, 8 * F};
+    const SOp sb{p.xts + tscale_at(H, nt * TILE + row_s, q0), 0, 4 * H};
     f32x16 acc[4][4];
     mainloop_mx(acc, smem, la, lb, sa, sb, nk, 128 * wm, bn, wm, wn);
     bf16* __restrict__ dwg = static_cast<bf16*>(p.dwg) + (size_t)e * F * H;

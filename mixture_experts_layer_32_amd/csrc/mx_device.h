@@ -96,4 +96,13 @@ __device__ __forceinline__ float block_amax(const float (&v)[8]) {
   return BLK ? mx_amax_x16(v) : mx_amax_x4(v);
 }
 
+// Scale bytes of the pair-contiguous transposed copies ([nr][Q] fp8, blocks of 32 along the pairs):
+// stored K-tile-major, [Q/128][nr][4], so that the 4 bytes of a row's 128-pair K-tile form one dword
+// and a tile's rows are contiguous. A producer that covers 128 pairs of a few rows then writes whole
+// lines (a [nr][Q/32] layout gave each line of scales 4-byte runs from 32 different tiles). Offset
+// of the byte for row r, pair column q:
+__device__ __forceinline__ size_t tscale_at(int64_t nr, int64_t r, int64_t q) {
+  return (size_t)(((q >> 7) * nr + r) * 4 + ((q >> 5) & 3));
+}
+
 }  // namespace moe

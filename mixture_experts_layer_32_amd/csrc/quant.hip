@@ -1,6 +1,7 @@
 // MXFP8 quantisation of the GEMM operands that are not produced by a GEMM epilogue. Every output is
-// K-major (the contraction axis contiguous), with its e8m0 scales in a [rows][K/32] byte array, so
-// that the fp8 GEMMs read both operands the same way.
+// K-major (the contraction axis contiguous), with its e8m0 scales in a [rows][K/32] byte array
+// (the pair-contiguous copies: [K/128][rows][4]), so that the fp8 GEMMs read both operands the same
+// way.
 //
 //   k_quant_rows      along the contiguous axis: x and dY rows (along H), W_gate and W_up rows
 //                     (along H), W_down rows (along F), and the transposed hw copy (along pairs).
@@ -13,12 +14,15 @@
 //                     Either orientation is skipped when its output is null.
 //   k_gather_t_quant  along an expert's pairs, transposing and gathering: dY and x rows of the
 //                     expert's tokens, in the sorted pair order, into [H][Q] where the expert's
-//                     pairs occupy columns qoff[e] .. qoff[e+1] (zero-padded to a multiple of 128).
+//                     pairs occupy columns qoff[e] .. qoff[e+1] (zero-padded to a multiple of 128);
+//                     its scales are K-tile-major, [Q/128][H][4] (tscale_at).
 // The transposing kernels stage 128 x 64 tiles (k_quant_both: 128 x 128) in LDS, so that every
-// row segment they read or write is one or two whole 128-byte lines. Their scale bytes are the
-// exception: a tile writes 4 of them per row, so a 128-byte line of scales is filled by many
-// blocks. Their grids are one-dimensional with consecutive tiles on one XCD (xcd_logical_block),
-// so that those blocks meet in one L2, which merges the line before writing it back.
+// row segment they read or write is one or two whole 128-byte lines. The weights' scale bytes are
+// the exception: a tile writes 4 of them per row of a [rows][K/32] array, so a 128-byte line of
+// scales is filled by many blocks. The grids are one-dimensional with consecutive tiles on one XCD
+// (xcd_logical_block), so that those blocks meet in one L2, which merges the line before writing
+// it back. (The gathered transpose's scales are K-tile-major: a tile's 64 rows x 4 bytes are
+// contiguous.)
 // The quantised element and scale formulas are in mx_device.h.
 //
 // Blockwise FP8 (template flag BLK): k_quant_rows takes blocks of 128 along the row (16 lanes),
@@ -289,7 +293,7 @@ __global__ __launch_bounds__(256) void k_gather_t_quant(const bf16* __restrict__
     __syncthreads();
     if (h0 + 64 * GT_SPLIT < H) load(h0 + 64 * GT_SPLIT, nxt);
     const size_t orow = (size_t)h0 + (threadIdx.x & 63);
-    column_pass<BLK>(tile, q + orow * qc + q0, sc + orow * (qc / 32) + q0 / 32, cmax);
+    column_pass<BLK>(tile, q + orow * qc + q0, sc + tscale_at(H, orow, q0), cmax);
     __syncthreads();   // the tile (and cmax) are overwritten next
   }
 }

@@ -303,7 +303,9 @@ def test_mx_operands_left_in_saved(mode):
     else:
         assert off["wdt"] == 0 and off["wgut"] == 0
     hwt = sv[off["hwt"]:off["hwt"] + F * qc].reshape(F, qc)
-    hws = sv[off["hwt_scales"]:off["hwt_scales"] + F * qc // 32].reshape(F, qc // 32)
+    # scales K-tile-major, [Q/128][F][4]: as [F][Q/32]
+    hws = sv[off["hwt_scales"]:off["hwt_scales"] + F * qc // 32].reshape(qc // 128, F, 4).transpose(1, 0, 2)
+    hws = hws.reshape(F, qc // 32)
     x64 = L["x"].astype(np.float64)
     for e in range(El):
         pairs = r["perm"][r["offsets"][e]:r["offsets"][e + 1]]
