@@ -628,11 +628,7 @@ __device__ __forceinline__ void dh_tiles(const BwdParams& p, char* smem, int* s_
   TileSched ts(p.sched + 0 * kSchedInts, *p.num_mtiles2 * ((p.F + TILE - 1) / TILE));
   for (int tile = ts.first(s_tile); tile >= 0; tile = ts.next(s_tile)) dh_tile(p, smem, tile, [&] { ts.fetch(); });
 }
-// the dgrad of x, from the counter of slot 1
-__device__ __forceinline__ void dgrad_x_tiles(const BwdParams& p, char* smem, int* s_tile) {
-  TileSched ts(p.sched + 1 * kSchedInts, *p.num_mtiles2 * (p.H / TILE));
-  for (int tile = ts.first(s_tile); tile >= 0; tile = ts.next(s_tile)) dgrad_x_tile(p, smem, tile, [&] { ts.fetch(); });
-}
+
 // the down weight gradient over its XCD's cost-balanced range, round-robin
 __device__ __forceinline__ void wgrad_down_tiles(const BwdParams& p, char* smem) {
   const XcdRange xr = xcd_range_split(p.sched + kSchedWgradDown * kSchedInts);
@@ -676,18 +672,63 @@ __device__ __forceinline__ void mainloop_pre(f32x16 (&acc)[MI][NJ], char* smem, 
   mainloop_body<AMN, BMN, 32, MI>(acc, smem, la, lb, nk, am0, bn, false);
 }
 
-// K-tile 0 of a tile into stage 0 (its row indices first)
+// K-tile 0 of a tile into stage 0 (its row indices first); skip_a: this wave loads no A rows (the
+// upper waves of a half tile)
 template <class LA, class LB>
-__device__ __forceinline__ void issue_k0(char* smem, LA& la, LB& lb) {
+__device__ __forceinline__ void issue_k0(char* smem, LA& la, LB& lb, bool skip_a = false) {
   la.prologue_prefetch(0);
   lb.prologue_prefetch(0);
-  la.prologue_issue(smem, 0);
+  if (!skip_a) la.prologue_issue(smem, 0);
   lb.prologue_issue(smem + OPB, 0);
+}
+
+// mainloop_pre for the row-tiled kernels (row block i of the wave at am0 + AST i, as in
+// mainloop_rows): a half tile runs only the first MI/2 row blocks, and its waves 4-7 load no A rows
+// (issue_k0 with skip_a for its K-tile 0). after_stores is true only when exactly NS stores were
+// issued after K-tile 0; otherwise the wait also covers whatever stores preceded K-tile 1.
+template <int NS, bool AMN, bool BMN, int AST, int MI, int NJ, class LA, class LB>
+__device__ __forceinline__ void mainloop_pre_rows(f32x16 (&acc)[MI][NJ], char* smem, LA& la, LB& lb, int nk, int am0,
+                                                  const int (&bn)[NJ], bool after_stores, bool half) {
+  static_assert(AST * MI == TILE && !AMN, "row blocks, K-major A");
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  if (nk <= 0) return;
+  const bool skip_a = half && wave_id() >= NWAVE / 2;
+  block_sync();   // every wave is done reading its staging area in stage 1
+  if (nk > 1) {
+    la.prologue_prefetch(1);
+    lb.prologue_prefetch(1);
+    if (!skip_a) la.prologue_issue(smem + STB, 1);
+    lb.prologue_issue(smem + STB + OPB, 1);
+    if (nk > 2) {
+      la.prefetch(2);
+      lb.prefetch(2);
+    }
+    // K-tile 0 has landed once only the stores after it (NS or none) and K-tile 1 remain
+    if (skip_a) {
+      if (after_stores) wait_vm<NS + LOADS>();
+      else wait_vm<LOADS>();
+    } else {
+      if (after_stores) wait_vm<NS + 2 * LOADS>();
+      else wait_vm<2 * LOADS>();
+    }
+  } else {
+    if (after_stores) wait_vm<NS>();
+    else wait_vm<0>();
+  }
+  block_sync();
+  if (half) mainloop_body<AMN, BMN, AST, MI / 2>(acc, smem, la, lb, nk, am0, bn, skip_a);
+  else mainloop_body<AMN, BMN, AST, MI>(acc, smem, la, lb, nk, am0, bn, false);
 }
 
 // store_wave_block with the rows staged as bf16 in ring stage 1 (4.6 KB per wave for NJ = 2), so
 // that stage 0 can take the next tile's first K-tile meanwhile. The values are rounded to bf16 once,
-// as in store_wave_block. Every row is stored: MI * 32 * 4 NJ / 64 stores per lane.
+// as in store_wave_block. Rows whose out_row is null are skipped; with every row stored, that is
+// MI * 32 * 4 NJ / 64 stores per lane.
 template <int MI, int NJ, class OutRow>
 __device__ __forceinline__ void store_wave_block_s1(char* smem, const f32x16 (&acc)[MI][NJ], int lane, OutRow out_row) {
   constexpr int LDB = 32 * NJ + 8;               // staged row stride (bf16)
@@ -704,7 +745,8 @@ __device__ __forceinline__ void store_wave_block_s1(char* smem, const f32x16 (&a
 #pragma unroll
     for (int s = 0; s < 32 / RPP; ++s) {
       const int rl = lane / LPR + RPP * s, c0 = (lane % LPR) * 8;
-      st16_nt(out_row(32 * i + rl) + c0, *reinterpret_cast<const uint4*>(st + rl * LDB + c0));
+      bf16* o = out_row(32 * i + rl);
+      if (o) st16_nt(o + c0, *reinterpret_cast<const uint4*>(st + rl * LDB + c0));
     }
   }
 }
@@ -767,6 +809,67 @@ __device__ __forceinline__ void wgrad_gateup_tiles(const BwdParams& p, char* sme
     store_wave_block_s1(smem, acc, lane, [&](int m) {
       const int mm = mq + m;
       return (mm < F ? dwg + (size_t)mm * H : dwu + (size_t)(mm - F) * H) + nq;
+    });
+  }
+}
+
+// backward: dX = [da db] [W_gate[e]; W_up[e]] over a static range per XCD taken round-robin (every
+// tile contracts over 2F, so equal counts balance; an expert's half tile does half the MFMAs), each
+// tile's first K-tile issued before the previous tile's epilogue, which stages its rows as bf16 in
+// ring stage 1 (mainloop_pre_rows). Same operands, wave layout and bits as dgrad_x_tile.
+__device__ __forceinline__ void dgrad_x_tiles_pre(const BwdParams& p, char* smem) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;   // 128x64 per wave
+  const int H = p.H, F = p.F, ntn = H / TILE, nk = 2 * F / KTILE;
+  const XcdRange xr = xcd_range(ld_uniform(p.num_mtiles2, 0) * ntn);
+  const bf16* __restrict__ dab = static_cast<const bf16*>(p.dab);
+  bf16* __restrict__ dxp = static_cast<bf16*>(p.dxp);
+  KOp la;
+  MNOp<WeightRows> lb;
+  int r0 = 0, seg_end = 0, nt = 0;
+  bool half = false;
+  // loaders of tile `tile`; scalar loads for the tables (a vector load's compiler-inserted wait
+  // would also wait for the direct-to-LDS loads in flight)
+  auto setup = [&](int tile) {
+    const int mt = tile / ntn;
+    nt = tile - mt * ntn;
+    const int e = ld_uniform(reinterpret_cast<const int*>(p.mtile2), 2 * mt);
+    r0 = ld_uniform(reinterpret_cast<const int*>(p.mtile2), 2 * mt + 1);
+    seg_end = ld_uniform(p.offsets, e + 1);
+    half = seg_end - r0 <= 128;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int r = min(r0 + KOp::row_of(j), seg_end - 1);
+      la.p[j] = reinterpret_cast<const char*>(dab + (size_t)r * 2 * F) + 16 * KOp::chunk_of(j);
+    }
+    lb.rows = WeightRows{reinterpret_cast<const char*>(static_cast<const bf16*>(p.wg) + (size_t)e * F * H + nt * TILE),
+                         reinterpret_cast<const char*>(static_cast<const bf16*>(p.wu) + (size_t)e * F * H + nt * TILE),
+                         (size_t)H * 2, F};
+    lb.zero = static_cast<const char*>(p.zeros);
+    lb.init(nt * TILE, H);
+  };
+  const int bn[2] = {64 * wn, 64 * wn + 32};
+  constexpr int NS = 4 * 32 * 8 / 64;   // epilogue stores per lane of a full tile (MI = 4, NJ = 2)
+  int lid = xr.first;
+  if (lid >= xr.end) return;
+  setup(lid);
+  issue_k0(smem, la, lb, half && wave_id() >= NWAVE / 2);
+  bool after_stores = false;
+  for (; lid < xr.end; lid += xr.stride) {
+    f32x16 acc[4][2];
+    mainloop_pre_rows<NS, false, true, 64>(acc, smem, la, lb, nk, 32 * wm, bn, after_stores, half);
+    const int cr0 = r0, cseg = seg_end, cnt = nt;
+    // every wave is past the main loop's last barrier: stage 0 is free
+    after_stores = false;
+    if (lid + xr.stride < xr.end) {
+      setup(lid + xr.stride);
+      issue_k0(smem, la, lb, half && wave_id() >= NWAVE / 2);
+      after_stores = cseg - cr0 >= TILE;   // every row of the tile is stored: NS stores follow
+    }
+    const int rq = cr0 + 32 * wm;   // the wave's row m is tile row 32 wm + 64 (m / 32) + m % 32
+    bf16* const oq = dxp + cnt * TILE + 64 * wn;
+    store_wave_block_s1(smem, acc, lane, [&](int m) {
+      const int r = rq + 64 * (m >> 5) + (m & 31);
+      return r < cseg ? oq + (size_t)r * H : nullptr;
     });
   }
 }
@@ -856,8 +959,7 @@ __global__ __launch_bounds__(NTHR8, 1) void k_bwd_dh_bf16(BwdParams p) {
 }
 __global__ __launch_bounds__(NTHR8, 1) void k_dgrad_x_bf16(BwdParams p) {
   MOE_SMEM
-  __shared__ int s_tile;
-  dgrad_x_tiles(p, smem, &s_tile);
+  dgrad_x_tiles_pre(p, smem);
 }
 __global__ __launch_bounds__(NTHR8, 1) void k_wgrad_down_bf16(BwdParams p) {
   MOE_SMEM
