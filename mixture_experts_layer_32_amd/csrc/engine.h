@@ -24,8 +24,9 @@ constexpr int NTHR = 256;            // threads of a 4-wave workgroup
 // wave-uniform). Written as inline assembly so that the compiler neither tracks it nor inserts
 // waits for it. The main loop orders these loads with explicit vmcnt waits and barriers.
 __device__ __forceinline__ void gl2lds(const void* g, char* lds) {
-  const unsigned off = __builtin_amdgcn_readfirstlane(
-      (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
+  // the LDS address: the low 32 bits of a generic pointer into the LDS aperture (a cast to the LDS
+  // address space would add a null check, which needs the aperture's high half in a register)
+  const unsigned off = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(off), "v"(g) : "memory", "m0");
 }
 // wait until at most N vector memory operations of this wave are outstanding
