@@ -313,6 +313,132 @@ constexpr int SMEM_BYTES = STAGES * STB > SLABS_BYTES ? STAGES * STB : SLABS_BYT
 static_assert(SMEM_BYTES <= 160 * 1024, "LDS");
 #define MOE_SMEM __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
 
+// Persistent tiles with the next tile's first K-tile issued before the current tile's epilogue:
+// the caller issues K-tile 0 of a tile into stage 0 (after the previous main loop's last barrier,
+// before the previous epilogue), and stages that epilogue in bf16 in stage 1. mainloop_pre then
+// waits for every wave's staging reads, issues K-tile 1 into stage 1 and waits for K-tile 0 only,
+// so K-tile 0's latency and the epilogue's stores overlap. after_stores says whether this wave
+// issued its NS epilogue stores after K-tile 0 (false for its first tile): the vector-memory counter
+// completes in order, so K-tile 0 has landed once at most NS stores and K-tile 1's loads remain.
+template <int NS, bool AMN, bool BMN, int MI, int NJ, class LA, class LB>
+__device__ __forceinline__ void mainloop_pre(f32x16 (&acc)[MI][NJ], char* smem, LA& la, LB& lb, int nk, int am0,
+                                             const int (&bn)[NJ], bool after_stores) {
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  if (nk <= 0) return;
+  block_sync();   // every wave is done reading its staging area in stage 1
+  if (nk > 1) {
+    la.prologue_prefetch(1);
+    lb.prologue_prefetch(1);
+    la.prologue_issue(smem + STB, 1);
+    lb.prologue_issue(smem + STB + OPB, 1);
+    if (nk > 2) {
+      la.prefetch(2);
+      lb.prefetch(2);
+    }
+    if (after_stores) wait_vm<NS + 2 * LOADS>();
+    else wait_vm<2 * LOADS>();
+  } else {
+    if (after_stores) wait_vm<NS>();
+    else wait_vm<0>();
+  }
+  block_sync();
+  mainloop_body<AMN, BMN, 32, MI>(acc, smem, la, lb, nk, am0, bn, false);
+}
+
+// K-tile 0 of a tile into stage 0 (its row indices first); skip_a: this wave loads no A rows (the
+// upper waves of a half tile)
+template <class LA, class LB>
+__device__ __forceinline__ void issue_k0(char* smem, LA& la, LB& lb, bool skip_a = false) {
+  la.prologue_prefetch(0);
+  lb.prologue_prefetch(0);
+  if (!skip_a) la.prologue_issue(smem, 0);
+  lb.prologue_issue(smem + OPB, 0);
+}
+
+// mainloop_pre for the row-tiled kernels (row block i of the wave at am0 + AST i, as in
+// mainloop_rows): a half tile runs only the first MI/2 row blocks, and its waves 4-7 load no A rows
+// (issue_k0 with skip_a for its K-tile 0). after_stores is true only when exactly NS stores were
+// issued after K-tile 0; otherwise the wait also covers whatever stores preceded K-tile 1.
+template <int NS, bool AMN, bool BMN, int AST, int MI, int NJ, class LA, class LB>
+__device__ __forceinline__ void mainloop_pre_rows(f32x16 (&acc)[MI][NJ], char* smem, LA& la, LB& lb, int nk, int am0,
+                                                  const int (&bn)[NJ], bool after_stores, bool half) {
+  static_assert(AST * MI == TILE && !AMN, "row blocks, K-major A");
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  if (nk <= 0) return;
+  const bool skip_a = half && wave_id() >= NWAVE / 2;
+  block_sync();   // every wave is done reading its staging area in stage 1
+  if (nk > 1) {
+    la.prologue_prefetch(1);
+    lb.prologue_prefetch(1);
+    if (!skip_a) la.prologue_issue(smem + STB, 1);
+    lb.prologue_issue(smem + STB + OPB, 1);
+    if (nk > 2) {
+      la.prefetch(2);
+      lb.prefetch(2);
+    }
+    // K-tile 0 has landed once only the stores after it (NS or none) and K-tile 1 remain
+    if (skip_a) {
+      if (after_stores) wait_vm<NS + LOADS>();
+      else wait_vm<LOADS>();
+    } else {
+      if (after_stores) wait_vm<NS + 2 * LOADS>();
+      else wait_vm<2 * LOADS>();
+    }
+  } else {
+    if (after_stores) wait_vm<NS>();
+    else wait_vm<0>();
+  }
+  block_sync();
+  if (half) mainloop_body<AMN, BMN, AST, MI / 2>(acc, smem, la, lb, nk, am0, bn, skip_a);
+  else mainloop_body<AMN, BMN, AST, MI>(acc, smem, la, lb, nk, am0, bn, false);
+}
+
+// store_wave_block with the rows staged as bf16 in ring stage 1, RS rows at a time (32 rows: 4.6 KB
+// per wave for NJ = 2; 16 rows: 4.4 KB for NJ = 4), so that stage 0 can take the next tile's first
+// K-tile meanwhile. The values are rounded to bf16 once, as in store_wave_block. Rows whose out_row
+// is null are skipped; with every row stored, that is MI * 32 * 4 NJ / 64 stores per lane. The row
+// stride of 4 banks mod 64 keeps the staging writes (lane l: row l % 32, 4 columns) conflict-free.
+template <int MI, int NJ, int RS = 32, class OutRow>
+__device__ __forceinline__ void store_wave_block_s1(char* smem, const f32x16 (&acc)[MI][NJ], int lane, OutRow out_row) {
+  static_assert(RS == 32 || RS == 16, "staged rows");
+  constexpr int LDB = 32 * NJ + 8;               // staged row stride (bf16)
+  constexpr int LPR = 4 * NJ, RPP = 64 / LPR;    // lanes per row, rows per pass
+  static_assert(NWAVE * RS * LDB * 2 <= STB, "the staging fits ring stage 1");
+  bf16* st = reinterpret_cast<bf16*>(smem + STB) + wave_id() * RS * LDB;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+#pragma unroll
+    for (int h = 0; h < 32 / RS; ++h) {
+      // the lanes holding rows h RS .. h RS + RS - 1 of the block stage them (LDS accesses of one
+      // wave run in order, so these writes follow the previous half's reads)
+      if (RS == 32 || (lane & 31) / RS == h) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+            st8(st + ((lane & 31) % RS) * LDB + 32 * j + acc_n(a, lane),
+                pack4(acc[i][j][4 * a], acc[i][j][4 * a + 1], acc[i][j][4 * a + 2], acc[i][j][4 * a + 3]));
+      }
+#pragma unroll
+      for (int s = 0; s < RS / RPP; ++s) {
+        const int rl = lane / LPR + RPP * s, c0 = (lane % LPR) * 8;
+        bf16* o = out_row(32 * i + RS * h + rl);
+        if (o) st16_nt(o + c0, *reinterpret_cast<const uint4*>(st + rl * LDB + c0));
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------------------
 // forward: [a | b] = gather(x) [W_gate; W_up]^T, then ab and hw = w * silu(a) * b
 // QT: the pair-contiguous copy of hw is written as MXFP8 (blocks of 32 along the pairs, quantised
@@ -405,21 +531,29 @@ __global__ __launch_bounds__(NTHR8, 1) void k_gateup_bf16(FwdParams p) {
 }
 
 // forward: o' = hw W_down[e]^T
+// Static per-XCD tile ranges taken round-robin (every tile contracts over F, so equal counts
+// balance), each tile's first K-tile issued before the previous tile's epilogue, which stages its
+// rows as bf16 in ring stage 1, 16 at a time (mainloop_pre_rows, store_wave_block_s1).
 __global__ __launch_bounds__(NTHR8, 1) void k_down_bf16(FwdParams p) {
   MOE_SMEM
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;   // 64x128 per wave
   const bf16* __restrict__ hw = static_cast<const bf16*>(p.hw);
   const bf16* __restrict__ wd = static_cast<const bf16*>(p.wd);
   bf16* __restrict__ o = static_cast<bf16*>(p.o);
-  const int H = p.H, F = p.F, ntn = H / TILE;
-  __shared__ int s_tile;
-  TileSched ts(p.sched + 1 * kSchedInts, *p.num_mtiles2 * ntn);
+  const int H = p.H, F = p.F, ntn = H / TILE, nk = F / KTILE;
+  const XcdRange xr = xcd_range(ld_uniform(p.num_mtiles2, 0) * ntn);
   const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
-  for (int tile = ts.first(&s_tile); tile >= 0; tile = ts.next(&s_tile)) {
-    const int mt = tile / ntn, nt = tile - mt * ntn;
-    const int2 me = p.mtile2[mt];
-    const int e = me.x, r0 = me.y, seg_end = p.offsets[e + 1];
-    KOp la, lb;
+  KOp la, lb;
+  int r0 = 0, seg_end = 0, nt = 0;
+  bool half = false;
+  // loaders of tile `tile` (scalar loads for the tables: see dgrad_x_tiles_pre)
+  auto setup = [&](int tile) {
+    const int mt = tile / ntn;
+    nt = tile - mt * ntn;
+    const int e = ld_uniform(reinterpret_cast<const int*>(p.mtile2), 2 * mt);
+    r0 = ld_uniform(reinterpret_cast<const int*>(p.mtile2), 2 * mt + 1);
+    seg_end = ld_uniform(p.offsets, e + 1);
+    half = seg_end - r0 <= 128;
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       const int row = KOp::row_of(j), c = KOp::chunk_of(j);
@@ -427,15 +561,30 @@ __global__ __launch_bounds__(NTHR8, 1) void k_down_bf16(FwdParams p) {
       la.p[j] = reinterpret_cast<const char*>(hw + (size_t)r * F) + 16 * c;
       lb.p[j] = reinterpret_cast<const char*>(wd + ((size_t)e * H + nt * TILE + row) * F) + 16 * c;
     }
+  };
+  constexpr int NS = 2 * 32 * 16 / 64;   // epilogue stores per lane of a full tile (MI = 2, NJ = 4)
+  int lid = xr.first;
+  if (lid >= xr.end) return;
+  setup(lid);
+  issue_k0(smem, la, lb, half && wave_id() >= NWAVE / 2);
+  bool after_stores = false;
+  for (; lid < xr.end; lid += xr.stride) {
     f32x16 acc[2][4];
-    mainloop_rows<false, false, 128>(acc, smem, la, lb, F / KTILE, 32 * wm, bn, seg_end - r0 <= 128);
-    ts.fetch();
-    const int rq = r0 + 32 * wm;   // the wave's row m is tile row 32 wm + 128 (m / 32) + m % 32
-    bf16* const oq = o + nt * TILE + 128 * wn;
-    store_wave_block(smem, acc, lane, [&](int m) {
+    mainloop_pre_rows<NS, false, false, 128>(acc, smem, la, lb, nk, 32 * wm, bn, after_stores, half);
+    const int cr0 = r0, cseg = seg_end, cnt = nt;
+    // every wave is past the main loop's last barrier: stage 0 is free
+    after_stores = false;
+    if (lid + xr.stride < xr.end) {
+      setup(lid + xr.stride);
+      issue_k0(smem, la, lb, half && wave_id() >= NWAVE / 2);
+      after_stores = cseg - cr0 >= TILE;   // every row of the tile is stored: NS stores follow
+    }
+    const int rq = cr0 + 32 * wm;   // the wave's row m is tile row 32 wm + 128 (m / 32) + m % 32
+    bf16* const oq = o + cnt * TILE + 128 * wn;
+    store_wave_block_s1<2, 4, 16>(smem, acc, lane, [&](int m) {
       const int r = rq + 128 * (m >> 5) + (m & 31);
-      return r < seg_end ? oq + (size_t)r * H : nullptr;
-    }, 128);
+      return r < cseg ? oq + (size_t)r * H : nullptr;
+    });
   }
 }
 
@@ -633,122 +782,6 @@ __device__ __forceinline__ void dh_tiles(const BwdParams& p, char* smem, int* s_
 __device__ __forceinline__ void wgrad_down_tiles(const BwdParams& p, char* smem) {
   const XcdRange xr = xcd_range_split(p.sched + kSchedWgradDown * kSchedInts);
   for (int lid = xr.first; lid < xr.end; lid += xr.stride) wgrad_down_tile(p, smem, lid, [] {});
-}
-
-// Persistent tiles with the next tile's first K-tile issued before the current tile's epilogue:
-// the caller issues K-tile 0 of a tile into stage 0 (after the previous main loop's last barrier,
-// before the previous epilogue), and stages that epilogue in bf16 in stage 1. mainloop_pre then
-// waits for every wave's staging reads, issues K-tile 1 into stage 1 and waits for K-tile 0 only,
-// so K-tile 0's latency and the epilogue's stores overlap. after_stores says whether this wave
-// issued its NS epilogue stores after K-tile 0 (false for its first tile): the vector-memory counter
-// completes in order, so K-tile 0 has landed once at most NS stores and K-tile 1's loads remain.
-template <int NS, bool AMN, bool BMN, int MI, int NJ, class LA, class LB>
-__device__ __forceinline__ void mainloop_pre(f32x16 (&acc)[MI][NJ], char* smem, LA& la, LB& lb, int nk, int am0,
-                                             const int (&bn)[NJ], bool after_stores) {
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-  if (nk <= 0) return;
-  block_sync();   // every wave is done reading its staging area in stage 1
-  if (nk > 1) {
-    la.prologue_prefetch(1);
-    lb.prologue_prefetch(1);
-    la.prologue_issue(smem + STB, 1);
-    lb.prologue_issue(smem + STB + OPB, 1);
-    if (nk > 2) {
-      la.prefetch(2);
-      lb.prefetch(2);
-    }
-    if (after_stores) wait_vm<NS + 2 * LOADS>();
-    else wait_vm<2 * LOADS>();
-  } else {
-    if (after_stores) wait_vm<NS>();
-    else wait_vm<0>();
-  }
-  block_sync();
-  mainloop_body<AMN, BMN, 32, MI>(acc, smem, la, lb, nk, am0, bn, false);
-}
-
-// K-tile 0 of a tile into stage 0 (its row indices first); skip_a: this wave loads no A rows (the
-// upper waves of a half tile)
-template <class LA, class LB>
-__device__ __forceinline__ void issue_k0(char* smem, LA& la, LB& lb, bool skip_a = false) {
-  la.prologue_prefetch(0);
-  lb.prologue_prefetch(0);
-  if (!skip_a) la.prologue_issue(smem, 0);
-  lb.prologue_issue(smem + OPB, 0);
-}
-
-// mainloop_pre for the row-tiled kernels (row block i of the wave at am0 + AST i, as in
-// mainloop_rows): a half tile runs only the first MI/2 row blocks, and its waves 4-7 load no A rows
-// (issue_k0 with skip_a for its K-tile 0). after_stores is true only when exactly NS stores were
-// issued after K-tile 0; otherwise the wait also covers whatever stores preceded K-tile 1.
-template <int NS, bool AMN, bool BMN, int AST, int MI, int NJ, class LA, class LB>
-__device__ __forceinline__ void mainloop_pre_rows(f32x16 (&acc)[MI][NJ], char* smem, LA& la, LB& lb, int nk, int am0,
-                                                  const int (&bn)[NJ], bool after_stores, bool half) {
-  static_assert(AST * MI == TILE && !AMN, "row blocks, K-major A");
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-  if (nk <= 0) return;
-  const bool skip_a = half && wave_id() >= NWAVE / 2;
-  block_sync();   // every wave is done reading its staging area in stage 1
-  if (nk > 1) {
-    la.prologue_prefetch(1);
-    lb.prologue_prefetch(1);
-    if (!skip_a) la.prologue_issue(smem + STB, 1);
-    lb.prologue_issue(smem + STB + OPB, 1);
-    if (nk > 2) {
-      la.prefetch(2);
-      lb.prefetch(2);
-    }
-    // K-tile 0 has landed once only the stores after it (NS or none) and K-tile 1 remain
-    if (skip_a) {
-      if (after_stores) wait_vm<NS + LOADS>();
-      else wait_vm<LOADS>();
-    } else {
-      if (after_stores) wait_vm<NS + 2 * LOADS>();
-      else wait_vm<2 * LOADS>();
-    }
-  } else {
-    if (after_stores) wait_vm<NS>();
-    else wait_vm<0>();
-  }
-  block_sync();
-  if (half) mainloop_body<AMN, BMN, AST, MI / 2>(acc, smem, la, lb, nk, am0, bn, skip_a);
-  else mainloop_body<AMN, BMN, AST, MI>(acc, smem, la, lb, nk, am0, bn, false);
-}
-
-// store_wave_block with the rows staged as bf16 in ring stage 1 (4.6 KB per wave for NJ = 2), so
-// that stage 0 can take the next tile's first K-tile meanwhile. The values are rounded to bf16 once,
-// as in store_wave_block. Rows whose out_row is null are skipped; with every row stored, that is
-// MI * 32 * 4 NJ / 64 stores per lane.
-template <int MI, int NJ, class OutRow>
-__device__ __forceinline__ void store_wave_block_s1(char* smem, const f32x16 (&acc)[MI][NJ], int lane, OutRow out_row) {
-  constexpr int LDB = 32 * NJ + 8;               // staged row stride (bf16)
-  constexpr int LPR = 4 * NJ, RPP = 64 / LPR;    // lanes per row, rows per pass
-  bf16* st = reinterpret_cast<bf16*>(smem + STB) + wave_id() * 32 * LDB;
-#pragma unroll
-  for (int i = 0; i < MI; ++i) {
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-        st8(st + (lane & 31) * LDB + 32 * j + acc_n(a, lane),
-            pack4(acc[i][j][4 * a], acc[i][j][4 * a + 1], acc[i][j][4 * a + 2], acc[i][j][4 * a + 3]));
-#pragma unroll
-    for (int s = 0; s < 32 / RPP; ++s) {
-      const int rl = lane / LPR + RPP * s, c0 = (lane % LPR) * 8;
-      bf16* o = out_row(32 * i + rl);
-      if (o) st16_nt(o + c0, *reinterpret_cast<const uint4*>(st + rl * LDB + c0));
-    }
-  }
 }
 
 // backward: [dW_gate; dW_up][e] (2F x H) = sum over the expert's pairs of [da; db]_r x_t^T
