@@ -406,10 +406,12 @@ __device__ __forceinline__ void mainloop_pre_rows(f32x16 (&acc)[MI][NJ], char* s
 // store_wave_block with the rows staged as bf16 in ring stage 1, RS rows at a time (32 rows: 4.6 KB
 // per wave for NJ = 2; 16 rows: 4.4 KB for NJ = 4), so that stage 0 can take the next tile's first
 // K-tile meanwhile. The values are rounded to bf16 once, as in store_wave_block. Rows whose out_row
-// is null are skipped; with every row stored, that is MI * 32 * 4 NJ / 64 stores per lane. The row
-// stride of 4 banks mod 64 keeps the staging writes (lane l: row l % 32, 4 columns) conflict-free.
+// is null, and columns from ncols on, are skipped; with every row and column stored, that is
+// MI * 32 * 4 NJ / 64 stores per lane. The row stride of 4 banks mod 64 keeps the staging writes
+// (lane l: row l % 32, 4 columns) conflict-free.
 template <int MI, int NJ, int RS = 32, class OutRow>
-__device__ __forceinline__ void store_wave_block_s1(char* smem, const f32x16 (&acc)[MI][NJ], int lane, OutRow out_row) {
+__device__ __forceinline__ void store_wave_block_s1(char* smem, const f32x16 (&acc)[MI][NJ], int lane, OutRow out_row,
+                                                    int ncols = 32 * NJ) {
   static_assert(RS == 32 || RS == 16, "staged rows");
   constexpr int LDB = 32 * NJ + 8;               // staged row stride (bf16)
   constexpr int LPR = 4 * NJ, RPP = 64 / LPR;    // lanes per row, rows per pass
@@ -433,7 +435,7 @@ __device__ __forceinline__ void store_wave_block_s1(char* smem, const f32x16 (&a
       for (int s = 0; s < RS / RPP; ++s) {
         const int rl = lane / LPR + RPP * s, c0 = (lane % LPR) * 8;
         bf16* o = out_row(32 * i + RS * h + rl);
-        if (o) st16_nt(o + c0, *reinterpret_cast<const uint4*>(st + rl * LDB + c0));
+        if (o && c0 < ncols) st16_nt(o + c0, *reinterpret_cast<const uint4*>(st + rl * LDB + c0));
       }
     }
   }
@@ -778,10 +780,60 @@ __device__ __forceinline__ void dh_tiles(const BwdParams& p, char* smem, int* s_
   for (int tile = ts.first(s_tile); tile >= 0; tile = ts.next(s_tile)) dh_tile(p, smem, tile, [&] { ts.fetch(); });
 }
 
-// the down weight gradient over its XCD's cost-balanced range, round-robin
+// the down weight gradient over its XCD's cost-balanced range, round-robin, each tile's first K-tile
+// issued before the previous tile's epilogue, which stages its rows as bf16 in ring stage 1 sixteen
+// at a time (as the down GEMM). Same operands, wave layout and bits as wgrad_down_tile.
 __device__ __forceinline__ void wgrad_down_tiles(const BwdParams& p, char* smem) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;   // 64x128 per wave
+  const int H = p.H, F = p.F, ntn = (F + TILE - 1) / TILE, tpe = (H / TILE) * ntn;
   const XcdRange xr = xcd_range_split(p.sched + kSchedWgradDown * kSchedInts);
-  for (int lid = xr.first; lid < xr.end; lid += xr.stride) wgrad_down_tile(p, smem, lid, [] {});
+  MNOp<GatherRows> la;
+  KOp lb;
+  int e = 0, mt = 0, nt = 0, nk = 0;
+  // loaders of tile lid (scalar loads for the tables); B rows hwT[n][qoff[e] ..], contiguous along
+  // the expert's pairs (zero-padded to 32)
+  auto setup = [&](int lid) {
+    e = lid / tpe;
+    const int t = lid - e * tpe;
+    mt = t / ntn;
+    nt = t - mt * ntn;
+    const int seg0 = ld_uniform(p.offsets, e), seg_end = ld_uniform(p.offsets, e + 1);
+    nk = (seg_end - seg0 + KTILE - 1) / KTILE;
+    la.rows = GatherRows{reinterpret_cast<const char*>(static_cast<const bf16*>(p.dy) + mt * TILE), p.ptok,
+                         (size_t)H * 2, seg0, seg_end, {}};
+    la.zero = static_cast<const char*>(p.zeros);
+    la.init(mt * TILE, H);
+    const bf16* hwt = static_cast<const bf16*>(p.hwt) + ld_uniform(p.qoff, e);
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int n = min(nt * TILE + KOp::row_of(j), F - 1);
+      lb.p[j] = reinterpret_cast<const char*>(hwt + (size_t)n * p.qc) + 16 * KOp::chunk_of(j);
+    }
+  };
+  const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
+  constexpr int NS = 2 * 32 * 16 / 64;   // epilogue stores per lane of a whole wave block (MI = 2, NJ = 4)
+  int lid = xr.first;
+  if (lid >= xr.end) return;
+  setup(lid);
+  if (nk > 0) issue_k0(smem, la, lb);
+  bool after_stores = false;
+  for (; lid < xr.end; lid += xr.stride) {
+    f32x16 acc[2][4];
+    mainloop_pre<NS, true, false>(acc, smem, la, lb, nk, 64 * wm, bn, after_stores);
+    const int ce = e, cmt = mt, cnt = nt;
+    const int mq = cmt * TILE + 64 * wm, nq = cnt * TILE + 128 * wn;
+    // every wave is past the main loop's last barrier (or the tile had no K-tile): stage 0 is free
+    after_stores = false;
+    if (lid + xr.stride < xr.end) {
+      setup(lid + xr.stride);
+      if (nk > 0) {
+        issue_k0(smem, la, lb);
+        after_stores = F - nq >= 128;   // the wave's block lies inside F: NS stores follow
+      }
+    }
+    bf16* __restrict__ out = static_cast<bf16*>(p.dwd) + (size_t)ce * H * F;
+    store_wave_block_s1<2, 4, 16>(smem, acc, lane, [&](int m) { return out + (size_t)(mq + m) * F + nq; }, F - nq);
+  }
 }
 
 // backward: [dW_gate; dW_up][e] (2F x H) = sum over the expert's pairs of [da; db]_r x_t^T

@@ -52,6 +52,9 @@ SMALL = [
     pytest.param(inputs.CONFIGS["tiny"].with_(dtype="bf16"), None, "bf16", id="tiny_bf16"),
     custom("ragged_T333", T=333, H=512, F=256, E=16, k=4, seed=11),
     custom("ragged_fp32", mode="fp32", T=397, H=256, F=384, E=8, k=3, seed=12),
+    # F = 384: the last N-tile of the down weight gradient holds 128 columns; ~337 pairs per expert
+    # give every expert a full and a half M-tile
+    custom("ragged_F384", T=900, H=512, F=384, E=8, k=3, seed=27),
     custom("k1", T=200, H=256, F=128, E=4, k=1, seed=13),
     custom("k_equals_E", T=96, H=256, F=128, E=4, k=4, seed=14),
     custom("single_token", T=1, H=256, F=128, E=8, k=2, seed=15),
