@@ -29,11 +29,13 @@
 //    indices of gathered contraction rows come through scalar loads, so that the vector memory
 //    counter tracks nothing but the tile loads.
 //  * The kernels are persistent. Each XCD takes one contiguous range of the expert-major tile list,
-//    so the blocks sharing an expert's operands share that XCD's L2. The row-tiled kernels hand out
-//    the tiles of a range dynamically (TileSched), since an expert's last tile may be a half tile;
-//    the others assign them round-robin (the weight-gradient tiles cost the same within an expert,
-//    and the dynamic order measured 3-5 % slower there; the dgrad of h, with its 128x64 waves, ran
-//    its half-tile form 15 % slower, through register pressure).
+//    so the blocks sharing an expert's operands share that XCD's L2. The gate/up GEMM and the dgrad
+//    of h hand out the tiles of a range dynamically (TileSched), since an expert's last tile may be
+//    a half tile (or, for the dgrad of h, multiply fewer row blocks); the others assign them
+//    round-robin and issue each tile's first K-tile before the previous tile's epilogue
+//    (mainloop_pre): the weight-gradient tiles cost the same within an expert (the dynamic order
+//    measured 3-5 % slower there), and the down GEMM's and the dgrad of x's tiles all contract over
+//    the same K, the pre-issued K-tile gaining more than the counter's balance of half tiles.
 #include "engine.h"
 #include "moe_internal.h"
 
