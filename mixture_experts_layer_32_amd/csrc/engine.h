@@ -217,6 +217,42 @@ __device__ __forceinline__ void store_wave_block(char* smem, const f32x16 (&acc)
   }
 }
 
+// store_wave_block with the rows staged as bf16 (rounded once, as in store_wave_block) in a
+// caller-chosen LDS area, RS rows at a time: wave w uses RS (32 NJ + 8) bf16 from area +
+// w RS (32 NJ + 8) 2 bytes. Rows whose out_row is null, and columns from ncols on, are skipped; with
+// every row and column stored, that is MI * 32 * 4 NJ / 64 stores per lane. The row stride of 4
+// banks mod 64 keeps the staging writes (lane l: row l % 32, 4 columns) conflict-free.
+template <int MI, int NJ, int RS = 32, class OutRow>
+__device__ __forceinline__ void store_wave_block_bf16(char* area, const f32x16 (&acc)[MI][NJ], int lane, OutRow out_row,
+                                                      int ncols = 32 * NJ) {
+  static_assert(RS == 32 || RS == 16, "staged rows");
+  constexpr int LDB = 32 * NJ + 8;               // staged row stride (bf16)
+  constexpr int LPR = 4 * NJ, RPP = 64 / LPR;    // lanes per row, rows per pass
+  bf16* st = reinterpret_cast<bf16*>(area) + wave_id() * RS * LDB;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+#pragma unroll
+    for (int h = 0; h < 32 / RS; ++h) {
+      // the lanes holding rows h RS .. h RS + RS - 1 of the block stage them (LDS accesses of one
+      // wave run in order, so these writes follow the previous half's reads)
+      if (RS == 32 || (lane & 31) / RS == h) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+            st8(st + ((lane & 31) % RS) * LDB + 32 * j + acc_n(a, lane),
+                pack4(acc[i][j][4 * a], acc[i][j][4 * a + 1], acc[i][j][4 * a + 2], acc[i][j][4 * a + 3]));
+      }
+#pragma unroll
+      for (int s = 0; s < RS / RPP; ++s) {
+        const int rl = lane / LPR + RPP * s, c0 = (lane % LPR) * 8;
+        bf16* o = out_row(32 * i + RS * h + rl);
+        if (o && c0 < ncols) st16_nt(o + c0, *reinterpret_cast<const uint4*>(st + rl * LDB + c0));
+      }
+    }
+  }
+}
+
 // Writes staged columns [0, ncol) of the 32 staged rows to a pair-contiguous transposed copy.
 // dst(c) is the copy's row for staged column c, at the pair column of staged row 0 (null: skip).
 // Four lanes cover one column, 8 consecutive pair rows each: one 16-byte store, 64 contiguous bytes

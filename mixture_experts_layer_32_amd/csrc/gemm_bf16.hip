@@ -405,42 +405,14 @@ __device__ __forceinline__ void mainloop_pre_rows(f32x16 (&acc)[MI][NJ], char* s
   else mainloop_body<AMN, BMN, AST, MI>(acc, smem, la, lb, nk, am0, bn, false);
 }
 
-// store_wave_block with the rows staged as bf16 in ring stage 1, RS rows at a time (32 rows: 4.6 KB
-// per wave for NJ = 2; 16 rows: 4.4 KB for NJ = 4), so that stage 0 can take the next tile's first
-// K-tile meanwhile. The values are rounded to bf16 once, as in store_wave_block. Rows whose out_row
-// is null, and columns from ncols on, are skipped; with every row and column stored, that is
-// MI * 32 * 4 NJ / 64 stores per lane. The row stride of 4 banks mod 64 keeps the staging writes
-// (lane l: row l % 32, 4 columns) conflict-free.
+// store_wave_block_bf16 (engine.h) with its staging in ring stage 1, so that stage 0 can take the
+// next tile's first K-tile meanwhile (32 rows at a time: 4.6 KB per wave for NJ = 2; 16 rows: 4.4 KB
+// for NJ = 4)
 template <int MI, int NJ, int RS = 32, class OutRow>
 __device__ __forceinline__ void store_wave_block_s1(char* smem, const f32x16 (&acc)[MI][NJ], int lane, OutRow out_row,
                                                     int ncols = 32 * NJ) {
-  static_assert(RS == 32 || RS == 16, "staged rows");
-  constexpr int LDB = 32 * NJ + 8;               // staged row stride (bf16)
-  constexpr int LPR = 4 * NJ, RPP = 64 / LPR;    // lanes per row, rows per pass
-  static_assert(NWAVE * RS * LDB * 2 <= STB, "the staging fits ring stage 1");
-  bf16* st = reinterpret_cast<bf16*>(smem + STB) + wave_id() * RS * LDB;
-#pragma unroll
-  for (int i = 0; i < MI; ++i) {
-#pragma unroll
-    for (int h = 0; h < 32 / RS; ++h) {
-      // the lanes holding rows h RS .. h RS + RS - 1 of the block stage them (LDS accesses of one
-      // wave run in order, so these writes follow the previous half's reads)
-      if (RS == 32 || (lane & 31) / RS == h) {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-          for (int a = 0; a < 4; ++a)
-            st8(st + ((lane & 31) % RS) * LDB + 32 * j + acc_n(a, lane),
-                pack4(acc[i][j][4 * a], acc[i][j][4 * a + 1], acc[i][j][4 * a + 2], acc[i][j][4 * a + 3]));
-      }
-#pragma unroll
-      for (int s = 0; s < RS / RPP; ++s) {
-        const int rl = lane / LPR + RPP * s, c0 = (lane % LPR) * 8;
-        bf16* o = out_row(32 * i + RS * h + rl);
-        if (o && c0 < ncols) st16_nt(o + c0, *reinterpret_cast<const uint4*>(st + rl * LDB + c0));
-      }
-    }
-  }
+  static_assert(NWAVE * RS * (32 * NJ + 8) * 2 <= STB, "the staging fits ring stage 1");
+  store_wave_block_bf16<MI, NJ, RS>(smem + STB, acc, lane, out_row, ncols);
 }
 
 // ------------------------------------------------------------------------------------------------

@@ -55,8 +55,7 @@ constexpr int SMEM_MX = STAGES * STB_MX > 8 * SLAB * 4 ? STAGES * STB_MX : 8 * S
 
 // lane i copies 4 bytes from g into lds + 4*i (lds wave-uniform); see gl2lds
 __device__ __forceinline__ void gl2lds_dword(const void* g, char* lds) {
-  const unsigned off = __builtin_amdgcn_readfirstlane(
-      (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
+  const unsigned off = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds);   // the LDS address
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(off), "v"(g) : "memory", "m0");
 }
 
