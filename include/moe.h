@@ -167,9 +167,9 @@ moe_status moe_fwd(const moe_desc* d, const void* x, const float* logits,
  * weights and the per-block expert masks in one kernel), then the layer as moe_fwd. The pages fold the
  * routing into the fused operation ("Prime Mega MoE: kernel fuso per l'addestramento MoE" on "Prime
  * Mega MoE: il kernel che accelera il training AI del 55%"); the projection is the linear router of
- * moe_router_fwd. `logits` [T, E_total] fp32 is an output here: the logits the routing used (their
- * bits are those of this kernel's fp32 accumulation over H, which is not moe_router_fwd's order), so
- * that the routing is exactly oracle routing of `logits`. w_router [E_total, H] bf16, 16-byte aligned.
+ * moe_router_fwd. `logits` [T, E_total] fp32 is an output here: the logits the routing used, so
+ * that the routing is exactly oracle routing of `logits` (moe_router_fwd runs the same projection
+ * kernel, so moe_router_fwd then moe_fwd routes alike). w_router [E_total, H] bf16, 16-byte aligned.
  * The backward is moe_bwd, then moe_router_bwd with moe_bwd's dlogits.
  * Bf16 I/O modes only (MOE_ERR_UNSUPPORTED_MODE in MOE_MODE_FP32), E_total <= 256 and topk <= 8
  * (MOE_ERR_UNSUPPORTED_SHAPE otherwise: use moe_router_fwd, then moe_fwd). Workspace and `saved` as
@@ -206,9 +206,11 @@ moe_status moe_bwd(const moe_desc* d, const void* dy, const void* x,
  * moe_router_bwd gives the gradient of the whole x -> router -> layer composition. In an expert
  * share, dlogits is the share's contribution and the call is linear in it, so the shares' calls
  * add up to the full gradient.
- * Arithmetic: bf16 MFMA with fp32 accumulation. The contractions over H (forward) and over the
- * tokens (dw_router) are split into slices whose fp32 partial sums are added in a fixed order; the
- * backward multiplies a bf16 copy of dlogits, and dx is read, added to in fp32 and rounded once.
+ * Arithmetic: bf16 MFMA with fp32 accumulation. Up to 256 experts the forward is one workgroup per
+ * 64 tokens over all of H (the kernel moe_fwd_router uses, so the logits are bitwise the same);
+ * beyond that, and for the contraction over the tokens (dw_router), the sums are split into slices
+ * whose fp32 partial sums are added in a fixed order. The backward multiplies a bf16 copy of
+ * dlogits, and dx is read, added to in fp32 and rounded once.
  * In MOE_MODE_FP32 (the test mode) x, w_router, dx and dw_router are fp32 and every output is a
  * plain fp32 sum in a fixed order. No atomics: results are bitwise reproducible.
  * Modes: all four (MXFP8 and FP8_BWD take bf16 I/O; the projection itself stays bf16). Every

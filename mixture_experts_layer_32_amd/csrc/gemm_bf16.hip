@@ -1175,13 +1175,25 @@ __global__ __launch_bounds__(256) void k_router_sum_logits(RouterParams p) {
     if (e + c < p.E) out[e + c] = r[c];
 }
 
-// backward: dlb = bf16(dlogits), zero-padded to Ep columns; the zero page
+// backward: dlb = bf16(dlogits), zero-padded to Ep columns (8 per thread: Ep is a multiple of 64, so
+// a thread's 8 stay in one row; 16-byte loads when dlogits and its rows are 16-byte aligned); the
+// zero page
 __global__ __launch_bounds__(256) void k_router_dl_bf16(RouterParams p) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
   if (blockIdx.x == 0 && threadIdx.x < kZeroBytes / 16) static_cast<uint4*>(p.zeros)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
   if (i >= p.T * p.Ep) return;
-  const int64_t t = i / p.Ep, c = i - t * p.Ep;
-  static_cast<bf16*>(p.dlb)[i] = (bf16)(c < p.E ? p.dlogits[t * p.E + c] : 0.f);
+  const int64_t t = i / p.Ep;
+  const int c = (int)(i - t * p.Ep);
+  const float* src = p.dlogits + t * p.E + c;
+  float v[8];
+  if ((p.E & 3) == 0 && (reinterpret_cast<uintptr_t>(p.dlogits) & 15) == 0 && c + 8 <= p.E) {
+    const float4 a = *reinterpret_cast<const float4*>(src), b = *reinterpret_cast<const float4*>(src + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = c + e < p.E ? src[e] : 0.f;
+  }
+  *reinterpret_cast<uint4*>(static_cast<bf16*>(p.dlb) + i) = pack8(v);
 }
 
 // backward: dx[t][h] += sum_e dlb[t][e] W_r[e][h] (contraction over E; W_r is MN-major here)
@@ -1388,7 +1400,7 @@ hipError_t launch_router_fwd_bf16(const RouterParams& p, int grid, hipStream_t s
 hipError_t launch_router_bwd_bf16(const RouterParams& p, int grid, hipStream_t s) {
   hipError_t err;
   prof_mark_begin("router_dlogits_bf16", s);
-  k_router_dl_bf16<<<(unsigned)((p.T * p.Ep + 255) / 256), 256, 0, s>>>(p);
+  k_router_dl_bf16<<<(unsigned)((p.T * p.Ep / 8 + 255) / 256), 256, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   prof_mark_end(s);
   prof_mark_begin("router_dx_gemm", s);

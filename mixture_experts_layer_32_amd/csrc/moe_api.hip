@@ -806,8 +806,13 @@ moe_status moe_router_fwd(const moe_desc* d, const void* x, const void* w_router
   p.Ep = R.Ep;
   p.S = R.Sf;
   p.kc = R.kcf;
+  // up to 256 experts: the fused forward's projection (one workgroup per 64 tokens, all experts, no
+  // partial sums), so that these logits are bitwise the ones moe_fwd_router routes on
   hipError_t e = d->mode == MOE_MODE_FP32 ? launch_router_fwd_f32(p, static_cast<hipStream_t>(stream))
-                                          : launch_router_fwd_bf16(p, persistent_grid(1), static_cast<hipStream_t>(stream));
+                 : d->E_total <= 256
+                     ? launch_router_logits_bf16(x, w_router, logits, d->T, d->H, d->E_total,
+                                                 static_cast<hipStream_t>(stream))
+                     : launch_router_fwd_bf16(p, persistent_grid(1), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "router forward launch");
   return MOE_OK;
 }

@@ -83,6 +83,9 @@ hipError_t launch_route_tail(const RouteParams& p, hipStream_t s);
 // tail; the logits [T, E] fp32 are written to `logits`
 hipError_t launch_router_route_bf16(const RouteParams& p, const void* x, const void* w_router, float* logits, int H,
                                     hipStream_t s);
+// the projection of launch_router_route_bf16 alone (E <= 256): logits [T, E] fp32
+hipError_t launch_router_logits_bf16(const void* x, const void* w_router, float* logits, int64_t T, int H, int E,
+                                     hipStream_t s);
 
 // Row-tiled grouped GEMMs and wgrad GEMMs; T = float or bf16.
 struct FwdParams {

@@ -46,7 +46,10 @@ __device__ __forceinline__ const char* rat(const char* tile, int r, int c) {
   return tile + r * RB + ((c ^ rswz<RB>(r)) << 4);
 }
 
-template <int NB, int RB, int S>
+// TOPK: route the block's tokens (top-k, weights, masks) after writing the logits; without it the
+// kernel is the projection alone (moe_router_fwd), whose logits are then bitwise those the routing
+// uses in the fused forward.
+template <int NB, int RB, int S, bool TOPK>
 __global__ __launch_bounds__(512, 1) void k_router_topk_bf16(RouteParams rp, const bf16* __restrict__ x,
                                                              const bf16* __restrict__ wr, float* __restrict__ lg_out,
                                                              int H) {
@@ -66,7 +69,8 @@ __global__ __launch_bounds__(512, 1) void k_router_topk_bf16(RouteParams rp, con
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, th = w >> 2, eg = w & 3;
   const int64_t t0 = (int64_t)blockIdx.x * RT;
   const int E = rp.E;
-  for (int e = tid; e < rp.El; e += 512) mask[e] = 0ull;
+  if (TOPK)
+    for (int e = tid; e < rp.El; e += 512) mask[e] = 0ull;
   // Load i of this lane moves row (w L + i) RPI + lane / NC of its operand, chunk slot lane % NC
   // (global chunk slot ^ swizzle): one wave instruction fills 1 KB of whole row segments.
   const char* xp[LX];
@@ -146,6 +150,7 @@ __global__ __launch_bounds__(512, 1) void k_router_topk_bf16(RouteParams rp, con
     for (int r = w; r < nrow; r += 8)
       for (int c = lane; c < E; c += 64) lo[(size_t)r * E + c] = lg[r * LDL + c];
   }
+  if constexpr (!TOPK) return;
   // top-k: 8 lanes per token
   const int tl = tid >> 3;
   if (t0 + tl < rp.T)
@@ -165,12 +170,29 @@ hipError_t launch_router_route_bf16(const RouteParams& p, const void* x, const v
   prof_mark_begin("router_topk_fused", s);
   const bf16* xb = static_cast<const bf16*>(x);
   const bf16* wb = static_cast<const bf16*>(w_router);
-  if (p.E <= 128) k_router_topk_bf16<1, 256, 3><<<p.nblk, 512, 0, s>>>(p, xb, wb, logits, H);
-  else k_router_topk_bf16<2, 128, 3><<<p.nblk, 512, 0, s>>>(p, xb, wb, logits, H);
+  if (p.E <= 128) k_router_topk_bf16<1, 256, 3, true><<<p.nblk, 512, 0, s>>>(p, xb, wb, logits, H);
+  else k_router_topk_bf16<2, 128, 3, true><<<p.nblk, 512, 0, s>>>(p, xb, wb, logits, H);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   prof_mark_end(s);
   return launch_route_tail(p, s);
+}
+
+hipError_t launch_router_logits_bf16(const void* x, const void* w_router, float* logits, int64_t T, int H, int E,
+                                     hipStream_t s) {
+  RouteParams p{};   // the projection reads only T and E
+  p.T = T;
+  p.E = E;
+  const unsigned nblk = (unsigned)((T + kRouteTokens - 1) / kRouteTokens);
+  prof_mark_begin("router_fwd_gemm", s);
+  const bf16* xb = static_cast<const bf16*>(x);
+  const bf16* wb = static_cast<const bf16*>(w_router);
+  if (E <= 128) k_router_topk_bf16<1, 256, 3, false><<<nblk, 512, 0, s>>>(p, xb, wb, logits, H);
+  else k_router_topk_bf16<2, 128, 3, false><<<nblk, 512, 0, s>>>(p, xb, wb, logits, H);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  prof_mark_end(s);
+  return hipSuccess;
 }
 
 }  // namespace moe

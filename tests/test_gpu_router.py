@@ -2,15 +2,18 @@
 against the float64 oracle (oracle.router_forward, oracle.router_backward).
 
 Bar (relative Frobenius error per output, as for the layer):
- * logits <= 1e-5. Products of bf16 values are exact in fp32, and the fp32 sums (MFMA blocks of the
-   H-slices, then at most 4 slice partials in a fixed order) stay within a few 2^-24 sqrt(H) of
-   the float64 values relative to the row's scale: about 4e-6 at H = 4096.
+ * logits <= 1e-5. Products of bf16 values are exact in fp32, and the fp32 sums (MFMA blocks over H,
+   two interleaved chains; beyond 256 experts H-slices, then at most 4 slice partials in a fixed
+   order) stay within a few 2^-24 sqrt(H) of the float64 values relative to the row's scale: about
+   4e-6 at H = 4096.
  * dW_r and the router's part of dx <= 1e-2 (the bf16 bar): the backward multiplies a bf16 copy of
    dlogits (relative rounding 2^-9) and rounds its outputs to bf16 once.
  * Bitwise reproducible across calls.
  * The fp32 test mode (fp32 tensors, plain fp32 sums): every output <= 1e-5.
 The composition test runs x, W_r -> router -> layer -> router backward on the GPU and compares the
 total dx and dW_r with the oracle's chain on the same fp32 logits (so that both route alike).
+Up to 256 experts moe_router_fwd runs the fused forward's projection (one pass over H per 64 tokens),
+so its logits are bitwise those moe_fwd_router routes on; beyond, split-H partial sums.
 """
 import numpy as np
 import pytest
@@ -112,6 +115,31 @@ def test_router_deterministic():
     assert outs[0] == outs[1]
 
 
+@pytest.mark.parametrize("E", [96, 40, 37])
+def test_router_backward_dlogits_alignment(E):
+    """dlogits needs only 4-byte alignment: a copy at a 4-byte offset (and rows of E % 4 != 0 floats)
+    takes the conversion's scalar loads, and must give the bits of the 16-byte-aligned call."""
+    print(f"case router dlogits alignment E={E}", flush=True)
+    cfg, x, wr = router_inputs(T=300, H=256, E=E, k=4, seed=63)
+    layer = MoELayer(cfg.T, cfg.H, 128, cfg.E, cfg.k, "bf16")
+    xd, wrd = to_dev(x, torch.bfloat16), to_dev(wr, torch.bfloat16)
+    dl_np = sparse_dlogits(cfg.T, cfg.E, cfg.k, 64)
+    dl = to_dev(dl_np, torch.float32)
+    buf = torch.empty(cfg.T * cfg.E + 4, dtype=torch.float32, device="cuda")
+    dl_off = buf[1:1 + cfg.T * cfg.E].view(cfg.T, cfg.E)
+    dl_off.copy_(dl)
+    assert dl_off.data_ptr() % 16 == 4
+    outs = []
+    for d in (dl, dl_off):
+        dx = torch.zeros(cfg.T, cfg.H, dtype=torch.bfloat16, device="cuda")
+        dwr = layer.router_backward(xd, wrd, d, dx)
+        torch.cuda.synchronize()
+        outs.append((dx.view(torch.int16).clone(), dwr.view(torch.int16).clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    dwr_ref, dxr_ref = oracle.router_backward(dl_np, x, wr)
+    assert oracle.rel_frobenius(outs[0][1].view(torch.bfloat16).float().cpu().numpy(), dwr_ref) <= TOL_BWD
+
+
 def test_router_then_layer_composition():
     """x, W_r -> logits -> layer forward/backward -> router backward, all on the GPU."""
     print("case router composition", flush=True)
@@ -202,6 +230,10 @@ def test_fwd_router_fused(name, T, H, F, E, k, el, e0, mode):
     y2 = ref.forward(x, lg, wg, wu, wd)
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "y differs from moe_fwd on the same logits"
+    # moe_router_fwd runs the same projection: moe_router_fwd + moe_fwd routes exactly as moe_fwd_router
+    lg2 = ref.router_forward(x, wrd)
+    torch.cuda.synchronize()
+    assert torch.equal(lg2, lg), "moe_router_fwd's logits differ from moe_fwd_router's"
 
 
 @pytest.mark.slow
