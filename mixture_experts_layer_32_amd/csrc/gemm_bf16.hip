@@ -36,6 +36,8 @@
 //    (mainloop_pre): the weight-gradient tiles cost the same within an expert (the dynamic order
 //    measured 3-5 % slower there), and the down GEMM's and the dgrad of x's tiles all contract over
 //    the same K, the pre-issued K-tile gaining more than the counter's balance of half tiles.
+#include <mutex>
+
 #include "engine.h"
 #include "moe_internal.h"
 
@@ -1421,6 +1423,32 @@ hipError_t launch_router_bwd_bf16(const RouterParams& p, int grid, hipStream_t s
 hipError_t launch_backward_gemms_bf16(const BwdParams& p, int grid, hipStream_t s) {
   hipError_t err;
   if ((err = launch_sched_setup(p, KTILE, s)) != hipSuccess) return err;
+  std::unique_lock<std::mutex> lk;
+  hipStream_t s1 = 4 * p.El <= p.E ? nullptr : side_stream_fork(s, lk);
+  if (s1) {
+    // dH, then the dgrad of x, on the caller's stream (the critical path to the dx combine); the two
+    // weight gradients on the side stream, the down one from the start (it needs only dY and w h),
+    // the gate/up one after dH; their workgroups take the CUs that dH's and the dgrad's free
+    prof_mark_begin("gemm_bwd_dh_dswiglu", s);
+    k_bwd_dh_bf16<<<grid, NTHR8, 0, s>>>(p);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    prof_mark_end(s);
+    if ((err = side_stream_mark(s)) != hipSuccess) return err;   // dH done: the gate/up one may start
+    prof_mark_begin("gemm_wgrad_down", s1);
+    k_wgrad_down_bf16<<<grid, NTHR8, 0, s1>>>(p);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    prof_mark_end(s1);
+    if ((err = side_stream_wait_mark()) != hipSuccess) return err;
+    prof_mark_begin("gemm_dgrad_x", s);
+    k_dgrad_x_bf16<<<grid, NTHR8, 0, s>>>(p);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    prof_mark_end(s);
+    prof_mark_begin("gemm_wgrad_gateup", s1);
+    k_wgrad_gateup_bf16<<<grid, NTHR8, 0, s1>>>(p);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    prof_mark_end(s1);
+    return hipSuccess;   // joined after the dx combine (side_stream_join), which need not wait
+  }
   if (4 * p.El <= p.E) {   // an expert share: two launches of two GEMMs each
     prof_mark_begin("gemm_dh+wgrad_down", s);
     k_dh_wgrad_down_bf16<<<grid, NTHR8, 0, s>>>(p);

@@ -772,9 +772,15 @@ hipError_t launch_forward_gemms_mx(const FwdParams& p, int grid, hipStream_t s, 
   return hipSuccess;
 }
 
+// dH, then the dgrad of x, on the caller's stream; the two weight gradients on the device's side
+// stream when there is one (the down one from the start, the gate/up one after dH), as in the bf16
+// backward
 hipError_t launch_backward_gemms_mx(const BwdParams& p, int grid, hipStream_t s) {
   hipError_t err;
   if ((err = launch_sched_setup(p, KTILE, s)) != hipSuccess) return err;
+  std::unique_lock<std::mutex> lk;
+  hipStream_t s1 = side_stream_fork(s, lk);
+  hipStream_t sw = s1 ? s1 : s;   // the weight gradients' stream
   prof_mark_begin("gemm_bwd_dh_dswiglu", s);
   if (p.blk)
     k_bwd_dh_mx<true><<<grid, NTHR, 0, s>>>(p);
@@ -782,14 +788,16 @@ hipError_t launch_backward_gemms_mx(const BwdParams& p, int grid, hipStream_t s)
     k_bwd_dh_mx<false><<<grid, NTHR, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   prof_mark_end(s);
-  prof_mark_begin("gemm_wgrad_down", s);
-  k_wgrad_down_mx<<<grid, NTHR, 0, s>>>(p);
+  if (s1 && (err = side_stream_mark(s)) != hipSuccess) return err;
+  prof_mark_begin("gemm_wgrad_down", sw);
+  k_wgrad_down_mx<<<grid, NTHR, 0, sw>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  prof_mark_end(s);
-  prof_mark_begin("gemm_wgrad_gateup", s);
-  k_wgrad_gateup_mx<<<grid, NTHR, 0, s>>>(p);
+  prof_mark_end(sw);
+  if (s1 && (err = side_stream_wait_mark()) != hipSuccess) return err;
+  prof_mark_begin("gemm_wgrad_gateup", sw);
+  k_wgrad_gateup_mx<<<grid, NTHR, 0, sw>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  prof_mark_end(s);
+  prof_mark_end(sw);
   prof_mark_begin("gemm_dgrad_x", s);
   k_dgrad_x_mx<<<grid, NTHR, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;

@@ -171,6 +171,71 @@ static moe_status hip_fail(hipError_t e, const char* where) {
   return fail(MOE_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
 }
 
+// The backward's weight-gradient GEMMs run on a second stream per device, ordered against the
+// caller's stream by events, so that their workgroups take the CUs the critical path's kernels free
+// at their tails. The stream and its events are created on first use outside a graph capture (no
+// side stream then: everything runs in order on the caller's stream). The caller holds the device's
+// lock from the fork to its last launch on the side stream, so that the events' record/wait pairs
+// of different host threads do not interleave; the join, later, may order after another thread's
+// side work as well (never before its own).
+namespace {
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, mid = nullptr, join = nullptr;
+  bool tried = false;
+  std::mutex mu;
+};
+SideStream g_side[64];
+thread_local SideStream* t_side_pending = nullptr;
+SideStream* side_of_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  return &g_side[dev];
+}
+}  // namespace
+
+hipStream_t side_stream_fork(hipStream_t s, std::unique_lock<std::mutex>& lk) {
+  SideStream* ss = side_of_device();
+  if (!ss) return nullptr;
+  lk = std::unique_lock<std::mutex>(ss->mu);
+  if (!ss->s) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (ss->tried || hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+    ss->tried = true;
+    if (hipStreamCreateWithFlags(&ss->s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ss->fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss->mid, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss->join, hipEventDisableTiming) != hipSuccess) {
+      ss->s = nullptr;
+      return nullptr;
+    }
+  }
+  if (hipEventRecord(ss->fork, s) != hipSuccess || hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess)
+    return nullptr;
+  t_side_pending = ss;
+  return ss->s;
+}
+
+hipError_t side_stream_mark(hipStream_t s) {
+  SideStream* ss = t_side_pending;
+  return ss ? hipEventRecord(ss->mid, s) : hipSuccess;
+}
+
+hipError_t side_stream_wait_mark() {
+  SideStream* ss = t_side_pending;
+  return ss ? hipStreamWaitEvent(ss->s, ss->mid, 0) : hipSuccess;
+}
+
+hipError_t side_stream_join(hipStream_t s) {
+  SideStream* ss = t_side_pending;
+  if (!ss) return hipSuccess;
+  t_side_pending = nullptr;
+  std::lock_guard<std::mutex> g(ss->mu);
+  hipError_t err = hipEventRecord(ss->join, ss->s);
+  if (err != hipSuccess) return err;
+  return hipStreamWaitEvent(s, ss->join, 0);
+}
+
 int persistent_grid(int blocks_per_cu) {
   static int cached_dev = -1, cached_cus = 0;
   int dev = 0;
@@ -725,9 +790,14 @@ moe_status moe_bwd(const moe_desc* d, const void* dy, const void* x, const void*
     e = d->mode == MOE_MODE_FP32 ? launch_backward<float>(p, persistent_grid(2), s)
                                  : launch_backward_gemms_bf16(p, persistent_grid(1), s);
   }
-  if (e != hipSuccess) return hip_fail(e, "backward GEMM launch");
+  if (e != hipSuccess) {
+    side_stream_join(s);   // whatever reached the side stream is still waited for
+    return hip_fail(e, "backward GEMM launch");
+  }
   e = d->mode == MOE_MODE_FP32 ? launch_combine_bwd<float>(p, s) : launch_combine_bwd<bf16>(p, s);
+  hipError_t ej = side_stream_join(s);
   if (e != hipSuccess) return hip_fail(e, "backward combine launch");
+  if (ej != hipSuccess) return hip_fail(ej, "side stream join");
   return MOE_OK;
 }
 
