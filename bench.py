@@ -19,7 +19,8 @@ Printed on one JSON line:
                 checkpointed form (the backward recomputes the gate/up activations);
                 full_layer_2f_b_ms is the first
   roofline      the dominant kernel: algorithmic flops per launch / its mean duration (HIP events
-                on the launch stream) against the bf16 MFMA peak
+                on the launch stream, all launches on one stream for this pass) against the MFMA
+                peak of its arithmetic
   cpu_baseline  the float64 oracle on whole expert shares, at least 10 s of host time
 
     python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
@@ -335,7 +336,9 @@ def main():
     bwd_ms = float(np.median([e1.elapsed_time(e2) for _, e1, e2 in evs]))
     step_ev = np.array([e0.elapsed_time(e2) for e0, _, e2 in evs])   # GPU time of each fwd+bwd step
 
-    # per-kernel durations: the same K steps again with every launch bracketed by HIP events
+    # per-kernel durations: the same K steps again with every launch bracketed by HIP events (the
+    # library then keeps the backward's weight gradients on its stream, so that each pair of
+    # events brackets one kernel alone)
     binding.profile_enable(64 * a.steps)
     torch.cuda.synchronize()
     t1 = time.perf_counter()

@@ -42,9 +42,14 @@
  *  - Preconditions that are not checked: logits are finite, and buffers do not overlap.
  *  - Results are deterministic: no floating-point atomics anywhere, so repeated calls give
  *    bitwise-identical outputs.
- *  - The library keeps no state between calls apart from the profiling records and a
- *    thread-local error string. Calls on different streams may run concurrently if their
- *    buffers are distinct.
+ *  - The library keeps no state between calls apart from the profiling records, a
+ *    thread-local error string and, per device, one more stream with three events, which the
+ *    first moe_bwd on that device outside graph capture creates (at default priority). moe_bwd
+ *    runs its two weight-gradient GEMMs there: that stream first waits for everything enqueued
+ *    on `stream` before the call, and `stream` waits for it before any work enqueued after the
+ *    call, so the ordering seen on `stream` is as if all ran there. moe_bwd calls on one device
+ *    share that stream. Calls on different streams may run concurrently if their buffers are
+ *    distinct.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -283,7 +288,9 @@ const char* moe_last_error(void);
 /* Kernel timing with HIP events, for measurement tools. While enabled, every kernel the
  * library launches is bracketed by two events recorded on the launch stream. The library
  * creates them up front, `max_launches` pairs, and reuses them. Launches beyond that are not
- * recorded. moe_profile_enable() clears earlier records.
+ * recorded. moe_profile_enable() clears earlier records. While enabled, the backward also
+ * keeps its weight-gradient GEMMs on the launch stream (otherwise they run on a second stream of
+ * the device, overlapping the dH and dgrad GEMMs), so that each duration is that kernel's alone.
  * moe_profile_collect() waits for the recorded events and sums each kernel's durations.
  * Kernel names are returned by index: moe_profile_kernel(i, &name, &launches, &total_ms)
  * gives MOE_ERR_INVALID_ARG once i runs past the last kernel. */

@@ -194,8 +194,11 @@ SideStream* side_of_device() {
 }
 }  // namespace
 
+static bool prof_active();
+
 hipStream_t side_stream_fork(hipStream_t s, std::unique_lock<std::mutex>& lk) {
-  SideStream* ss = side_of_device();
+  // while kernel timing is on, everything stays on s so that each kernel's events bracket it alone
+  SideStream* ss = prof_active() ? nullptr : side_of_device();
   if (!ss) return nullptr;
   lk = std::unique_lock<std::mutex>(ss->mu);
   if (!ss->s) {
@@ -268,6 +271,8 @@ Prof& prof() {
 }
 thread_local int t_pending = -1;
 }  // namespace
+
+static bool prof_active() { return prof().on; }
 
 void prof_mark_begin(const char* name, hipStream_t s) {
   Prof& P = prof();

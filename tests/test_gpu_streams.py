@@ -1,0 +1,129 @@
+"""GPU: the backward's second stream.
+
+moe_bwd runs its two weight-gradient GEMMs on a stream of its own per device, forked from the
+caller's stream with an event and joined back into it after the dx combine. Nothing of this may
+be visible to a caller:
+ * the outputs are bitwise those of the single-stream order (the library keeps every launch on
+   the caller's stream while kernel timing is on);
+ * work enqueued on the caller's stream right after moe_bwd sees the finished weight gradients;
+ * two host threads running the layer at once, each on a stream of its own, get the results each
+   gets alone.
+"""
+import threading
+
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_layer_32_amd import binding, inputs
+from mixture_experts_layer_32_amd.layer import MoELayer
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("dx", "dlogits", "dw_gate", "dw_up", "dw_down")
+
+
+class Case:
+    def __init__(self, T, H, F, E, k, mode, seed, E_local=-1):
+        cfg, L = inputs.custom_layer(T=T, H=H, F=F, E=E, k=k, seed=seed, E_local=E_local)
+        dev = lambda a, t=torch.bfloat16: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(t)
+        self.x, self.dy, self.lg = dev(L["x"]), dev(L["dy"]), dev(L["logits"], torch.float32)
+        self.wg, self.wu, self.wd = dev(L["wg"]), dev(L["wu"]), dev(L["wd"])
+        self.layer = MoELayer(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, mode, cfg.el, cfg.e0)
+        self.y = torch.empty_like(self.x)
+        self.out = dict(dx=torch.empty_like(self.x),
+                        dlogits=torch.empty(cfg.T, cfg.E, dtype=torch.float32, device="cuda"),
+                        dw_gate=torch.empty_like(self.wg), dw_up=torch.empty_like(self.wu),
+                        dw_down=torch.empty_like(self.wd))
+
+    def poison(self, stream):
+        with torch.cuda.stream(stream):
+            for v in list(self.out.values()) + [self.y]:
+                v.view(torch.uint8).fill_(0xFF)        # NaN in every float format used
+
+    def step(self, stream):
+        self.layer.forward(self.x, self.lg, self.wg, self.wu, self.wd, self.y, stream=stream)
+        self.layer.backward(self.dy, self.x, self.wg, self.wu, self.wd, out=self.out, stream=stream)
+
+    def snapshot(self):
+        d = {n: v.view(torch.uint8).clone() for n, v in self.out.items()}
+        d["y"] = self.y.view(torch.uint8).clone()
+        return d
+
+
+def _same(a, b, tag):
+    for n in a:
+        assert torch.equal(a[n], b[n]), (tag, n)
+
+
+@pytest.mark.parametrize("mode", ["bf16", "mxfp8", "fp8"])
+def test_two_streams_match_one_stream(mode):
+    print(f"case streams bitwise mode={mode}", flush=True)
+    c = Case(T=900, H=512, F=384, E=8, k=3, mode=mode, seed=91)
+    st = torch.cuda.current_stream()
+    c.poison(st)
+    c.step(st)                          # weight gradients on the side stream
+    torch.cuda.synchronize()
+    two = c.snapshot()
+    binding.profile_enable(256)         # every launch stays on the caller's stream
+    try:
+        c.poison(st)
+        c.step(st)
+        torch.cuda.synchronize()
+        binding.profile_collect()
+    finally:
+        binding.profile_disable()
+    one = c.snapshot()
+    _same(two, one, mode)
+    assert not torch.isnan(c.out["dw_gate"].float()).any()
+
+
+def test_caller_stream_waits_for_weight_gradients():
+    """Copies enqueued on the caller's stream right after moe_bwd, before any host
+    synchronisation, equal the final outputs (the weight gradients are the last GEMMs to finish
+    when they run beside the dgrad)."""
+    print("case streams ordering", flush=True)
+    c = Case(T=2000, H=1024, F=512, E=16, k=4, mode="bf16", seed=92)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    for r in range(3):
+        c.poison(st)
+        c.step(st)
+        with torch.cuda.stream(st):
+            early = c.snapshot()        # enqueued behind moe_bwd on the same stream
+        torch.cuda.synchronize()
+        _same(early, c.snapshot(), r)
+        assert not torch.isnan(c.out["dw_down"].float()).any()
+
+
+def test_two_host_threads():
+    print("case streams two host threads", flush=True)
+    cases = [Case(T=1500, H=512, F=256, E=16, k=4, mode="bf16", seed=93),
+             Case(T=700, H=1024, F=384, E=8, k=2, mode="mxfp8", seed=94)]
+    streams = [torch.cuda.Stream() for _ in cases]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    ref = []
+    for c, s in zip(cases, streams):
+        c.step(s)
+        s.synchronize()
+        ref.append(c.snapshot())
+    errors = []
+
+    def run(i):
+        try:
+            for _ in range(4):
+                cases[i].step(streams[i])
+            streams[i].synchronize()
+        except Exception as e:   # surfaced below, on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for i, c in enumerate(cases):
+        _same(c.snapshot(), ref[i], i)
