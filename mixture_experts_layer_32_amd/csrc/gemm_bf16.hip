@@ -36,7 +36,6 @@
 //    (mainloop_pre): the weight-gradient tiles cost the same within an expert (the dynamic order
 //    measured 3-5 % slower there), and the down GEMM's and the dgrad of x's tiles all contract over
 //    the same K, the pre-issued K-tile gaining more than the counter's balance of half tiles.
-#include <mutex>
 
 #include "engine.h"
 #include "moe_internal.h"
@@ -1423,8 +1422,7 @@ hipError_t launch_router_bwd_bf16(const RouterParams& p, int grid, hipStream_t s
 hipError_t launch_backward_gemms_bf16(const BwdParams& p, int grid, hipStream_t s) {
   hipError_t err;
   if ((err = launch_sched_setup(p, KTILE, s)) != hipSuccess) return err;
-  std::unique_lock<std::mutex> lk;
-  hipStream_t s1 = 4 * p.El <= p.E ? nullptr : side_stream_fork(s, lk);
+  hipStream_t s1 = 4 * p.El <= p.E ? nullptr : side_stream_fork(s);
   if (s1) {
     // dH, then the dgrad of x, on the caller's stream (the critical path to the dx combine); the two
     // weight gradients on the side stream, the down one from the start (it needs only dY and w h),

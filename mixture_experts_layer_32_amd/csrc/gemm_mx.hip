@@ -778,8 +778,7 @@ hipError_t launch_forward_gemms_mx(const FwdParams& p, int grid, hipStream_t s, 
 hipError_t launch_backward_gemms_mx(const BwdParams& p, int grid, hipStream_t s) {
   hipError_t err;
   if ((err = launch_sched_setup(p, KTILE, s)) != hipSuccess) return err;
-  std::unique_lock<std::mutex> lk;
-  hipStream_t s1 = side_stream_fork(s, lk);
+  hipStream_t s1 = side_stream_fork(s);
   hipStream_t sw = s1 ? s1 : s;   // the weight gradients' stream
   prof_mark_begin("gemm_bwd_dh_dswiglu", s);
   if (p.blk)

@@ -174,10 +174,10 @@ static moe_status hip_fail(hipError_t e, const char* where) {
 // The backward's weight-gradient GEMMs run on a second stream per device, ordered against the
 // caller's stream by events, so that their workgroups take the CUs the critical path's kernels free
 // at their tails. The stream and its events are created on first use outside a graph capture (no
-// side stream then: everything runs in order on the caller's stream). The caller holds the device's
-// lock from the fork to its last launch on the side stream, so that the events' record/wait pairs
-// of different host threads do not interleave; the join, later, may order after another thread's
-// side work as well (never before its own).
+// side stream then: everything runs in order on the caller's stream). A thread holds the device's
+// lock from the fork to the join, so that the events' record/wait pairs of different host threads
+// do not interleave, and a side stream taken into one thread's graph capture is back out of it
+// before another thread uses it.
 namespace {
 struct SideStream {
   hipStream_t s = nullptr;
@@ -186,7 +186,11 @@ struct SideStream {
   std::mutex mu;
 };
 SideStream g_side[64];
+// between side_stream_fork and side_stream_join the calling thread holds the device's lock, so that
+// no other thread's backward reaches the side stream while this one's work is forked onto it (under
+// graph capture, the side stream belongs to the capture until the join)
 thread_local SideStream* t_side_pending = nullptr;
+thread_local std::unique_lock<std::mutex> t_side_lock;
 SideStream* side_of_device() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
@@ -196,11 +200,12 @@ SideStream* side_of_device() {
 
 static bool prof_active();
 
-hipStream_t side_stream_fork(hipStream_t s, std::unique_lock<std::mutex>& lk) {
+hipStream_t side_stream_fork(hipStream_t s) {
+  if (t_side_pending) side_stream_join(s);   // a fork left unjoined: never hold two locks
   // while kernel timing is on, everything stays on s so that each kernel's events bracket it alone
   SideStream* ss = prof_active() ? nullptr : side_of_device();
   if (!ss) return nullptr;
-  lk = std::unique_lock<std::mutex>(ss->mu);
+  std::unique_lock<std::mutex> lk(ss->mu);
   if (!ss->s) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (ss->tried || hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
@@ -216,6 +221,7 @@ hipStream_t side_stream_fork(hipStream_t s, std::unique_lock<std::mutex>& lk) {
   if (hipEventRecord(ss->fork, s) != hipSuccess || hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess)
     return nullptr;
   t_side_pending = ss;
+  t_side_lock = std::move(lk);
   return ss->s;
 }
 
@@ -233,7 +239,7 @@ hipError_t side_stream_join(hipStream_t s) {
   SideStream* ss = t_side_pending;
   if (!ss) return hipSuccess;
   t_side_pending = nullptr;
-  std::lock_guard<std::mutex> g(ss->mu);
+  std::unique_lock<std::mutex> lk = std::move(t_side_lock);   // released on return
   hipError_t err = hipEventRecord(ss->join, ss->s);
   if (err != hipSuccess) return err;
   return hipStreamWaitEvent(s, ss->join, 0);

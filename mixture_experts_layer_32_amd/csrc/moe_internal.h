@@ -1,6 +1,5 @@
 // Host-side internals of libmoe: buffer layout and kernel launchers.
 #pragma once
-#include <mutex>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -208,11 +207,12 @@ hipError_t launch_gather_t_quant(const void* x, const int* ptok, const int* offs
 
 int persistent_grid(int blocks_per_cu);
 // The device's side stream for the backward's weight gradients (moe_api.hip). side_stream_fork
-// orders it after the work on s so far and returns it with the device's lock held in lk (null: no
-// side stream, run everything on s); side_stream_mark records a point on s, side_stream_wait_mark
-// makes the side stream wait for it (both under that lock); side_stream_join, after the backward's
-// last launch on s, makes s wait for the side stream's work (nothing if this thread did not fork).
-hipStream_t side_stream_fork(hipStream_t s, std::unique_lock<std::mutex>& lk);
+// orders it after the work on s so far and returns it (null: no side stream, run everything on s);
+// from then until side_stream_join the calling thread holds the device's side-stream lock.
+// side_stream_mark records a point on s, side_stream_wait_mark makes the side stream wait for it;
+// side_stream_join, after the backward's last launch on s, makes s wait for the side stream's work
+// and releases the lock (nothing if this thread did not fork). Every fork must be joined.
+hipStream_t side_stream_fork(hipStream_t s);
 hipError_t side_stream_mark(hipStream_t s);
 hipError_t side_stream_wait_mark();
 hipError_t side_stream_join(hipStream_t s);
