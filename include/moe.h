@@ -34,8 +34,10 @@
  *      logits, dlogits               [T, E_total]      float (fp32)
  *      w_gate, w_up, dw_gate, dw_up  [E_local, F, H]   elem (out x in, K contiguous)
  *      w_down, dw_down               [E_local, H, F]   elem
- *  - stream is a hipStream_t (NULL: the default stream). Every call only enqueues work on it
- *    and returns. No call synchronises the host or copies device data to the host.
+ *  - stream is a hipStream_t (NULL: the default stream) of the calling thread's current device,
+ *    where every buffer lives (another device's stream: MOE_ERR_INVALID_ARG). Every call only
+ *    enqueues work on it and returns. No call synchronises the host or copies device data to the
+ *    host.
  *  - Validation happens on the host before anything is enqueued. On any error nothing is
  *    enqueued and no output is touched. Launch failures return MOE_ERR_HIP. A device fault
  *    surfaces at the caller's next synchronisation.

@@ -171,6 +171,21 @@ static moe_status hip_fail(hipError_t e, const char* where) {
   return fail(MOE_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
 }
 
+// The work goes to the stream's device, the CU count, the side stream and the static scratch are the
+// calling thread's current device's: the two must be the same (the null stream is the current
+// device's).
+static moe_status check_stream(void* stream) {
+  if (!stream) return MOE_OK;
+  int cur = 0;
+  hipDevice_t sd = 0;
+  if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(static_cast<hipStream_t>(stream), &sd) != hipSuccess)
+    return fail(MOE_ERR_INVALID_ARG, "stream: its device could not be queried");
+  if (sd != cur)
+    return fail(MOE_ERR_INVALID_ARG, "stream belongs to device " + std::to_string(sd) +
+                                         ", not to the current device " + std::to_string(cur));
+  return MOE_OK;
+}
+
 // The backward's weight-gradient GEMMs run on a second stream per device, ordered against the
 // caller's stream by events, so that their workgroups take the CUs the critical path's kernels free
 // at their tails. The stream and its events are created on first use outside a graph capture (no
@@ -409,6 +424,7 @@ moe_status moe_route(const moe_desc* d, const float* logits, void* saved, void* 
   if (st != MOE_OK) return st;
   if ((st = check_ptrs({{logits, "logits"}}, 4)) != MOE_OK) return st;
   if ((st = check_ptrs({{saved, "saved"}, {ws, "ws"}}, 256)) != MOE_OK) return st;
+  if ((st = check_stream(stream)) != MOE_OK) return st;
   const Layout L = make_layout(*d);
   if (ws_bytes < L.fwd_total) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "forward workspace too small");
   hipError_t e = launch_route(route_params(*d, L, logits, saved, ws), static_cast<hipStream_t>(stream));
@@ -472,6 +488,7 @@ moe_status moe_route_static(const moe_desc* d, const float* logits, void* saved,
   if (st != MOE_OK) return st;
   if ((st = check_ptrs({{logits, "logits"}}, 4)) != MOE_OK) return st;
   if ((st = check_ptrs({{saved, "saved"}}, 256)) != MOE_OK) return st;
+  if ((st = check_stream(stream)) != MOE_OK) return st;
   const RouteScratch R = route_scratch(*d);
   if (R.total > kStaticScratchBytes)
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_route_static needs " + std::to_string(R.total) +
@@ -504,6 +521,7 @@ static moe_status fwd_impl(const moe_desc* d, const void* x, const float* logits
   if ((st = check_ptrs({{w_router ? logits_out : logits, "logits"}}, 4)) != MOE_OK) return st;
   if (w_router && (st = check_ptrs({{w_router, "w_router"}}, 16)) != MOE_OK) return st;
   if ((st = check_ptrs({{saved, "saved"}, {ws, "ws"}}, 256)) != MOE_OK) return st;
+  if ((st = check_stream(stream)) != MOE_OK) return st;
   const Layout L = make_layout(*d);
   if (ws_bytes < L.fwd_total) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "forward workspace too small");
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -709,6 +727,7 @@ moe_status moe_bwd(const moe_desc* d, const void* dy, const void* x, const void*
     return st;
   if ((st = check_ptrs({{dlogits, "dlogits"}}, 4)) != MOE_OK) return st;
   if ((st = check_ptrs({{saved, "saved"}, {ws, "ws"}}, 256)) != MOE_OK) return st;
+  if ((st = check_stream(stream)) != MOE_OK) return st;
   const Layout L = make_layout(*d);
   if (ws_bytes < L.bwd_total) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "backward workspace too small");
   const char* sv = static_cast<const char*>(saved);
@@ -874,6 +893,7 @@ moe_status moe_router_fwd(const moe_desc* d, const void* x, const void* w_router
   if (st != MOE_OK) return st;
   if ((st = check_ptrs({{x, "x"}, {w_router, "w_router"}, {logits, "logits"}}, 16)) != MOE_OK) return st;
   if ((st = check_ptrs({{ws, "ws"}}, 256)) != MOE_OK) return st;
+  if ((st = check_stream(stream)) != MOE_OK) return st;
   const RouterLayout R = router_layout(*d);
   if (ws_bytes < R.fwd_total) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "router forward workspace too small");
   RouterParams p{};
@@ -907,6 +927,7 @@ moe_status moe_router_bwd(const moe_desc* d, const void* x, const void* w_router
     return st;
   if ((st = check_ptrs({{dlogits, "dlogits"}}, 4)) != MOE_OK) return st;
   if ((st = check_ptrs({{ws, "ws"}}, 256)) != MOE_OK) return st;
+  if ((st = check_stream(stream)) != MOE_OK) return st;
   const RouterLayout R = router_layout(*d);
   if (ws_bytes < R.bwd_total) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "router backward workspace too small");
   char* w = static_cast<char*>(ws);
@@ -937,6 +958,7 @@ moe_status moe_mx_quantize(const void* in, int64_t rows, int64_t cols, int axis,
   moe_status st;
   if ((st = check_ptrs({{in, "in"}, {q, "q"}}, 16)) != MOE_OK) return st;
   if ((st = check_ptrs({{scales, "scales"}}, 4)) != MOE_OK) return st;
+  if ((st = check_stream(stream)) != MOE_OK) return st;
   if (rows < 1 || cols < 1) return fail(MOE_ERR_INVALID_ARG, "rows and cols must be positive");
   if (axis != 0 && axis != 1) return fail(MOE_ERR_INVALID_ARG, "axis must be 0 or 1");
   if (axis == 1 && cols % 32 != 0) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "cols must be a multiple of 32 (axis 1)");
@@ -958,6 +980,7 @@ moe_status moe_fp8_block_quantize(const void* in, int64_t rows, int64_t cols, in
   moe_status st;
   if ((st = check_ptrs({{in, "in"}, {q, "q"}}, 16)) != MOE_OK) return st;
   if ((st = check_ptrs({{scales, "scales"}}, 4)) != MOE_OK) return st;
+  if ((st = check_stream(stream)) != MOE_OK) return st;
   if (rows < 1 || cols < 1) return fail(MOE_ERR_INVALID_ARG, "rows and cols must be positive");
   if (weight != 0 && weight != 1) return fail(MOE_ERR_INVALID_ARG, "weight must be 0 or 1");
   if (weight == 1) {
