@@ -43,8 +43,6 @@ FWD_GEMMS = ("gemm_gateup_swiglu", "gemm_down")
 GEMM_FLOPS_PER_PAIR = {  # in units of H*F
     "gemm_gateup_swiglu": 4, "gemm_down": 2, "gemm_bwd_dh_dswiglu": 2,
     "gemm_wgrad_down": 2, "gemm_wgrad_gateup": 4, "gemm_dgrad_x": 4,
-    # on an expert share the backward runs two GEMMs per launch
-    "gemm_dh+wgrad_down": 4, "gemm_dgrad_x+wgrad_gateup": 8,
 }
 
 
@@ -353,7 +351,7 @@ def main():
     value = flops / (ms_step * 1e-3) / 1e12
     # time the step's GEMM flops would take at the MFMA peak of each GEMM's arithmetic
     ideal_ms = sum(GEMM_FLOPS_PER_PAIR[n] * cfg.H * cfg.F * P / (kernel_peak(n, mode) * 1e12) * 1e3
-                   for n in GEMM_FLOPS_PER_PAIR if "+" not in n)
+                   for n in GEMM_FLOPS_PER_PAIR)
     per_kernel = {}
     for name, (n, tot) in kern.items():
         avg = tot / n

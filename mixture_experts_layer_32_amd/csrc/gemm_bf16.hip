@@ -682,73 +682,6 @@ __device__ __forceinline__ void dh_tile(const BwdParams& p, char* smem, int tile
   }
 }
 
-// backward: dX = [da db] [W_gate[e]; W_up[e]] (contraction over 2F)
-template <class Fetch>
-__device__ __forceinline__ void dgrad_x_tile(const BwdParams& p, char* smem, int tile, Fetch fetch) {
-  // 128x64 per wave: B (the weights, MN-major) goes through the slower transposing LDS read, so
-  // each wave takes 2 B blocks and 4 A blocks rather than 4 and 2
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
-  const bf16* __restrict__ dab = static_cast<const bf16*>(p.dab);
-  bf16* __restrict__ dxp = static_cast<bf16*>(p.dxp);
-  const int H = p.H, F = p.F, ntn = H / TILE;
-  const int bn[2] = {64 * wn, 64 * wn + 32};
-  {
-    const int mt = tile / ntn, nt = tile - mt * ntn;
-    const int2 me = p.mtile2[mt];
-    const int e = me.x, r0 = me.y, seg_end = p.offsets[e + 1];
-    KOp la;
-#pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
-      const int r = min(r0 + KOp::row_of(j), seg_end - 1);
-      la.p[j] = reinterpret_cast<const char*>(dab + (size_t)r * 2 * F) + 16 * KOp::chunk_of(j);
-    }
-    MNOp<WeightRows> lb;
-    lb.rows = WeightRows{reinterpret_cast<const char*>(static_cast<const bf16*>(p.wg) + (size_t)e * F * H + nt * TILE),
-                         reinterpret_cast<const char*>(static_cast<const bf16*>(p.wu) + (size_t)e * F * H + nt * TILE),
-                         (size_t)H * 2, F};
-    lb.zero = static_cast<const char*>(p.zeros);
-    lb.init(nt * TILE, H);
-    f32x16 acc[4][2];
-    mainloop_rows<false, true, 64>(acc, smem, la, lb, 2 * F / KTILE, 32 * wm, bn, seg_end - r0 <= 128);
-    fetch();
-    const int rq = r0 + 32 * wm;   // the wave's row m is tile row 32 wm + 64 (m / 32) + m % 32
-    bf16* const oq = dxp + nt * TILE + 64 * wn;
-    store_wave_block(smem, acc, lane, [&](int m) {
-      const int r = rq + 64 * (m >> 5) + (m & 31);
-      return r < seg_end ? oq + (size_t)r * H : nullptr;
-    }, 64);
-  }
-}
-
-// backward: dW_down[e] (H x F) = sum over the expert's pairs of dY_t hw_r^T
-template <class Fetch>
-__device__ __forceinline__ void wgrad_down_tile(const BwdParams& p, char* smem, int lid, Fetch fetch) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;   // 64x128 per wave
-  const int H = p.H, F = p.F, ntn = (F + TILE - 1) / TILE, tpe = (H / TILE) * ntn;
-  const int e = lid / tpe, t = lid - e * tpe, mt = t / ntn, nt = t - mt * ntn;
-  const int seg0 = p.offsets[e], seg_end = p.offsets[e + 1];
-  MNOp<GatherRows> la;
-  la.rows = GatherRows{reinterpret_cast<const char*>(static_cast<const bf16*>(p.dy) + mt * TILE), p.ptok,
-                       (size_t)H * 2, seg0, seg_end, {}};
-  la.zero = static_cast<const char*>(p.zeros);
-  la.init(mt * TILE, H);
-  // B rows: hwT[n][qoff[e] ..], contiguous along the expert's pairs (zero-padded to 32)
-  KOp lb;
-  const bf16* hwt = static_cast<const bf16*>(p.hwt) + p.qoff[e];
-#pragma unroll
-  for (int j = 0; j < LOADS; ++j) {
-    const int n = min(nt * TILE + KOp::row_of(j), F - 1);
-    lb.p[j] = reinterpret_cast<const char*>(hwt + (size_t)n * p.qc) + 16 * KOp::chunk_of(j);
-  }
-  const int bn[4] = {128 * wn, 128 * wn + 32, 128 * wn + 64, 128 * wn + 96};
-  f32x16 acc[2][4];
-  mainloop<true, false>(acc, smem, la, lb, (seg_end - seg0 + KTILE - 1) / KTILE, 64 * wm, bn);
-  fetch();
-  bf16* __restrict__ out = static_cast<bf16*>(p.dwd) + (size_t)e * H * F;
-  const int mq = mt * TILE + 64 * wm, nq = nt * TILE + 128 * wn;
-  store_wave_block(smem, acc, lane, [&](int m) { return out + (size_t)(mq + m) * F + nq; }, F - nq);
-}
-
 // the dgrad of h over its M-tile list, from the counter of scheduler slot 0
 __device__ __forceinline__ void dh_tiles(const BwdParams& p, char* smem, int* s_tile) {
   TileSched ts(p.sched + 0 * kSchedInts, *p.num_mtiles2 * ((p.F + TILE - 1) / TILE));
@@ -757,7 +690,7 @@ __device__ __forceinline__ void dh_tiles(const BwdParams& p, char* smem, int* s_
 
 // the down weight gradient over its XCD's cost-balanced range, round-robin, each tile's first K-tile
 // issued before the previous tile's epilogue, which stages its rows as bf16 in ring stage 1 sixteen
-// at a time (as the down GEMM). Same operands, wave layout and bits as wgrad_down_tile.
+// at a time (as the down GEMM).
 __device__ __forceinline__ void wgrad_down_tiles(const BwdParams& p, char* smem) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;   // 64x128 per wave
   const int H = p.H, F = p.F, ntn = (F + TILE - 1) / TILE, tpe = (H / TILE) * ntn;
@@ -876,7 +809,7 @@ __device__ __forceinline__ void wgrad_gateup_tiles(const BwdParams& p, char* sme
 // backward: dX = [da db] [W_gate[e]; W_up[e]] over a static range per XCD taken round-robin (every
 // tile contracts over 2F, so equal counts balance; an expert's half tile does half the MFMAs), each
 // tile's first K-tile issued before the previous tile's epilogue, which stages its rows as bf16 in
-// ring stage 1 (mainloop_pre_rows). Same operands, wave layout and bits as dgrad_x_tile.
+// ring stage 1 (mainloop_pre_rows).
 __device__ __forceinline__ void dgrad_x_tiles_pre(const BwdParams& p, char* smem) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;   // 128x64 per wave
   const int H = p.H, F = p.F, ntn = H / TILE, nk = 2 * F / KTILE;
@@ -934,84 +867,9 @@ __device__ __forceinline__ void dgrad_x_tiles_pre(const BwdParams& p, char* smem
   }
 }
 
-// One gate/up weight-gradient tile without the pre-issued first K-tile (for the dynamic queue of an
-// expert share, where the next tile is not known before the epilogue).
-template <class Fetch>
-__device__ __forceinline__ void wgrad_gateup_tile(const BwdParams& p, char* smem, int lid, Fetch fetch) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;   // 128x64 per wave
-  const int H = p.H, F = p.F, ntn = H / TILE, tpe = (2 * F / TILE) * ntn;
-  const int e = lid / tpe, t = lid - e * tpe, mt = t / ntn, nt = t - mt * ntn;
-  const int seg0 = ld_uniform(p.offsets, e), seg_end = ld_uniform(p.offsets, e + 1);
-  const bf16* dabt = static_cast<const bf16*>(p.dabt) + ld_uniform(p.qoff, e);
-  KOp la;
-#pragma unroll
-  for (int j = 0; j < LOADS; ++j) {
-    const int m = mt * TILE + KOp::row_of(j);
-    la.p[j] = reinterpret_cast<const char*>(dabt + (size_t)m * p.qc) + 16 * KOp::chunk_of(j);
-  }
-  MNOp<GatherRows> lb;
-  lb.rows = GatherRows{reinterpret_cast<const char*>(static_cast<const bf16*>(p.x) + nt * TILE), p.ptok,
-                       (size_t)H * 2, seg0, seg_end, {}};
-  lb.zero = static_cast<const char*>(p.zeros);
-  lb.init(nt * TILE, H);
-  const int bn[2] = {64 * wn, 64 * wn + 32};
-  f32x16 acc[4][2];
-  mainloop<false, true>(acc, smem, la, lb, (seg_end - seg0 + KTILE - 1) / KTILE, 128 * wm, bn);
-  fetch();
-  bf16* __restrict__ dwg = static_cast<bf16*>(p.dwg) + (size_t)e * F * H;
-  bf16* __restrict__ dwu = static_cast<bf16*>(p.dwu) + (size_t)e * F * H;
-  const int mq = mt * TILE + 128 * wm, nq = nt * TILE + 64 * wn;
-  store_wave_block(smem, acc, lane, [&](int m) {
-    const int mm = mq + m;
-    return (mm < F ? dwg + (size_t)mm * H : dwu + (size_t)(mm - F) * H) + nq;
-  }, 64);
-}
-
-// Two tile lists behind one dynamic scheduler per XCD: the XCD's equal share of list A (na tiles in
-// all), then its range [b[x], b[x+1]) of list B (a weight gradient's cost-balanced split), taken in
-// that order from one counter (zero at launch). first() and next() return the queue position (below
-// qa: A tile a0 + position; below qa + qb: B tile b0 + position - qa) or -1 at the end; fetch() runs
-// once per tile after its main loop. next() opens with a barrier of its own, since a tile without a
-// K-tile (an empty expert's weight gradient) has none before the slot is written again.
-struct TileQueue2 {
-  int* ctr;
-  int a0, qa, b0, qb, nxt;
-  __device__ __forceinline__ TileQueue2(int* counters, int na, const int* b) {
-    const int xcd = blockIdx.x & 7, per = (na + 7) >> 3;
-    a0 = min(na, xcd * per);
-    qa = min(na, a0 + per) - a0;
-    b0 = ld_uniform(b, xcd);
-    qb = ld_uniform(b, xcd + 1) - b0;
-    ctr = counters + xcd;
-    nxt = 0;
-  }
-  __device__ __forceinline__ int take(int q) {
-    nxt = qa + qb;   // past the queue unless fetch() runs
-    return q < qa + qb ? q : -1;
-  }
-  __device__ __forceinline__ void fetch() {
-    if (threadIdx.x == 0) nxt = atomicAdd(ctr, 1);
-  }
-  __device__ __forceinline__ int first(int* slot) {
-    if (threadIdx.x == 0) *slot = atomicAdd(ctr, 1);
-    block_sync();
-    return take(*slot);
-  }
-  __device__ __forceinline__ int next(int* slot) {
-    block_sync();
-    if (threadIdx.x == 0) *slot = nxt;
-    block_sync();
-    return take(*slot);
-  }
-};
-
-// The backward GEMMs as kernels: each alone, and, for an expert share, in two launches that each run
-// two independent GEMMs. A share of the 30B-A3B layer (16 of 128 experts: about 16 k pairs) gives the
-// dgrad of h 204 tiles for 256 CUs; in one launch with the down weight gradient (and the gate/up
-// weight gradient with the dgrad of x, which both need only da and db) the two GEMMs' tiles fill the
-// CUs together. Each XCD's workgroups take the two GEMMs' tiles from one queue (TileQueue2), the
-// longer row-tiled tiles first, so that the shorter weight-gradient tiles fill the ends. (On the full
-// layer every GEMM fills the CUs alone, and they run as separate kernels.)
+// The backward GEMMs as kernels. On an expert share too (16 of 128 experts of the 30B-A3B layer:
+// about 16 k pairs, 204 dH tiles for 256 CUs) they fill each other's tails on the two streams: 3 %
+// faster there than two launches of two GEMMs each from one tile queue per XCD.
 __global__ __launch_bounds__(NTHR8, 1) void k_bwd_dh_bf16(BwdParams p) {
   MOE_SMEM
   __shared__ int s_tile;
@@ -1028,26 +886,6 @@ __global__ __launch_bounds__(NTHR8, 1) void k_wgrad_down_bf16(BwdParams p) {
 __global__ __launch_bounds__(NTHR8, 1) void k_wgrad_gateup_bf16(BwdParams p) {
   MOE_SMEM
   wgrad_gateup_tiles(p, smem);
-}
-__global__ __launch_bounds__(NTHR8, 1) void k_dh_wgrad_down_bf16(BwdParams p) {
-  MOE_SMEM
-  __shared__ int s_tile;
-  TileQueue2 q(p.sched + kSchedShareA * kSchedInts, *p.num_mtiles2 * ((p.F + TILE - 1) / TILE),
-               p.sched + kSchedWgradDown * kSchedInts);
-  for (int t = q.first(&s_tile); t >= 0; t = q.next(&s_tile)) {
-    if (t < q.qa) dh_tile(p, smem, q.a0 + t, [&] { q.fetch(); });
-    else wgrad_down_tile(p, smem, q.b0 + t - q.qa, [&] { q.fetch(); });
-  }
-}
-__global__ __launch_bounds__(NTHR8, 1) void k_dgrad_x_wgrad_gateup_bf16(BwdParams p) {
-  MOE_SMEM
-  __shared__ int s_tile;
-  TileQueue2 q(p.sched + kSchedShareB * kSchedInts, *p.num_mtiles2 * (p.H / TILE),
-               p.sched + kSchedWgradGateup * kSchedInts);
-  for (int t = q.first(&s_tile); t >= 0; t = q.next(&s_tile)) {
-    if (t < q.qa) dgrad_x_tile(p, smem, q.a0 + t, [&] { q.fetch(); });
-    else wgrad_gateup_tile(p, smem, q.b0 + t - q.qa, [&] { q.fetch(); });
-  }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -1419,61 +1257,34 @@ hipError_t launch_router_bwd_bf16(const RouterParams& p, int grid, hipStream_t s
   return hipSuccess;
 }
 
+// dH, then the dgrad of x, on the caller's stream (the critical path to the dx combine); the two
+// weight gradients on the device's side stream when there is one (on s otherwise), the down one from
+// the start (it needs only dY and w h), the gate/up one after dH. Their workgroups take the CUs that
+// dH's and the dgrad's free in those kernels' tails; the caller's stream waits for them after the dx
+// combine (side_stream_join).
 hipError_t launch_backward_gemms_bf16(const BwdParams& p, int grid, hipStream_t s) {
   hipError_t err;
   if ((err = launch_sched_setup(p, KTILE, s)) != hipSuccess) return err;
-  hipStream_t s1 = 4 * p.El <= p.E ? nullptr : side_stream_fork(s);
-  if (s1) {
-    // dH, then the dgrad of x, on the caller's stream (the critical path to the dx combine); the two
-    // weight gradients on the side stream, the down one from the start (it needs only dY and w h),
-    // the gate/up one after dH; their workgroups take the CUs that dH's and the dgrad's free
-    prof_mark_begin("gemm_bwd_dh_dswiglu", s);
-    k_bwd_dh_bf16<<<grid, NTHR8, 0, s>>>(p);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    prof_mark_end(s);
-    if ((err = side_stream_mark(s)) != hipSuccess) return err;   // dH done: the gate/up one may start
-    prof_mark_begin("gemm_wgrad_down", s1);
-    k_wgrad_down_bf16<<<grid, NTHR8, 0, s1>>>(p);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    prof_mark_end(s1);
-    if ((err = side_stream_wait_mark()) != hipSuccess) return err;
-    prof_mark_begin("gemm_dgrad_x", s);
-    k_dgrad_x_bf16<<<grid, NTHR8, 0, s>>>(p);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    prof_mark_end(s);
-    prof_mark_begin("gemm_wgrad_gateup", s1);
-    k_wgrad_gateup_bf16<<<grid, NTHR8, 0, s1>>>(p);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    prof_mark_end(s1);
-    return hipSuccess;   // joined after the dx combine (side_stream_join), which need not wait
-  }
-  if (4 * p.El <= p.E) {   // an expert share: two launches of two GEMMs each
-    prof_mark_begin("gemm_dh+wgrad_down", s);
-    k_dh_wgrad_down_bf16<<<grid, NTHR8, 0, s>>>(p);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    prof_mark_end(s);
-    prof_mark_begin("gemm_dgrad_x+wgrad_gateup", s);
-    k_dgrad_x_wgrad_gateup_bf16<<<grid, NTHR8, 0, s>>>(p);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    prof_mark_end(s);
-    return hipSuccess;
-  }
+  hipStream_t s1 = side_stream_fork(s);
+  hipStream_t sw = s1 ? s1 : s;   // the weight gradients' stream
   prof_mark_begin("gemm_bwd_dh_dswiglu", s);
   k_bwd_dh_bf16<<<grid, NTHR8, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   prof_mark_end(s);
-  prof_mark_begin("gemm_wgrad_down", s);
-  k_wgrad_down_bf16<<<grid, NTHR8, 0, s>>>(p);
+  if (s1 && (err = side_stream_mark(s)) != hipSuccess) return err;   // dH done: the gate/up one may start
+  prof_mark_begin("gemm_wgrad_down", sw);
+  k_wgrad_down_bf16<<<grid, NTHR8, 0, sw>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  prof_mark_end(s);
-  prof_mark_begin("gemm_wgrad_gateup", s);
-  k_wgrad_gateup_bf16<<<grid, NTHR8, 0, s>>>(p);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  prof_mark_end(s);
+  prof_mark_end(sw);
+  if (s1 && (err = side_stream_wait_mark()) != hipSuccess) return err;
   prof_mark_begin("gemm_dgrad_x", s);
   k_dgrad_x_bf16<<<grid, NTHR8, 0, s>>>(p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   prof_mark_end(s);
+  prof_mark_begin("gemm_wgrad_gateup", sw);
+  k_wgrad_gateup_bf16<<<grid, NTHR8, 0, sw>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark_end(sw);
   return hipSuccess;
 }
 

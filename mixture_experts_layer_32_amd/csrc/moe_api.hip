@@ -171,6 +171,8 @@ static moe_status hip_fail(hipError_t e, const char* where) {
   return fail(MOE_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
 }
 
+static bool kernel_timing_on();
+
 // The work goes to the stream's device, the CU count, the side stream and the static scratch are the
 // calling thread's current device's: the two must be the same (the null stream is the current
 // device's).
@@ -213,12 +215,10 @@ SideStream* side_of_device() {
 }
 }  // namespace
 
-static bool prof_active();
-
 hipStream_t side_stream_fork(hipStream_t s) {
   if (t_side_pending) side_stream_join(s);   // a fork left unjoined: never hold two locks
   // while kernel timing is on, everything stays on s so that each kernel's events bracket it alone
-  SideStream* ss = prof_active() ? nullptr : side_of_device();
+  SideStream* ss = kernel_timing_on() ? nullptr : side_of_device();
   if (!ss) return nullptr;
   std::unique_lock<std::mutex> lk(ss->mu);
   if (!ss->s) {
@@ -293,7 +293,7 @@ Prof& prof() {
 thread_local int t_pending = -1;
 }  // namespace
 
-static bool prof_active() { return prof().on; }
+static bool kernel_timing_on() { return prof().on; }
 
 void prof_mark_begin(const char* name, hipStream_t s) {
   Prof& P = prof();

@@ -18,8 +18,6 @@ constexpr int kSchedInts = 16;      // ints per GEMM's tile-scheduler slot (8 pe
 constexpr int kSchedSlots = 8;      // scheduler slots per workspace
 // backward slots holding the weight-gradient GEMMs' per-XCD tile ranges (9 boundaries each)
 constexpr int kSchedWgradDown = 2, kSchedWgradGateup = 3;
-// backward slots of the two-GEMM queues of an expert share (their counters)
-constexpr int kSchedShareA = 4, kSchedShareB = 5;
 
 // Byte offsets of every region inside the three caller-provided buffers.
 struct Layout {

@@ -56,10 +56,14 @@ def _same(a, b, tag):
         assert torch.equal(a[n], b[n]), (tag, n)
 
 
-@pytest.mark.parametrize("mode", ["bf16", "mxfp8", "fp8"])
-def test_two_streams_match_one_stream(mode):
-    print(f"case streams bitwise mode={mode}", flush=True)
-    c = Case(T=900, H=512, F=384, E=8, k=3, mode=mode, seed=91)
+@pytest.mark.parametrize("mode,share", [("bf16", False), ("mxfp8", False), ("fp8", False), ("bf16", True),
+                                        ("mxfp8", True)])
+def test_two_streams_match_one_stream(mode, share):
+    print(f"case streams bitwise mode={mode} share={share}", flush=True)
+    if share:   # 8 of 32 experts on this GPU
+        c = Case(T=1200, H=512, F=256, E=32, k=4, mode=mode, seed=95, E_local=8)
+    else:
+        c = Case(T=900, H=512, F=384, E=8, k=3, mode=mode, seed=91)
     st = torch.cuda.current_stream()
     c.poison(st)
     c.step(st)                          # weight gradients on the side stream
