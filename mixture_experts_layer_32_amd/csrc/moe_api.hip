@@ -203,11 +203,8 @@ struct SideStream {
   std::mutex mu;
 };
 SideStream g_side[64];
-// between side_stream_fork and side_stream_join the calling thread holds the device's lock, so that
-// no other thread's backward reaches the side stream while this one's work is forked onto it (under
-// graph capture, the side stream belongs to the capture until the join)
-thread_local SideStream* t_side_pending = nullptr;
-thread_local std::unique_lock<std::mutex> t_side_lock;
+thread_local SideStream* t_side_pending = nullptr;     // forked and not yet joined by this thread
+thread_local std::unique_lock<std::mutex> t_side_lock;  // that device's lock, held until the join
 SideStream* side_of_device() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
