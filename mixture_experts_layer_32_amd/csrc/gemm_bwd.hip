@@ -292,12 +292,15 @@ __global__ __launch_bounds__(256) void k_combine_bwd(BwdParams p, int tpw) {
       gbar += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wg), tt * k + j));
     const float val = w * (g - gbar);   // dlogits of slot q's expert, meaningful in the token's lanes
     float* row = p.dlogits + (t0 + tt) * p.E;
-    for (int e = lane; e < p.E; e += 64) {
+    // uniform over the wave, so that every lane is active at the readlane (the token's lanes can lie
+    // past E, where a loop over e < E would leave val uncomputed)
+    for (int eb = 0; eb < p.E; eb += 64) {
+      const int e = eb + lane;
       float v = 0.f;
       for (int j = 0; j < k; ++j)
         if (__builtin_amdgcn_readlane(ex, tt * k + j) == e)
           v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, val), tt * k + j));
-      row[e] = v;
+      if (e < p.E) row[e] = v;
     }
   }
 }

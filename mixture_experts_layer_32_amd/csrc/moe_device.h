@@ -269,11 +269,15 @@ __host__ __device__ constexpr int combine_tpw(int k, int E_local, int E_total) {
 
 // dst row part `part` (of nparts) = the sum, in slot order and fp32, of the source rows src[pp] of the
 // k slots whose pair positions pp sit in lanes slot0 .. slot0+k-1 of ppv (pp < 0: not local). Each
-// lane takes two chunks, so 16 slot rows are in flight per lane.
+// lane takes two chunks, so 16 slot rows are in flight per lane. The loop is uniform over the wave,
+// with every lane active at the readlane (a value computed under a narrower exec mask is undefined in
+// the lanes outside it, and the slots' lanes can lie past a short row's last chunk): lanes past the
+// row's end load zeros and store nothing.
 template <class T, int VEC>
 __device__ __forceinline__ void combine_row_part(const T* __restrict__ src, int ppv, int slot0, int k, int H, int nch,
                                                  int part, int nparts, int lane, T* __restrict__ dst) {
-  for (int c0 = lane + 128 * part; c0 < nch; c0 += 128 * nparts) {
+  for (int cb = 128 * part; cb < nch; cb += 128 * nparts) {
+    const int c0 = cb + lane;
     float acc[2][VEC];
 #pragma unroll
     for (int h = 0; h < 2; ++h)

@@ -65,6 +65,11 @@ SMALL = [
     # shares of at most a quarter of the experts: the backward runs two GEMMs per launch
     custom("share_quarter", T=700, H=512, F=384, E=32, k=4, E_local=8, e0=12, seed=25),
     custom("share_with_empty_experts", T=500, H=256, F=256, E=64, k=2, E_local=12, e0=14, zipf_s=0.3, seed=26),
+    # several tokens per combine wavefront whose slot lanes lie past E (dlogits) and past the row's
+    # chunks (H = 256): cross-lane reads from lanes outside a narrower loop's exec mask
+    custom("share_small_E_k8", T=411, H=512, F=128, E=18, k=8, E_local=2, e0=16, zipf_s=1.1, seed=28),
+    custom("share_k16_H256", T=300, H=256, F=128, E=40, k=16, E_local=8, e0=4, seed=29),
+    custom("share_k16_H256_fp32", mode="fp32", T=300, H=256, F=128, E=40, k=16, E_local=8, e0=4, seed=29),
     custom("wide_H4096_F1536", T=130, H=4096, F=1536, E=4, k=2, seed=20),
 ]
 

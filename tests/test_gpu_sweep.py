@@ -31,7 +31,7 @@ def _case(i):
     return mode, kw
 
 
-CASES = [pytest.param(*_case(i), id=f"sweep{i}") for i in range(20)]
+CASES = [pytest.param(*_case(i), id=f"sweep{i}") for i in range(40)]
 
 
 @pytest.mark.parametrize("mode,kw", CASES)
