@@ -2,7 +2,8 @@
 
 Each case draws its shape from a fixed seed: T, H (a multiple of 256), F (a multiple of 128), E, k,
 an expert share (E_local, e0) and sometimes a Zipf-like skew of the expert loads, so that the
-kernels meet shapes and routing outcomes the hand-picked cases do not name. Bar: routing bit-exact,
+kernels meet shapes and routing outcomes the hand-picked cases do not name (a second, wider set
+reaches 160 experts, top-32 and H = 1024). Bar: routing bit-exact,
 every output within the mode's relative Frobenius tolerance, experts with no rows exactly zero.
 """
 import numpy as np
@@ -31,7 +32,23 @@ def _case(i):
     return mode, kw
 
 
-CASES = [pytest.param(*_case(i), id=f"sweep{i}") for i in range(40)]
+def _wide_case(i):
+    # wider draws: up to 160 experts and top-32, H up to 1024, F up to 1024, longer token counts
+    rng = np.random.default_rng(3000 + i)
+    mode = MODES[i % len(MODES)]
+    E = int(rng.integers(2, 161))
+    k = int(rng.integers(1, min(32, E) + 1))
+    share = rng.random() < 0.4
+    el = int(rng.integers(1, E + 1)) if share else E
+    e0 = int(rng.integers(0, E - el + 1)) if share else 0
+    kw = dict(T=int(rng.integers(1, 1500)), H=int(rng.choice([256, 512, 768, 1024])),
+              F=int(rng.choice([128, 256, 384, 512, 768, 1024])), E=E, k=k, seed=4000 + i,
+              E_local=el if share else -1, e0=e0, zipf_s=float(rng.choice([0.0, 0.0, 1.1, 2.5])))
+    return mode, kw
+
+
+CASES = [pytest.param(*_case(i), id=f"sweep{i}") for i in range(40)] + \
+    [pytest.param(*_wide_case(i), id=f"wide{i}") for i in range(30)]
 
 
 @pytest.mark.parametrize("mode,kw", CASES)
