@@ -3,7 +3,7 @@
 Each case draws its shape from a fixed seed: T, H (a multiple of 256), F (a multiple of 128), E, k,
 an expert share (E_local, e0) and sometimes a Zipf-like skew of the expert loads, so that the
 kernels meet shapes and routing outcomes the hand-picked cases do not name (a second, wider set
-reaches 160 experts, top-32 and H = 1024). Bar: routing bit-exact,
+reaches 160 experts, top-32 and H = 1024, a third model-sized H and F on few tokens). Bar: routing bit-exact,
 every output within the mode's relative Frobenius tolerance, experts with no rows exactly zero.
 """
 import numpy as np
@@ -47,8 +47,24 @@ def _wide_case(i):
     return mode, kw
 
 
+def _big_case(i):
+    # model-sized H and F (up to 7168 and 2560) on few tokens
+    rng = np.random.default_rng(5000 + i)
+    mode = MODES[i % len(MODES)]
+    E = int(rng.integers(2, 65))
+    k = int(rng.integers(1, min(8, E) + 1))
+    share = rng.random() < 0.3
+    el = int(rng.integers(1, E + 1)) if share else E
+    e0 = int(rng.integers(0, E - el + 1)) if share else 0
+    kw = dict(T=int(rng.integers(1, 200)), H=int(rng.choice([2048, 4096, 7168])),
+              F=int(rng.choice([1536, 2048, 2560])), E=E, k=k, seed=6000 + i,
+              E_local=el if share else -1, e0=e0, zipf_s=float(rng.choice([0.0, 1.1])))
+    return mode, kw
+
+
 CASES = [pytest.param(*_case(i), id=f"sweep{i}") for i in range(40)] + \
-    [pytest.param(*_wide_case(i), id=f"wide{i}") for i in range(30)]
+    [pytest.param(*_wide_case(i), id=f"wide{i}") for i in range(30)] + \
+    [pytest.param(*_big_case(i), id=f"big{i}") for i in range(10)]
 
 
 @pytest.mark.parametrize("mode,kw", CASES)
