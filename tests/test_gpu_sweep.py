@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 from mixture_experts_layer_32_amd import inputs
-from gpu_util import OUTS, TOL, run_layer
+from gpu_util import OUTS, TOL, raw_bits, run_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -88,3 +88,19 @@ def test_sweep_parity(mode, kw):
     for e in np.nonzero(r["counts"] == 0)[0]:
         for n in ("dwg", "dwu", "dwd"):
             assert not np.any(got[n][e]), (n, e)
+
+
+RECOMPUTE_CASES = [pytest.param(*_case(i), id=f"sweep{i}") for i in range(0, 40, 3)] + \
+    [pytest.param(*_wide_case(i), id=f"wide{i}") for i in range(0, 30, 3)]
+
+
+@pytest.mark.parametrize("mode,kw", RECOMPUTE_CASES)
+def test_sweep_recompute_bitwise(mode, kw):
+    """Activation checkpointing (the backward recomputes the gate/up activations) gives the same
+    bits as keeping them, on the sweep's shapes."""
+    print(f"case sweep recompute mode={mode} {kw}", flush=True)
+    cfg, L = inputs.custom_layer(dtype="fp32" if mode == "fp32" else "bf16", **kw)
+    a = raw_bits(cfg, L, mode)
+    b = raw_bits(cfg, L, mode, recompute=True)
+    for n in OUTS:
+        assert a[n] == b[n], n
