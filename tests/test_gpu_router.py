@@ -59,6 +59,17 @@ def router_inputs(T, H, E, k, seed, dtype="bf16"):
     return cfg, L["x"], inputs.router_weight(cfg)
 
 
+def _router_sweep_case(i):
+    rng = np.random.default_rng(7000 + i)
+    E = int(rng.integers(1, 513))
+    shape = dict(T=int(rng.integers(1, 1500)), H=int(rng.choice([256, 512, 768, 1024, 2048])), E=E,
+                 k=int(rng.integers(1, min(32, E) + 1)))
+    return (f"sweep{i}", shape, ("bf16", "bf16", "mxfp8", "fp32")[i % 4])
+
+
+CASES += [_router_sweep_case(i) for i in range(16)]
+
+
 @pytest.mark.parametrize("name,shape,mode", CASES, ids=[c[0] for c in CASES])
 def test_router_parity(name, shape, mode):
     print(f"case router {name} mode={mode} {shape}", flush=True)
@@ -204,6 +215,20 @@ FUSED = [
     ("E64_k1", 129, 256, 128, 64, 1, None, 0, "bf16"),
     ("E128_mxfp8", 300, 512, 256, 128, 8, None, 0, "mxfp8"),
 ]
+
+
+def _fused_sweep_case(i):
+    rng = np.random.default_rng(8000 + i)
+    E = int(rng.integers(2, 257))
+    k = int(rng.integers(1, min(8, E) + 1))
+    share = rng.random() < 0.3
+    el = int(rng.integers(1, E + 1)) if share else None
+    e0 = int(rng.integers(0, E - el + 1)) if share else 0
+    return (f"sweep{i}", int(rng.integers(1, 1200)), int(rng.choice([256, 512, 1024])), 128, E, k, el, e0,
+            ("bf16", "mxfp8", "fp8_bwd", "fp8")[i % 4])
+
+
+FUSED += [_fused_sweep_case(i) for i in range(12)]
 
 
 @pytest.mark.parametrize("name,T,H,F,E,k,el,e0,mode", FUSED, ids=[c[0] for c in FUSED])
