@@ -97,6 +97,20 @@ def test_small_layer_parity(cfg, L, mode):
         assert not np.any(got["y"][none]) and not np.any(got["dx"][none])
 
 
+@pytest.mark.parametrize("mode", ["bf16", "mxfp8", "fp8", "fp32"])
+def test_share_with_no_local_pairs(mode):
+    """An expert share that no token routes to (P = 0): every output is written, and exactly zero,
+    whatever the workspace held (poisoned with NaN bit patterns)."""
+    print(f"case share with no local pairs mode={mode}", flush=True)
+    cfg, L = inputs.custom_layer(T=500, H=256, F=128, E=64, k=2, E_local=4, e0=60, zipf_s=5.0, seed=30,
+                                 dtype="fp32" if mode == "fp32" else "bf16")
+    got = run_layer(cfg, L, mode, poison=True)
+    r = check_routing(cfg, L, got["routing"])
+    assert r["counts"].sum() == 0
+    for n in OUTS:
+        assert not np.any(got[n]), n
+
+
 def test_expert_shares_add_up_on_gpu():
     cfg, L = inputs.custom_layer(T=256, H=256, F=128, E=8, k=2, dtype="bf16", seed=21)
     full = run_layer(cfg, L)
