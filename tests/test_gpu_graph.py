@@ -22,17 +22,19 @@ def _snapshot(t):
     return {n: v.view(torch.uint8).clone() for n, v in t.items()}
 
 
-@pytest.mark.parametrize("mode", ["bf16", "mxfp8", "fp32"])
-@pytest.mark.parametrize("recompute", [False, True])
-def test_step_replays_bitwise(mode, recompute):
-    print(f"case graph step mode={mode} recompute={recompute}", flush=True)
+@pytest.mark.parametrize("mode,recompute,share", [
+    ("bf16", False, False), ("mxfp8", False, False), ("fp32", False, False),
+    ("bf16", True, False), ("mxfp8", True, False), ("fp32", True, False),
+    ("fp8", False, False), ("fp8_bwd", False, False), ("bf16", False, True), ("mxfp8", True, True)])
+def test_step_replays_bitwise(mode, recompute, share):
+    print(f"case graph step mode={mode} recompute={recompute} share={share}", flush=True)
     cfg, L = inputs.custom_layer(T=333, H=512, F=256, E=16, k=4, dtype="fp32" if mode == "fp32" else "bf16",
-                                 seed=81)
+                                 seed=81, E_local=4 if share else -1, e0=8 if share else 0)
     dt = torch.float32 if mode == "fp32" else torch.bfloat16
     dev = lambda a, t=dt: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(t)
     x, dy, lg = dev(L["x"]), dev(L["dy"]), dev(L["logits"], torch.float32)
     wg, wu, wd = dev(L["wg"]), dev(L["wu"]), dev(L["wd"])
-    layer = MoELayer(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, mode, recompute=recompute)
+    layer = MoELayer(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, mode, cfg.el, cfg.e0, recompute=recompute)
     out = dict(y=torch.empty(cfg.T, cfg.H, dtype=dt, device="cuda"), dx=torch.empty_like(x),
                dlogits=torch.empty(cfg.T, cfg.E, dtype=torch.float32, device="cuda"),
                dw_gate=torch.empty_like(wg), dw_up=torch.empty_like(wu), dw_down=torch.empty_like(wd))
