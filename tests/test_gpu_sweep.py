@@ -62,9 +62,20 @@ def _big_case(i):
     return mode, kw
 
 
+# many tokens on a narrow layer: thousands of routing blocks and combine wavefronts
+LONG = [
+    ("bf16", dict(T=5000, H=256, F=128, E=300, k=8, seed=7001)),
+    ("mxfp8", dict(T=20000, H=256, F=128, E=64, k=2, seed=7002)),
+    ("fp32", dict(T=33000, H=256, F=128, E=128, k=8, seed=7003)),
+    ("fp8", dict(T=12000, H=256, F=128, E=8, k=2, seed=7004)),
+    ("fp8_bwd", dict(T=16384, H=256, F=128, E=128, k=8, seed=7005, E_local=16, e0=48)),
+    ("bf16", dict(T=25000, H=256, F=128, E=512, k=32, seed=7006, E_local=40, e0=0)),
+]
+
 CASES = [pytest.param(*_case(i), id=f"sweep{i}") for i in range(40)] + \
     [pytest.param(*_wide_case(i), id=f"wide{i}") for i in range(30)] + \
-    [pytest.param(*_big_case(i), id=f"big{i}") for i in range(10)]
+    [pytest.param(*_big_case(i), id=f"big{i}") for i in range(10)] + \
+    [pytest.param(m, kw, id=f"long{i}") for i, (m, kw) in enumerate(LONG)]
 
 
 @pytest.mark.parametrize("mode,kw", CASES)
