@@ -278,9 +278,8 @@ def main():
     a = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
-        print("bench.py measures the one-GPU layer only: this build runs on a single MI355X and has no "
-              "multi-GPU path (how the layer would shard over experts is described in DESIGN.md).",
-              file=sys.stderr)
+        print("bench.py measures the layer on one GPU only: the library runs on a single MI355X and has no "
+              "multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
