@@ -278,7 +278,7 @@ def main():
     a = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
-        print("bench.py measures the layer on one GPU only: the library runs on a single MI355X and has no "
+        print("bench.py measures the one-GPU layer only: the library runs on a single MI355X and has no "
               "multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
