@@ -18,6 +18,7 @@ import torch
 import oracle
 from mixture_experts_layer_32_amd import inputs
 from gpu_util import OUTS, ROW_TOL, TOL, run_layer
+from mixture_experts_layer_32_amd.layer import MoELayer
 
 pytestmark = pytest.mark.gpu
 
@@ -256,3 +257,38 @@ def test_wgrad_xcd_split_balances_a_skewed_load():
         assert even.max() > 1.1 * even.mean()                   # the skew defeats equal counts
         assert cost.max() <= cost.sum() / 8 + tile_cost.max(), (cost, b)
         assert cost.max() < even.max()
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+def test_element_offsets_beyond_32_bits():
+    """320 k routed pairs of H = 7168 (2.3e9 elements in the per-pair buffers the down GEMM writes, the
+    dgrad of x writes and both combines read): y, dx and dlogits rows of the tokens whose pairs sit
+    at the highest positions, and of a few others, against the oracle computed from those tokens'
+    own pairs."""
+    print("case offsets beyond 32 bits: T=160000 H=7168 F=2048 E=4 k=2", flush=True)
+    cfg, L = inputs.custom_layer(T=160000, H=7168, F=2048, E=4, k=2, seed=32)
+    dt = torch.bfloat16
+    dev = lambda a, t=dt: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(t)
+    x, dy, lg = dev(L["x"]), dev(L["dy"]), dev(L["logits"], torch.float32)
+    wg, wu, wd = dev(L["wg"]), dev(L["wu"]), dev(L["wd"])
+    layer = MoELayer(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, "bf16")
+    y = layer.forward(x, lg, wg, wu, wd)
+    g = layer.backward(dy, x, wg, wu, wd)
+    torch.cuda.synchronize()
+    rt = layer.routing()
+    pp = rt["pair_pos"].numpy().reshape(cfg.T, cfg.k)
+    assert int(rt["offsets"][-1]) * cfg.H >= 2 ** 31
+    top = np.argsort(-pp.max(axis=1))[:8]                  # pairs at the highest positions
+    rest = np.random.default_rng(33).choice(cfg.T, 8, replace=False)
+    toks = np.unique(np.concatenate([top, rest]))
+    ti = torch.from_numpy(toks).to("cuda")
+    got = dict(y=y[ti].float().cpu().numpy(), dx=g["dx"][ti].float().cpu().numpy(),
+               dlogits=g["dlogits"][ti].cpu().numpy())
+    ref = oracle.token_rows(toks, L["dy"], L["x"], L["logits"], L["wg"], L["wu"], L["wd"], cfg.k)
+    for n in ("y", "dx", "dlogits"):
+        ref_n = ref[n]
+        e = oracle.rel_frobenius(got[n], ref_n)
+        worst = float(np.max(row_errors(got[n], ref_n)))
+        print(n, f"{e:.2e} worst row {worst:.2e}", flush=True)
+        assert e <= TOL["bf16"] and worst <= ROW_TOL["bf16"], (n, e, worst)
