@@ -261,18 +261,19 @@ def test_wgrad_xcd_split_balances_a_skewed_load():
 
 @pytest.mark.slow
 @pytest.mark.timeout(600)
-def test_element_offsets_beyond_32_bits():
+@pytest.mark.parametrize("mode", ["bf16", "mxfp8"])
+def test_element_offsets_beyond_32_bits(mode):
     """320 k routed pairs of H = 7168 (2.3e9 elements in the per-pair buffers the down GEMM writes, the
     dgrad of x writes and both combines read): y, dx and dlogits rows of the tokens whose pairs sit
     at the highest positions, and of a few others, against the oracle computed from those tokens'
     own pairs."""
-    print("case offsets beyond 32 bits: T=160000 H=7168 F=2048 E=4 k=2", flush=True)
+    print(f"case offsets beyond 32 bits: T=160000 H=7168 F=2048 E=4 k=2 mode={mode}", flush=True)
     cfg, L = inputs.custom_layer(T=160000, H=7168, F=2048, E=4, k=2, seed=32)
     dt = torch.bfloat16
     dev = lambda a, t=dt: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(t)
     x, dy, lg = dev(L["x"]), dev(L["dy"]), dev(L["logits"], torch.float32)
     wg, wu, wd = dev(L["wg"]), dev(L["wu"]), dev(L["wd"])
-    layer = MoELayer(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, "bf16")
+    layer = MoELayer(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, mode)
     y = layer.forward(x, lg, wg, wu, wd)
     g = layer.backward(dy, x, wg, wu, wd)
     torch.cuda.synchronize()
@@ -285,10 +286,11 @@ def test_element_offsets_beyond_32_bits():
     ti = torch.from_numpy(toks).to("cuda")
     got = dict(y=y[ti].float().cpu().numpy(), dx=g["dx"][ti].float().cpu().numpy(),
                dlogits=g["dlogits"][ti].cpu().numpy())
-    ref = oracle.token_rows(toks, L["dy"], L["x"], L["logits"], L["wg"], L["wu"], L["wd"], cfg.k)
+    ref = oracle.token_rows(toks, L["dy"], L["x"], L["logits"], L["wg"], L["wu"], L["wd"], cfg.k,
+                            mode=None if mode == "bf16" else mode)
     for n in ("y", "dx", "dlogits"):
         ref_n = ref[n]
         e = oracle.rel_frobenius(got[n], ref_n)
         worst = float(np.max(row_errors(got[n], ref_n)))
         print(n, f"{e:.2e} worst row {worst:.2e}", flush=True)
-        assert e <= TOL["bf16"] and worst <= ROW_TOL["bf16"], (n, e, worst)
+        assert e <= TOL[mode] and worst <= ROW_TOL[mode], (n, e, worst)
