@@ -62,6 +62,20 @@ def _big_case(i):
     return mode, kw
 
 
+def _tiny_case(i):
+    # one to eight tokens against up to 512 experts and top-32 (most experts and tiles empty)
+    rng = np.random.default_rng(97000 + i)
+    mode = MODES[i % len(MODES)]
+    E = int(rng.choice([1, 2, 3, 7, 32, 64, 255, 256, 257, 511, 512]))
+    k = int(rng.integers(1, min(32, E) + 1))
+    share = rng.random() < 0.4
+    el = int(rng.integers(1, E + 1)) if share else E
+    e0 = int(rng.integers(0, E - el + 1)) if share else 0
+    kw = dict(T=int(rng.integers(1, 9)), H=int(rng.choice([256, 512])), F=int(rng.choice([128, 256])), E=E, k=k,
+              seed=98000 + i, E_local=el if share else -1, e0=e0)
+    return mode, kw
+
+
 # many tokens on a narrow layer: thousands of routing blocks and combine wavefronts
 LONG = [
     ("bf16", dict(T=5000, H=256, F=128, E=300, k=8, seed=7001)),
@@ -75,7 +89,8 @@ LONG = [
 CASES = [pytest.param(*_case(i), id=f"sweep{i}") for i in range(40)] + \
     [pytest.param(*_wide_case(i), id=f"wide{i}") for i in range(30)] + \
     [pytest.param(*_big_case(i), id=f"big{i}") for i in range(10)] + \
-    [pytest.param(m, kw, id=f"long{i}") for i, (m, kw) in enumerate(LONG)]
+    [pytest.param(m, kw, id=f"long{i}") for i, (m, kw) in enumerate(LONG)] + \
+    [pytest.param(*_tiny_case(i), id=f"tiny{i}") for i in range(15)]
 
 
 @pytest.mark.parametrize("mode,kw", CASES)
